@@ -1,0 +1,244 @@
+"""CPU oracle for the matrix-core GEMM library -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never reaches it, and it
+never reaches the GPU library: the two share no code, header or constant.
+
+The arithmetic lives in ``oracle.c`` (plain C11 + OpenMP); this module only
+builds/loads it and marshals numpy arrays.  What each routine computes, and the
+passages it follows, is stated in ``oracle.c``:
+
+* ``gemm_float``   -- D = alpha*sA*sB*(A*B) + beta*C, binary64 accumulation in
+  ascending k, rounded once to binary32 ("Accurate Models of AMD Matrix Cores",
+  Section 2, Eq. (1)).
+* ``gemm_i8``      -- exact int8 x int8 -> int32 (wraps mod 2^32).
+* ``compress24`` / ``decompress24`` -- the 2:4 compressed form ("RDNA4 sparse
+  WMMA builtins", Structured sparsity (2:4 pattern); Common parameters, index).
+* ``gemm_sparse24`` -- decompress, then ``gemm_float``.
+* ``float_bound`` / ``check_float`` / ``check_exact`` -- the acceptance test:
+  |D_gpu - D_ref| <= 4*2^-24*(K+2)*|alpha*sA*sB|*S + 2^-24*|D_ref| (+ 2^-24*|beta*c|
+  when beta is not 0 or +-1), S = sum_k |a_ik*b_kj|; integers must be equal.
+
+Every function here is pinned by the ``-m "not gpu"`` tests in
+``tests/test_oracle_*.py`` against closed forms, brute force, library witnesses
+and the values the pages print.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_liboracle.so")
+
+DTYPES = {"bf16": 0, "f16": 1, "i8": 2, "e4m3": 3, "e5m2": 4}
+LAYOUTS = {"k_contig": 0, "mn_contig": 1}
+CODE_NP = {"bf16": np.uint16, "f16": np.uint16, "i8": np.int8, "e4m3": np.uint8, "e5m2": np.uint8}
+
+U = 2.0 ** -24  # unit roundoff of binary32
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with the host C compiler (no HIP involved)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off",
+                               "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
+        L.orc_decode.argtypes = [i32, i64, vp, vp]
+        L.orc_gemm_float_elems.argtypes = [i32, i32, i32, i32, i64, i64, i64, vp, i64, vp, i64,
+                                           vp, i64, dbl, dbl, dbl, dbl, i64, vp, vp, vp, vp]
+        L.orc_gemm_float_full.argtypes = [i32, i32, i32, i32, i64, i64, i64, vp, i64, vp, i64,
+                                          vp, i64, dbl, dbl, dbl, dbl, vp, vp]
+        L.orc_gemm_i8_elems.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64,
+                                        i64, i64, i64, vp, vp, vp]
+        L.orc_gemm_i8_full.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64,
+                                       i64, i64, vp]
+        L.orc_compress24.argtypes = [i32, i64, i64, vp, i64, vp, i64, vp, i64]
+        L.orc_compress24.restype = i64
+        L.orc_decompress24.argtypes = [i32, i64, i64, vp, i64, vp, i64, vp, i64]
+        L.orc_max_threads.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _flat(a, dtype):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.dtype(dtype):
+        raise TypeError(f"expected {np.dtype(dtype)} array, got {a.dtype}")
+    return a
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
+
+
+def decode(dtype: str, codes) -> np.ndarray:
+    """Exact binary64 values of an array of raw codes of ``dtype``."""
+    c = _flat(codes, CODE_NP[dtype])
+    out = np.empty(c.shape, dtype=np.float64)
+    rc = lib().orc_decode(DTYPES[dtype], c.size, _ptr(c), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"orc_decode failed ({rc})")
+    return out
+
+
+def gemm_float(dtA, dtB, layA, layB, M, N, K, A, lda, B, ldb, C=None, ldc=None,
+               alpha=1.0, beta=0.0, sA=1.0, sB=1.0, rows=None, cols=None):
+    """Reference for the float paths.
+
+    A and B are flat (or any-shape, contiguous) arrays of raw codes addressed
+    through (layout, leading dimension) as described in oracle.c.  C is a
+    float32 array addressed as C[i*ldc + j].  With rows/cols given, only those
+    output elements are computed and 1-D arrays are returned; otherwise full
+    M x N arrays.  Returns (d_ref float32, abs_sum float64).
+    """
+    A = _flat(A, CODE_NP[dtA])
+    B = _flat(B, CODE_NP[dtB])
+    if beta != 0.0:
+        C = _flat(C, np.float32)
+    else:
+        C = None
+    ldc = N if ldc is None else ldc
+    L = lib()
+    if rows is None:
+        d = np.empty((M, N), np.float32)
+        s = np.empty((M, N), np.float64)
+        rc = L.orc_gemm_float_full(DTYPES[dtA], DTYPES[dtB], LAYOUTS[layA], LAYOUTS[layB],
+                                   M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
+                                   float(alpha), float(beta), float(sA), float(sB),
+                                   _ptr(d), _ptr(s))
+    else:
+        rows = _flat(np.asarray(rows, np.int64), np.int64)
+        cols = _flat(np.asarray(cols, np.int64), np.int64)
+        assert rows.shape == cols.shape
+        d = np.empty(rows.shape, np.float32)
+        s = np.empty(rows.shape, np.float64)
+        rc = L.orc_gemm_float_elems(DTYPES[dtA], DTYPES[dtB], LAYOUTS[layA], LAYOUTS[layB],
+                                    M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
+                                    float(alpha), float(beta), float(sA), float(sB),
+                                    rows.size, _ptr(rows), _ptr(cols), _ptr(d), _ptr(s))
+    if rc != 0:
+        raise ValueError(f"oracle float GEMM rejected its arguments ({rc})")
+    return d, s
+
+
+def gemm_i8(layA, layB, M, N, K, A, lda, B, ldb, C=None, ldc=None, alpha=1, beta=0,
+            rows=None, cols=None):
+    """Reference for int8 x int8 -> int32 (exact, wraps mod 2^32)."""
+    A = _flat(A, np.int8)
+    B = _flat(B, np.int8)
+    C = _flat(C, np.int32) if beta != 0 else None
+    ldc = N if ldc is None else ldc
+    L = lib()
+    if rows is None:
+        d = np.empty((M, N), np.int32)
+        rc = L.orc_gemm_i8_full(LAYOUTS[layA], LAYOUTS[layB], M, N, K, _ptr(A), lda,
+                                _ptr(B), ldb, _ptr(C), ldc, int(alpha), int(beta), _ptr(d))
+    else:
+        rows = _flat(np.asarray(rows, np.int64), np.int64)
+        cols = _flat(np.asarray(cols, np.int64), np.int64)
+        d = np.empty(rows.shape, np.int32)
+        rc = L.orc_gemm_i8_elems(LAYOUTS[layA], LAYOUTS[layB], M, N, K, _ptr(A), lda,
+                                 _ptr(B), ldb, _ptr(C), ldc, int(alpha), int(beta),
+                                 rows.size, _ptr(rows), _ptr(cols), _ptr(d))
+    if rc != 0:
+        raise ValueError(f"oracle int8 GEMM rejected its arguments ({rc})")
+    return d
+
+
+def compress24(dtype, A):
+    """2:4-compress a row-major M x K code array.  Returns (vals M x K/2,
+    idx M x ceil(K/32) uint32, number of groups with more than two non-zeros)."""
+    A = _flat(A, CODE_NP[dtype])
+    M, K = A.shape
+    vals = np.zeros((M, K // 2), CODE_NP[dtype])
+    idx = np.zeros((M, (K + 31) // 32), np.uint32)
+    n = lib().orc_compress24(DTYPES[dtype], M, K, _ptr(A), K, _ptr(vals), K // 2,
+                             _ptr(idx), idx.shape[1])
+    if n < 0:
+        raise ValueError(f"oracle compress24 rejected its arguments ({n})")
+    return vals, idx, int(n)
+
+
+def decompress24(dtype, vals, idx, K):
+    """Inverse of ``compress24``: a dense row-major M x K code array."""
+    vals = _flat(vals, CODE_NP[dtype])
+    idx = _flat(idx, np.uint32)
+    M = vals.shape[0]
+    A = np.zeros((M, K), CODE_NP[dtype])
+    rc = lib().orc_decompress24(DTYPES[dtype], M, K, _ptr(vals), vals.shape[1],
+                                _ptr(idx), idx.shape[1], _ptr(A), K)
+    if rc == -2:
+        raise ValueError("index code does not name two ascending positions")
+    if rc != 0:
+        raise ValueError(f"oracle decompress24 rejected its arguments ({rc})")
+    return A
+
+
+def gemm_sparse24(dtA, dtB, layB, M, N, K, vals, idx, B, ldb, C=None, ldc=None,
+                  alpha=1.0, beta=0.0, rows=None, cols=None):
+    """Sparse-A reference: decompress A, then the dense float GEMM with the
+    dense K (A row-major, i.e. K-contiguous)."""
+    A = decompress24(dtA, vals, idx, K)
+    return gemm_float(dtA, dtB, "k_contig", layB, M, N, K, A, K, B, ldb, C, ldc,
+                      alpha, beta, 1.0, 1.0, rows, cols)
+
+
+def float_bound(d_ref, abs_sum, K, alpha=1.0, sA=1.0, sB=1.0, beta=0.0, c=None):
+    """Per-element acceptance bound for float results (binary64)."""
+    bound = (4.0 * U * (K + 2) * abs(alpha * sA * sB)) * np.asarray(abs_sum, np.float64) \
+        + U * np.abs(np.asarray(d_ref, np.float64))
+    if beta not in (0.0, 1.0, -1.0) and c is not None:
+        bound = bound + U * np.abs(beta * np.asarray(c, np.float64))
+    return bound
+
+
+def check_float(d_gpu, d_ref, abs_sum, K, alpha=1.0, sA=1.0, sB=1.0, beta=0.0, c=None):
+    """Compare GPU float results with the oracle.  Returns a dict with ``ok``,
+    the number of violations (NaN counts as one), max |delta|/bound and the
+    first offending flat indices."""
+    g = np.asarray(d_gpu, np.float64).ravel()
+    r = np.asarray(d_ref, np.float64).ravel()
+    b = float_bound(d_ref, abs_sum, K, alpha, sA, sB, beta, c).ravel()
+    delta = np.abs(g - r)
+    bad = ~(delta <= b)  # NaN compares false, so it is flagged
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(b > 0, delta / np.where(b > 0, b, 1.0), np.where(delta > 0, np.inf, 0.0))
+    finite = ratio[np.isfinite(ratio)]
+    return {
+        "ok": not bool(bad.any()),
+        "violations": int(bad.sum()),
+        "max_ratio": float(finite.max()) if finite.size else (float("inf") if bad.any() else 0.0),
+        "first_bad": np.flatnonzero(bad)[:8].tolist(),
+        "n": int(g.size),
+    }
+
+
+def check_exact(d_gpu, d_ref):
+    """Bit-exact comparison (integers, indices, raw codes)."""
+    g = np.asarray(d_gpu).ravel()
+    r = np.asarray(d_ref).ravel()
+    bad = g != r
+    return {"ok": not bool(bad.any()), "violations": int(bad.sum()),
+            "first_bad": np.flatnonzero(bad)[:8].tolist(), "n": int(g.size)}
