@@ -1,0 +1,209 @@
+"""Benchmark of the matrix-core GEMM hot path on one MI355X.
+
+One timed step is one pass over every entry point of the hot path on its
+full-size synthetic workload (8192^3 for every GEMM):
+  gemm_dense  bf16 x bf16 -> f32   (A row-major, B column-major, C ~ N(0,1), alpha = beta = 1)
+  gemm_dense  f16  x f16  -> f32   (same recipe)
+  gemm_dense  i8   x i8   -> i32   (C uniform int in [-2^20, 2^20], alpha = beta = 1)
+  gemm_dense  e4m3 x e4m3 -> f32   (per-tensor scales, C = 0)
+  gemm_dense  e4m3 x e5m2 -> f32   (per-tensor scales, C = 0)
+  compress24  bf16 8192 x 8192     (2:4 compressor)
+  gemm_sparse24 bf16 (2:4 A) x bf16 -> f32
+Each call is bracketed by HIP events on the stream it is launched on, so every
+kernel's average duration is measured live.  `value` is the dense bf16 8192^3
+rate (TFLOP/s); the per-dtype rates the metric asks for are in `per_dtype`.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s (TOPS int8) at 8192³ per dtype + % of MI355X MFMA peak"
+# MI355X published dense peaks (TFLOP/s or TOPS) and HBM bandwidth (GB/s)
+PEAK = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "i8": 5000.0}
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--size", type=int, default=8192)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", default="", help="comma list of entries to run (profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import matrix_core_gemm_amd as mcg
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    n = args.size
+    M = N = K = n
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+    t0 = time.time()
+    log(f"generating inputs (n = {n}) ...")
+    ops = {}
+    for dt in ("bf16", "f16"):
+        A = W.operand("A", dt, M, K, "normal", "k_contig")
+        B = W.operand("B", dt, K, N, "normal", "k_contig")
+        ops[dt] = (dev(A.codes), A.ld, dev(B.codes), B.ld, 1.0, 1.0)
+        if dt == "bf16":
+            host_bf16 = (A, B)
+    C = dev(W.c_matrix(M, N, "normal"))
+    Ci = dev(W.c_matrix(M, N, "int20"))
+    A = W.operand("A", "i8", M, K, "int8", "k_contig")
+    B = W.operand("B", "i8", K, N, "int8", "k_contig")
+    ops["i8"] = (dev(A.codes), A.ld, dev(B.codes), B.ld, 1.0, 1.0)
+    A8 = W.operand("A", "e4m3", M, K, "normal", "k_contig", fp8_scaled=True)
+    B8 = W.operand("B", "e4m3", K, N, "normal", "k_contig", fp8_scaled=True)
+    B85 = W.operand("B", "e5m2", K, N, "normal", "k_contig", fp8_scaled=True)
+    dA8 = dev(A8.codes)
+    ops["e4m3xe4m3"] = (dA8, A8.ld, dev(B8.codes), B8.ld, A8.scale, B8.scale)
+    ops["e4m3xe5m2"] = (dA8, A8.ld, dev(B85.codes), B85.ld, A8.scale, B85.scale)
+    As = dev(W.sparse24_dense("bf16", M, K))
+    Bs = ops["bf16"][2]
+    vals = torch.empty((M, K // 2), dtype=torch.int16, device="cuda")
+    idx = torch.empty((M, (K + 31) // 32), dtype=torch.int32, device="cuda")
+    D = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    Di = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+
+    stream = torch.cuda.Stream()
+    s = stream.cuda_stream
+
+    def call(name):
+        if name in ("bf16", "f16"):
+            a, lda, b, ldb, sa, sb = ops[name]
+            mcg.gemm_dense(name, name, 0, 0, M, N, K, a, lda, b, ldb, C, D, N, "f32", 1.0, 1.0,
+                           stream=s)
+        elif name == "i8":
+            a, lda, b, ldb, sa, sb = ops[name]
+            mcg.gemm_dense("i8", "i8", 0, 0, M, N, K, a, lda, b, ldb, Ci, Di, N, "i32", 1, 1, stream=s)
+        elif name.startswith("e4m3x"):
+            a, lda, b, ldb, sa, sb = ops[name]
+            mcg.gemm_dense("e4m3", name.split("x")[1], 0, 0, M, N, K, a, lda, b, ldb, None, D, N, "f32",
+                           1.0, 0.0, sa, sb, stream=s)
+        elif name == "compress24":
+            mcg.compress24("bf16", M, K, As, K, vals, K // 2, idx, idx.shape[1], None, stream=s)
+        elif name == "sparse24":
+            mcg.gemm_sparse24("bf16", "bf16", 0, M, N, K, vals, K // 2, idx, idx.shape[1], Bs, K, None,
+                              D, N, "f32", 1.0, 0.0, stream=s)
+
+    names = ["bf16", "f16", "i8", "e4m3xe4m3", "e4m3xe5m2", "compress24", "sparse24"]
+    if args.only:
+        keep = set(args.only.split(","))
+        names = [x for x in names if x in keep or x == "compress24" and "sparse24" in keep]
+    ev = {x: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for x in names}
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            for x in names:
+                call(x)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for step in range(args.steps):
+            for x in names:
+                ev[x][step][0].record(stream)
+                call(x)
+                ev[x][step][1].record(stream)
+        torch.cuda.synchronize()
+        t_end = time.perf_counter()
+
+    ms = {x: float(np.mean([a.elapsed_time(b) for a, b in ev[x]])) for x in names}
+    flops = 2.0 * M * N * K
+    per = {}
+    for x in names:
+        t = ms[x] * 1e-3
+        if x == "compress24":
+            nbytes = M * K * 2 + M * K // 2 * 2 + M * ((K + 31) // 32) * 4
+            per[x] = {"GB/s": nbytes / t / 1e9, "ms": ms[x], "frac_of_hbm_peak": nbytes / t / 1e9 / HBM_PEAK_GBS,
+                      "bytes": nbytes}
+        elif x == "sparse24":
+            tf = flops / t / 1e12
+            per[x] = {"TFLOP/s_dense_equiv": tf, "TFLOP/s_algorithmic": tf / 2, "ms": ms[x],
+                      "frac_of_dense_bf16_peak": tf / PEAK["bf16"],
+                      "vs_dense_bf16": tf / (flops / (ms["bf16"] * 1e-3) / 1e12) if "bf16" in ms else None}
+        else:
+            pk = PEAK["fp8"] if x.startswith("e4m3") else PEAK[x]
+            tf = flops / t / 1e12
+            per[x] = {("TOPS" if x == "i8" else "TFLOP/s"): tf, "ms": ms[x], "peak": pk, "frac_of_peak": tf / pk}
+    head = "bf16" if "bf16" in names else names[0]
+    value = flops / (ms[head] * 1e-3) / 1e12 if head != "compress24" else per[head]["GB/s"]
+
+    # CPU oracle baseline: whole rows of D of the bf16 workload, timed on the host cores
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        A, B = host_bf16
+        nthr = oracle.max_threads()
+        t1 = time.perf_counter()
+        rows, cols = np.zeros(N, np.int64), np.arange(N, dtype=np.int64)
+        oracle.gemm_float("bf16", "bf16", "k_contig", "k_contig", M, N, K, A.codes, A.ld, B.codes,
+                          B.ld, rows=rows, cols=cols)
+        one = time.perf_counter() - t1
+        nrows = max(1, min(M, int(args.cpu_seconds / max(one, 1e-6))))
+        rr = np.repeat(np.arange(nrows, dtype=np.int64) * (M // nrows), N)
+        cc = np.tile(np.arange(N, dtype=np.int64), nrows)
+        t1 = time.perf_counter()
+        oracle.gemm_float("bf16", "bf16", "k_contig", "k_contig", M, N, K, A.codes, A.ld, B.codes,
+                          B.ld, rows=rr, cols=cc)
+        tcpu = time.perf_counter() - t1
+        cpu = {"value": 2.0 * nrows * N * K / tcpu / 1e12, "unit": "TFLOP/s", "cores": nthr,
+               "kind": "oracle",
+               "sample": f"{nrows} whole rows ({nrows * N} outputs, K={K}) of the dense bf16 {n}^3 "
+                         f"workload; {tcpu:.1f} s on {nthr} threads ({platform.processor() or 'host'})"}
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": (t_end - t_start) * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"dense bf16 GEMM {n}x{n}x{n}, A row-major, B column-major, "
+                               f"C ~ N(0,1) fp32, alpha=beta=1, fp32 out; step = all "
+                               f"{len(names)} hot-path calls at {n}^3",
+                   "M": M, "N": N, "K": K, "entries": names},
+        "roofline": {"bound": "mfma", "achieved": value, "peak": PEAK["bf16"], "unit": "TFLOP/s",
+                     "frac": value / PEAK["bf16"], "traffic": None,
+                     "kernel": "gemm_dense_kernel (bf16)", "kernel_ms": ms.get(head)},
+        "cpu_baseline": cpu,
+        "per_dtype": per,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

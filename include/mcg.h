@@ -1,0 +1,196 @@
+/*
+ * mcg.h -- C ABI of the MI355X (gfx950, CDNA4) matrix-core GEMM library.
+ *
+ * The library multiplies matrices with the wavefront-level matrix fused
+ * multiply-add instructions (MFMA, and the 2:4-sparse SMFMAC) of gfx950:
+ *
+ *     D = alpha * scaleA * scaleB * (A . B) + beta * C
+ *
+ * The operation is the matrix fused multiply-add D = A B + C of "Accurate
+ * Models of AMD Matrix Cores" (Section 2, Notations and Definitions, Eq. (1)),
+ * with BLAS-style alpha/beta and per-tensor fp8 dequantisation scales.  One
+ * MFMA instruction computes one K-step of a small tile; the library tiles and
+ * loops over K ("CDNA3 dense MFMA builtins", Naming convention; Using MFMA
+ * builtins as a compute policy).  The sparse variant takes A in the 2:4
+ * compressed form of "RDNA4 sparse WMMA builtins" (Structured sparsity (2:4
+ * pattern); Common parameters, index), with the compressed values and the
+ * index stored separately (Using sparse WMMA builtins as a compute policy).
+ *
+ * Conventions common to every entry point
+ *  - Pointers named A, B, C, D, A_compressed, A_index, d_violations are
+ *    DEVICE pointers (gfx950 global memory) owned by the caller.  The library
+ *    keeps no state, allocates no device memory and never frees caller memory.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is
+ *    the null stream) and return as soon as the work is enqueued.
+ *  - Leading dimensions are in ELEMENTS.  Sizes are int64.
+ *  - Return value: 0 (MCG_SUCCESS) or a positive mcg_status.  Argument errors
+ *    are found on the host before anything is launched; then nothing is read
+ *    or written.  The library never aborts and never throws.
+ *  - Only gfx950 devices are supported (MCG_ERR_UNSUPPORTED_ARCH otherwise).
+ *  - Thread-safe: no global mutable state beyond a per-device arch check.
+ */
+#ifndef MCG_H
+#define MCG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  Float formats are decoded as in "Accurate Models of AMD
+ * Matrix Cores", Table 1: bfloat16, binary16, fp8 E4M3 and fp8 E5M2 in their
+ * OCP encodings (E4M3: bias 7, no infinities, largest 448; E5M2: bias 15,
+ * largest 57344).  MCG_I8 is signed ("CDNA3 dense MFMA builtins",
+ * INT32-accumulate builtins). */
+typedef enum {
+    MCG_BF16 = 0,
+    MCG_F16 = 1,
+    MCG_I8 = 2,
+    MCG_FP8_E4M3 = 3,
+    MCG_FP8_E5M2 = 4,
+    MCG_F32 = 5,
+    MCG_I32 = 6
+} mcg_dtype;
+
+/* Storage order of the operands.  A is logically M x K, B is K x N.
+ *   MCG_K_CONTIG : A row-major    (A[i*lda + k], lda >= K)
+ *                  B column-major (B[j*ldb + k], ldb >= K)
+ *   MCG_MN_CONTIG: A column-major (A[k*lda + i], lda >= M)
+ *                  B row-major    (B[k*ldb + j], ldb >= N)
+ * C and D are always row-major M x N (C[i*ldc + j], ldc >= N). */
+typedef enum {
+    MCG_K_CONTIG = 0,
+    MCG_MN_CONTIG = 1
+} mcg_layout;
+
+typedef enum {
+    MCG_SUCCESS = 0,
+    MCG_ERR_NULL_POINTER = 1,      /* a required pointer is NULL                     */
+    MCG_ERR_INVALID_SIZE = 2,      /* negative size, or K % 4 != 0 for 2:4           */
+    MCG_ERR_INVALID_LD = 3,        /* a leading dimension below its minimum          */
+    MCG_ERR_UNSUPPORTED_DTYPE = 4, /* dtype/layout combination not provided          */
+    MCG_ERR_MISALIGNED = 5,        /* pointer/ld alignment the entry point requires  */
+    MCG_ERR_NOT_2_4_SPARSE = 6,    /* a group of four holds more than two non-zeros  */
+    MCG_ERR_INVALID_INDEX = 7,     /* reserved: malformed 2:4 index word             */
+    MCG_ERR_UNSUPPORTED_ARCH = 8,  /* current device is not gfx950                   */
+    MCG_ERR_HIP = 9,               /* a HIP runtime call failed                      */
+    MCG_ERR_INVALID_VALUE = 10     /* alpha/beta/scale not usable for this dtype     */
+} mcg_status;
+
+/*
+ * gemm_dense -- D = alpha*scaleA*scaleB*(A.B) + beta*C on MFMA.
+ *
+ * dtypeA/dtypeB : supported pairs are BF16xBF16, F16xF16, I8xI8 and any pair
+ *                 of FP8_E4M3/FP8_E5M2.
+ * layoutA/B     : mcg_layout (all four combinations for every pair).
+ * M, N, K       : any sizes >= 0.  M == 0 or N == 0 is a no-op.  K == 0 gives
+ *                 D = beta*C.  Ragged edges are handled inside the kernels.
+ * A, lda        : logical M x K in layoutA; lda >= K (K_CONTIG) or >= M.
+ * B, ldb        : logical K x N in layoutB; ldb >= K (K_CONTIG) or >= N.
+ * C             : row-major M x N of dtypeD, read only when beta != 0 (may be
+ *                 NULL then).  D: row-major M x N of dtypeD; D may alias C
+ *                 exactly (same pointer); other overlaps are undefined.
+ * ldc           : leading dimension of both C and D, ldc >= N.
+ * dtypeD        : MCG_F32 for float inputs (fp32 accumulation), MCG_I32 for
+ *                 int8 (exact int32 accumulation, wrapping mod 2^32).
+ * alpha, beta   : float paths use them as fp32.  The int8 path requires
+ *                 integral values in int32 range and computes
+ *                 alpha*acc + beta*C in wrapping int32 arithmetic.
+ * scaleA/scaleB : per-tensor dequantisation scales of fp8 operands (real
+ *                 value = scale * decoded code), folded into the epilogue as
+ *                 fp32 alpha*scaleA*scaleB.  Must be 1.0f for non-fp8 inputs.
+ * stream        : hipStream_t or NULL.
+ * Accuracy      : float results are the fp32 result of a non-IEEE matrix-core
+ *                 accumulation, not bit-reproducible across architectures
+ *                 ("Accurate Models of AMD Matrix Cores", Abstract); int8
+ *                 results are exact.
+ * Alignment     : none required; 16-byte aligned pointers and leading
+ *                 dimensions whose byte size is a multiple of 16 take the
+ *                 vector-load path, anything else a slower element path.
+ */
+int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB,
+               int64_t M, int64_t N, int64_t K,
+               const void* A, int64_t lda, const void* B, int64_t ldb,
+               const void* C, void* D, int64_t ldc, int dtypeD,
+               double alpha, double beta, float scaleA, float scaleB, void* stream);
+
+/*
+ * gemm_sparse24 -- D = alpha*(A.B) + beta*C with A given in 2:4 compressed
+ * form and multiplied on the sparse matrix cores (SMFMAC).
+ *
+ * dtypeA/dtypeB : MCG_BF16 x MCG_BF16 or MCG_F16 x MCG_F16; dtypeD = MCG_F32.
+ * layoutB       : mcg_layout of B (A is always the compressed row-major form).
+ * K             : the DENSE K; K % 4 == 0.
+ * A_compressed  : M x K/2 values, row-major, lda_c >= K/2.  Row i holds, for
+ *                 each group g of four along K, the two kept values of that
+ *                 group in ascending position order.
+ * A_index       : M x ceil(K/32) uint32 words, row-major, ld_idx >=
+ *                 ceil(K/32).  Group g of row i has the 4-bit code
+ *                 p0 | (p1 << 2) (positions 0..3 of its two kept values,
+ *                 p0 < p1) at bits 4*(g % 8) of word g/8; unused trailing
+ *                 codes are zero.  This is the canonical layout produced by
+ *                 compress24 / compress24_host; kernels re-pack it per lane.
+ *                 Codes with p0 >= p1 give undefined results.
+ * B, ldb, C, D, ldc, alpha, beta, stream: as for gemm_dense.
+ */
+int gemm_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int64_t K,
+                  const void* A_compressed, int64_t lda_c,
+                  const uint32_t* A_index, int64_t ld_idx,
+                  const void* B, int64_t ldb, const void* C, void* D, int64_t ldc,
+                  int dtypeD, double alpha, double beta, void* stream);
+
+/*
+ * compress24 -- 2:4 compressor on the device ("RDNA4 sparse WMMA builtins",
+ * Structured sparsity (2:4 pattern): walk K in groups of four and keep the
+ * two non-zero positions).
+ *
+ * dtype         : MCG_BF16, MCG_F16, MCG_I8, MCG_FP8_E4M3 or MCG_FP8_E5M2.
+ * A, lda        : dense row-major M x K, lda >= K, K % 4 == 0.
+ * A_compressed, lda_c, A_index, ld_idx: outputs in the layout described at
+ *                 gemm_sparse24.  A group with fewer than two non-zeros keeps
+ *                 the lowest unused positions; +0 and -0 count as zero and NaN
+ *                 as non-zero.  A group with more than two non-zeros is
+ *                 written as two zeros with code p0=0, p1=1.
+ * d_violations  : optional device int32; if not NULL it is set to the number
+ *                 of groups with more than two non-zeros (the library zeroes
+ *                 it first, in stream order).
+ */
+int compress24(int dtype, int64_t M, int64_t K, const void* A, int64_t lda,
+               void* A_compressed, int64_t lda_c, uint32_t* A_index, int64_t ld_idx,
+               int32_t* d_violations, void* stream);
+
+/*
+ * compress24_host -- the same compressor for HOST pointers, synchronous, for
+ * preparing weights offline.  Returns MCG_ERR_NOT_2_4_SPARSE if any group
+ * held more than two non-zeros (outputs are still fully written).
+ */
+int compress24_host(int dtype, int64_t M, int64_t K, const void* A, int64_t lda,
+                    void* A_compressed, int64_t lda_c, uint32_t* A_index, int64_t ld_idx);
+
+/* Host-only argument checks: the exact validation the entry points above run
+ * before touching the device (same arguments, minus outputs' contents and the
+ * stream).  They never call HIP and return an mcg_status. */
+int mcg_validate_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int64_t N,
+                       int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                       const void* C, const void* D, int64_t ldc, int dtypeD, double alpha,
+                       double beta, float scaleA, float scaleB);
+int mcg_validate_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int64_t K,
+                          const void* A_compressed, int64_t lda_c, const uint32_t* A_index,
+                          int64_t ld_idx, const void* B, int64_t ldb, const void* C, const void* D,
+                          int64_t ldc, int dtypeD, double alpha, double beta);
+int mcg_validate_compress24(int dtype, int64_t M, int64_t K, const void* A, int64_t lda,
+                            const void* A_compressed, int64_t lda_c, const uint32_t* A_index,
+                            int64_t ld_idx);
+
+/* Human-readable name of an mcg_status value (static storage). */
+const char* mcg_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mcg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MCG_H */

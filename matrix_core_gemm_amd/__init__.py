@@ -1,0 +1,160 @@
+"""Python binding of the gfx950 matrix-core GEMM library (include/mcg.h).
+
+Argument marshalling only: every function has the C entry point's name and
+argument order, turns torch tensors into device pointers, defaults the stream
+to torch's current stream, and raises ``MCGError`` on a non-zero status.  All
+arithmetic runs in the HIP kernels of ``_libmcg.so``; there is no fallback.
+If the library has not been built, importing this package fails.
+
+dtype and layout arguments take the C enum values or their names:
+  dtypes : "bf16", "f16", "i8", "e4m3", "e5m2", "f32", "i32"
+  layouts: "k_contig" (A row-major / B column-major),
+           "mn_contig" (A column-major / B row-major)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first so the library binds to torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_libmcg.so")
+
+DTYPES = {"bf16": 0, "f16": 1, "i8": 2, "e4m3": 3, "e5m2": 4, "f32": 5, "i32": 6}
+LAYOUTS = {"k_contig": 0, "mn_contig": 1}
+STATUS = {0: "MCG_SUCCESS", 1: "MCG_ERR_NULL_POINTER", 2: "MCG_ERR_INVALID_SIZE",
+          3: "MCG_ERR_INVALID_LD", 4: "MCG_ERR_UNSUPPORTED_DTYPE", 5: "MCG_ERR_MISALIGNED",
+          6: "MCG_ERR_NOT_2_4_SPARSE", 7: "MCG_ERR_INVALID_INDEX", 8: "MCG_ERR_UNSUPPORTED_ARCH",
+          9: "MCG_ERR_HIP", 10: "MCG_ERR_INVALID_VALUE"}
+
+# Every symbol include/mcg.h declares.
+EXPORTS = ("gemm_dense", "gemm_sparse24", "compress24", "compress24_host", "mcg_status_string",
+           "mcg_version", "mcg_validate_dense", "mcg_validate_sparse24", "mcg_validate_compress24")
+
+
+class MCGError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = _lib.mcg_status_string(status).decode() if _lib is not None else ""
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({msg})")
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with matrix_core_gemm_amd.build.build() "
+                      "(or __graft_entry__.build()); there is no non-GPU fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i32, _i64, _dbl, _f32, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_float, ctypes.c_void_p
+_lib.gemm_dense.argtypes = [_i32, _i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
+                            _vp, _vp, _i64, _i32, _dbl, _dbl, _f32, _f32, _vp]
+_lib.gemm_sparse24.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                               _vp, _vp, _i64, _i32, _dbl, _dbl, _vp]
+_lib.compress24.argtypes = [_i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp]
+_lib.compress24_host.argtypes = [_i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
+_lib.mcg_status_string.argtypes = [_i32]
+_lib.mcg_status_string.restype = ctypes.c_char_p
+_lib.mcg_version.argtypes = []
+_lib.mcg_validate_dense.argtypes = [_i32, _i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
+                                    _vp, _vp, _i64, _i32, _dbl, _dbl, _f32, _f32]
+_lib.mcg_validate_sparse24.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
+                                       _vp, _i64, _vp, _vp, _i64, _i32, _dbl, _dbl]
+_lib.mcg_validate_compress24.argtypes = [_i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
+
+
+def lib():
+    """The loaded ctypes library."""
+    return _lib
+
+
+def _dt(x) -> int:
+    return DTYPES[x] if isinstance(x, str) else int(x)
+
+
+def _lay(x) -> int:
+    return LAYOUTS[x] if isinstance(x, str) else int(x)
+
+
+def _ptr(t):
+    """Device (or host) address of a tensor, an int address, or None."""
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        return t.data_ptr()
+    if hasattr(t, "ctypes"):  # numpy array (host entry points only)
+        return t.ctypes.data
+    return int(t)
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MCGError(fn, status)
+
+
+def gemm_dense(dtypeA, dtypeB, layoutA, layoutB, M, N, K, A, lda, B, ldb, C, D, ldc, dtypeD,
+               alpha=1.0, beta=0.0, scaleA=1.0, scaleB=1.0, stream=None) -> None:
+    _check("gemm_dense", _lib.gemm_dense(
+        _dt(dtypeA), _dt(dtypeB), _lay(layoutA), _lay(layoutB), M, N, K, _ptr(A), lda, _ptr(B), ldb,
+        _ptr(C), _ptr(D), ldc, _dt(dtypeD), float(alpha), float(beta), float(scaleA), float(scaleB),
+        _stream(stream)))
+
+
+def gemm_sparse24(dtypeA, dtypeB, layoutB, M, N, K, A_compressed, lda_c, A_index, ld_idx, B, ldb,
+                  C, D, ldc, dtypeD, alpha=1.0, beta=0.0, stream=None) -> None:
+    _check("gemm_sparse24", _lib.gemm_sparse24(
+        _dt(dtypeA), _dt(dtypeB), _lay(layoutB), M, N, K, _ptr(A_compressed), lda_c, _ptr(A_index),
+        ld_idx, _ptr(B), ldb, _ptr(C), _ptr(D), ldc, _dt(dtypeD), float(alpha), float(beta),
+        _stream(stream)))
+
+
+def compress24(dtype, M, K, A, lda, A_compressed, lda_c, A_index, ld_idx, d_violations=None,
+               stream=None) -> None:
+    _check("compress24", _lib.compress24(
+        _dt(dtype), M, K, _ptr(A), lda, _ptr(A_compressed), lda_c, _ptr(A_index), ld_idx,
+        _ptr(d_violations), _stream(stream)))
+
+
+def compress24_host(dtype, M, K, A, lda, A_compressed, lda_c, A_index, ld_idx) -> int:
+    """Host compressor; returns the status (0, or MCG_ERR_NOT_2_4_SPARSE = 6)
+    and raises on any other error."""
+    st = _lib.compress24_host(_dt(dtype), M, K, _ptr(A), lda, _ptr(A_compressed), lda_c,
+                              _ptr(A_index), ld_idx)
+    if st not in (0, 6):
+        raise MCGError("compress24_host", st)
+    return st
+
+
+def validate_dense(dtypeA, dtypeB, layoutA, layoutB, M, N, K, A, lda, B, ldb, C, D, ldc, dtypeD,
+                   alpha=1.0, beta=0.0, scaleA=1.0, scaleB=1.0) -> int:
+    return _lib.mcg_validate_dense(_dt(dtypeA), _dt(dtypeB), _lay(layoutA), _lay(layoutB), M, N, K,
+                                   _ptr(A), lda, _ptr(B), ldb, _ptr(C), _ptr(D), ldc, _dt(dtypeD),
+                                   float(alpha), float(beta), float(scaleA), float(scaleB))
+
+
+def validate_sparse24(dtypeA, dtypeB, layoutB, M, N, K, A_compressed, lda_c, A_index, ld_idx, B,
+                      ldb, C, D, ldc, dtypeD, alpha=1.0, beta=0.0) -> int:
+    return _lib.mcg_validate_sparse24(_dt(dtypeA), _dt(dtypeB), _lay(layoutB), M, N, K,
+                                      _ptr(A_compressed), lda_c, _ptr(A_index), ld_idx, _ptr(B),
+                                      ldb, _ptr(C), _ptr(D), ldc, _dt(dtypeD), float(alpha),
+                                      float(beta))
+
+
+def validate_compress24(dtype, M, K, A, lda, A_compressed, lda_c, A_index, ld_idx) -> int:
+    return _lib.mcg_validate_compress24(_dt(dtype), M, K, _ptr(A), lda, _ptr(A_compressed), lda_c,
+                                        _ptr(A_index), ld_idx)
+
+
+def status_string(status: int) -> str:
+    return _lib.mcg_status_string(status).decode()
+
+
+def version() -> int:
+    return _lib.mcg_version()

@@ -1,0 +1,277 @@
+// api.cpp -- the C ABI declared in include/mcg.h: argument validation (pure host code,
+// no HIP call before it has passed), the gfx950 check, and dispatch to the kernels.
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/mcg.h"
+#include "gemm_kernels.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool is_float8(int dt) { return dt == MCG_FP8_E4M3 || dt == MCG_FP8_E5M2; }
+bool is_in_dtype(int dt) { return dt >= MCG_BF16 && dt <= MCG_FP8_E5M2; }
+int elem_bytes(int dt) {
+  switch (dt) {
+    case MCG_BF16:
+    case MCG_F16: return 2;
+    case MCG_I8:
+    case MCG_FP8_E4M3:
+    case MCG_FP8_E5M2: return 1;
+    case MCG_F32:
+    case MCG_I32: return 4;
+    default: return 0;
+  }
+}
+bool aligned_to(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+bool valid_layout(int l) { return l == MCG_K_CONTIG || l == MCG_MN_CONTIG; }
+bool int32_integral(double v) {
+  return std::isfinite(v) && v == std::floor(v) && v >= -2147483648.0 && v <= 2147483647.0;
+}
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+std::atomic<int> g_arch_state[64];
+
+int check_arch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MCG_ERR_HIP;
+  if (dev < 0 || dev >= 64) return MCG_ERR_UNSUPPORTED_ARCH;
+  int st = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MCG_ERR_HIP;
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? MCG_SUCCESS : MCG_ERR_UNSUPPORTED_ARCH;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MCG_SUCCESS : MCG_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+// Validation of gemm_dense arguments; touches no device state.
+int mcg_validate_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int64_t N,
+                       int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                       const void* C, const void* D, int64_t ldc, int dtypeD, double alpha,
+                       double beta, float scaleA, float scaleB) {
+  if (!is_in_dtype(dtypeA) || !is_in_dtype(dtypeB)) return MCG_ERR_UNSUPPORTED_DTYPE;
+  const bool f8 = is_float8(dtypeA) && is_float8(dtypeB);
+  if (!f8 && dtypeA != dtypeB) return MCG_ERR_UNSUPPORTED_DTYPE;
+  if (is_float8(dtypeA) != is_float8(dtypeB)) return MCG_ERR_UNSUPPORTED_DTYPE;
+  const bool i8 = dtypeA == MCG_I8;
+  if (dtypeD != (i8 ? MCG_I32 : MCG_F32)) return MCG_ERR_UNSUPPORTED_DTYPE;
+  if (!valid_layout(layoutA) || !valid_layout(layoutB)) return MCG_ERR_UNSUPPORTED_DTYPE;
+  if (M < 0 || N < 0 || K < 0) return MCG_ERR_INVALID_SIZE;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return MCG_ERR_INVALID_SIZE;
+  if (M == 0 || N == 0) return MCG_SUCCESS;
+  if (!D) return MCG_ERR_NULL_POINTER;
+  if (K > 0 && (!A || !B)) return MCG_ERR_NULL_POINTER;
+  if (beta != 0.0 && !C) return MCG_ERR_NULL_POINTER;
+  const int64_t min_lda = layoutA == MCG_K_CONTIG ? K : M;
+  const int64_t min_ldb = layoutB == MCG_K_CONTIG ? K : N;
+  if (lda < (min_lda > 1 ? min_lda : 1) || ldb < (min_ldb > 1 ? min_ldb : 1) || ldc < N)
+    return MCG_ERR_INVALID_LD;
+  if (!aligned_to(A, elem_bytes(dtypeA)) || !aligned_to(B, elem_bytes(dtypeB)) ||
+      !aligned_to(D, 4) || (C && !aligned_to(C, 4)))
+    return MCG_ERR_MISALIGNED;
+  if (i8) {
+    if (!int32_integral(alpha) || !int32_integral(beta)) return MCG_ERR_INVALID_VALUE;
+  } else if (!std::isfinite(alpha) || !std::isfinite(beta)) {
+    return MCG_ERR_INVALID_VALUE;
+  }
+  if (!f8 && (scaleA != 1.0f || scaleB != 1.0f)) return MCG_ERR_INVALID_VALUE;
+  if (f8 && (!std::isfinite(scaleA) || !std::isfinite(scaleB))) return MCG_ERR_INVALID_VALUE;
+  return MCG_SUCCESS;
+}
+
+int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
+               const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, void* D,
+               int64_t ldc, int dtypeD, double alpha, double beta, float scaleA, float scaleB,
+               void* stream) {
+  int st = mcg_validate_dense(dtypeA, dtypeB, layoutA, layoutB, M, N, K, A, lda, B, ldb, C, D, ldc,
+                              dtypeD, alpha, beta, scaleA, scaleB);
+  if (st != MCG_SUCCESS || M == 0 || N == 0) return st;
+  st = check_arch();
+  if (st != MCG_SUCCESS) return st;
+
+  const int eb = elem_bytes(dtypeA);
+  mcg::DenseArgs a{};
+  a.A = (const char*)A;
+  a.B = (const char*)B;
+  a.C = C;
+  a.D = D;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.alpha = (float)(alpha * (double)scaleA * (double)scaleB);
+  a.beta = (float)beta;
+  a.alpha_i = dtypeA == MCG_I8 ? (int)alpha : 0;
+  a.beta_i = dtypeA == MCG_I8 ? (int)beta : 0;
+  a.use_c = beta != 0.0;
+  a.vec_cd = aligned_to(D, 16) && (!a.use_c || aligned_to(C, 16)) && ldc % 4 == 0;
+  const bool aligned = K == 0 || (aligned_to(A, 16) && aligned_to(B, 16) && (lda * eb) % 16 == 0 &&
+                                  (ldb * eb) % 16 == 0);
+  return hip_status(mcg::launch_dense(dtypeA, dtypeB, layoutA, layoutB, aligned, a, (hipStream_t)stream));
+}
+
+int mcg_validate_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int64_t K,
+                          const void* A_compressed, int64_t lda_c, const uint32_t* A_index,
+                          int64_t ld_idx, const void* B, int64_t ldb, const void* C, const void* D,
+                          int64_t ldc, int dtypeD, double alpha, double beta) {
+  if (!((dtypeA == MCG_BF16 && dtypeB == MCG_BF16) || (dtypeA == MCG_F16 && dtypeB == MCG_F16)))
+    return MCG_ERR_UNSUPPORTED_DTYPE;
+  if (dtypeD != MCG_F32 || !valid_layout(layoutB)) return MCG_ERR_UNSUPPORTED_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || K % 4 != 0) return MCG_ERR_INVALID_SIZE;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return MCG_ERR_INVALID_SIZE;
+  if (M == 0 || N == 0) return MCG_SUCCESS;
+  if (!D) return MCG_ERR_NULL_POINTER;
+  if (K > 0 && (!A_compressed || !A_index || !B)) return MCG_ERR_NULL_POINTER;
+  if (beta != 0.0 && !C) return MCG_ERR_NULL_POINTER;
+  const int64_t min_ldb = layoutB == MCG_K_CONTIG ? K : N;
+  if (lda_c < (K / 2 > 1 ? K / 2 : 1) || ld_idx < ((K + 31) / 32 > 1 ? (K + 31) / 32 : 1) ||
+      ldb < (min_ldb > 1 ? min_ldb : 1) || ldc < N)
+    return MCG_ERR_INVALID_LD;
+  if (!aligned_to(A_compressed, 2) || !aligned_to(B, 2) || !aligned_to(A_index, 4) ||
+      !aligned_to(D, 4) || (C && !aligned_to(C, 4)))
+    return MCG_ERR_MISALIGNED;
+  if (!std::isfinite(alpha) || !std::isfinite(beta)) return MCG_ERR_INVALID_VALUE;
+  return MCG_SUCCESS;
+}
+
+int gemm_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int64_t K,
+                  const void* A_compressed, int64_t lda_c, const uint32_t* A_index, int64_t ld_idx,
+                  const void* B, int64_t ldb, const void* C, void* D, int64_t ldc, int dtypeD,
+                  double alpha, double beta, void* stream) {
+  int st = mcg_validate_sparse24(dtypeA, dtypeB, layoutB, M, N, K, A_compressed, lda_c, A_index,
+                                 ld_idx, B, ldb, C, D, ldc, dtypeD, alpha, beta);
+  if (st != MCG_SUCCESS || M == 0 || N == 0) return st;
+  st = check_arch();
+  if (st != MCG_SUCCESS) return st;
+  mcg::SparseArgs a{};
+  a.Ac = (const char*)A_compressed;
+  a.idx = A_index;
+  a.B = (const char*)B;
+  a.C = C;
+  a.D = D;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.lda_c = lda_c;
+  a.ld_idx = ld_idx;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.alpha = (float)alpha;
+  a.beta = (float)beta;
+  a.use_c = beta != 0.0;
+  a.vec_cd = aligned_to(D, 16) && (!a.use_c || aligned_to(C, 16)) && ldc % 4 == 0;
+  const bool aligned = K == 0 || (aligned_to(A_compressed, 16) && aligned_to(B, 16) &&
+                                  aligned_to(A_index, 16) && (lda_c * 2) % 16 == 0 &&
+                                  (ldb * 2) % 16 == 0 && (ld_idx * 4) % 16 == 0);
+  return hip_status(mcg::launch_sparse(dtypeA, layoutB, aligned, a, (hipStream_t)stream));
+}
+
+int mcg_validate_compress24(int dtype, int64_t M, int64_t K, const void* A, int64_t lda,
+                            const void* A_compressed, int64_t lda_c, const uint32_t* A_index,
+                            int64_t ld_idx) {
+  if (!is_in_dtype(dtype)) return MCG_ERR_UNSUPPORTED_DTYPE;
+  if (M < 0 || K < 0 || K % 4 != 0) return MCG_ERR_INVALID_SIZE;
+  if (M == 0 || K == 0) return MCG_SUCCESS;
+  if (!A || !A_compressed || !A_index) return MCG_ERR_NULL_POINTER;
+  if (lda < K || lda_c < K / 2 || ld_idx < (K + 31) / 32) return MCG_ERR_INVALID_LD;
+  const int eb = elem_bytes(dtype);
+  if (!aligned_to(A, eb) || !aligned_to(A_compressed, eb) || !aligned_to(A_index, 4))
+    return MCG_ERR_MISALIGNED;
+  return MCG_SUCCESS;
+}
+
+int compress24(int dtype, int64_t M, int64_t K, const void* A, int64_t lda, void* A_compressed,
+               int64_t lda_c, uint32_t* A_index, int64_t ld_idx, int32_t* d_violations,
+               void* stream) {
+  int st = mcg_validate_compress24(dtype, M, K, A, lda, A_compressed, lda_c, A_index, ld_idx);
+  if (st != MCG_SUCCESS) return st;
+  if (d_violations && !aligned_to(d_violations, 4)) return MCG_ERR_MISALIGNED;
+  if ((M == 0 || K == 0) && !d_violations) return MCG_SUCCESS;
+  st = check_arch();
+  if (st != MCG_SUCCESS) return st;
+  mcg::CompressArgs a{};
+  a.A = (const char*)A;
+  a.Ac = (char*)A_compressed;
+  a.idx = A_index;
+  a.violations = d_violations;
+  a.M = M;
+  a.K = K;
+  a.lda = lda;
+  a.lda_c = lda_c;
+  a.ld_idx = ld_idx;
+  return hip_status(mcg::launch_compress(dtype, a, (hipStream_t)stream));
+}
+
+int compress24_host(int dtype, int64_t M, int64_t K, const void* A, int64_t lda, void* A_compressed,
+                    int64_t lda_c, uint32_t* A_index, int64_t ld_idx) {
+  int st = mcg_validate_compress24(dtype, M, K, A, lda, A_compressed, lda_c, A_index, ld_idx);
+  if (st != MCG_SUCCESS) return st;
+  const int eb = elem_bytes(dtype);
+  const int64_t ngroups = K / 4, nwords = (K + 31) / 32;
+  int64_t bad = 0;
+  for (int64_t i = 0; i < M; ++i) {
+    const unsigned char* row = (const unsigned char*)A + i * lda * eb;
+    unsigned char* out = (unsigned char*)A_compressed + i * lda_c * eb;
+    for (int64_t w = 0; w < nwords; ++w) {
+      uint32_t word = 0;
+      for (int gi = 0; gi < 8 && w * 8 + gi < ngroups; ++gi) {
+        const int64_t g = w * 8 + gi;
+        int sel[4], nz = 0;
+        for (int e = 0; e < 4; ++e) {
+          uint32_t v = 0;
+          std::memcpy(&v, row + (4 * g + e) * eb, eb);
+          const bool isnz = dtype == MCG_I8 ? v != 0 : (eb == 2 ? (v & 0x7fffu) != 0 : (v & 0x7fu) != 0);
+          if (isnz && nz < 4) sel[nz] = e;
+          nz += isnz;
+        }
+        int p0 = 0, p1 = 1;
+        if (nz > 2) {
+          ++bad;
+          std::memset(out + 2 * g * eb, 0, 2 * eb);
+        } else {
+          if (nz == 2) { p0 = sel[0]; p1 = sel[1]; }
+          else if (nz == 1 && sel[0] != 0) { p0 = 0; p1 = sel[0]; }
+          std::memcpy(out + 2 * g * eb, row + (4 * g + p0) * eb, eb);
+          std::memcpy(out + (2 * g + 1) * eb, row + (4 * g + p1) * eb, eb);
+        }
+        word |= (uint32_t)(p0 | (p1 << 2)) << (4 * gi);
+      }
+      A_index[i * ld_idx + w] = word;
+    }
+  }
+  return bad ? MCG_ERR_NOT_2_4_SPARSE : MCG_SUCCESS;
+}
+
+const char* mcg_status_string(int status) {
+  switch (status) {
+    case MCG_SUCCESS: return "success";
+    case MCG_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case MCG_ERR_INVALID_SIZE: return "invalid size";
+    case MCG_ERR_INVALID_LD: return "leading dimension below its minimum";
+    case MCG_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype or layout combination";
+    case MCG_ERR_MISALIGNED: return "pointer not aligned to its element size";
+    case MCG_ERR_NOT_2_4_SPARSE: return "a group of four holds more than two non-zeros";
+    case MCG_ERR_INVALID_INDEX: return "malformed 2:4 index";
+    case MCG_ERR_UNSUPPORTED_ARCH: return "current device is not gfx950";
+    case MCG_ERR_HIP: return "HIP runtime error";
+    case MCG_ERR_INVALID_VALUE: return "alpha, beta or scale not usable for this dtype";
+    default: return "unknown status";
+  }
+}
+
+int mcg_version(void) { return kVersion; }
+
+}  // extern "C"

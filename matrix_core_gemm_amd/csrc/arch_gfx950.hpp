@@ -1,0 +1,155 @@
+// arch_gfx950.hpp -- gfx950 (CDNA4) matrix-core instruction wrappers and fragment layouts.
+//
+// One MFMA instruction computes one K-step of a small output tile across the 64
+// lanes of a wavefront ("CDNA3 dense MFMA builtins", Naming convention and
+// Accumulator layout).  The pages document the CDNA3 (gfx942) layouts; the
+// gfx950 layouts below were measured on an MI355X with one-hot operands and are
+// re-checked end to end by the one-hot GEMM tests:
+//
+//  Dense 16x16xK (bf16/f16 K=32, i8 K=64, f8f6f4 K=128), wave64:
+//    operand P (the instruction's "A"): lane l holds row (l & 15),
+//    operand Q (the instruction's "B"): lane l holds column (l & 15),
+//    and both hold the K run selected by lane group g = l >> 4; the K positions
+//    of element e of lane group g are the same function for P and Q, so any
+//    consistent K order of the two fragments gives the same product.
+//    Output: lane l, register r holds out[4*(l >> 4) + r][l & 15]
+//    (the single-block case of the 16x16 accumulator layout).
+//
+//  Sparse 16x16x64 (smfmac bf16/f16; 2:4 on P, dense K = 64):
+//    P (compressed, 8 values per lane): lane l holds row (l & 15); lane group
+//    g = l >> 4 covers dense K 16g..16g+15 as four groups of four; compressed
+//    values 2n, 2n+1 belong to group n and sit at the positions given by the
+//    4-bit code n of the index (p0 = code & 3, p1 = code >> 2).  The index
+//    VGPR holds two 16-bit halves of four codes; the abid modifier selects
+//    the half (0: bits 0..15).
+//    Q (dense, 16 values per lane): lane l holds column (l & 15); elements
+//    0..7 are dense K 8g..8g+7 and elements 8..15 are K 32+8g..32+8g+7.
+//    Output: same as the dense 16x16 layout.
+//
+//  Transposing LDS reads (per 16-lane group; lane L supplies an 8-byte address):
+//    ds_read_b64_tr_b16: output lane t, element e (0..3) = 16-bit element (t & 3)
+//      of the 8 bytes addressed by lane 4e + (t >> 2).
+//    ds_read_b64_tr_b8 : output lane t, element e (0..7) = byte (t & 7) of the
+//      8 bytes addressed by lane 2e + (t >> 3).
+//
+// fp8 operands use the OCP encodings (measured: code 0x7E of E4M3 is 448); the
+// f8f6f4 instruction takes the A/B formats in its cbsz/blgp fields
+// (0 = E4M3, 1 = E5M2) and, with zero scale operands, computes plain products.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mcg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+template <class T, class S>
+__device__ __forceinline__ T bit_cast(const S& s) {
+  static_assert(sizeof(T) == sizeof(S), "bit_cast size mismatch");
+  T t;
+  __builtin_memcpy(&t, &s, sizeof(T));
+  return t;
+}
+
+// Element-type codes, identical in value to the public mcg_dtype enum.
+enum : int { DT_BF16 = 0, DT_F16 = 1, DT_I8 = 2, DT_E4M3 = 3, DT_E5M2 = 4 };
+
+// f8f6f4 format field values
+__host__ __device__ constexpr int f8fmt(int dt) { return dt == DT_E5M2 ? 1 : 0; }
+
+// ------------------------------------------------------------------ dense ops
+// Every op multiplies a 16x16 output tile by one K-step.  LANE_BYTES is the
+// fragment size per lane per operand; K_STEP the K extent of one instruction.
+// mma(p, q, acc): acc += P.Q with P/Q in the layout described above.
+
+struct OpBF16 {
+  static constexpr int ELEM_BYTES = 2, LANE_BYTES = 16, K_STEP = 32;
+  static constexpr bool INT_ACC = false;
+  using frag_t = i32x4;
+  using acc_t = f32x4;
+  __device__ static __forceinline__ acc_t mma(frag_t p, frag_t q, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bit_cast<bf16x8>(p), bit_cast<bf16x8>(q), c, 0, 0, 0);
+  }
+};
+
+struct OpF16 {
+  static constexpr int ELEM_BYTES = 2, LANE_BYTES = 16, K_STEP = 32;
+  static constexpr bool INT_ACC = false;
+  using frag_t = i32x4;
+  using acc_t = f32x4;
+  __device__ static __forceinline__ acc_t mma(frag_t p, frag_t q, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(bit_cast<f16x8>(p), bit_cast<f16x8>(q), c, 0, 0, 0);
+  }
+};
+
+struct OpI8 {
+  static constexpr int ELEM_BYTES = 1, LANE_BYTES = 16, K_STEP = 64;
+  static constexpr bool INT_ACC = true;
+  using frag_t = i32x4;
+  using acc_t = i32x4;
+  __device__ static __forceinline__ acc_t mma(frag_t p, frag_t q, acc_t c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(p, q, c, 0, 0, 0);
+  }
+};
+
+// FP = format of operand P, FQ = format of operand Q (0 = E4M3, 1 = E5M2).
+template <int FP, int FQ>
+struct OpF8 {
+  static constexpr int ELEM_BYTES = 1, LANE_BYTES = 32, K_STEP = 128;
+  static constexpr bool INT_ACC = false;
+  using frag_t = i32x8;
+  using acc_t = f32x4;
+  __device__ static __forceinline__ acc_t mma(frag_t p, frag_t q, acc_t c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(p, q, c, FP, FQ, 0, 0, 0, 0);
+  }
+};
+
+// ----------------------------------------------------------------- sparse ops
+struct SpBF16 {
+  static constexpr int ELEM_BYTES = 2, K_STEP = 64;  // dense K per instruction
+  __device__ static __forceinline__ f32x4 mma(i32x4 p_comp, i32x8 q, f32x4 c, int index) {
+    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(bit_cast<bf16x8>(p_comp), bit_cast<bf16x16>(q), c,
+                                                     index, 0, 0);
+  }
+};
+struct SpF16 {
+  static constexpr int ELEM_BYTES = 2, K_STEP = 64;
+  __device__ static __forceinline__ f32x4 mma(i32x4 p_comp, i32x8 q, f32x4 c, int index) {
+    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(bit_cast<f16x8>(p_comp), bit_cast<f16x16>(q), c,
+                                                    index, 0, 0);
+  }
+};
+
+// ------------------------------------------------------------ output layout
+// 16x16 output tile: lane l, register r -> (row, col) of the instruction output.
+__host__ __device__ constexpr int out_row(int lane, int r) { return 4 * (lane >> 4) + r; }
+__host__ __device__ constexpr int out_col(int lane) { return lane & 15; }
+
+// ------------------------------------------------------------ LDS primitives
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ i32x4 lds_read_b128(const lds_char* base, int off) {
+  return *(const __attribute__((address_space(3))) i32x4*)(base + off);
+}
+__device__ __forceinline__ void lds_write_b128(lds_char* base, int off, i32x4 v) {
+  *(__attribute__((address_space(3))) i32x4*)(base + off) = v;
+}
+__device__ __forceinline__ i32x2 lds_read_tr16(const lds_char* base, int off) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(const_cast<lds_char*>(base) + off));
+  return bit_cast<i32x2>(v);
+}
+__device__ __forceinline__ i32x2 lds_read_tr8(const lds_char* base, int off) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) i32x2*)(const_cast<lds_char*>(base) + off));
+}
+
+}  // namespace mcg

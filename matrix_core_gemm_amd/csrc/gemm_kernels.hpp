@@ -1,0 +1,49 @@
+// gemm_kernels.hpp -- kernel argument blocks and launchers shared by the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mcg {
+
+struct DenseArgs {
+  const char* A;
+  const char* B;
+  const void* C;
+  void* D;
+  int64_t M, N, K;
+  int64_t lda, ldb, ldc;  // elements
+  float alpha, beta;      // float paths: alpha already includes scaleA*scaleB
+  int alpha_i, beta_i;    // int8 path
+  int use_c;              // beta != 0: C is read
+  int vec_cd;             // C/D 16-byte aligned with ldc % 4 == 0
+  int tiles_m, tiles_n;   // filled by the launcher
+};
+
+struct SparseArgs {
+  const char* Ac;       // compressed values, M x K/2
+  const uint32_t* idx;  // index words, M x ceil(K/32)
+  const char* B;
+  const void* C;
+  void* D;
+  int64_t M, N, K;               // dense K
+  int64_t lda_c, ld_idx, ldb, ldc;
+  float alpha, beta;
+  int use_c, vec_cd;
+  int tiles_m, tiles_n;
+};
+
+struct CompressArgs {
+  const char* A;
+  char* Ac;
+  uint32_t* idx;
+  int32_t* violations;  // may be null
+  int64_t M, K, lda, lda_c, ld_idx;
+};
+
+// Enqueue the kernels; arguments were validated by the caller.
+hipError_t launch_dense(int dtA, int dtB, int layoutA, int layoutB, bool aligned, const DenseArgs& a,
+                        hipStream_t s);
+hipError_t launch_sparse(int dt, int layoutB, bool aligned, const SparseArgs& a, hipStream_t s);
+hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s);
+
+}  // namespace mcg

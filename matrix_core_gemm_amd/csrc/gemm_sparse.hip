@@ -1,0 +1,279 @@
+// gemm_sparse.hip -- 2:4 structured-sparse GEMM on the sparse matrix cores (SMFMAC) and the
+// device 2:4 compressor.
+//
+// The sparse operand follows the 2:4 model of "RDNA4 sparse WMMA builtins"
+// (Structured sparsity (2:4 pattern): in every group of four along K at most two
+// values are non-zero; only those are stored, halving A's storage and
+// bandwidth; an index of 2-bit positions tells the hardware where each stored
+// value sits; Common parameters: the index operand packs the positions of all
+// values a lane holds into one 32-bit register).  The same model is provided on
+// CDNA by SMFMAC, the wave64 sparse MFMA named on that page's introduction.
+//
+// Index layout in memory (the library's canonical form): group g of row i has
+// the 4-bit code p0 | p1 << 2 at bits 4*(g % 8) of word g/8.  On gfx950 a lane
+// of smfmac_f32_16x16x64 holds four consecutive groups and reads their codes
+// from one 16-bit half of its index register, nibble n for compressed values
+// 2n and 2n+1 (measured).  So a lane's index is a 16-bit slice of one canonical
+// word and needs no re-packing.
+//
+// Sparse kernel structure: as the dense kernel (256 threads, 2 x 2 waves,
+// double-buffered LDS), with K tiles of 128 dense k: A_c tile 128 bytes per
+// row (64 kept values), index tile 16 bytes per row (4 words), B tile
+// 256 bytes of K per column.  The sparse operand must be the instruction's P,
+// so output lanes hold four consecutive rows of one column of D.
+#include "gemm_kernels.hpp"
+#include "tile_io.hpp"
+
+namespace mcg {
+
+// Replace every all-zero 4-bit code with 0b0100 (positions 0 and 1).  Zero codes
+// only occur past the end of K (padding) where all values are zero; this keeps
+// every code the instruction sees a valid 2:4 selection.
+__device__ __forceinline__ uint32_t fix_zero_codes(uint32_t w) {
+  uint32_t t = w | (w >> 1);
+  t |= t >> 2;
+  const uint32_t zero = (~t) & 0x11111111u;
+  return w | (zero << 2);
+}
+
+template <class Op, int LB, int BM, int BN, bool ALIGNED>
+__global__ __launch_bounds__(256) void gemm_sparse_kernel(SparseArgs p) {
+  constexpr int NT = 256;
+  constexpr int EB = Op::ELEM_BYTES;    // 2
+  constexpr int KD = 128;               // dense K per tile
+  constexpr int KTB_A = KD / 2 * EB;    // 128 bytes of kept values per row
+  constexpr int KTB_B = KD * EB;        // 256 bytes of dense K per column
+  constexpr int STEPS = KD / Op::K_STEP;
+  constexpr int WTM = BM / 2 / 16, WTN = BN / 2 / 16;
+  using GA = TileGeom<EB, LAYOUT_K, BM, KTB_A>;
+  using GB = TileGeom<EB, LB, BN, KTB_B>;
+  using RA = FragReader<EB, 16, LAYOUT_K, BM, KTB_A>;
+  using RB = FragReader<EB, 16, LB, BN, KTB_B>;
+  constexpr int IDX_BYTES = BM * 16;
+
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * (GA::BYTES + GB::BYTES + IDX_BYTES)];
+  lds_char* smem = (lds_char*)smem_raw;
+  constexpr int STAGE = GA::BYTES + GB::BYTES + IDX_BYTES;
+  lds_char* ldsA[2] = {smem, smem + STAGE};
+  lds_char* ldsB[2] = {smem + GA::BYTES, smem + STAGE + GA::BYTES};
+  lds_char* ldsI[2] = {smem + GA::BYTES + GB::BYTES, smem + STAGE + GA::BYTES + GB::BYTES};
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int pid = blockIdx.x;
+  const int group = 8;
+  const int tiles_in_group = group * p.tiles_n;
+  const int gid = pid / tiles_in_group;
+  const int first_m = gid * group;
+  const int gsize = min(p.tiles_m - first_m, group);
+  const int tm = first_m + (pid % tiles_in_group) % gsize;
+  const int tn = (pid % tiles_in_group) / gsize;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  const int nk = (int)((p.K + KD - 1) / KD);
+  const int64_t Kc = p.K / 2;             // kept values per row
+  const int64_t nwords = (p.K + 31) / 32; // index words per row
+
+  TileLoader<EB, LAYOUT_K, BM, NT, ALIGNED, KTB_A> la;
+  TileLoader<EB, LB, BN, NT, ALIGNED, KTB_B> lb;
+  i32x4 ireg = {0, 0, 0, 0};  // threads < BM: one row of 4 index words
+  auto load_tiles = [&](int kt) {
+    const int64_t k0 = (int64_t)kt * KD;
+    la.load(p.Ac, p.lda_c, m0, k0 / 2, p.M, Kc, tid);
+    if constexpr (LB == LAYOUT_K) lb.load(p.B, p.ldb, n0, k0, p.N, p.K, tid);
+    else lb.load(p.B, p.ldb, k0, n0, p.K, p.N, tid);
+    if (tid < BM) {
+      const int64_t row = m0 + tid, w0 = k0 / 32;
+      const uint32_t* src = p.idx + row * p.ld_idx + w0;
+      if (ALIGNED && row < p.M && w0 + 4 <= nwords) {
+        ireg = *(const i32x4*)src;
+      } else {
+        ireg = i32x4{0, 0, 0, 0};
+        if (row < p.M)
+          for (int e = 0; e < 4; ++e)
+            if (w0 + e < nwords) ireg[e] = (int)src[e];
+      }
+    }
+  };
+  auto store_tiles = [&](int buf) {
+    la.store(ldsA[buf], tid);
+    lb.store(ldsB[buf], tid);
+    if (tid < BM) lds_write_b128(ldsI[buf], tid * 16, ireg);
+  };
+
+  f32x4 acc[WTM][WTN];
+#pragma unroll
+  for (int i = 0; i < WTM; ++i)
+#pragma unroll
+    for (int j = 0; j < WTN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nk > 0) {
+    load_tiles(0);
+    store_tiles(0);
+    __syncthreads();
+  }
+  const int g = lane >> 4;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_tiles(kt + 1);
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      i32x4 fa[WTM];
+      int fi[WTM];
+      i32x8 fb[WTN];
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        const int rb = wm * (BM / 2) + i * 16;
+        fa[i] = RA::run16(ldsA[cur], rb, 16 * (4 * s + g), lane);
+        // codes of dense k [64s + 16g, +16): word 2s + g/2, half g % 2
+        const int row = rb + (lane & 15);
+        const uint32_t w = *(const __attribute__((address_space(3))) uint32_t*)(ldsI[cur] + row * 16 + 4 * (2 * s + (g >> 1)));
+        fi[i] = (int)(fix_zero_codes(w >> (16 * (g & 1))) & 0xffffu);
+      }
+#pragma unroll
+      for (int j = 0; j < WTN; ++j) {
+        const int rb = wn * (BN / 2) + j * 16;
+        // dense k [64s + 8g, +8) and [64s + 32 + 8g, +8)
+        const i32x4 lo = RB::run16(ldsB[cur], rb, EB * (64 * s + 8 * g), lane);
+        const i32x4 hi = RB::run16(ldsB[cur], rb, EB * (64 * s + 32 + 8 * g), lane);
+        fb[j] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
+#pragma unroll
+      for (int i = 0; i < WTM; ++i)
+#pragma unroll
+        for (int j = 0; j < WTN; ++j) acc[i][j] = Op::mma(fa[i], fb[j], acc[i][j], fi[i]);
+    }
+    if (kt + 1 < nk) store_tiles(cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds D[m .. m+3][n], m = row base + 4*(lane >> 4), n = column base + (lane & 15)
+  const float* C = (const float*)p.C;
+  float* D = (float*)p.D;
+#pragma unroll
+  for (int i = 0; i < WTM; ++i) {
+#pragma unroll
+    for (int j = 0; j < WTN; ++j) {
+      const int64_t n = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4) + r;
+        if (m >= p.M) continue;
+        const int64_t off = m * p.ldc + n;
+        const float v = acc[i][j][r];
+        D[off] = p.use_c ? __builtin_fmaf(p.alpha, v, p.beta * C[off]) : p.alpha * v;
+      }
+    }
+  }
+}
+
+template <class Op, int LB, bool AL>
+static hipError_t launch_sparse_one(const SparseArgs& a0, hipStream_t s) {
+  constexpr int BM = 128, BN = 128;
+  SparseArgs a = a0;
+  a.tiles_m = (int)((a.M + BM - 1) / BM);
+  a.tiles_n = (int)((a.N + BN - 1) / BN);
+  const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_sparse_kernel<Op, LB, BM, BN, AL>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse(int dt, int lb, bool aligned, const SparseArgs& a, hipStream_t s) {
+#define MCG_S(OP)                                                                        \
+  if (lb == LAYOUT_K)                                                                    \
+    return aligned ? launch_sparse_one<OP, LAYOUT_K, true>(a, s) : launch_sparse_one<OP, LAYOUT_K, false>(a, s); \
+  return aligned ? launch_sparse_one<OP, LAYOUT_MN, true>(a, s) : launch_sparse_one<OP, LAYOUT_MN, false>(a, s);
+  if (dt == DT_BF16) { MCG_S(SpBF16) }
+  MCG_S(SpF16)
+#undef MCG_S
+}
+
+// ------------------------------------------------------------- compressor
+// One thread per (row, index word): reads the 32 dense values of 8 groups,
+// keeps the non-zeros of each group (ascending; padded with the lowest free
+// positions), writes the kept values and the word of codes.  +0 and -0 count
+// as zero and NaN as non-zero.  A group with more than two non-zeros is
+// counted and written as two zeros with code 0b0100.
+
+template <int EB>
+__device__ __forceinline__ bool nonzero_code(uint32_t v) {
+  if constexpr (EB == 2) return (v & 0x7fffu) != 0;
+  else return (v & 0x7fu) != 0;
+}
+
+template <int EB, bool INT8>
+__global__ __launch_bounds__(256) void compress24_kernel(CompressArgs p) {
+  const int64_t nwords = (p.K + 31) / 32;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= p.M * nwords) return;
+  const int64_t row = t / nwords, w = t % nwords;
+  const int64_t g0 = w * 8;
+  const int64_t ngroups = p.K / 4;
+  const char* src = p.A + (row * p.lda + g0 * 4) * EB;
+  char* dst = p.Ac + (row * p.lda_c + g0 * 2) * EB;
+  uint32_t word = 0;
+  int bad = 0;
+  for (int gi = 0; gi < 8; ++gi) {
+    if (g0 + gi >= ngroups) break;
+    uint32_t v[4];
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (EB == 2) v[e] = *(const uint16_t*)(src + (gi * 4 + e) * 2);
+      else v[e] = (uint8_t)src[gi * 4 + e];
+    }
+    int pos[4], nz = 0;
+    for (int e = 0; e < 4; ++e) {
+      const bool isnz = INT8 ? (v[e] != 0) : nonzero_code<EB>(v[e]);
+      if (isnz) pos[nz++ & 3] = e;
+    }
+    int p0, p1;
+    uint32_t k0, k1;
+    if (nz > 2) {
+      ++bad;
+      p0 = 0; p1 = 1; k0 = 0; k1 = 0;
+    } else {
+      if (nz == 0) { p0 = 0; p1 = 1; }
+      else if (nz == 1) {
+        if (pos[0] == 0) { p0 = 0; p1 = 1; }
+        else { p0 = 0; p1 = pos[0]; }
+      } else { p0 = pos[0]; p1 = pos[1]; }
+      k0 = v[p0]; k1 = v[p1];
+    }
+    word |= (uint32_t)(p0 | (p1 << 2)) << (4 * gi);
+    if constexpr (EB == 2) {
+      *(uint16_t*)(dst + (gi * 2) * 2) = (uint16_t)k0;
+      *(uint16_t*)(dst + (gi * 2 + 1) * 2) = (uint16_t)k1;
+    } else {
+      dst[gi * 2] = (char)k0;
+      dst[gi * 2 + 1] = (char)k1;
+    }
+  }
+  p.idx[row * p.ld_idx + w] = word;
+  if (bad && p.violations) atomicAdd(p.violations, bad);
+}
+
+__global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
+
+hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s) {
+  if (a.violations) {
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, s, a.violations);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t nwords = (a.K + 31) / 32;
+  const int64_t threads = a.M * nwords;
+  if (threads <= 0) return hipSuccess;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (dtype == DT_BF16 || dtype == DT_F16)
+    hipLaunchKernelGGL((compress24_kernel<2, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else if (dtype == DT_I8)
+    hipLaunchKernelGGL((compress24_kernel<1, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((compress24_kernel<1, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mcg

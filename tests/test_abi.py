@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, rejects bad arguments on the host before touching the device,
+and its host compressor matches the oracle byte for byte."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mcg.h")
+
+m = pytest.importorskip("matrix_core_gemm_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for fn in ("gemm_dense", "gemm_sparse24", "compress24", "compress24_host", "mcg_status_string"):
+        assert fn in names
+    assert set(names) == set(m.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for fn in declared_functions():
+        assert hasattr(lib, fn), fn
+
+
+def test_status_strings():
+    for s in range(11):
+        assert m.status_string(s) and "unknown" not in m.status_string(s)
+    assert "unknown" in m.status_string(999)
+    assert m.version() >= 100
+
+
+FAKE = 0x10000  # a 64 KiB-aligned non-null address; validation never dereferences it
+
+
+def dense_args(**kw):
+    a = dict(dtypeA="bf16", dtypeB="bf16", layoutA="k_contig", layoutB="k_contig", M=64, N=32, K=48,
+             A=FAKE, lda=48, B=FAKE, ldb=48, C=None, D=FAKE, ldc=32, dtypeD="f32", alpha=1.0,
+             beta=0.0, scaleA=1.0, scaleB=1.0)
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, 0),
+    ({"dtypeA": "f16"}, 4),                          # mixed non-fp8 pair
+    ({"dtypeA": "i8", "dtypeB": "i8"}, 4),           # int8 needs i32 output
+    ({"dtypeA": "i8", "dtypeB": "i8", "dtypeD": "i32"}, 0),
+    ({"dtypeA": "e4m3", "dtypeB": "e5m2"}, 0),
+    ({"dtypeA": "e4m3", "dtypeB": "bf16"}, 4),
+    ({"dtypeA": 9}, 4),
+    ({"layoutA": 2}, 4),
+    ({"M": -1}, 2),
+    ({"K": -5}, 2),
+    ({"M": 0, "A": None, "B": None, "D": None}, 0),  # empty output: no-op
+    ({"N": 0, "D": None}, 0),
+    ({"D": None}, 1),
+    ({"A": None}, 1),
+    ({"K": 0, "A": None, "B": None, "lda": 1, "ldb": 1}, 0),
+    ({"beta": 1.0}, 1),                              # C needed
+    ({"beta": 1.0, "C": FAKE}, 0),
+    ({"lda": 47}, 3),
+    ({"ldb": 47}, 3),
+    ({"ldc": 31}, 3),
+    ({"layoutA": "mn_contig", "lda": 63}, 3),
+    ({"layoutA": "mn_contig", "lda": 64}, 0),
+    ({"layoutB": "mn_contig", "ldb": 31}, 3),
+    ({"A": FAKE + 1}, 5),                            # bf16 pointer not 2-byte aligned
+    ({"D": FAKE + 2}, 5),
+    ({"A": FAKE + 2, "lda": 49}, 0),                 # unaligned to 16 is allowed (slow path)
+    ({"scaleA": 2.0}, 10),                           # scales only for fp8
+    ({"dtypeA": "e4m3", "dtypeB": "e4m3", "scaleA": 0.25}, 0),
+    ({"dtypeA": "i8", "dtypeB": "i8", "dtypeD": "i32", "alpha": 1.5}, 10),
+    ({"dtypeA": "i8", "dtypeB": "i8", "dtypeD": "i32", "beta": 2.0 ** 31, "C": FAKE}, 10),
+    ({"alpha": float("nan")}, 10),
+])
+def test_dense_validation(kw, status):
+    assert m.validate_dense(**dense_args(**kw)) == status
+
+
+def test_entry_points_reject_before_touching_the_device():
+    # These calls fail validation, so no HIP call happens (no GPU here).
+    with pytest.raises(m.MCGError) as e:
+        m.gemm_dense(**dense_args(lda=1), stream=0)
+    assert e.value.status == 3
+    with pytest.raises(m.MCGError):
+        m.gemm_sparse24("bf16", "bf16", "k_contig", 8, 8, 6, FAKE, 3, FAKE, 1, FAKE, 6, None, FAKE, 8,
+                        "f32", stream=0)
+    with pytest.raises(m.MCGError):
+        m.compress24("bf16", 4, 10, FAKE, 10, FAKE, 5, FAKE, 1, stream=0)
+    # empty problems succeed without a device
+    m.gemm_dense(**dense_args(M=0), stream=0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, 0),
+    ({"K": 10}, 2),
+    ({"dtypeA": "i8", "dtypeB": "i8"}, 4),
+    ({"dtypeD": "i32"}, 4),
+    ({"lda_c": 31}, 3),
+    ({"ld_idx": 1}, 3),
+    ({"A_index": None}, 1),
+    ({"A_index": FAKE + 2}, 5),
+    ({"layoutB": "mn_contig", "ldb": 48}, 3),
+    ({"layoutB": "mn_contig", "ldb": 96}, 0),
+])
+def test_sparse_validation(kw, status):
+    a = dict(dtypeA="bf16", dtypeB="bf16", layoutB="k_contig", M=64, N=96, K=64, A_compressed=FAKE,
+             lda_c=32, A_index=FAKE, ld_idx=2, B=FAKE, ldb=64, C=None, D=FAKE, ldc=96, dtypeD="f32")
+    a.update(kw)
+    assert m.validate_sparse24(**a) == status
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "i8", "e4m3", "e5m2"])
+@pytest.mark.parametrize("shape", [(1, 4), (7, 36), (33, 200), (16, 256)])
+def test_compress24_host_matches_oracle(dt, shape):
+    M, K = shape
+    A = W.sparse24_dense(dt, M, K, dist="int8" if dt == "i8" else "normal")
+    vals = np.zeros((M, K // 2), W.CODE_NP[dt])
+    idx = np.zeros((M, (K + 31) // 32), np.uint32)
+    assert m.compress24_host(dt, M, K, A, K, vals, K // 2, idx, idx.shape[1]) == 0
+    ov, oi, viol = oracle.compress24(dt, A)
+    assert viol == 0
+    assert np.array_equal(vals, ov) and np.array_equal(idx, oi)
+
+
+def test_compress24_host_flags_violations_like_oracle():
+    rng = np.random.default_rng(0)
+    A = rng.integers(-3, 4, (9, 64)).astype(np.int8)   # dense: many groups have > 2 non-zeros
+    vals = np.zeros((9, 32), np.int8)
+    idx = np.zeros((9, 2), np.uint32)
+    assert m.compress24_host("i8", 9, 64, A, 64, vals, 32, idx, 2) == 6
+    ov, oi, viol = oracle.compress24("i8", A)
+    assert viol > 0
+    assert np.array_equal(vals, ov) and np.array_equal(idx, oi)

@@ -1,0 +1,238 @@
+"""GPU parity of gemm_dense against the CPU oracle (MI355X).
+
+Float paths must satisfy |D_gpu - D_ref| <= 4*2^-24*(K+2)*|alpha*sA*sB|*S + 2^-24*|D_ref|
+element-wise (S = sum_k |a_ik b_kj|); int8 must be bit-exact; inputs whose
+partial sums are all exactly representable must be bit-exact on every path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import compare, dev, need_gpu, oracle_dense, run_dense, say
+
+pytestmark = pytest.mark.gpu
+
+PAIRS = [("bf16", "bf16"), ("f16", "f16"), ("i8", "i8"), ("e4m3", "e4m3"), ("e4m3", "e5m2"),
+         ("e5m2", "e4m3"), ("e5m2", "e5m2")]
+LAYOUTS = [("k_contig", "k_contig"), ("k_contig", "mn_contig"), ("mn_contig", "k_contig"),
+           ("mn_contig", "mn_contig")]
+
+
+def operands(dtA, dtB, layA, layB, M, N, K, dist=None, pad=0, seed=0):
+    dist = dist or ("int8" if dtA == "i8" else "normal")
+    fp8 = dtA in ("e4m3", "e5m2")
+    ldA = (K if layA == "k_contig" else M) + pad
+    ldB = (K if layB == "k_contig" else N) + pad
+    A = W.operand("A", dtA, M, K, dist, layA, seed=10 * seed, ld=ldA, fp8_scaled=fp8)
+    B = W.operand("B", dtB, K, N, dist, layB, seed=10 * seed + 1, ld=ldB, fp8_scaled=fp8)
+    return A, B
+
+
+def check_case(mcg, dtA, dtB, layA, layB, M, N, K, pad=0, beta=1.0, alpha=None, ldc_pad=0, seed=0,
+               dist=None):
+    say(f"case {dtA}x{dtB} {layA}/{layB} M={M} N={N} K={K} pad={pad} beta={beta}")
+    A, B = operands(dtA, dtB, layA, layB, M, N, K, dist, pad, seed)
+    ldc = N + ldc_pad
+    i8 = dtA == "i8"
+    if alpha is None:
+        alpha = 3 if i8 else 1.5
+    C = None
+    if beta != 0:
+        C = W.c_matrix(M, N, "int20" if i8 else "normal", seed=10 * seed + 2, ldc=ldc)
+    d = run_dense(mcg, dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, ldc, alpha,
+                  beta, A.scale, B.scale)
+    ref, s = oracle_dense(dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, ldc,
+                          alpha, beta, A.scale, B.scale)
+    compare(dtA, d[:M, :N], ref, s, K, alpha, A.scale, B.scale, beta,
+            None if C is None else C[:M, :N], what=f"{dtA}x{dtB} {layA}/{layB} {M}x{N}x{K}")
+    if ldc_pad:  # padding columns of D untouched
+        if i8:
+            assert np.all(d[:M, N:] == -0x5A5A5A5A)
+        else:
+            assert np.all(np.isnan(d[:M, N:]))
+
+
+def test_config_bf16_256_cubed():
+    """bf16 256^3, A row-major, B column-major, C = 0, alpha = 1, beta = 0,
+    entries uniform in [-1, 1] rounded to bf16: full comparison."""
+    mcg = need_gpu()
+    wl = W.standard_workloads()[0]
+    A = W.operand("A", "bf16", 256, 256, "uniform", "k_contig")
+    B = W.operand("B", "bf16", 256, 256, "uniform", "k_contig")
+    d = run_dense(mcg, "bf16", "bf16", "k_contig", "k_contig", 256, 256, 256, A.codes, A.ld,
+                  B.codes, B.ld)
+    ref, s = oracle.gemm_float("bf16", "bf16", "k_contig", "k_contig", 256, 256, 256, A.codes,
+                               A.ld, B.codes, B.ld)
+    r = compare("bf16", d, ref, s, 256, what=wl.name)
+    say("config bf16 256^3 max |delta|/bound", r["max_ratio"])
+
+
+@pytest.mark.parametrize("dtA,dtB", PAIRS)
+@pytest.mark.parametrize("layA,layB", LAYOUTS)
+def test_multi_tile_ragged(dtA, dtB, layA, layB):
+    """Several tiles with ragged tails in M, N and K (vector-load path)."""
+    mcg = need_gpu()
+    check_case(mcg, dtA, dtB, layA, layB, 300, 200, 300, pad=20, ldc_pad=4)
+
+
+@pytest.mark.parametrize("dtA,dtB", PAIRS)
+@pytest.mark.parametrize("shape", [(1, 1, 1), (17, 33, 65), (255, 257, 129), (64, 48, 3)])
+def test_small_odd_shapes_element_path(dtA, dtB, shape):
+    """Odd sizes with unpadded leading dimensions take the element-load path."""
+    mcg = need_gpu()
+    M, N, K = shape
+    for layA, layB in LAYOUTS:
+        check_case(mcg, dtA, dtB, layA, layB, M, N, K, pad=0)
+
+
+@pytest.mark.parametrize("dtA,dtB", PAIRS)
+def test_beta_zero_and_alpha(dtA, dtB):
+    mcg = need_gpu()
+    check_case(mcg, dtA, dtB, "k_contig", "k_contig", 130, 140, 256, beta=0.0)
+    check_case(mcg, dtA, dtB, "mn_contig", "k_contig", 130, 140, 256, beta=-2 if dtA == "i8" else 0.5,
+               alpha=-1 if dtA == "i8" else -0.25)
+
+
+SMALL = {"bf16": 8, "f16": 8, "e4m3": 16, "e5m2": 8}
+
+
+@pytest.mark.parametrize("dtA,dtB", [p for p in PAIRS if p[0] != "i8"])
+@pytest.mark.parametrize("layA,layB", LAYOUTS)
+def test_small_integers_bit_exact(dtA, dtB, layA, layB):
+    """Integer-valued inputs with all partial sums below 2^24: any accumulation
+    order or alignment scheme gives the exact result, so the GPU must match the
+    oracle bit for bit."""
+    mcg = need_gpu()
+    M, N, K = 192, 160, 512
+    r = min(SMALL[dtA], SMALL[dtB])
+    A = W.operand("A", dtA, M, K, f"smallint{r}", layA, seed=5)
+    B = W.operand("B", dtB, K, N, f"smallint{r}", layB, seed=6)
+    C = np.round(W.c_matrix(M, N, "normal", seed=7) * 1000).astype(np.float32)
+    d = run_dense(mcg, dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, N, 1.0, 1.0)
+    ref, _ = oracle.gemm_float(dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, N,
+                               1.0, 1.0)
+    assert np.array_equal(d, ref)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "i8", "e4m3"])
+@pytest.mark.parametrize("layA,layB", LAYOUTS)
+def test_permutation_bit_exact(dt, layA, layB):
+    """D = P.B (+ C): every output is one input value (plus C), rounded once."""
+    mcg = need_gpu()
+    n, N = 256, 136
+    perm = np.random.default_rng(3).permutation(n)
+    Pm = torch.zeros((n, n), dtype=torch.float32)
+    Pm[torch.arange(n), torch.from_numpy(perm)] = 1.0
+    Pq, _ = W.quantize(Pm if dt != "i8" else Pm.to(torch.int64), dt)
+    Ps, lda = W.store(Pq, "A", layA)
+    B = W.operand("B", dt, n, N, "int8" if dt == "i8" else "normal", layB, seed=8)
+    C = W.c_matrix(n, N, "int20" if dt == "i8" else "normal", seed=9)
+    d = run_dense(mcg, dt, dt, layA, layB, n, N, n, W.codes_of(Ps, dt), lda, B.codes, B.ld, C, N,
+                  1, 1)
+    ref, _ = oracle_dense(dt, dt, layA, layB, n, N, n, W.codes_of(Ps, dt), lda, B.codes, B.ld, C, N,
+                          1, 1)
+    assert np.array_equal(d, ref)
+
+
+def test_every_output_written_and_c_not_read_when_beta_zero():
+    mcg = need_gpu()
+    M, N, K = 333, 222, 96
+    A, B = operands("bf16", "bf16", "k_contig", "k_contig", M, N, K)
+    c_nan = torch.full((M, N), float("nan"), device="cuda")
+    d = run_dense(mcg, "bf16", "bf16", "k_contig", "k_contig", M, N, K, A.codes, A.ld, B.codes,
+                  B.ld, None, N, 1.0, 0.0, c_dev=c_nan)
+    assert not np.isnan(d).any()
+
+
+def test_k_zero_gives_beta_c_and_m_zero_is_noop():
+    mcg = need_gpu()
+    M, N = 70, 90
+    C = W.c_matrix(M, N, "normal")
+    A = np.zeros((M, 8), np.uint16)
+    B = np.zeros((N, 8), np.uint16)
+    d = run_dense(mcg, "bf16", "bf16", "k_contig", "k_contig", M, N, 0, A, 8, B, 8, C, N, 1.0, 2.0)
+    assert np.array_equal(d, (2.0 * C).astype(np.float32))
+    D = torch.full((4, 4), 7.0, device="cuda")
+    mcg.gemm_dense("bf16", "bf16", 0, 0, 0, 4, 4, None, 4, None, 4, None, D, 4, "f32")
+    torch.cuda.synchronize()
+    assert torch.all(D == 7.0)
+
+
+def test_d_aliases_c():
+    mcg = need_gpu()
+    M, N, K = 200, 136, 192
+    A, B = operands("f16", "f16", "k_contig", "mn_contig", M, N, K)
+    C = W.c_matrix(M, N, "normal")
+    cd = dev(C)
+    mcg.gemm_dense("f16", "f16", "k_contig", "mn_contig", M, N, K, dev(A.codes), A.ld, dev(B.codes),
+                   B.ld, cd, cd, N, "f32", 1.0, 1.0)
+    torch.cuda.synchronize()
+    ref, s = oracle.gemm_float("f16", "f16", "k_contig", "mn_contig", M, N, K, A.codes, A.ld,
+                               B.codes, B.ld, C, N, 1.0, 1.0)
+    compare("f16", cd.cpu().numpy(), ref, s, K, beta=1.0, c=C)
+
+
+def test_int8_wraps_mod_2_32():
+    mcg = need_gpu()
+    M, N, K = 64, 64, 512
+    A = np.full((M, K), 127, np.int8)
+    B = np.full((N, K), 127, np.int8)
+    C = np.full((M, N), 2 ** 30, np.int32)
+    d = run_dense(mcg, "i8", "i8", "k_contig", "k_contig", M, N, K, A, K, B, K, C, N, 7, 3)
+    ref = oracle.gemm_i8("k_contig", "k_contig", M, N, K, A, K, B, K, C, N, 7, 3)
+    assert np.array_equal(d, ref)
+
+
+def test_streams_are_honoured():
+    mcg = need_gpu()
+    M = N = K = 512
+    A, B = operands("bf16", "bf16", "k_contig", "k_contig", M, N, K)
+    dA, dB = dev(A.codes), dev(B.codes)
+    s = torch.cuda.Stream()
+    D = torch.empty((M, N), device="cuda")
+    with torch.cuda.stream(s):
+        mcg.gemm_dense("bf16", "bf16", 0, 0, M, N, K, dA, A.ld, dB, B.ld, None, D, N, "f32")
+    s.synchronize()
+    ref, sref = oracle.gemm_float("bf16", "bf16", "k_contig", "k_contig", M, N, K, A.codes, A.ld,
+                                  B.codes, B.ld)
+    compare("bf16", D.cpu().numpy(), ref, sref, K)
+
+
+# ------------------------------------------------------- full-size configurations
+
+def sampled_check(mcg, wl, seed=0):
+    """Full-size run in the benchmark's launch configuration; the oracle
+    computes sampled outputs one by one (whole rows, whole columns, random
+    elements, corners)."""
+    say(f"full-size: {wl.name}")
+    M, N, K = wl.M, wl.N, wl.K
+    A = W.operand("A", wl.dtA, M, K, wl.dist, wl.layA, fp8_scaled=wl.fp8_scaled)
+    B = W.operand("B", wl.dtB, K, N, wl.dist, wl.layB, fp8_scaled=wl.fp8_scaled)
+    C = W.c_matrix(M, N, wl.c_dist) if wl.c_dist else None
+    d = run_dense(mcg, wl.dtA, wl.dtB, wl.layA, wl.layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C,
+                  N, wl.alpha, wl.beta, A.scale, B.scale)
+    rows, cols = W.sample_coords(M, N, n_random=4096, full_rows=(0, M // 2 + 5, M - 1),
+                                 full_cols=(1, N - 1))
+    ref, s = oracle_dense(wl.dtA, wl.dtB, wl.layA, wl.layB, M, N, K, A.codes, A.ld, B.codes, B.ld,
+                          C, N, wl.alpha, wl.beta, A.scale, B.scale, rows, cols)
+    r = compare(wl.dtA, d[rows, cols], ref, s, K, wl.alpha, A.scale, B.scale, wl.beta,
+                None if C is None else C[rows, cols], what=wl.name)
+    if wl.dtA != "i8":
+        assert not np.isnan(d).any()
+    say(f"  sampled {r['n']} outputs ok; max |delta|/bound = {r.get('max_ratio')}")
+    return d
+
+
+FULL = [w for w in W.standard_workloads() if not w.sparse and w.M > 256]
+
+
+@pytest.mark.parametrize("wl", FULL, ids=[w.name.split(",")[0] for w in FULL])
+def test_full_size_configurations(wl):
+    mcg = need_gpu()
+    d1 = sampled_check(mcg, wl)
+    if wl.dtA == "i8":
+        # run-to-run determinism of the exact path over the whole output
+        d2 = sampled_check(mcg, wl)
+        assert np.array_equal(d1, d2)

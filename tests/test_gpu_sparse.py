@@ -1,0 +1,128 @@
+"""GPU parity of the 2:4 path: the device compressor must equal the oracle's
+byte for byte; gemm_sparse24 must meet the float bound against "decompress,
+then the dense oracle" (bit-exact on integer-valued inputs)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import compare, dev, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "i8", "e4m3", "e5m2"])
+@pytest.mark.parametrize("shape", [(1, 4), (7, 36), (130, 200), (64, 1024), (3, 4100)])
+def test_compress24_matches_oracle(dt, shape):
+    mcg = need_gpu()
+    M, K = shape
+    say(f"compress24 {dt} {shape}")
+    A = W.sparse24_dense(dt, M, K, dist="int8" if dt == "i8" else "normal")
+    nw = (K + 31) // 32
+    vals = torch.full((M, K // 2), 0x5A, dtype=torch.uint8 if W.ELEM_BYTES[dt] == 1 else torch.int16,
+                      device="cuda")
+    idx = torch.full((M, nw), -1, dtype=torch.int32, device="cuda")
+    viol = torch.full((1,), 123, dtype=torch.int32, device="cuda")
+    mcg.compress24(dt, M, K, dev(A), K, vals, K // 2, idx, nw, viol)
+    torch.cuda.synchronize()
+    ov, oi, ovio = oracle.compress24(dt, A)
+    assert int(viol.item()) == ovio == 0
+    assert np.array_equal(vals.cpu().numpy().view(W.CODE_NP[dt]).reshape(ov.shape), ov)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), oi)
+
+
+def test_compress24_counts_violations():
+    mcg = need_gpu()
+    rng = np.random.default_rng(1)
+    M, K = 40, 256
+    A = rng.integers(-2, 3, (M, K)).astype(np.int8)
+    vals = torch.zeros((M, K // 2), dtype=torch.int8, device="cuda")
+    idx = torch.zeros((M, K // 32), dtype=torch.int32, device="cuda")
+    viol = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    mcg.compress24("i8", M, K, dev(A), K, vals, K // 2, idx, K // 32, viol)
+    torch.cuda.synchronize()
+    ov, oi, ovio = oracle.compress24("i8", A)
+    assert ovio > 0 and int(viol.item()) == ovio
+    assert np.array_equal(vals.cpu().numpy(), ov)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), oi)
+
+
+def run_sparse(mcg, dt, layB, M, N, K, A_dense, B, C=None, alpha=1.0, beta=0.0, via_device=True):
+    """Compress A (device compressor) and run gemm_sparse24; returns D, vals, idx."""
+    nw = (K + 31) // 32
+    if via_device:
+        vals = torch.empty((M, K // 2), dtype=torch.int16, device="cuda")
+        idx = torch.empty((M, nw), dtype=torch.int32, device="cuda")
+        viol = torch.zeros((1,), dtype=torch.int32, device="cuda")
+        mcg.compress24(dt, M, K, dev(A_dense), K, vals, K // 2, idx, nw, viol)
+    else:
+        v, i, _ = oracle.compress24(dt, A_dense)
+        vals, idx = dev(v), dev(i.view(np.int32))
+    D = torch.full((M, N), float("nan"), device="cuda")
+    mcg.gemm_sparse24(dt, dt, layB, M, N, K, vals, K // 2, idx, nw, dev(B.codes), B.ld,
+                      None if C is None else dev(C), D, N, "f32", alpha, beta)
+    torch.cuda.synchronize()
+    if via_device:
+        assert int(viol.item()) == 0
+    return D.cpu().numpy(), vals, idx
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("layB", ["k_contig", "mn_contig"])
+@pytest.mark.parametrize("shape", [(256, 256, 256), (300, 200, 388), (17, 33, 4), (130, 140, 1000)])
+def test_sparse_gemm_matches_oracle(dt, layB, shape):
+    mcg = need_gpu()
+    M, N, K = shape
+    say(f"sparse {dt} B {layB} {shape}")
+    A = W.sparse24_dense(dt, M, K)
+    B = W.operand("B", dt, K, N, "normal", layB, seed=11)
+    C = W.c_matrix(M, N, "normal", seed=12)
+    d, vals, idx = run_sparse(mcg, dt, layB, M, N, K, A, B, C, 0.75, 1.0)
+    v, i, _ = oracle.compress24(dt, A)
+    ref, s = oracle.gemm_sparse24(dt, dt, layB, M, N, K, v, i, B.codes, B.ld, C, N, 0.75, 1.0)
+    compare(dt, d, ref, s, K, 0.75, beta=1.0, c=C, what=f"sparse {dt} {layB} {shape}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_sparse_small_integers_bit_exact(dt):
+    mcg = need_gpu()
+    M, N, K = 160, 192, 512
+    A = W.sparse24_dense(dt, M, K, dist="smallint8")
+    B = W.operand("B", dt, K, N, "smallint8", "k_contig", seed=13)
+    d, _, _ = run_sparse(mcg, dt, "k_contig", M, N, K, A, B)
+    v, i, _ = oracle.compress24(dt, A)
+    ref, _ = oracle.gemm_sparse24(dt, dt, "k_contig", M, N, K, v, i, B.codes, B.ld)
+    assert np.array_equal(d, ref)
+
+
+def test_sparse_with_host_compressed_operand():
+    """Operand compressed by the oracle (not the device) gives the same result."""
+    mcg = need_gpu()
+    M, N, K = 256, 128, 512
+    A = W.sparse24_dense("bf16", M, K)
+    B = W.operand("B", "bf16", K, N, "normal", "k_contig", seed=14)
+    d1, _, _ = run_sparse(mcg, "bf16", "k_contig", M, N, K, A, B)
+    d2, _, _ = run_sparse(mcg, "bf16", "k_contig", M, N, K, A, B, via_device=False)
+    assert np.array_equal(d1, d2)
+
+
+def test_full_size_sparse_configuration():
+    """2:4 bf16 8192^3 in the benchmark's launch configuration; sampled outputs."""
+    mcg = need_gpu()
+    wl = [w for w in W.standard_workloads() if w.sparse][0]
+    M, N, K = wl.M, wl.N, wl.K
+    say(f"full-size: {wl.name}")
+    A = W.sparse24_dense("bf16", M, K)
+    B = W.operand("B", "bf16", K, N, "normal", "k_contig")
+    d, vals, idx = run_sparse(mcg, "bf16", "k_contig", M, N, K, A, B)
+    assert not np.isnan(d).any()
+    rows, cols = W.sample_coords(M, N, n_random=4096, full_rows=(0, M - 1), full_cols=(N // 3,))
+    # the device-compressed operand equals the oracle's on sampled rows
+    v, i, _ = oracle.compress24("bf16", A[np.unique(rows)])
+    assert np.array_equal(vals.cpu().numpy().view(np.uint16)[np.unique(rows)], v)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32)[np.unique(rows)], i)
+    ref, s = oracle.gemm_float("bf16", "bf16", "k_contig", "k_contig", M, N, K, A, K, B.codes, B.ld,
+                               rows=rows, cols=cols)
+    r = compare("bf16", d[rows, cols], ref, s, K, what=wl.name)
+    say(f"  sampled {r['n']} outputs ok; max |delta|/bound = {r['max_ratio']}")
