@@ -66,12 +66,26 @@ enum : int { DT_BF16 = 0, DT_F16 = 1, DT_I8 = 2, DT_E4M3 = 3, DT_E5M2 = 4 };
 __host__ __device__ constexpr int f8fmt(int dt) { return dt == DT_E5M2 ? 1 : 0; }
 
 // ------------------------------------------------------------------ dense ops
-// Every op multiplies a 16x16 output tile by one K-step.  LANE_BYTES is the
-// fragment size per lane per operand; K_STEP the K extent of one instruction.
-// mma(p, q, acc): acc += P.Q with P/Q in the layout described above.
+// Every op multiplies a 16x16 output tile by one K-step.  STEPS is the number
+// of K-steps in a 128-byte K tile.  mma(p, q, acc): acc += P.Q with P/Q in the
+// layout described above.  frag_a / frag_b read the A (instruction Q) and B
+// (instruction P) fragments of K-step s from LDS through a FragReader R.
 
-struct OpBF16 {
-  static constexpr int ELEM_BYTES = 2, LANE_BYTES = 16, K_STEP = 32;
+struct DirectFrags {
+  template <class R>
+  __device__ static __forceinline__ typename R::frag_t frag_a(const __attribute__((address_space(3))) char* t,
+                                                               int rb, int s, int lane) {
+    return R::read(t, rb, s, lane);
+  }
+  template <class R>
+  __device__ static __forceinline__ typename R::frag_t frag_b(const __attribute__((address_space(3))) char* t,
+                                                               int rb, int s, int lane) {
+    return R::read(t, rb, s, lane);
+  }
+};
+
+struct OpBF16 : DirectFrags {
+  static constexpr int ELEM_BYTES = 2, LANE_BYTES = 16, K_STEP = 32, STEPS = 2;
   static constexpr bool INT_ACC = false;
   using frag_t = i32x4;
   using acc_t = f32x4;
@@ -80,8 +94,8 @@ struct OpBF16 {
   }
 };
 
-struct OpF16 {
-  static constexpr int ELEM_BYTES = 2, LANE_BYTES = 16, K_STEP = 32;
+struct OpF16 : DirectFrags {
+  static constexpr int ELEM_BYTES = 2, LANE_BYTES = 16, K_STEP = 32, STEPS = 2;
   static constexpr bool INT_ACC = false;
   using frag_t = i32x4;
   using acc_t = f32x4;
@@ -90,8 +104,8 @@ struct OpF16 {
   }
 };
 
-struct OpI8 {
-  static constexpr int ELEM_BYTES = 1, LANE_BYTES = 16, K_STEP = 64;
+struct OpI8 : DirectFrags {
+  static constexpr int ELEM_BYTES = 1, LANE_BYTES = 16, K_STEP = 64, STEPS = 2;
   static constexpr bool INT_ACC = true;
   using frag_t = i32x4;
   using acc_t = i32x4;
@@ -100,15 +114,66 @@ struct OpI8 {
   }
 };
 
-// FP = format of operand P, FQ = format of operand Q (0 = E4M3, 1 = E5M2).
+// Native fp8: FP = format of operand P (the B tensor), FQ = format of Q (A tensor);
+// 0 = E4M3, 1 = E5M2.
 template <int FP, int FQ>
-struct OpF8 {
-  static constexpr int ELEM_BYTES = 1, LANE_BYTES = 32, K_STEP = 128;
+struct OpF8 : DirectFrags {
+  static constexpr int ELEM_BYTES = 1, LANE_BYTES = 32, K_STEP = 128, STEPS = 1;
   static constexpr bool INT_ACC = false;
   using frag_t = i32x8;
   using acc_t = f32x4;
   __device__ static __forceinline__ acc_t mma(frag_t p, frag_t q, acc_t c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(p, q, c, FP, FQ, 0, 0, 0, 0);
+  }
+};
+
+// Eight fp8 codes (two dwords) -> eight bf16 values, exactly: the hardware
+// conversion to fp32 is exact for every finite fp8 value, and an fp32 that
+// came from fp8 has at most 4 significant bits, so its upper 16 bits are the
+// bf16 encoding of the same value.
+template <int FMT>
+__device__ __forceinline__ i32x4 fp8x8_to_bf16x8(i32x2 v) {
+  i32x4 r;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    f32x2 lo, hi;
+    if constexpr (FMT == 0) {
+      lo = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], false);
+      hi = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], true);
+    } else {
+      lo = __builtin_amdgcn_cvt_pk_f32_bf8(v[w], false);
+      hi = __builtin_amdgcn_cvt_pk_f32_bf8(v[w], true);
+    }
+    // select the upper halves: result = (hi16(y) << 16) | hi16(x)
+    r[2 * w] = (int)__builtin_amdgcn_perm(bit_cast<uint32_t>(lo.y), bit_cast<uint32_t>(lo.x), 0x07060302u);
+    r[2 * w + 1] = (int)__builtin_amdgcn_perm(bit_cast<uint32_t>(hi.y), bit_cast<uint32_t>(hi.x), 0x07060302u);
+  }
+  return r;
+}
+
+// Widened fp8: the fp8 tiles are staged in LDS as fp8, each lane reads eight
+// consecutive K values per K-step, converts them exactly to bf16 and issues the
+// bf16 instruction (full fp32-class accumulation).  FA/FB = formats of the A/B
+// tensors.  K-step s of lane group g covers tile K bytes [32s + 8g, +8).
+template <int FA, int FB>
+struct OpF8W {
+  static constexpr int ELEM_BYTES = 1, LANE_BYTES = 8, K_STEP = 32, STEPS = 4;
+  static constexpr bool INT_ACC = false;
+  using frag_t = i32x4;
+  using acc_t = f32x4;
+  template <class R>
+  __device__ static __forceinline__ frag_t frag_a(const __attribute__((address_space(3))) char* t, int rb,
+                                                  int s, int lane) {
+    return fp8x8_to_bf16x8<FA>(R::run8(t, rb, 32 * s + 8 * (lane >> 4), lane));
+  }
+  template <class R>
+  __device__ static __forceinline__ frag_t frag_b(const __attribute__((address_space(3))) char* t, int rb,
+                                                  int s, int lane) {
+    return fp8x8_to_bf16x8<FB>(R::run8(t, rb, 32 * s + 8 * (lane >> 4), lane));
+  }
+  __device__ static __forceinline__ acc_t mma(frag_t p, frag_t q, acc_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bit_cast<bf16x8>(p), bit_cast<bf16x8>(q), c, 0, 0, 0);
   }
 };
 

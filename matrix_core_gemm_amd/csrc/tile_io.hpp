@@ -170,6 +170,24 @@ struct FragReader {
     }
   }
 
+  // 8 bytes of K starting at K byte kb (multiple of 8) for row rb + (lane & 15);
+  // 8-bit elements only.
+  __device__ static __forceinline__ i32x2 run8(const lds_char* tile, int rb, int kb, int lane) {
+    static_assert(EB == 1, "8-byte K runs are used for 8-bit elements");
+    if constexpr (LAYOUT == LAYOUT_K) {
+      const int r = rb + (lane & 15);
+      const int c = kb >> 4;
+      return *(const __attribute__((address_space(3))) i32x2*)(
+          tile + r * G::W + ((c ^ swz<EB, LAYOUT, G::CPR>(r)) * 16) + (kb & 8));
+    } else {
+      const int L = lane & 15;
+      const int row = kb + (L >> 1);
+      const int byte = rb + 8 * (L & 1);
+      const int c = byte >> 4, w = byte & 15;
+      return lds_read_tr8(tile, row * G::W + ((c ^ swz<EB, LAYOUT, G::CPR>(row)) * 16) + w);
+    }
+  }
+
   __device__ static __forceinline__ frag_t read(const lds_char* tile, int rb, int s, int lane) {
     const int g = lane >> 4;
     if constexpr (LANE_BYTES == 16) {

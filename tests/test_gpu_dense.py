@@ -236,3 +236,43 @@ def test_full_size_configurations(wl):
         # run-to-run determinism of the exact path over the whole output
         d2 = sampled_check(mcg, wl)
         assert np.array_equal(d1, d2)
+
+
+# ------------------------------------------------ fp8 accumulation-precision cases
+
+def adversarial_fp8(M, N, K, dtA, dtB, seed=21):
+    """Per group of eight consecutive k: one product of magnitude 2^8 and seven
+    of magnitude 2^-6 (14 binades below), with random signs."""
+    big = {"e4m3": 16.0, "e5m2": 16.0}
+    rng = np.random.default_rng(seed)
+    k = np.arange(K)
+    Av = np.where(k % 8 == 0, big[dtA], 0.125)[None, :] * rng.choice([-1.0, 1.0], (M, K))
+    Bv = np.where(k % 8 == 0, big[dtB], 0.125)[:, None] * rng.choice([-1.0, 1.0], (K, N))
+    Aq, _ = W.quantize(torch.from_numpy(Av).float(), dtA)
+    Bq, _ = W.quantize(torch.from_numpy(Bv).float(), dtB)
+    As, lda = W.store(Aq, "A", "k_contig")
+    Bs, ldb = W.store(Bq, "B", "k_contig")
+    return W.codes_of(As, dtA), lda, W.codes_of(Bs, dtB), ldb
+
+
+@pytest.mark.parametrize("dtA,dtB", [("e4m3", "e4m3"), ("e4m3", "e5m2")])
+@pytest.mark.parametrize("K", [8, 65, 1000, 6143, 6144, 8192])
+def test_fp8_wide_dynamic_range_meets_bound(dtA, dtB, K):
+    """The bound must hold for every K, including where one product per
+    eight-element group dwarfs the others (the regime where the native fp8
+    instruction's short alignment window loses the small products)."""
+    mcg = need_gpu()
+    M, N = 32, 48
+    A, lda, B, ldb = adversarial_fp8(M, N, K, dtA, dtB)
+    d = run_dense(mcg, dtA, dtB, "k_contig", "k_contig", M, N, K, A, lda, B, ldb)
+    ref, s = oracle.gemm_float(dtA, dtB, "k_contig", "k_contig", M, N, K, A, lda, B, ldb)
+    r = compare(dtA, d, ref, s, K, what=f"fp8 dynamic range K={K}")
+    say(f"fp8 {dtA}x{dtB} K={K}: max |delta|/bound = {r['max_ratio']:.3f}")
+
+
+@pytest.mark.parametrize("dtA,dtB", [("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")])
+@pytest.mark.parametrize("layA,layB", LAYOUTS)
+def test_fp8_native_path_at_threshold(dtA, dtB, layA, layB):
+    """K = 6144: the first K served by the native fp8 instruction; full check."""
+    mcg = need_gpu()
+    check_case(mcg, dtA, dtB, layA, layB, 96, 80, 6144, pad=16)
