@@ -16,7 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "_libmcg.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["gemm_dense.hip", "gemm_sparse.hip", "api.cpp"]
+SOURCES = ["gemm_dense.hip", "gemm_fast.hip", "gemm_sparse.hip", "api.cpp"]
 HEADERS = ["arch_gfx950.hpp", "tile_io.hpp", "gemm_kernels.hpp"]
 
 # Packed fp32 VALU forms are disabled for all device code (hipcc's host pass

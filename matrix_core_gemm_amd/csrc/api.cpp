@@ -120,6 +120,8 @@ int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int6
   a.vec_cd = aligned_to(D, 16) && (!a.use_c || aligned_to(C, 16)) && ldc % 4 == 0;
   const bool aligned = K == 0 || (aligned_to(A, 16) && aligned_to(B, 16) && (lda * eb) % 16 == 0 &&
                                   (ldb * eb) % 16 == 0);
+  if (mcg::fast_path_ok(dtypeA, layoutA, layoutB, a, aligned))
+    return hip_status(mcg::launch_fast(dtypeA, dtypeB, layoutA, layoutB, a, (hipStream_t)stream));
   return hip_status(mcg::launch_dense(dtypeA, dtypeB, layoutA, layoutB, aligned, a, (hipStream_t)stream));
 }
 

@@ -40,9 +40,19 @@ struct CompressArgs {
   int64_t M, K, lda, lda_c, ld_idx;
 };
 
+// fp8 inputs: the native f8f6f4 instruction sums each group of eight products
+// keeping only about 13 bits below the group's largest product (measured on
+// gfx950), then accumulates groups with about 24 bits.  Its worst-case error is
+// then below 2^-10 * S + (K/8) * 2^-22 * S (S = sum |a b|), which is inside the
+// accuracy bound 4 * 2^-24 * (K + 2) * S once 7K/8 >= 4096.  Below this K the
+// fp8 operands are widened exactly to bf16 and multiplied on the bf16 path.
+constexpr int64_t FP8_NATIVE_MIN_K = 6144;
+
 // Enqueue the kernels; arguments were validated by the caller.
 hipError_t launch_dense(int dtA, int dtB, int layoutA, int layoutB, bool aligned, const DenseArgs& a,
                         hipStream_t s);
+bool fast_path_ok(int dtA, int layoutA, int layoutB, const DenseArgs& a, bool aligned);
+hipError_t launch_fast(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
 hipError_t launch_sparse(int dt, int layoutB, bool aligned, const SparseArgs& a, hipStream_t s);
 hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s);
 

@@ -29,10 +29,14 @@ struct TileGeom {
 };
 
 // Swizzle of the 16-byte chunk index within an LDS row.
-//  K-contiguous rows: 16 consecutive rows read at one logical chunk land on 16
-//  distinct chunk slots modulo 256 bytes and 8 consecutive rows on 8 distinct
-//  slots modulo 128 bytes (8-chunk rows: XOR with (r ^ r/8) mod 8; 16-chunk
-//  rows: XOR with r mod 16).
+//  LDS on gfx950 has 64 four-byte banks; measured: an 8-byte read (plain or
+//  transposing) serves lanes 0-31 and 32-63 in one cycle each when their
+//  addresses fall in distinct banks, and a 16-byte read of 16 rows x 128 bytes
+//  at one logical chunk per lane group is conflict-free when the chunk is
+//  XOR-ed with (row / 2) mod 8 (but not with (row ^ row/8) mod 8).
+//  K-contiguous rows: 8-chunk rows XOR with (r / 2) mod 8, so 16 consecutive
+//  rows land on 16 distinct 16-byte slots modulo 256 bytes; 16-chunk rows XOR
+//  with r mod 16.
 //  MN-contiguous rows read with ds_read_b64_tr_b16 (4 rows x 2 chunks per 16
 //  lanes) or ds_read_b64_tr_b8 (8 rows x 1 chunk per 16 lanes): XOR with the
 //  row's position inside that group, plus a half-row flip between the groups
@@ -40,7 +44,7 @@ struct TileGeom {
 template <int EB, int LAYOUT, int CPR>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (LAYOUT == LAYOUT_K) {
-    if constexpr (CPR == 8) return (row ^ (row >> 3)) & 7;
+    if constexpr (CPR == 8) return (row >> 1) & 7;
     else return row & (CPR - 1);
   } else if constexpr (EB == 2) {
     int f = 2 * (row & 3) | (8 * ((row >> 3) & 1));
