@@ -32,6 +32,27 @@ METRIC = "TFLOP/s (TOPS int8) at 8192³ per dtype + % of MI355X MFMA peak"
 PEAK = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "i8": 5000.0}
 HBM_PEAK_GBS = 8000.0
 
+# HBM bytes per launch of the dense bf16 8192^3 kernel, from two rocprofv3 --pmc
+# passes (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000; the factors make a plain 1 GiB
+# copy kernel read as 1 GiB).  Valid only for the kernel sources they were taken
+# with: when the hash of those sources differs, traffic is reported as null.
+KERNEL_SOURCES = ("gemm_fast.hip", "arch_gfx950.hpp", "gemm_kernels.hpp", "tile_io.hpp")
+TRAFFIC_MEASURED = {
+    "sources_sha256": "b9c1af37f5559cd1c11078412c0985afa92dd7397afe992a9315b796ad29e0de",
+    "read_bytes": 1851 * 2**20, "write_bytes": 324 * 2**20,
+}
+
+
+def measured_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "matrix_core_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != TRAFFIC_MEASURED["sources_sha256"]:
+        return None
+    return TRAFFIC_MEASURED["read_bytes"] + TRAFFIC_MEASURED["write_bytes"]
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -197,8 +218,10 @@ def main():
                                f"{len(names)} hot-path calls at {n}^3",
                    "M": M, "N": N, "K": K, "entries": names},
         "roofline": {"bound": "mfma", "achieved": value, "peak": PEAK["bf16"], "unit": "TFLOP/s",
-                     "frac": value / PEAK["bf16"], "traffic": None,
-                     "kernel": "gemm_dense_kernel (bf16)", "kernel_ms": ms.get(head)},
+                     "frac": value / PEAK["bf16"], "traffic": measured_traffic() if head == "bf16" and n == 8192 else None,
+                     "traffic_unit": "HBM bytes per launch",
+                     "algorithmic_bytes": (2 * M * K + 2 * K * N + 8 * M * N),
+                     "kernel": "mcg::fast::gemm_fast_kernel<BF16, 0, 0>", "kernel_ms": ms.get(head)},
         "cpu_baseline": cpu,
         "per_dtype": per,
     }
