@@ -178,6 +178,8 @@ int gemm_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int
   const bool aligned = K == 0 || (aligned_to(A_compressed, 16) && aligned_to(B, 16) &&
                                   aligned_to(A_index, 16) && (lda_c * 2) % 16 == 0 &&
                                   (ldb * 2) % 16 == 0 && (ld_idx * 4) % 16 == 0);
+  if (mcg::sparse_fast_ok(layoutB, a))
+    return hip_status(mcg::launch_sparse_fast(dtypeA, layoutB, a, (hipStream_t)stream));
   return hip_status(mcg::launch_sparse(dtypeA, layoutB, aligned, a, (hipStream_t)stream));
 }
 

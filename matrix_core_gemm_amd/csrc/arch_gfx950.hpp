@@ -199,6 +199,10 @@ __host__ __device__ constexpr int out_row(int lane, int r) { return 4 * (lane >>
 __host__ __device__ constexpr int out_col(int lane) { return lane & 15; }
 
 // ------------------------------------------------------------ LDS primitives
+// operand storage order along K: K-contiguous (A row-major, B column-major) or
+// MN-contiguous (A column-major, B row-major)
+enum : int { LAYOUT_K = 0, LAYOUT_MN = 1 };
+
 typedef __attribute__((address_space(3))) char lds_char;
 
 __device__ __forceinline__ i32x4 lds_read_b128(const lds_char* base, int off) {

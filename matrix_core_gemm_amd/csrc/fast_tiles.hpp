@@ -1,0 +1,164 @@
+// fast_tiles.hpp -- LDS tile geometry, HBM -> LDS loaders and LDS -> VGPR
+// fragment readers shared by the 256 x 256 dense and 2:4 sparse kernels.
+//
+// A tile holds, for one stage, KTB bytes of K of ROWS_MN rows (M rows of A or
+// N columns of B).  K-contiguous operands keep one LDS row per matrix row
+// (KTB bytes); MN-contiguous operands keep one LDS row per k (ROWS_MN
+// elements).  Rows are split in 16-byte chunks whose order is XOR-swizzled
+// per row so that the fragment reads are free of LDS bank conflicts (measured
+// with SQ_LDS_BANK_CONFLICT on gfx950 for exactly these access patterns):
+//   K-contiguous rows of CPR chunks: chunk ^= (row / (16 / CPR)) mod CPR
+//     (16 consecutive rows of one chunk land in 16 distinct 16-byte slots of
+//     the 256 bytes the 64 banks serve per cycle);
+//   MN-contiguous 16-bit rows (transposing 16-bit reads): chunk ^= 4 * (row mod 4);
+//   MN-contiguous 8-bit rows (transposing 8-bit reads): chunk ^= 2 * (row mod 8).
+// The swizzle is applied on the global side: each lane of a buffer_load ... lds
+// instruction fetches the global chunk that belongs at its (fixed) LDS slot.
+#pragma once
+#include "arch_gfx950.hpp"
+
+namespace mcg {
+namespace fast {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int NW = 4;                      // wavefronts per workgroup
+constexpr uint32_t BUF_OOB = 0x80000000u;  // buffer offset past every window: the load returns zeros
+
+template <int EB, int LAYOUT, int ROWS_MN, int KTB>
+struct Geom {
+  static constexpr int R = LAYOUT == LAYOUT_K ? ROWS_MN : KTB / EB;  // LDS rows
+  static constexpr int W = LAYOUT == LAYOUT_K ? KTB : ROWS_MN * EB;  // bytes per row
+  static constexpr int CPR = W / 16;
+  static constexpr int CHUNKS = R * CPR;
+  static constexpr int BYTES = R * W;
+};
+
+template <int EB, int LAYOUT, int CPR>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (LAYOUT == LAYOUT_K) {
+    static_assert(CPR == 2 || CPR == 4 || CPR == 8, "K-contiguous rows of 32, 64 or 128 bytes");
+    constexpr int SH = CPR == 2 ? 3 : CPR == 4 ? 2 : 1;  // log2(16 / CPR)
+    return (row >> SH) & (CPR - 1);
+  }
+  else if constexpr (EB == 2) return (4 * (row & 3)) & (CPR - 1);
+  else return (2 * (row & 7)) & (CPR - 1);
+}
+
+// Buffer resource over [base, base + bytes) built from wave-uniform values.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, (int)n, 0x00020000);
+}
+
+// HBM -> LDS loader of one operand tile: wave w, instruction i of a stage
+// writes LDS bytes [(i * NW + w) * 1024, +1024) of that stage's tile.  K is
+// counted in elements of this operand.
+template <int EB, int LAYOUT, int ROWS_MN, int KTB>
+struct Loader {
+  using G = Geom<EB, LAYOUT, ROWS_MN, KTB>;
+  static constexpr int INSTR = G::CHUNKS / (64 * NW);
+  static_assert(G::CHUNKS % (64 * NW) == 0, "tile must split into whole wave instructions");
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off[INSTR];
+  int kpos[INSTR];
+  uint32_t kstride;
+
+  __device__ __forceinline__ void init(const char* base, uint32_t bytes, int64_t ld, int wave, int lane) {
+    rsrc = make_rsrc(base, bytes);
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+      const int q = (i * NW + wave) * 64 + lane;
+      const int r = q / G::CPR, pc = q % G::CPR;
+      const int lc = pc ^ swz<EB, LAYOUT, G::CPR>(r);
+      off[i] = (uint32_t)(r * ld * EB + lc * 16);
+      kpos[i] = LAYOUT == LAYOUT_K ? lc * (16 / EB) : r;
+    }
+    kstride = LAYOUT == LAYOUT_K ? (uint32_t)KTB : (uint32_t)(KTB / EB * ld * EB);
+  }
+
+  __device__ __forceinline__ void issue(lds_char* dst, int kt, int64_t K, int wave) const {
+    const int64_t k0 = (int64_t)kt * (KTB / EB);
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+      uint32_t o = off[i] + (uint32_t)kt * kstride;
+      if constexpr (LAYOUT == LAYOUT_K) o = (k0 + kpos[i] < K) ? o : BUF_OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(dst + (i * NW + wave) * 1024), 16, o, 0, 0, 0);
+    }
+  }
+};
+
+// LDS -> VGPR fragments of the 32 rows [rb, rb + 32) of a tile.  Lane group
+// g = lane >> 5 reads 16 bytes of K starting at byte kb (chosen by the caller
+// per lane group); MN-contiguous tiles gather them with transposing reads.
+template <int EB, int LAYOUT, int ROWS_MN, int KTB>
+struct Reader {
+  using G = Geom<EB, LAYOUT, ROWS_MN, KTB>;
+  __device__ static __forceinline__ int addr(int row, int byte) {
+    const int c = byte >> 4;
+    return row * G::W + ((c ^ swz<EB, LAYOUT, G::CPR>(row)) << 4) + (byte & 15);
+  }
+  __device__ static __forceinline__ i32x4 read16k(const lds_char* tile, int rb, int kb, int lane) {
+    if constexpr (LAYOUT == LAYOUT_K) {
+      return lds_read_b128(tile, addr(rb + (lane & 31), kb));
+    } else if constexpr (EB == 2) {
+      // 8 k values = 2 transposed reads of 4 k rows; sub-group (lane >> 4) & 1
+      // serves the second 16 columns of the 32-row block
+      const int L = lane & 15;
+      const int col = rb + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+      const int row = kb / 2 + (L >> 2);
+      const i32x2 lo = lds_read_tr16(tile, addr(row, 2 * col));
+      const i32x2 hi = lds_read_tr16(tile, addr(row + 4, 2 * col));
+      return i32x4{lo.x, lo.y, hi.x, hi.y};
+    } else {
+      // 16 k values = 2 transposed reads of 8 k rows
+      const int L = lane & 15;
+      const int col = rb + 16 * ((lane >> 4) & 1) + 8 * (L & 1);
+      const int row = kb + (L >> 1);
+      const i32x2 lo = lds_read_tr8(tile, addr(row, col));
+      const i32x2 hi = lds_read_tr8(tile, addr(row + 8, col));
+      return i32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+  }
+  // dense 32x32 instructions: lane group g owns tile K bytes [32g, 32g + 32);
+  // sub-step s is its half [32g + 16s, +16)
+  __device__ static __forceinline__ i32x4 read16(const lds_char* tile, int rb, int s, int lane) {
+    return read16k(tile, rb, 32 * (lane >> 5) + 16 * s, lane);
+  }
+  __device__ static __forceinline__ i32x8 read32(const lds_char* tile, int rb, int lane) {
+    const i32x4 a = read16(tile, rb, 0, lane), b = read16(tile, rb, 1, lane);
+    return i32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  }
+};
+
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup -> output tile.  Workgroups are dispatched round-robin over the 8
+// XCDs; the sequence is permuted so that the workgroups of one XCD take
+// consecutive logical tiles, which are ordered in groups of GROUP tile rows
+// (column-major inside a group) so that concurrently resident workgroups share
+// A and B panels in their XCD's L2.
+template <int GROUP>
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int nwg = tiles_m * tiles_n;
+  int pid = blockIdx.x;
+  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  const int tiles_in_group = GROUP * tiles_n;
+  const int gid = pid / tiles_in_group;
+  const int first_m = gid * GROUP;
+  const int gsize = min(tiles_m - first_m, GROUP);
+  tm = __builtin_amdgcn_readfirstlane(first_m + (pid % tiles_in_group) % gsize);
+  tn = __builtin_amdgcn_readfirstlane((pid % tiles_in_group) / gsize);
+}
+
+}  // namespace fast
+}  // namespace mcg

@@ -34,19 +34,16 @@
 // Preconditions (checked on the host): 16-byte aligned operands, K * elem_bytes
 // and ld * elem_bytes multiples of 16, M, N >= 256, and each workgroup's
 // operand window below 2 GiB (32-bit buffer offsets).
+#include "fast_tiles.hpp"
 #include "gemm_kernels.hpp"
-#include "tile_io.hpp"
 
 namespace mcg {
 namespace fast {
 
 constexpr int KTB = 64;  // bytes of K per LDS row and stage
 constexpr int NST = 5;   // LDS stages
-constexpr int BM = 256, BN = 256, NW = 4;
-constexpr uint32_t BUF_OOB = 0x80000000u;
+constexpr int BM = 256, BN = 256;
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 // ------------------------------------------------------------- 32x32 ops
 // P (first operand) = B fragment, Q = A fragment.  Lane group g = lane >> 5 of
@@ -113,122 +110,20 @@ struct F8W {
   }
 };
 
-// ----------------------------------------------------------- LDS geometry
-template <int EB, int LAYOUT, int ROWS_MN>
-struct Geom {
-  static constexpr int R = LAYOUT == LAYOUT_K ? ROWS_MN : KTB / EB;  // LDS rows
-  static constexpr int W = LAYOUT == LAYOUT_K ? KTB : ROWS_MN * EB;  // bytes per row
-  static constexpr int CPR = W / 16;
-  static constexpr int CHUNKS = R * CPR;
-  static constexpr int BYTES = R * W;
-};
-
-template <int EB, int LAYOUT, int CPR>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (LAYOUT == LAYOUT_K) return (row >> 2) & 3;
-  else if constexpr (EB == 2) return (4 * (row & 3)) & (CPR - 1);
-  else return (2 * (row & 7)) & (CPR - 1);
-}
-
-// HBM -> LDS loader of one operand: wave w, instruction i of a stage writes
-// LDS bytes [(i * NW + w) * 1024, +1024) of that stage's tile.
-template <int EB, int LAYOUT, int ROWS_MN>
-struct Loader {
-  using G = Geom<EB, LAYOUT, ROWS_MN>;
-  static constexpr int INSTR = G::CHUNKS / (64 * NW);
-  static_assert(G::CHUNKS % (64 * NW) == 0, "tile must split into whole wave instructions");
-  __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t off[INSTR];
-  int kpos[INSTR];
-  uint32_t kstride;
-
-  __device__ __forceinline__ void init(const char* base, uint32_t bytes, int64_t ld, int wave, int lane) {
-    const uint64_t b = (uint64_t)base;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-    rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, (int)n, 0x00020000);
-#pragma unroll
-    for (int i = 0; i < INSTR; ++i) {
-      const int q = (i * NW + wave) * 64 + lane;
-      const int r = q / G::CPR, pc = q % G::CPR;
-      const int lc = pc ^ swz<EB, LAYOUT, G::CPR>(r);
-      off[i] = (uint32_t)(r * ld * EB + lc * 16);
-      kpos[i] = LAYOUT == LAYOUT_K ? lc * (16 / EB) : r;
-    }
-    kstride = LAYOUT == LAYOUT_K ? (uint32_t)KTB : (uint32_t)(KTB / EB * ld * EB);
-  }
-
-  __device__ __forceinline__ void issue(lds_char* dst, int kt, int64_t K, int wave) const {
-    const int64_t k0 = (int64_t)kt * (KTB / EB);
-#pragma unroll
-    for (int i = 0; i < INSTR; ++i) {
-      uint32_t o = off[i] + (uint32_t)kt * kstride;
-      if constexpr (LAYOUT == LAYOUT_K) o = (k0 + kpos[i] < K) ? o : BUF_OOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc, (__attribute__((address_space(3))) void*)(dst + (i * NW + wave) * 1024), 16, o, 0, 0, 0);
-    }
-  }
-};
-
-// LDS -> VGPR fragments of the 32 rows [rb, rb + 32): read16 returns sub-step
-// s (16 bytes of K), read32 both sub-steps.
-template <int EB, int LAYOUT, int ROWS_MN>
-struct Reader {
-  using G = Geom<EB, LAYOUT, ROWS_MN>;
-  __device__ static __forceinline__ int addr(int row, int byte) {
-    const int c = byte >> 4;
-    return row * G::W + ((c ^ swz<EB, LAYOUT, G::CPR>(row)) << 4) + (byte & 15);
-  }
-  __device__ static __forceinline__ i32x4 read16(const lds_char* tile, int rb, int s, int lane) {
-    const int g = lane >> 5;
-    if constexpr (LAYOUT == LAYOUT_K) {
-      return lds_read_b128(tile, addr(rb + (lane & 31), 32 * g + 16 * s));
-    } else if constexpr (EB == 2) {
-      // 8 k values = 2 transposed reads of 4 k rows; sub-group (lane >> 4) & 1
-      // serves the second 16 columns of the 32-row block
-      const int L = lane & 15;
-      const int col = rb + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
-      const int row = 16 * g + 8 * s + (L >> 2);
-      const i32x2 lo = lds_read_tr16(tile, addr(row, 2 * col));
-      const i32x2 hi = lds_read_tr16(tile, addr(row + 4, 2 * col));
-      return i32x4{lo.x, lo.y, hi.x, hi.y};
-    } else {
-      // 16 k values = 2 transposed reads of 8 k rows
-      const int L = lane & 15;
-      const int col = rb + 16 * ((lane >> 4) & 1) + 8 * (L & 1);
-      const int row = 32 * g + 16 * s + (L >> 1);
-      const i32x2 lo = lds_read_tr8(tile, addr(row, col));
-      const i32x2 hi = lds_read_tr8(tile, addr(row + 8, col));
-      return i32x4{lo.x, lo.y, hi.x, hi.y};
-    }
-  }
-  __device__ static __forceinline__ i32x8 read32(const lds_char* tile, int rb, int lane) {
-    const i32x4 a = read16(tile, rb, 0, lane), b = read16(tile, rb, 1, lane);
-    return i32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  }
-};
-
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 template <class Op, int LA, int LB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_fast_kernel(DenseArgs p) {
   constexpr int EB = Op::EB;
   constexpr int WT = 4;  // 32 x 32 instruction tiles per wave along m and n
-  using GA = Geom<EB, LA, BM>;
-  using GB = Geom<EB, LB, BN>;
-  using RA = Reader<EB, LA, BM>;
-  using RB = Reader<EB, LB, BN>;
+  using GA = Geom<EB, LA, BM, KTB>;
+  using GB = Geom<EB, LB, BN, KTB>;
+  using RA = Reader<EB, LA, BM, KTB>;
+  using RB = Reader<EB, LB, BN, KTB>;
   using acc_t = typename Op::acc_t;
   using v4 = typename std::conditional<Op::INT_ACC, i32x4, f32x4>::type;
   using s1 = typename std::conditional<Op::INT_ACC, int, float>::type;
   constexpr int STAGE = GA::BYTES + GB::BYTES;
-  constexpr int PER_TILE = Loader<EB, LA, BM>::INSTR + Loader<EB, LB, BN>::INSTR;  // loads per wave
+  constexpr int PER_TILE = Loader<EB, LA, BM, KTB>::INSTR + Loader<EB, LB, BN, KTB>::INSTR;  // loads per wave
   static_assert(PER_TILE == 8, "vmcnt bookkeeping assumes 8 loads per wave per K tile");
 
   __shared__ __attribute__((aligned(1024))) char smem_raw[NST * STAGE];
@@ -238,21 +133,12 @@ void gemm_fast_kernel(DenseArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // XCD-aware, grouped tile order
-  const int nwg = p.tiles_m * p.tiles_n;
-  int pid = blockIdx.x;
-  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
-  const int group = 4;
-  const int tiles_in_group = group * p.tiles_n;
-  const int gid = pid / tiles_in_group;
-  const int first_m = gid * group;
-  const int gsize = min(p.tiles_m - first_m, group);
-  const int tm = __builtin_amdgcn_readfirstlane(first_m + (pid % tiles_in_group) % gsize);
-  const int tn = __builtin_amdgcn_readfirstlane((pid % tiles_in_group) / gsize);
+  int tm, tn;
+  tile_coords<4>(p.tiles_m, p.tiles_n, tm, tn);  // XCD-aware, grouped tile order
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-  Loader<EB, LA, BM> la;
-  Loader<EB, LB, BN> lb;
+  Loader<EB, LA, BM, KTB> la;
+  Loader<EB, LB, BN, KTB> lb;
   if constexpr (LA == LAYOUT_K)
     la.init(p.A + m0 * p.lda * EB, (uint32_t)(min(p.M - m0, (int64_t)BM) * p.lda * EB), p.lda, wave, lane);
   else

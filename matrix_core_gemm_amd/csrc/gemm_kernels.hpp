@@ -54,6 +54,8 @@ hipError_t launch_dense(int dtA, int dtB, int layoutA, int layoutB, bool aligned
 bool fast_path_ok(int dtA, int layoutA, int layoutB, const DenseArgs& a, bool aligned);
 hipError_t launch_fast(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
 hipError_t launch_sparse(int dt, int layoutB, bool aligned, const SparseArgs& a, hipStream_t s);
+bool sparse_fast_ok(int layoutB, const SparseArgs& a);
+hipError_t launch_sparse_fast(int dt, int layoutB, const SparseArgs& a, hipStream_t s);
 hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s);
 
 }  // namespace mcg

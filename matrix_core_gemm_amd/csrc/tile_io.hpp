@@ -15,7 +15,6 @@ namespace mcg {
 
 constexpr int KT_BYTES = 128;  // bytes of K per tile row
 
-enum : int { LAYOUT_K = 0, LAYOUT_MN = 1 };
 
 // KTB: bytes of K per tile row (128 for the dense kernels).
 template <int EB, int LAYOUT, int ROWS_MN, int KTB = KT_BYTES>

@@ -85,9 +85,55 @@ def test_sparse_gemm_matches_oracle(dt, layB, shape):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("layB", ["k_contig", "mn_contig"])
+@pytest.mark.parametrize("shape,pads", [
+    ((300, 520, 400), (8, 3, 16)),     # ragged M and N, K % 32 == 16 (partial last stage)
+    ((512, 768, 1024), (0, 0, 0)),     # whole tiles, unpadded
+    ((257, 304, 16), (16, 1, 8)),      # one stage, one row past a tile
+    ((600, 256, 2000), (24, 5, 40)),   # many stages, odd index stride
+])
+def test_sparse_256_tile_path(dt, layB, shape, pads):
+    """Shapes taken by the 256 x 256 sparse kernel (M, N >= 256, K % 16 == 0, aligned),
+    with padded leading dimensions of the kept values, the index and B."""
+    mcg = need_gpu()
+    M, N, K = shape
+    pad_v, pad_i, pad_b = pads
+    say(f"sparse 256-tile {dt} B {layB} {shape} pads {pads}")
+    A = W.sparse24_dense(dt, M, K, seed=21)
+    B = W.operand("B", dt, K, N, "normal", layB, seed=22,
+                  ld=(K if layB == "k_contig" else N) + pad_b)
+    C = W.c_matrix(M, N, "normal", seed=23)
+    v, i, _ = oracle.compress24(dt, A)
+    nw = (K + 31) // 32
+    lda_c, ld_idx = K // 2 + pad_v, nw + pad_i
+    vp = np.zeros((M, lda_c), v.dtype)
+    vp[:, :K // 2] = v
+    ip = np.full((M, ld_idx), 0xFFFFFFFF, np.uint32)  # padding words are never read
+    ip[:, :nw] = i
+    D = torch.full((M, N), float("nan"), device="cuda")
+    mcg.gemm_sparse24(dt, dt, layB, M, N, K, dev(vp), lda_c, dev(ip.view(np.int32)), ld_idx,
+                      dev(B.codes), B.ld, dev(C), D, N, "f32", 1.5, -0.5)
+    torch.cuda.synchronize()
+    ref, s = oracle.gemm_sparse24(dt, dt, layB, M, N, K, v, i, B.codes, B.ld, C, N, 1.5, -0.5)
+    compare(dt, D.cpu().numpy(), ref, s, K, 1.5, beta=-0.5, c=C, what=f"sparse256 {dt} {layB} {shape}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_sparse_small_integers_bit_exact(dt):
     mcg = need_gpu()
     M, N, K = 160, 192, 512
+    _sparse_smallint_case(mcg, dt, M, N, K)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_sparse_small_integers_bit_exact_256_tiles(dt):
+    """The 256 x 256 kernel: every partial sum is an exact small integer, so the
+    result must equal the oracle bit for bit (pins the operand and index layouts)."""
+    mcg = need_gpu()
+    _sparse_smallint_case(mcg, dt, 512, 512, 1024)
+
+
+def _sparse_smallint_case(mcg, dt, M, N, K):
     A = W.sparse24_dense(dt, M, K, dist="smallint8")
     B = W.operand("B", dt, K, N, "smallint8", "k_contig", seed=13)
     d, _, _ = run_sparse(mcg, dt, "k_contig", M, N, K, A, B)
