@@ -5,32 +5,31 @@
 // Models of AMD Matrix Cores", Section 2, Eq. (1), tiled over K as in "CDNA3
 // dense MFMA builtins", Using MFMA builtins as a compute policy); what differs
 // is the mapping onto CDNA4:
-//   - 256 x 256 output tile per workgroup of 4 wavefronts (one per SIMD); each
-//     wavefront owns a 128 x 128 sub-tile = 4 x 4 instructions of 32 x 32
-//     (all 256 accumulator registers of its lanes), so each operand fragment
-//     read from LDS feeds 4 instructions.
+//   - 256 x 256 output tile per workgroup of 8 wavefronts, two per SIMD
+//     (wavefronts w and w + 4 share a SIMD, measured).  Each wavefront owns a
+//     128 x 64 sub-tile = 4 x 2 instructions of 32 x 32 (128 accumulator
+//     registers per lane).
 //   - K is staged in tiles of 64 bytes per row (32 bf16 / 64 8-bit values) in
-//     a ring of 5 LDS stages of 32 KiB (A and B); HBM -> LDS uses
-//     buffer_load ... lds (16 bytes per lane, no VGPRs), issued 3 K tiles ahead
-//     of use.  The XOR swizzle of the LDS rows is folded into the global
-//     address each lane loads; lanes whose chunk lies outside the matrix get
-//     an out-of-range offset and the buffer unit writes zeros.
-//   - the instructions of a K tile are split in two halves around the
-//     workgroup barrier; for 16-byte fragments (bf16, f16, int8) the next K
-//     tile's first-half fragments are read from LDS while the second half
-//     executes (two 32-VGPR fragment sets).
-//   - epilogue: for interior tiles, straight-line code reads C in four batches
-//     of 16 vector loads per lane (so the loads overlap) and stores
-//     D = alpha * acc + beta * C (16 bytes per lane per
-//     row segment, thanks to issuing each instruction with the B fragment as its
-//     first operand); edge tiles use per-element bounds.
+//     a ring of 5 LDS stages of 32 KiB (A and B), filled by buffer_load ... lds
+//     (16 bytes per lane, no VGPRs) 4 K tiles ahead of use.  The XOR swizzle
+//     of the LDS rows is folded into the global address each lane loads;
+//     chunks outside the matrix get an out-of-range offset and the buffer unit
+//     writes zeros.
+//   - ping-pong schedule: the two wavefronts of a SIMD alternate between a
+//     multiply phase (only matrix instructions, on fragments already in
+//     registers) and a memory phase (LDS -> register reads of the next K
+//     tile's fragments and the DMA issues for a future K tile), separated by
+//     workgroup barriers, so that one of them keeps the SIMD's matrix core
+//     busy while the other waits on memory.  Wavefronts 0-3 multiply K tile t
+//     in slot 2t, wavefronts 4-7 in slot 2t + 1; wavefronts 4-7 issue the A
+//     tile DMAs, wavefronts 0-3 the B tile DMAs.
+//   - epilogue: for interior tiles, straight-line code reads C in batches of
+//     16 vector loads per lane (so the loads overlap) and stores
+//     D = alpha * acc + beta * C (16 bytes per lane per row segment, thanks to
+//     issuing each instruction with the B fragment as its first operand); edge
+//     tiles use per-element bounds.
 //   - the 8 XCDs receive workgroups round-robin; the tile sequence is permuted
 //     so that the workgroups resident on one XCD cover a compact block of tiles.
-// LDS swizzles were chosen by measuring SQ_LDS_BANK_CONFLICT for the exact
-// access patterns on an MI355X (all conflict-free):
-//   K-contiguous rows (64 bytes, 4 chunks): chunk ^= (row / 4) mod 4;
-//   MN-contiguous 16-bit rows (transposing 16-bit reads): chunk ^= 4 * (row mod 4);
-//   MN-contiguous 8-bit rows (transposing 8-bit reads): chunk ^= 2 * (row mod 8).
 // Preconditions (checked on the host): 16-byte aligned operands, K * elem_bytes
 // and ld * elem_bytes multiples of 16, M, N >= 256, and each workgroup's
 // operand window below 2 GiB (32-bit buffer offsets).
@@ -40,9 +39,11 @@
 namespace mcg {
 namespace fast {
 
-constexpr int KTB = 64;  // bytes of K per LDS row and stage
-constexpr int NST = 5;   // LDS stages
+constexpr int KTB = 64;      // bytes of K per LDS row and stage
+constexpr int NST = 5;       // LDS stages
+constexpr int PD = NST - 1;  // DMA prefetch distance in K tiles
 constexpr int BM = 256, BN = 256;
+constexpr int THREADS = 512;
 
 
 // ------------------------------------------------------------- 32x32 ops
@@ -111,210 +112,201 @@ struct F8W {
 };
 
 template <class Op, int LA, int LB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_fast_kernel(DenseArgs p) {
   constexpr int EB = Op::EB;
-  constexpr int WT = 4;  // 32 x 32 instruction tiles per wave along m and n
+  constexpr int S = Op::SUBSTEPS;
+  constexpr int WTM = 4, WTN = 2;  // 32 x 32 instruction tiles per wave along m and n
   using GA = Geom<EB, LA, BM, KTB>;
   using GB = Geom<EB, LB, BN, KTB>;
   using RA = Reader<EB, LA, BM, KTB>;
   using RB = Reader<EB, LB, BN, KTB>;
+  using LdA = Loader<EB, LA, BM, KTB>;
+  using LdB = Loader<EB, LB, BN, KTB>;
   using acc_t = typename Op::acc_t;
+  using frag_t = typename Op::frag_t;
   using v4 = typename std::conditional<Op::INT_ACC, i32x4, f32x4>::type;
   using s1 = typename std::conditional<Op::INT_ACC, int, float>::type;
   constexpr int STAGE = GA::BYTES + GB::BYTES;
-  constexpr int PER_TILE = Loader<EB, LA, BM, KTB>::INSTR + Loader<EB, LB, BN, KTB>::INSTR;  // loads per wave
-  static_assert(PER_TILE == 8, "vmcnt bookkeeping assumes 8 loads per wave per K tile");
+  static_assert(LdA::INSTR == 4 && LdB::INSTR == 4, "vmcnt bookkeeping assumes 4 loads per wave per K tile");
 
   __shared__ __attribute__((aligned(1024))) char smem_raw[NST * STAGE];
   lds_char* smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int grp = wave >> 2;  // 0: multiplies in even slots and loads B; 1: odd slots, loads A
+  const int q = wave & 3;     // wavefronts q and q + 4 share a SIMD and a 128 x 128 quadrant
+  const int rbA = (q >> 1) * 128, rbB = (q & 1) * 128 + grp * 64;
 
   int tm, tn;
   tile_coords<4>(p.tiles_m, p.tiles_n, tm, tn);  // XCD-aware, grouped tile order
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-  Loader<EB, LA, BM, KTB> la;
-  Loader<EB, LB, BN, KTB> lb;
-  if constexpr (LA == LAYOUT_K)
-    la.init(p.A + m0 * p.lda * EB, (uint32_t)(min(p.M - m0, (int64_t)BM) * p.lda * EB), p.lda, wave, lane);
-  else
-    la.init(p.A + m0 * EB, (uint32_t)((p.K * p.lda - m0) * EB), p.lda, wave, lane);
-  if constexpr (LB == LAYOUT_K)
-    lb.init(p.B + n0 * p.ldb * EB, (uint32_t)(min(p.N - n0, (int64_t)BN) * p.ldb * EB), p.ldb, wave, lane);
-  else
-    lb.init(p.B + n0 * EB, (uint32_t)((p.K * p.ldb - n0) * EB), p.ldb, wave, lane);
-
-  acc_t acc[WT][WT];
+  acc_t acc[WTM][WTN];
 #pragma unroll
-  for (int i = 0; i < WT; ++i)
+  for (int i = 0; i < WTM; ++i)
 #pragma unroll
-    for (int j = 0; j < WT; ++j) acc[i][j] = acc_t{};
+    for (int j = 0; j < WTN; ++j) acc[i][j] = acc_t{};
 
   const int nk = (int)((p.K + KTB / EB - 1) / (KTB / EB));
-  const int rbA = wm * (BM / 2), rbB = wn * (BN / 2);
   auto stA = [&](int kt) { return smem + (kt % NST) * STAGE; };
   auto stB = [&](int kt) { return smem + (kt % NST) * STAGE + GA::BYTES; };
-
-  // Prologue: K tiles 0 .. NST-2.  Loads of tiles at or beyond nk read nothing
-  // (every lane's offset is out of range) and fill their stage with zeros, so
-  // the loop below issues the same 8 loads per wave in every iteration and the
-  // number of loads still in flight at each wait is constant.
+  frag_t fa[S][WTM], fb[S][WTN];
+  auto read_frags = [&](int kt) {
 #pragma unroll
-  for (int kt = 0; kt < NST - 1; ++kt) {
-    la.issue(stA(kt), kt, p.K, wave);
-    lb.issue(stB(kt), kt, p.K, wave);
-  }
-  asm volatile("s_waitcnt vmcnt(24)" ::: "memory");  // tile 0 has landed
-  barrier_lds();
-
-  if constexpr (Op::SUBSTEPS == 2) {
-    // f0 holds sub-step 0 of the current tile, f1 sub-step 1.  Per tile:
-    //   read sub-step 1 | multiply sub-step 0       (interleaved 1 read : 2 mfma)
-    //   wait for tile kt+1, barrier
-    //   refill the stage of tile kt-1 with tile kt+NST-1 | read the next tile's
-    //   sub-step 0 | multiply sub-step 1           (interleaved 1 load : 1 mfma : 1 read : 1 mfma)
-    i32x4 fa0[WT], fb0[WT], fa1[WT], fb1[WT];
+    for (int s = 0; s < S; ++s) {
 #pragma unroll
-    for (int i = 0; i < WT; ++i) fa0[i] = RA::read16(stA(0), rbA + 32 * i, 0, lane);
-#pragma unroll
-    for (int j = 0; j < WT; ++j) fb0[j] = RB::read16(stB(0), rbB + 32 * j, 0, lane);
-    for (int kt = 0; kt < nk; ++kt) {
-#pragma unroll
-      for (int i = 0; i < WT; ++i) fa1[i] = RA::read16(stA(kt), rbA + 32 * i, 1, lane);
-#pragma unroll
-      for (int j = 0; j < WT; ++j) fb1[j] = RB::read16(stB(kt), rbB + 32 * j, 1, lane);
-#pragma unroll
-      for (int i = 0; i < WT; ++i)
-#pragma unroll
-        for (int j = 0; j < WT; ++j) Op::mma(acc[i][j], fb0[j], fa0[i]);
-#pragma unroll
-      for (int r = 0; r < 2 * WT; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
+      for (int i = 0; i < WTM; ++i) {
+        if constexpr (S == 2) fa[s][i] = RA::read16(stA(kt), rbA + 32 * i, s, lane);
+        else fa[s][i] = RA::read32(stA(kt), rbA + 32 * i, lane);
       }
-      __builtin_amdgcn_sched_barrier(0);  // keep the first half before the barrier
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // tile kt+1 has landed
+#pragma unroll
+      for (int j = 0; j < WTN; ++j) {
+        if constexpr (S == 2) fb[s][j] = RB::read16(stB(kt), rbB + 32 * j, s, lane);
+        else fb[s][j] = RB::read32(stB(kt), rbB + 32 * j, lane);
+      }
+    }
+  };
+  auto multiply = [&]() {
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int i = 0; i < WTM; ++i)
+#pragma unroll
+        for (int j = 0; j < WTN; ++j) Op::mma(acc[i][j], fb[s][j], fa[s][i]);
+  };
+
+  // Slot 2t: group 0 multiplies K tile t while group 1 reads tile t's
+  // fragments and issues the A DMA of tile t + PD; slot 2t + 1: group 1
+  // multiplies tile t while group 0 reads tile t + 1 and issues the B DMA of
+  // tile t + PD.  The stage of tile t + PD is that of tile t - 1, whose last
+  // reads ended before the barrier closing slot 2t - 2.  Before the barrier
+  // closing slot 2t every wave has waited for its own share of tile t + 1, so
+  // tile t + 1 is complete in LDS from slot 2t + 1 on.  DMA of tiles at or
+  // beyond nk read nothing and fill their stage with zeros.  Each group runs
+  // its own loop (two barriers per K tile in both), so that each loop body is
+  // straight-line code.
+  if (grp == 0) {
+    LdB lb;
+    if constexpr (LB == LAYOUT_K)
+      lb.init(p.B + n0 * p.ldb * EB, (uint32_t)(min(p.N - n0, (int64_t)BN) * p.ldb * EB), p.ldb, q, lane);
+    else
+      lb.init(p.B + n0 * EB, (uint32_t)((p.K * p.ldb - n0) * EB), p.ldb, q, lane);
+#pragma unroll
+    for (int kt = 0; kt < PD; ++kt) lb.issue(stB(kt), kt, p.K, q);
+    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");  // own share of tile 0 has landed
+    barrier_lds();
+    read_frags(0);
+    for (int kt = 0; kt < nk; ++kt) {
+      __builtin_amdgcn_sched_barrier(0);
+      multiply();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // own share (B) of tile kt+1
       barrier_lds();
       __builtin_amdgcn_sched_barrier(0);
-      // next tile's sub-step 0 is read before the new DMA loads are issued, so
-      // no LDS read has to wait for in-flight DMA writes it cannot alias
-#pragma unroll
-      for (int i = 0; i < WT; ++i) fa0[i] = RA::read16(stA(kt + 1), rbA + 32 * i, 0, lane);
-#pragma unroll
-      for (int j = 0; j < WT; ++j) fb0[j] = RB::read16(stB(kt + 1), rbB + 32 * j, 0, lane);
-      la.issue(stA(kt + NST - 1), kt + NST - 1, p.K, wave);
-      lb.issue(stB(kt + NST - 1), kt + NST - 1, p.K, wave);
-#pragma unroll
-      for (int i = 0; i < WT; ++i)
-#pragma unroll
-        for (int j = 0; j < WT; ++j) Op::mma(acc[i][j], fb1[j], fa1[i]);
-#pragma unroll
-      for (int r = 0; r < 2 * WT; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      }
-#pragma unroll
-      for (int r = 0; r < 2 * WT; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // buffer load -> LDS
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      read_frags(kt + 1);
+      lb.issue(stB(kt + PD), kt + PD, p.K, q);
+      barrier_lds();
     }
   } else {
-    // one instruction per 32-byte fragment: a single fragment set; the first
-    // half of the tile's instructions runs before the barrier, the next tile's
-    // fragments are read after the second half.
-    i32x8 fa[WT], fb[WT];
+    LdA la;
+    if constexpr (LA == LAYOUT_K)
+      la.init(p.A + m0 * p.lda * EB, (uint32_t)(min(p.M - m0, (int64_t)BM) * p.lda * EB), p.lda, q, lane);
+    else
+      la.init(p.A + m0 * EB, (uint32_t)((p.K * p.lda - m0) * EB), p.lda, q, lane);
+#pragma unroll
+    for (int kt = 0; kt < PD; ++kt) la.issue(stA(kt), kt, p.K, q);
+    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");  // own share of tile 0 has landed
+    barrier_lds();
     for (int kt = 0; kt < nk; ++kt) {
-#pragma unroll
-      for (int i = 0; i < WT; ++i) fa[i] = RA::read32(stA(kt), rbA + 32 * i, lane);
-#pragma unroll
-      for (int j = 0; j < WT; ++j) fb[j] = RB::read32(stB(kt), rbB + 32 * j, lane);
-#pragma unroll
-      for (int i = 0; i < WT / 2; ++i)
-#pragma unroll
-        for (int j = 0; j < WT; ++j) Op::mma(acc[i][j], fb[j], fa[i]);
-      __builtin_amdgcn_sched_barrier(0);  // keep the first half before the barrier
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // tile kt+1 has landed
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(kt);
+      la.issue(stA(kt + PD), kt + PD, p.K, q);
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");  // own share (A) of tile kt+1
       barrier_lds();
       __builtin_amdgcn_sched_barrier(0);
-      la.issue(stA(kt + NST - 1), kt + NST - 1, p.K, wave);
-      lb.issue(stB(kt + NST - 1), kt + NST - 1, p.K, wave);
-#pragma unroll
-      for (int i = WT / 2; i < WT; ++i)
-#pragma unroll
-        for (int j = 0; j < WT; ++j) Op::mma(acc[i][j], fb[j], fa[i]);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // buffer load -> LDS
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      }
+      multiply();
       __builtin_amdgcn_sched_barrier(0);
+      barrier_lds();
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA outstanding at exit
 
-  // epilogue: tile (i, j), register group q: lane holds D[m][n .. n+3] with
-  // m = m0 + rbA + 32 i + (lane & 31), n = n0 + rbB + 32 j + 8 q + 4 (lane >> 5)
+  // epilogue: tile (i, j), register group r4: lane holds D[m][n .. n+3] with
+  // m = m0 + rbA + 32 i + (lane & 31), n = n0 + rbB + 32 j + 8 r4 + 4 (lane >> 5)
   const bool vec_ok = p.vec_cd;
   const s1* C = (const s1*)p.C;
   s1* D = (s1*)p.D;
-  auto combine = [&](const acc_t& a, int q, const v4& c, bool use_c) {
+  if constexpr (Op::INT_ACC) {
+    // wrapping alpha * acc, in place (keeps the products out of the C batches)
+    if (p.alpha_i != 1) {
+#pragma unroll
+      for (int i = 0; i < WTM; ++i)
+#pragma unroll
+        for (int j = 0; j < WTN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = (int)((uint32_t)p.alpha_i * (uint32_t)acc[i][j][r]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  auto combine = [&](const acc_t& a, int r4, const v4& c, bool use_c) {
     v4 o;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if constexpr (Op::INT_ACC)
-        o[r] = (int)((uint32_t)p.alpha_i * (uint32_t)a[4 * q + r] +
-                     (use_c ? (uint32_t)p.beta_i * (uint32_t)c[r] : 0u));
+        o[r] = (int)((uint32_t)a[4 * r4 + r] + (use_c ? (uint32_t)p.beta_i * (uint32_t)c[r] : 0u));
       else
-        o[r] = use_c ? __builtin_fmaf(p.alpha, a[4 * q + r], p.beta * c[r]) : p.alpha * a[4 * q + r];
+        o[r] = use_c ? __builtin_fmaf(p.alpha, a[4 * r4 + r], p.beta * c[r]) : p.alpha * a[4 * r4 + r];
     }
     return o;
   };
   if (vec_ok && m0 + BM <= p.M && n0 + BN <= p.N) {
-    // interior tile: straight-line code, C read in four batches of 16 vector
-    // loads per lane (issued back to back)
+    // interior tile: straight-line code, C read in batches of 16 vector loads
+    // per lane (two rows of instruction tiles), issued back to back
     const s1* Cb = C + (m0 + rbA + (lane & 31)) * p.ldc + n0 + rbB + 4 * (lane >> 5);
     s1* Db = D + (m0 + rbA + (lane & 31)) * p.ldc + n0 + rbB + 4 * (lane >> 5);
     if (p.use_c) {
 #pragma unroll
-      for (int i = 0; i < WT; ++i) {
-        v4 cbuf[WT][4];
+      for (int i0 = 0; i0 < WTM; i0 += 2) {
+        __builtin_amdgcn_sched_barrier(0);  // keep each batch's arithmetic after its loads
+        v4 cbuf[2][WTN][4];
 #pragma unroll
-        for (int j = 0; j < WT; ++j)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            cbuf[j][q] = *(const v4*)(Cb + (32 * i) * p.ldc + 32 * j + 8 * q);
+          for (int j = 0; j < WTN; ++j)
 #pragma unroll
-        for (int j = 0; j < WT; ++j)
+            for (int r4 = 0; r4 < 4; ++r4)
+              cbuf[i][j][r4] = *(const v4*)(Cb + (32 * (i0 + i)) * p.ldc + 32 * j + 8 * r4);
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *(v4*)(Db + (32 * i) * p.ldc + 32 * j + 8 * q) = combine(acc[i][j], q, cbuf[j][q], true);
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < WTN; ++j)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+              *(v4*)(Db + (32 * (i0 + i)) * p.ldc + 32 * j + 8 * r4) =
+                  combine(acc[i0 + i][j], r4, cbuf[i][j][r4], true);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < WT; ++i)
+      for (int i = 0; i < WTM; ++i)
 #pragma unroll
-        for (int j = 0; j < WT; ++j)
+        for (int j = 0; j < WTN; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *(v4*)(Db + (32 * i) * p.ldc + 32 * j + 8 * q) = combine(acc[i][j], q, v4{}, false);
+          for (int r4 = 0; r4 < 4; ++r4)
+            *(v4*)(Db + (32 * i) * p.ldc + 32 * j + 8 * r4) = combine(acc[i][j], r4, v4{}, false);
     }
   } else {
     // edge tile: per-element bounds
 #pragma unroll
-    for (int i = 0; i < WT; ++i) {
+    for (int i = 0; i < WTM; ++i) {
       const int64_t m = m0 + rbA + 32 * i + (lane & 31);
       if (m >= p.M) continue;
 #pragma unroll
-      for (int j = 0; j < WT; ++j)
+      for (int j = 0; j < WTN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n = n0 + rbB + 32 * j + 8 * q + 4 * (lane >> 5);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int64_t n = n0 + rbB + 32 * j + 8 * r4 + 4 * (lane >> 5);
           if (n >= p.N) continue;
           const bool full = vec_ok && n + 4 <= p.N;
           v4 c = {};
@@ -324,7 +316,7 @@ void gemm_fast_kernel(DenseArgs p) {
               for (int r = 0; r < 4; ++r)
                 if (n + r < p.N) c[r] = C[m * p.ldc + n + r];
           }
-          const v4 o = combine(acc[i][j], q, c, p.use_c);
+          const v4 o = combine(acc[i][j], r4, c, p.use_c);
           if (full) {
             *(v4*)(D + m * p.ldc + n) = o;
           } else {
@@ -343,7 +335,7 @@ static hipError_t launch_one(const DenseArgs& a0, hipStream_t s) {
   a.tiles_n = (int)((a.N + BN - 1) / BN);
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_fast_kernel<Op, LA, LB>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_fast_kernel<Op, LA, LB>), dim3((unsigned)blocks), dim3(THREADS), 0, s, a);
   return hipGetLastError();
 }
 
