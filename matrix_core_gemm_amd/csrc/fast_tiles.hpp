@@ -93,6 +93,56 @@ struct Loader {
   }
 };
 
+// HBM -> LDS loader with one lane offset and uniform strides.  The chunk a
+// lane fetches is the same in every instruction of a stage up to a whole
+// number of swizzle periods of rows, so instruction i only adds i * istride
+// and K tile kt adds kt * kstride.  Every offset is passed as the per-lane
+// (range-checked) buffer offset, so rows past M / N and k past K read zeros.
+// For K-contiguous rows of 128 bytes every 8 lanes fetch one whole 128-byte
+// line of a row.
+template <int EB, int LAYOUT, int ROWS_MN, int KTB>
+struct LineLoader {
+  using G = Geom<EB, LAYOUT, ROWS_MN, KTB>;
+  static constexpr int INSTR = G::CHUNKS / (64 * NW);   // per wave and stage
+  static constexpr int ROWS_PER_I = NW * 64 / G::CPR;   // LDS rows advanced per instruction
+  static_assert(G::CHUNKS % (64 * NW) == 0, "tile must split into whole wave instructions");
+  static_assert(LAYOUT != LAYOUT_K || ROWS_PER_I % 16 == 0, "swizzle period (16 rows) per instruction");
+  static_assert(LAYOUT == LAYOUT_K || ROWS_PER_I % (EB == 2 ? 4 : 8) == 0, "swizzle period per instruction");
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff;     // lane offset of instruction 0, K tile 0
+  int klim;          // K-contiguous: K tiles kt < klim hold this lane's chunk inside K
+  uint32_t istride;  // bytes between consecutive instructions
+  uint32_t kstride;  // bytes per K tile
+
+  __device__ __forceinline__ void init(const char* base, uint32_t bytes, int64_t ld, int64_t K, int wave,
+                                       int lane) {
+    rsrc = make_rsrc(base, bytes);
+    const int q = wave * 64 + lane;
+    const int r = q / G::CPR, pc = q % G::CPR;
+    const int lc = pc ^ swz<EB, LAYOUT, G::CPR>(r);
+    voff = (uint32_t)(r * ld * EB + lc * 16);
+    istride = __builtin_amdgcn_readfirstlane((uint32_t)(ROWS_PER_I * ld * EB));
+    kstride = __builtin_amdgcn_readfirstlane(LAYOUT == LAYOUT_K ? (uint32_t)KTB : (uint32_t)(KTB / EB * ld * EB));
+    if constexpr (LAYOUT == LAYOUT_K) {
+      const int64_t left = K - (int64_t)lc * (16 / EB);  // k values from this chunk to the end of K
+      klim = left <= 0 ? 0 : (int)((left + KTB / EB - 1) / (KTB / EB));
+    } else {
+      klim = 0x7fffffff;  // MN-contiguous: rows past K lie outside the buffer window
+    }
+  }
+
+  // instructions [i0, i0 + n) of K tile kt into stage `dst`.  The out-of-range
+  // offset plus i * istride cannot wrap: every window is below 2 GiB.
+  __device__ __forceinline__ void issue(lds_char* dst, int kt, int i0, int n, int wave) const {
+    const uint32_t v = kt < klim ? voff + (uint32_t)kt * kstride : BUF_OOB;
+#pragma unroll
+    for (int i = i0; i < i0 + n; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(dst + (i * NW + wave) * 1024), 16,
+          v + (uint32_t)i * istride, 0, 0, 0);
+  }
+};
+
 // LDS -> VGPR fragments of the 32 rows [rb, rb + 32) of a tile.  Lane group
 // g = lane >> 5 reads 16 bytes of K starting at byte kb (chosen by the caller
 // per lane group); MN-contiguous tiles gather them with transposing reads.

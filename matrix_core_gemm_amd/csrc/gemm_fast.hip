@@ -9,20 +9,20 @@
 //     (wavefronts w and w + 4 share a SIMD, measured).  Each wavefront owns a
 //     128 x 64 sub-tile = 4 x 2 instructions of 32 x 32 (128 accumulator
 //     registers per lane).
-//   - K is staged in tiles of 64 bytes per row (32 bf16 / 64 8-bit values) in
-//     a ring of 5 LDS stages of 32 KiB (A and B), filled by buffer_load ... lds
-//     (16 bytes per lane, no VGPRs) 4 K tiles ahead of use.  The XOR swizzle
-//     of the LDS rows is folded into the global address each lane loads;
-//     chunks outside the matrix get an out-of-range offset and the buffer unit
-//     writes zeros.
+//   - K is staged in tiles of 128 bytes per row (64 bf16 / 128 8-bit values),
+//     so that every 8 lanes of a load fetch one whole 128-byte line: twice the
+//     bytes per outstanding L1 miss of a 64-byte tile, which measured as the
+//     limit of the HBM -> LDS stream.  A has 2 LDS stages and B 3 (32 KiB each,
+//     160 KiB), filled by buffer_load ... lds (16 bytes per lane, no VGPRs).
+//     The XOR swizzle of the LDS rows is folded into the global address each
+//     lane loads; chunks outside the matrix get an out-of-range offset and the
+//     buffer unit writes zeros.
 //   - ping-pong schedule: the two wavefronts of a SIMD alternate between a
 //     multiply phase (only matrix instructions, on fragments already in
-//     registers) and a memory phase (LDS -> register reads of the next K
-//     tile's fragments and the DMA issues for a future K tile), separated by
-//     workgroup barriers, so that one of them keeps the SIMD's matrix core
-//     busy while the other waits on memory.  Wavefronts 0-3 multiply K tile t
-//     in slot 2t, wavefronts 4-7 in slot 2t + 1; wavefronts 4-7 issue the A
-//     tile DMAs, wavefronts 0-3 the B tile DMAs.
+//     registers) and a memory phase (LDS -> register reads of the next half K
+//     tile's fragments and 4 DMA issues per wave), separated by workgroup
+//     barriers, so that one of them keeps the SIMD's matrix core busy while
+//     the other waits on memory.
 //   - epilogue: for interior tiles, straight-line code reads C in batches of
 //     16 vector loads per lane (so the loads overlap) and stores
 //     D = alpha * acc + beta * C (16 bytes per lane per row segment, thanks to
@@ -39,24 +39,24 @@
 namespace mcg {
 namespace fast {
 
-constexpr int KTB = 64;      // bytes of K per LDS row and stage
-constexpr int NST = 5;       // LDS stages
-constexpr int PD = NST - 1;  // DMA prefetch distance in K tiles
+constexpr int KTB = 128;     // bytes of K per LDS row and stage: one 128-byte line per row
+constexpr int NSA = 2;       // LDS stages of A
+constexpr int NSB = 3;       // LDS stages of B
 constexpr int BM = 256, BN = 256;
 constexpr int THREADS = 512;
 
 
 // ------------------------------------------------------------- 32x32 ops
-// P (first operand) = B fragment, Q = A fragment.  Lane group g = lane >> 5 of
-// a 32-row fragment owns the tile K bytes [32g, 32g + 32) of its row (gathered
-// by transposing reads when the operand is MN-contiguous).  Ops with
-// SUBSTEPS == 2 consume them as two 16-byte halves (sub-step s = bytes
-// [32g + 16s, +16)), one instruction each; SUBSTEPS == 1 ops take all 32 bytes
-// in one instruction.  Output lane l, register r holds
-// out[8*(r/4) + 4*(l/32) + r%4][l % 32] (the 32 x 32 accumulator layout).
+// P (first operand) = B fragment, Q = A fragment.  One instruction takes
+// LANE_BYTES bytes of K per lane; lane group g = lane >> 5 of a 32-row
+// fragment holds the g-th LANE_BYTES-byte part of the instruction's K range
+// (gathered by transposing reads when the operand is MN-contiguous); A and B
+// use the same assignment, so any consistent choice is valid.  Output lane l,
+// register r holds out[8*(r/4) + 4*(l/32) + r%4][l % 32] (the 32 x 32
+// accumulator layout).
 
 struct BF16 {
-  static constexpr int EB = 2, SUBSTEPS = 2;
+  static constexpr int EB = 2, LANE_BYTES = 16;
   static constexpr bool INT_ACC = false;
   using acc_t = f32x16;
   using frag_t = i32x4;
@@ -65,7 +65,7 @@ struct BF16 {
   }
 };
 struct F16 {
-  static constexpr int EB = 2, SUBSTEPS = 2;
+  static constexpr int EB = 2, LANE_BYTES = 16;
   static constexpr bool INT_ACC = false;
   using acc_t = f32x16;
   using frag_t = i32x4;
@@ -74,7 +74,7 @@ struct F16 {
   }
 };
 struct I8 {
-  static constexpr int EB = 1, SUBSTEPS = 2;
+  static constexpr int EB = 1, LANE_BYTES = 16;
   static constexpr bool INT_ACC = true;
   using acc_t = i32x16;
   using frag_t = i32x4;
@@ -85,7 +85,7 @@ struct I8 {
 // native fp8: FP = format of P (B tensor), FQ = format of Q (A tensor)
 template <int FP, int FQ>
 struct F8 {
-  static constexpr int EB = 1, SUBSTEPS = 1;
+  static constexpr int EB = 1, LANE_BYTES = 32;
   static constexpr bool INT_ACC = false;
   using acc_t = f32x16;
   using frag_t = i32x8;
@@ -94,10 +94,10 @@ struct F8 {
   }
 };
 // fp8 widened exactly to bf16 (K below the native-fp8 threshold): FA/FB = formats
-// of A/B; a 16-byte sub-step holds 16 fp8 values = two bf16 instructions.
+// of A/B; 16 bytes per lane hold 16 fp8 values = two bf16 instructions.
 template <int FA, int FB>
 struct F8W {
-  static constexpr int EB = 1, SUBSTEPS = 2;
+  static constexpr int EB = 1, LANE_BYTES = 16;
   static constexpr bool INT_ACC = false;
   using acc_t = f32x16;
   using frag_t = i32x4;
@@ -115,33 +115,46 @@ template <class Op, int LA, int LB>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_fast_kernel(DenseArgs p) {
   constexpr int EB = Op::EB;
-  constexpr int S = Op::SUBSTEPS;
-  constexpr int WTM = 4, WTN = 2;  // 32 x 32 instruction tiles per wave along m and n
+  constexpr int LB16 = Op::LANE_BYTES;  // bytes of K per lane and instruction (16 or 32)
+  constexpr int S = 64 / (2 * LB16);    // instructions per block and half K tile
+  constexpr int WTM = 4, WTN = 2;       // 32 x 32 instruction tiles per wave along m and n
   using GA = Geom<EB, LA, BM, KTB>;
   using GB = Geom<EB, LB, BN, KTB>;
   using RA = Reader<EB, LA, BM, KTB>;
   using RB = Reader<EB, LB, BN, KTB>;
-  using LdA = Loader<EB, LA, BM, KTB>;
-  using LdB = Loader<EB, LB, BN, KTB>;
+  using LdA = LineLoader<EB, LA, BM, KTB>;
+  using LdB = LineLoader<EB, LB, BN, KTB>;
   using acc_t = typename Op::acc_t;
   using frag_t = typename Op::frag_t;
   using v4 = typename std::conditional<Op::INT_ACC, i32x4, f32x4>::type;
   using s1 = typename std::conditional<Op::INT_ACC, int, float>::type;
-  constexpr int STAGE = GA::BYTES + GB::BYTES;
-  static_assert(LdA::INSTR == 4 && LdB::INSTR == 4, "vmcnt bookkeeping assumes 4 loads per wave per K tile");
+  static_assert(GA::BYTES == 32768 && GB::BYTES == 32768, "32 KiB per operand stage");
+  static_assert(LdA::INSTR == 8 && LdB::INSTR == 8, "vmcnt bookkeeping assumes 4 + 4 loads per stage and group");
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[NST * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[(NSA + NSB) * 32768];
   lds_char* smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;  // 0: multiplies in even slots and loads B; 1: odd slots, loads A
+  const int grp = wave >> 2;  // 0: multiplies in even slots; 1: in odd slots
   const int q = wave & 3;     // wavefronts q and q + 4 share a SIMD and a 128 x 128 quadrant
   const int rbA = (q >> 1) * 128, rbB = (q & 1) * 128 + grp * 64;
+  const int g = lane >> 5;
 
   int tm, tn;
   tile_coords<4>(p.tiles_m, p.tiles_n, tm, tn);  // XCD-aware, grouped tile order
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  LdA la;
+  LdB lb;
+  if constexpr (LA == LAYOUT_K)
+    la.init(p.A + m0 * p.lda * EB, (uint32_t)(min(p.M - m0, (int64_t)BM) * p.lda * EB), p.lda, p.K, q, lane);
+  else
+    la.init(p.A + m0 * EB, (uint32_t)((p.K * p.lda - m0) * EB), p.lda, p.K, q, lane);
+  if constexpr (LB == LAYOUT_K)
+    lb.init(p.B + n0 * p.ldb * EB, (uint32_t)(min(p.N - n0, (int64_t)BN) * p.ldb * EB), p.ldb, p.K, q, lane);
+  else
+    lb.init(p.B + n0 * EB, (uint32_t)((p.K * p.ldb - n0) * EB), p.ldb, p.K, q, lane);
 
   acc_t acc[WTM][WTN];
 #pragma unroll
@@ -150,21 +163,39 @@ void gemm_fast_kernel(DenseArgs p) {
     for (int j = 0; j < WTN; ++j) acc[i][j] = acc_t{};
 
   const int nk = (int)((p.K + KTB / EB - 1) / (KTB / EB));
-  auto stA = [&](int kt) { return smem + (kt % NST) * STAGE; };
-  auto stB = [&](int kt) { return smem + (kt % NST) * STAGE + GA::BYTES; };
+  auto stA = [&](int kt) { return smem + (kt & 1) * 32768; };
+  auto stB = [&](int kt) { return smem + NSA * 32768 + (kt % NSB) * 32768; };
+  // this group's half (4 of the 8 load instructions per wave) of operand X of K tile kt
+  const int ihalf = 4 * grp;
+  auto issueA = [&](int kt) { la.issue(stA(kt), kt, ihalf, 4, q); };
+  auto issueB = [&](int kt) { lb.issue(stB(kt), kt, ihalf, 4, q); };
+
   frag_t fa[S][WTM], fb[S][WTN];
-  auto read_frags = [&](int kt) {
+  // fragments of half h (K bytes [64h, 64h + 64) of each row) of K tile kt;
+  // instruction s of the half takes lane group g's bytes [64h + 2 LB16 s + LB16 g, +LB16)
+  auto read_frags = [&](int kt, int h) {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
+      const int kb = 64 * h + 2 * LB16 * s + LB16 * g;
 #pragma unroll
       for (int i = 0; i < WTM; ++i) {
-        if constexpr (S == 2) fa[s][i] = RA::read16(stA(kt), rbA + 32 * i, s, lane);
-        else fa[s][i] = RA::read32(stA(kt), rbA + 32 * i, lane);
+        if constexpr (LB16 == 16) {
+          fa[s][i] = RA::read16k(stA(kt), rbA + 32 * i, kb, lane);
+        } else {
+          const i32x4 x = RA::read16k(stA(kt), rbA + 32 * i, kb, lane);
+          const i32x4 y = RA::read16k(stA(kt), rbA + 32 * i, kb + 16, lane);
+          fa[s][i] = frag_t{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+        }
       }
 #pragma unroll
       for (int j = 0; j < WTN; ++j) {
-        if constexpr (S == 2) fb[s][j] = RB::read16(stB(kt), rbB + 32 * j, s, lane);
-        else fb[s][j] = RB::read32(stB(kt), rbB + 32 * j, lane);
+        if constexpr (LB16 == 16) {
+          fb[s][j] = RB::read16k(stB(kt), rbB + 32 * j, kb, lane);
+        } else {
+          const i32x4 x = RB::read16k(stB(kt), rbB + 32 * j, kb, lane);
+          const i32x4 y = RB::read16k(stB(kt), rbB + 32 * j, kb + 16, lane);
+          fb[s][j] = frag_t{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+        }
       }
     }
   };
@@ -177,58 +208,53 @@ void gemm_fast_kernel(DenseArgs p) {
         for (int j = 0; j < WTN; ++j) Op::mma(acc[i][j], fb[s][j], fa[s][i]);
   };
 
-  // Slot 2t: group 0 multiplies K tile t while group 1 reads tile t's
-  // fragments and issues the A DMA of tile t + PD; slot 2t + 1: group 1
-  // multiplies tile t while group 0 reads tile t + 1 and issues the B DMA of
-  // tile t + PD.  The stage of tile t + PD is that of tile t - 1, whose last
-  // reads ended before the barrier closing slot 2t - 2.  Before the barrier
-  // closing slot 2t every wave has waited for its own share of tile t + 1, so
-  // tile t + 1 is complete in LDS from slot 2t + 1 on.  DMA of tiles at or
-  // beyond nk read nothing and fill their stage with zeros.  Each group runs
-  // its own loop (two barriers per K tile in both), so that each loop body is
-  // straight-line code.
+  // Half tiles u = 2t + h.  Group 0 reads half u in slot 2u - 1 and multiplies
+  // it in slot 2u; group 1 reads it in slot 2u and multiplies it in slot
+  // 2u + 1; slots are separated by workgroup barriers.  K tile t (A stage
+  // t % 2, B stage t % 3) is last read in slot 4t + 2 and first needed in slot
+  // 4t + 3 (= 4(t+1) - 1 for tile t + 1).  DMA halves, 4 instructions per wave
+  // in every memory phase:
+  //   slot 4t     (group 1): second half of A(t+1)  -> A stage of tile t-1, free since slot 4t-1
+  //   slot 4t + 1 (group 0): first half of B(t+2)   -> B stage of tile t-1
+  //   slot 4t + 2 (group 1): second half of B(t+2)
+  //   slot 4t + 3 (group 0): first half of A(t+2)   -> A stage of tile t, free since slot 4t+3
+  // At the end of slot 4t + 2 each wave waits until only its newest 4 loads
+  // (its half of B(t+2)) are in flight, so tile t+1 is complete from slot 4t+3.
+  // DMA of tiles at or beyond nk read nothing and fill their stage with zeros.
+  issueB(0);
+  issueA(0);
+  issueB(1);
+  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // own shares of tile 0 have landed
+  barrier_lds();
+  const int nu = 2 * nk;
   if (grp == 0) {
-    LdB lb;
-    if constexpr (LB == LAYOUT_K)
-      lb.init(p.B + n0 * p.ldb * EB, (uint32_t)(min(p.N - n0, (int64_t)BN) * p.ldb * EB), p.ldb, q, lane);
-    else
-      lb.init(p.B + n0 * EB, (uint32_t)((p.K * p.ldb - n0) * EB), p.ldb, q, lane);
-#pragma unroll
-    for (int kt = 0; kt < PD; ++kt) lb.issue(stB(kt), kt, p.K, q);
-    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");  // own share of tile 0 has landed
-    barrier_lds();
-    read_frags(0);
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int u = 0; u < nu; ++u) {
+      const int t = u >> 1, h = u & 1;
       __builtin_amdgcn_sched_barrier(0);
-      multiply();
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // own share (B) of tile kt+1
+      read_frags(t, h);  // slot 2u - 1: memory phase
+      if (h == 0) issueA(t + 1);
+      else issueB(t + 2);
       barrier_lds();
       __builtin_amdgcn_sched_barrier(0);
-      read_frags(kt + 1);
-      lb.issue(stB(kt + PD), kt + PD, p.K, q);
+      multiply();  // slot 2u
+      __builtin_amdgcn_sched_barrier(0);
+      if (h == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
       barrier_lds();
     }
   } else {
-    LdA la;
-    if constexpr (LA == LAYOUT_K)
-      la.init(p.A + m0 * p.lda * EB, (uint32_t)(min(p.M - m0, (int64_t)BM) * p.lda * EB), p.lda, q, lane);
-    else
-      la.init(p.A + m0 * EB, (uint32_t)((p.K * p.lda - m0) * EB), p.lda, q, lane);
-#pragma unroll
-    for (int kt = 0; kt < PD; ++kt) la.issue(stA(kt), kt, p.K, q);
-    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");  // own share of tile 0 has landed
-    barrier_lds();
-    for (int kt = 0; kt < nk; ++kt) {
+    barrier_lds();  // slot -1
+    for (int u = 0; u < nu; ++u) {
+      const int t = u >> 1, h = u & 1;
       __builtin_amdgcn_sched_barrier(0);
-      read_frags(kt);
-      la.issue(stA(kt + PD), kt + PD, p.K, q);
-      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");  // own share (A) of tile kt+1
+      read_frags(t, h);  // slot 2u: memory phase
+      if (h == 0) issueA(t + 1);
+      else issueB(t + 2);
+      if (h == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
       barrier_lds();
       __builtin_amdgcn_sched_barrier(0);
-      multiply();
+      multiply();  // slot 2u + 1
       __builtin_amdgcn_sched_barrier(0);
-      barrier_lds();
+      if (u + 1 < nu) barrier_lds();
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA outstanding at exit
@@ -356,7 +382,7 @@ bool fast_path_ok(int dtA, int la, int lb, const DenseArgs& a, bool aligned) {
   // every buffer window (and offset into it) must stay below 2 GiB
   const int64_t lim = (int64_t)1 << 31;
   // MN-contiguous offsets advance by whole K tiles, up to NST tiles past the end of K
-  const int64_t kpad = fast::NST * fast::KTB / eb;
+  const int64_t kpad = 4 * fast::KTB / eb;
   const int64_t wa = la == 0 ? 256 * a.lda * eb : (a.K + kpad) * a.lda * eb;
   const int64_t wb = lb == 0 ? 256 * a.ldb * eb : (a.K + kpad) * a.ldb * eb;
   return wa < lim && wb < lim;
