@@ -7,23 +7,25 @@
 // pattern) and Common parameters: two kept values per group of four along K,
 // ascending, and a 2-bit position per kept value).  The mapping onto CDNA4:
 //   - smfmac_f32_32x32x32_{bf16,f16}: 32 x 32 outputs and 32 dense k per
-//     instruction, twice the dense instruction's work in the same issue time.
-//     Measured operand layout: lane group g = lane >> 5 of the sparse operand
-//     holds the 8 kept values of dense k [16g, 16g + 16) of its row; lane
-//     group g of the dense operand holds k [8g, 8g + 8) and [16 + 8g, 24 + 8g)
-//     of its column; the lane's index register holds, in the 16-bit half that
-//     the instruction's abid selects, one 4-bit code per group of four (code n
-//     for kept values 2n and 2n + 1).  The canonical index word of a row and 32
-//     dense k therefore serves both lane groups directly: group g uses bits
-//     [16g, 16g + 16).
-//   - 256 x 256 output tile per workgroup of 4 wavefronts (one per SIMD), each
-//     owning 128 x 128 = 4 x 4 instructions of 32 x 32.
-//   - one stage = 32 dense k: kept values 256 rows x 32 bytes, B 256 x 64
-//     bytes, index 256 rows x 4 bytes (25 KiB); a ring of 6 stages; every
-//     stage is filled by buffer_load ... lds (16 bytes per lane for values and
-//     B, 4 bytes per lane for the index), issued 5 stages ahead.
-//   - per stage: half of the instructions run before the workgroup barrier;
-//     after it the next stage's fragments are read while the other half runs.
+//     instruction, twice the dense instruction's work in about the same issue
+//     time.  Measured operand layout: lane group g = lane >> 5 of the sparse
+//     operand holds the 8 kept values of dense k [16g, 16g + 16) of its row;
+//     lane group g of the dense operand holds k [8g, 8g + 8) and
+//     [16 + 8g, 24 + 8g) of its column; the lane's index register holds, in
+//     the 16-bit half that the instruction's abid selects, one 4-bit code per
+//     group of four (code n for kept values 2n and 2n + 1).  The canonical
+//     index word of a row and 32 dense k therefore serves both lane groups
+//     directly: group g uses bits [16g, 16g + 16).
+//   - 256 x 256 output tile per workgroup of 8 wavefronts, two per SIMD, each
+//     owning 128 x 64 outputs = 4 x 2 instructions of 32 x 32.
+//   - LDS: kept values in stages of 128 dense k (128 bytes = one cache line
+//     per row) together with their index words (16 bytes per row), 2 stages of
+//     36 KiB; B in stages of 64 dense k (one 128-byte line per column), 2
+//     stages of 32 KiB.  All filled by buffer_load ... lds.
+//   - ping-pong schedule as in the dense kernel: the two wavefronts of a SIMD
+//     alternate between multiplying one 64-k step (16 instructions) and a
+//     memory phase (fragment reads of the next step and DMA issues); wavefronts
+//     0-3 issue the B loads, wavefronts 4-7 the kept values and index words.
 //   - the sparse operand must be the instruction's first operand, so a lane's
 //     output registers hold four consecutive rows of one column: the epilogue
 //     stores one 4-byte value per register (each store instruction writes two
@@ -34,11 +36,12 @@
 namespace mcg {
 namespace fast {
 
-constexpr int SP_KD = 32;                 // dense k per stage
-constexpr int SP_KTB_A = SP_KD / 2 * 2;   // bytes of kept values per row and stage (16 x 16-bit)
-constexpr int SP_KTB_B = SP_KD * 2;       // bytes of B per column and stage
-constexpr int SP_NST = 6;                 // LDS stages
+constexpr int SP_KA = 128;               // dense k per stage of kept values (128 bytes per row)
+constexpr int SP_KB = 64;                // dense k per stage of B (128 bytes per column)
 constexpr int SP_BM = 256, SP_BN = 256;
+constexpr int SP_THREADS = 512;
+constexpr int SP_A_STAGE = 32768 + 4096;  // kept values + index words of 256 rows
+constexpr int SP_B_STAGE = 32768;
 
 struct Sp32BF16 {
   __device__ static __forceinline__ void mma(f32x16& c, const i32x4& a, const i32x8& b, int idx) {
@@ -51,134 +54,148 @@ struct Sp32F16 {
   }
 };
 
-__device__ __forceinline__ uint32_t lds_read_b32(const lds_char* base, int off) {
-  return *(const __attribute__((address_space(3))) uint32_t*)(base + off);
-}
 
 template <class Op, int LB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(SP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_sparse_fast_kernel(SparseArgs p) {
-  constexpr int WT = 4;
-  using GA = Geom<2, LAYOUT_K, SP_BM, SP_KTB_A>;
-  using GB = Geom<2, LB, SP_BN, SP_KTB_B>;
-  using RA = Reader<2, LAYOUT_K, SP_BM, SP_KTB_A>;
-  using RB = Reader<2, LB, SP_BN, SP_KTB_B>;
-  using LDA = Loader<2, LAYOUT_K, SP_BM, SP_KTB_A>;
-  using LDB = Loader<2, LB, SP_BN, SP_KTB_B>;
-  constexpr int IDX_BYTES = SP_BM * 4;
-  constexpr int STAGE = GA::BYTES + GB::BYTES + IDX_BYTES;
-  static_assert(LDA::INSTR + LDB::INSTR + 1 == 7, "vmcnt bookkeeping assumes 7 loads per wave per stage");
-  static_assert(IDX_BYTES == NW * 64 * 4, "one 4-byte index load per lane and stage");
-  static_assert(STAGE % 1024 == 0 && SP_NST * STAGE <= 160 * 1024, "LDS ring");
+  constexpr int WTM = 4, WTN = 2;
+  using RA = Reader<2, LAYOUT_K, SP_BM, 128>;
+  using RB = Reader<2, LB, SP_BN, 128>;
+  using LdA = LineLoader<2, LAYOUT_K, SP_BM, 128>;
+  using LdB = LineLoader<2, LB, SP_BN, 128>;
+  static_assert(Geom<2, LAYOUT_K, SP_BM, 128>::BYTES == 32768 && Geom<2, LB, SP_BN, 128>::BYTES == 32768, "");
+  static_assert(LdA::INSTR == 8 && LdB::INSTR == 8, "8 loads per wave and stage");
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[SP_NST * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * SP_A_STAGE + 2 * SP_B_STAGE];
   lds_char* smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int grp = wave >> 2;  // 0: multiplies in even slots, loads B; 1: odd slots, loads A and index
+  const int q = wave & 3;
+  const int rbA = (q >> 1) * 128, rbB = (q & 1) * 128 + grp * 64;
+  const int g = lane >> 5;
   int tm, tn;
   tile_coords<4>(p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * SP_BM, n0 = (int64_t)tn * SP_BN;
   const int64_t rows = min(p.M - m0, (int64_t)SP_BM);
-
-  LDA la;
-  LDB lb;
-  la.init(p.Ac + m0 * p.lda_c * 2, (uint32_t)(rows * p.lda_c * 2), p.lda_c, wave, lane);
-  if constexpr (LB == LAYOUT_K)
-    lb.init(p.B + n0 * p.ldb * 2, (uint32_t)(min(p.N - n0, (int64_t)SP_BN) * p.ldb * 2), p.ldb, wave, lane);
-  else
-    lb.init(p.B + n0 * 2, (uint32_t)((p.K * p.ldb - n0) * 2), p.ldb, wave, lane);
-  // index: lane (wave, lane) fetches the word of row 64 * wave + lane
-  const __amdgpu_buffer_rsrc_t rs_idx =
-      make_rsrc((const char*)(p.idx + m0 * p.ld_idx), (uint32_t)(rows * p.ld_idx * 4));
-  const uint32_t off_idx = (uint32_t)((64 * wave + lane) * p.ld_idx * 4);
-
   const int64_t Kc = p.K / 2;  // kept values per row
-  const int nk = (int)((p.K + SP_KD - 1) / SP_KD);
-  auto stA = [&](int kt) { return smem + (kt % SP_NST) * STAGE; };
-  auto stB = [&](int kt) { return smem + (kt % SP_NST) * STAGE + GA::BYTES; };
-  auto stI = [&](int kt) { return smem + (kt % SP_NST) * STAGE + GA::BYTES + GB::BYTES; };
-  auto issue = [&](int kt) {
-    la.issue(stA(kt), kt, Kc, wave);
-    lb.issue(stB(kt), kt, p.K, wave);
-    const uint32_t o = kt < nk ? off_idx + (uint32_t)kt * 4u : BUF_OOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs_idx, (__attribute__((address_space(3))) void*)(stI(kt) + wave * 256), 4, o, 0, 0, 0);
-  };
+  const int nwords = (int)((p.K + 31) / 32);
+  const int nu = (int)((p.K + SP_KB - 1) / SP_KB);   // 64-k steps
 
-  f32x16 acc[WT][WT];
-#pragma unroll
-  for (int i = 0; i < WT; ++i)
-#pragma unroll
-    for (int j = 0; j < WT; ++j) acc[i][j] = f32x16{};
+  auto stA = [&](int T) { return smem + (T & 1) * SP_A_STAGE; };
+  auto stI = [&](int T) { return smem + (T & 1) * SP_A_STAGE + 32768; };
+  auto stB = [&](int u) { return smem + 2 * SP_A_STAGE + (u & 1) * SP_B_STAGE; };
 
-  const int rbA = wm * (SP_BM / 2), rbB = wn * (SP_BN / 2);
-  const int g = lane >> 5;
-  const int ishift = 16 * g;
-  struct Frags {
-    i32x4 a[WT];
-    i32x8 b[WT];
-    int idx[WT];
-  };
-  auto read_frags = [&](Frags& f, int kt) {
+  LdA la;
+  LdB lb;
+  __amdgpu_buffer_rsrc_t rs_idx;
+  uint32_t off_idx[4];
+  int word_idx[4];
+  if (grp) {
+    la.init(p.Ac + m0 * p.lda_c * 2, (uint32_t)(rows * p.lda_c * 2), p.lda_c, Kc, q, lane);
+    rs_idx = make_rsrc((const char*)(p.idx + m0 * p.ld_idx), (uint32_t)(rows * p.ld_idx * 4));
 #pragma unroll
-    for (int i = 0; i < WT; ++i) {
-      f.a[i] = RA::read16k(stA(kt), rbA + 32 * i, 16 * g, lane);
-      f.idx[i] = (int)(lds_read_b32(stI(kt), (rbA + 32 * i + (lane & 31)) * 4) >> ishift);
+    for (int i = 0; i < 4; ++i) {  // 4-byte loads: lane -> (row, word) of a 16-byte index row
+      const int e = i * 256 + q * 64 + lane;
+      word_idx[i] = e & 3;
+      off_idx[i] = (uint32_t)((e >> 2) * p.ld_idx * 4 + (e & 3) * 4);
     }
-#pragma unroll
-    for (int j = 0; j < WT; ++j) {
-      const i32x4 lo = RB::read16k(stB(kt), rbB + 32 * j, 16 * g, lane);
-      const i32x4 hi = RB::read16k(stB(kt), rbB + 32 * j, 32 + 16 * g, lane);
-      f.b[j] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
-  };
-
-  // Prologue: stages 0 .. NST-1.  Loads of stages at or beyond nk read nothing
-  // (every offset is out of range) and fill their stage with zeros, so every
-  // iteration issues the same 7 loads per wave and the number of loads in
-  // flight at each wait is constant.
-#pragma unroll
-  for (int kt = 0; kt < SP_NST; ++kt) issue(kt);
-  asm volatile("s_waitcnt vmcnt(35)" ::: "memory");  // stage 0 has landed
-  barrier_lds();
-
-  // Per stage kt (its fragments already requested into `cur`):
-  //   multiply rows 0-1 of the wave's blocks
-  //   wait for stage kt+1, barrier (every wave has finished reading stage kt)
-  //   read stage kt+1 into `nxt` | refill stage kt with stage kt+NST | multiply rows 2-3
-  auto step = [&](Frags& cur, Frags& nxt, int kt) {
-#pragma unroll
-    for (int i = 0; i < WT / 2; ++i)
-#pragma unroll
-      for (int j = 0; j < WT; ++j) Op::mma(acc[i][j], cur.a[i], cur.b[j], cur.idx[i]);
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(28)" ::: "memory");  // stage kt+1 has landed
-    barrier_lds();
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(nxt, kt + 1);
-    issue(kt + SP_NST);
-#pragma unroll
-    for (int i = WT / 2; i < WT; ++i)
-#pragma unroll
-      for (int j = 0; j < WT; ++j) Op::mma(acc[i][j], cur.a[i], cur.b[j], cur.idx[i]);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  Frags f0, f1;
-  read_frags(f0, 0);
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    step(f0, f1, kt);
-    step(f1, f0, kt + 1);
+  } else {
+    if constexpr (LB == LAYOUT_K)
+      lb.init(p.B + n0 * p.ldb * 2, (uint32_t)(min(p.N - n0, (int64_t)SP_BN) * p.ldb * 2), p.ldb, p.K, q, lane);
+    else
+      lb.init(p.B + n0 * 2, (uint32_t)((p.K * p.ldb - n0) * 2), p.ldb, p.K, q, lane);
   }
-  if (kt < nk) step(f0, f1, kt);
+  // kept values and index words of stage T (group 1, all 8 + 4 loads per wave)
+  auto issueA = [&](int T) {
+    la.issue(stA(T), T, 0, 8, q);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t o = T * 4 + word_idx[i] < nwords ? off_idx[i] + (uint32_t)T * 16u : BUF_OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs_idx, (__attribute__((address_space(3))) void*)(stI(T) + (i * 256 + q * 64) * 4), 4, o, 0, 0, 0);
+    }
+  };
+  auto issueB = [&](int u) { lb.issue(stB(u), u, 0, 8, q); };  // group 0, all 8 loads per wave
+
+  f32x16 acc[WTM][WTN];
+#pragma unroll
+  for (int i = 0; i < WTM; ++i)
+#pragma unroll
+    for (int j = 0; j < WTN; ++j) acc[i][j] = f32x16{};
+
+  i32x4 fa[2][WTM];
+  i32x8 fb[2][WTN];
+  int fi[2][WTM];
+  // fragments of 64-k step u = 2T + h: instruction s covers dense k [64h + 32s, +32) of stage T
+  auto read_frags = [&](int u) {
+    const int T = u >> 1, h = u & 1;
+#pragma unroll
+    for (int i = 0; i < WTM; ++i) {
+      const int row = rbA + 32 * i + (lane & 31);
+      const i32x2 w = *(const __attribute__((address_space(3))) i32x2*)(stI(T) + row * 16 + 8 * h);
+      fi[0][i] = (int)((uint32_t)w.x >> (16 * g));
+      fi[1][i] = (int)((uint32_t)w.y >> (16 * g));
+#pragma unroll
+      for (int s = 0; s < 2; ++s) fa[s][i] = RA::read16k(stA(T), rbA + 32 * i, 64 * h + 32 * s + 16 * g, lane);
+    }
+#pragma unroll
+    for (int j = 0; j < WTN; ++j)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const i32x4 lo = RB::read16k(stB(u), rbB + 32 * j, 64 * s + 16 * g, lane);
+        const i32x4 hi = RB::read16k(stB(u), rbB + 32 * j, 64 * s + 32 + 16 * g, lane);
+        fb[s][j] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
+  };
+  auto multiply = [&]() {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < WTM; ++i)
+#pragma unroll
+        for (int j = 0; j < WTN; ++j) Op::mma(acc[i][j], fa[s][i], fb[s][j], fi[s][i]);
+  };
+
+  // Steps u (64 dense k).  Group 0 reads step u in slot 2u - 1 and multiplies
+  // it in slot 2u; group 1 reads it in slot 2u and multiplies it in slot
+  // 2u + 1; slots are separated by workgroup barriers.  B stage u % 2 is last
+  // read in slot 2u; group 0 refills it with B(u + 2) in slot 2u + 1 and waits
+  // for it at the end of slot 2u + 2.  Kept-value stage T % 2 is last read in
+  // slot 4T + 2; group 1 refills it with stage T + 2 in slot 4T + 4 and waits
+  // for it at the end of slot 4T + 6.  Loads of stages past K read nothing
+  // and fill their stage with zeros.
+  if (grp == 0) issueB(0);
+  else issueA(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  barrier_lds();
+  if (grp == 0) {
+    for (int u = 0; u < nu; ++u) {
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(u);  // slot 2u - 1
+      issueB(u + 1);
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      multiply();  // slot 2u
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // B(u + 1)
+      barrier_lds();
+    }
+  } else {
+    barrier_lds();  // slot -1
+    for (int u = 0; u < nu; ++u) {
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(u);  // slot 2u
+      if ((u & 1) == 0) issueA((u >> 1) + 1);
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // kept values of stage (u >> 1) + 1
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      multiply();  // slot 2u + 1
+      __builtin_amdgcn_sched_barrier(0);
+      if (u + 1 < nu) barrier_lds();
+    }
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA outstanding at exit
 
   // epilogue: block (i, j), register r holds D[m][n] with
@@ -187,9 +204,9 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   float* D = (float*)p.D;
   const bool interior = m0 + SP_BM <= p.M && n0 + SP_BN <= p.N;
 #pragma unroll
-  for (int i = 0; i < WT; ++i)
+  for (int i = 0; i < WTM; ++i)
 #pragma unroll
-    for (int j = 0; j < WT; ++j) {
+    for (int j = 0; j < WTN; ++j) {
       const int64_t n = n0 + rbB + 32 * j + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -208,7 +225,7 @@ static hipError_t launch_sparse_fast_one(const SparseArgs& a0, hipStream_t s) {
   a.tiles_n = (int)((a.N + SP_BN - 1) / SP_BN);
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_sparse_fast_kernel<Op, LB>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_sparse_fast_kernel<Op, LB>), dim3((unsigned)blocks), dim3(SP_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -225,7 +242,7 @@ bool sparse_fast_ok(int layoutB, const SparseArgs& a) {
   // every buffer window (and offset into it) must stay below 2 GiB;
   // MN-contiguous B offsets advance by whole stages, up to NST stages past K
   const int64_t lim = (int64_t)1 << 31;
-  const int64_t kpad = (int64_t)fast::SP_NST * fast::SP_KD;
+  const int64_t kpad = 3 * (int64_t)fast::SP_KB;
   const int64_t wa = (int64_t)fast::SP_BM * a.lda_c * 2;
   const int64_t wi = (int64_t)fast::SP_BM * a.ld_idx * 4;
   const int64_t wb = layoutB == LAYOUT_K ? (int64_t)fast::SP_BN * a.ldb * 2 : (a.K + kpad) * a.ldb * 2;
