@@ -255,6 +255,68 @@ __global__ __launch_bounds__(256) void compress24_kernel(CompressArgs p) {
   if (bad && p.violations) atomicAdd(p.violations, bad);
 }
 
+// Vector form for aligned rows (K * elem_bytes a multiple of 16): one lane per
+// 16-byte chunk of a row (G = 2 groups of 16-bit or 4 groups of 8-bit values),
+// consecutive lanes on consecutive chunks, so the 16-byte loads, the 8-byte
+// stores of the kept values and the 1- or 2-byte stores of the codes are all
+// contiguous across a wavefront.  Chunk slots past the last chunk of a row,
+// up to the end of its last index word, write zero codes (the padding of a
+// partial last word).  Same selection rule as compress24_kernel.
+template <int EB, bool INT8>
+__global__ __launch_bounds__(256) void compress24_vec_kernel(CompressArgs p, int64_t slots) {
+  constexpr int G = 16 / (4 * EB);  // groups per chunk
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= p.M * slots) return;
+  const int64_t row = t / slots, c = t % slots;
+  const int64_t nchunks = p.K * EB / 16;
+  uint8_t* idxb = (uint8_t*)(p.idx + row * p.ld_idx);
+  if (c >= nchunks) {
+    if constexpr (G == 2) idxb[c] = 0;
+    else *(uint16_t*)(idxb + 2 * c) = 0;
+    return;
+  }
+  const i32x4 v = *(const i32x4*)(p.A + row * p.lda * EB + c * 16);
+  uint32_t code = 0;
+  uint64_t kept = 0;
+  int bad = 0;
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    uint32_t x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int el = 4 * gi + e;
+      if constexpr (EB == 2) x[e] = ((uint32_t)v[el >> 1] >> (16 * (el & 1))) & 0xFFFFu;
+      else x[e] = ((uint32_t)v[el >> 2] >> (8 * (el & 3))) & 0xFFu;
+    }
+    int pos[4], nz = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool isnz = INT8 ? (x[e] != 0) : nonzero_code<EB>(x[e]);
+      if (isnz) pos[nz++ & 3] = e;
+    }
+    int p0, p1;
+    uint32_t k0, k1;
+    if (nz > 2) {
+      ++bad;
+      p0 = 0; p1 = 1; k0 = 0; k1 = 0;
+    } else {
+      if (nz == 0) { p0 = 0; p1 = 1; }
+      else if (nz == 1) {
+        if (pos[0] == 0) { p0 = 0; p1 = 1; }
+        else { p0 = 0; p1 = pos[0]; }
+      } else { p0 = pos[0]; p1 = pos[1]; }
+      k0 = x[p0]; k1 = x[p1];
+    }
+    code |= (uint32_t)(p0 | (p1 << 2)) << (4 * gi);
+    kept |= (uint64_t)k0 << (2 * gi * 8 * EB);
+    kept |= (uint64_t)k1 << ((2 * gi + 1) * 8 * EB);
+  }
+  *(uint64_t*)(p.Ac + row * p.lda_c * EB + c * 8) = kept;
+  if constexpr (G == 2) idxb[c] = (uint8_t)code;
+  else *(uint16_t*)(idxb + 2 * c) = (uint16_t)code;
+  if (bad && p.violations) atomicAdd(p.violations, bad);
+}
+
 __global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
 
 hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s) {
@@ -264,6 +326,22 @@ hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   const int64_t nwords = (a.K + 31) / 32;
+  const int eb = (dtype == DT_BF16 || dtype == DT_F16) ? 2 : 1;
+  const bool vec = (a.K * eb) % 16 == 0 && (uintptr_t)a.A % 16 == 0 && (a.lda * eb) % 16 == 0 &&
+                   (uintptr_t)a.Ac % 8 == 0 && (a.lda_c * eb) % 8 == 0;
+  if (vec) {
+    const int64_t slots = nwords * (eb == 2 ? 4 : 2);  // chunk slots per row (whole index words)
+    const int64_t threads = a.M * slots;
+    if (threads <= 0) return hipSuccess;
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (eb == 2)
+      hipLaunchKernelGGL((compress24_vec_kernel<2, false>), dim3((unsigned)blocks), dim3(256), 0, s, a, slots);
+    else if (dtype == DT_I8)
+      hipLaunchKernelGGL((compress24_vec_kernel<1, true>), dim3((unsigned)blocks), dim3(256), 0, s, a, slots);
+    else hipLaunchKernelGGL((compress24_vec_kernel<1, false>), dim3((unsigned)blocks), dim3(256), 0, s, a, slots);
+    return hipGetLastError();
+  }
   const int64_t threads = a.M * nwords;
   if (threads <= 0) return hipSuccess;
   const int64_t blocks = (threads + 255) / 256;

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16", "i8", "e4m3", "e5m2"])
-@pytest.mark.parametrize("shape", [(1, 4), (7, 36), (130, 200), (64, 1024), (3, 4100)])
+@pytest.mark.parametrize("shape", [(1, 4), (7, 36), (130, 200), (64, 1024), (3, 4100), (5, 272), (33, 8208)])
 def test_compress24_matches_oracle(dt, shape):
     mcg = need_gpu()
     M, K = shape
@@ -32,19 +32,27 @@ def test_compress24_matches_oracle(dt, shape):
     assert np.array_equal(idx.cpu().numpy().view(np.uint32), oi)
 
 
-def test_compress24_counts_violations():
+@pytest.mark.parametrize("dt", ["i8", "bf16"])
+@pytest.mark.parametrize("K", [256, 36])  # vector path (K * elem_bytes % 16 == 0) and general path
+def test_compress24_counts_violations(dt, K):
     mcg = need_gpu()
     rng = np.random.default_rng(1)
-    M, K = 40, 256
-    A = rng.integers(-2, 3, (M, K)).astype(np.int8)
-    vals = torch.zeros((M, K // 2), dtype=torch.int8, device="cuda")
-    idx = torch.zeros((M, K // 32), dtype=torch.int32, device="cuda")
+    M = 40
+    ints = rng.integers(-2, 3, (M, K))
+    if dt == "i8":
+        A = ints.astype(np.int8)
+        vals = torch.zeros((M, K // 2), dtype=torch.int8, device="cuda")
+    else:
+        A = torch.from_numpy(ints.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        vals = torch.zeros((M, K // 2), dtype=torch.int16, device="cuda")
+    nw = (K + 31) // 32
+    idx = torch.zeros((M, nw), dtype=torch.int32, device="cuda")
     viol = torch.zeros((1,), dtype=torch.int32, device="cuda")
-    mcg.compress24("i8", M, K, dev(A), K, vals, K // 2, idx, K // 32, viol)
+    mcg.compress24(dt, M, K, dev(A), K, vals, K // 2, idx, nw, viol)
     torch.cuda.synchronize()
-    ov, oi, ovio = oracle.compress24("i8", A)
+    ov, oi, ovio = oracle.compress24(dt, A)
     assert ovio > 0 and int(viol.item()) == ovio
-    assert np.array_equal(vals.cpu().numpy(), ov)
+    assert np.array_equal(vals.cpu().numpy().view(ov.dtype).reshape(ov.shape), ov)
     assert np.array_equal(idx.cpu().numpy().view(np.uint32), oi)
 
 
