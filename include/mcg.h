@@ -183,6 +183,15 @@ int mcg_validate_compress24(int dtype, int64_t M, int64_t K, const void* A, int6
                             const void* A_compressed, int64_t lda_c, const uint32_t* A_index,
                             int64_t ld_idx);
 
+/* Kernel selection, for callers that tune shapes and for tests: 1 if gemm_dense
+   (resp. gemm_sparse24) with these arguments runs the 256 x 256 pipelined
+   kernel, 0 if it runs the general kernel (any shape, alignment or leading
+   dimension).  Host-only, no validation, no device access. */
+int mcg_dense_path(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A,
+                   int64_t lda, const void* B, int64_t ldb);
+int mcg_sparse24_path(int layoutB, int64_t M, int64_t N, int64_t K, const void* A_compressed, int64_t lda_c,
+                      const uint32_t* A_index, int64_t ld_idx, const void* B, int64_t ldb);
+
 /* Human-readable name of an mcg_status value (static storage). */
 const char* mcg_status_string(int status);
 

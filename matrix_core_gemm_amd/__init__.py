@@ -30,7 +30,8 @@ STATUS = {0: "MCG_SUCCESS", 1: "MCG_ERR_NULL_POINTER", 2: "MCG_ERR_INVALID_SIZE"
 
 # Every symbol include/mcg.h declares.
 EXPORTS = ("gemm_dense", "gemm_sparse24", "compress24", "compress24_host", "mcg_status_string",
-           "mcg_version", "mcg_validate_dense", "mcg_validate_sparse24", "mcg_validate_compress24")
+           "mcg_version", "mcg_validate_dense", "mcg_validate_sparse24", "mcg_validate_compress24",
+           "mcg_dense_path", "mcg_sparse24_path")
 
 
 class MCGError(RuntimeError):
@@ -60,6 +61,8 @@ _lib.mcg_validate_dense.argtypes = [_i32, _i32, _i32, _i32, _i64, _i64, _i64, _v
 _lib.mcg_validate_sparse24.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
                                        _vp, _i64, _vp, _vp, _i64, _i32, _dbl, _dbl]
 _lib.mcg_validate_compress24.argtypes = [_i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
+_lib.mcg_dense_path.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64]
+_lib.mcg_sparse24_path.argtypes = [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
 
 
 def lib():
@@ -150,6 +153,18 @@ def validate_sparse24(dtypeA, dtypeB, layoutB, M, N, K, A_compressed, lda_c, A_i
 def validate_compress24(dtype, M, K, A, lda, A_compressed, lda_c, A_index, ld_idx) -> int:
     return _lib.mcg_validate_compress24(_dt(dtype), M, K, _ptr(A), lda, _ptr(A_compressed), lda_c,
                                         _ptr(A_index), ld_idx)
+
+
+def dense_path(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb) -> int:
+    """1 if gemm_dense with these arguments runs the 256 x 256 kernel, else 0."""
+    return _lib.mcg_dense_path(_dt(dtypeA), _lay(layoutA), _lay(layoutB), M, N, K, _ptr(A), lda,
+                               _ptr(B), ldb)
+
+
+def sparse24_path(layoutB, M, N, K, A_compressed, lda_c, A_index, ld_idx, B, ldb) -> int:
+    """1 if gemm_sparse24 with these arguments runs the 256 x 256 kernel, else 0."""
+    return _lib.mcg_sparse24_path(_lay(layoutB), M, N, K, _ptr(A_compressed), lda_c, _ptr(A_index),
+                                  ld_idx, _ptr(B), ldb)
 
 
 def status_string(status: int) -> str:

@@ -90,6 +90,11 @@ int mcg_validate_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t
   return MCG_SUCCESS;
 }
 
+// 16-byte aligned operands whose rows are whole 16-byte chunks: the vector load paths.
+static bool dense_aligned(int eb, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb) {
+  return K == 0 || (aligned_to(A, 16) && aligned_to(B, 16) && (lda * eb) % 16 == 0 && (ldb * eb) % 16 == 0);
+}
+
 int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
                const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, void* D,
                int64_t ldc, int dtypeD, double alpha, double beta, float scaleA, float scaleB,
@@ -118,8 +123,7 @@ int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int6
   a.beta_i = dtypeA == MCG_I8 ? (int)beta : 0;
   a.use_c = beta != 0.0;
   a.vec_cd = aligned_to(D, 16) && (!a.use_c || aligned_to(C, 16)) && ldc % 4 == 0;
-  const bool aligned = K == 0 || (aligned_to(A, 16) && aligned_to(B, 16) && (lda * eb) % 16 == 0 &&
-                                  (ldb * eb) % 16 == 0);
+  const bool aligned = dense_aligned(eb, K, A, lda, B, ldb);
   if (mcg::fast_path_ok(dtypeA, layoutA, layoutB, a, aligned))
     return hip_status(mcg::launch_fast(dtypeA, dtypeB, layoutA, layoutB, a, (hipStream_t)stream));
   return hip_status(mcg::launch_dense(dtypeA, dtypeB, layoutA, layoutB, aligned, a, (hipStream_t)stream));
@@ -257,6 +261,36 @@ int compress24_host(int dtype, int64_t M, int64_t K, const void* A, int64_t lda,
     }
   }
   return bad ? MCG_ERR_NOT_2_4_SPARSE : MCG_SUCCESS;
+}
+
+int mcg_dense_path(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A,
+                   int64_t lda, const void* B, int64_t ldb) {
+  if (dtypeA < MCG_BF16 || dtypeA > MCG_FP8_E5M2) return 0;
+  const int eb = elem_bytes(dtypeA);
+  mcg::DenseArgs a{};
+  a.A = (const char*)A;
+  a.B = (const char*)B;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.lda = lda;
+  a.ldb = ldb;
+  return mcg::fast_path_ok(dtypeA, layoutA, layoutB, a, dense_aligned(eb, K, A, lda, B, ldb)) ? 1 : 0;
+}
+
+int mcg_sparse24_path(int layoutB, int64_t M, int64_t N, int64_t K, const void* A_compressed, int64_t lda_c,
+                      const uint32_t* A_index, int64_t ld_idx, const void* B, int64_t ldb) {
+  mcg::SparseArgs a{};
+  a.Ac = (const char*)A_compressed;
+  a.idx = A_index;
+  a.B = (const char*)B;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.lda_c = lda_c;
+  a.ld_idx = ld_idx;
+  a.ldb = ldb;
+  return mcg::sparse_fast_ok(layoutB, a) ? 1 : 0;
 }
 
 const char* mcg_status_string(int status) {

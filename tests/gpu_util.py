@@ -29,11 +29,14 @@ def dev(a: np.ndarray) -> torch.Tensor:
 
 
 def run_dense(mcg, dtA, dtB, layA, layB, M, N, K, A, lda, B, ldb, C=None, ldc=None, alpha=1.0,
-              beta=0.0, sA=1.0, sB=1.0, d_fill=float("nan"), c_dev=None):
-    """Run gemm_dense on host code arrays; returns D (numpy, shape (M, ldc))."""
+              beta=0.0, sA=1.0, sB=1.0, d_fill=float("nan"), c_dev=None, expect_path=None):
+    """Run gemm_dense on host code arrays; returns D (numpy, shape (M, ldc)).
+    expect_path: 1 / 0 asserts that the call runs the 256 x 256 / general kernel."""
     i8 = dtA == "i8"
     ldc = N if ldc is None else ldc
     dA, dB = dev(A), dev(B)
+    if expect_path is not None:
+        assert mcg.dense_path(dtA, layA, layB, M, N, K, dA, lda, dB, ldb) == expect_path
     if c_dev is None and C is not None:
         c_dev = dev(C)
     if i8:

@@ -20,6 +20,9 @@ LAYOUTS = [("k_contig", "k_contig"), ("k_contig", "mn_contig"), ("mn_contig", "k
            ("mn_contig", "mn_contig")]
 
 
+SMALL = {"bf16": 8, "f16": 8, "e4m3": 16, "e5m2": 8}
+
+
 def operands(dtA, dtB, layA, layB, M, N, K, dist=None, pad=0, seed=0):
     dist = dist or ("int8" if dtA == "i8" else "normal")
     fp8 = dtA in ("e4m3", "e5m2")
@@ -31,7 +34,7 @@ def operands(dtA, dtB, layA, layB, M, N, K, dist=None, pad=0, seed=0):
 
 
 def check_case(mcg, dtA, dtB, layA, layB, M, N, K, pad=0, beta=1.0, alpha=None, ldc_pad=0, seed=0,
-               dist=None):
+               dist=None, expect_path=None):
     say(f"case {dtA}x{dtB} {layA}/{layB} M={M} N={N} K={K} pad={pad} beta={beta}")
     A, B = operands(dtA, dtB, layA, layB, M, N, K, dist, pad, seed)
     ldc = N + ldc_pad
@@ -42,7 +45,7 @@ def check_case(mcg, dtA, dtB, layA, layB, M, N, K, pad=0, beta=1.0, alpha=None, 
     if beta != 0:
         C = W.c_matrix(M, N, "int20" if i8 else "normal", seed=10 * seed + 2, ldc=ldc)
     d = run_dense(mcg, dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, ldc, alpha,
-                  beta, A.scale, B.scale)
+                  beta, A.scale, B.scale, expect_path=expect_path)
     ref, s = oracle_dense(dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, ldc,
                           alpha, beta, A.scale, B.scale)
     compare(dtA, d[:M, :N], ref, s, K, alpha, A.scale, B.scale, beta,
@@ -74,7 +77,41 @@ def test_config_bf16_256_cubed():
 def test_multi_tile_ragged(dtA, dtB, layA, layB):
     """Several tiles with ragged tails in M, N and K (vector-load path)."""
     mcg = need_gpu()
-    check_case(mcg, dtA, dtB, layA, layB, 300, 200, 300, pad=20, ldc_pad=4)
+    check_case(mcg, dtA, dtB, layA, layB, 300, 200, 300, pad=20, ldc_pad=4, expect_path=0)
+
+
+# Shapes taken by the 256 x 256 kernel for every dtype and layout (M, N >= 256,
+# K and every leading dimension a multiple of 16 elements): ragged M and N tiles,
+# K ending inside a 128-byte stage, a single partial stage, padded leading
+# dimensions.
+FAST_SHAPES = [(528, 304, 208, 16), (256, 272, 80, 0), (304, 528, 1040, 32)]
+
+
+@pytest.mark.parametrize("dtA,dtB", PAIRS)
+@pytest.mark.parametrize("layA,layB", LAYOUTS)
+@pytest.mark.parametrize("shape", FAST_SHAPES, ids=["528x304x208", "256x272x80", "304x528x1040"])
+def test_256_tile_path_ragged(dtA, dtB, layA, layB, shape):
+    mcg = need_gpu()
+    M, N, K, pad = shape
+    check_case(mcg, dtA, dtB, layA, layB, M, N, K, pad=pad, ldc_pad=4, seed=3, expect_path=1)
+
+
+@pytest.mark.parametrize("dtA,dtB", [p for p in PAIRS if p[0] != "i8"])
+@pytest.mark.parametrize("layA,layB", LAYOUTS)
+def test_small_integers_bit_exact_256_tiles(dtA, dtB, layA, layB):
+    """Exactly representable partial sums on the 256 x 256 kernel (ragged M and N,
+    K ending inside a stage): the result must equal the oracle bit for bit."""
+    mcg = need_gpu()
+    M, N, K = 512, 304, 1104
+    r = min(SMALL[dtA], SMALL[dtB])
+    A = W.operand("A", dtA, M, K, f"smallint{r}", layA, seed=15)
+    B = W.operand("B", dtB, K, N, f"smallint{r}", layB, seed=16)
+    C = np.round(W.c_matrix(M, N, "normal", seed=17) * 1000).astype(np.float32)
+    d = run_dense(mcg, dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, N, 1.0, 1.0,
+                  expect_path=1)
+    ref, _ = oracle.gemm_float(dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, N,
+                               1.0, 1.0)
+    assert np.array_equal(d, ref)
 
 
 @pytest.mark.parametrize("dtA,dtB", PAIRS)
@@ -93,9 +130,6 @@ def test_beta_zero_and_alpha(dtA, dtB):
     check_case(mcg, dtA, dtB, "k_contig", "k_contig", 130, 140, 256, beta=0.0)
     check_case(mcg, dtA, dtB, "mn_contig", "k_contig", 130, 140, 256, beta=-2 if dtA == "i8" else 0.5,
                alpha=-1 if dtA == "i8" else -0.25)
-
-
-SMALL = {"bf16": 8, "f16": 8, "e4m3": 16, "e5m2": 8}
 
 
 @pytest.mark.parametrize("dtA,dtB", [p for p in PAIRS if p[0] != "i8"])
@@ -212,7 +246,7 @@ def sampled_check(mcg, wl, seed=0):
     B = W.operand("B", wl.dtB, K, N, wl.dist, wl.layB, fp8_scaled=wl.fp8_scaled)
     C = W.c_matrix(M, N, wl.c_dist) if wl.c_dist else None
     d = run_dense(mcg, wl.dtA, wl.dtB, wl.layA, wl.layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C,
-                  N, wl.alpha, wl.beta, A.scale, B.scale)
+                  N, wl.alpha, wl.beta, A.scale, B.scale, expect_path=1)
     rows, cols = W.sample_coords(M, N, n_random=4096, full_rows=(0, M // 2 + 5, M - 1),
                                  full_cols=(1, N - 1))
     ref, s = oracle_dense(wl.dtA, wl.dtB, wl.layA, wl.layB, M, N, K, A.codes, A.ld, B.codes, B.ld,

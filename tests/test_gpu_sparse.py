@@ -119,8 +119,10 @@ def test_sparse_256_tile_path(dt, layB, shape, pads):
     ip = np.full((M, ld_idx), 0xFFFFFFFF, np.uint32)  # padding words are never read
     ip[:, :nw] = i
     D = torch.full((M, N), float("nan"), device="cuda")
-    mcg.gemm_sparse24(dt, dt, layB, M, N, K, dev(vp), lda_c, dev(ip.view(np.int32)), ld_idx,
-                      dev(B.codes), B.ld, dev(C), D, N, "f32", 1.5, -0.5)
+    dv, di, dbb = dev(vp), dev(ip.view(np.int32)), dev(B.codes)
+    assert mcg.sparse24_path(layB, M, N, K, dv, lda_c, di, ld_idx, dbb, B.ld) == 1
+    mcg.gemm_sparse24(dt, dt, layB, M, N, K, dv, lda_c, di, ld_idx, dbb, B.ld, dev(C), D, N, "f32",
+                      1.5, -0.5)
     torch.cuda.synchronize()
     ref, s = oracle.gemm_sparse24(dt, dt, layB, M, N, K, v, i, B.codes, B.ld, C, N, 1.5, -0.5)
     compare(dt, D.cpu().numpy(), ref, s, K, 1.5, beta=-0.5, c=C, what=f"sparse256 {dt} {layB} {shape}")
