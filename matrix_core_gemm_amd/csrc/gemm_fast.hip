@@ -207,6 +207,24 @@ void gemm_fast_kernel(DenseArgs p) {
 #pragma unroll
         for (int j = 0; j < WTN; ++j) Op::mma(acc[i][j], fb[s][j], fa[s][i]);
   };
+  // Memory phase of half tile (t, H): this group's DMA half and the fragment
+  // reads.  The DMA targets another stage than the reads, so with K-contiguous
+  // operands it goes first (more time in flight).  Transposing reads of an
+  // MN-contiguous operand are preceded by a compiler-inserted wait for all of
+  // the wave's LDS DMA, so there the reads go first.
+  auto dma = [&](auto hc, int t) {
+    if constexpr (decltype(hc)::value == 0) issueA(t + 1);
+    else issueB(t + 2);
+  };
+  auto mem = [&](auto hc, int t) {
+    if constexpr (LA == LAYOUT_K && LB == LAYOUT_K) {
+      dma(hc, t);
+      read_frags(t, decltype(hc)::value);
+    } else {
+      read_frags(t, decltype(hc)::value);
+      dma(hc, t);
+    }
+  };
 
   // Half tiles u = 2t + h.  Group 0 reads half u in slot 2u - 1 and multiplies
   // it in slot 2u; group 1 reads it in slot 2u and multiplies it in slot
@@ -226,35 +244,44 @@ void gemm_fast_kernel(DenseArgs p) {
   issueB(1);
   asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // own shares of tile 0 have landed
   barrier_lds();
-  const int nu = 2 * nk;
+  // The two half tiles of a K tile are written out (no run-time choice between
+  // the A and B loads, whose buffer descriptors then stay in scalar registers).
   if (grp == 0) {
-    for (int u = 0; u < nu; ++u) {
-      const int t = u >> 1, h = u & 1;
+    for (int t = 0; t < nk; ++t) {
       __builtin_amdgcn_sched_barrier(0);
-      read_frags(t, h);  // slot 2u - 1: memory phase
-      if (h == 0) issueA(t + 1);
-      else issueB(t + 2);
+      mem(std::integral_constant<int, 0>{}, t);  // slot 4t - 1
       barrier_lds();
       __builtin_amdgcn_sched_barrier(0);
-      multiply();  // slot 2u
+      multiply();  // slot 4t
       __builtin_amdgcn_sched_barrier(0);
-      if (h == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      mem(std::integral_constant<int, 1>{}, t);  // slot 4t + 1
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      multiply();  // slot 4t + 2
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // own shares of tile t+1
       barrier_lds();
     }
   } else {
     barrier_lds();  // slot -1
-    for (int u = 0; u < nu; ++u) {
-      const int t = u >> 1, h = u & 1;
+    for (int t = 0; t < nk; ++t) {
       __builtin_amdgcn_sched_barrier(0);
-      read_frags(t, h);  // slot 2u: memory phase
-      if (h == 0) issueA(t + 1);
-      else issueB(t + 2);
-      if (h == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      mem(std::integral_constant<int, 0>{}, t);  // slot 4t
       barrier_lds();
       __builtin_amdgcn_sched_barrier(0);
-      multiply();  // slot 2u + 1
+      multiply();  // slot 4t + 1
       __builtin_amdgcn_sched_barrier(0);
-      if (u + 1 < nu) barrier_lds();
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      mem(std::integral_constant<int, 1>{}, t);  // slot 4t + 2
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // own shares of tile t+1
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      multiply();  // slot 4t + 3
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < nk) barrier_lds();
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA outstanding at exit
