@@ -37,6 +37,11 @@ _LIB_PATH = os.path.join(_HERE, "_liboracle.so")
 
 DTYPES = {"bf16": 0, "f16": 1, "i8": 2, "e4m3": 3, "e5m2": 4}
 LAYOUTS = {"k_contig": 0, "mn_contig": 1}
+# output (and C) formats of the float GEMM; unit roundoff and half the smallest
+# subnormal of each (the largest rounding error of a result in that format)
+OUTS = {"f32": 0, "bf16": 1, "f16": 2}
+OUT_UNIT = {"f32": 2.0 ** -24, "bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+OUT_SUBNORMAL_HALF = {"f32": 2.0 ** -150, "bf16": 2.0 ** -134, "f16": 2.0 ** -25}
 CODE_NP = {"bf16": np.uint16, "f16": np.uint16, "i8": np.int8, "e4m3": np.uint8, "e5m2": np.uint8}
 
 U = 2.0 ** -24  # unit roundoff of binary32
@@ -63,9 +68,10 @@ def lib():
         i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
         L.orc_decode.argtypes = [i32, i64, vp, vp]
         L.orc_gemm_float_elems.argtypes = [i32, i32, i32, i32, i64, i64, i64, vp, i64, vp, i64,
-                                           vp, i64, dbl, dbl, dbl, dbl, i64, vp, vp, vp, vp]
+                                           vp, i64, i32, dbl, dbl, dbl, dbl, i64, vp, vp, vp, vp]
         L.orc_gemm_float_full.argtypes = [i32, i32, i32, i32, i64, i64, i64, vp, i64, vp, i64,
-                                          vp, i64, dbl, dbl, dbl, dbl, vp, vp]
+                                          vp, i64, i32, dbl, dbl, dbl, dbl, vp, vp]
+        L.orc_round.argtypes = [i32, i64, vp, vp]
         L.orc_gemm_i8_elems.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64,
                                         i64, i64, i64, vp, vp, vp]
         L.orc_gemm_i8_full.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64,
@@ -103,20 +109,33 @@ def decode(dtype: str, codes) -> np.ndarray:
     return out
 
 
+def round_to(out, x):
+    """Round binary64 values once to the output format `out` (f32, bf16, f16):
+    nearest, ties to even, gradual underflow, overflow to infinity."""
+    x = _flat(np.asarray(x, np.float64), np.float64)
+    y = np.empty_like(x)
+    rc = lib().orc_round(OUTS[out], x.size, _ptr(x), _ptr(y))
+    if rc != 0:
+        raise ValueError(f"oracle round rejected its arguments ({rc})")
+    return y
+
+
 def gemm_float(dtA, dtB, layA, layB, M, N, K, A, lda, B, ldb, C=None, ldc=None,
-               alpha=1.0, beta=0.0, sA=1.0, sB=1.0, rows=None, cols=None):
+               alpha=1.0, beta=0.0, sA=1.0, sB=1.0, rows=None, cols=None, out="f32"):
     """Reference for the float paths.
 
     A and B are flat (or any-shape, contiguous) arrays of raw codes addressed
-    through (layout, leading dimension) as described in oracle.c.  C is a
-    float32 array addressed as C[i*ldc + j].  With rows/cols given, only those
-    output elements are computed and 1-D arrays are returned; otherwise full
-    M x N arrays.  Returns (d_ref float32, abs_sum float64).
+    through (layout, leading dimension) as described in oracle.c.  C is an
+    array in the output format `out` (float32, or bfloat16 / binary16 codes as
+    uint16) addressed as C[i*ldc + j].  With rows/cols given, only those output
+    elements are computed and 1-D arrays are returned; otherwise full M x N
+    arrays.  Returns (d_ref float32 holding the value in the output format,
+    abs_sum float64).
     """
     A = _flat(A, CODE_NP[dtA])
     B = _flat(B, CODE_NP[dtB])
     if beta != 0.0:
-        C = _flat(C, np.float32)
+        C = _flat(C, np.float32 if out == "f32" else np.uint16)
     else:
         C = None
     ldc = N if ldc is None else ldc
@@ -125,7 +144,7 @@ def gemm_float(dtA, dtB, layA, layB, M, N, K, A, lda, B, ldb, C=None, ldc=None,
         d = np.empty((M, N), np.float32)
         s = np.empty((M, N), np.float64)
         rc = L.orc_gemm_float_full(DTYPES[dtA], DTYPES[dtB], LAYOUTS[layA], LAYOUTS[layB],
-                                   M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
+                                   M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, OUTS[out],
                                    float(alpha), float(beta), float(sA), float(sB),
                                    _ptr(d), _ptr(s))
     else:
@@ -135,7 +154,7 @@ def gemm_float(dtA, dtB, layA, layB, M, N, K, A, lda, B, ldb, C=None, ldc=None,
         d = np.empty(rows.shape, np.float32)
         s = np.empty(rows.shape, np.float64)
         rc = L.orc_gemm_float_elems(DTYPES[dtA], DTYPES[dtB], LAYOUTS[layA], LAYOUTS[layB],
-                                    M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc,
+                                    M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, OUTS[out],
                                     float(alpha), float(beta), float(sA), float(sB),
                                     rows.size, _ptr(rows), _ptr(cols), _ptr(d), _ptr(s))
     if rc != 0:
@@ -197,30 +216,38 @@ def decompress24(dtype, vals, idx, K):
 
 
 def gemm_sparse24(dtA, dtB, layB, M, N, K, vals, idx, B, ldb, C=None, ldc=None,
-                  alpha=1.0, beta=0.0, rows=None, cols=None):
+                  alpha=1.0, beta=0.0, rows=None, cols=None, out="f32"):
     """Sparse-A reference: decompress A, then the dense float GEMM with the
     dense K (A row-major, i.e. K-contiguous)."""
     A = decompress24(dtA, vals, idx, K)
     return gemm_float(dtA, dtB, "k_contig", layB, M, N, K, A, K, B, ldb, C, ldc,
-                      alpha, beta, 1.0, 1.0, rows, cols)
+                      alpha, beta, 1.0, 1.0, rows, cols, out)
 
 
-def float_bound(d_ref, abs_sum, K, alpha=1.0, sA=1.0, sB=1.0, beta=0.0, c=None):
-    """Per-element acceptance bound for float results (binary64)."""
-    bound = (4.0 * U * (K + 2) * abs(alpha * sA * sB)) * np.asarray(abs_sum, np.float64) \
-        + U * np.abs(np.asarray(d_ref, np.float64))
+def float_bound(d_ref, abs_sum, K, alpha=1.0, sA=1.0, sB=1.0, beta=0.0, c=None, out="f32"):
+    """Per-element acceptance bound for float results (binary64).
+
+    For a binary32 result: 4u(K+2)|alpha sA sB| S + u|D_ref| (u = 2^-24), plus
+    u|beta c| when beta is not 0 or +-1.  A result delivered in bfloat16 or
+    binary16 is the binary32 value rounded once more, while the reference is
+    the exact value rounded once, so both roundings to the output format are
+    added: e + u_out (2 |D_ref| + e) + 2 * (half the smallest subnormal)."""
+    d = np.abs(np.asarray(d_ref, np.float64))
+    bound = (4.0 * U * (K + 2) * abs(alpha * sA * sB)) * np.asarray(abs_sum, np.float64) + U * d
     if beta not in (0.0, 1.0, -1.0) and c is not None:
         bound = bound + U * np.abs(beta * np.asarray(c, np.float64))
+    if out != "f32":
+        bound = bound + OUT_UNIT[out] * (2.0 * d + bound) + 2.0 * OUT_SUBNORMAL_HALF[out]
     return bound
 
 
-def check_float(d_gpu, d_ref, abs_sum, K, alpha=1.0, sA=1.0, sB=1.0, beta=0.0, c=None):
+def check_float(d_gpu, d_ref, abs_sum, K, alpha=1.0, sA=1.0, sB=1.0, beta=0.0, c=None, out="f32"):
     """Compare GPU float results with the oracle.  Returns a dict with ``ok``,
     the number of violations (NaN counts as one), max |delta|/bound and the
     first offending flat indices."""
     g = np.asarray(d_gpu, np.float64).ravel()
     r = np.asarray(d_ref, np.float64).ravel()
-    b = float_bound(d_ref, abs_sum, K, alpha, sA, sB, beta, c).ravel()
+    b = float_bound(d_ref, abs_sum, K, alpha, sA, sB, beta, c, out).ravel()
     delta = np.abs(g - r)
     bad = ~(delta <= b)  # NaN compares false, so it is flagged
     with np.errstate(divide="ignore", invalid="ignore"):

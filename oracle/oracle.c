@@ -25,6 +25,12 @@
  *    binary64, and the result is rounded ONCE to binary32 (round to nearest
  *    even, the C cast).  The same loop returns S = sum_k |a_ik*b_kj| for the
  *    error bound.
+ *  - Float paths may also deliver D (and read C) in bfloat16 or binary16: the
+ *    exact binary64 value t is then rounded ONCE, directly to that format
+ *    (round to nearest, ties to even; gradual underflow; magnitudes beyond the
+ *    largest finite value become infinities), with the format parameters of
+ *    Table 1 (precision 8 / 11, smallest normal 2^-126 / 2^-14, largest
+ *    finite (2 - 2^-7) 2^127 / 65504).
  *  - int8 path: exact int64 accumulation, t = alpha*acc + beta*c, wrapped to
  *    int32 (mod 2^32).
  *  - 2:4 structured sparsity ("RDNA4 sparse WMMA builtins", Structured
@@ -48,6 +54,8 @@
 enum { ORC_BF16 = 0, ORC_F16 = 1, ORC_I8 = 2, ORC_E4M3 = 3, ORC_E5M2 = 4 };
 enum { ORC_K_CONTIG = 0, ORC_MN_CONTIG = 1 };
 enum { ORC_OK = 0, ORC_BAD_ARG = -1, ORC_BAD_INDEX = -2 };
+/* output (and C) formats of the float GEMM */
+enum { ORC_OUT_F32 = 0, ORC_OUT_BF16 = 1, ORC_OUT_F16 = 2 };
 
 /* ---------------------------------------------------------------- decoders */
 
@@ -120,6 +128,50 @@ static int elem_bytes(int dtype) {
 
 static int valid_dtype(int d) { return d >= ORC_BF16 && d <= ORC_E5M2; }
 
+/* ------------------------------------------------------------- rounding */
+
+/* Round t to the binary format with p significant bits, smallest normal
+ * exponent emin and largest exponent emax: the representable numbers near t
+ * are the integer multiples of the quantum 2^(max(E, emin) - p + 1), where E
+ * is the exponent of t's leading bit; the nearest multiple is taken, a tie
+ * going to the even multiple (rint in the default rounding mode); results
+ * beyond the largest finite value (2 - 2^(1-p)) 2^emax become infinities.
+ * Scaling by powers of two is exact in binary64 for every t used here. */
+static double round_to_format(double t, int p, int emin, int emax) {
+    if (t == 0.0 || !isfinite(t)) return t;
+    int ex;
+    frexp(t, &ex);                       /* |t| = m 2^ex, 0.5 <= m < 1 */
+    const int E = ex - 1;                /* exponent of the leading bit */
+    const int q = (E > emin ? E : emin) - p + 1;
+    const double r = ldexp(rint(ldexp(t, -q)), q);
+    const double maxf = ldexp(2.0 - ldexp(1.0, 1 - p), emax);
+    if (fabs(r) > maxf) return r > 0 ? INFINITY : -INFINITY;
+    return r;
+}
+
+static double round_out(int outfmt, double t) {
+    switch (outfmt) {
+    case ORC_OUT_BF16: return round_to_format(t, 8, -126, 127);
+    case ORC_OUT_F16:  return round_to_format(t, 11, -14, 15);
+    default:           return (double)(float)t;  /* binary32: the C cast rounds to nearest even */
+    }
+}
+
+static double dec_out(int outfmt, const void* base, int64_t idx) {
+    switch (outfmt) {
+    case ORC_OUT_BF16: return dec_bf16(((const uint16_t*)base)[idx]);
+    case ORC_OUT_F16:  return dec_f16(((const uint16_t*)base)[idx]);
+    default:           return (double)((const float*)base)[idx];
+    }
+}
+
+/* Element-wise rounding (exposed so that the rounding itself can be tested). */
+int orc_round(int outfmt, int64_t n, const double* src, double* dst) {
+    if (outfmt < ORC_OUT_F32 || outfmt > ORC_OUT_F16 || n < 0 || (n > 0 && (!src || !dst))) return ORC_BAD_ARG;
+    for (int64_t i = 0; i < n; ++i) dst[i] = round_out(outfmt, src[i]);
+    return ORC_OK;
+}
+
 int orc_decode(int dtype, int64_t n, const void* src, double* dst) {
     if (!valid_dtype(dtype) || n < 0 || (n > 0 && (!src || !dst))) return ORC_BAD_ARG;
     for (int64_t t = 0; t < n; ++t) dst[t] = dec(dtype, src, t);
@@ -146,6 +198,7 @@ typedef struct {
     const void* A; int64_t lda;
     const void* B; int64_t ldb;
     const void* C; int64_t ldc;
+    int outfmt;
 } Gemm;
 
 static int check_gemm(const Gemm* g, int need_c) {
@@ -160,7 +213,8 @@ static int check_gemm(const Gemm* g, int need_c) {
 }
 
 /* One output element of the float GEMM: ascending-k binary64 sum of exact
- * products, then the alpha/beta combination, then one rounding to binary32. */
+ * products, then the alpha/beta combination, then one rounding to the output
+ * format (the rounded value is exact in binary32, which carries it back). */
 static void float_elem(const Gemm* g, double alpha, double beta, double sA, double sB,
                        int64_t i, int64_t j, float* d, double* s) {
     double acc = 0.0, sabs = 0.0;
@@ -171,8 +225,8 @@ static void float_elem(const Gemm* g, double alpha, double beta, double sA, doub
         sabs += fabs(p);
     }
     double t = (alpha * sA * sB) * acc;
-    if (beta != 0.0) t += beta * (double)((const float*)g->C)[i * g->ldc + j];
-    *d = (float)t;
+    if (beta != 0.0) t += beta * dec_out(g->outfmt, g->C, i * g->ldc + j);
+    *d = (float)round_out(g->outfmt, t);
     *s = sabs;
 }
 
@@ -193,12 +247,13 @@ static int32_t i8_elem(const Gemm* g, int64_t alpha, int64_t beta, int64_t i, in
 int orc_gemm_float_elems(int dtA, int dtB, int layA, int layB,
                          int64_t M, int64_t N, int64_t K,
                          const void* A, int64_t lda, const void* B, int64_t ldb,
-                         const float* C, int64_t ldc,
+                         const void* C, int64_t ldc, int outfmt,
                          double alpha, double beta, double sA, double sB,
                          int64_t n, const int64_t* rows, const int64_t* cols,
                          float* d_ref, double* abs_sum) {
-    Gemm g = {dtA, dtB, layA, layB, M, N, K, A, lda, B, ldb, C, ldc};
+    Gemm g = {dtA, dtB, layA, layB, M, N, K, A, lda, B, ldb, C, ldc, outfmt};
     if (dtA == ORC_I8 || dtB == ORC_I8) return ORC_BAD_ARG;
+    if (outfmt < ORC_OUT_F32 || outfmt > ORC_OUT_F16) return ORC_BAD_ARG;
     if (check_gemm(&g, beta != 0.0) != ORC_OK || n < 0) return ORC_BAD_ARG;
     for (int64_t t = 0; t < n; ++t)
         if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N) return ORC_BAD_ARG;
@@ -212,11 +267,12 @@ int orc_gemm_float_elems(int dtA, int dtB, int layA, int layB,
 int orc_gemm_float_full(int dtA, int dtB, int layA, int layB,
                         int64_t M, int64_t N, int64_t K,
                         const void* A, int64_t lda, const void* B, int64_t ldb,
-                        const float* C, int64_t ldc,
+                        const void* C, int64_t ldc, int outfmt,
                         double alpha, double beta, double sA, double sB,
                         float* d_ref, double* abs_sum) {
-    Gemm g = {dtA, dtB, layA, layB, M, N, K, A, lda, B, ldb, C, ldc};
+    Gemm g = {dtA, dtB, layA, layB, M, N, K, A, lda, B, ldb, C, ldc, outfmt};
     if (dtA == ORC_I8 || dtB == ORC_I8) return ORC_BAD_ARG;
+    if (outfmt < ORC_OUT_F32 || outfmt > ORC_OUT_F16) return ORC_BAD_ARG;
     if (check_gemm(&g, beta != 0.0) != ORC_OK) return ORC_BAD_ARG;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < M; ++i)
@@ -230,7 +286,7 @@ int orc_gemm_i8_elems(int layA, int layB, int64_t M, int64_t N, int64_t K,
                       const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
                       const int32_t* C, int64_t ldc, int64_t alpha, int64_t beta,
                       int64_t n, const int64_t* rows, const int64_t* cols, int32_t* d_ref) {
-    Gemm g = {ORC_I8, ORC_I8, layA, layB, M, N, K, A, lda, B, ldb, C, ldc};
+    Gemm g = {ORC_I8, ORC_I8, layA, layB, M, N, K, A, lda, B, ldb, C, ldc, ORC_OUT_F32};
     if (check_gemm(&g, beta != 0) != ORC_OK || n < 0) return ORC_BAD_ARG;
     for (int64_t t = 0; t < n; ++t)
         if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N) return ORC_BAD_ARG;
@@ -243,7 +299,7 @@ int orc_gemm_i8_elems(int layA, int layB, int64_t M, int64_t N, int64_t K,
 int orc_gemm_i8_full(int layA, int layB, int64_t M, int64_t N, int64_t K,
                      const int8_t* A, int64_t lda, const int8_t* B, int64_t ldb,
                      const int32_t* C, int64_t ldc, int64_t alpha, int64_t beta, int32_t* d_ref) {
-    Gemm g = {ORC_I8, ORC_I8, layA, layB, M, N, K, A, lda, B, ldb, C, ldc};
+    Gemm g = {ORC_I8, ORC_I8, layA, layB, M, N, K, A, lda, B, ldb, C, ldc, ORC_OUT_F32};
     if (check_gemm(&g, beta != 0) != ORC_OK) return ORC_BAD_ARG;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < M; ++i)
