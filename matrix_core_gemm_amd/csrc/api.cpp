@@ -14,6 +14,12 @@ constexpr int kVersion = 100;  // 0.1.0
 
 bool is_float8(int dt) { return dt == MCG_FP8_E4M3 || dt == MCG_FP8_E5M2; }
 bool is_in_dtype(int dt) { return dt >= MCG_BF16 && dt <= MCG_FP8_E5M2; }
+// Output format of D (and C) for the kernels; 0 for binary32 / int32.
+static int out_format(int dtypeD) {
+  return dtypeD == MCG_BF16 ? mcg::OUT_BF16 : dtypeD == MCG_F16 ? mcg::OUT_F16 : mcg::OUT_32;
+}
+static bool float_out(int dtypeD) { return dtypeD == MCG_F32 || dtypeD == MCG_BF16 || dtypeD == MCG_F16; }
+
 int elem_bytes(int dt) {
   switch (dt) {
     case MCG_BF16:
@@ -65,7 +71,7 @@ int mcg_validate_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t
   if (!f8 && dtypeA != dtypeB) return MCG_ERR_UNSUPPORTED_DTYPE;
   if (is_float8(dtypeA) != is_float8(dtypeB)) return MCG_ERR_UNSUPPORTED_DTYPE;
   const bool i8 = dtypeA == MCG_I8;
-  if (dtypeD != (i8 ? MCG_I32 : MCG_F32)) return MCG_ERR_UNSUPPORTED_DTYPE;
+  if (i8 ? dtypeD != MCG_I32 : !float_out(dtypeD)) return MCG_ERR_UNSUPPORTED_DTYPE;
   if (!valid_layout(layoutA) || !valid_layout(layoutB)) return MCG_ERR_UNSUPPORTED_DTYPE;
   if (M < 0 || N < 0 || K < 0) return MCG_ERR_INVALID_SIZE;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return MCG_ERR_INVALID_SIZE;
@@ -77,8 +83,9 @@ int mcg_validate_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t
   const int64_t min_ldb = layoutB == MCG_K_CONTIG ? K : N;
   if (lda < (min_lda > 1 ? min_lda : 1) || ldb < (min_ldb > 1 ? min_ldb : 1) || ldc < N)
     return MCG_ERR_INVALID_LD;
+  const int ebd = elem_bytes(dtypeD);
   if (!aligned_to(A, elem_bytes(dtypeA)) || !aligned_to(B, elem_bytes(dtypeB)) ||
-      !aligned_to(D, 4) || (C && !aligned_to(C, 4)))
+      !aligned_to(D, ebd) || (C && !aligned_to(C, ebd)))
     return MCG_ERR_MISALIGNED;
   if (i8) {
     if (!int32_integral(alpha) || !int32_integral(beta)) return MCG_ERR_INVALID_VALUE;
@@ -122,7 +129,9 @@ int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int6
   a.alpha_i = dtypeA == MCG_I8 ? (int)alpha : 0;
   a.beta_i = dtypeA == MCG_I8 ? (int)beta : 0;
   a.use_c = beta != 0.0;
-  a.vec_cd = aligned_to(D, 16) && (!a.use_c || aligned_to(C, 16)) && ldc % 4 == 0;
+  a.out = out_format(dtypeD);
+  const int vb = 4 * elem_bytes(dtypeD);  // bytes of 4 consecutive C/D elements
+  a.vec_cd = aligned_to(D, vb) && (!a.use_c || aligned_to(C, vb)) && ldc % 4 == 0;
   const bool aligned = dense_aligned(eb, K, A, lda, B, ldb);
   if (mcg::fast_path_ok(dtypeA, layoutA, layoutB, a, aligned))
     return hip_status(mcg::launch_fast(dtypeA, dtypeB, layoutA, layoutB, a, (hipStream_t)stream));
@@ -135,7 +144,7 @@ int mcg_validate_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_
                           int64_t ldc, int dtypeD, double alpha, double beta) {
   if (!((dtypeA == MCG_BF16 && dtypeB == MCG_BF16) || (dtypeA == MCG_F16 && dtypeB == MCG_F16)))
     return MCG_ERR_UNSUPPORTED_DTYPE;
-  if (dtypeD != MCG_F32 || !valid_layout(layoutB)) return MCG_ERR_UNSUPPORTED_DTYPE;
+  if (!float_out(dtypeD) || !valid_layout(layoutB)) return MCG_ERR_UNSUPPORTED_DTYPE;
   if (M < 0 || N < 0 || K < 0 || K % 4 != 0) return MCG_ERR_INVALID_SIZE;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return MCG_ERR_INVALID_SIZE;
   if (M == 0 || N == 0) return MCG_SUCCESS;
@@ -146,8 +155,9 @@ int mcg_validate_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_
   if (lda_c < (K / 2 > 1 ? K / 2 : 1) || ld_idx < ((K + 31) / 32 > 1 ? (K + 31) / 32 : 1) ||
       ldb < (min_ldb > 1 ? min_ldb : 1) || ldc < N)
     return MCG_ERR_INVALID_LD;
+  const int ebd = elem_bytes(dtypeD);
   if (!aligned_to(A_compressed, 2) || !aligned_to(B, 2) || !aligned_to(A_index, 4) ||
-      !aligned_to(D, 4) || (C && !aligned_to(C, 4)))
+      !aligned_to(D, ebd) || (C && !aligned_to(C, ebd)))
     return MCG_ERR_MISALIGNED;
   if (!std::isfinite(alpha) || !std::isfinite(beta)) return MCG_ERR_INVALID_VALUE;
   return MCG_SUCCESS;
@@ -178,7 +188,9 @@ int gemm_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int
   a.alpha = (float)alpha;
   a.beta = (float)beta;
   a.use_c = beta != 0.0;
-  a.vec_cd = aligned_to(D, 16) && (!a.use_c || aligned_to(C, 16)) && ldc % 4 == 0;
+  a.out = out_format(dtypeD);
+  const int vb = 4 * elem_bytes(dtypeD);
+  a.vec_cd = aligned_to(D, vb) && (!a.use_c || aligned_to(C, vb)) && ldc % 4 == 0;
   const bool aligned = K == 0 || (aligned_to(A_compressed, 16) && aligned_to(B, 16) &&
                                   aligned_to(A_index, 16) && (lda_c * 2) % 16 == 0 &&
                                   (ldb * 2) % 16 == 0 && (ld_idx * 4) % 16 == 0);

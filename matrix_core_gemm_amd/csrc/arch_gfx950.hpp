@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm_kernels.hpp"
+
 namespace mcg {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -199,6 +201,48 @@ __host__ __device__ constexpr int out_row(int lane, int r) { return 4 * (lane >>
 __host__ __device__ constexpr int out_col(int lane) { return lane & 15; }
 
 // ------------------------------------------------------------ LDS primitives
+// ----------------------------------------------------- output conversions
+// Output formats of the float epilogues (OUT_32, OUT_BF16, OUT_F16) are
+// declared with the kernel argument blocks; C is read in the output format.
+
+// binary32 -> bfloat16 bits, round to nearest, ties to even (adding 0x7fff plus
+// the lowest kept bit carries exactly when the dropped half is above the
+// midpoint, or at it with an odd kept part); overflow gives infinity; a NaN
+// stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  const uint32_t u = bit_cast<uint32_t>(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+// binary32 -> binary16 bits by the hardware conversion (round to nearest even,
+// gradual underflow, overflow to infinity in the default mode).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float x) {
+  return bit_cast<uint16_t>((_Float16)x);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return bit_cast<float>(h << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)bit_cast<_Float16>((uint16_t)h);
+}
+__device__ __forceinline__ uint32_t to_out_bits(int out, float x) {
+  return out == OUT_BF16 ? f32_to_bf16_bits(x) : f32_to_f16_bits(x);
+}
+__device__ __forceinline__ float from_out_bits(int out, uint32_t h) {
+  return out == OUT_BF16 ? bf16_bits_to_f32(h) : f16_bits_to_f32(h);
+}
+
+// D[off] = alpha * v + beta * C[off] (C read only when use_c), with C and D in
+// the output format `out`; the fp32 result is rounded once to a 16-bit format.
+__device__ __forceinline__ void combine_store(const void* C, void* D, int64_t off, float v, float alpha,
+                                              float beta, bool use_c, int out) {
+  if (out == OUT_32) {
+    const float c = use_c ? ((const float*)C)[off] : 0.f;
+    ((float*)D)[off] = use_c ? __builtin_fmaf(alpha, v, beta * c) : alpha * v;
+  } else {
+    const float c = use_c ? from_out_bits(out, ((const uint16_t*)C)[off]) : 0.f;
+    ((uint16_t*)D)[off] = (uint16_t)to_out_bits(out, use_c ? __builtin_fmaf(alpha, v, beta * c) : alpha * v);
+  }
+}
+
 // operand storage order along K: K-contiguous (A row-major, B column-major) or
 // MN-contiguous (A column-major, B row-major)
 enum : int { LAYOUT_K = 0, LAYOUT_MN = 1 };

@@ -133,22 +133,34 @@ __global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs p) {
         else
           for (int r = 0; r < 4; ++r) if (n + r < p.N) D[off + r] = o[r];
       } else {
-        const float* C = (const float*)p.C;
-        float* D = (float*)p.D;
         f32x4 a = acc[i][j];
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
         const bool full = vec_ok && n + 4 <= p.N;
-        if (p.use_c) {
-          if (full) c = *(const f32x4*)(C + off);
-          else
-            for (int r = 0; r < 4; ++r) if (n + r < p.N) c[r] = C[off + r];
+        const int out = p.out;
+        if (out == OUT_32) {
+          const float* C = (const float*)p.C;
+          if (p.use_c) {
+            if (full) c = *(const f32x4*)(C + off);
+            else
+              for (int r = 0; r < 4; ++r) if (n + r < p.N) c[r] = C[off + r];
+          }
+        } else {  // bfloat16 / binary16 C
+          const uint16_t* C = (const uint16_t*)p.C;
+          if (p.use_c)
+            for (int r = 0; r < 4; ++r) if (n + r < p.N) c[r] = from_out_bits(out, C[off + r]);
         }
         f32x4 o;
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[r] = p.use_c ? __builtin_fmaf(p.alpha, a[r], p.beta * c[r]) : p.alpha * a[r];
-        if (full) *(f32x4*)(D + off) = o;
-        else
-          for (int r = 0; r < 4; ++r) if (n + r < p.N) D[off + r] = o[r];
+        if (out == OUT_32) {
+          float* D = (float*)p.D;
+          if (full) *(f32x4*)(D + off) = o;
+          else
+            for (int r = 0; r < 4; ++r) if (n + r < p.N) D[off + r] = o[r];
+        } else {  // rounded once to the output format
+          uint16_t* D = (uint16_t*)p.D;
+          for (int r = 0; r < 4; ++r) if (n + r < p.N) D[off + r] = (uint16_t)to_out_bits(out, o[r]);
+        }
       }
     }
   }

@@ -314,6 +314,53 @@ void gemm_fast_kernel(DenseArgs p) {
     }
     return o;
   };
+  if constexpr (!Op::INT_ACC) {
+    if (p.out != OUT_32) {
+      // bfloat16 / binary16 C and D: 4 consecutive elements = 8 bytes per lane
+      // and row segment; the fp32 result is rounded once to the output format
+      const int out = p.out;
+      const uint16_t* C16 = (const uint16_t*)p.C;
+      uint16_t* D16 = (uint16_t*)p.D;
+      auto unpack = [&](const i32x2 w) {
+        return v4{from_out_bits(out, (uint32_t)w.x & 0xffffu), from_out_bits(out, (uint32_t)w.x >> 16),
+                  from_out_bits(out, (uint32_t)w.y & 0xffffu), from_out_bits(out, (uint32_t)w.y >> 16)};
+      };
+      auto pack = [&](const v4& o) {
+        return i32x2{(int)(to_out_bits(out, o[0]) | (to_out_bits(out, o[1]) << 16)),
+                     (int)(to_out_bits(out, o[2]) | (to_out_bits(out, o[3]) << 16))};
+      };
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int64_t m = m0 + rbA + 32 * i + (lane & 31);
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < WTN; ++j)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int64_t n = n0 + rbB + 32 * j + 8 * r4 + 4 * (lane >> 5);
+            if (n >= p.N) continue;
+            const int64_t off = m * p.ldc + n;
+            const bool full = vec_ok && n + 4 <= p.N;
+            v4 c = {};
+            if (p.use_c) {
+              if (full) c = unpack(*(const i32x2*)(C16 + off));
+              else
+                for (int r = 0; r < 4; ++r)
+                  if (n + r < p.N) c[r] = from_out_bits(out, C16[off + r]);
+            }
+            const v4 o = combine(acc[i][j], r4, c, p.use_c);
+            if (full) {
+              *(i32x2*)(D16 + off) = pack(o);
+            } else {
+              for (int r = 0; r < 4; ++r)
+                if (n + r < p.N) D16[off + r] = (uint16_t)to_out_bits(out, o[r]);
+            }
+          }
+      }
+      return;
+    }
+  }
   if (vec_ok && m0 + BM <= p.M && n0 + BN <= p.N) {
     // interior tile: straight-line code, C read in batches of 16 vector loads
     // per lane (two rows of instruction tiles), issued back to back

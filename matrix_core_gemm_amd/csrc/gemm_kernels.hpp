@@ -4,6 +4,8 @@
 #include <stdint.h>
 
 namespace mcg {
+// Format of C and D: binary32 (int32 for int8 inputs), bfloat16 or binary16.
+enum : int { OUT_32 = 0, OUT_BF16 = 1, OUT_F16 = 2 };
 
 struct DenseArgs {
   const char* A;
@@ -15,7 +17,8 @@ struct DenseArgs {
   float alpha, beta;      // float paths: alpha already includes scaleA*scaleB
   int alpha_i, beta_i;    // int8 path
   int use_c;              // beta != 0: C is read
-  int vec_cd;             // C/D 16-byte aligned with ldc % 4 == 0
+  int vec_cd;             // 4 consecutive C/D elements can be moved as one vector (aligned, ldc % 4 == 0)
+  int out;                // OUT_32 (binary32 / int32), OUT_BF16 or OUT_F16: format of C and D
   int tiles_m, tiles_n;   // filled by the launcher
 };
 
@@ -29,6 +32,7 @@ struct SparseArgs {
   int64_t lda_c, ld_idx, ldb, ldc;
   float alpha, beta;
   int use_c, vec_cd;
+  int out;  // OUT_32, OUT_BF16 or OUT_F16: format of C and D
   int tiles_m, tiles_n;
 };
 

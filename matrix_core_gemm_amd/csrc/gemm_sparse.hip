@@ -149,8 +149,6 @@ __global__ __launch_bounds__(256) void gemm_sparse_kernel(SparseArgs p) {
   }
 
   // epilogue: lane holds D[m .. m+3][n], m = row base + 4*(lane >> 4), n = column base + (lane & 15)
-  const float* C = (const float*)p.C;
-  float* D = (float*)p.D;
 #pragma unroll
   for (int i = 0; i < WTM; ++i) {
 #pragma unroll
@@ -161,9 +159,7 @@ __global__ __launch_bounds__(256) void gemm_sparse_kernel(SparseArgs p) {
       for (int r = 0; r < 4; ++r) {
         const int64_t m = m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4) + r;
         if (m >= p.M) continue;
-        const int64_t off = m * p.ldc + n;
-        const float v = acc[i][j][r];
-        D[off] = p.use_c ? __builtin_fmaf(p.alpha, v, p.beta * C[off]) : p.alpha * v;
+        combine_store(p.C, p.D, m * p.ldc + n, acc[i][j][r], p.alpha, p.beta, p.use_c, p.out);
       }
     }
   }

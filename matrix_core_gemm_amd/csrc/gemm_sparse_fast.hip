@@ -282,8 +282,6 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
 
   // epilogue: block (i, j), register r holds D[m][n] with
   // m = m0 + rbA + 32 i + 8 (r / 4) + 4 (lane >> 5) + r % 4, n = n0 + rbB + 32 j + (lane & 31)
-  const float* C = (const float*)p.C;
-  float* D = (float*)p.D;
   const bool interior = m0 + SP_BM <= p.M && n0 + SP_BN <= p.N;
 #pragma unroll
   for (int i = 0; i < WTM; ++i)
@@ -294,8 +292,7 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + rbA + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
         if (!interior && (m >= p.M || n >= p.N)) continue;
-        const float v = acc[i][j][r];
-        D[m * p.ldc + n] = p.use_c ? __builtin_fmaf(p.alpha, v, p.beta * C[m * p.ldc + n]) : p.alpha * v;
+        combine_store(p.C, p.D, m * p.ldc + n, acc[i][j][r], p.alpha, p.beta, p.use_c, p.out);
       }
     }
 }

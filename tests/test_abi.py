@@ -86,6 +86,15 @@ def dense_args(**kw):
     ({"dtypeA": "i8", "dtypeB": "i8", "dtypeD": "i32", "alpha": 1.5}, 10),
     ({"dtypeA": "i8", "dtypeB": "i8", "dtypeD": "i32", "beta": 2.0 ** 31, "C": FAKE}, 10),
     ({"alpha": float("nan")}, 10),
+    ({"dtypeD": "bf16"}, 0),                         # 16-bit outputs for float inputs
+    ({"dtypeD": "f16", "beta": 1.0, "C": FAKE}, 0),
+    ({"dtypeA": "e4m3", "dtypeB": "e5m2", "dtypeD": "bf16"}, 0),
+    ({"dtypeD": "bf16", "D": FAKE + 2}, 0),          # 16-bit D needs only 2-byte alignment
+    ({"dtypeD": "bf16", "D": FAKE + 1}, 5),
+    ({"dtypeD": "f16", "beta": 1.0, "C": FAKE + 1}, 5),
+    ({"dtypeD": "i32"}, 4),                          # int32 output only for int8 inputs
+    ({"dtypeA": "i8", "dtypeB": "i8", "dtypeD": "bf16"}, 4),
+    ({"dtypeD": "e4m3"}, 4),
 ])
 def test_dense_validation(kw, status):
     assert m.validate_dense(**dense_args(**kw)) == status
@@ -116,6 +125,9 @@ def test_entry_points_reject_before_touching_the_device():
     ({"A_index": FAKE + 2}, 5),
     ({"layoutB": "mn_contig", "ldb": 48}, 3),
     ({"layoutB": "mn_contig", "ldb": 96}, 0),
+    ({"dtypeD": "bf16"}, 0),
+    ({"dtypeD": "f16", "D": FAKE + 2}, 0),
+    ({"dtypeD": "f16", "D": FAKE + 1}, 5),
 ])
 def test_sparse_validation(kw, status):
     a = dict(dtypeA="bf16", dtypeB="bf16", layoutB="k_contig", M=64, N=96, K=64, A_compressed=FAKE,
