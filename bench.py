@@ -9,6 +9,8 @@ full-size synthetic workload (8192^3 for every GEMM):
   gemm_dense  e4m3 x e5m2 -> f32   (per-tensor scales, C = 0)
   compress24  bf16 8192 x 8192     (2:4 compressor)
   gemm_sparse24 bf16 (2:4 A) x bf16 -> f32
+  gemm_dense  bf16 x bf16 -> bf16  (C and D in bfloat16, alpha = beta = 1)
+  gemm_dense  skinny bf16 32768 x 16 x 8192 and 16 x 32768 x 8192 (C absent): HBM-bound
 Each call is bracketed by HIP events on the stream it is launched on, so every
 kernel's average duration is measured live.  `value` is the dense bf16 8192^3
 rate (TFLOP/s); the per-dtype rates the metric asks for are in `per_dtype`.
@@ -111,6 +113,15 @@ def main():
     idx = torch.empty((M, (K + 31) // 32), dtype=torch.int32, device="cuda")
     D = torch.empty((M, N), dtype=torch.float32, device="cuda")
     Di = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    # bfloat16 C and D for the 16-bit output entry
+    C16 = C.to(torch.bfloat16).view(torch.int16)
+    D16 = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    # skinny problems: the wide operand (4n x n bf16 ~ N(0,1)) drawn on the device
+    SK = (4 * n, 16)
+    g = torch.Generator(device="cuda").manual_seed(W.SEED_A)
+    Wide = torch.randn((SK[0], K), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
+    Narrow = torch.randn((SK[1], K), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
+    Dsk = torch.empty((SK[0], SK[1]), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s")
 
@@ -134,8 +145,19 @@ def main():
         elif name == "sparse24":
             mcg.gemm_sparse24("bf16", "bf16", 0, M, N, K, vals, K // 2, idx, idx.shape[1], Bs, K, None,
                               D, N, "f32", 1.0, 0.0, stream=s)
+        elif name == "bf16_out":
+            a, lda, b, ldb, sa, sb = ops["bf16"]
+            mcg.gemm_dense("bf16", "bf16", 0, 0, M, N, K, a, lda, b, ldb, C16, D16, N, "bf16", 1.0, 1.0,
+                           stream=s)
+        elif name == "skinny_n16":  # A = Wide (M = 4n), B = Narrow (N = 16, column-major)
+            mcg.gemm_dense("bf16", "bf16", 0, 0, SK[0], SK[1], K, Wide, K, Narrow, K, None, Dsk, SK[1],
+                           "f32", 1.0, 0.0, stream=s)
+        elif name == "skinny_m16":  # A = Narrow (M = 16), B = Wide (N = 4n, column-major)
+            mcg.gemm_dense("bf16", "bf16", 0, 0, SK[1], SK[0], K, Narrow, K, Wide, K, None, Dsk, SK[0],
+                           "f32", 1.0, 0.0, stream=s)
 
-    names = ["bf16", "f16", "i8", "e4m3xe4m3", "e4m3xe5m2", "compress24", "sparse24"]
+    names = ["bf16", "f16", "i8", "e4m3xe4m3", "e4m3xe5m2", "compress24", "sparse24", "bf16_out",
+             "skinny_n16", "skinny_m16"]
     if args.only:
         keep = set(args.only.split(","))
         names = [x for x in names if x in keep or x == "compress24" and "sparse24" in keep]
@@ -165,6 +187,14 @@ def main():
             nbytes = M * K * 2 + M * K // 2 * 2 + M * ((K + 31) // 32) * 4
             per[x] = {"GB/s": nbytes / t / 1e9, "ms": ms[x], "frac_of_hbm_peak": nbytes / t / 1e9 / HBM_PEAK_GBS,
                       "bytes": nbytes}
+        elif x.startswith("skinny"):
+            nbytes = SK[0] * K * 2 + SK[1] * K * 2 + SK[0] * SK[1] * 4
+            shape = (SK[0], SK[1], K) if x == "skinny_n16" else (SK[1], SK[0], K)
+            per[x] = {"GB/s": nbytes / t / 1e9, "ms": ms[x], "frac_of_hbm_peak": nbytes / t / 1e9 / HBM_PEAK_GBS,
+                      "bytes": nbytes, "TFLOP/s": 2.0 * SK[0] * SK[1] * K / t / 1e12, "MxNxK": shape}
+        elif x == "bf16_out":
+            tf = flops / t / 1e12
+            per[x] = {"TFLOP/s": tf, "ms": ms[x], "peak": PEAK["bf16"], "frac_of_peak": tf / PEAK["bf16"]}
         elif x == "sparse24":
             tf = flops / t / 1e12
             per[x] = {"TFLOP/s_dense_equiv": tf, "TFLOP/s_algorithmic": tf / 2, "ms": ms[x],

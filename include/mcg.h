@@ -92,8 +92,11 @@ typedef enum {
  *                 NULL then).  D: row-major M x N of dtypeD; D may alias C
  *                 exactly (same pointer); other overlaps are undefined.
  * ldc           : leading dimension of both C and D, ldc >= N.
- * dtypeD        : MCG_F32 for float inputs (fp32 accumulation), MCG_I32 for
- *                 int8 (exact int32 accumulation, wrapping mod 2^32).
+ * dtypeD        : format of C and D.  Float inputs: MCG_F32, MCG_BF16 or
+ *                 MCG_F16 (fp32 accumulation; a bfloat16/binary16 D is the
+ *                 fp32 result rounded once to nearest-even, C is read in the
+ *                 same format).  int8: MCG_I32 (exact int32 accumulation,
+ *                 wrapping mod 2^32).
  * alpha, beta   : float paths use them as fp32.  The int8 path requires
  *                 integral values in int32 range and computes
  *                 alpha*acc + beta*C in wrapping int32 arithmetic.
@@ -108,6 +111,16 @@ typedef enum {
  * Alignment     : none required; 16-byte aligned pointers and leading
  *                 dimensions whose byte size is a multiple of 16 take the
  *                 vector-load path, anything else a slower element path.
+ * Split K       : problems with too few output tiles to fill the device
+ *                 (e.g. N <= 32, M <= 32, or a long K over a small D) may cut
+ *                 K into ranges run by separate workgroups when D is MCG_F32
+ *                 or MCG_I32 and is not C with beta != 0.  D is then zeroed,
+ *                 receives the partial sums through device-scope atomic adds
+ *                 and is finally set to alpha*D + beta*C, so D must be
+ *                 ordinary device memory.  Float results of a split problem
+ *                 may differ in the last bits between runs (the order of the
+ *                 additions is not fixed); int32 results are exact.
+ *                 mcg_dense_splits reports the split a call would use.
  */
 int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB,
                int64_t M, int64_t N, int64_t K,
@@ -183,12 +196,22 @@ int mcg_validate_compress24(int dtype, int64_t M, int64_t K, const void* A, int6
                             const void* A_compressed, int64_t lda_c, const uint32_t* A_index,
                             int64_t ld_idx);
 
-/* Kernel selection, for callers that tune shapes and for tests: 1 if gemm_dense
-   (resp. gemm_sparse24) with these arguments runs the 256 x 256 pipelined
-   kernel, 0 if it runs the general kernel (any shape, alignment or leading
-   dimension).  Host-only, no validation, no device access. */
+/* Kernel selection, for callers that tune shapes and for tests.  Host-only,
+   no validation, no device access.
+   mcg_dense_path: the kernel gemm_dense runs for these operands with a
+     binary32/int32 D that is not C: 0 general kernel, 128 x 128 tiles (any
+     shape, alignment or leading dimension); 1 the 256 x 256 pipelined kernel;
+     2 general kernel with 128 x 32 tiles (N <= 32, aligned operands);
+     3 general kernel with 32 x 128 tiles (M <= 32, aligned operands).
+   mcg_dense_splits: the number of K ranges (1 = no split) gemm_dense uses
+     with exactly these arguments.
+   mcg_sparse24_path: 1 if gemm_sparse24 runs the 256 x 256 pipelined kernel,
+     0 for the general one. */
 int mcg_dense_path(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A,
                    int64_t lda, const void* B, int64_t ldb);
+int mcg_dense_splits(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A,
+                     int64_t lda, const void* B, int64_t ldb, const void* C, const void* D, int dtypeD,
+                     double beta);
 int mcg_sparse24_path(int layoutB, int64_t M, int64_t N, int64_t K, const void* A_compressed, int64_t lda_c,
                       const uint32_t* A_index, int64_t ld_idx, const void* B, int64_t ldb);
 

@@ -31,7 +31,7 @@ STATUS = {0: "MCG_SUCCESS", 1: "MCG_ERR_NULL_POINTER", 2: "MCG_ERR_INVALID_SIZE"
 # Every symbol include/mcg.h declares.
 EXPORTS = ("gemm_dense", "gemm_sparse24", "compress24", "compress24_host", "mcg_status_string",
            "mcg_version", "mcg_validate_dense", "mcg_validate_sparse24", "mcg_validate_compress24",
-           "mcg_dense_path", "mcg_sparse24_path")
+           "mcg_dense_path", "mcg_dense_splits", "mcg_sparse24_path")
 
 
 class MCGError(RuntimeError):
@@ -62,6 +62,8 @@ _lib.mcg_validate_sparse24.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, 
                                        _vp, _i64, _vp, _vp, _i64, _i32, _dbl, _dbl]
 _lib.mcg_validate_compress24.argtypes = [_i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
 _lib.mcg_dense_path.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64]
+_lib.mcg_dense_splits.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp,
+                                  _i32, ctypes.c_double]
 _lib.mcg_sparse24_path.argtypes = [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
 
 
@@ -156,9 +158,17 @@ def validate_compress24(dtype, M, K, A, lda, A_compressed, lda_c, A_index, ld_id
 
 
 def dense_path(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb) -> int:
-    """1 if gemm_dense with these arguments runs the 256 x 256 kernel, else 0."""
+    """Kernel gemm_dense runs for these operands (binary32/int32 D, not C):
+    0 general 128 x 128, 1 the 256 x 256 kernel, 2 general 128 x 32 (N <= 32),
+    3 general 32 x 128 (M <= 32)."""
     return _lib.mcg_dense_path(_dt(dtypeA), _lay(layoutA), _lay(layoutB), M, N, K, _ptr(A), lda,
                                _ptr(B), ldb)
+
+
+def dense_splits(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb, C, D, dtypeD, beta) -> int:
+    """Number of K ranges gemm_dense uses with these arguments (1 = no split)."""
+    return _lib.mcg_dense_splits(_dt(dtypeA), _lay(layoutA), _lay(layoutB), M, N, K, _ptr(A), lda,
+                                 _ptr(B), ldb, _ptr(C), _ptr(D), _dt(dtypeD), float(beta))
 
 
 def sparse24_path(layoutB, M, N, K, A_compressed, lda_c, A_index, ld_idx, B, ldb) -> int:

@@ -102,6 +102,12 @@ static bool dense_aligned(int eb, int64_t K, const void* A, int64_t lda, const v
   return K == 0 || (aligned_to(A, 16) && aligned_to(B, 16) && (lda * eb) % 16 == 0 && (ldb * eb) % 16 == 0);
 }
 
+// Split K zeroes D and adds partial sums into it: only for binary32 / int32 D
+// that is not also the C being read.
+static bool can_split_k(const mcg::DenseArgs& a, const void* C, const void* D) {
+  return a.out == mcg::OUT_32 && !(a.use_c && C == D);
+}
+
 int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
                const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, void* D,
                int64_t ldc, int dtypeD, double alpha, double beta, float scaleA, float scaleB,
@@ -133,9 +139,10 @@ int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int6
   const int vb = 4 * elem_bytes(dtypeD);  // bytes of 4 consecutive C/D elements
   a.vec_cd = aligned_to(D, vb) && (!a.use_c || aligned_to(C, vb)) && ldc % 4 == 0;
   const bool aligned = dense_aligned(eb, K, A, lda, B, ldb);
-  if (mcg::fast_path_ok(dtypeA, layoutA, layoutB, a, aligned))
+  const mcg::DensePlan plan = mcg::plan_dense(dtypeA, layoutA, layoutB, a, aligned, can_split_k(a, C, D));
+  if (plan.kernel == mcg::KERNEL_FAST)
     return hip_status(mcg::launch_fast(dtypeA, dtypeB, layoutA, layoutB, a, (hipStream_t)stream));
-  return hip_status(mcg::launch_dense(dtypeA, dtypeB, layoutA, layoutB, aligned, a, (hipStream_t)stream));
+  return hip_status(mcg::launch_dense(dtypeA, dtypeB, layoutA, layoutB, aligned, a, plan, (hipStream_t)stream));
 }
 
 int mcg_validate_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int64_t K,
@@ -275,9 +282,8 @@ int compress24_host(int dtype, int64_t M, int64_t K, const void* A, int64_t lda,
   return bad ? MCG_ERR_NOT_2_4_SPARSE : MCG_SUCCESS;
 }
 
-int mcg_dense_path(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A,
-                   int64_t lda, const void* B, int64_t ldb) {
-  if (dtypeA < MCG_BF16 || dtypeA > MCG_FP8_E5M2) return 0;
+static mcg::DensePlan dense_plan(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
+                                 const void* A, int64_t lda, const void* B, int64_t ldb, bool can_split) {
   const int eb = elem_bytes(dtypeA);
   mcg::DenseArgs a{};
   a.A = (const char*)A;
@@ -287,7 +293,21 @@ int mcg_dense_path(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, i
   a.K = K;
   a.lda = lda;
   a.ldb = ldb;
-  return mcg::fast_path_ok(dtypeA, layoutA, layoutB, a, dense_aligned(eb, K, A, lda, B, ldb)) ? 1 : 0;
+  return mcg::plan_dense(dtypeA, layoutA, layoutB, a, dense_aligned(eb, K, A, lda, B, ldb), can_split);
+}
+
+int mcg_dense_path(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A,
+                   int64_t lda, const void* B, int64_t ldb) {
+  if (dtypeA < MCG_BF16 || dtypeA > MCG_FP8_E5M2) return 0;
+  return dense_plan(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb, true).kernel;
+}
+
+int mcg_dense_splits(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A,
+                     int64_t lda, const void* B, int64_t ldb, const void* C, const void* D, int dtypeD,
+                     double beta) {
+  if (dtypeA < MCG_BF16 || dtypeA > MCG_FP8_E5M2) return 1;
+  const bool can_split = (dtypeD == MCG_F32 || dtypeD == MCG_I32) && !(beta != 0.0 && C == D);
+  return dense_plan(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb, can_split).splits;
 }
 
 int mcg_sparse24_path(int layoutB, int64_t M, int64_t N, int64_t K, const void* A_compressed, int64_t lda_c,

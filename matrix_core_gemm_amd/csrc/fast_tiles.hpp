@@ -134,7 +134,11 @@ struct LineLoader {
   // instructions [i0, i0 + n) of K tile kt into stage `dst`.  The out-of-range
   // offset plus i * istride cannot wrap: every window is below 2 GiB.
   __device__ __forceinline__ void issue(lds_char* dst, int kt, int i0, int n, int wave) const {
-    const uint32_t v = kt < klim ? voff + (uint32_t)kt * kstride : BUF_OOB;
+    issue_if(dst, kt, i0, n, wave, true);
+  }
+  // the same; when !live the instructions read nothing and fill the stage with zeros
+  __device__ __forceinline__ void issue_if(lds_char* dst, int kt, int i0, int n, int wave, bool live) const {
+    const uint32_t v = live && kt < klim ? voff + (uint32_t)kt * kstride : BUF_OOB;
 #pragma unroll
     for (int i = i0; i < i0 + n; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -183,6 +187,71 @@ struct Reader {
   __device__ static __forceinline__ i32x8 read32(const lds_char* tile, int rb, int lane) {
     const i32x4 a = read16(tile, rb, 0, lane), b = read16(tile, rb, 1, lane);
     return i32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  }
+};
+
+// ------------------------------------------------------------- 32x32 ops
+// P (first operand) = B fragment, Q = A fragment.  One instruction takes
+// LANE_BYTES bytes of K per lane; lane group g = lane >> 5 of a 32-row
+// fragment holds the g-th LANE_BYTES-byte part of the instruction's K range
+// (gathered by transposing reads when the operand is MN-contiguous); A and B
+// use the same assignment, so any consistent choice is valid.  Output lane l,
+// register r holds out[8*(r/4) + 4*(l/32) + r%4][l % 32] (the 32 x 32
+// accumulator layout).
+
+struct BF16 {
+  static constexpr int EB = 2, LANE_BYTES = 16;
+  static constexpr bool INT_ACC = false;
+  using acc_t = f32x16;
+  using frag_t = i32x4;
+  __device__ static __forceinline__ void mma(acc_t& c, const frag_t& p, const frag_t& q) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bit_cast<bf16x8>(p), bit_cast<bf16x8>(q), c, 0, 0, 0);
+  }
+};
+struct F16 {
+  static constexpr int EB = 2, LANE_BYTES = 16;
+  static constexpr bool INT_ACC = false;
+  using acc_t = f32x16;
+  using frag_t = i32x4;
+  __device__ static __forceinline__ void mma(acc_t& c, const frag_t& p, const frag_t& q) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(bit_cast<f16x8>(p), bit_cast<f16x8>(q), c, 0, 0, 0);
+  }
+};
+struct I8 {
+  static constexpr int EB = 1, LANE_BYTES = 16;
+  static constexpr bool INT_ACC = true;
+  using acc_t = i32x16;
+  using frag_t = i32x4;
+  __device__ static __forceinline__ void mma(acc_t& c, const frag_t& p, const frag_t& q) {
+    c = __builtin_amdgcn_mfma_i32_32x32x32_i8(p, q, c, 0, 0, 0);
+  }
+};
+// native fp8: FP = format of P (B tensor), FQ = format of Q (A tensor)
+template <int FP, int FQ>
+struct F8 {
+  static constexpr int EB = 1, LANE_BYTES = 32;
+  static constexpr bool INT_ACC = false;
+  using acc_t = f32x16;
+  using frag_t = i32x8;
+  __device__ static __forceinline__ void mma(acc_t& c, const frag_t& p, const frag_t& q) {
+    c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(p, q, c, FP, FQ, 0, 0, 0, 0);
+  }
+};
+// fp8 widened exactly to bf16 (K below the native-fp8 threshold): FA/FB = formats
+// of A/B; 16 bytes per lane hold 16 fp8 values = two bf16 instructions.
+template <int FA, int FB>
+struct F8W {
+  static constexpr int EB = 1, LANE_BYTES = 16;
+  static constexpr bool INT_ACC = false;
+  using acc_t = f32x16;
+  using frag_t = i32x4;
+  __device__ static __forceinline__ void mma(acc_t& c, const frag_t& p, const frag_t& q) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const i32x4 pb = fp8x8_to_bf16x8<FB>(i32x2{p[2 * h], p[2 * h + 1]});
+      const i32x4 qb = fp8x8_to_bf16x8<FA>(i32x2{q[2 * h], q[2 * h + 1]});
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bit_cast<bf16x8>(pb), bit_cast<bf16x8>(qb), c, 0, 0, 0);
+    }
   }
 };
 

@@ -1,213 +1,148 @@
-// gemm_dense.hip -- dense MFMA GEMM kernels for gfx950.
+// gemm_dense.hip -- the general dense kernel with 128 x 128 tiles, split-K
+// support kernels, and the choice of kernel and K split for a dense problem.
 //
-// D = alpha * (A . B) + beta * C: the matrix fused multiply-add of "Accurate
-// Models of AMD Matrix Cores" (Section 2, Eq. (1)) tiled over a workgroup, one
-// MFMA K-step at a time as the builtins are meant to be used ("CDNA3 dense
-// MFMA builtins", Naming convention: one instruction per K step, the caller
-// loops over K; Using MFMA builtins as a compute policy: block tiles are
-// multiples of the instruction tile and K tiles multiples of its K step).
-//
-// Kernel structure (per workgroup of 256 threads = 4 wavefronts):
-//   - a BM x BN output tile; waves in a 2 x 2 grid, each owning a
-//     (BM/2) x (BN/2) sub-tile of 16x16 instruction tiles;
-//   - K is walked in tiles of 128 bytes; each tile of A and B is staged from
-//     HBM into LDS (16-byte loads, swizzled rows), double-buffered so the loads
-//     of tile t+1 are in flight while tile t is multiplied;
-//   - the instruction is issued with P = B fragment and Q = A fragment, so the
-//     output registers of a lane hold four consecutive columns of one row of D
-//     (one 16-byte store per lane in the epilogue);
-//   - epilogue: D = alpha*acc + beta*C in fp32 (float inputs) or wrapping
-//     int32 (int8 inputs); C is not read when beta == 0.
+// Split K: when a problem has too few output tiles to occupy the 256 compute
+// units (skinny shapes such as N <= 32, or few tiles with a long K), the K
+// loop is cut into ranges multiplied by separate workgroups.  D (binary32 or
+// int32) is zeroed first, every workgroup adds alpha times its partial sum
+// into D with device-scope atomic adds, and when beta != 0 a last pass adds
+// beta * C with one rounding.  C enters once, after all partial sums: adding
+// it to the running sum first would round every later partial sum against
+// |C|, which the accuracy bound does not allow for when |C| dominates.  The
+// order of the atomic additions is not fixed, so float results may differ in
+// the last bits from run to run (int32 sums wrap modulo 2^32 and are exact).
+#include <algorithm>
+
+#include "dense_general.hpp"
 #include "gemm_kernels.hpp"
-#include "tile_io.hpp"
 
 namespace mcg {
 
-template <class Op, int LA, int LB, int BM, int BN, bool ALIGNED>
-__global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs p) {
-  constexpr int NT = 256;
-  constexpr int EB = Op::ELEM_BYTES;
-  constexpr int STEPS = Op::STEPS;
-  constexpr int WTM = BM / 2 / 16, WTN = BN / 2 / 16;  // instruction tiles per wave
-  using GA = TileGeom<EB, LA, BM>;
-  using GB = TileGeom<EB, LB, BN>;
-  using RA = FragReader<EB, Op::LANE_BYTES == 32 ? 32 : 16, LA, BM>;
-  using RB = FragReader<EB, Op::LANE_BYTES == 32 ? 32 : 16, LB, BN>;
-  using acc_t = typename Op::acc_t;
+// D[m][n] = 0 for m < M, n < N (all-zero bits: +0.0f and int 0).  Grid:
+// x covers N in blocks of 256, y strides over the rows.
+__global__ __launch_bounds__(256) void splitk_zero_kernel(DenseArgs p) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= p.N) return;
+  for (int64_t m = blockIdx.y; m < p.M; m += gridDim.y) ((int*)p.D)[m * p.ldc + n] = 0;
+}
 
-  __shared__ __attribute__((aligned(16))) char smem_raw[2 * (GA::BYTES + GB::BYTES)];
-  lds_char* smem = (lds_char*)smem_raw;
-  lds_char* ldsA[2] = {smem, smem + GA::BYTES + GB::BYTES};
-  lds_char* ldsB[2] = {smem + GA::BYTES, smem + 2 * GA::BYTES + GB::BYTES};
+// D = D + beta * C with one rounding (fp32 fma), or in wrapping int32; run
+// only when beta != 0.
+template <bool INT>
+__global__ __launch_bounds__(256) void splitk_finish_kernel(DenseArgs p) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= p.N) return;
+  for (int64_t m = blockIdx.y; m < p.M; m += gridDim.y) {
+    const int64_t off = m * p.ldc + n;
+    if constexpr (INT) {
+      int* D = (int*)p.D;
+      D[off] = (int)((uint32_t)D[off] + (uint32_t)p.beta_i * (uint32_t)((const int*)p.C)[off]);
+    } else {
+      float* D = (float*)p.D;
+      D[off] = __builtin_fmaf(p.beta, ((const float*)p.C)[off], D[off]);
+    }
+  }
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+static dim3 rows_grid(const DenseArgs& a) {
+  return dim3((unsigned)((a.N + 255) / 256), (unsigned)(a.M < 4096 ? a.M : 4096));
+}
 
-  // workgroup -> output tile, grouped by 8 tile rows for L2 reuse
-  const int pid = blockIdx.x;
-  const int group = 8;
-  const int tiles_in_group = group * p.tiles_n;
-  const int gid = pid / tiles_in_group;
-  const int first_m = gid * group;
-  const int gsize = min(p.tiles_m - first_m, group);
-  const int tm = first_m + (pid % tiles_in_group) % gsize;
-  const int tn = (pid % tiles_in_group) / gsize;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+// ------------------------------------------------------------------ plan
 
-  const int KE = KT_BYTES / EB;  // K elements per tile
-  const int nk = (int)((p.K + KE - 1) / KE);
+namespace {
+constexpr int64_t NUM_CU = 256;           // gfx950 (MI355X) compute units
+constexpr int64_t FAST_MIN_TILES = 128;   // 256 x 256 tiles from which the fast kernel wins
+// Split-K cost model of the 4-wave general kernels (MI355X, measured with
+// bf16, fp8 and int8 over 256^2..2048^2 outputs and K up to 65536):
+//   time(s) ~ rounds * (KT_US * ceil(nk / s) + ROUND_US) + ATOMIC_US * s * M * N + SPLIT_US [s > 1]
+// with rounds = ceil(tiles * s / NUM_CU) workgroups per CU, KT_US per 128-byte
+// K tile of a workgroup, ATOMIC_US per device-scope atomic add of D and
+// SPLIT_US for zeroing D and the extra launches.
+constexpr double KT_US = 1.0, ROUND_US = 3.0, ATOMIC_US = 1.4e-5, SPLIT_US = 5.0;
+// The streaming kernel is HBM-bound: split only when there are too few blocks
+// to spread over the CUs, keeping 16 K tiles or more per split.
+constexpr int64_t STREAM_MIN_BLOCKS = 64, STREAM_MIN_KT = 16;
+}  // namespace
 
-  TileLoader<EB, LA, BM, NT, ALIGNED> la;
-  TileLoader<EB, LB, BN, NT, ALIGNED> lb;
-  auto load_tiles = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * KE;
-    if constexpr (LA == LAYOUT_K) la.load(p.A, p.lda, m0, k0, p.M, p.K, tid);
-    else la.load(p.A, p.lda, k0, m0, p.K, p.M, tid);
-    if constexpr (LB == LAYOUT_K) lb.load(p.B, p.ldb, n0, k0, p.N, p.K, tid);
-    else lb.load(p.B, p.ldb, k0, n0, p.K, p.N, tid);
+DensePlan plan_dense(int dtA, int la, int lb, const DenseArgs& a, bool aligned, bool can_split) {
+  const int64_t eb = (dtA == DT_BF16 || dtA == DT_F16) ? 2 : 1;
+  const int64_t KE = KT_BYTES / eb;
+  const int64_t nk = (a.K + KE - 1) / KE;
+  auto cdiv = [](int64_t x, int64_t y) { return (x + y - 1) / y; };
+  // number of K ranges for `tiles` workgroups of the general kernels
+  auto splits_for = [&](int64_t tiles) -> int64_t {
+    if (!can_split || nk < 2) return 1;
+    int64_t best = 1;
+    double best_t = 0;
+    for (int64_t s = 1; s <= nk / 2 + 1 && s <= 1024; s = s < 4 ? s + 1 : s * 2) {
+      const int64_t ss = std::min(s, nk);
+      const double rounds = (double)cdiv(tiles * ss, NUM_CU);
+      const double t = rounds * (KT_US * (double)cdiv(nk, ss) + ROUND_US) +
+                       ATOMIC_US * (double)ss * (double)a.M * (double)a.N + (ss > 1 ? SPLIT_US : 0.0);
+      if (s == 1 || t < best_t) { best = ss; best_t = t; }
+    }
+    return best;
+  };
+  auto make = [&](int kernel, int64_t s) {
+    DensePlan p{kernel, 1, (int)(nk > 0 ? nk : 1), 0};
+    if (s > 1) {
+      const int64_t kps = cdiv(nk, s);
+      p.kt_per_split = (int)kps;
+      p.splits = (int)cdiv(nk, kps);  // every range non-empty
+    }
+    return p;
   };
 
-  acc_t acc[WTM][WTN];
-#pragma unroll
-  for (int i = 0; i < WTM; ++i)
-#pragma unroll
-    for (int j = 0; j < WTN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
-
-  if (nk > 0) {
-    load_tiles(0);
-    la.store(ldsA[0], tid);
-    lb.store(ldsB[0], tid);
-    __syncthreads();
+  if (fast_path_ok(dtA, la, lb, a, aligned) && cdiv(a.M, 256) * cdiv(a.N, 256) >= FAST_MIN_TILES)
+    return make(KERNEL_FAST, 1);
+  if (stream_path_ok(dtA, la, lb, a, aligned)) {
+    // 128-row blocks when that still gives most CUs a block, else 32-row blocks
+    // (measured: more blocks beat wider ones below 16384 rows)
+    const int64_t wide = a.N <= 32 && a.N <= a.M ? a.M : a.N;
+    const int bw = wide >= 64 * NUM_CU ? 128 : 32;
+    const int64_t blocks = cdiv(wide, bw);
+    int64_t s = 1;
+    if (can_split && blocks < STREAM_MIN_BLOCKS)
+      s = std::max<int64_t>(1, std::min(cdiv(STREAM_MIN_BLOCKS, blocks), nk / STREAM_MIN_KT));
+    DensePlan pl = make(KERNEL_STREAM, s);
+    pl.stream_bw = bw;
+    return pl;
   }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_tiles(kt + 1);
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-      typename Op::frag_t fa[WTM];
-      typename Op::frag_t fb[WTN];
-#pragma unroll
-      for (int i = 0; i < WTM; ++i) fa[i] = Op::template frag_a<RA>(ldsA[cur], wm * (BM / 2) + i * 16, s, lane);
-#pragma unroll
-      for (int j = 0; j < WTN; ++j) fb[j] = Op::template frag_b<RB>(ldsB[cur], wn * (BN / 2) + j * 16, s, lane);
-#pragma unroll
-      for (int i = 0; i < WTM; ++i)
-#pragma unroll
-        for (int j = 0; j < WTN; ++j) acc[i][j] = Op::mma(fb[j], fa[i], acc[i][j]);
-    }
-    if (kt + 1 < nk) {
-      la.store(ldsA[cur ^ 1], tid);
-      lb.store(ldsB[cur ^ 1], tid);
-    }
-    __syncthreads();
-  }
-
-  // epilogue: lane holds D[m][n .. n+3] with m = row base + (lane & 15),
-  // n = column base + 4 * (lane >> 4)
-  const bool vec_ok = p.vec_cd;
-#pragma unroll
-  for (int i = 0; i < WTM; ++i) {
-    const int64_t m = m0 + wm * (BM / 2) + i * 16 + (lane & 15);
-    if (m >= p.M) continue;
-#pragma unroll
-    for (int j = 0; j < WTN; ++j) {
-      const int64_t n = n0 + wn * (BN / 2) + j * 16 + 4 * (lane >> 4);
-      if (n >= p.N) continue;
-      const int64_t off = m * p.ldc + n;
-      if constexpr (Op::INT_ACC) {
-        const int* C = (const int*)p.C;
-        int* D = (int*)p.D;
-        i32x4 a = acc[i][j];
-        i32x4 c = {0, 0, 0, 0};
-        const bool full = vec_ok && n + 4 <= p.N;
-        if (p.use_c) {
-          if (full) c = *(const i32x4*)(C + off);
-          else
-            for (int r = 0; r < 4; ++r) if (n + r < p.N) c[r] = C[off + r];
-        }
-        i32x4 o;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          o[r] = (int)((uint32_t)p.alpha_i * (uint32_t)a[r] + (uint32_t)p.beta_i * (uint32_t)c[r]);
-        if (full) *(i32x4*)(D + off) = o;
-        else
-          for (int r = 0; r < 4; ++r) if (n + r < p.N) D[off + r] = o[r];
-      } else {
-        f32x4 a = acc[i][j];
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
-        const bool full = vec_ok && n + 4 <= p.N;
-        const int out = p.out;
-        if (out == OUT_32) {
-          const float* C = (const float*)p.C;
-          if (p.use_c) {
-            if (full) c = *(const f32x4*)(C + off);
-            else
-              for (int r = 0; r < 4; ++r) if (n + r < p.N) c[r] = C[off + r];
-          }
-        } else {  // bfloat16 / binary16 C
-          const uint16_t* C = (const uint16_t*)p.C;
-          if (p.use_c)
-            for (int r = 0; r < 4; ++r) if (n + r < p.N) c[r] = from_out_bits(out, C[off + r]);
-        }
-        f32x4 o;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = p.use_c ? __builtin_fmaf(p.alpha, a[r], p.beta * c[r]) : p.alpha * a[r];
-        if (out == OUT_32) {
-          float* D = (float*)p.D;
-          if (full) *(f32x4*)(D + off) = o;
-          else
-            for (int r = 0; r < 4; ++r) if (n + r < p.N) D[off + r] = o[r];
-        } else {  // rounded once to the output format
-          uint16_t* D = (uint16_t*)p.D;
-          for (int r = 0; r < 4; ++r) if (n + r < p.N) D[off + r] = (uint16_t)to_out_bits(out, o[r]);
-        }
-      }
-    }
-  }
+  if (aligned && a.N <= 32 && a.N <= a.M) return make(KERNEL_SKINNY_N, splits_for(cdiv(a.M, 128)));
+  if (aligned && a.M <= 32) return make(KERNEL_SKINNY_M, splits_for(cdiv(a.N, 128)));
+  return make(KERNEL_GENERAL, splits_for(cdiv(a.M, 128) * cdiv(a.N, 128)));
 }
 
-// ------------------------------------------------------------------ dispatch
+// ------------------------------------------------------------------ launch
 
-
-template <class Op, int LA, int LB, bool AL>
-static hipError_t launch_one(const DenseArgs& a0, hipStream_t s) {
-  constexpr int BM = 128, BN = 128;
+hipError_t launch_dense(int dtA, int dtB, int la, int lb, bool aligned, const DenseArgs& a0,
+                        const DensePlan& plan, hipStream_t s) {
   DenseArgs a = a0;
-  a.tiles_m = (int)((a.M + BM - 1) / BM);
-  a.tiles_n = (int)((a.N + BN - 1) / BN);
-  const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_dense_kernel<Op, LA, LB, BM, BN, AL>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
-template <class Op>
-static hipError_t launch_layouts(int la, int lb, bool aligned, const DenseArgs& a, hipStream_t s) {
-#define MCG_L(LA_, LB_)                                                        \
-  if (la == LA_ && lb == LB_)                                                  \
-    return aligned ? launch_one<Op, LA_, LB_, true>(a, s) : launch_one<Op, LA_, LB_, false>(a, s);
-  MCG_L(0, 0) MCG_L(0, 1) MCG_L(1, 0) MCG_L(1, 1)
-#undef MCG_L
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_dense(int dtA, int dtB, int la, int lb, bool aligned, const DenseArgs& a, hipStream_t s) {
-  if (dtA == DT_BF16) return launch_layouts<OpBF16>(la, lb, aligned, a, s);
-  if (dtA == DT_F16) return launch_layouts<OpF16>(la, lb, aligned, a, s);
-  if (dtA == DT_I8) return launch_layouts<OpI8>(la, lb, aligned, a, s);
-  const int fa = f8fmt(dtA), fb = f8fmt(dtB);
-  if (a.K >= FP8_NATIVE_MIN_K) {
-    // P = B fragment, Q = A fragment: the P format is B's.
-    if (fb == 0 && fa == 0) return launch_layouts<OpF8<0, 0>>(la, lb, aligned, a, s);
-    if (fb == 1 && fa == 0) return launch_layouts<OpF8<1, 0>>(la, lb, aligned, a, s);
-    if (fb == 0 && fa == 1) return launch_layouts<OpF8<0, 1>>(la, lb, aligned, a, s);
-    return launch_layouts<OpF8<1, 1>>(la, lb, aligned, a, s);
+  a.splits = plan.splits;
+  a.kt_per_split = plan.kt_per_split;
+  a.stream_bw = plan.stream_bw;
+  const bool split = a.splits > 1;
+  const bool is_int = dtA == DT_I8;
+  if (split) {
+    if (a.out != OUT_32) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(splitk_zero_kernel, rows_grid(a), dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  if (fa == 0 && fb == 0) return launch_layouts<OpF8W<0, 0>>(la, lb, aligned, a, s);
-  if (fa == 0 && fb == 1) return launch_layouts<OpF8W<0, 1>>(la, lb, aligned, a, s);
-  if (fa == 1 && fb == 0) return launch_layouts<OpF8W<1, 0>>(la, lb, aligned, a, s);
-  return launch_layouts<OpF8W<1, 1>>(la, lb, aligned, a, s);
+  hipError_t e;
+  switch (plan.kernel) {
+    case KERNEL_SKINNY_N: e = launch_skinny_n(dtA, dtB, la, lb, a, s); break;
+    case KERNEL_SKINNY_M: e = launch_skinny_m(dtA, dtB, la, lb, a, s); break;
+    case KERNEL_STREAM: e = launch_stream(dtA, dtB, la, lb, a, s); break;
+    default:
+      e = aligned ? launch_general<128, 128, true>(dtA, dtB, la, lb, a, s)
+                  : launch_general<128, 128, false>(dtA, dtB, la, lb, a, s);
+  }
+  if (e != hipSuccess || !split || !a.use_c) return e;
+  if (is_int) hipLaunchKernelGGL(splitk_finish_kernel<true>, rows_grid(a), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(splitk_finish_kernel<false>, rows_grid(a), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace mcg

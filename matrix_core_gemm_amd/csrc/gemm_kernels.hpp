@@ -19,7 +19,26 @@ struct DenseArgs {
   int use_c;              // beta != 0: C is read
   int vec_cd;             // 4 consecutive C/D elements can be moved as one vector (aligned, ldc % 4 == 0)
   int out;                // OUT_32 (binary32 / int32), OUT_BF16 or OUT_F16: format of C and D
+  int splits;             // K ranges multiplied by separate workgroups (1: no split)
+  int kt_per_split;       // K tiles per range
+  int stream_bw;          // streaming kernel: rows of the wide operand per workgroup
   int tiles_m, tiles_n;   // filled by the launcher
+};
+
+// Kernel chosen for a dense problem (also reported by mcg_dense_path).
+enum : int {
+  KERNEL_GENERAL = 0,   // 128 x 128 tiles, 4 waves, register-staged LDS double buffer
+  KERNEL_FAST = 1,      // 256 x 256 tiles, 8 waves, LDS-DMA ring (large problems)
+  KERNEL_SKINNY_N = 2,  // general kernel with 128 x 32 tiles (N <= 32)
+  KERNEL_SKINNY_M = 3,  // general kernel with 32 x 128 tiles (M <= 32)
+  KERNEL_STREAM = 4     // streaming kernel for N <= 32 or M <= 32 (K-contiguous, aligned)
+};
+
+struct DensePlan {
+  int kernel;
+  int splits;        // >1: K split over grid.y, partial sums added into D
+  int kt_per_split;  // K tiles of 128 bytes per split
+  int stream_bw;     // KERNEL_STREAM: 32, 64 or 128 rows of the wide operand per workgroup
 };
 
 struct SparseArgs {
@@ -52,9 +71,18 @@ struct CompressArgs {
 // fp8 operands are widened exactly to bf16 and multiplied on the bf16 path.
 constexpr int64_t FP8_NATIVE_MIN_K = 6144;
 
+// Kernel and K split for a dense problem.  can_split: D is binary32/int32 and
+// is not C (split K zeroes D first and adds the partial sums into it).
+DensePlan plan_dense(int dtA, int layoutA, int layoutB, const DenseArgs& a, bool aligned, bool can_split);
+
 // Enqueue the kernels; arguments were validated by the caller.
 hipError_t launch_dense(int dtA, int dtB, int layoutA, int layoutB, bool aligned, const DenseArgs& a,
-                        hipStream_t s);
+                        const DensePlan& plan, hipStream_t s);
+// The general kernel with skinny tiles (aligned operands only), one per translation unit.
+hipError_t launch_skinny_n(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
+hipError_t launch_skinny_m(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
+bool stream_path_ok(int dtA, int layoutA, int layoutB, const DenseArgs& a, bool aligned);
+hipError_t launch_stream(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
 bool fast_path_ok(int dtA, int layoutA, int layoutB, const DenseArgs& a, bool aligned);
 hipError_t launch_fast(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
 hipError_t launch_sparse(int dt, int layoutB, bool aligned, const SparseArgs& a, hipStream_t s);

@@ -23,9 +23,9 @@ LAYOUTS = [("k_contig", "k_contig"), ("k_contig", "mn_contig"), ("mn_contig", "k
 SMALL = {"bf16": 8, "f16": 8, "e4m3": 16, "e5m2": 8}
 
 
-def operands(dtA, dtB, layA, layB, M, N, K, dist=None, pad=0, seed=0):
+def operands(dtA, dtB, layA, layB, M, N, K, dist=None, pad=0, seed=0, scaled=True):
     dist = dist or ("int8" if dtA == "i8" else "normal")
-    fp8 = dtA in ("e4m3", "e5m2")
+    fp8 = scaled and dtA in ("e4m3", "e5m2")
     ldA = (K if layA == "k_contig" else M) + pad
     ldB = (K if layB == "k_contig" else N) + pad
     A = W.operand("A", dtA, M, K, dist, layA, seed=10 * seed, ld=ldA, fp8_scaled=fp8)
@@ -80,38 +80,73 @@ def test_multi_tile_ragged(dtA, dtB, layA, layB):
     check_case(mcg, dtA, dtB, layA, layB, 300, 200, 300, pad=20, ldc_pad=4, expect_path=0)
 
 
-# Shapes taken by the 256 x 256 kernel for every dtype and layout (M, N >= 256,
-# K and every leading dimension a multiple of 16 elements): ragged M and N tiles,
-# K ending inside a 128-byte stage, a single partial stage, padded leading
-# dimensions.
-FAST_SHAPES = [(528, 304, 208, 16), (256, 272, 80, 0), (304, 528, 1040, 32)]
+# Shapes taken by the 256 x 256 kernel for every dtype and layout (at least 128
+# output tiles of 256 x 256, K and every leading dimension a multiple of 16
+# elements): ragged M and N tiles, K ending inside a 128-byte stage, a single
+# partial stage, padded leading dimensions.  Outputs are compared on every
+# element of the rows and columns at tile boundaries and 4096 random ones.
+FAST_SHAPES = [(2832, 3088, 208, 16), (3072, 2832, 80, 0), (2320, 3344, 1040, 32)]
+
+
+def tile_edges(n, t=256):
+    """First and last index of the first tile, of the last whole tile, and of the
+    ragged tail (when there is one)."""
+    last = (n // t) * t
+    e = {0, t - 1, t, last - 1, n - 1}
+    if last < n:
+        e.add(last)
+    return tuple(sorted(x for x in e if 0 <= x < n))
+
+
+def check_case_sampled(mcg, dtA, dtB, layA, layB, M, N, K, pad=0, ldc_pad=0, seed=0, dist=None,
+                       alpha=None, beta=1.0, expect_path=None, exact=False):
+    say(f"sampled case {dtA}x{dtB} {layA}/{layB} M={M} N={N} K={K} pad={pad}")
+    # exact checks use the small integers unscaled (fp8 scaling would make them inexact)
+    A, B = operands(dtA, dtB, layA, layB, M, N, K, dist, pad, seed, scaled=not exact)
+    ldc = N + ldc_pad
+    i8 = dtA == "i8"
+    alpha = (3 if i8 else 1.5) if alpha is None else alpha
+    C = None
+    if beta != 0:
+        C = W.c_matrix(M, N, "int20" if i8 else "normal", seed=10 * seed + 2, ldc=ldc)
+        if exact and not i8:
+            C = np.round(C * 1000).astype(np.float32)
+    d = run_dense(mcg, dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, ldc, alpha,
+                  beta, A.scale, B.scale, expect_path=expect_path)
+    rows, cols = W.sample_coords(M, N, n_random=4096, full_rows=tile_edges(M), full_cols=tile_edges(N))
+    ref, s = oracle_dense(dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, ldc,
+                          alpha, beta, A.scale, B.scale, rows, cols)
+    if exact:
+        assert np.array_equal(d[rows, cols], ref)
+    else:
+        compare(dtA, d[rows, cols], ref, s, K, alpha, A.scale, B.scale, beta,
+                None if C is None else C[rows, cols], what=f"{dtA}x{dtB} {layA}/{layB} {M}x{N}x{K}")
+    if ldc_pad:  # padding columns of D untouched
+        if i8:
+            assert np.all(d[:M, N:] == -0x5A5A5A5A)
+        else:
+            assert np.all(np.isnan(d[:M, N:]))
 
 
 @pytest.mark.parametrize("dtA,dtB", PAIRS)
 @pytest.mark.parametrize("layA,layB", LAYOUTS)
-@pytest.mark.parametrize("shape", FAST_SHAPES, ids=["528x304x208", "256x272x80", "304x528x1040"])
+@pytest.mark.parametrize("shape", FAST_SHAPES, ids=["2832x3088x208", "3072x2832x80", "2320x3344x1040"])
 def test_256_tile_path_ragged(dtA, dtB, layA, layB, shape):
     mcg = need_gpu()
     M, N, K, pad = shape
-    check_case(mcg, dtA, dtB, layA, layB, M, N, K, pad=pad, ldc_pad=4, seed=3, expect_path=1)
+    check_case_sampled(mcg, dtA, dtB, layA, layB, M, N, K, pad=pad, ldc_pad=4, seed=3, expect_path=1)
 
 
 @pytest.mark.parametrize("dtA,dtB", [p for p in PAIRS if p[0] != "i8"])
 @pytest.mark.parametrize("layA,layB", LAYOUTS)
 def test_small_integers_bit_exact_256_tiles(dtA, dtB, layA, layB):
     """Exactly representable partial sums on the 256 x 256 kernel (ragged M and N,
-    K ending inside a stage): the result must equal the oracle bit for bit."""
+    K ending inside a stage): the sampled outputs must equal the oracle bit for bit."""
     mcg = need_gpu()
-    M, N, K = 512, 304, 1104
+    M, N, K = 2832, 2832, 1104
     r = min(SMALL[dtA], SMALL[dtB])
-    A = W.operand("A", dtA, M, K, f"smallint{r}", layA, seed=15)
-    B = W.operand("B", dtB, K, N, f"smallint{r}", layB, seed=16)
-    C = np.round(W.c_matrix(M, N, "normal", seed=17) * 1000).astype(np.float32)
-    d = run_dense(mcg, dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, N, 1.0, 1.0,
-                  expect_path=1)
-    ref, _ = oracle.gemm_float(dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, N,
-                               1.0, 1.0)
-    assert np.array_equal(d, ref)
+    check_case_sampled(mcg, dtA, dtB, layA, layB, M, N, K, seed=15, dist=f"smallint{r}", alpha=1.0,
+                       beta=1.0, expect_path=1, exact=True)
 
 
 @pytest.mark.parametrize("dtA,dtB", PAIRS)

@@ -39,19 +39,22 @@ def run_dense16(mcg, dtA, dtB, layA, layB, M, N, K, A, B, C, ldc, out, alpha, be
 
 
 DENSE_PAIRS = [("bf16", "bf16"), ("f16", "f16"), ("e4m3", "e4m3"), ("e4m3", "e5m2")]
-DENSE_CASES = [  # (M, N, K, pad, expected kernel)
-    (130, 140, 200, 8, 0),   # general kernel, ragged
-    (528, 304, 208, 16, 1),  # 256 x 256 kernel, ragged M, N and K
+DENSE_CASES = [  # (M, N, K, pad, expected kernel, sampled)
+    (130, 140, 200, 8, 0, False),      # general kernel, ragged
+    (2832, 2576, 208, 16, 1, True),    # 256 x 256 kernel, ragged M, N and K
+    (1024, 16, 1040, 0, 4, False),     # streaming kernel (N <= 32)
 ]
 
 
 @pytest.mark.parametrize("out", ["bf16", "f16"])
 @pytest.mark.parametrize("dtA,dtB", DENSE_PAIRS)
 @pytest.mark.parametrize("layA,layB", [("k_contig", "k_contig"), ("mn_contig", "mn_contig")])
-@pytest.mark.parametrize("case", DENSE_CASES, ids=["general", "tile256"])
+@pytest.mark.parametrize("case", DENSE_CASES, ids=["general", "tile256", "stream"])
 def test_dense_16bit_output(out, dtA, dtB, layA, layB, case):
     mcg = need_gpu()
-    M, N, K, pad, path = case
+    M, N, K, pad, path, sampled = case
+    if path == 4 and layA != "k_contig":
+        path = 2  # MN-contiguous skinny problems take the general kernel with 128 x 32 tiles
     say(f"dense {dtA}x{dtB} {layA}/{layB} {M}x{N}x{K} -> {out}")
     fp8 = dtA in ("e4m3", "e5m2")
     A = W.operand("A", dtA, M, K, "normal", layA, seed=31,
@@ -62,11 +65,19 @@ def test_dense_16bit_output(out, dtA, dtB, layA, layB, case):
     C = c_codes(M, ldc, out, 33)
     alpha, beta = -0.75, 1.5
     d = run_dense16(mcg, dtA, dtB, layA, layB, M, N, K, A, B, C, ldc, out, alpha, beta, path)
+    rows = cols = None
+    if sampled:
+        rows, cols = W.sample_coords(M, N, n_random=4096, full_rows=(0, 255, 256, M - 1),
+                                     full_cols=(0, 255, 256, N - 1))
     ref, s = oracle.gemm_float(dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, ldc,
-                               alpha, beta, A.scale, B.scale, out=out)
+                               alpha, beta, A.scale, B.scale, rows=rows, cols=cols, out=out)
     got = decode(d, out)
-    r = oracle.check_float(got[:, :N], ref, s, K, alpha, A.scale, B.scale, beta,
-                           decode(C, out)[:, :N], out=out)
+    cdec = decode(C, out)
+    if sampled:
+        got, cdec = got[rows, cols], cdec[rows, cols]
+    else:
+        got, cdec = got[:, :N], cdec[:, :N]
+    r = oracle.check_float(got, ref, s, K, alpha, A.scale, B.scale, beta, cdec, out=out)
     assert r["ok"], r
     assert np.all(d[:, N:] == NAN_CODE[out])  # padding columns of D untouched
 
