@@ -217,9 +217,14 @@ def decompress24(dtype, vals, idx, K):
 
 def gemm_sparse24(dtA, dtB, layB, M, N, K, vals, idx, B, ldb, C=None, ldc=None,
                   alpha=1.0, beta=0.0, rows=None, cols=None, out="f32"):
-    """Sparse-A reference: decompress A, then the dense float GEMM with the
-    dense K (A row-major, i.e. K-contiguous)."""
+    """Sparse-A reference: decompress A, then the dense GEMM with the dense K
+    (A row-major, i.e. K-contiguous).  Float inputs return (d_ref, abs_sum) as
+    ``gemm_float``; int8 returns (d_ref int32, None), exact as ``gemm_i8``.
+    fp8 dequantisation scales, if any, are part of alpha."""
     A = decompress24(dtA, vals, idx, K)
+    if dtA == "i8":
+        return gemm_i8("k_contig", layB, M, N, K, A, K, B, ldb, C, ldc, int(alpha), int(beta),
+                       rows, cols), None
     return gemm_float(dtA, dtB, "k_contig", layB, M, N, K, A, K, B, ldb, C, ldc,
                       alpha, beta, 1.0, 1.0, rows, cols, out)
 

@@ -132,3 +132,66 @@ def test_generator_gives_exactly_two_nonzeros_per_group():
     A = W.sparse24_dense("bf16", 64, 256)
     nz = (A.reshape(64, 64, 4) & 0x7FFF) != 0
     assert np.all(nz.sum(-1) == 2)
+
+
+def _brute_sparse_int(vals, idx, K, B, ldb, layB, N, C, alpha, beta):
+    """Python-int walk over the compressed form itself: for every group of four,
+    its 4-bit code names the two dense positions of its two kept values."""
+    M = vals.shape[0]
+    out = np.zeros((M, N), np.int64)
+    for i in range(M):
+        for j in range(N):
+            acc = 0
+            for g in range(K // 4):
+                code = (int(idx[i, g // 8]) >> (4 * (g % 8))) & 0xF
+                for slot, pos in enumerate((code & 3, code >> 2)):
+                    k = 4 * g + pos
+                    b = int(B[j * ldb + k]) if layB == "k_contig" else int(B[k * ldb + j])
+                    acc += int(vals[i, 2 * g + slot]) * b
+            t = alpha * acc + (beta * int(C[i, j]) if beta else 0)
+            out[i, j] = ((t + 2**31) % 2**32) - 2**31
+    return out.astype(np.int32)
+
+
+@pytest.mark.parametrize("layB", ["k_contig", "mn_contig"])
+def test_sparse_int8_gemm_matches_brute_force(layB):
+    M, N, K = 5, 7, 72
+    A = W.sparse24_dense("i8", M, K, dist="int8", seed=5)
+    B = W.operand("B", "i8", K, N, "int8", layB, seed=6)
+    C = W.c_matrix(M, N, "int20", seed=7)
+    vals, idx, viol = oracle.compress24("i8", A)
+    assert viol == 0
+    d, s = oracle.gemm_sparse24("i8", "i8", layB, M, N, K, vals, idx, B.codes, B.ld, C, N, -3, 2)
+    assert s is None
+    want = _brute_sparse_int(vals, idx, K, B.codes.ravel(), B.ld, layB, N, C, -3, 2)
+    assert np.array_equal(d, want)
+
+
+def test_sparse_int8_wraps_mod_2_32():
+    """All products 127 * 127 over K = 1024 with alpha = 2^30: the int32 result wraps."""
+    M, N, K = 2, 3, 1024
+    A = np.zeros((M, K), np.int8)
+    A[:, 0::4] = 127
+    A[:, 3::4] = 127
+    B = np.full((N, K), 127, np.int8)
+    vals, idx, _ = oracle.compress24("i8", A)
+    d, _ = oracle.gemm_sparse24("i8", "i8", "k_contig", M, N, K, vals, idx, B, K, alpha=2**30)
+    exact = 2**30 * (K // 2) * 127 * 127
+    assert np.all(d == np.int32(((exact + 2**31) % 2**32) - 2**31))
+
+
+@pytest.mark.parametrize("dtA,dtB", [("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")])
+def test_sparse_fp8_gemm_matches_float64(dtA, dtB):
+    """fp8 2:4 reference against numpy float64 on the decoded dense operands
+    (scales folded into alpha), rounded once to binary32."""
+    M, N, K = 9, 11, 96
+    A = W.sparse24_dense(dtA, M, K, seed=8)
+    B = W.operand("B", dtB, K, N, "normal", "k_contig", seed=9, fp8_scaled=True)
+    vals, idx, viol = oracle.compress24(dtA, A)
+    assert viol == 0
+    alpha = 0.375 * B.scale
+    d, _ = oracle.gemm_sparse24(dtA, dtB, "k_contig", M, N, K, vals, idx, B.codes, B.ld, alpha=alpha)
+    Ad = oracle.decode(dtA, A).reshape(M, K)
+    Bd = oracle.decode(dtB, B.codes).reshape(N, K).T
+    want = (alpha * (Ad @ Bd)).astype(np.float32)
+    assert np.array_equal(d, want)
