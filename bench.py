@@ -11,6 +11,7 @@ full-size synthetic workload (8192^3 for every GEMM):
   gemm_sparse24 bf16 (2:4 A) x bf16 -> f32
   gemm_dense  bf16 x bf16 -> bf16  (C and D in bfloat16, alpha = beta = 1)
   gemm_dense  skinny bf16 32768 x 16 x 8192 and 16 x 32768 x 8192 (C absent): HBM-bound
+  gemm_sparse24 int8 (2:4 A) x int8 -> i32 and e4m3 (2:4 A) x e4m3 -> f32 (C absent)
 Each call is bracketed by HIP events on the stream it is launched on, so every
 kernel's average duration is measured live.  `value` is the dense bf16 8192^3
 rate (TFLOP/s); the per-dtype rates the metric asks for are in `per_dtype`.
@@ -111,6 +112,15 @@ def main():
     Bs = ops["bf16"][2]
     vals = torch.empty((M, K // 2), dtype=torch.int16, device="cuda")
     idx = torch.empty((M, (K + 31) // 32), dtype=torch.int32, device="cuda")
+    # 8-bit 2:4 operands, compressed on the device before timing
+    sp8 = {}
+    for dt, B_ in (("i8", ops["i8"][2]), ("e4m3", ops["e4m3xe4m3"][2])):
+        A_ = dev(W.sparse24_dense(dt, M, K, dist="int8" if dt == "i8" else "normal"))
+        v_ = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+        i_ = torch.empty((M, (K + 31) // 32), dtype=torch.int32, device="cuda")
+        mcg.compress24(dt, M, K, A_, K, v_, K // 2, i_, i_.shape[1], None)
+        del A_
+        sp8[dt] = (v_, i_, B_)
     D = torch.empty((M, N), dtype=torch.float32, device="cuda")
     Di = torch.empty((M, N), dtype=torch.int32, device="cuda")
     # bfloat16 C and D for the 16-bit output entry
@@ -145,6 +155,14 @@ def main():
         elif name == "sparse24":
             mcg.gemm_sparse24("bf16", "bf16", 0, M, N, K, vals, K // 2, idx, idx.shape[1], Bs, K, None,
                               D, N, "f32", 1.0, 0.0, stream=s)
+        elif name == "sparse24_i8":
+            v_, i_, B_ = sp8["i8"]
+            mcg.gemm_sparse24("i8", "i8", 0, M, N, K, v_, K // 2, i_, i_.shape[1], B_, K, None, Di, N,
+                              "i32", 1, 0, stream=s)
+        elif name == "sparse24_e4m3":
+            v_, i_, B_ = sp8["e4m3"]
+            mcg.gemm_sparse24("e4m3", "e4m3", 0, M, N, K, v_, K // 2, i_, i_.shape[1], B_, K, None, D, N,
+                              "f32", B8.scale, 0.0, stream=s)
         elif name == "bf16_out":
             a, lda, b, ldb, sa, sb = ops["bf16"]
             mcg.gemm_dense("bf16", "bf16", 0, 0, M, N, K, a, lda, b, ldb, C16, D16, N, "bf16", 1.0, 1.0,
@@ -157,7 +175,7 @@ def main():
                            "f32", 1.0, 0.0, stream=s)
 
     names = ["bf16", "f16", "i8", "e4m3xe4m3", "e4m3xe5m2", "compress24", "sparse24", "bf16_out",
-             "skinny_n16", "skinny_m16"]
+             "skinny_n16", "skinny_m16", "sparse24_i8", "sparse24_e4m3"]
     if args.only:
         keep = set(args.only.split(","))
         names = [x for x in names if x in keep or x == "compress24" and "sparse24" in keep]
@@ -195,6 +213,14 @@ def main():
         elif x == "bf16_out":
             tf = flops / t / 1e12
             per[x] = {"TFLOP/s": tf, "ms": ms[x], "peak": PEAK["bf16"], "frac_of_peak": tf / PEAK["bf16"]}
+        elif x in ("sparse24_i8", "sparse24_e4m3"):
+            tf = flops / t / 1e12
+            dense = "i8" if x == "sparse24_i8" else "e4m3xe4m3"
+            pk = PEAK["i8"] if x == "sparse24_i8" else PEAK["fp8"]
+            u = "TOPS" if x == "sparse24_i8" else "TFLOP/s"
+            per[x] = {f"{u}_dense_equiv": tf, f"{u}_algorithmic": tf / 2, "ms": ms[x],
+                      "frac_of_dense_peak": tf / pk,
+                      f"vs_dense_{dense}": tf / (flops / (ms[dense] * 1e-3) / 1e12) if dense in ms else None}
         elif x == "sparse24":
             tf = flops / t / 1e12
             per[x] = {"TFLOP/s_dense_equiv": tf, "TFLOP/s_algorithmic": tf / 2, "ms": ms[x],

@@ -107,7 +107,14 @@ typedef enum {
  * Accuracy      : float results are the fp32 result of a non-IEEE matrix-core
  *                 accumulation, not bit-reproducible across architectures
  *                 ("Accurate Models of AMD Matrix Cores", Abstract); int8
- *                 results are exact.
+ *                 results are exact.  Every float result stays within
+ *                 4*2^-24*(K+2)*|alpha*scaleA*scaleB|*sum|a*b| + 2^-24*|D| of
+ *                 the exact value (plus the output rounding for 16-bit D).
+ *                 The native fp8 instructions keep only about 13 bits below
+ *                 the largest product of each group they sum (measured), which
+ *                 fits that bound from K = 6144 on; below it fp8 operands are
+ *                 widened exactly to bfloat16 and multiplied on the bfloat16
+ *                 instructions.
  * Alignment     : none required; 16-byte aligned pointers and leading
  *                 dimensions whose byte size is a multiple of 16 take the
  *                 vector-load path, anything else a slower element path.
@@ -132,7 +139,14 @@ int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB,
  * gemm_sparse24 -- D = alpha*(A.B) + beta*C with A given in 2:4 compressed
  * form and multiplied on the sparse matrix cores (SMFMAC).
  *
- * dtypeA/dtypeB : MCG_BF16 x MCG_BF16 or MCG_F16 x MCG_F16; dtypeD = MCG_F32.
+ * dtypeA/dtypeB : MCG_BF16 x MCG_BF16, MCG_F16 x MCG_F16 (dtypeD MCG_F32,
+ *                 MCG_BF16 or MCG_F16), any pair of MCG_FP8_E4M3 / MCG_FP8_E5M2
+ *                 (same outputs; per-tensor dequantisation scales are folded
+ *                 into alpha by the caller), or MCG_I8 x MCG_I8 (dtypeD
+ *                 MCG_I32, integral alpha/beta, exact wrapping int32 as for
+ *                 gemm_dense).  fp8 with K below 6144 is widened exactly to
+ *                 bfloat16 and multiplied on the bfloat16 sparse instruction
+ *                 (see Accuracy at gemm_dense).
  * layoutB       : mcg_layout of B (A is always the compressed row-major form).
  * K             : the DENSE K; K % 4 == 0.
  * A_compressed  : M x K/2 values, row-major, lda_c >= K/2.  Row i holds, for
@@ -212,8 +226,8 @@ int mcg_dense_path(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, i
 int mcg_dense_splits(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A,
                      int64_t lda, const void* B, int64_t ldb, const void* C, const void* D, int dtypeD,
                      double beta);
-int mcg_sparse24_path(int layoutB, int64_t M, int64_t N, int64_t K, const void* A_compressed, int64_t lda_c,
-                      const uint32_t* A_index, int64_t ld_idx, const void* B, int64_t ldb);
+int mcg_sparse24_path(int dtypeA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A_compressed,
+                      int64_t lda_c, const uint32_t* A_index, int64_t ld_idx, const void* B, int64_t ldb);
 
 /* Human-readable name of an mcg_status value (static storage). */
 const char* mcg_status_string(int status);

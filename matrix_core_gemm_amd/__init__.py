@@ -64,7 +64,7 @@ _lib.mcg_validate_compress24.argtypes = [_i32, _i64, _i64, _vp, _i64, _vp, _i64,
 _lib.mcg_dense_path.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64]
 _lib.mcg_dense_splits.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp,
                                   _i32, ctypes.c_double]
-_lib.mcg_sparse24_path.argtypes = [_i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
+_lib.mcg_sparse24_path.argtypes = [_i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
 
 
 def lib():
@@ -171,10 +171,10 @@ def dense_splits(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb, C, D, dtypeD
                                  _ptr(B), ldb, _ptr(C), _ptr(D), _dt(dtypeD), float(beta))
 
 
-def sparse24_path(layoutB, M, N, K, A_compressed, lda_c, A_index, ld_idx, B, ldb) -> int:
+def sparse24_path(dtypeA, layoutB, M, N, K, A_compressed, lda_c, A_index, ld_idx, B, ldb) -> int:
     """1 if gemm_sparse24 with these arguments runs the 256 x 256 kernel, else 0."""
-    return _lib.mcg_sparse24_path(_lay(layoutB), M, N, K, _ptr(A_compressed), lda_c, _ptr(A_index),
-                                  ld_idx, _ptr(B), ldb)
+    return _lib.mcg_sparse24_path(_dt(dtypeA), _lay(layoutB), M, N, K, _ptr(A_compressed), lda_c,
+                                  _ptr(A_index), ld_idx, _ptr(B), ldb)
 
 
 def status_string(status: int) -> str:

@@ -149,9 +149,12 @@ int mcg_validate_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_
                           const void* A_compressed, int64_t lda_c, const uint32_t* A_index,
                           int64_t ld_idx, const void* B, int64_t ldb, const void* C, const void* D,
                           int64_t ldc, int dtypeD, double alpha, double beta) {
-  if (!((dtypeA == MCG_BF16 && dtypeB == MCG_BF16) || (dtypeA == MCG_F16 && dtypeB == MCG_F16)))
+  const bool fp8 = (dtypeA == MCG_FP8_E4M3 || dtypeA == MCG_FP8_E5M2) &&
+                   (dtypeB == MCG_FP8_E4M3 || dtypeB == MCG_FP8_E5M2);
+  const bool i8 = dtypeA == MCG_I8 && dtypeB == MCG_I8;
+  if (!((dtypeA == MCG_BF16 && dtypeB == MCG_BF16) || (dtypeA == MCG_F16 && dtypeB == MCG_F16) || fp8 || i8))
     return MCG_ERR_UNSUPPORTED_DTYPE;
-  if (!float_out(dtypeD) || !valid_layout(layoutB)) return MCG_ERR_UNSUPPORTED_DTYPE;
+  if ((i8 ? dtypeD != MCG_I32 : !float_out(dtypeD)) || !valid_layout(layoutB)) return MCG_ERR_UNSUPPORTED_DTYPE;
   if (M < 0 || N < 0 || K < 0 || K % 4 != 0) return MCG_ERR_INVALID_SIZE;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return MCG_ERR_INVALID_SIZE;
   if (M == 0 || N == 0) return MCG_SUCCESS;
@@ -162,11 +165,15 @@ int mcg_validate_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_
   if (lda_c < (K / 2 > 1 ? K / 2 : 1) || ld_idx < ((K + 31) / 32 > 1 ? (K + 31) / 32 : 1) ||
       ldb < (min_ldb > 1 ? min_ldb : 1) || ldc < N)
     return MCG_ERR_INVALID_LD;
-  const int ebd = elem_bytes(dtypeD);
-  if (!aligned_to(A_compressed, 2) || !aligned_to(B, 2) || !aligned_to(A_index, 4) ||
+  const int ebd = elem_bytes(dtypeD), eb = elem_bytes(dtypeA);
+  if (!aligned_to(A_compressed, eb) || !aligned_to(B, eb) || !aligned_to(A_index, 4) ||
       !aligned_to(D, ebd) || (C && !aligned_to(C, ebd)))
     return MCG_ERR_MISALIGNED;
-  if (!std::isfinite(alpha) || !std::isfinite(beta)) return MCG_ERR_INVALID_VALUE;
+  if (i8) {
+    if (!int32_integral(alpha) || !int32_integral(beta)) return MCG_ERR_INVALID_VALUE;
+  } else if (!std::isfinite(alpha) || !std::isfinite(beta)) {
+    return MCG_ERR_INVALID_VALUE;
+  }
   return MCG_SUCCESS;
 }
 
@@ -194,16 +201,19 @@ int gemm_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int
   a.ldc = ldc;
   a.alpha = (float)alpha;
   a.beta = (float)beta;
+  a.alpha_i = dtypeA == MCG_I8 ? (int)alpha : 0;
+  a.beta_i = dtypeA == MCG_I8 ? (int)beta : 0;
   a.use_c = beta != 0.0;
   a.out = out_format(dtypeD);
   const int vb = 4 * elem_bytes(dtypeD);
   a.vec_cd = aligned_to(D, vb) && (!a.use_c || aligned_to(C, vb)) && ldc % 4 == 0;
+  const int eb = elem_bytes(dtypeA);
   const bool aligned = K == 0 || (aligned_to(A_compressed, 16) && aligned_to(B, 16) &&
-                                  aligned_to(A_index, 16) && (lda_c * 2) % 16 == 0 &&
-                                  (ldb * 2) % 16 == 0 && (ld_idx * 4) % 16 == 0);
-  if (mcg::sparse_fast_ok(layoutB, a))
-    return hip_status(mcg::launch_sparse_fast(dtypeA, layoutB, a, (hipStream_t)stream));
-  return hip_status(mcg::launch_sparse(dtypeA, layoutB, aligned, a, (hipStream_t)stream));
+                                  aligned_to(A_index, 16) && (lda_c * eb) % 16 == 0 &&
+                                  (ldb * eb) % 16 == 0 && (ld_idx * 4) % 16 == 0);
+  if (mcg::sparse_fast_ok(dtypeA, layoutB, a))
+    return hip_status(mcg::launch_sparse_fast(dtypeA, dtypeB, layoutB, a, (hipStream_t)stream));
+  return hip_status(mcg::launch_sparse(dtypeA, dtypeB, layoutB, aligned, a, (hipStream_t)stream));
 }
 
 int mcg_validate_compress24(int dtype, int64_t M, int64_t K, const void* A, int64_t lda,
@@ -310,8 +320,9 @@ int mcg_dense_splits(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N,
   return dense_plan(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb, can_split).splits;
 }
 
-int mcg_sparse24_path(int layoutB, int64_t M, int64_t N, int64_t K, const void* A_compressed, int64_t lda_c,
-                      const uint32_t* A_index, int64_t ld_idx, const void* B, int64_t ldb) {
+int mcg_sparse24_path(int dtypeA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A_compressed,
+                      int64_t lda_c, const uint32_t* A_index, int64_t ld_idx, const void* B, int64_t ldb) {
+  if (dtypeA < MCG_BF16 || dtypeA > MCG_FP8_E5M2) return 0;
   mcg::SparseArgs a{};
   a.Ac = (const char*)A_compressed;
   a.idx = A_index;
@@ -322,7 +333,7 @@ int mcg_sparse24_path(int layoutB, int64_t M, int64_t N, int64_t K, const void* 
   a.lda_c = lda_c;
   a.ld_idx = ld_idx;
   a.ldb = ldb;
-  return mcg::sparse_fast_ok(layoutB, a) ? 1 : 0;
+  return mcg::sparse_fast_ok(dtypeA, layoutB, a) ? 1 : 0;
 }
 
 const char* mcg_status_string(int status) {

@@ -179,22 +179,6 @@ struct OpF8W {
   }
 };
 
-// ----------------------------------------------------------------- sparse ops
-struct SpBF16 {
-  static constexpr int ELEM_BYTES = 2, K_STEP = 64;  // dense K per instruction
-  __device__ static __forceinline__ f32x4 mma(i32x4 p_comp, i32x8 q, f32x4 c, int index) {
-    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(bit_cast<bf16x8>(p_comp), bit_cast<bf16x16>(q), c,
-                                                     index, 0, 0);
-  }
-};
-struct SpF16 {
-  static constexpr int ELEM_BYTES = 2, K_STEP = 64;
-  __device__ static __forceinline__ f32x4 mma(i32x4 p_comp, i32x8 q, f32x4 c, int index) {
-    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(bit_cast<f16x8>(p_comp), bit_cast<f16x16>(q), c,
-                                                    index, 0, 0);
-  }
-};
-
 // ------------------------------------------------------------ output layout
 // 16x16 output tile: lane l, register r -> (row, col) of the instruction output.
 __host__ __device__ constexpr int out_row(int lane, int r) { return 4 * (lane >> 4) + r; }

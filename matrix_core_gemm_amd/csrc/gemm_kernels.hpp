@@ -49,9 +49,10 @@ struct SparseArgs {
   void* D;
   int64_t M, N, K;               // dense K
   int64_t lda_c, ld_idx, ldb, ldc;
-  float alpha, beta;
+  float alpha, beta;    // float paths (fp8: alpha carries the dequantisation scales)
+  int alpha_i, beta_i;  // int8 path
   int use_c, vec_cd;
-  int out;  // OUT_32, OUT_BF16 or OUT_F16: format of C and D
+  int out;  // OUT_32 (binary32 / int32), OUT_BF16 or OUT_F16: format of C and D
   int tiles_m, tiles_n;
 };
 
@@ -85,9 +86,9 @@ bool stream_path_ok(int dtA, int layoutA, int layoutB, const DenseArgs& a, bool 
 hipError_t launch_stream(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
 bool fast_path_ok(int dtA, int layoutA, int layoutB, const DenseArgs& a, bool aligned);
 hipError_t launch_fast(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
-hipError_t launch_sparse(int dt, int layoutB, bool aligned, const SparseArgs& a, hipStream_t s);
-bool sparse_fast_ok(int layoutB, const SparseArgs& a);
-hipError_t launch_sparse_fast(int dt, int layoutB, const SparseArgs& a, hipStream_t s);
+hipError_t launch_sparse(int dtA, int dtB, int layoutB, bool aligned, const SparseArgs& a, hipStream_t s);
+bool sparse_fast_ok(int dtA, int layoutB, const SparseArgs& a);
+hipError_t launch_sparse_fast(int dtA, int dtB, int layoutB, const SparseArgs& a, hipStream_t s);
 hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s);
 
 }  // namespace mcg

@@ -10,17 +10,19 @@
 // CDNA by SMFMAC, the wave64 sparse MFMA named on that page's introduction.
 //
 // Index layout in memory (the library's canonical form): group g of row i has
-// the 4-bit code p0 | p1 << 2 at bits 4*(g % 8) of word g/8.  On gfx950 a lane
-// of smfmac_f32_16x16x64 holds four consecutive groups and reads their codes
-// from one 16-bit half of its index register, nibble n for compressed values
-// 2n and 2n+1 (measured).  So a lane's index is a 16-bit slice of one canonical
-// word and needs no re-packing.
+// the 4-bit code p0 | p1 << 2 at bits 4*(g % 8) of word g/8.  On gfx950 the
+// sparse instructions read, per lane, the codes of the groups its kept values
+// belong to, nibble n for kept values 2n and 2n+1 (measured): a lane of the
+// 16-bit instructions (8 kept values, 4 groups) uses one 16-bit half of a
+// canonical word, a lane of the 8-bit instructions (16 kept values, 8 groups)
+// a whole word.  So a lane's index is a slice of one canonical word and needs
+// no re-packing.
 //
 // Sparse kernel structure: as the dense kernel (256 threads, 2 x 2 waves,
-// double-buffered LDS), with K tiles of 128 dense k: A_c tile 128 bytes per
-// row (64 kept values), index tile 16 bytes per row (4 words), B tile
-// 256 bytes of K per column.  The sparse operand must be the instruction's P,
-// so output lanes hold four consecutive rows of one column of D.
+// double-buffered LDS), with K tiles of KD dense k (128 for 16-bit, 256 for
+// 8-bit elements): kept values 128 bytes per row, index KD / 32 words per row,
+// B 256 bytes of K per column.  The sparse operand must be the instruction's
+// first operand, so output lanes hold four consecutive rows of one column of D.
 #include "gemm_kernels.hpp"
 #include "tile_io.hpp"
 
@@ -36,11 +38,119 @@ __device__ __forceinline__ uint32_t fix_zero_codes(uint32_t w) {
   return w | (zero << 2);
 }
 
+// ---------------------------------------------------------------- 16x16 ops
+// Per instruction s of a tile, lane l serves row / column l & 15 and lane
+// group g = l >> 4 (measured layouts):
+//   16-bit (16x16x64): kept values of dense k [16g, 16g + 16) of the
+//     instruction's 64 (8 values, kept bytes [32s... see frag_a]); B k
+//     [8g, 8g + 8) and [32 + 8g, 40 + 8g); codes in half g % 2 of word 2s + g / 2.
+//   8-bit (16x16x128): kept values of dense k [32g, 32g + 32) (16 values); B
+//     k [16g, 16g + 16) and [64 + 16g, 80 + 16g); codes in word 4s + g.
+// In bytes both read 16 kept bytes at 16 (4s + g) and B bytes at 128s + 16g
+// and 128s + 64 + 16g.
+template <int EB_>
+struct SpTile {
+  static constexpr int EB = EB_;
+  static constexpr int KD = 256 / EB_;  // dense k per LDS tile
+  static constexpr int IW = KD / 32;    // index words per row and tile
+};
+
+template <class R>
+__device__ __forceinline__ i32x8 sp_b_bytes(const lds_char* t, int rb, int s, int g, int lane) {
+  const i32x4 lo = R::run16(t, rb, 128 * s + 16 * g, lane);
+  const i32x4 hi = R::run16(t, rb, 128 * s + 64 + 16 * g, lane);
+  return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+template <bool F16>
+struct SpH : SpTile<2> {  // bfloat16 / binary16
+  static constexpr int K_STEP = 64;  // dense k per instruction
+  static constexpr bool INT_ACC = false;
+  using acc_t = f32x4;
+  using frag_a_t = i32x4;
+  template <class R>
+  __device__ static __forceinline__ i32x4 frag_a(const lds_char* t, int rb, int s, int lane) {
+    return R::run16(t, rb, 16 * (4 * s + (lane >> 4)), lane);
+  }
+  template <class R>
+  __device__ static __forceinline__ i32x8 frag_b(const lds_char* t, int rb, int s, int lane) {
+    return sp_b_bytes<R>(t, rb, s, lane >> 4, lane);
+  }
+  __device__ static __forceinline__ int frag_i(const lds_char* ti, int row, int s, int lane) {
+    const int g = lane >> 4;
+    const uint32_t w = *(const __attribute__((address_space(3))) uint32_t*)(ti + row * 4 * IW + 4 * (2 * s + (g >> 1)));
+    return (int)(fix_zero_codes(w >> (16 * (g & 1))) & 0xffffu);
+  }
+  __device__ static __forceinline__ acc_t mma(i32x4 a, i32x8 b, acc_t c, int idx) {
+    if constexpr (F16)
+      return __builtin_amdgcn_smfmac_f32_16x16x64_f16(bit_cast<f16x8>(a), bit_cast<f16x16>(b), c, idx, 0, 0);
+    else
+      return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(bit_cast<bf16x8>(a), bit_cast<bf16x16>(b), c, idx, 0, 0);
+  }
+};
+
+// 8-bit: KIND 0 int8, 1 native fp8 (FA / FB = formats of A / B: 0 E4M3, 1 E5M2)
+template <int KIND, int FA = 0, int FB = 0>
+struct Sp8 : SpTile<1> {
+  static constexpr int K_STEP = 128;
+  static constexpr bool INT_ACC = KIND == 0;
+  using acc_t = typename std::conditional<KIND == 0, i32x4, f32x4>::type;
+  template <class R>
+  __device__ static __forceinline__ i32x4 frag_a(const lds_char* t, int rb, int s, int lane) {
+    return R::run16(t, rb, 16 * (4 * s + (lane >> 4)), lane);
+  }
+  template <class R>
+  __device__ static __forceinline__ i32x8 frag_b(const lds_char* t, int rb, int s, int lane) {
+    return sp_b_bytes<R>(t, rb, s, lane >> 4, lane);
+  }
+  __device__ static __forceinline__ int frag_i(const lds_char* ti, int row, int s, int lane) {
+    const uint32_t w = *(const __attribute__((address_space(3))) uint32_t*)(ti + row * 4 * IW + 4 * (4 * s + (lane >> 4)));
+    return (int)fix_zero_codes(w);
+  }
+  __device__ static __forceinline__ acc_t mma(i32x4 a, i32x8 b, acc_t c, int idx) {
+    if constexpr (KIND == 0) return __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, c, idx, 0, 0);
+    else if constexpr (FA == 0 && FB == 0) return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(a, b, c, idx, 0, 0);
+    else if constexpr (FA == 0 && FB == 1) return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_bf8(a, b, c, idx, 0, 0);
+    else if constexpr (FA == 1 && FB == 0) return __builtin_amdgcn_smfmac_f32_16x16x128_bf8_fp8(a, b, c, idx, 0, 0);
+    else return __builtin_amdgcn_smfmac_f32_16x16x128_bf8_bf8(a, b, c, idx, 0, 0);
+  }
+};
+
+// fp8 widened exactly to bfloat16 and multiplied by the bfloat16 instruction
+// (K below the native-fp8 threshold): the 8-bit tiles of Sp8, read in the
+// 16-bit instruction's k assignment 8 bytes at a time and converted.
+template <int FA, int FB>
+struct Sp8W : SpTile<1> {
+  static constexpr int K_STEP = 64;
+  static constexpr bool INT_ACC = false;
+  using acc_t = f32x4;
+  template <class R>
+  __device__ static __forceinline__ i32x4 frag_a(const lds_char* t, int rb, int s, int lane) {
+    return fp8x8_to_bf16x8<FA>(R::run8(t, rb, 32 * s + 8 * (lane >> 4), lane));
+  }
+  template <class R>
+  __device__ static __forceinline__ i32x8 frag_b(const lds_char* t, int rb, int s, int lane) {
+    const int g = lane >> 4;
+    const i32x4 lo = fp8x8_to_bf16x8<FB>(R::run8(t, rb, 64 * s + 8 * g, lane));
+    const i32x4 hi = fp8x8_to_bf16x8<FB>(R::run8(t, rb, 64 * s + 32 + 8 * g, lane));
+    return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  }
+  __device__ static __forceinline__ int frag_i(const lds_char* ti, int row, int s, int lane) {
+    const int g = lane >> 4;
+    const uint32_t w = *(const __attribute__((address_space(3))) uint32_t*)(ti + row * 4 * IW + 4 * (2 * s + (g >> 1)));
+    return (int)(fix_zero_codes(w >> (16 * (g & 1))) & 0xffffu);
+  }
+  __device__ static __forceinline__ acc_t mma(i32x4 a, i32x8 b, acc_t c, int idx) {
+    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(bit_cast<bf16x8>(a), bit_cast<bf16x16>(b), c, idx, 0, 0);
+  }
+};
+
 template <class Op, int LB, int BM, int BN, bool ALIGNED>
 __global__ __launch_bounds__(256) void gemm_sparse_kernel(SparseArgs p) {
   constexpr int NT = 256;
-  constexpr int EB = Op::ELEM_BYTES;    // 2
-  constexpr int KD = 128;               // dense K per tile
+  constexpr int EB = Op::EB;
+  constexpr int KD = Op::KD;            // dense K per tile
+  constexpr int IW = Op::IW;            // index words per row and tile
   constexpr int KTB_A = KD / 2 * EB;    // 128 bytes of kept values per row
   constexpr int KTB_B = KD * EB;        // 256 bytes of dense K per column
   constexpr int STEPS = KD / Op::K_STEP;
@@ -49,7 +159,9 @@ __global__ __launch_bounds__(256) void gemm_sparse_kernel(SparseArgs p) {
   using GB = TileGeom<EB, LB, BN, KTB_B>;
   using RA = FragReader<EB, 16, LAYOUT_K, BM, KTB_A>;
   using RB = FragReader<EB, 16, LB, BN, KTB_B>;
-  constexpr int IDX_BYTES = BM * 16;
+  using acc_t = typename Op::acc_t;
+  constexpr int IDX_BYTES = BM * 4 * IW;
+  static_assert(KTB_A == 128 && KTB_B == 256 && IW % 4 == 0, "tile geometry");
 
   __shared__ __attribute__((aligned(16))) char smem_raw[2 * (GA::BYTES + GB::BYTES + IDX_BYTES)];
   lds_char* smem = (lds_char*)smem_raw;
@@ -77,7 +189,7 @@ __global__ __launch_bounds__(256) void gemm_sparse_kernel(SparseArgs p) {
 
   TileLoader<EB, LAYOUT_K, BM, NT, ALIGNED, KTB_A> la;
   TileLoader<EB, LB, BN, NT, ALIGNED, KTB_B> lb;
-  i32x4 ireg = {0, 0, 0, 0};  // threads < BM: one row of 4 index words
+  i32x4 ireg[IW / 4];  // threads < BM: the index words of one row
   auto load_tiles = [&](int kt) {
     const int64_t k0 = (int64_t)kt * KD;
     la.load(p.Ac, p.lda_c, m0, k0 / 2, p.M, Kc, tid);
@@ -86,34 +198,38 @@ __global__ __launch_bounds__(256) void gemm_sparse_kernel(SparseArgs p) {
     if (tid < BM) {
       const int64_t row = m0 + tid, w0 = k0 / 32;
       const uint32_t* src = p.idx + row * p.ld_idx + w0;
-      if (ALIGNED && row < p.M && w0 + 4 <= nwords) {
-        ireg = *(const i32x4*)src;
-      } else {
-        ireg = i32x4{0, 0, 0, 0};
-        if (row < p.M)
-          for (int e = 0; e < 4; ++e)
-            if (w0 + e < nwords) ireg[e] = (int)src[e];
+#pragma unroll
+      for (int v = 0; v < IW / 4; ++v) {
+        if (ALIGNED && row < p.M && w0 + 4 * v + 4 <= nwords) {
+          ireg[v] = *(const i32x4*)(src + 4 * v);
+        } else {
+          ireg[v] = i32x4{0, 0, 0, 0};
+          if (row < p.M)
+            for (int e = 0; e < 4; ++e)
+              if (w0 + 4 * v + e < nwords) ireg[v][e] = (int)src[4 * v + e];
+        }
       }
     }
   };
   auto store_tiles = [&](int buf) {
     la.store(ldsA[buf], tid);
     lb.store(ldsB[buf], tid);
-    if (tid < BM) lds_write_b128(ldsI[buf], tid * 16, ireg);
+    if (tid < BM)
+#pragma unroll
+      for (int v = 0; v < IW / 4; ++v) lds_write_b128(ldsI[buf], tid * 4 * IW + 16 * v, ireg[v]);
   };
 
-  f32x4 acc[WTM][WTN];
+  acc_t acc[WTM][WTN];
 #pragma unroll
   for (int i = 0; i < WTM; ++i)
 #pragma unroll
-    for (int j = 0; j < WTN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < WTN; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
 
   if (nk > 0) {
     load_tiles(0);
     store_tiles(0);
     __syncthreads();
   }
-  const int g = lane >> 4;
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) load_tiles(kt + 1);
@@ -125,20 +241,11 @@ __global__ __launch_bounds__(256) void gemm_sparse_kernel(SparseArgs p) {
 #pragma unroll
       for (int i = 0; i < WTM; ++i) {
         const int rb = wm * (BM / 2) + i * 16;
-        fa[i] = RA::run16(ldsA[cur], rb, 16 * (4 * s + g), lane);
-        // codes of dense k [64s + 16g, +16): word 2s + g/2, half g % 2
-        const int row = rb + (lane & 15);
-        const uint32_t w = *(const __attribute__((address_space(3))) uint32_t*)(ldsI[cur] + row * 16 + 4 * (2 * s + (g >> 1)));
-        fi[i] = (int)(fix_zero_codes(w >> (16 * (g & 1))) & 0xffffu);
+        fa[i] = Op::template frag_a<RA>(ldsA[cur], rb, s, lane);
+        fi[i] = Op::frag_i(ldsI[cur], rb + (lane & 15), s, lane);
       }
 #pragma unroll
-      for (int j = 0; j < WTN; ++j) {
-        const int rb = wn * (BN / 2) + j * 16;
-        // dense k [64s + 8g, +8) and [64s + 32 + 8g, +8)
-        const i32x4 lo = RB::run16(ldsB[cur], rb, EB * (64 * s + 8 * g), lane);
-        const i32x4 hi = RB::run16(ldsB[cur], rb, EB * (64 * s + 32 + 8 * g), lane);
-        fb[j] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      }
+      for (int j = 0; j < WTN; ++j) fb[j] = Op::template frag_b<RB>(ldsB[cur], wn * (BN / 2) + j * 16, s, lane);
 #pragma unroll
       for (int i = 0; i < WTM; ++i)
 #pragma unroll
@@ -159,7 +266,13 @@ __global__ __launch_bounds__(256) void gemm_sparse_kernel(SparseArgs p) {
       for (int r = 0; r < 4; ++r) {
         const int64_t m = m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4) + r;
         if (m >= p.M) continue;
-        combine_store(p.C, p.D, m * p.ldc + n, acc[i][j][r], p.alpha, p.beta, p.use_c, p.out);
+        const int64_t off = m * p.ldc + n;
+        if constexpr (Op::INT_ACC) {
+          const uint32_t c = p.use_c ? (uint32_t)((const int*)p.C)[off] : 0u;
+          ((int*)p.D)[off] = (int)((uint32_t)p.alpha_i * (uint32_t)acc[i][j][r] + (uint32_t)p.beta_i * c);
+        } else {
+          combine_store(p.C, p.D, off, acc[i][j][r], p.alpha, p.beta, p.use_c, p.out);
+        }
       }
     }
   }
@@ -178,14 +291,28 @@ static hipError_t launch_sparse_one(const SparseArgs& a0, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_sparse(int dt, int lb, bool aligned, const SparseArgs& a, hipStream_t s) {
-#define MCG_S(OP)                                                                        \
-  if (lb == LAYOUT_K)                                                                    \
-    return aligned ? launch_sparse_one<OP, LAYOUT_K, true>(a, s) : launch_sparse_one<OP, LAYOUT_K, false>(a, s); \
-  return aligned ? launch_sparse_one<OP, LAYOUT_MN, true>(a, s) : launch_sparse_one<OP, LAYOUT_MN, false>(a, s);
-  if (dt == DT_BF16) { MCG_S(SpBF16) }
-  MCG_S(SpF16)
-#undef MCG_S
+template <class Op>
+static hipError_t launch_sparse_layouts(int lb, bool aligned, const SparseArgs& a, hipStream_t s) {
+  if (lb == LAYOUT_K)
+    return aligned ? launch_sparse_one<Op, LAYOUT_K, true>(a, s) : launch_sparse_one<Op, LAYOUT_K, false>(a, s);
+  return aligned ? launch_sparse_one<Op, LAYOUT_MN, true>(a, s) : launch_sparse_one<Op, LAYOUT_MN, false>(a, s);
+}
+
+hipError_t launch_sparse(int dtA, int dtB, int lb, bool aligned, const SparseArgs& a, hipStream_t s) {
+  if (dtA == DT_BF16) return launch_sparse_layouts<SpH<false>>(lb, aligned, a, s);
+  if (dtA == DT_F16) return launch_sparse_layouts<SpH<true>>(lb, aligned, a, s);
+  if (dtA == DT_I8) return launch_sparse_layouts<Sp8<0>>(lb, aligned, a, s);
+  const int fa = f8fmt(dtA), fb = f8fmt(dtB);
+  if (a.K >= FP8_NATIVE_MIN_K) {
+    if (fa == 0 && fb == 0) return launch_sparse_layouts<Sp8<1, 0, 0>>(lb, aligned, a, s);
+    if (fa == 0 && fb == 1) return launch_sparse_layouts<Sp8<1, 0, 1>>(lb, aligned, a, s);
+    if (fa == 1 && fb == 0) return launch_sparse_layouts<Sp8<1, 1, 0>>(lb, aligned, a, s);
+    return launch_sparse_layouts<Sp8<1, 1, 1>>(lb, aligned, a, s);
+  }
+  if (fa == 0 && fb == 0) return launch_sparse_layouts<Sp8W<0, 0>>(lb, aligned, a, s);
+  if (fa == 0 && fb == 1) return launch_sparse_layouts<Sp8W<0, 1>>(lb, aligned, a, s);
+  if (fa == 1 && fb == 0) return launch_sparse_layouts<Sp8W<1, 0>>(lb, aligned, a, s);
+  return launch_sparse_layouts<Sp8W<1, 1>>(lb, aligned, a, s);
 }
 
 // ------------------------------------------------------------- compressor

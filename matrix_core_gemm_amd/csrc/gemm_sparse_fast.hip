@@ -1,31 +1,36 @@
 // gemm_sparse_fast.hip -- 256 x 256 pipelined 2:4 sparse GEMM on the gfx950
 // sparse matrix cores (the fast path of gemm_sparse24 for aligned problems of
-// at least 256 x 256 with K a multiple of 16).
+// at least 256 x 256 with K * elem_bytes a multiple of 32; fp8 from K = 6144).
 //
 // The operation and the operand format are those of the general sparse kernel
 // (the 2:4 model of "RDNA4 sparse WMMA builtins", Structured sparsity (2:4
 // pattern) and Common parameters: two kept values per group of four along K,
 // ascending, and a 2-bit position per kept value).  The mapping onto CDNA4:
-//   - smfmac_f32_32x32x32_{bf16,f16}: 32 x 32 outputs and 32 dense k per
-//     instruction, twice the dense instruction's work in about the same issue
-//     time.  Measured operand layout: lane group g = lane >> 5 of the sparse
-//     operand holds the 8 kept values of dense k [16g, 16g + 16) of its row;
-//     lane group g of the dense operand holds k [8g, 8g + 8) and
-//     [16 + 8g, 24 + 8g) of its column; the lane's index register holds, in
-//     the 16-bit half that the instruction's abid selects, one 4-bit code per
-//     group of four (code n for kept values 2n and 2n + 1).  The canonical
-//     index word of a row and 32 dense k therefore serves both lane groups
-//     directly: group g uses bits [16g, 16g + 16).
+//   - 32 x 32 outputs per instruction: smfmac_f32_32x32x32_{bf16,f16} (32
+//     dense k) and smfmac_{i32_32x32x64_i8, f32_32x32x64_<fp8|bf8>_<fp8|bf8>}
+//     (64 dense k), twice the dense instruction's work in about the same issue
+//     time.  Measured operand layouts, the same in bytes for both widths: lane
+//     group g = lane >> 5 of the sparse operand holds the 16 kept bytes of
+//     dense k [16g, 16g + 16) (16-bit) or [32g, 32g + 32) (8-bit) of its row;
+//     lane group g of the dense operand holds bytes [16g, 16g + 16) and
+//     [32 + 16g, 48 + 16g) of its column's 64 bytes; the lane's index register
+//     holds one 4-bit code per group of four (code n for kept values 2n and
+//     2n + 1): for 16-bit elements in the 16-bit half that abid selects, so
+//     group g uses bits [16g, 16g + 16) of the canonical word of 32 dense k,
+//     for 8-bit elements the whole register, so group g uses the canonical
+//     word g of the instruction's 64 dense k.
 //   - 256 x 256 output tile per workgroup of 8 wavefronts, two per SIMD, each
 //     owning 128 x 64 outputs = 4 x 2 instructions of 32 x 32.
-//   - LDS: kept values in stages of 128 dense k (128 bytes = one cache line
-//     per row) together with their index words (16 bytes per row), 2 stages of
-//     36 KiB; B in stages of 64 dense k (one 128-byte line per column), 2
-//     stages of 32 KiB.  All filled by buffer_load ... lds.
+//   - LDS: kept values in stages of 128 bytes per row (one cache line: 128
+//     dense k of 16-bit or 256 of 8-bit elements) together with their index
+//     words (16 or 32 bytes per row), 2 stages; B in stages of 128 bytes per
+//     column (64 or 128 dense k), 2 stages per column half.  All filled by
+//     buffer_load ... lds.
 //   - ping-pong schedule as in the dense kernel: the two wavefronts of a SIMD
-//     alternate between multiplying one 64-k step (16 instructions) and a
-//     memory phase (fragment reads of the next step and DMA issues); wavefronts
-//     0-3 issue the B loads, wavefronts 4-7 the kept values and index words.
+//     alternate between multiplying one step (16 instructions) and a memory
+//     phase (fragment reads of the next step and DMA issues); each group of
+//     wavefronts loads the other group's half of B, half of the kept values,
+//     and group 0 the index words.
 //   - the sparse operand must be the instruction's first operand, so a lane's
 //     output registers hold four consecutive rows of one column: the epilogue
 //     stores one 4-byte value per register (each store instruction writes two
@@ -36,21 +41,57 @@
 namespace mcg {
 namespace fast {
 
-constexpr int SP_KA = 128;               // dense k per stage of kept values (128 bytes per row)
-constexpr int SP_KB = 64;                // dense k per stage of B (128 bytes per column)
 constexpr int SP_BM = 256, SP_BN = 256;
 constexpr int SP_THREADS = 512;
-constexpr int SP_A_STAGE = 32768 + 4096;  // kept values + index words of 256 rows
-constexpr int SP_BH_STAGE = 16384;        // one column half of B, 64 dense k
+constexpr int SP_BH_STAGE = 16384;  // one column half of B: 128 columns x 128 bytes
+
+// Per element width EB: a kept-value stage holds 128 bytes per row (KA dense k)
+// plus the index words of those k (IWB bytes per row); a B stage holds 128
+// bytes per column (KB dense k); one instruction takes 32 kept bytes and 64
+// B bytes of each row / column.
+template <int EB>
+struct SpGeom {
+  static constexpr int KA = 256 / EB;                       // dense k per kept-value stage
+  static constexpr int KB = 128 / EB;                       // dense k per B stage
+  static constexpr int IWB = KA / 32 * 4;                   // index bytes per row and stage
+  static constexpr int A_STAGE = SP_BM * 128 + SP_BM * IWB;  // kept values + index words
+};
 
 struct Sp32BF16 {
-  __device__ static __forceinline__ void mma(f32x16& c, const i32x4& a, const i32x8& b, int idx) {
+  static constexpr int EB = 2;
+  static constexpr bool INT_ACC = false;
+  using acc_t = f32x16;
+  __device__ static __forceinline__ void mma(acc_t& c, const i32x4& a, const i32x8& b, int idx) {
     c = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(bit_cast<bf16x8>(a), bit_cast<bf16x16>(b), c, idx, 0, 0);
   }
 };
 struct Sp32F16 {
-  __device__ static __forceinline__ void mma(f32x16& c, const i32x4& a, const i32x8& b, int idx) {
+  static constexpr int EB = 2;
+  static constexpr bool INT_ACC = false;
+  using acc_t = f32x16;
+  __device__ static __forceinline__ void mma(acc_t& c, const i32x4& a, const i32x8& b, int idx) {
     c = __builtin_amdgcn_smfmac_f32_32x32x32_f16(bit_cast<f16x8>(a), bit_cast<f16x16>(b), c, idx, 0, 0);
+  }
+};
+struct Sp32I8 {
+  static constexpr int EB = 1;
+  static constexpr bool INT_ACC = true;
+  using acc_t = i32x16;
+  __device__ static __forceinline__ void mma(acc_t& c, const i32x4& a, const i32x8& b, int idx) {
+    c = __builtin_amdgcn_smfmac_i32_32x32x64_i8(a, b, c, idx, 0, 0);
+  }
+};
+// native fp8: FA / FB = formats of A / B (0 E4M3, 1 E5M2)
+template <int FA, int FB>
+struct Sp32F8 {
+  static constexpr int EB = 1;
+  static constexpr bool INT_ACC = false;
+  using acc_t = f32x16;
+  __device__ static __forceinline__ void mma(acc_t& c, const i32x4& a, const i32x8& b, int idx) {
+    if constexpr (FA == 0 && FB == 0) c = __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(a, b, c, idx, 0, 0);
+    else if constexpr (FA == 0 && FB == 1) c = __builtin_amdgcn_smfmac_f32_32x32x64_fp8_bf8(a, b, c, idx, 0, 0);
+    else if constexpr (FA == 1 && FB == 0) c = __builtin_amdgcn_smfmac_f32_32x32x64_bf8_fp8(a, b, c, idx, 0, 0);
+    else c = __builtin_amdgcn_smfmac_f32_32x32x64_bf8_bf8(a, b, c, idx, 0, 0);
   }
 };
 
@@ -62,10 +103,11 @@ struct Sp32F16 {
 // pattern as LineLoader (whole 128-byte lines for K-contiguous rows); the
 // second 64 columns are reached by an extra uniform jump (K-contiguous: for
 // instructions 2 and 3) or a per-lane offset (MN-contiguous: chunks 8..15).
-template <int LB>
+template <int EB, int LB>
 struct BHalfLoader {
-  using G = Geom<2, LB, 128, 128>;
+  using G = Geom<EB, LB, 128, 128>;
   static constexpr int INSTR = G::CHUNKS / (64 * NW);
+  static constexpr int EPC = 16 / EB;  // elements per 16-byte chunk
   static_assert(INSTR == 4, "4 loads per wave and half stage");
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t voff, istride, jump, kstride;
@@ -75,23 +117,25 @@ struct BHalfLoader {
                                        int wave, int lane) {
     const int q = wave * 64 + lane;
     const int r = q / G::CPR, pc = q % G::CPR;
-    const int lc = pc ^ swz<2, LB, G::CPR>(r);
+    const int lc = pc ^ swz<EB, LB, G::CPR>(r);
     const int64_t col0 = n0 + 64 * c;
     if constexpr (LB == LAYOUT_K) {
       const int64_t rows = min(N - n0, (int64_t)256) - 64 * c;  // tile columns from col0 to the end of N
-      rsrc = make_rsrc(B + col0 * ldb * 2, (uint32_t)(rows > 0 ? rows * ldb * 2 : 0));
-      voff = (uint32_t)(r * ldb * 2 + lc * 16);
-      istride = __builtin_amdgcn_readfirstlane((uint32_t)(32 * ldb * 2));
-      jump = __builtin_amdgcn_readfirstlane((uint32_t)(64 * ldb * 2));
+      rsrc = make_rsrc(B + col0 * ldb * EB, (uint32_t)(rows > 0 ? rows * ldb * EB : 0));
+      voff = (uint32_t)(r * ldb * EB + lc * 16);
+      istride = __builtin_amdgcn_readfirstlane((uint32_t)(32 * ldb * EB));
+      jump = __builtin_amdgcn_readfirstlane((uint32_t)(64 * ldb * EB));
       kstride = 128;
-      const int64_t left = K - (int64_t)lc * 8;
-      klim = left <= 0 ? 0 : (int)((left + 63) / 64);
+      const int64_t left = K - (int64_t)lc * EPC;
+      klim = left <= 0 ? 0 : (int)((left + SpGeom<EB>::KB - 1) / SpGeom<EB>::KB);
     } else {
-      rsrc = make_rsrc(B + col0 * 2, (uint32_t)((K * ldb - col0) * 2));
-      voff = (uint32_t)(r * ldb * 2 + lc * 16 + (lc >= 8 ? 128 : 0));
-      istride = __builtin_amdgcn_readfirstlane((uint32_t)(16 * ldb * 2));
+      // an LDS row holds columns [0, 64) then [128, 192) of the half: chunks
+      // past the first 64 columns jump over the other group's 64
+      rsrc = make_rsrc(B + col0 * EB, (uint32_t)((K * ldb - col0) * EB));
+      voff = (uint32_t)(r * ldb * EB + lc * 16 + (lc >= 4 * EB ? 64 * EB : 0));
+      istride = __builtin_amdgcn_readfirstlane((uint32_t)(NW * 64 / G::CPR * ldb * EB));  // k rows per instruction
       jump = 0;
-      kstride = __builtin_amdgcn_readfirstlane((uint32_t)(64 * ldb * 2));
+      kstride = __builtin_amdgcn_readfirstlane((uint32_t)(SpGeom<EB>::KB * ldb * EB));
       klim = 0x7fffffff;  // rows past K lie outside the buffer window
     }
   }
@@ -110,13 +154,20 @@ template <class Op, int LB>
 __global__ __launch_bounds__(SP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_sparse_fast_kernel(SparseArgs p) {
   constexpr int WTM = 4, WTN = 2;
-  using RA = Reader<2, LAYOUT_K, SP_BM, 128>;
-  using RB = Reader<2, LB, 128, 128>;
-  using LdA = LineLoader<2, LAYOUT_K, SP_BM, 128>;
-  static_assert(Geom<2, LAYOUT_K, SP_BM, 128>::BYTES == 32768 && Geom<2, LB, 128, 128>::BYTES == SP_BH_STAGE, "");
+  constexpr int EB = Op::EB;
+  using SG = SpGeom<EB>;
+  constexpr int A_STAGE = SG::A_STAGE, IWB = SG::IWB;
+  constexpr int WPR = IWB / 4;                   // index words per row and stage
+  constexpr int II = SP_BM * WPR / (64 * NW);    // 4-byte index loads per wave and stage
+  using RA = Reader<EB, LAYOUT_K, SP_BM, 128>;
+  using RB = Reader<EB, LB, 128, 128>;
+  using LdA = LineLoader<EB, LAYOUT_K, SP_BM, 128>;
+  using acc_t = typename Op::acc_t;
+  static_assert(Geom<EB, LAYOUT_K, SP_BM, 128>::BYTES == 32768 && Geom<EB, LB, 128, 128>::BYTES == SP_BH_STAGE, "");
   static_assert(LdA::INSTR == 8, "8 loads per wave and kept-value stage");
+  static_assert(II == 4 || II == 8, "index loads per stage");
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * SP_A_STAGE + 4 * SP_BH_STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * A_STAGE + 4 * SP_BH_STAGE];
   lds_char* smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -132,58 +183,67 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   const int64_t rows = min(p.M - m0, (int64_t)SP_BM);
   const int64_t Kc = p.K / 2;  // kept values per row
   const int nwords = (int)((p.K + 31) / 32);
-  const int nT = (int)((p.K + SP_KA - 1) / SP_KA);  // kept-value stages; 2 steps of 64 dense k each
+  const int nT = (int)((p.K + SG::KA - 1) / SG::KA);  // kept-value stages; 2 steps of KB dense k each
 
-  auto stA = [&](int T) { return smem + (T & 1) * SP_A_STAGE; };
-  auto stI = [&](int T) { return smem + (T & 1) * SP_A_STAGE + 32768; };
+  auto stA = [&](int T) { return smem + (T & 1) * A_STAGE; };
+  auto stI = [&](int T) { return smem + (T & 1) * A_STAGE + 32768; };
   // B half c of step u
-  auto stBh = [&](int c, int u) { return smem + 2 * SP_A_STAGE + (2 * c + (u & 1)) * SP_BH_STAGE; };
+  auto stBh = [&](int c, int u) { return smem + 2 * A_STAGE + (2 * c + (u & 1)) * SP_BH_STAGE; };
 
   // every wave loads half of the kept values (instructions 4 grp .. 4 grp + 3)
   // and the other group's half of B; group 0 also loads the index words
   LdA la;
-  la.init(p.Ac + m0 * p.lda_c * 2, (uint32_t)(rows * p.lda_c * 2), p.lda_c, Kc, q, lane);
-  BHalfLoader<LB> lb;
+  la.init(p.Ac + m0 * p.lda_c * EB, (uint32_t)(rows * p.lda_c * EB), p.lda_c, Kc, q, lane);
+  BHalfLoader<EB, LB> lb;
   lb.init(p.B, n0, 1 - grp, p.N, p.K, p.ldb, q, lane);
   __amdgpu_buffer_rsrc_t rs_idx;
-  uint32_t off_idx[4];
-  int word_idx[4];
+  uint32_t off_idx[II];
+  int word_idx[II];
   rs_idx = make_rsrc((const char*)(p.idx + m0 * p.ld_idx), (uint32_t)(rows * p.ld_idx * 4));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {  // 4-byte loads: lane -> (row, word) of a 16-byte index row
+  for (int i = 0; i < II; ++i) {  // 4-byte loads: lane -> (row, word) of an IWB-byte index row
     const int e = i * 256 + q * 64 + lane;
-    word_idx[i] = e & 3;
-    off_idx[i] = (uint32_t)((e >> 2) * p.ld_idx * 4 + (e & 3) * 4);
+    word_idx[i] = e % WPR;
+    off_idx[i] = (uint32_t)((e / WPR) * p.ld_idx * 4 + (e % WPR) * 4);
   }
   auto issueA = [&](int T) { la.issue(stA(T), T, 4 * grp, 4, q); };
   auto issueI = [&](int T) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t o = T * 4 + word_idx[i] < nwords ? off_idx[i] + (uint32_t)T * 16u : BUF_OOB;
+    for (int i = 0; i < II; ++i) {
+      const uint32_t o = T * WPR + word_idx[i] < nwords ? off_idx[i] + (uint32_t)(T * IWB) : BUF_OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs_idx, (__attribute__((address_space(3))) void*)(stI(T) + (i * 256 + q * 64) * 4), 4, o, 0, 0, 0);
     }
   };
   auto issueB = [&](int u) { lb.issue(stBh(1 - grp, u), u, q); };  // the other group's half
 
-  f32x16 acc[WTM][WTN];
+  acc_t acc[WTM][WTN];
 #pragma unroll
   for (int i = 0; i < WTM; ++i)
 #pragma unroll
-    for (int j = 0; j < WTN; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < WTN; ++j) acc[i][j] = acc_t{};
 
   i32x4 fa[2][WTM];
   i32x8 fb[2][WTN];
   int fi[2][WTM];
-  // fragments of 64-k step u = 2T + h: instruction s covers dense k [64h + 32s, +32) of stage T
+  // fragments of step u = 2T + h (KB dense k): instruction s covers kept bytes
+  // [64h + 32s, +32) of stage T and B bytes [64s, +64) of step u.  Index codes:
+  // 16-bit elements use half g of word 2h + s (32 dense k per instruction),
+  // 8-bit elements word 4h + 2s + g (64 dense k per instruction).
   auto read_frags = [&](int u) {
     const int T = u >> 1, h = u & 1;
 #pragma unroll
     for (int i = 0; i < WTM; ++i) {
       const int row = rbA + 32 * i + (lane & 31);
-      const i32x2 w = *(const __attribute__((address_space(3))) i32x2*)(stI(T) + row * 16 + 8 * h);
-      fi[0][i] = (int)((uint32_t)w.x >> (16 * g));
-      fi[1][i] = (int)((uint32_t)w.y >> (16 * g));
+      if constexpr (EB == 2) {
+        const i32x2 w = *(const __attribute__((address_space(3))) i32x2*)(stI(T) + row * IWB + 8 * h);
+        fi[0][i] = (int)((uint32_t)w.x >> (16 * g));
+        fi[1][i] = (int)((uint32_t)w.y >> (16 * g));
+      } else {
+        const i32x4 w = *(const __attribute__((address_space(3))) i32x4*)(stI(T) + row * IWB + 16 * h);
+        fi[0][i] = g ? w.y : w.x;
+        fi[1][i] = g ? w.w : w.z;
+      }
 #pragma unroll
       for (int s = 0; s < 2; ++s) fa[s][i] = RA::read16k(stA(T), rbA + 32 * i, 64 * h + 32 * s + 16 * g, lane);
     }
@@ -237,7 +297,7 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
       issueB(u + 1);
       issueA(T + 1);
       issueI(T + 1);
-      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");  // group 1's half of B(u)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 + II) : "memory");  // group 1's half of B(u)
       barrier_lds();
       __builtin_amdgcn_sched_barrier(0);
       multiply();  // slot 4T
@@ -292,7 +352,13 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
       for (int r = 0; r < 16; ++r) {
         const int64_t m = m0 + rbA + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
         if (!interior && (m >= p.M || n >= p.N)) continue;
-        combine_store(p.C, p.D, m * p.ldc + n, acc[i][j][r], p.alpha, p.beta, p.use_c, p.out);
+        const int64_t off = m * p.ldc + n;
+        if constexpr (Op::INT_ACC) {
+          const uint32_t c = p.use_c ? (uint32_t)((const int*)p.C)[off] : 0u;
+          ((int*)p.D)[off] = (int)((uint32_t)p.alpha_i * (uint32_t)acc[i][j][r] + (uint32_t)p.beta_i * c);
+        } else {
+          combine_store(p.C, p.D, off, acc[i][j][r], p.alpha, p.beta, p.use_c, p.out);
+        }
       }
     }
 }
@@ -310,32 +376,45 @@ static hipError_t launch_sparse_fast_one(const SparseArgs& a0, hipStream_t s) {
 
 }  // namespace fast
 
-bool sparse_fast_ok(int layoutB, const SparseArgs& a) {
-  // 16-byte chunks of kept values (8 values = 16 dense k) and of B (8 k) never
-  // straddle the end of K when K % 16 == 0; index words are fetched 4 bytes at a time
+bool sparse_fast_ok(int dtA, int layoutB, const SparseArgs& a) {
+  const int64_t eb = (dtA == DT_BF16 || dtA == DT_F16) ? 2 : 1;
+  // 16-byte chunks of kept values (16 / eb values = 32 / eb dense k) and of B
+  // never straddle the end of K when K * eb % 32 == 0; index words are fetched
+  // 4 bytes at a time.  Native fp8 only from the accuracy threshold on (below
+  // it fp8 is widened to bf16 by the general kernel).
   auto al = [](const void* q, int64_t n) { return ((uintptr_t)q % (uintptr_t)n) == 0; };
-  const bool aligned = al(a.Ac, 16) && al(a.B, 16) && al(a.idx, 4) && (a.lda_c * 2) % 16 == 0 &&
-                       (a.ldb * 2) % 16 == 0;
-  if (!aligned || a.K == 0 || a.K % 16 != 0) return false;
+  const bool aligned = al(a.Ac, 16) && al(a.B, 16) && al(a.idx, 4) && (a.lda_c * eb) % 16 == 0 &&
+                       (a.ldb * eb) % 16 == 0;
+  if (!aligned || a.K == 0 || (a.K * eb) % 32 != 0) return false;
+  if ((dtA == DT_E4M3 || dtA == DT_E5M2) && a.K < FP8_NATIVE_MIN_K) return false;
   if (a.M < fast::SP_BM || a.N < fast::SP_BN) return false;
   // every buffer window (and offset into it) must stay below 2 GiB;
-  // MN-contiguous B offsets advance by whole stages, up to NST stages past K
+  // MN-contiguous B offsets advance by whole stages, up to 4 stages past K
   const int64_t lim = (int64_t)1 << 31;
-  const int64_t kpad = 4 * (int64_t)fast::SP_KB;
-  const int64_t wa = (int64_t)fast::SP_BM * a.lda_c * 2;
+  const int64_t kpad = 4 * 128 / eb;
+  const int64_t wa = (int64_t)fast::SP_BM * a.lda_c * eb;
   const int64_t wi = (int64_t)fast::SP_BM * a.ld_idx * 4;
-  const int64_t wb = layoutB == LAYOUT_K ? (int64_t)fast::SP_BN * a.ldb * 2 : (a.K + kpad) * a.ldb * 2;
+  const int64_t wb = layoutB == LAYOUT_K ? (int64_t)fast::SP_BN * a.ldb * eb : (a.K + kpad) * a.ldb * eb;
   const int64_t tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
   return wa < lim && wi < lim && wb < lim && tiles <= 0x7fffffff;
 }
 
-hipError_t launch_sparse_fast(int dt, int layoutB, const SparseArgs& a, hipStream_t s) {
+template <class Op>
+static hipError_t launch_sparse_fast_layouts(int layoutB, const SparseArgs& a, hipStream_t s) {
+  return layoutB == LAYOUT_K ? fast::launch_sparse_fast_one<Op, LAYOUT_K>(a, s)
+                             : fast::launch_sparse_fast_one<Op, LAYOUT_MN>(a, s);
+}
+
+hipError_t launch_sparse_fast(int dtA, int dtB, int layoutB, const SparseArgs& a, hipStream_t s) {
   using namespace fast;
-  if (dt == DT_BF16)
-    return layoutB == LAYOUT_K ? launch_sparse_fast_one<Sp32BF16, LAYOUT_K>(a, s)
-                               : launch_sparse_fast_one<Sp32BF16, LAYOUT_MN>(a, s);
-  return layoutB == LAYOUT_K ? launch_sparse_fast_one<Sp32F16, LAYOUT_K>(a, s)
-                             : launch_sparse_fast_one<Sp32F16, LAYOUT_MN>(a, s);
+  if (dtA == DT_BF16) return launch_sparse_fast_layouts<Sp32BF16>(layoutB, a, s);
+  if (dtA == DT_F16) return launch_sparse_fast_layouts<Sp32F16>(layoutB, a, s);
+  if (dtA == DT_I8) return launch_sparse_fast_layouts<Sp32I8>(layoutB, a, s);
+  const int fa = f8fmt(dtA), fb = f8fmt(dtB);
+  if (fa == 0 && fb == 0) return launch_sparse_fast_layouts<Sp32F8<0, 0>>(layoutB, a, s);
+  if (fa == 0 && fb == 1) return launch_sparse_fast_layouts<Sp32F8<0, 1>>(layoutB, a, s);
+  if (fa == 1 && fb == 0) return launch_sparse_fast_layouts<Sp32F8<1, 0>>(layoutB, a, s);
+  return launch_sparse_fast_layouts<Sp32F8<1, 1>>(layoutB, a, s);
 }
 
 }  // namespace mcg

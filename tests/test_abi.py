@@ -117,7 +117,15 @@ def test_entry_points_reject_before_touching_the_device():
 @pytest.mark.parametrize("kw,status", [
     ({}, 0),
     ({"K": 10}, 2),
-    ({"dtypeA": "i8", "dtypeB": "i8"}, 4),
+    ({"dtypeA": "i8", "dtypeB": "i8"}, 4),                    # int8 needs an int32 D
+    ({"dtypeA": "i8", "dtypeB": "i8", "dtypeD": "i32"}, 0),
+    ({"dtypeA": "i8", "dtypeB": "i8", "dtypeD": "i32", "alpha": 0.5}, 10),
+    ({"dtypeA": "i8", "dtypeB": "bf16", "dtypeD": "i32"}, 4),
+    ({"dtypeA": "e4m3", "dtypeB": "e5m2"}, 0),
+    ({"dtypeA": "e5m2", "dtypeB": "e4m3", "dtypeD": "bf16"}, 0),
+    ({"dtypeA": "e4m3", "dtypeB": "i8"}, 4),
+    ({"dtypeA": "e4m3", "dtypeB": "e4m3", "dtypeD": "i32"}, 4),
+    ({"dtypeA": "e4m3", "dtypeB": "e4m3", "A_compressed": FAKE + 1}, 0),   # 1-byte elements
     ({"dtypeD": "i32"}, 4),
     ({"lda_c": 31}, 3),
     ({"ld_idx": 1}, 3),

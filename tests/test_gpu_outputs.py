@@ -94,7 +94,7 @@ def test_sparse_16bit_output(out, dt, case):
     v, i, _ = oracle.compress24(dt, A)
     nw = (K + 31) // 32
     dv, di, dbb = dev(v), dev(i.view(np.int32)), dev(B.codes)
-    assert mcg.sparse24_path("k_contig", M, N, K, dv, K // 2, di, nw, dbb, B.ld) == path
+    assert mcg.sparse24_path(dt, "k_contig", M, N, K, dv, K // 2, di, nw, dbb, B.ld) == path
     C = c_codes(M, N, out, 36)
     D = torch.full((M, N), NAN_CODE[out], dtype=torch.int32).to(torch.int16).to("cuda")
     mcg.gemm_sparse24(dt, dt, "k_contig", M, N, K, dv, K // 2, di, nw, dbb, B.ld,

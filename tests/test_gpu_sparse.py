@@ -120,7 +120,7 @@ def test_sparse_256_tile_path(dt, layB, shape, pads):
     ip[:, :nw] = i
     D = torch.full((M, N), float("nan"), device="cuda")
     dv, di, dbb = dev(vp), dev(ip.view(np.int32)), dev(B.codes)
-    assert mcg.sparse24_path(layB, M, N, K, dv, lda_c, di, ld_idx, dbb, B.ld) == 1
+    assert mcg.sparse24_path(dt, layB, M, N, K, dv, lda_c, di, ld_idx, dbb, B.ld) == 1
     mcg.gemm_sparse24(dt, dt, layB, M, N, K, dv, lda_c, di, ld_idx, dbb, B.ld, dev(C), D, N, "f32",
                       1.5, -0.5)
     torch.cuda.synchronize()
@@ -182,3 +182,118 @@ def test_full_size_sparse_configuration():
                                rows=rows, cols=cols)
     r = compare("bf16", d[rows, cols], ref, s, K, what=wl.name)
     say(f"  sampled {r['n']} outputs ok; max |delta|/bound = {r['max_ratio']}")
+
+
+# ------------------------------------------------------------ 8-bit sparse (int8, fp8)
+
+SP8 = [("i8", "i8"), ("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m2", "e5m2")]
+
+
+def sparse8_case(mcg, dtA, dtB, layB, M, N, K, path, pads=(0, 0, 0), seed=0, alpha=None, beta=1.0,
+                 sample=None, A=None, B=None):
+    """Compress A on the device into padded buffers, run gemm_sparse24, compare
+    with the oracle (int8 bit-exact, fp8 within the bound; fp8 scales in alpha)."""
+    i8 = dtA == "i8"
+    pad_v, pad_i, pad_b = pads
+    if A is None:
+        A = W.sparse24_dense(dtA, M, K, dist="int8" if i8 else "normal", seed=70 + seed)
+    if B is None:
+        B = W.operand("B", dtB, K, N, "int8" if i8 else "normal", layB, seed=71 + seed,
+                      ld=(K if layB == "k_contig" else N) + pad_b, fp8_scaled=not i8)
+    if alpha is None:
+        alpha = 3 if i8 else 1.25 * B.scale
+    C = None if beta == 0 else W.c_matrix(M, N, "int20" if i8 else "normal", seed=72 + seed)
+    nw = (K + 31) // 32
+    lda_c, ld_idx = K // 2 + pad_v, nw + pad_i
+    vals = torch.full((M, lda_c), 0x5A, dtype=torch.uint8, device="cuda")
+    idx = torch.full((M, ld_idx), -1, dtype=torch.int32, device="cuda")
+    viol = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    mcg.compress24(dtA, M, K, dev(A), K, vals, lda_c, idx, ld_idx, viol)
+    dbb = dev(B.codes)
+    assert mcg.sparse24_path(dtA, layB, M, N, K, vals, lda_c, idx, ld_idx, dbb, B.ld) == path
+    D = torch.full((M, N), -0x5A5A5A5A if i8 else float("nan"), dtype=torch.int32 if i8 else torch.float32,
+                   device="cuda")
+    mcg.gemm_sparse24(dtA, dtB, layB, M, N, K, vals, lda_c, idx, ld_idx, dbb, B.ld,
+                      None if C is None else dev(C), D, N, "i32" if i8 else "f32", alpha, beta)
+    torch.cuda.synchronize()
+    assert int(viol.item()) == 0
+    v, ix, _ = oracle.compress24(dtA, A)
+    rows, cols = sample if sample is not None else (None, None)
+    ref, s = oracle.gemm_sparse24(dtA, dtB, layB, M, N, K, v, ix, B.codes, B.ld, C, N, alpha, beta,
+                                  rows=rows, cols=cols)
+    d = D.cpu().numpy()
+    got = d if rows is None else d[rows, cols]
+    c = None if C is None else (C if rows is None else C[rows, cols])
+    return compare(dtA, got, ref, s, K, alpha, beta=beta, c=c,
+                   what=f"sparse {dtA}x{dtB} {layB} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("dtA,dtB", SP8)
+@pytest.mark.parametrize("layB", ["k_contig", "mn_contig"])
+@pytest.mark.parametrize("shape", [(130, 140, 1000), (300, 200, 388), (17, 33, 4), (64, 96, 6176)])
+def test_sparse8_general_kernel(dtA, dtB, layB, shape):
+    """General kernel: ragged tiles, K ending inside a tile; fp8 widened to
+    bfloat16 below K = 6144 and native above."""
+    mcg = need_gpu()
+    M, N, K = shape
+    say(f"sparse8 general {dtA}x{dtB} {layB} {shape}")
+    sparse8_case(mcg, dtA, dtB, layB, M, N, K, 0, seed=1)
+
+
+@pytest.mark.parametrize("dtA,dtB", SP8)
+@pytest.mark.parametrize("layB", ["k_contig", "mn_contig"])
+@pytest.mark.parametrize("shape,pads", [
+    ((512, 512, 6144), (0, 0, 0)),       # whole tiles
+    ((300, 528, 6176), (16, 3, 32)),     # ragged M and N, last stage partial, padded ld's
+    ((257, 304, 6400), (32, 1, 16)),     # one row past a tile
+])
+def test_sparse8_256_tile_path(dtA, dtB, layB, shape, pads):
+    """The 256 x 256 sparse kernel with 8-bit operands (native fp8 from K = 6144)."""
+    mcg = need_gpu()
+    M, N, K = shape
+    say(f"sparse8 256-tile {dtA}x{dtB} {layB} {shape} pads {pads}")
+    sparse8_case(mcg, dtA, dtB, layB, M, N, K, 1, pads=pads, seed=2)
+
+
+@pytest.mark.parametrize("layB", ["k_contig", "mn_contig"])
+def test_sparse_int8_256_tile_short_k(layB):
+    """int8 takes the 256 x 256 kernel at any K that is a multiple of 32."""
+    mcg = need_gpu()
+    sparse8_case(mcg, "i8", "i8", layB, 512, 288, 1056, 1, alpha=-7, beta=2, seed=3)
+    sparse8_case(mcg, "i8", "i8", layB, 256, 256, 32, 1, alpha=1, beta=0, seed=4)
+
+
+@pytest.mark.parametrize("dtA,dtB", [("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")])
+@pytest.mark.parametrize("K", [256, 2048, 6144])
+def test_sparse_fp8_wide_dynamic_range_meets_bound(dtA, dtB, K):
+    """Kept values of magnitude 16 at the first kept position of every other
+    group and 1/8 elsewhere (14 binades between products): the regime where the
+    native fp8 instruction drops small products.  Widened below K = 6144,
+    native from there; the bound must hold either way."""
+    mcg = need_gpu()
+    M, N = 256, 256
+    rng = np.random.default_rng(5)
+    g = np.arange(K) // 4
+    vals = np.where((np.arange(K) % 4 == 0) & (g % 2 == 0), 16.0, 0.125)
+    keep = (np.arange(K) % 4) < 2
+    Av = np.where(keep, vals, 0.0)[None, :] * rng.choice([-1.0, 1.0], (M, K))
+    Bv = np.where(np.arange(K) % 8 == 0, 16.0, 0.125)[:, None] * rng.choice([-1.0, 1.0], (K, N))
+    Aq, _ = W.quantize(torch.from_numpy(Av).float(), dtA)
+    A = W.codes_of(Aq, dtA)
+    Bq, _ = W.quantize(torch.from_numpy(Bv).float(), dtB)
+    Bs, ldb = W.store(Bq, "B", "k_contig")
+    B = W.Operand(dtB, "k_contig", W.codes_of(Bs, dtB), ldb, 1.0)
+    r = sparse8_case(mcg, dtA, dtB, "k_contig", M, N, K, 1 if K >= 6144 else 0, alpha=1.0, beta=0.0,
+                     A=A, B=B)
+    say(f"sparse fp8 {dtA}x{dtB} K={K}: max |delta|/bound = {r['max_ratio']:.3f}")
+
+
+@pytest.mark.parametrize("dtA,dtB", [("i8", "i8"), ("e4m3", "e4m3")])
+def test_full_size_sparse8(dtA, dtB):
+    """8192^3 in the benchmark's launch configuration (C absent); sampled outputs."""
+    mcg = need_gpu()
+    M = N = K = 8192
+    rows, cols = W.sample_coords(M, N, n_random=4096, full_rows=(0, M - 1), full_cols=(N // 3,))
+    r = sparse8_case(mcg, dtA, dtB, "k_contig", M, N, K, 1, beta=0.0, alpha=1 if dtA == "i8" else None,
+                     sample=(rows, cols), seed=6)
+    say(f"  full-size sparse {dtA}: sampled {r['n']} outputs ok; max ratio {r.get('max_ratio', 0)}")
