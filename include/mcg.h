@@ -229,6 +229,30 @@ int mcg_dense_splits(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N,
 int mcg_sparse24_path(int dtypeA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A_compressed,
                       int64_t lda_c, const uint32_t* A_index, int64_t ld_idx, const void* B, int64_t ldb);
 
+/*
+ * mcg_mfma_eval -- one gfx950 matrix-core instruction per test vector, for
+ * numerical characterisation ("Accurate Models of AMD Matrix Cores", Section 2,
+ * Eq. (1): d = sum_l a_l b_l + c for one output element; Section 3: targeted
+ * and randomised test vectors).
+ *
+ * dtype  : MCG_BF16, MCG_F16, MCG_FP8_E4M3 or MCG_FP8_E5M2 (a and b alike).
+ * shape  : 16 (mfma_f32_16x16x32_{bf16,f16}, mfma_scale_f32_16x16x128_f8f6f4)
+ *          or 32 (mfma_f32_32x32x16_{bf16,f16}, mfma_scale_f32_32x32x64_f8f6f4).
+ * a, b   : DEVICE arrays of n * k element codes, k = mcg_mfma_eval_k(dtype,
+ *          shape); test vector t is a[t*k .. t*k + k) and b[t*k .. t*k + k).
+ *          Element l goes to operand slot l: lane group g holds slots
+ *          [g*E, (g+1)*E) in register order (E = 8 for 16-bit, 32 for fp8
+ *          elements per lane).
+ * c, d   : DEVICE arrays of n floats: c[t] is accumulator element (0, 0) of
+ *          test t, d[t] receives result element (0, 0).  All other operand
+ *          elements are zero.
+ * Returns an mcg_status; asynchronous on stream.
+ */
+int mcg_mfma_eval(int dtype, int shape, int64_t n, const void* a, const void* b, const float* c, float* d,
+                  void* stream);
+/* Elements per test vector for mcg_mfma_eval (0 if unsupported). */
+int mcg_mfma_eval_k(int dtype, int shape);
+
 /* Human-readable name of an mcg_status value (static storage). */
 const char* mcg_status_string(int status);
 

@@ -31,7 +31,7 @@ STATUS = {0: "MCG_SUCCESS", 1: "MCG_ERR_NULL_POINTER", 2: "MCG_ERR_INVALID_SIZE"
 # Every symbol include/mcg.h declares.
 EXPORTS = ("gemm_dense", "gemm_sparse24", "compress24", "compress24_host", "mcg_status_string",
            "mcg_version", "mcg_validate_dense", "mcg_validate_sparse24", "mcg_validate_compress24",
-           "mcg_dense_path", "mcg_dense_splits", "mcg_sparse24_path")
+           "mcg_dense_path", "mcg_dense_splits", "mcg_sparse24_path", "mcg_mfma_eval", "mcg_mfma_eval_k")
 
 
 class MCGError(RuntimeError):
@@ -65,6 +65,8 @@ _lib.mcg_dense_path.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _
 _lib.mcg_dense_splits.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp,
                                   _i32, ctypes.c_double]
 _lib.mcg_sparse24_path.argtypes = [_i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
+_lib.mcg_mfma_eval.argtypes = [_i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp]
+_lib.mcg_mfma_eval_k.argtypes = [_i32, _i32]
 
 
 def lib():
@@ -183,3 +185,15 @@ def status_string(status: int) -> str:
 
 def version() -> int:
     return _lib.mcg_version()
+
+
+def mfma_eval_k(dtype, shape) -> int:
+    """Elements per test vector of mfma_eval (0 if unsupported)."""
+    return _lib.mcg_mfma_eval_k(_dt(dtype), int(shape))
+
+
+def mfma_eval(dtype, shape, n, a, b, c, d, stream=None) -> None:
+    """One matrix-core instruction per test vector: d[t] = element (0, 0) of the
+    instruction fed with a[t*k:], b[t*k:] and c[t] (see mcg.h)."""
+    _check("mcg_mfma_eval", _lib.mcg_mfma_eval(_dt(dtype), int(shape), n, _ptr(a), _ptr(b), _ptr(c), _ptr(d),
+                                               _stream(stream)))

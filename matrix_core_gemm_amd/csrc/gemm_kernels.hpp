@@ -90,5 +90,8 @@ hipError_t launch_sparse(int dtA, int dtB, int layoutB, bool aligned, const Spar
 bool sparse_fast_ok(int dtA, int layoutB, const SparseArgs& a);
 hipError_t launch_sparse_fast(int dtA, int dtB, int layoutB, const SparseArgs& a, hipStream_t s);
 hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s);
+int mfma_eval_k(int dt, int shape);
+hipError_t launch_mfma_eval(int dt, int shape, const void* a, const void* b, const float* c, float* d,
+                            int64_t n, hipStream_t s);
 
 }  // namespace mcg
