@@ -12,12 +12,17 @@ passages it follows, is stated in ``oracle.c``:
   ascending k, rounded once to binary32 ("Accurate Models of AMD Matrix Cores",
   Section 2, Eq. (1)).
 * ``gemm_i8``      -- exact int8 x int8 -> int32 (wraps mod 2^32).
+* ``gemm_f64``     -- D = alpha*(A*B) + beta*C for binary64 operands: exact
+  products summed in binary128 in ascending k, rounded once to binary64 (the
+  FP64-accumulate instructions of "CDNA3 dense MFMA builtins").
 * ``compress24`` / ``decompress24`` -- the 2:4 compressed form ("RDNA4 sparse
   WMMA builtins", Structured sparsity (2:4 pattern); Common parameters, index).
 * ``gemm_sparse24`` -- decompress, then ``gemm_float``.
 * ``float_bound`` / ``check_float`` / ``check_exact`` -- the acceptance test:
   |D_gpu - D_ref| <= 4*2^-24*(K+2)*|alpha*sA*sB|*S + 2^-24*|D_ref| (+ 2^-24*|beta*c|
   when beta is not 0 or +-1), S = sum_k |a_ik*b_kj|; integers must be equal.
+* ``f64_bound`` / ``check_f64`` -- the same acceptance test for binary64
+  results with u = 2^-53.
 
 Every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_*.py`` against closed forms, brute force, library witnesses
@@ -45,6 +50,7 @@ OUT_SUBNORMAL_HALF = {"f32": 2.0 ** -150, "bf16": 2.0 ** -134, "f16": 2.0 ** -25
 CODE_NP = {"bf16": np.uint16, "f16": np.uint16, "i8": np.int8, "e4m3": np.uint8, "e5m2": np.uint8}
 
 U = 2.0 ** -24  # unit roundoff of binary32
+U64 = 2.0 ** -53  # unit roundoff of binary64
 
 _lib = None
 
@@ -76,6 +82,10 @@ def lib():
                                         i64, i64, i64, vp, vp, vp]
         L.orc_gemm_i8_full.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64,
                                        i64, i64, vp]
+        L.orc_gemm_f64_elems.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64,
+                                         dbl, dbl, i64, vp, vp, vp, vp]
+        L.orc_gemm_f64_full.argtypes = [i32, i32, i64, i64, i64, vp, i64, vp, i64, vp, i64,
+                                        dbl, dbl, vp, vp]
         L.orc_compress24.argtypes = [i32, i64, i64, vp, i64, vp, i64, vp, i64]
         L.orc_compress24.restype = i64
         L.orc_decompress24.argtypes = [i32, i64, i64, vp, i64, vp, i64, vp, i64]
@@ -186,6 +196,34 @@ def gemm_i8(layA, layB, M, N, K, A, lda, B, ldb, C=None, ldc=None, alpha=1, beta
     return d
 
 
+def gemm_f64(layA, layB, M, N, K, A, lda, B, ldb, C=None, ldc=None, alpha=1.0, beta=0.0,
+             rows=None, cols=None):
+    """Reference for binary64 operands: returns (d_ref float64, abs_sum
+    float64), full M x N arrays or, with rows/cols, 1-D arrays."""
+    A = _flat(A, np.float64)
+    B = _flat(B, np.float64)
+    C = _flat(C, np.float64) if beta != 0.0 and C is not None else None
+    ldc = N if ldc is None else ldc
+    L = lib()
+    if rows is None:
+        d = np.empty((M, N), np.float64)
+        s = np.empty((M, N), np.float64)
+        rc = L.orc_gemm_f64_full(LAYOUTS[layA], LAYOUTS[layB], M, N, K, _ptr(A), lda, _ptr(B), ldb,
+                                 _ptr(C), ldc, float(alpha), float(beta), _ptr(d), _ptr(s))
+    else:
+        rows = _flat(np.asarray(rows, np.int64), np.int64)
+        cols = _flat(np.asarray(cols, np.int64), np.int64)
+        assert rows.shape == cols.shape
+        d = np.empty(rows.shape, np.float64)
+        s = np.empty(rows.shape, np.float64)
+        rc = L.orc_gemm_f64_elems(LAYOUTS[layA], LAYOUTS[layB], M, N, K, _ptr(A), lda, _ptr(B), ldb,
+                                  _ptr(C), ldc, float(alpha), float(beta), rows.size, _ptr(rows),
+                                  _ptr(cols), _ptr(d), _ptr(s))
+    if rc != 0:
+        raise ValueError(f"oracle binary64 GEMM rejected its arguments ({rc})")
+    return d, s
+
+
 def compress24(dtype, A):
     """2:4-compress a row-major M x K code array.  Returns (vals M x K/2,
     idx M x ceil(K/32) uint32, number of groups with more than two non-zeros)."""
@@ -246,13 +284,33 @@ def float_bound(d_ref, abs_sum, K, alpha=1.0, sA=1.0, sB=1.0, beta=0.0, c=None, 
     return bound
 
 
+def f64_bound(d_ref, abs_sum, K, alpha=1.0, beta=0.0, c=None):
+    """Per-element acceptance bound for binary64 results: the binary32 bound's
+    form with u = 2^-53, i.e. 4u(K+2)|alpha| S + u|D_ref| (+ u|beta c| when
+    beta is not 0 or +-1)."""
+    d = np.abs(np.asarray(d_ref, np.float64))
+    bound = (4.0 * U64 * (K + 2) * abs(alpha)) * np.asarray(abs_sum, np.float64) + U64 * d
+    if beta not in (0.0, 1.0, -1.0) and c is not None:
+        bound = bound + U64 * np.abs(beta * np.asarray(c, np.float64))
+    return bound
+
+
+def check_f64(d_gpu, d_ref, abs_sum, K, alpha=1.0, beta=0.0, c=None):
+    """``check_float`` for binary64 results (``f64_bound``)."""
+    return _compare(d_gpu, d_ref, f64_bound(d_ref, abs_sum, K, alpha, beta, c))
+
+
 def check_float(d_gpu, d_ref, abs_sum, K, alpha=1.0, sA=1.0, sB=1.0, beta=0.0, c=None, out="f32"):
     """Compare GPU float results with the oracle.  Returns a dict with ``ok``,
     the number of violations (NaN counts as one), max |delta|/bound and the
     first offending flat indices."""
+    return _compare(d_gpu, d_ref, float_bound(d_ref, abs_sum, K, alpha, sA, sB, beta, c, out))
+
+
+def _compare(d_gpu, d_ref, bound):
     g = np.asarray(d_gpu, np.float64).ravel()
     r = np.asarray(d_ref, np.float64).ravel()
-    b = float_bound(d_ref, abs_sum, K, alpha, sA, sB, beta, c, out).ravel()
+    b = np.asarray(bound, np.float64).ravel()
     delta = np.abs(g - r)
     bad = ~(delta <= b)  # NaN compares false, so it is flagged
     with np.errstate(divide="ignore", invalid="ignore"):

@@ -33,6 +33,14 @@
  *    finite (2 - 2^-7) 2^127 / 65504).
  *  - int8 path: exact int64 accumulation, t = alpha*acc + beta*c, wrapped to
  *    int32 (mod 2^32).
+ *  - binary64 path (the FP64-accumulate matrix instructions of "CDNA3 dense
+ *    MFMA builtins", FP64-accumulate builtins: binary64 inputs and outputs):
+ *    every product of two binary64 inputs is exact in binary128 (at most
+ *    106 significant bits of its 113, and the exponent range cannot be
+ *    left), the k sum runs in ascending k order in binary128, alpha*acc +
+ *    beta*c is formed in binary128, and the result is rounded ONCE to
+ *    binary64 (nearest even).  The binary128 sum's own error is at most
+ *    (K+2) 2^-113 (|alpha| S + |beta c|), far below the binary64 bound.
  *  - 2:4 structured sparsity ("RDNA4 sparse WMMA builtins", Structured
  *    sparsity (2:4 pattern) and Common parameters, the index operand): in each
  *    contiguous group of four along K at most two values are non-zero; the
@@ -304,6 +312,68 @@ int orc_gemm_i8_full(int layA, int layB, int64_t M, int64_t N, int64_t K,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < M; ++i)
         for (int64_t j = 0; j < N; ++j) d_ref[i * N + j] = i8_elem(&g, alpha, beta, i, j);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------ binary64 GEMM */
+
+typedef __float128 quad;
+
+/* One output element of the binary64 GEMM: ascending-k binary128 sum of the
+ * exact products, then alpha*acc + beta*c in binary128, rounded once to
+ * binary64.  *s receives S = sum_k |a_ik b_kj| (rounded to binary64). */
+static void f64_elem(int layA, int layB, const double* A, int64_t lda, const double* B, int64_t ldb,
+                     const double* C, int64_t ldc, int64_t K, double alpha, double beta,
+                     int64_t i, int64_t j, double* d, double* s) {
+    quad acc = 0, sabs = 0;
+    for (int64_t k = 0; k < K; ++k) {
+        const double a = A[a_off(layA, i, k, lda)], b = B[b_off(layB, k, j, ldb)];
+        const quad p = (quad)a * (quad)b;
+        acc += p;
+        sabs += (quad)fabs(a) * (quad)fabs(b);
+    }
+    quad t = (quad)alpha * acc;
+    if (beta != 0.0) t += (quad)beta * (quad)C[i * ldc + j];
+    *d = (double)t;
+    *s = (double)sabs;
+}
+
+static int check_f64(int layA, int layB, int64_t M, int64_t N, int64_t K, const double* A,
+                     const double* B, const double* C, double beta) {
+    if ((layA != ORC_K_CONTIG && layA != ORC_MN_CONTIG) || (layB != ORC_K_CONTIG && layB != ORC_MN_CONTIG))
+        return ORC_BAD_ARG;
+    if (M < 0 || N < 0 || K < 0) return ORC_BAD_ARG;
+    if (K > 0 && M > 0 && !A) return ORC_BAD_ARG;
+    if (K > 0 && N > 0 && !B) return ORC_BAD_ARG;
+    if (beta != 0.0 && !C) return ORC_BAD_ARG;
+    return ORC_OK;
+}
+
+/* binary64 GEMM over a list of output coordinates (rows[t], cols[t]). */
+int orc_gemm_f64_elems(int layA, int layB, int64_t M, int64_t N, int64_t K,
+                       const double* A, int64_t lda, const double* B, int64_t ldb,
+                       const double* C, int64_t ldc, double alpha, double beta,
+                       int64_t n, const int64_t* rows, const int64_t* cols,
+                       double* d_ref, double* abs_sum) {
+    if (check_f64(layA, layB, M, N, K, A, B, C, beta) != ORC_OK || n < 0) return ORC_BAD_ARG;
+    for (int64_t t = 0; t < n; ++t)
+        if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N) return ORC_BAD_ARG;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t t = 0; t < n; ++t)
+        f64_elem(layA, layB, A, lda, B, ldb, C, ldc, K, alpha, beta, rows[t], cols[t], &d_ref[t], &abs_sum[t]);
+    return ORC_OK;
+}
+
+/* binary64 GEMM over the whole M x N output (row-major, leading dimension N). */
+int orc_gemm_f64_full(int layA, int layB, int64_t M, int64_t N, int64_t K,
+                      const double* A, int64_t lda, const double* B, int64_t ldb,
+                      const double* C, int64_t ldc, double alpha, double beta,
+                      double* d_ref, double* abs_sum) {
+    if (check_f64(layA, layB, M, N, K, A, B, C, beta) != ORC_OK) return ORC_BAD_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            f64_elem(layA, layB, A, lda, B, ldb, C, ldc, K, alpha, beta, i, j, &d_ref[i * N + j], &abs_sum[i * N + j]);
     return ORC_OK;
 }
 

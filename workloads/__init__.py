@@ -35,12 +35,13 @@ TORCH_DTYPE = {
     "e4m3": torch.float8_e4m3fn,
     "e5m2": torch.float8_e5m2,
     "i8": torch.int8,
+    "f64": torch.float64,
 }
 CODE_VIEW = {"bf16": torch.int16, "f16": torch.int16, "e4m3": torch.uint8,
-             "e5m2": torch.uint8, "i8": torch.int8}
+             "e5m2": torch.uint8, "i8": torch.int8, "f64": torch.float64}
 CODE_NP = {"bf16": np.uint16, "f16": np.uint16, "e4m3": np.uint8, "e5m2": np.uint8,
-           "i8": np.int8}
-ELEM_BYTES = {"bf16": 2, "f16": 2, "e4m3": 1, "e5m2": 1, "i8": 1}
+           "i8": np.int8, "f64": np.float64}
+ELEM_BYTES = {"bf16": 2, "f16": 2, "e4m3": 1, "e5m2": 1, "i8": 1, "f64": 8}
 # largest finite value of each fp8 format (OCP encodings)
 FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
 
@@ -59,17 +60,23 @@ def codes_of(t: torch.Tensor, dtype: str) -> np.ndarray:
 def to_tensor(codes: np.ndarray, dtype: str) -> torch.Tensor:
     """CPU torch tensor of the input dtype holding these raw codes."""
     view = CODE_VIEW[dtype]
-    np_view = {torch.int16: np.int16, torch.uint8: np.uint8, torch.int8: np.int8}[view]
+    np_view = {torch.int16: np.int16, torch.uint8: np.uint8, torch.int8: np.int8,
+               torch.float64: np.float64}[view]
     return torch.from_numpy(np.ascontiguousarray(codes).view(np_view)).view(TORCH_DTYPE[dtype])
 
 
-def draw(dist: str, shape, seed: int) -> torch.Tensor:
-    """Logical values (float32, or int64 for integer distributions)."""
+def draw(dist: str, shape, seed: int, fdtype=torch.float32) -> torch.Tensor:
+    """Logical values (fdtype, float32 unless asked otherwise, or int64 for
+    integer distributions)."""
     g = gen(seed)
     if dist == "uniform":          # 2u - 1, u ~ U[0, 1): values in [-1, 1)
-        return torch.rand(shape, generator=g, dtype=torch.float32) * 2.0 - 1.0
+        return torch.rand(shape, generator=g, dtype=fdtype) * 2.0 - 1.0
     if dist == "normal":
-        return torch.randn(shape, generator=g, dtype=torch.float32)
+        return torch.randn(shape, generator=g, dtype=fdtype)
+    if dist == "lognormal":        # sign * exp(2 z): magnitudes over about 2^-17 .. 2^17
+        z = torch.randn(shape, generator=g, dtype=fdtype)
+        sgn = torch.randint(0, 2, shape, generator=g).to(fdtype) * 2.0 - 1.0
+        return sgn * torch.exp(2.0 * z)
     if dist == "int8":             # uniform integers in [-128, 127]
         return torch.randint(-128, 128, shape, generator=g, dtype=torch.int64)
     if dist.startswith("smallint"):  # uniform integers in [-r, r], e.g. "smallint8"
@@ -85,6 +92,8 @@ def quantize(values: torch.Tensor, dtype: str, fp8_scaled: bool = False):
     Returns (tensor of dtype, dequant scale as a python float)."""
     if dtype == "i8":
         return values.to(torch.int8), 1.0
+    if dtype == "f64":
+        return values.to(torch.float64), 1.0
     scale = 1.0
     v = values.to(torch.float32)
     if dtype in FP8_MAX and fp8_scaled:
@@ -127,18 +136,21 @@ def operand(role, dtype, rows, cols, dist, layout="k_contig", seed=None, ld=None
             fp8_scaled=False) -> Operand:
     """A (rows=M, cols=K) or B (rows=K, cols=N) operand."""
     seed = (SEED_A if role == "A" else SEED_B) if seed is None else seed
-    vals, scale = quantize(draw(dist, (rows, cols), seed), dtype, fp8_scaled)
+    fdtype = torch.float64 if dtype == "f64" else torch.float32  # binary64 draws use all 53 bits
+    vals, scale = quantize(draw(dist, (rows, cols), seed, fdtype), dtype, fp8_scaled)
     s, ld = store(vals, role, layout, ld)
     return Operand(dtype, layout, codes_of(s, dtype), ld, scale)
 
 
 def c_matrix(M, N, dist, seed=SEED_C, ldc=None, dtype="f32") -> np.ndarray:
-    """C, row-major (M, ldc): float32 (normal/uniform) or int32 (dist "int20":
-    uniform integers in [-2^20, 2^20])."""
+    """C, row-major (M, ldc): float32 (normal/uniform), float64 (dtype "f64") or
+    int32 (dist "int20": uniform integers in [-2^20, 2^20])."""
     g = gen(seed)
     if dist == "int20":
         c = torch.randint(-(1 << 20), (1 << 20) + 1, (M, N), generator=g, dtype=torch.int64)
         c = c.to(torch.int32)
+    elif dtype == "f64":
+        c = draw(dist, (M, N), seed, torch.float64)
     else:
         c = draw(dist, (M, N), seed).to(torch.float32)
     ldc = N if ldc is None else ldc
