@@ -42,7 +42,8 @@ extern "C" {
  * Matrix Cores", Table 1: bfloat16, binary16, fp8 E4M3 and fp8 E5M2 in their
  * OCP encodings (E4M3: bias 7, no infinities, largest 448; E5M2: bias 15,
  * largest 57344).  MCG_I8 is signed ("CDNA3 dense MFMA builtins",
- * INT32-accumulate builtins). */
+ * INT32-accumulate builtins).  MCG_F64 is IEEE binary64, the operand and
+ * accumulator format of the FP64-accumulate builtins of the same page. */
 typedef enum {
     MCG_BF16 = 0,
     MCG_F16 = 1,
@@ -50,7 +51,8 @@ typedef enum {
     MCG_FP8_E4M3 = 3,
     MCG_FP8_E5M2 = 4,
     MCG_F32 = 5,
-    MCG_I32 = 6
+    MCG_I32 = 6,
+    MCG_F64 = 7
 } mcg_dtype;
 
 /* Storage order of the operands.  A is logically M x K, B is K x N.
@@ -81,8 +83,8 @@ typedef enum {
 /*
  * gemm_dense -- D = alpha*scaleA*scaleB*(A.B) + beta*C on MFMA.
  *
- * dtypeA/dtypeB : supported pairs are BF16xBF16, F16xF16, I8xI8 and any pair
- *                 of FP8_E4M3/FP8_E5M2.
+ * dtypeA/dtypeB : supported pairs are BF16xBF16, F16xF16, I8xI8, F64xF64 and
+ *                 any pair of FP8_E4M3/FP8_E5M2.
  * layoutA/B     : mcg_layout (all four combinations for every pair).
  * M, N, K       : any sizes >= 0.  M == 0 or N == 0 is a no-op.  K == 0 gives
  *                 D = beta*C.  Ragged edges are handled inside the kernels.
@@ -96,7 +98,9 @@ typedef enum {
  *                 MCG_F16 (fp32 accumulation; a bfloat16/binary16 D is the
  *                 fp32 result rounded once to nearest-even, C is read in the
  *                 same format).  int8: MCG_I32 (exact int32 accumulation,
- *                 wrapping mod 2^32).
+ *                 wrapping mod 2^32).  F64: MCG_F64 (binary64 accumulation on
+ *                 the FP64 matrix instructions, alpha and beta used as
+ *                 binary64).
  * alpha, beta   : float paths use them as fp32.  The int8 path requires
  *                 integral values in int32 range and computes
  *                 alpha*acc + beta*C in wrapping int32 arithmetic.
@@ -114,14 +118,18 @@ typedef enum {
  *                 the largest product of each group they sum (measured), which
  *                 fits that bound from K = 6144 on; below it fp8 operands are
  *                 widened exactly to bfloat16 and multiplied on the bfloat16
- *                 instructions.
- * Alignment     : none required; 16-byte aligned pointers and leading
+ *                 instructions.  Binary64 results stay within
+ *                 4*2^-53*(K+2)*|alpha|*sum|a*b| + 2^-53*|D| of the exact value
+ *                 (plus 2^-53*|beta*c| when beta is not 0 or +-1).
+ * Alignment     : none beyond the element size (binary64 operands take the
+ *                 same path at any leading dimension); 16-byte aligned
+ *                 pointers and leading
  *                 dimensions whose byte size is a multiple of 16 take the
  *                 vector-load path, anything else a slower element path.
  * Split K       : problems with too few output tiles to fill the device
  *                 (e.g. N <= 32, M <= 32, or a long K over a small D) may cut
- *                 K into ranges run by separate workgroups when D is MCG_F32
- *                 or MCG_I32 and is not C with beta != 0.  D is then zeroed,
+ *                 K into ranges run by separate workgroups when D is MCG_F32,
+ *                 MCG_I32 or MCG_F64 and is not C with beta != 0.  D is then zeroed,
  *                 receives the partial sums through device-scope atomic adds
  *                 and is finally set to alpha*D + beta*C, so D must be
  *                 ordinary device memory.  Float results of a split problem
@@ -216,7 +224,9 @@ int mcg_validate_compress24(int dtype, int64_t M, int64_t K, const void* A, int6
      binary32/int32 D that is not C: 0 general kernel, 128 x 128 tiles (any
      shape, alignment or leading dimension); 1 the 256 x 256 pipelined kernel;
      2 general kernel with 128 x 32 tiles (N <= 32, aligned operands);
-     3 general kernel with 32 x 128 tiles (M <= 32, aligned operands).
+     3 general kernel with 32 x 128 tiles (M <= 32, aligned operands);
+     4 the streaming kernel (N <= 32 or M <= 32, K-contiguous aligned
+     operands); 5 the binary64 kernel (dtypeA MCG_F64, any shape).
    mcg_dense_splits: the number of K ranges (1 = no split) gemm_dense uses
      with exactly these arguments.
    mcg_sparse24_path: 1 if gemm_sparse24 runs the 256 x 256 pipelined kernel,

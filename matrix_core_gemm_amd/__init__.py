@@ -7,7 +7,7 @@ arithmetic runs in the HIP kernels of ``_libmcg.so``; there is no fallback.
 If the library has not been built, importing this package fails.
 
 dtype and layout arguments take the C enum values or their names:
-  dtypes : "bf16", "f16", "i8", "e4m3", "e5m2", "f32", "i32"
+  dtypes : "bf16", "f16", "i8", "e4m3", "e5m2", "f32", "i32", "f64"
   layouts: "k_contig" (A row-major / B column-major),
            "mn_contig" (A column-major / B row-major)
 """
@@ -21,7 +21,7 @@ import torch  # loaded first so the library binds to torch's HIP runtime
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_libmcg.so")
 
-DTYPES = {"bf16": 0, "f16": 1, "i8": 2, "e4m3": 3, "e5m2": 4, "f32": 5, "i32": 6}
+DTYPES = {"bf16": 0, "f16": 1, "i8": 2, "e4m3": 3, "e5m2": 4, "f32": 5, "i32": 6, "f64": 7}
 LAYOUTS = {"k_contig": 0, "mn_contig": 1}
 STATUS = {0: "MCG_SUCCESS", 1: "MCG_ERR_NULL_POINTER", 2: "MCG_ERR_INVALID_SIZE",
           3: "MCG_ERR_INVALID_LD", 4: "MCG_ERR_UNSUPPORTED_DTYPE", 5: "MCG_ERR_MISALIGNED",
@@ -162,7 +162,7 @@ def validate_compress24(dtype, M, K, A, lda, A_compressed, lda_c, A_index, ld_id
 def dense_path(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb) -> int:
     """Kernel gemm_dense runs for these operands (binary32/int32 D, not C):
     0 general 128 x 128, 1 the 256 x 256 kernel, 2 general 128 x 32 (N <= 32),
-    3 general 32 x 128 (M <= 32)."""
+    3 general 32 x 128 (M <= 32), 4 streaming kernel, 5 binary64 kernel."""
     return _lib.mcg_dense_path(_dt(dtypeA), _lay(layoutA), _lay(layoutB), M, N, K, _ptr(A), lda,
                                _ptr(B), ldb)
 

@@ -29,6 +29,7 @@ int elem_bytes(int dt) {
     case MCG_FP8_E5M2: return 1;
     case MCG_F32:
     case MCG_I32: return 4;
+    case MCG_F64: return 8;
     default: return 0;
   }
 }
@@ -66,12 +67,17 @@ int mcg_validate_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t
                        int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
                        const void* C, const void* D, int64_t ldc, int dtypeD, double alpha,
                        double beta, float scaleA, float scaleB) {
-  if (!is_in_dtype(dtypeA) || !is_in_dtype(dtypeB)) return MCG_ERR_UNSUPPORTED_DTYPE;
+  if (dtypeA == MCG_F64 || dtypeB == MCG_F64) {
+    if (dtypeA != dtypeB || dtypeD != MCG_F64) return MCG_ERR_UNSUPPORTED_DTYPE;
+  } else if (!is_in_dtype(dtypeA) || !is_in_dtype(dtypeB)) {
+    return MCG_ERR_UNSUPPORTED_DTYPE;
+  }
   const bool f8 = is_float8(dtypeA) && is_float8(dtypeB);
   if (!f8 && dtypeA != dtypeB) return MCG_ERR_UNSUPPORTED_DTYPE;
   if (is_float8(dtypeA) != is_float8(dtypeB)) return MCG_ERR_UNSUPPORTED_DTYPE;
   const bool i8 = dtypeA == MCG_I8;
-  if (i8 ? dtypeD != MCG_I32 : !float_out(dtypeD)) return MCG_ERR_UNSUPPORTED_DTYPE;
+  const bool f64 = dtypeA == MCG_F64;
+  if (i8 ? dtypeD != MCG_I32 : f64 ? dtypeD != MCG_F64 : !float_out(dtypeD)) return MCG_ERR_UNSUPPORTED_DTYPE;
   if (!valid_layout(layoutA) || !valid_layout(layoutB)) return MCG_ERR_UNSUPPORTED_DTYPE;
   if (M < 0 || N < 0 || K < 0) return MCG_ERR_INVALID_SIZE;
   if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX) return MCG_ERR_INVALID_SIZE;
@@ -108,6 +114,25 @@ static bool can_split_k(const mcg::DenseArgs& a, const void* C, const void* D) {
   return a.out == mcg::OUT_32 && !(a.use_c && C == D);
 }
 
+static mcg::F64Args f64_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                             int64_t ldb, const void* C, void* D, int64_t ldc, double alpha, double beta) {
+  mcg::F64Args a{};
+  a.A = (const double*)A;
+  a.B = (const double*)B;
+  a.C = (const double*)C;
+  a.D = (double*)D;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.use_c = beta != 0.0;
+  return a;
+}
+
 int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
                const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, void* D,
                int64_t ldc, int dtypeD, double alpha, double beta, float scaleA, float scaleB,
@@ -117,6 +142,11 @@ int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int6
   if (st != MCG_SUCCESS || M == 0 || N == 0) return st;
   st = check_arch();
   if (st != MCG_SUCCESS) return st;
+  if (dtypeA == MCG_F64) {
+    const mcg::F64Args a = f64_args(M, N, K, A, lda, B, ldb, C, D, ldc, alpha, beta);
+    const mcg::F64Plan plan = mcg::plan_f64(a, !(a.use_c && C == D));
+    return hip_status(mcg::launch_f64(layoutA, layoutB, a, plan, (hipStream_t)stream));
+  }
 
   const int eb = elem_bytes(dtypeA);
   mcg::DenseArgs a{};
@@ -308,6 +338,7 @@ static mcg::DensePlan dense_plan(int dtypeA, int layoutA, int layoutB, int64_t M
 
 int mcg_dense_path(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A,
                    int64_t lda, const void* B, int64_t ldb) {
+  if (dtypeA == MCG_F64) return mcg::KERNEL_F64;
   if (dtypeA < MCG_BF16 || dtypeA > MCG_FP8_E5M2) return 0;
   return dense_plan(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb, true).kernel;
 }
@@ -315,6 +346,10 @@ int mcg_dense_path(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, i
 int mcg_dense_splits(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A,
                      int64_t lda, const void* B, int64_t ldb, const void* C, const void* D, int dtypeD,
                      double beta) {
+  if (dtypeA == MCG_F64) {
+    const mcg::F64Args a = f64_args(M, N, K, A, lda, B, ldb, C, (void*)D, N, 1.0, beta);
+    return mcg::plan_f64(a, dtypeD == MCG_F64 && !(beta != 0.0 && C == D)).splits;
+  }
   if (dtypeA < MCG_BF16 || dtypeA > MCG_FP8_E5M2) return 1;
   const bool can_split = (dtypeD == MCG_F32 || dtypeD == MCG_I32) && !(beta != 0.0 && C == D);
   return dense_plan(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb, can_split).splits;

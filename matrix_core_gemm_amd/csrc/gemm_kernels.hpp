@@ -31,7 +31,8 @@ enum : int {
   KERNEL_FAST = 1,      // 256 x 256 tiles, 8 waves, LDS-DMA ring (large problems)
   KERNEL_SKINNY_N = 2,  // general kernel with 128 x 32 tiles (N <= 32)
   KERNEL_SKINNY_M = 3,  // general kernel with 32 x 128 tiles (M <= 32)
-  KERNEL_STREAM = 4     // streaming kernel for N <= 32 or M <= 32 (K-contiguous, aligned)
+  KERNEL_STREAM = 4,    // streaming kernel for N <= 32 or M <= 32 (K-contiguous, aligned)
+  KERNEL_F64 = 5        // binary64 kernel (128 x 128 tiles on the 4x4x4 FP64 instruction)
 };
 
 struct DensePlan {
@@ -55,6 +56,37 @@ struct SparseArgs {
   int out;  // OUT_32 (binary32 / int32), OUT_BF16 or OUT_F16: format of C and D
   int tiles_m, tiles_n;
 };
+
+// binary64 GEMM (DGEMM)
+struct F64Args {
+  const double* A;
+  const double* B;
+  const double* C;
+  double* D;
+  int64_t M, N, K;
+  int64_t lda, ldb, ldc;  // elements
+  double alpha, beta;
+  int use_c;              // beta != 0: C is read
+  int kt_per_split;       // K tiles of 16 per workgroup range (filled by the launcher)
+  int tiles_m, tiles_n;   // filled by the launcher
+};
+
+struct F64Plan {
+  int splits;        // >1: K split over grid.y, partial sums added into D with atomics
+  int kt_per_split;  // K tiles of 16 per range
+};
+
+// Split-K cost model of the binary64 kernel (microseconds; gfx950, 256 CUs).
+constexpr int64_t F64_NUM_CU = 256;
+constexpr int64_t F64_SPLIT_MIN_KT = 16;  // at least 256 K values per range
+constexpr double F64_KT_US = 1.8;         // one K tile of a resident 128 x 128 tile
+constexpr double F64_ROUND_US = 3.0;      // per wave of resident tiles (prologue, epilogue)
+constexpr double F64_ATOMIC_US = 1.4e-5;  // per atomic add of a partial sum
+constexpr double F64_SPLIT_US = 5.0;      // zeroing D and the extra launch
+
+// can_split: D is not C with beta != 0.
+F64Plan plan_f64(const F64Args& a, bool can_split);
+hipError_t launch_f64(int layoutA, int layoutB, const F64Args& a, const F64Plan& plan, hipStream_t s);
 
 struct CompressArgs {
   const char* A;

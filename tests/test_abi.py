@@ -95,6 +95,15 @@ def dense_args(**kw):
     ({"dtypeD": "i32"}, 4),                          # int32 output only for int8 inputs
     ({"dtypeA": "i8", "dtypeB": "i8", "dtypeD": "bf16"}, 4),
     ({"dtypeD": "e4m3"}, 4),
+    ({"dtypeA": "f64", "dtypeB": "f64", "dtypeD": "f64"}, 0),   # binary64
+    ({"dtypeA": "f64", "dtypeB": "f64", "dtypeD": "f32"}, 4),   # binary64 output only
+    ({"dtypeA": "f64", "dtypeB": "bf16", "dtypeD": "f64"}, 4),
+    ({"dtypeA": "bf16", "dtypeB": "f64", "dtypeD": "f64"}, 4),
+    ({"dtypeD": "f64"}, 4),                                     # binary64 output only for binary64 inputs
+    ({"dtypeA": "f64", "dtypeB": "f64", "dtypeD": "f64", "A": FAKE + 4}, 5),
+    ({"dtypeA": "f64", "dtypeB": "f64", "dtypeD": "f64", "D": FAKE + 8, "lda": 49}, 0),
+    ({"dtypeA": "f64", "dtypeB": "f64", "dtypeD": "f64", "scaleB": 0.5}, 10),
+    ({"dtypeA": "f64", "dtypeB": "f64", "dtypeD": "f64", "beta": float("inf"), "C": FAKE}, 10),
 ])
 def test_dense_validation(kw, status):
     assert m.validate_dense(**dense_args(**kw)) == status
