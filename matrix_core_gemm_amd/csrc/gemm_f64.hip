@@ -20,16 +20,28 @@
 // accumulator is redundant and no cross-lane reduction is needed.
 //
 // Tiling.  128 x 128 output tiles, 8 waves (2 along M x 4 along N, 64 x 32 per
-// wave: 4 x 8 instructions per K index group), K in tiles of 16.  Each thread
-// moves 4 elements of A and 4 of B per K tile from HBM into registers (8-byte
-// loads, any alignment of the leading dimensions, zero outside the matrix) while
-// the previous tile is multiplied, then stores them into the other half of a
-// 2 x 32 KiB LDS double buffer; one barrier per K tile.  LDS rows hold the 16 K
-// values of one row of A (column of B) as eight 16-byte chunks, chunk c of row r at
-// position c ^ (r & 7), so the 8 rows a fragment read touches at once use 8
-// different chunks.  A lane's fragment read takes K = 4g + 2h and 4g + 2h + 1
-// (g = lane >> 4, h = 0, 1) with one 16-byte read; the two instructions that use
-// them take the K index sets {4g + 2h} and {4g + 2h + 1}, consistently for A and B.
+// wave: 4 x 8 instructions per K index group), K in tiles of 32, two LDS stages of
+// 64 KiB.  Lane group g (lane >> 4) owns K = 8g .. 8g + 7 of each tile and reads
+// them as four pairs (h = 0..3); the two instructions fed by pair h take the K
+// index sets {8g + 2h} and {8g + 2h + 1}, consistently for A and B.
+//
+// LDS images.  A K-contiguous operand keeps one row of A (column of B) per 256
+// bytes, 16-byte chunk c of row r at position c ^ (r & 7), so the 8 rows read
+// together by a fragment read hit 8 different chunks; pairs are read with one
+// 16-byte read.  An MN-contiguous operand keeps one K per 1 KiB row, unswizzled
+// (16 lanes read 128 consecutive bytes); pairs are read as two 8-byte values 1 KiB
+// apart.
+//
+// Loads.  The FP64 matrix instructions leave no issue slots to vector ALU work
+// (the pages' throughput table lists no co-execution for them), so the steady
+// state keeps both registers and vector arithmetic out of the loads: tiles inside
+// M and N move HBM -> LDS by buffer_load ... lds (16 bytes per lane, 1 KiB per wave
+// instruction) from a scalar descriptor at the tile's corner, with one fixed
+// per-lane offset and scalar offsets per instruction, into the stage the previous
+// tile is not using; the swizzle is applied on the global side (each lane fetches
+// the chunk that belongs at its LDS position).  A K tile that crosses the end of K
+// and every tile crossing the edge of M or N are loaded element by element with
+// bounds checks (zeros outside) and stored with ds_write.
 //
 // Split K (few output tiles, long K): grid.y ranges of K tiles; the ranges add
 // alpha * partial into a zeroed D with binary64 atomic adds, and beta * C is added
@@ -38,78 +50,129 @@
 #include "fast_tiles.hpp"
 #include "gemm_kernels.hpp"
 
+#include <type_traits>
+
 namespace mcg {
 namespace f64 {
 
-constexpr int BM = 128, BN = 128, BK = 16, THREADS = 512;
+constexpr int BM = 128, BN = 128, BK = 32, THREADS = 512;
 constexpr int WM = 64, WN = 32;            // wave tile
 constexpr int FM = WM / 16, FN = WN / 4;   // instructions per K index group: FM x FN
-constexpr int ROW_BYTES = BK * 8;          // one LDS row: 16 binary64 K values
-constexpr int A_BYTES = BM * ROW_BYTES;    // 16 KiB
-constexpr int STAGE_BYTES = A_BYTES + BN * ROW_BYTES;
-constexpr int PER_THREAD = BM * BK / THREADS;  // elements of each operand per thread and K tile
+constexpr int OP_BYTES = BM * BK * 8;      // 32 KiB: one operand's tile
+constexpr int STAGE = 2 * OP_BYTES;        // A then B
+constexpr int PT = BM * BK / THREADS;      // elements of each operand per thread in the checked path
 static_assert(BM == BN, "one loader geometry serves both operands");
-static_assert(PER_THREAD * THREADS == BM * BK, "loader covers the tile");
+static_assert(PT * THREADS == BM * BK, "checked loader covers the tile");
+static_assert(OP_BYTES == 32 * 1024, "4 DMA instructions of 1 KiB per wave and operand");
 
 typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Byte offset of K value k (0..15) of LDS row r.
-__device__ __forceinline__ int lds_at(int r, int k) {
-  return r * ROW_BYTES + ((((k >> 1) ^ r) & 7) << 4) + ((k & 1) << 3);
+// LDS byte offset of element (r, k) of an operand tile (r: row of A / column of B).
+template <int LAY>
+__device__ __forceinline__ int lds_elem(int r, int k) {
+  if constexpr (LAY == 0) return r * 256 + ((((k >> 1) ^ r) & 7) | ((k >> 1) & 8)) * 16 + (k & 1) * 8;
+  else return k * 1024 + r * 8;
 }
 
-// Moves one operand's 128 x 16 tile.  LAY 0 (K-contiguous): element (r, k) at
-// X[r * ld + k]; LAY 1 (MN-contiguous): at X[k * ld + r].  Thread t moves
-// elements e = t + 512 p: (r, k) = (e >> 4, e & 15) for LAY 0, so 16 threads read
-// one 128-byte row; (e & 127, e >> 7) for LAY 1, so consecutive threads read
-// consecutive rows of one K.
+// One operand's tiles.  LAY 0 (K-contiguous): element (r, k) at X[r * ld + k];
+// LAY 1 (MN-contiguous): at X[k * ld + r].
 template <int LAY>
-struct Loader {
-  const double* ptr[PER_THREAD];
-  int64_t step;  // elements between consecutive K tiles
-  int r[PER_THREAD], k[PER_THREAD];
-  bool row_ok[PER_THREAD];
-  double v[PER_THREAD];
+struct Operand {
+  const double* X;
+  int64_t ld, rows, K, r0;
+  // DMA: wave w, instruction i fills LDS bytes [(8i + w) KiB, +1 KiB) of the tile.
+  //   LAY 0: rows 32i + 4w + (l >> 4); lane l's LDS position l & 15 takes global chunk
+  //          (l & 15) ^ (row & 7) of that row
+  //   LAY 1: K row 8i + w; lane l takes values 2l, 2l + 1 of it
+  uint32_t voff;  // per lane
+  uint32_t soff;  // per wave, instruction 0
+  uint32_t istr;  // per instruction
 
-  __device__ __forceinline__ void init(const double* X, int64_t ld, int64_t r0, int64_t rows, int64_t k0,
-                                       int tid) {
-#pragma unroll
-    for (int p = 0; p < PER_THREAD; ++p) {
-      const int e = tid + THREADS * p;
-      r[p] = LAY == 0 ? e >> 4 : e & (BM - 1);
-      k[p] = LAY == 0 ? e & (BK - 1) : e >> 7;
-      row_ok[p] = r0 + r[p] < rows;
-      const int64_t rg = row_ok[p] ? r0 + r[p] : 0;
-      ptr[p] = LAY == 0 ? X + rg * ld + k0 + k[p] : X + (k0 + k[p]) * ld + rg;
-    }
-    step = LAY == 0 ? BK : BK * ld;
-  }
-  // Load the tile starting at K = k0 (elements with K >= kend or outside the rows read 0) and
-  // advance to the next tile.
-  __device__ __forceinline__ void load(int64_t k0, int64_t kend) {
-    if (k0 + BK <= kend) {
-#pragma unroll
-      for (int p = 0; p < PER_THREAD; ++p) v[p] = row_ok[p] ? *ptr[p] : 0.0;
+  __device__ __forceinline__ void init(const double* X_, int64_t ld_, int64_t r0_, int64_t rows_, int64_t K_,
+                                       int w, int lane) {
+    X = X_;
+    ld = ld_;
+    rows = rows_;
+    K = K_;
+    r0 = r0_;
+    if constexpr (LAY == 0) {
+      const int row = 4 * w + (lane >> 4);
+      const int c = (lane & 15) ^ (row & 7);
+      voff = (uint32_t)(row * ld * 8 + c * 16);
+      soff = 0;
+      istr = __builtin_amdgcn_readfirstlane((uint32_t)(32 * ld * 8));
     } else {
+      voff = (uint32_t)(lane * 16);
+      soff = __builtin_amdgcn_readfirstlane((uint32_t)(w * ld * 8));
+      istr = __builtin_amdgcn_readfirstlane((uint32_t)(8 * ld * 8));
+    }
+  }
+  // K tile starting at k0, inside the rows and K: four 1 KiB DMA instructions per wave.
+  __device__ __forceinline__ void dma(char* dst, int64_t k0, int w) const {
+    const char* corner = (const char*)(X + (LAY == 0 ? r0 * ld + k0 : k0 * ld + r0));
+    const __amdgpu_buffer_rsrc_t rs = fast::make_rsrc(corner, 0xFFFFFFFFu);
 #pragma unroll
-      for (int p = 0; p < PER_THREAD; ++p) v[p] = (row_ok[p] && k0 + k[p] < kend) ? *ptr[p] : 0.0;
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (8 * i + w) * 1024), 16, voff,
+                                               soff + (uint32_t)i * istr, 0, 0);
+  }
+  // Any K tile: element by element, zeros outside the rows and K, stored with ds_write.
+  // Element p of thread t: LAY 0 (r, k) = ((t >> 5) + 16 p, t & 31); LAY 1 (t & 127, (t >> 7) + 4 p).
+  __device__ __forceinline__ void checked(char* dst, int64_t k0, int tid) const {
+    double v[PT];
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const int r = LAY == 0 ? (tid >> 5) + 16 * p : tid & 127;
+      const int k = LAY == 0 ? tid & 31 : (tid >> 7) + 4 * p;
+      const int64_t gr = r0 + r, gk = k0 + k;
+      v[p] = (gr < rows && gk < K) ? X[LAY == 0 ? gr * ld + gk : gk * ld + gr] : 0.0;
     }
 #pragma unroll
-    for (int p = 0; p < PER_THREAD; ++p) ptr[p] += step;
+    for (int p = 0; p < PT; ++p) {
+      const int r = LAY == 0 ? (tid >> 5) + 16 * p : tid & 127;
+      const int k = LAY == 0 ? tid & 31 : (tid >> 7) + 4 * p;
+      *(double*)(dst + lds_elem<LAY>(r, k)) = v[p];
+    }
   }
-  __device__ __forceinline__ void store(char* lds) const {
+};
+
+// Fragment reads of one operand for pair h: lane row (column) base rb, groups of
+// 16 rows (A, stride 16) or 4 columns (B, stride 4).
+template <int LAY, int N, int STRIDE>
+struct Frags {
+  int base[4][2];  // LAY 0: per h and parity of the group index; LAY 1: per h
+  __device__ __forceinline__ void init(int rb, int g) {
 #pragma unroll
-    for (int p = 0; p < PER_THREAD; ++p) *(double*)(lds + lds_at(r[p], k[p])) = v[p];
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const int r = rb + par * STRIDE;
+        base[h][par] = LAY == 0 ? rb * 256 + (((4 * g + h) ^ (r & 7)) << 4) : (8 * g + 2 * h) * 1024 + rb * 8;
+      }
+  }
+  __device__ __forceinline__ void read(const char* op, int h, f64x2 (&x)[N]) const {
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      if constexpr (LAY == 0) {
+        x[q] = *(const f64x2*)(op + base[h][q & 1] + q * STRIDE * 256);
+      } else {
+        const char* a = op + base[h][0] + q * STRIDE * 8;
+        x[q][0] = *(const double*)a;
+        x[q][1] = *(const double*)(a + 1024);
+      }
+    }
   }
 };
 
 template <int LA, int LB>
 __global__ __launch_bounds__(THREADS) void dgemm_kernel(F64Args p) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
   int tm, tn;
   fast::tile_coords<8>(p.tiles_m, p.tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = (w & 1) * WM, wn = (w >> 1) * WN;
 
   // K range of this workgroup (grid.y > 1: split K)
@@ -118,10 +181,15 @@ __global__ __launch_bounds__(THREADS) void dgemm_kernel(F64Args p) {
   const int64_t nk = nk_all - kt0 < p.kt_per_split ? nk_all - kt0 : p.kt_per_split;
   const int64_t kbeg = kt0 * BK;
 
-  Loader<LA> la;
-  Loader<LB> lb;
-  la.init(p.A, p.lda, m0, p.M, kbeg, tid);
-  lb.init(p.B, p.ldb, n0, p.N, kbeg, tid);
+  Operand<LA> oa;
+  Operand<LB> ob;
+  oa.init(p.A, p.lda, m0, p.M, p.K, w, lane);
+  ob.init(p.B, p.ldb, n0, p.N, p.K, w, lane);
+  const int g = lane >> 4;
+  Frags<LA, FM, 16> fa;
+  Frags<LB, FN, 4> fb;
+  fa.init(wm + (lane & 15), g);
+  fb.init(wn + (lane & 3), g);
 
   double acc[FM][FN];
 #pragma unroll
@@ -129,32 +197,12 @@ __global__ __launch_bounds__(THREADS) void dgemm_kernel(F64Args p) {
 #pragma unroll
     for (int c = 0; c < FN; ++c) acc[f][c] = 0.0;
 
-  const int g = lane >> 4;
-  const int ra = wm + (lane & 15);  // A row of this lane (+ 16 f)
-  const int cb = wn + (lane & 3);   // B column of this lane (+ 4 c)
-
-  if (nk > 0) {
-    la.load(kbeg, p.K);
-    lb.load(kbeg, p.K);
-    la.store(lds);
-    lb.store(lds + A_BYTES);
-    __syncthreads();
-  }
-  for (int64_t t = 0; t < nk; ++t) {
-    const bool more = t + 1 < nk;
-    if (more) {
-      la.load(kbeg + (t + 1) * BK, p.K);
-      lb.load(kbeg + (t + 1) * BK, p.K);
-    }
-    const char* sA = lds + (t & 1) * STAGE_BYTES;
-    const char* sB = sA + A_BYTES;
+  auto compute = [&](const char* st) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 4; ++h) {
       f64x2 a[FM], b[FN];
-#pragma unroll
-      for (int f = 0; f < FM; ++f) a[f] = *(const f64x2*)(sA + lds_at(ra + 16 * f, 4 * g + 2 * h));
-#pragma unroll
-      for (int c = 0; c < FN; ++c) b[c] = *(const f64x2*)(sB + lds_at(cb + 4 * c, 4 * g + 2 * h));
+      fa.read(st, h, a);
+      fb.read(st + OP_BYTES, h, b);
 #pragma unroll
       for (int e = 0; e < 2; ++e)
 #pragma unroll
@@ -163,12 +211,51 @@ __global__ __launch_bounds__(THREADS) void dgemm_kernel(F64Args p) {
           for (int c = 0; c < FN; ++c)
             acc[f][c] = __builtin_amdgcn_mfma_f64_4x4x4f64(a[f][e], b[c][e], acc[f][c], 0, 0, 0);
     }
-    if (more) {
-      char* nxt = lds + ((t + 1) & 1) * STAGE_BYTES;
-      la.store(nxt);
-      lb.store(nxt + A_BYTES);
+  };
+  auto checked = [&](char* st, int64_t k0) {
+    oa.checked(st, k0, tid);
+    ob.checked(st + OP_BYTES, k0, tid);
+  };
+
+  if (p.dma_ok && m0 + BM <= p.M && n0 + BN <= p.N) {
+    // tiles inside M and N: DMA for every K tile inside K, the checked path for the tail
+    auto fill = [&](char* st, int64_t t) {
+      const int64_t k0 = kbeg + t * BK;
+      if (k0 + BK <= p.K) {
+        oa.dma(st, k0, w);
+        ob.dma(st + OP_BYTES, k0, w);
+      } else {
+        checked(st, k0);
+      }
+    };
+    // the DMA writes of a wave are complete once its vmcnt drains; the barrier then
+    // publishes the stage to every wave
+    auto publish = [&]() {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    };
+    auto step = [&](auto stage, int64_t t) {
+      constexpr int S = decltype(stage)::value;
+      if (t + 1 < nk) fill(lds + (1 - S) * STAGE, t + 1);
+      compute(lds + S * STAGE);
+      publish();
+    };
+    if (nk > 0) {
+      fill(lds, 0);
+      publish();
     }
-    __syncthreads();
+    for (int64_t t = 0; t < nk; t += 2) {
+      step(std::integral_constant<int, 0>(), t);
+      if (t + 1 < nk) step(std::integral_constant<int, 1>(), t + 1);
+    }
+  } else {
+    // edge tiles: one stage, checked loads
+    for (int64_t t = 0; t < nk; ++t) {
+      checked(lds, kbeg + t * BK);
+      __syncthreads();
+      compute(lds);
+      __syncthreads();
+    }
   }
 
   // result lane l: row 4((l >> 2) & 3) + (l >> 4), column l & 3 of each 16 x 4 piece
@@ -218,6 +305,14 @@ static void launch_tiles(const F64Args& a, int splits, hipStream_t s) {
                      0, s, a);
 }
 
+// DMA path: 16-byte aligned rows (base and leading dimension) and every offset of a
+// tile from its corner in 32 bits: at most (127 ld + 31) * 8 (K-contiguous) or
+// (31 ld + 127) * 8 (MN-contiguous), plus 16 bytes.
+static bool f64_dma_ok(int lay, const double* X, int64_t ld) {
+  const int64_t span = lay == 0 ? (127 * ld + 31) * 8 : (31 * ld + 127) * 8;
+  return ((uintptr_t)X % 16) == 0 && ld % 2 == 0 && span + 16 < ((int64_t)0xFFFFFFFF);
+}
+
 }  // namespace f64
 
 F64Plan plan_f64(const F64Args& a, bool can_split) {
@@ -255,6 +350,7 @@ hipError_t launch_f64(int la, int lb, const F64Args& a0, const F64Plan& plan, hi
   a.tiles_m = (int)((a.M + BM - 1) / BM);
   a.tiles_n = (int)((a.N + BN - 1) / BN);
   a.kt_per_split = plan.kt_per_split;
+  a.dma_ok = a.K == 0 || (f64_dma_ok(la, a.A, a.lda) && f64_dma_ok(lb, a.B, a.ldb));
   const dim3 rows_grid((unsigned)((a.N + 255) / 256), (unsigned)(a.M < 4096 ? a.M : 4096));
   if (plan.splits > 1) {
     hipLaunchKernelGGL(zero_kernel, rows_grid, dim3(256), 0, s, a);
