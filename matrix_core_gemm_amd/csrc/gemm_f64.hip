@@ -19,16 +19,19 @@
 // and result lane l holds row 4((l >> 2) & 3) + (l >> 4), column l & 3.  No
 // accumulator is redundant and no cross-lane reduction is needed.
 //
-// Tiling.  128 x 128 output tiles, 8 waves (2 along M x 4 along N, 64 x 32 per
-// wave: 4 x 8 instructions per K index group), K in tiles of 32, two LDS stages of
-// 64 KiB.  Lane group g (lane >> 4) owns K = 8g .. 8g + 7 of each tile and reads
-// them as four pairs (h = 0..3); the two instructions fed by pair h take the K
-// index sets {8g + 2h} and {8g + 2h + 1}, consistently for A and B.
+// Tiling.  128 x 128 output tiles, 4 waves of 64 x 64 (4 x 16 instructions per K
+// index group), K in tiles of 16, two LDS stages of 32 KiB; two workgroups share
+// a CU, so each SIMD holds waves of two workgroups whose barriers and tile starts
+// do not coincide and one keeps the matrix core busy while the other waits.  Lane
+// group g (lane >> 4) owns K = 4g .. 4g + 3 of each tile and reads them as two
+// pairs (h = 0, 1); the two instructions fed by pair h take the K index sets
+// {4g + 2h} and {4g + 2h + 1}, consistently for A and B.
 //
-// LDS images.  A K-contiguous operand keeps one row of A (column of B) per 256
-// bytes, 16-byte chunk c of row r at position c ^ (r & 7), so the 8 rows read
-// together by a fragment read hit 8 different chunks; pairs are read with one
-// 16-byte read.  An MN-contiguous operand keeps one K per 1 KiB row, unswizzled
+// LDS images.  A K-contiguous operand keeps one row of A (column of B) per 128
+// bytes, 16-byte chunk c of row r at position c ^ ((r >> 1) & 7): the 16
+// consecutive rows read by one 16-lane group then cover 16 different 16-byte bank
+// slots (rows of either parity sit in different halves of 256 bytes).  Pairs are
+// read with one 16-byte read.  An MN-contiguous operand keeps one K per 1 KiB row
 // (16 lanes read 128 consecutive bytes); pairs are read as two 8-byte values 1 KiB
 // apart.
 //
@@ -55,15 +58,16 @@
 namespace mcg {
 namespace f64 {
 
-constexpr int BM = 128, BN = 128, BK = 32, THREADS = 512;
-constexpr int WM = 64, WN = 32;            // wave tile
+constexpr int BM = 128, BN = 128, BK = 16, THREADS = 256, NWAVE = 4;
+constexpr int WM = 64, WN = 64;            // wave tile
 constexpr int FM = WM / 16, FN = WN / 4;   // instructions per K index group: FM x FN
-constexpr int OP_BYTES = BM * BK * 8;      // 32 KiB: one operand's tile
+constexpr int OP_BYTES = BM * BK * 8;      // 16 KiB: one operand's tile
 constexpr int STAGE = 2 * OP_BYTES;        // A then B
+constexpr int DMA_I = OP_BYTES / 1024 / NWAVE;  // 1 KiB DMA instructions per wave and operand
 constexpr int PT = BM * BK / THREADS;      // elements of each operand per thread in the checked path
 static_assert(BM == BN, "one loader geometry serves both operands");
 static_assert(PT * THREADS == BM * BK, "checked loader covers the tile");
-static_assert(OP_BYTES == 32 * 1024, "4 DMA instructions of 1 KiB per wave and operand");
+static_assert(DMA_I * NWAVE * 1024 == OP_BYTES, "whole DMA instructions");
 
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -71,7 +75,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // LDS byte offset of element (r, k) of an operand tile (r: row of A / column of B).
 template <int LAY>
 __device__ __forceinline__ int lds_elem(int r, int k) {
-  if constexpr (LAY == 0) return r * 256 + ((((k >> 1) ^ r) & 7) | ((k >> 1) & 8)) * 16 + (k & 1) * 8;
+  if constexpr (LAY == 0) return r * 128 + (((k >> 1) ^ (r >> 1)) & 7) * 16 + (k & 1) * 8;
   else return k * 1024 + r * 8;
 }
 
@@ -81,10 +85,10 @@ template <int LAY>
 struct Operand {
   const double* X;
   int64_t ld, rows, K, r0;
-  // DMA: wave w, instruction i fills LDS bytes [(8i + w) KiB, +1 KiB) of the tile.
-  //   LAY 0: rows 32i + 4w + (l >> 4); lane l's LDS position l & 15 takes global chunk
-  //          (l & 15) ^ (row & 7) of that row
-  //   LAY 1: K row 8i + w; lane l takes values 2l, 2l + 1 of it
+  // DMA: wave w, instruction i fills LDS bytes [(4i + w) KiB, +1 KiB) of the tile.
+  //   LAY 0: rows 32i + 8w + (l >> 3); lane l's LDS position l & 7 takes global chunk
+  //          (l & 7) ^ ((row >> 1) & 7) of that row
+  //   LAY 1: K row 4i + w; lane l takes values 2l, 2l + 1 of it
   uint32_t voff;  // per lane
   uint32_t soff;  // per wave, instruction 0
   uint32_t istr;  // per instruction
@@ -97,76 +101,81 @@ struct Operand {
     K = K_;
     r0 = r0_;
     if constexpr (LAY == 0) {
-      const int row = 4 * w + (lane >> 4);
-      const int c = (lane & 15) ^ (row & 7);
+      const int row = 8 * w + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
       voff = (uint32_t)(row * ld * 8 + c * 16);
       soff = 0;
       istr = __builtin_amdgcn_readfirstlane((uint32_t)(32 * ld * 8));
     } else {
       voff = (uint32_t)(lane * 16);
       soff = __builtin_amdgcn_readfirstlane((uint32_t)(w * ld * 8));
-      istr = __builtin_amdgcn_readfirstlane((uint32_t)(8 * ld * 8));
+      istr = __builtin_amdgcn_readfirstlane((uint32_t)(4 * ld * 8));
     }
   }
-  // K tile starting at k0, inside the rows and K: four 1 KiB DMA instructions per wave.
+  // K tile starting at k0, inside the rows and K.
   __device__ __forceinline__ void dma(char* dst, int64_t k0, int w) const {
     const char* corner = (const char*)(X + (LAY == 0 ? r0 * ld + k0 : k0 * ld + r0));
     const __amdgpu_buffer_rsrc_t rs = fast::make_rsrc(corner, 0xFFFFFFFFu);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (8 * i + w) * 1024), 16, voff,
+    for (int i = 0; i < DMA_I; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (NWAVE * i + w) * 1024), 16, voff,
                                                soff + (uint32_t)i * istr, 0, 0);
   }
   // Any K tile: element by element, zeros outside the rows and K, stored with ds_write.
-  // Element p of thread t: LAY 0 (r, k) = ((t >> 5) + 16 p, t & 31); LAY 1 (t & 127, (t >> 7) + 4 p).
+  // Element p of thread t: LAY 0 (r, k) = ((t >> 4) + 16 p, t & 15); LAY 1 (t & 127, (t >> 7) + 2 p).
   __device__ __forceinline__ void checked(char* dst, int64_t k0, int tid) const {
     double v[PT];
 #pragma unroll
     for (int p = 0; p < PT; ++p) {
-      const int r = LAY == 0 ? (tid >> 5) + 16 * p : tid & 127;
-      const int k = LAY == 0 ? tid & 31 : (tid >> 7) + 4 * p;
+      const int r = LAY == 0 ? (tid >> 4) + 16 * p : tid & 127;
+      const int k = LAY == 0 ? tid & 15 : (tid >> 7) + 2 * p;
       const int64_t gr = r0 + r, gk = k0 + k;
       v[p] = (gr < rows && gk < K) ? X[LAY == 0 ? gr * ld + gk : gk * ld + gr] : 0.0;
     }
 #pragma unroll
     for (int p = 0; p < PT; ++p) {
-      const int r = LAY == 0 ? (tid >> 5) + 16 * p : tid & 127;
-      const int k = LAY == 0 ? tid & 31 : (tid >> 7) + 4 * p;
+      const int r = LAY == 0 ? (tid >> 4) + 16 * p : tid & 127;
+      const int k = LAY == 0 ? tid & 15 : (tid >> 7) + 2 * p;
       *(double*)(dst + lds_elem<LAY>(r, k)) = v[p];
     }
   }
 };
 
-// Fragment reads of one operand for pair h: lane row (column) base rb, groups of
-// 16 rows (A, stride 16) or 4 columns (B, stride 4).
+// Fragment reads of one operand for pair h: lane row (column) rb, then groups of 16
+// rows (A: STRIDE 16) or 4 columns (B: STRIDE 4).  For LAY 0 the swizzle term of
+// group q depends on q mod VAR (VAR = 1 for A, 4 for B).
 template <int LAY, int N, int STRIDE>
 struct Frags {
-  int base[4][2];  // LAY 0: per h and parity of the group index; LAY 1: per h
+  static constexpr int VAR = LAY == 0 && STRIDE == 4 ? 4 : 1;
+  int base[2][VAR];
   __device__ __forceinline__ void init(int rb, int g) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int par = 0; par < 2; ++par) {
-        const int r = rb + par * STRIDE;
-        base[h][par] = LAY == 0 ? rb * 256 + (((4 * g + h) ^ (r & 7)) << 4) : (8 * g + 2 * h) * 1024 + rb * 8;
+      for (int v = 0; v < VAR; ++v) {
+        const int r = rb + v * STRIDE;
+        base[h][v] = LAY == 0 ? rb * 128 + (((2 * g + h) ^ (r >> 1)) & 7) * 16 : (4 * g + 2 * h) * 1024 + rb * 8;
       }
   }
-  __device__ __forceinline__ void read(const char* op, int h, f64x2 (&x)[N]) const {
+  // groups [Q0, Q0 + NQ)
+  template <int Q0, int NQ>
+  __device__ __forceinline__ void read(const char* op, int h, f64x2 (&x)[NQ]) const {
 #pragma unroll
-    for (int q = 0; q < N; ++q) {
+    for (int j = 0; j < NQ; ++j) {
+      const int q = Q0 + j;
       if constexpr (LAY == 0) {
-        x[q] = *(const f64x2*)(op + base[h][q & 1] + q * STRIDE * 256);
+        x[j] = *(const f64x2*)(op + base[h][q % VAR] + q * STRIDE * 128);
       } else {
         const char* a = op + base[h][0] + q * STRIDE * 8;
-        x[q][0] = *(const double*)a;
-        x[q][1] = *(const double*)(a + 1024);
+        x[j][0] = *(const double*)a;
+        x[j][1] = *(const double*)(a + 1024);
       }
     }
   }
 };
 
 template <int LA, int LB>
-__global__ __launch_bounds__(THREADS) void dgemm_kernel(F64Args p) {
+__global__ __launch_bounds__(THREADS, 2) void dgemm_kernel(F64Args p) {
   __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
   int tm, tn;
   fast::tile_coords<8>(p.tiles_m, p.tiles_n, tm, tn);
@@ -174,6 +183,7 @@ __global__ __launch_bounds__(THREADS) void dgemm_kernel(F64Args p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = (w & 1) * WM, wn = (w >> 1) * WN;
+  static_assert(2 * WM == BM && 2 * WN == BN, "2 x 2 waves");
 
   // K range of this workgroup (grid.y > 1: split K)
   const int64_t nk_all = (p.K + BK - 1) / BK;
@@ -199,17 +209,26 @@ __global__ __launch_bounds__(THREADS) void dgemm_kernel(F64Args p) {
 
   auto compute = [&](const char* st) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      f64x2 a[FM], b[FN];
-      fa.read(st, h, a);
-      fb.read(st + OP_BYTES, h, b);
+    for (int h = 0; h < 2; ++h) {
+      f64x2 a[FM];
+      fa.template read<0, FM>(st, h, a);
+      // B in two halves of FN / 2 column groups keeps the fragment registers low
+      auto half = [&](auto hb) {
+        constexpr int C0 = decltype(hb)::value * (FN / 2);
+        f64x2 b[FN / 2];
+        fb.template read<C0, FN / 2>(st + OP_BYTES, h, b);
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
+        for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int f = 0; f < FM; ++f)
+          for (int f = 0; f < FM; ++f)
 #pragma unroll
-          for (int c = 0; c < FN; ++c)
-            acc[f][c] = __builtin_amdgcn_mfma_f64_4x4x4f64(a[f][e], b[c][e], acc[f][c], 0, 0, 0);
+            for (int c = 0; c < FN / 2; ++c)
+              acc[f][C0 + c] = __builtin_amdgcn_mfma_f64_4x4x4f64(a[f][e], b[c][e], acc[f][C0 + c], 0, 0, 0);
+      };
+      half(std::integral_constant<int, 0>());
+      __builtin_amdgcn_sched_barrier(0);  // keep the second half's reads behind the first half
+      half(std::integral_constant<int, 1>());
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto checked = [&](char* st, int64_t k0) {
@@ -218,15 +237,13 @@ __global__ __launch_bounds__(THREADS) void dgemm_kernel(F64Args p) {
   };
 
   if (p.dma_ok && m0 + BM <= p.M && n0 + BN <= p.N) {
-    // tiles inside M and N: DMA for every K tile inside K, the checked path for the tail
-    auto fill = [&](char* st, int64_t t) {
-      const int64_t k0 = kbeg + t * BK;
-      if (k0 + BK <= p.K) {
-        oa.dma(st, k0, w);
-        ob.dma(st + OP_BYTES, k0, w);
-      } else {
-        checked(st, k0);
-      }
+    // tiles inside M and N: DMA for the K tiles inside K; a K tile crossing the end of K
+    // (the last one of the last range) follows the loop, loaded by the checked path
+    const int64_t kfull = (p.K - kbeg) / BK;
+    const int64_t nfull = kfull < nk ? kfull : nk;
+    auto dma = [&](char* st, int64_t t) {
+      oa.dma(st, kbeg + t * BK, w);
+      ob.dma(st + OP_BYTES, kbeg + t * BK, w);
     };
     // the DMA writes of a wave are complete once its vmcnt drains; the barrier then
     // publishes the stage to every wave
@@ -236,17 +253,23 @@ __global__ __launch_bounds__(THREADS) void dgemm_kernel(F64Args p) {
     };
     auto step = [&](auto stage, int64_t t) {
       constexpr int S = decltype(stage)::value;
-      if (t + 1 < nk) fill(lds + (1 - S) * STAGE, t + 1);
+      if (t + 1 < nfull) dma(lds + (1 - S) * STAGE, t + 1);
       compute(lds + S * STAGE);
       publish();
     };
-    if (nk > 0) {
-      fill(lds, 0);
+    if (nfull > 0) {
+      dma(lds, 0);
       publish();
     }
-    for (int64_t t = 0; t < nk; t += 2) {
+    for (int64_t t = 0; t < nfull; t += 2) {
       step(std::integral_constant<int, 0>(), t);
-      if (t + 1 < nk) step(std::integral_constant<int, 1>(), t + 1);
+      if (t + 1 < nfull) step(std::integral_constant<int, 1>(), t + 1);
+    }
+    if (nfull < nk) {
+      char* st = lds + (nfull & 1) * STAGE;  // last read before the previous barrier
+      checked(st, kbeg + nfull * BK);
+      __syncthreads();
+      compute(st);
     }
   } else {
     // edge tiles: one stage, checked loads
@@ -306,10 +329,10 @@ static void launch_tiles(const F64Args& a, int splits, hipStream_t s) {
 }
 
 // DMA path: 16-byte aligned rows (base and leading dimension) and every offset of a
-// tile from its corner in 32 bits: at most (127 ld + 31) * 8 (K-contiguous) or
-// (31 ld + 127) * 8 (MN-contiguous), plus 16 bytes.
+// tile from its corner in 32 bits: at most (127 ld + 15) * 8 (K-contiguous) or
+// (15 ld + 127) * 8 (MN-contiguous), plus 16 bytes.
 static bool f64_dma_ok(int lay, const double* X, int64_t ld) {
-  const int64_t span = lay == 0 ? (127 * ld + 31) * 8 : (31 * ld + 127) * 8;
+  const int64_t span = lay == 0 ? (127 * ld + 15) * 8 : (15 * ld + 127) * 8;
   return ((uintptr_t)X % 16) == 0 && ld % 2 == 0 && span + 16 < ((int64_t)0xFFFFFFFF);
 }
 

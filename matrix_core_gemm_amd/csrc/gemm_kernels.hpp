@@ -67,20 +67,21 @@ struct F64Args {
   int64_t lda, ldb, ldc;  // elements
   double alpha, beta;
   int use_c;              // beta != 0: C is read
-  int kt_per_split;       // K tiles of 32 per workgroup range (filled by the launcher)
+  int kt_per_split;       // K tiles of 16 per workgroup range (filled by the launcher)
   int dma_ok;             // operands fit the HBM -> LDS DMA path (filled by the launcher)
   int tiles_m, tiles_n;   // filled by the launcher
 };
 
 struct F64Plan {
   int splits;        // >1: K split over grid.y, partial sums added into D with atomics
-  int kt_per_split;  // K tiles of 32 per range
+  int kt_per_split;  // K tiles of 16 per range
 };
 
-// Split-K cost model of the binary64 kernel (microseconds; gfx950, 256 CUs).
-constexpr int64_t F64_NUM_CU = 256;
-constexpr int64_t F64_SPLIT_MIN_KT = 8;   // at least 256 K values per range
-constexpr double F64_KT_US = 3.6;         // one K tile (32) of a resident 128 x 128 tile
+// Split-K cost model of the binary64 kernel (microseconds; gfx950, 256 CUs with two
+// resident workgroups each).
+constexpr int64_t F64_NUM_CU = 512;       // resident 128 x 128 tiles
+constexpr int64_t F64_SPLIT_MIN_KT = 16;  // at least 256 K values per range
+constexpr double F64_KT_US = 3.4;         // one K tile (16) of a resident tile, two per CU
 constexpr double F64_ROUND_US = 3.0;      // per wave of resident tiles (prologue, epilogue)
 constexpr double F64_ATOMIC_US = 1.4e-5;  // per atomic add of a partial sum
 constexpr double F64_SPLIT_US = 5.0;      // zeroing D and the extra launch
