@@ -12,6 +12,7 @@ full-size synthetic workload (8192^3 for every GEMM):
   gemm_dense  bf16 x bf16 -> bf16  (C and D in bfloat16, alpha = beta = 1)
   gemm_dense  skinny bf16 32768 x 16 x 8192 and 16 x 32768 x 8192 (C absent): HBM-bound
   gemm_sparse24 int8 (2:4 A) x int8 -> i32 and e4m3 (2:4 A) x e4m3 -> f32 (C absent)
+  gemm_dense  f64  x f64  -> f64   (binary64, A row-major, B column-major, C ~ N(0,1), alpha = beta = 1)
 Each call is bracketed by HIP events on the stream it is launched on, so every
 kernel's average duration is measured live.  `value` is the dense bf16 8192^3
 rate (TFLOP/s); the per-dtype rates the metric asks for are in `per_dtype`.
@@ -32,7 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "TFLOP/s (TOPS int8) at 8192³ per dtype + % of MI355X MFMA peak"
 # MI355X published dense peaks (TFLOP/s or TOPS) and HBM bandwidth (GB/s)
-PEAK = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "i8": 5000.0}
+PEAK = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "i8": 5000.0, "f64": 78.6}
 HBM_PEAK_GBS = 8000.0
 
 # HBM bytes per launch of the dense bf16 8192^3 kernel, from two rocprofv3 --pmc
@@ -41,8 +42,8 @@ HBM_PEAK_GBS = 8000.0
 # with: when the hash of those sources differs, traffic is reported as null.
 KERNEL_SOURCES = ("gemm_fast.hip", "fast_tiles.hpp", "arch_gfx950.hpp", "gemm_kernels.hpp")
 TRAFFIC_MEASURED = {
-    "sources_sha256": "66b3636f929162bb44e5c897322d655656f815a36b1c00c99b95ed520fce9071",
-    "read_bytes": 1802 * 2**20, "write_bytes": 277 * 2**20,
+    "sources_sha256": "2d97937a0595142f2e73cbc1e34fea53b7816685b838926766ea8d0acd0cda65",
+    "read_bytes": 1808 * 2**20, "write_bytes": 276 * 2**20,
 }
 
 
@@ -132,6 +133,11 @@ def main():
     Wide = torch.randn((SK[0], K), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
     Narrow = torch.randn((SK[1], K), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
     Dsk = torch.empty((SK[0], SK[1]), dtype=torch.float32, device="cuda")
+    # binary64 operands ~ N(0,1), drawn on the device
+    A64 = torch.randn((M, K), generator=g, dtype=torch.float64, device="cuda")
+    B64 = torch.randn((N, K), generator=g, dtype=torch.float64, device="cuda")  # column-major K x N
+    C64 = torch.randn((M, N), generator=g, dtype=torch.float64, device="cuda")
+    D64 = torch.empty((M, N), dtype=torch.float64, device="cuda")
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s")
 
@@ -170,12 +176,14 @@ def main():
         elif name == "skinny_n16":  # A = Wide (M = 4n), B = Narrow (N = 16, column-major)
             mcg.gemm_dense("bf16", "bf16", 0, 0, SK[0], SK[1], K, Wide, K, Narrow, K, None, Dsk, SK[1],
                            "f32", 1.0, 0.0, stream=s)
+        elif name == "f64":
+            mcg.gemm_dense("f64", "f64", 0, 0, M, N, K, A64, K, B64, K, C64, D64, N, "f64", 1.0, 1.0, stream=s)
         elif name == "skinny_m16":  # A = Narrow (M = 16), B = Wide (N = 4n, column-major)
             mcg.gemm_dense("bf16", "bf16", 0, 0, SK[1], SK[0], K, Narrow, K, Wide, K, None, Dsk, SK[0],
                            "f32", 1.0, 0.0, stream=s)
 
     names = ["bf16", "f16", "i8", "e4m3xe4m3", "e4m3xe5m2", "compress24", "sparse24", "bf16_out",
-             "skinny_n16", "skinny_m16", "sparse24_i8", "sparse24_e4m3"]
+             "skinny_n16", "skinny_m16", "sparse24_i8", "sparse24_e4m3", "f64"]
     if args.only:
         keep = set(args.only.split(","))
         names = [x for x in names if x in keep or x == "compress24" and "sparse24" in keep]
