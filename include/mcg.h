@@ -120,7 +120,10 @@ typedef enum {
  *                 widened exactly to bfloat16 and multiplied on the bfloat16
  *                 instructions.  Binary64 results stay within
  *                 4*2^-53*(K+2)*|alpha|*sum|a*b| + 2^-53*|D| of the exact value
- *                 (plus 2^-53*|beta*c| when beta is not 0 or +-1).
+ *                 (plus 2^-53*|beta*c| when beta is not 0 or +-1); unless K is
+ *                 split they are deterministic: the FP64 instructions are
+ *                 chains of correctly rounded binary64 fused multiply-adds
+ *                 (measured), applied in a fixed K order.
  * Alignment     : none beyond the element size (binary64 operands take the
  *                 same path at any leading dimension); 16-byte aligned
  *                 pointers and leading
@@ -245,20 +248,25 @@ int mcg_sparse24_path(int dtypeA, int layoutB, int64_t M, int64_t N, int64_t K, 
  * Eq. (1): d = sum_l a_l b_l + c for one output element; Section 3: targeted
  * and randomised test vectors).
  *
- * dtype  : MCG_BF16, MCG_F16, MCG_FP8_E4M3 or MCG_FP8_E5M2 (a and b alike).
- * shape  : 16 (mfma_f32_16x16x32_{bf16,f16}, mfma_scale_f32_16x16x128_f8f6f4)
- *          or 32 (mfma_f32_32x32x16_{bf16,f16}, mfma_scale_f32_32x32x64_f8f6f4).
+ * dtype  : MCG_BF16, MCG_F16, MCG_FP8_E4M3 or MCG_FP8_E5M2 (a and b alike),
+ *          or MCG_F64 (the FP64-accumulate builtins of "CDNA3 dense MFMA
+ *          builtins").
+ * shape  : 16 (mfma_f32_16x16x32_{bf16,f16}, mfma_scale_f32_16x16x128_f8f6f4,
+ *          mfma_f64_16x16x4f64) or 32 (mfma_f32_32x32x16_{bf16,f16},
+ *          mfma_scale_f32_32x32x64_f8f6f4); for MCG_F64 also 4 (block 0 of
+ *          mfma_f64_4x4x4f64).
  * a, b   : DEVICE arrays of n * k element codes, k = mcg_mfma_eval_k(dtype,
  *          shape); test vector t is a[t*k .. t*k + k) and b[t*k .. t*k + k).
  *          Element l goes to operand slot l: lane group g holds slots
  *          [g*E, (g+1)*E) in register order (E = 8 for 16-bit, 32 for fp8
- *          elements per lane).
- * c, d   : DEVICE arrays of n floats: c[t] is accumulator element (0, 0) of
- *          test t, d[t] receives result element (0, 0).  All other operand
- *          elements are zero.
+ *          elements per lane; for MCG_F64 slot l is the K index l, k = 4).
+ * c, d   : DEVICE arrays of n accumulator elements (float; double for
+ *          MCG_F64): c[t] is accumulator element (0, 0) of test t, d[t]
+ *          receives result element (0, 0).  All other operand elements are
+ *          zero.
  * Returns an mcg_status; asynchronous on stream.
  */
-int mcg_mfma_eval(int dtype, int shape, int64_t n, const void* a, const void* b, const float* c, float* d,
+int mcg_mfma_eval(int dtype, int shape, int64_t n, const void* a, const void* b, const void* c, void* d,
                   void* stream);
 /* Elements per test vector for mcg_mfma_eval (0 if unsupported). */
 int mcg_mfma_eval_k(int dtype, int shape);

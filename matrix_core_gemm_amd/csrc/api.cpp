@@ -388,21 +388,23 @@ const char* mcg_status_string(int status) {
   }
 }
 
-int mcg_mfma_eval_k(int dtype, int shape) { return mcg::mfma_eval_k(dtype, shape); }
+int mcg_mfma_eval_k(int dtype, int shape) { return mcg::mfma_eval_k(dtype == MCG_F64 ? mcg::DT_F64 : dtype, shape); }
 
-int mcg_mfma_eval(int dtype, int shape, int64_t n, const void* a, const void* b, const float* c, float* d,
+int mcg_mfma_eval(int dtype, int shape, int64_t n, const void* a, const void* b, const void* c, void* d,
                   void* stream) {
-  const int k = mcg::mfma_eval_k(dtype, shape);
+  const int k = mcg::mfma_eval_k(dtype == MCG_F64 ? mcg::DT_F64 : dtype, shape);
   if (k == 0) return MCG_ERR_UNSUPPORTED_DTYPE;
   if (n < 0 || n > ((int64_t)1 << 31)) return MCG_ERR_INVALID_SIZE;
   if (n == 0) return MCG_SUCCESS;
   if (!a || !b || !c || !d) return MCG_ERR_NULL_POINTER;
-  if (!aligned_to(a, elem_bytes(dtype)) || !aligned_to(b, elem_bytes(dtype)) || !aligned_to(c, 4) ||
-      !aligned_to(d, 4))
+  const int acc_bytes = dtype == MCG_F64 ? 8 : 4;
+  if (!aligned_to(a, elem_bytes(dtype)) || !aligned_to(b, elem_bytes(dtype)) || !aligned_to(c, acc_bytes) ||
+      !aligned_to(d, acc_bytes))
     return MCG_ERR_MISALIGNED;
   int st = check_arch();
   if (st != MCG_SUCCESS) return st;
-  return hip_status(mcg::launch_mfma_eval(dtype, shape, a, b, c, d, n, (hipStream_t)stream));
+  return hip_status(
+      mcg::launch_mfma_eval(dtype == MCG_F64 ? mcg::DT_F64 : dtype, shape, a, b, c, d, n, (hipStream_t)stream));
 }
 
 int mcg_version(void) { return kVersion; }

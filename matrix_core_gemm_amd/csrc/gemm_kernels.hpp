@@ -57,7 +57,8 @@ struct SparseArgs {
   int tiles_m, tiles_n;
 };
 
-// binary64 GEMM (DGEMM)
+// binary64 GEMM (DGEMM); DT_F64 continues the input codes of arch_gfx950.hpp
+constexpr int DT_F64 = 7;
 struct F64Args {
   const double* A;
   const double* B;
@@ -125,7 +126,7 @@ bool sparse_fast_ok(int dtA, int layoutB, const SparseArgs& a);
 hipError_t launch_sparse_fast(int dtA, int dtB, int layoutB, const SparseArgs& a, hipStream_t s);
 hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s);
 int mfma_eval_k(int dt, int shape);
-hipError_t launch_mfma_eval(int dt, int shape, const void* a, const void* b, const float* c, float* d,
+hipError_t launch_mfma_eval(int dt, int shape, const void* a, const void* b, const void* c, void* d,
                             int64_t n, hipStream_t s);
 
 }  // namespace mcg

@@ -5,7 +5,8 @@
 // characterises a matrix core by the single output element
 //     d = sum_{l=1..k} a_l b_l + c
 // of one instruction, fed with targeted and with randomised test vectors.
-// mcg_mfma_eval runs exactly that on gfx950: test vector t places a[t*k ..]
+// mcg_mfma_eval runs exactly that on gfx950 (and on the FP64 instructions, "CDNA3
+// dense MFMA builtins", FP64-accumulate builtins): test vector t places a[t*k ..]
 // in row 0 of the instruction's A operand, b[t*k ..] in column 0 of its B
 // operand and c[t] in element (0, 0) of its accumulator input (everything
 // else zero) and returns element (0, 0) of the result.  Element l of a test
@@ -98,6 +99,34 @@ __global__ __launch_bounds__(256) void mfma_eval_kernel(const unsigned char* a, 
   if (lane == 0) d[t] = out;
 }
 
+// Binary64: SHAPE 16 is v_mfma_f64_16x16x4_f64, SHAPE 4 block 0 of v_mfma_f64_4x4x4_4b_f64.
+// Row 0 of A (block 0) and column 0 of B sit in lanes 16k (K index k = 0..3) for both, and
+// result element (0, 0) in lane 0, register 0.
+template <int SHAPE>
+__global__ __launch_bounds__(256) void mfma_eval_f64_kernel(const double* a, const double* b, const double* c,
+                                                            double* d, int64_t n) {
+  typedef double f64x4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= n) return;  // whole wavefronts leave together
+  double av = 0.0, bv = 0.0;
+  if ((lane & 15) == 0) {
+    av = a[t * 4 + (lane >> 4)];
+    bv = b[t * 4 + (lane >> 4)];
+  }
+  double out;
+  if constexpr (SHAPE == 16) {
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+    if (lane == 0) acc[0] = c[t];
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+    out = acc[0];
+  } else {
+    double acc = lane == 0 ? c[t] : 0.0;
+    out = __builtin_amdgcn_mfma_f64_4x4x4f64(av, bv, acc, 0, 0, 0);
+  }
+  if (lane == 0) d[t] = out;
+}
+
 template <int KIND>
 static hipError_t launch_kind(int shape, const void* a, const void* b, const float* c, float* d, int64_t n,
                               hipStream_t s) {
@@ -114,19 +143,32 @@ static hipError_t launch_kind(int shape, const void* a, const void* b, const flo
 }  // namespace numerics
 
 int mfma_eval_k(int dt, int shape) {
+  if (dt == DT_F64) return shape == 16 || shape == 4 ? 4 : 0;
   const bool f8 = dt == DT_E4M3 || dt == DT_E5M2;
   if ((dt < DT_BF16 || dt > DT_E5M2) || dt == DT_I8 || (shape != 16 && shape != 32)) return 0;
   return f8 ? (shape == 16 ? 128 : 64) : (shape == 16 ? 32 : 16);
 }
 
-hipError_t launch_mfma_eval(int dt, int shape, const void* a, const void* b, const float* c, float* d,
+hipError_t launch_mfma_eval(int dt, int shape, const void* a, const void* b, const void* c, void* d,
                             int64_t n, hipStream_t s) {
   using namespace numerics;
   if (n <= 0) return hipSuccess;
-  if (dt == DT_BF16) return launch_kind<0>(shape, a, b, c, d, n, s);
-  if (dt == DT_F16) return launch_kind<1>(shape, a, b, c, d, n, s);
-  if (dt == DT_E4M3) return launch_kind<2>(shape, a, b, c, d, n, s);
-  return launch_kind<3>(shape, a, b, c, d, n, s);
+  if (dt == DT_F64) {
+    const dim3 grid((unsigned)((n + 3) / 4));
+    if (shape == 16)
+      hipLaunchKernelGGL(mfma_eval_f64_kernel<16>, grid, dim3(256), 0, s, (const double*)a, (const double*)b,
+                         (const double*)c, (double*)d, n);
+    else
+      hipLaunchKernelGGL(mfma_eval_f64_kernel<4>, grid, dim3(256), 0, s, (const double*)a, (const double*)b,
+                         (const double*)c, (double*)d, n);
+    return hipGetLastError();
+  }
+  const float* cf = (const float*)c;
+  float* df = (float*)d;
+  if (dt == DT_BF16) return launch_kind<0>(shape, a, b, cf, df, n, s);
+  if (dt == DT_F16) return launch_kind<1>(shape, a, b, cf, df, n, s);
+  if (dt == DT_E4M3) return launch_kind<2>(shape, a, b, cf, df, n, s);
+  return launch_kind<3>(shape, a, b, cf, df, n, s);
 }
 
 }  // namespace mcg

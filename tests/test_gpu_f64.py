@@ -8,6 +8,8 @@ with ragged M, N and K tails, all four operand layouts, odd leading
 dimensions, beta = 0 (C never read), D aliasing C, K = 0, split K (atomic
 partial sums, beta * C added after) and the full 8192^3 workload on sampled
 outputs."""
+from fractions import Fraction
+
 import numpy as np
 import pytest
 import torch
@@ -162,3 +164,54 @@ def test_f64_full_size_sampled(layA, layB):
     cols = np.concatenate([cols, ec.ravel()]).astype(np.int64)
     r, _ = run_case(mcg, layA, layB, M, N, K, alpha=1.0, beta=1.0, sample=(rows, cols))
     say(f"full size {layA}/{layB}: max |delta|/bound {r['max_ratio']:.3g}")
+
+
+def kernel_order_model(A, B, C, alpha, beta, i, j):
+    """d_ij as the binary64 kernel computes it when K is not split: its FP64 matrix
+    instructions are chains of correctly rounded fused multiply-adds in slot order
+    (tests/test_gpu_numerics.py), one accumulator per output element, fed K tile by
+    K tile (16 deep); inside a tile, lane group g supplies K index 4g + 2h + e of the
+    instruction for pair h and element e, so the K order of one tile is
+    0, 4, 8, 12, 1, 5, 9, 13, 2, 6, 10, 14, 3, 7, 11, 15.  Then alpha * acc is rounded
+    and beta * c added with one fused multiply-add."""
+    K = A.shape[1]
+    acc = 0.0
+    for t in range(0, K, 16):
+        for h in range(2):
+            for e in range(2):
+                for g in range(4):
+                    k = t + 4 * g + 2 * h + e
+                    if k < K:
+                        acc = float(Fraction(float(A[i, k])) * Fraction(float(B[k, j])) + Fraction(acc))
+                    # k >= K: the tile holds zeros there, and fma(0, 0, acc) = acc
+    v = alpha * acc
+    if beta != 0.0:
+        v = float(Fraction(beta) * Fraction(float(C[i, j])) + Fraction(v))
+    return v
+
+
+@pytest.mark.parametrize("layA,layB", [("k_contig", "k_contig"), ("mn_contig", "k_contig"), ("k_contig", "mn_contig"),
+                                       ("mn_contig", "mn_contig")])
+def test_f64_bit_exact_against_instruction_model(layA, layB):
+    """Unsplit results equal, bit for bit, the kernel's order of binary64 fused
+    multiply-adds built from the measured instruction model, on tile edges and
+    random outputs of a 2 x 2-tile problem with a ragged K tail (and the edge
+    tiles' checked loads)."""
+    mcg = need_gpu()
+    M, N, K = 150, 140, 45
+    alpha, beta = 1.25, -0.75
+    A, B = operands(layA, layB, M, N, K, seed=3)
+    C = W.c_matrix(M, N, "normal", seed=93, dtype="f64")
+    D = torch.full((M, N), float("nan"), dtype=torch.float64, device="cuda")
+    assert mcg.dense_splits("f64", layA, layB, M, N, K, dev(A.codes), A.ld, dev(B.codes), B.ld, None, D, "f64",
+                            beta) == 1
+    mcg.gemm_dense("f64", "f64", layA, layB, M, N, K, dev(A.codes), A.ld, dev(B.codes), B.ld, dev(C), D, N, "f64",
+                   alpha, beta)
+    torch.cuda.synchronize()
+    d = D.cpu().numpy()
+    Al = A.codes[:M, :K] if layA == "k_contig" else A.codes[:K, :M].T
+    Bl = B.codes[:N, :K].T if layB == "k_contig" else B.codes[:K, :N]
+    rows, cols = W.sample_coords(M, N, 400, full_rows=(0, 127, 128, M - 1), full_cols=(127,))
+    bad = [(i, j) for i, j in zip(rows, cols) if d[i, j] != kernel_order_model(Al, Bl, C, alpha, beta, i, j)]
+    say(f"{layA}/{layB}: {len(bad)} of {len(rows)} outputs differ from the instruction-order model")
+    assert not bad, bad[:5]
