@@ -27,6 +27,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-Wno-unused-command-line-argument"]
 
 
+# Per-file device flags.  The binary64 kernel keeps its MFMA accumulators in VGPRs:
+# with the default AGPR form the compiler copies them between register files around
+# the K loop, which costs a third of the FP64 matrix rate.
+EXTRA = {"gemm_f64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _needs(obj: str, src: str) -> bool:
     if not os.path.exists(obj):
         return True
@@ -44,7 +50,7 @@ def build(force: bool = True, verbose: bool = False) -> str:
         obj = os.path.join(BUILD, s + ".o")
         objs.append(obj)
         if force or _needs(obj, src):
-            cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+            cmd = [HIPCC, *COMMON, *EXTRA.get(s, []), "-c", src, "-o", obj]
             if s.endswith(".hip"):
                 cmd[1:1] = ["-x", "hip"]
             if verbose:

@@ -4,22 +4,16 @@
 // by the FP64-accumulate matrix instructions ("CDNA3 dense MFMA builtins",
 // FP64-accumulate builtins; the accumulator layouts of the 4x4 FP64 tile shape).
 //
-// Instruction.  gfx950 issues the four-block 4x4x4 FP64 instruction at full rate
-// (16 cycles; 75.5 TFLOP/s over the chip, measured), while the one-block 16x16x4
-// FP64 instruction reaches only about 49 TFLOP/s (about 100 cycles per
-// instruction per SIMD, measured).  The broadcast modifiers (cbsz/abid) leave the
-// FP64 instructions of gfx950 unchanged (measured), so each of the four blocks
-// takes its own A and B.  Operand and result lanes (measured; D as the pages' 4x4
-// FP64 layout):
-//   A_b[i][k] in lane i + 4b + 16k,  B_b[k][j] in lane j + 4b + 16k,
-//   D_b[i][j] in lane 16i + 4b + j          (i, j, k, b in 0..3).
-// The kernel gives the four blocks four different groups of 4 rows of A and the
-// same 4 columns of B, so one instruction is a 16 x 4 x 4 product: A lane l holds
-// row (l & 15) at K index l >> 4, B lane l holds column (l & 3) at K index l >> 4,
-// and result lane l holds row 4((l >> 2) & 3) + (l >> 4), column l & 3.  No
-// accumulator is redundant and no cross-lane reduction is needed.
+// Instruction.  v_mfma_f64_16x16x4_f64 (one 16 x 16 x 4 block; 64 cycles) runs at
+// 78.0 TFLOP/s over the chip in a register-only loop (measured, 99% of the peak),
+// against 73-75 for the four-block 4x4x4 one, and reads a quarter of the operand
+// bytes per flop.  The compiler's default form keeps MFMA accumulators in AGPRs and
+// copies them to and from VGPRs around loops (about 49 TFLOP/s for the same loop);
+// this file is built with the VGPR form.  Operand and result lanes (measured; D as
+// the pages' 16 x 16 FP64 layout): A[i][k] in lane i + 16k, B[k][j] in lane j + 16k,
+// D[i][j] in lane 16 (i mod 4) + j, register pair i / 4.
 //
-// Tiling.  128 x 128 output tiles, 4 waves of 64 x 64 (4 x 16 instructions per K
+// Tiling.  128 x 128 output tiles, 4 waves of 64 x 64 (4 x 4 instructions per K
 // index group), K in tiles of 16, two LDS stages of 32 KiB; two workgroups share
 // a CU, so each SIMD holds waves of two workgroups whose barriers and tile starts
 // do not coincide and one keeps the matrix core busy while the other waits.  Lane
@@ -37,14 +31,17 @@
 //
 // Loads.  The FP64 matrix instructions leave no issue slots to vector ALU work
 // (the pages' throughput table lists no co-execution for them), so the steady
-// state keeps both registers and vector arithmetic out of the loads: tiles inside
-// M and N move HBM -> LDS by buffer_load ... lds (16 bytes per lane, 1 KiB per wave
-// instruction) from a scalar descriptor at the tile's corner, with one fixed
-// per-lane offset and scalar offsets per instruction, into the stage the previous
-// tile is not using; the swizzle is applied on the global side (each lane fetches
-// the chunk that belongs at its LDS position).  A K tile that crosses the end of K
-// and every tile crossing the edge of M or N are loaded element by element with
-// bounds checks (zeros outside) and stored with ds_write.
+// state keeps both registers and vector arithmetic out of the loads: K tiles move
+// HBM -> LDS by buffer_load ... lds (16 bytes per lane, 1 KiB per wave instruction)
+// from a scalar descriptor at the tile's corner, with fixed per-lane offsets, into
+// the stage the previous tile is not using; the swizzle is applied on the global
+// side (each lane fetches the chunk that belongs at its LDS position).  In the last
+// tiles of M or N, lanes whose rows lie past the matrix fetch a valid row instead
+// (those rows only feed outputs that are not stored).  A K tile that crosses the end
+// of K is loaded element by element with bounds checks (zeros outside) and stored
+// with ds_write; so is every tile of operands that do not suit the DMA (unaligned
+// rows, very large leading dimensions) and the last tile of an MN-contiguous operand
+// whose valid width is odd (a 16-byte pair would cross the edge).
 //
 // Split K (few output tiles, long K): grid.y ranges of K tiles; the ranges add
 // alpha * partial into a zeroed D with binary64 atomic adds, and beta * C is added
@@ -60,7 +57,7 @@ namespace f64 {
 
 constexpr int BM = 128, BN = 128, BK = 16, THREADS = 256, NWAVE = 4;
 constexpr int WM = 64, WN = 64;            // wave tile
-constexpr int FM = WM / 16, FN = WN / 4;   // instructions per K index group: FM x FN
+constexpr int FM = WM / 16, FN = WN / 16;  // instructions per K index group: FM x FN
 constexpr int OP_BYTES = BM * BK * 8;      // 16 KiB: one operand's tile
 constexpr int STAGE = 2 * OP_BYTES;        // A then B
 constexpr int DMA_I = OP_BYTES / 1024 / NWAVE;  // 1 KiB DMA instructions per wave and operand
@@ -89,9 +86,12 @@ struct Operand {
   //   LAY 0: rows 32i + 8w + (l >> 3); lane l's LDS position l & 7 takes global chunk
   //          (l & 7) ^ ((row >> 1) & 7) of that row
   //   LAY 1: K row 4i + w; lane l takes values 2l, 2l + 1 of it
-  uint32_t voff;  // per lane
-  uint32_t soff;  // per wave, instruction 0
-  uint32_t istr;  // per instruction
+  // Rows past the edge of the matrix (last tiles of M or N) fetch the last valid row
+  // (LAY 0) or the tile's first pair (LAY 1) instead: they only feed rows (columns)
+  // of D that are not stored.
+  uint32_t voff[DMA_I];  // per lane and instruction (LAY 1: instruction 0 only)
+  uint32_t soff;         // LAY 1: per wave, instruction 0
+  uint32_t istr;         // LAY 1: per instruction
 
   __device__ __forceinline__ void init(const double* X_, int64_t ld_, int64_t r0_, int64_t rows_, int64_t K_,
                                        int w, int lane) {
@@ -100,14 +100,19 @@ struct Operand {
     rows = rows_;
     K = K_;
     r0 = r0_;
+    const int64_t valid = rows - r0;  // rows of this tile inside the matrix (>= 1)
     if constexpr (LAY == 0) {
-      const int row = 8 * w + (lane >> 3);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
-      voff = (uint32_t)(row * ld * 8 + c * 16);
+#pragma unroll
+      for (int i = 0; i < DMA_I; ++i) {
+        const int row = 32 * i + 8 * w + (lane >> 3);
+        const int64_t src = row < valid ? row : valid - 1;
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
+        voff[i] = (uint32_t)(src * ld * 8 + c * 16);
+      }
       soff = 0;
-      istr = __builtin_amdgcn_readfirstlane((uint32_t)(32 * ld * 8));
+      istr = 0;
     } else {
-      voff = (uint32_t)(lane * 16);
+      voff[0] = (uint32_t)(2 * lane + 1 < valid ? lane * 16 : 0);
       soff = __builtin_amdgcn_readfirstlane((uint32_t)(w * ld * 8));
       istr = __builtin_amdgcn_readfirstlane((uint32_t)(4 * ld * 8));
     }
@@ -118,8 +123,8 @@ struct Operand {
     const __amdgpu_buffer_rsrc_t rs = fast::make_rsrc(corner, 0xFFFFFFFFu);
 #pragma unroll
     for (int i = 0; i < DMA_I; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (NWAVE * i + w) * 1024), 16, voff,
-                                               soff + (uint32_t)i * istr, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (NWAVE * i + w) * 1024), 16,
+                                               voff[LAY == 0 ? i : 0], soff + (uint32_t)i * istr, 0, 0);
   }
   // Any K tile: element by element, zeros outside the rows and K, stored with ds_write.
   // Element p of thread t: LAY 0 (r, k) = ((t >> 4) + 16 p, t & 15); LAY 1 (t & 127, (t >> 7) + 2 p).
@@ -142,11 +147,10 @@ struct Operand {
 };
 
 // Fragment reads of one operand for pair h: lane row (column) rb, then groups of 16
-// rows (A: STRIDE 16) or 4 columns (B: STRIDE 4).  For LAY 0 the swizzle term of
-// group q depends on q mod VAR (VAR = 1 for A, 4 for B).
+// rows (columns).  For LAY 0 the swizzle term of group q depends on q mod VAR.
 template <int LAY, int N, int STRIDE>
 struct Frags {
-  static constexpr int VAR = LAY == 0 && STRIDE == 4 ? 4 : 1;
+  static constexpr int VAR = LAY == 0 && STRIDE < 16 ? 16 / STRIDE : 1;
   int base[2][VAR];
   __device__ __forceinline__ void init(int rb, int g) {
 #pragma unroll
@@ -197,38 +201,37 @@ __global__ __launch_bounds__(THREADS, 2) void dgemm_kernel(F64Args p) {
   ob.init(p.B, p.ldb, n0, p.N, p.K, w, lane);
   const int g = lane >> 4;
   Frags<LA, FM, 16> fa;
-  Frags<LB, FN, 4> fb;
+  Frags<LB, FN, 16> fb;
   fa.init(wm + (lane & 15), g);
-  fb.init(wn + (lane & 3), g);
+  fb.init(wn + (lane & 15), g);
 
-  double acc[FM][FN];
+  typedef double f64x4 __attribute__((ext_vector_type(4)));
+  f64x4 acc[FM][FN];
 #pragma unroll
   for (int f = 0; f < FM; ++f)
 #pragma unroll
-    for (int c = 0; c < FN; ++c) acc[f][c] = 0.0;
+    for (int c = 0; c < FN; ++c) acc[f][c] = (f64x4){0.0, 0.0, 0.0, 0.0};
 
+  // fragments of pair h of the tile in stage st, and the 2 x FM x FN instructions they feed
+  auto read = [&](const char* st, int h, f64x2 (&a)[FM], f64x2 (&b)[FN]) {
+    fa.template read<0, FM>(st, h, a);
+    fb.template read<0, FN>(st + OP_BYTES, h, b);
+  };
+  auto mma = [&](const f64x2 (&a)[FM], const f64x2 (&b)[FN]) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int c = 0; c < FN; ++c)
+          acc[f][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[f][e], b[c][e], acc[f][c], 0, 0, 0);
+  };
   auto compute = [&](const char* st) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      f64x2 a[FM];
-      fa.template read<0, FM>(st, h, a);
-      // B in two halves of FN / 2 column groups keeps the fragment registers low
-      auto half = [&](auto hb) {
-        constexpr int C0 = decltype(hb)::value * (FN / 2);
-        f64x2 b[FN / 2];
-        fb.template read<C0, FN / 2>(st + OP_BYTES, h, b);
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-#pragma unroll
-          for (int f = 0; f < FM; ++f)
-#pragma unroll
-            for (int c = 0; c < FN / 2; ++c)
-              acc[f][C0 + c] = __builtin_amdgcn_mfma_f64_4x4x4f64(a[f][e], b[c][e], acc[f][C0 + c], 0, 0, 0);
-      };
-      half(std::integral_constant<int, 0>());
-      __builtin_amdgcn_sched_barrier(0);  // keep the second half's reads behind the first half
-      half(std::integral_constant<int, 1>());
-      __builtin_amdgcn_sched_barrier(0);
+      f64x2 a[FM], b[FN];
+      read(st, h, a, b);
+      mma(a, b);
     }
   };
   auto checked = [&](char* st, int64_t k0) {
@@ -236,9 +239,12 @@ __global__ __launch_bounds__(THREADS, 2) void dgemm_kernel(F64Args p) {
     ob.checked(st + OP_BYTES, k0, tid);
   };
 
-  if (p.dma_ok && m0 + BM <= p.M && n0 + BN <= p.N) {
-    // tiles inside M and N: DMA for the K tiles inside K; a K tile crossing the end of K
-    // (the last one of the last range) follows the loop, loaded by the checked path
+  // DMA unless an MN-contiguous operand's last tile ends inside a 16-byte pair
+  const bool pairs_a = LA == 0 || m0 + BM <= p.M || ((p.M - m0) & 1) == 0;
+  const bool pairs_b = LB == 0 || n0 + BN <= p.N || ((p.N - n0) & 1) == 0;
+  if (p.dma_ok && pairs_a && pairs_b) {
+    // DMA for the K tiles inside K; a K tile crossing the end of K (the last one of the
+    // last range) follows the loop, loaded by the checked path
     const int64_t kfull = (p.K - kbeg) / BK;
     const int64_t nfull = kfull < nk ? kfull : nk;
     auto dma = [&](char* st, int64_t t) {
@@ -251,15 +257,29 @@ __global__ __launch_bounds__(THREADS, 2) void dgemm_kernel(F64Args p) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     };
+    // Fragments are read one pair ahead of the instructions that use them: pair 1 of a
+    // tile before pair 0 is multiplied, and pair 0 of the next tile right after the
+    // barrier that publishes it, before pair 1 of this tile is multiplied; so no
+    // instruction waits for LDS.
+    f64x2 a0[FM], b0[FN], a1[FM], b1[FN];
     auto step = [&](auto stage, int64_t t) {
       constexpr int S = decltype(stage)::value;
+      const char* st = lds + S * STAGE;
       if (t + 1 < nfull) dma(lds + (1 - S) * STAGE, t + 1);
-      compute(lds + S * STAGE);
+      read(st, 1, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
       publish();
+      if (t + 1 < nfull) read(lds + (1 - S) * STAGE, 0, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
     };
     if (nfull > 0) {
       dma(lds, 0);
       publish();
+      read(lds, 0, a0, b0);
     }
     for (int64_t t = 0; t < nfull; t += 2) {
       step(std::integral_constant<int, 0>(), t);
@@ -272,7 +292,7 @@ __global__ __launch_bounds__(THREADS, 2) void dgemm_kernel(F64Args p) {
       compute(st);
     }
   } else {
-    // edge tiles: one stage, checked loads
+    // misaligned operands or odd edges: one stage, checked loads
     for (int64_t t = 0; t < nk; ++t) {
       checked(lds, kbeg + t * BK);
       __syncthreads();
@@ -281,28 +301,28 @@ __global__ __launch_bounds__(THREADS, 2) void dgemm_kernel(F64Args p) {
     }
   }
 
-  // result lane l: row 4((l >> 2) & 3) + (l >> 4), column l & 3 of each 16 x 4 piece
-  const int orow = 4 * ((lane >> 2) & 3) + (lane >> 4);
-  const int ocol = lane & 3;
+  // result register r of lane l: row 4r + (l >> 4), column l & 15 of each 16 x 16 piece
   double* D = p.D;
 #pragma unroll
-  for (int f = 0; f < FM; ++f) {
-    const int64_t row = m0 + wm + 16 * f + orow;
-    if (row >= p.M) continue;
+  for (int f = 0; f < FM; ++f)
 #pragma unroll
-    for (int c = 0; c < FN; ++c) {
-      const int64_t col = n0 + wn + 4 * c + ocol;
-      if (col >= p.N) continue;
-      const int64_t off = row * p.ldc + col;
-      if (gridDim.y > 1) {
-        atomicAdd(D + off, p.alpha * acc[f][c]);
-      } else {
-        double v = p.alpha * acc[f][c];
-        if (p.use_c) v = __builtin_fma(p.beta, p.C[off], v);
-        D[off] = v;
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = m0 + wm + 16 * f + 4 * r + (lane >> 4);
+      if (row >= p.M) continue;
+#pragma unroll
+      for (int c = 0; c < FN; ++c) {
+        const int64_t col = n0 + wn + 16 * c + (lane & 15);
+        if (col >= p.N) continue;
+        const int64_t off = row * p.ldc + col;
+        if (gridDim.y > 1) {
+          atomicAdd(D + off, p.alpha * acc[f][c][r]);
+        } else {
+          double v = p.alpha * acc[f][c][r];
+          if (p.use_c) v = __builtin_fma(p.beta, p.C[off], v);
+          D[off] = v;
+        }
       }
     }
-  }
 }
 
 // Split K, before the partial sums: D = 0 over M x N.
