@@ -29,7 +29,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
 
 # Per-file device flags.  The binary64 kernel keeps its MFMA accumulators in VGPRs:
 # with the default AGPR form the compiler copies them between register files around
-# the K loop, which costs a third of the FP64 matrix rate.
+# the K loop, which costs a third of the FP64 matrix rate.  (The other kernels were
+# measured both ways: the VGPR form gains nothing there.)
 EXTRA = {"gemm_f64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
