@@ -363,18 +363,24 @@ F64Plan plan_f64(const F64Args& a, bool can_split) {
   F64Plan plan{1, (int)((a.K + BK - 1) / BK)};
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const int64_t nk = (a.K + BK - 1) / BK;
-  if (!can_split || nk < 2 * F64_SPLIT_MIN_KT || tiles >= F64_NUM_CU) return plan;
-  // Estimated time of S ranges: waves of resident tiles times the K tiles of one range,
-  // plus the atomic adds of the partial sums and the extra launches.
+  const int64_t slots = 2 * F64_NUM_CU;
+  if (!can_split || nk < 2 * F64_SPLIT_MIN_KT || tiles >= 4 * slots) return plan;
+  // Estimated time of S ranges: full waves of resident workgroups (two per CU), then the
+  // last wave, whose workgroups run alone on their CUs when there are at most 256 of
+  // them; plus the atomic adds of the partial sums and the extra launches.
   auto cost = [&](int64_t S) {
     const int64_t per = (nk + S - 1) / S;
-    const int64_t rounds = (tiles * S + F64_NUM_CU - 1) / F64_NUM_CU;
-    return (double)rounds * (F64_KT_US * (double)per + F64_ROUND_US) +
-           F64_ATOMIC_US * (double)S * (double)a.M * (double)a.N + (S > 1 ? F64_SPLIT_US : 0.0);
+    const int64_t wgs = tiles * S;
+    const int64_t rounds = (wgs + slots - 1) / slots;
+    const int64_t last = wgs - (rounds - 1) * slots;
+    double t = (double)(rounds - 1) * (double)per * F64_KT_SHARED_US +
+               (double)per * (last <= F64_NUM_CU ? F64_KT_ALONE_US : F64_KT_SHARED_US);
+    if (S > 1) t += F64_ATOMIC_US * (double)S * (double)a.M * (double)a.N + F64_SPLIT_US;
+    return t;
   };
   int64_t best = 1;
   double best_t = cost(1);
-  for (int64_t S = 2; S <= nk / F64_SPLIT_MIN_KT && tiles * S <= 4 * F64_NUM_CU; ++S) {
+  for (int64_t S = 2; S <= nk / F64_SPLIT_MIN_KT && tiles * S <= 4 * slots; ++S) {
     const double t = cost(S);
     if (t < best_t) {
       best_t = t;

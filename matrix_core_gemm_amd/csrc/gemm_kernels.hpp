@@ -78,13 +78,14 @@ struct F64Plan {
   int kt_per_split;  // K tiles of 16 per range
 };
 
-// Split-K cost model of the binary64 kernel (microseconds; gfx950, 256 CUs with two
-// resident workgroups each).
-constexpr int64_t F64_NUM_CU = 512;       // resident 128 x 128 tiles
+// Split-K cost model of the binary64 kernel (microseconds; gfx950, 256 CUs, up to two
+// resident 128 x 128 workgroups each; fitted to forced-split timings from 1024^3 to
+// 256 x 256 x 65536).
+constexpr int64_t F64_NUM_CU = 256;
 constexpr int64_t F64_SPLIT_MIN_KT = 16;  // at least 256 K values per range
-constexpr double F64_KT_US = 3.4;         // one K tile (16) of a resident tile, two per CU
-constexpr double F64_ROUND_US = 3.0;      // per wave of resident tiles (prologue, epilogue)
-constexpr double F64_ATOMIC_US = 1.4e-5;  // per atomic add of a partial sum
+constexpr double F64_KT_ALONE_US = 2.05;  // one K tile (16) of a workgroup alone on its CU
+constexpr double F64_KT_SHARED_US = 3.4;  // the same with two workgroups sharing the CU
+constexpr double F64_ATOMIC_US = 7e-6;    // per atomic add of a partial sum (overlaps compute)
 constexpr double F64_SPLIT_US = 5.0;      // zeroing D and the extra launch
 
 // can_split: D is not C with beta != 0.
