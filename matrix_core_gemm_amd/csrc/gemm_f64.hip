@@ -39,9 +39,10 @@
 // tiles of M or N, lanes whose rows lie past the matrix fetch a valid row instead
 // (those rows only feed outputs that are not stored).  A K tile that crosses the end
 // of K is loaded element by element with bounds checks (zeros outside) and stored
-// with ds_write; so is every tile of operands that do not suit the DMA (unaligned
-// rows, very large leading dimensions) and the last tile of an MN-contiguous operand
-// whose valid width is odd (a 16-byte pair would cross the edge).
+// with ds_write; so are the last tile of an MN-contiguous operand whose valid width is
+// odd (a 16-byte pair would cross the edge) and every tile of operands with very large
+// leading dimensions.  Operands whose rows are not 16-byte aligned (odd leading
+// dimensions) load with 4-byte DMA into the same LDS images, edge tiles included.
 //
 // Split K (few output tiles, long K): grid.y ranges of K tiles; the ranges add
 // alpha * partial into a zeroed D with binary64 atomic adds, and beta * C is added
@@ -92,6 +93,13 @@ struct Operand {
   uint32_t voff[DMA_I];  // per lane and instruction (LAY 1: instruction 0 only)
   uint32_t soff;         // LAY 1: per wave, instruction 0
   uint32_t istr;         // LAY 1: per instruction
+  // 4-byte DMA (rows without 16-byte alignment; interior tiles): wave w, instruction i
+  // fills LDS bytes [256 (4i + w), +256) of the tile.
+  //   LAY 0: rows 8i + 2w + (l >> 5) (two 128-byte rows); lane l's dword l & 3 of LDS
+  //          chunk position (l >> 2) & 7 takes the same dword of global chunk
+  //          ((l >> 2) & 7) ^ ((4i + w) & 7), which depends on i only through its parity
+  //   LAY 1: K row i (4 x 256 bytes); lane l takes dword l of quarter w
+  uint32_t voff4[2];
 
   __device__ __forceinline__ void init(const double* X_, int64_t ld_, int64_t r0_, int64_t rows_, int64_t K_,
                                        int w, int lane) {
@@ -100,6 +108,15 @@ struct Operand {
     rows = rows_;
     K = K_;
     r0 = r0_;
+    if constexpr (LAY == 0) {
+#pragma unroll
+      for (int par = 0; par < 2; ++par) {
+        const int q = (lane >> 2) & 7;
+        voff4[par] = (uint32_t)((2 * w + (lane >> 5)) * ld * 8 + (q ^ ((4 * par + w) & 7)) * 16 + (lane & 3) * 4);
+      }
+    } else {
+      voff4[0] = voff4[1] = (uint32_t)(w * 256 + lane * 4);
+    }
     const int64_t valid = rows - r0;  // rows of this tile inside the matrix (>= 1)
     if constexpr (LAY == 0) {
 #pragma unroll
@@ -121,10 +138,67 @@ struct Operand {
   __device__ __forceinline__ void dma(char* dst, int64_t k0, int w) const {
     const char* corner = (const char*)(X + (LAY == 0 ? r0 * ld + k0 : k0 * ld + r0));
     const __amdgpu_buffer_rsrc_t rs = fast::make_rsrc(corner, 0xFFFFFFFFu);
+    typedef __attribute__((address_space(3))) char lds_c;
+    lds_c* base = (lds_c*)(lds_void*)(dst + w * 1024);
+    uint32_t so = soff, lo = 0;
 #pragma unroll
-    for (int i = 0; i < DMA_I; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (NWAVE * i + w) * 1024), 16,
-                                               voff[LAY == 0 ? i : 0], soff + (uint32_t)i * istr, 0, 0);
+    for (int i = 0; i < DMA_I; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + lo), 16, voff[LAY == 0 ? i : 0], so, 0, 0);
+      so += istr;
+      lo += NWAVE * 1024;
+      asm volatile("" : "+s"(so), "+s"(lo));
+    }
+  }
+  // The same with 4-byte DMA: any 4-byte aligned rows, tile inside the rows and K.
+  __device__ __forceinline__ void dma4(char* dst, int64_t k0, int w) const {
+    const char* corner = (const char*)(X + (LAY == 0 ? r0 * ld + k0 : k0 * ld + r0));
+    const __amdgpu_buffer_rsrc_t rs = fast::make_rsrc(corner, 0xFFFFFFFFu);
+    // running scalar global and LDS offsets: two registers, not 16 hoisted constants each
+    const uint32_t step = __builtin_amdgcn_readfirstlane((uint32_t)(LAY == 0 ? 8 * ld * 8 : ld * 8));
+    typedef __attribute__((address_space(3))) char lds_c;
+    lds_c* base = (lds_c*)(lds_void*)(dst + w * 256);
+    uint32_t so = 0, lo = 0;
+#pragma unroll
+    for (int i = 0; i < 4 * DMA_I; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + lo), 4, voff4[i & 1], so, 0, 0);
+      so += step;
+      lo += NWAVE * 256;
+      asm volatile("" : "+s"(so), "+s"(lo));
+    }
+  }
+  // 4-byte DMA of a tile that crosses the edge of the rows: lanes whose rows lie past
+  // the matrix fetch the last valid row (LAY 0; offsets computed per instruction) or
+  // the tile's first element (LAY 1); those rows only feed outputs that are not stored.
+  __device__ __forceinline__ void dma4_edge(char* dst, int64_t k0, int w, int lane) const {
+    const char* corner = (const char*)(X + (LAY == 0 ? r0 * ld + k0 : k0 * ld + r0));
+    const __amdgpu_buffer_rsrc_t rs = fast::make_rsrc(corner, 0xFFFFFFFFu);
+    const int valid = (int)(rows - r0 < BM ? rows - r0 : BM);
+    typedef __attribute__((address_space(3))) char lds_c;
+    lds_c* base = (lds_c*)(lds_void*)(dst + w * 256);
+    const uint32_t lane1 = (uint32_t)((32 * w + (lane >> 1)) < valid ? w * 256 + lane * 4 : (lane & 1) * 4);
+    const uint32_t step = __builtin_amdgcn_readfirstlane((uint32_t)(ld * 8));
+    // LAY 0: the chunk term for the two parities of i, and the row as a running value
+    // (recomputed per instruction rather than 16 offsets hoisted out of the K loop)
+    const uint32_t cterm[2] = {(uint32_t)(((((lane >> 2) & 7) ^ (w & 7)) * 16) + (lane & 3) * 4),
+                               (uint32_t)(((((lane >> 2) & 7) ^ ((4 + w) & 7)) * 16) + (lane & 3) * 4)};
+    int row = 2 * w + (lane >> 5);
+    uint32_t so = 0, lo = 0;
+#pragma unroll
+    for (int i = 0; i < 4 * DMA_I; ++i) {
+      uint32_t vo;
+      if constexpr (LAY == 0) {
+        const int src = row < valid ? row : valid - 1;
+        vo = (uint32_t)src * step + cterm[i & 1];
+        row += 8;
+        asm volatile("" : "+v"(row));
+      } else {
+        vo = lane1;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + lo), 4, vo, LAY == 0 ? 0u : so, 0, 0);
+      so += step;
+      lo += NWAVE * 256;
+      asm volatile("" : "+s"(so), "+s"(lo));
+    }
   }
   // Any K tile: element by element, zeros outside the rows and K, stored with ds_write.
   // Element p of thread t: LAY 0 (r, k) = ((t >> 4) + 16 p, t & 15); LAY 1 (t & 127, (t >> 7) + 2 p).
@@ -226,7 +300,7 @@ __global__ __launch_bounds__(THREADS, 2) void dgemm_kernel(F64Args p) {
         for (int c = 0; c < FN; ++c)
           acc[f][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[f][e], b[c][e], acc[f][c], 0, 0, 0);
   };
-  auto compute = [&](const char* st) {
+  auto compute = [&](const char* st) __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f64x2 a[FM], b[FN];
@@ -234,26 +308,43 @@ __global__ __launch_bounds__(THREADS, 2) void dgemm_kernel(F64Args p) {
       mma(a, b);
     }
   };
-  auto checked = [&](char* st, int64_t k0) {
+  auto checked = [&](char* st, int64_t k0) __attribute__((always_inline)) {
     oa.checked(st, k0, tid);
     ob.checked(st + OP_BYTES, k0, tid);
   };
 
-  // DMA unless an MN-contiguous operand's last tile ends inside a 16-byte pair
+  // 16-byte DMA unless an MN-contiguous operand's last tile ends inside a 16-byte pair;
+  // 4-byte DMA for interior tiles of operands whose rows are not 16-byte aligned
   const bool pairs_a = LA == 0 || m0 + BM <= p.M || ((p.M - m0) & 1) == 0;
   const bool pairs_b = LB == 0 || n0 + BN <= p.N || ((p.N - n0) & 1) == 0;
-  if (p.dma_ok && pairs_a && pairs_b) {
+  const bool dword = p.dma_mode == 2;
+  const bool inside_a = m0 + BM <= p.M, inside_b = n0 + BN <= p.N;
+  // The DMA loop, instantiated twice: EDGE for tiles of 4-byte DMA operands that cross
+  // the edge of M or N (per-instruction clamped offsets), and once for all other DMA
+  // tiles, so that the edge arithmetic holds no registers in the common loop.
+  auto dma_loop = [&](auto edge_tag) __attribute__((always_inline)) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     // DMA for the K tiles inside K; a K tile crossing the end of K (the last one of the
     // last range) follows the loop, loaded by the checked path
     const int64_t kfull = (p.K - kbeg) / BK;
     const int64_t nfull = kfull < nk ? kfull : nk;
-    auto dma = [&](char* st, int64_t t) {
-      oa.dma(st, kbeg + t * BK, w);
-      ob.dma(st + OP_BYTES, kbeg + t * BK, w);
+    auto dma = [&](char* st, int64_t t) __attribute__((always_inline)) {
+      if constexpr (EDGE) {
+        if (inside_a) oa.dma4(st, kbeg + t * BK, w);
+        else oa.dma4_edge(st, kbeg + t * BK, w, lane);
+        if (inside_b) ob.dma4(st + OP_BYTES, kbeg + t * BK, w);
+        else ob.dma4_edge(st + OP_BYTES, kbeg + t * BK, w, lane);
+      } else if (dword) {
+        oa.dma4(st, kbeg + t * BK, w);
+        ob.dma4(st + OP_BYTES, kbeg + t * BK, w);
+      } else {
+        oa.dma(st, kbeg + t * BK, w);
+        ob.dma(st + OP_BYTES, kbeg + t * BK, w);
+      }
     };
     // the DMA writes of a wave are complete once its vmcnt drains; the barrier then
     // publishes the stage to every wave
-    auto publish = [&]() {
+    auto publish = [&]() __attribute__((always_inline)) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     };
@@ -262,7 +353,7 @@ __global__ __launch_bounds__(THREADS, 2) void dgemm_kernel(F64Args p) {
     // barrier that publishes it, before pair 1 of this tile is multiplied; so no
     // instruction waits for LDS.
     f64x2 a0[FM], b0[FN], a1[FM], b1[FN];
-    auto step = [&](auto stage, int64_t t) {
+    auto step = [&](auto stage, int64_t t) __attribute__((always_inline)) {
       constexpr int S = decltype(stage)::value;
       const char* st = lds + S * STAGE;
       if (t + 1 < nfull) dma(lds + (1 - S) * STAGE, t + 1);
@@ -291,6 +382,11 @@ __global__ __launch_bounds__(THREADS, 2) void dgemm_kernel(F64Args p) {
       __syncthreads();
       compute(st);
     }
+  };
+  if (dword && !(inside_a && inside_b)) {
+    dma_loop(std::true_type{});
+  } else if ((p.dma_mode == 1 && pairs_a && pairs_b) || dword) {
+    dma_loop(std::false_type{});
   } else {
     // misaligned operands or odd edges: one stage, checked loads
     for (int64_t t = 0; t < nk; ++t) {
@@ -348,13 +444,14 @@ static void launch_tiles(const F64Args& a, int splits, hipStream_t s) {
                      0, s, a);
 }
 
-// DMA path: 16-byte aligned rows (base and leading dimension) and every offset of a
-// tile from its corner in 32 bits: at most (127 ld + 15) * 8 (K-contiguous) or
-// (15 ld + 127) * 8 (MN-contiguous), plus 16 bytes.
-static bool f64_dma_ok(int lay, const double* X, int64_t ld) {
+// DMA paths: every offset of a tile from its corner in 32 bits, at most (127 ld + 15) * 8
+// (K-contiguous) or (15 ld + 127) * 8 (MN-contiguous), plus 16 bytes; the 16-byte
+// path also needs 16-byte aligned rows (base and even leading dimension).
+static bool f64_offsets32(int lay, int64_t ld) {
   const int64_t span = lay == 0 ? (127 * ld + 15) * 8 : (15 * ld + 127) * 8;
-  return ((uintptr_t)X % 16) == 0 && ld % 2 == 0 && span + 16 < ((int64_t)0xFFFFFFFF);
+  return span + 16 < ((int64_t)0xFFFFFFFF);
 }
+static bool f64_rows16(const double* X, int64_t ld) { return ((uintptr_t)X % 16) == 0 && ld % 2 == 0; }
 
 }  // namespace f64
 
@@ -368,7 +465,7 @@ F64Plan plan_f64(const F64Args& a, bool can_split) {
   // Estimated time of S ranges: full waves of resident workgroups (two per CU), then the
   // last wave, whose workgroups run alone on their CUs when there are at most 256 of
   // them; plus the atomic adds of the partial sums and the extra launches.
-  auto cost = [&](int64_t S) {
+  auto cost = [&](int64_t S) __attribute__((always_inline)) {
     const int64_t per = (nk + S - 1) / S;
     const int64_t wgs = tiles * S;
     const int64_t rounds = (wgs + slots - 1) / slots;
@@ -399,7 +496,8 @@ hipError_t launch_f64(int la, int lb, const F64Args& a0, const F64Plan& plan, hi
   a.tiles_m = (int)((a.M + BM - 1) / BM);
   a.tiles_n = (int)((a.N + BN - 1) / BN);
   a.kt_per_split = plan.kt_per_split;
-  a.dma_ok = a.K == 0 || (f64_dma_ok(la, a.A, a.lda) && f64_dma_ok(lb, a.B, a.ldb));
+  const bool off32 = f64_offsets32(la, a.lda) && f64_offsets32(lb, a.ldb);
+  a.dma_mode = a.K == 0 || (off32 && f64_rows16(a.A, a.lda) && f64_rows16(a.B, a.ldb)) ? 1 : off32 ? 2 : 0;
   const dim3 rows_grid((unsigned)((a.N + 255) / 256), (unsigned)(a.M < 4096 ? a.M : 4096));
   if (plan.splits > 1) {
     hipLaunchKernelGGL(zero_kernel, rows_grid, dim3(256), 0, s, a);

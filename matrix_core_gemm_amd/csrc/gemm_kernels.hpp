@@ -69,7 +69,7 @@ struct F64Args {
   double alpha, beta;
   int use_c;              // beta != 0: C is read
   int kt_per_split;       // K tiles of 16 per workgroup range (filled by the launcher)
-  int dma_ok;             // operands fit the HBM -> LDS DMA path (filled by the launcher)
+  int dma_mode;           // HBM -> LDS DMA: 0 none, 1 16-byte, 2 4-byte (filled by the launcher)
   int tiles_m, tiles_n;   // filled by the launcher
 };
 

@@ -215,3 +215,30 @@ def test_f64_bit_exact_against_instruction_model(layA, layB):
     bad = [(i, j) for i, j in zip(rows, cols) if d[i, j] != kernel_order_model(Al, Bl, C, alpha, beta, i, j)]
     say(f"{layA}/{layB}: {len(bad)} of {len(rows)} outputs differ from the instruction-order model")
     assert not bad, bad[:5]
+
+
+@pytest.mark.parametrize("layA,layB", [("k_contig", "k_contig"), ("mn_contig", "k_contig"), ("k_contig", "mn_contig"),
+                                       ("mn_contig", "mn_contig")])
+def test_f64_odd_leading_dims_bit_exact(layA, layB):
+    """Leading dimensions of odd length (rows not 16-byte aligned: interior tiles load
+    with 4-byte DMA, edge tiles element by element) give exactly the instruction-order
+    model's results, over several interior tiles and a K tail."""
+    mcg = need_gpu()
+    M, N, K = 300, 290, 90
+    alpha, beta = 0.5, 1.5
+    A, B = operands(layA, layB, M, N, K, pad=1, seed=5)
+    assert A.ld % 2 == 1 and B.ld % 2 == 1
+    C = W.c_matrix(M, N, "normal", seed=95, dtype="f64")
+    D = torch.full((M, N), float("nan"), dtype=torch.float64, device="cuda")
+    mcg.gemm_dense("f64", "f64", layA, layB, M, N, K, dev(A.codes), A.ld, dev(B.codes), B.ld, dev(C), D, N, "f64",
+                   alpha, beta)
+    torch.cuda.synchronize()
+    d = D.cpu().numpy()
+    Al = A.codes[:M, :K] if layA == "k_contig" else A.codes[:K, :M].T
+    Bl = B.codes[:N, :K].T if layB == "k_contig" else B.codes[:K, :N]
+    rows, cols = W.sample_coords(M, N, 300, full_rows=(0, 127, 128, 255), full_cols=(0, 129, 255))
+    bad = [(i, j) for i, j in zip(rows, cols) if d[i, j] != kernel_order_model(Al, Bl, C, alpha, beta, i, j)]
+    say(f"{layA}/{layB} odd ld: {len(bad)} of {len(rows)} outputs differ from the instruction-order model")
+    assert not bad, bad[:5]
+    ref, s = oracle.gemm_f64(layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, N, alpha, beta)
+    assert oracle.check_f64(d, ref, s, K, alpha, beta, C)["ok"]
