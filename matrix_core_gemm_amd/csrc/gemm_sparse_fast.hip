@@ -23,7 +23,10 @@
 //     owning 128 x 64 outputs = 4 x 2 instructions of 32 x 32.
 //   - LDS: kept values in stages of 128 bytes per row (one cache line: 128
 //     dense k of 16-bit or 256 of 8-bit elements) together with their index
-//     words (16 or 32 bytes per row), 2 stages; B in stages of 128 bytes per
+//     words (16 or 32 bytes per row; rows with bit 4 set keep the two halves of
+//     their words swapped, so that the index reads of rows r and r + 16, which
+//     the same LDS cycle serves, fall in different banks), 2 stages; B in stages
+//     of 128 bytes per
 //     column (64 or 128 dense k), 2 stages per column half.  All filled by
 //     buffer_load ... lds.
 //   - ping-pong schedule as in the dense kernel: the two wavefronts of a SIMD
@@ -201,10 +204,11 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   int word_idx[II];
   rs_idx = make_rsrc((const char*)(p.idx + m0 * p.ld_idx), (uint32_t)(rows * p.ld_idx * 4));
 #pragma unroll
-  for (int i = 0; i < II; ++i) {  // 4-byte loads: lane -> (row, word) of an IWB-byte index row
+  for (int i = 0; i < II; ++i) {  // 4-byte loads: lane -> LDS (row, position) of an IWB-byte index row
     const int e = i * 256 + q * 64 + lane;
-    word_idx[i] = e % WPR;
-    off_idx[i] = (uint32_t)((e / WPR) * p.ld_idx * 4 + (e % WPR) * 4);
+    const int row = e / WPR;
+    word_idx[i] = (e % WPR) ^ ((WPR / 2) * ((row >> 4) & 1));  // the word kept at that position
+    off_idx[i] = (uint32_t)(row * p.ld_idx * 4 + word_idx[i] * 4);
   }
   auto issueA = [&](int T) { la.issue(stA(T), T, 4 * grp, 4, q); };
   auto issueI = [&](int T) {
@@ -230,17 +234,19 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   // [64h + 32s, +32) of stage T and B bytes [64s, +64) of step u.  Index codes:
   // 16-bit elements use half g of word 2h + s (32 dense k per instruction),
   // 8-bit elements word 4h + 2s + g (64 dense k per instruction).
+  // byte of this lane's index words in row rbA + (lane & 31) for h = 0 (h = 1: ^ IWB / 2);
+  // rows 32 i further add 32 i IWB
+  const int ibase = (rbA + (lane & 31)) * IWB + (IWB / 2) * ((lane >> 4) & 1);
   auto read_frags = [&](int u) {
     const int T = u >> 1, h = u & 1;
 #pragma unroll
     for (int i = 0; i < WTM; ++i) {
-      const int row = rbA + 32 * i + (lane & 31);
       if constexpr (EB == 2) {
-        const i32x2 w = *(const __attribute__((address_space(3))) i32x2*)(stI(T) + row * IWB + 8 * h);
+        const i32x2 w = *(const __attribute__((address_space(3))) i32x2*)(stI(T) + (ibase ^ (8 * h)) + 32 * i * IWB);
         fi[0][i] = (int)((uint32_t)w.x >> (16 * g));
         fi[1][i] = (int)((uint32_t)w.y >> (16 * g));
       } else {
-        const i32x4 w = *(const __attribute__((address_space(3))) i32x4*)(stI(T) + row * IWB + 16 * h);
+        const i32x4 w = *(const __attribute__((address_space(3))) i32x4*)(stI(T) + (ibase ^ (16 * h)) + 32 * i * IWB);
         fi[0][i] = g ? w.y : w.x;
         fi[1][i] = g ? w.w : w.z;
       }
