@@ -23,11 +23,13 @@
 //     tile's fragments and 4 DMA issues per wave), separated by workgroup
 //     barriers, so that one of them keeps the SIMD's matrix core busy while
 //     the other waits on memory.
-//   - epilogue: for interior tiles, straight-line code reads C in batches of
-//     16 vector loads per lane (so the loads overlap) and stores
-//     D = alpha * acc + beta * C (16 bytes per lane per row segment, thanks to
-//     issuing each instruction with the B fragment as its first operand); edge
-//     tiles use per-element bounds.
+//   - epilogue: a lane's accumulators hold 4 consecutive columns of one row
+//     (each instruction is issued with the B fragment as its first operand).
+//     Interior tiles pass each wavefront's 32 x 64 blocks through LDS, so that 16
+//     lanes read C and write D = alpha * acc + beta * C along one row segment
+//     (whole lines: storing from the accumulator layout wrote 32 rows x 16 or 32
+//     bytes per instruction, and the fixed cost of the launch was twice that of a
+//     line-wise store); edge tiles use per-element bounds.
 //   - the 8 XCDs receive workgroups round-robin; the tile sequence is permuted
 //     so that the workgroups resident on one XCD cover a compact block of tiles.
 // Preconditions (checked on the host): 16-byte aligned operands, K * elem_bytes
@@ -249,6 +251,86 @@ void gemm_fast_kernel(DenseArgs p) {
     }
     return o;
   };
+  if (vec_ok && m0 + BM <= p.M && n0 + BN <= p.N) {
+    // Interior tile.  Each wavefront passes the 32 x 64 block of its row group i
+    // through LDS (8 KiB, two buffers), so that 16 lanes then read C and write D
+    // along one row segment (256 bytes of binary32 / int32, 128 of 16-bit values):
+    // whole lines per store instruction instead of 32 rows x 16 or 32 bytes.
+    // Chunk ch (16 bytes) of staging row r sits at ch ^ (r & 15): the writes (32
+    // rows at one chunk) and the reads (4 rows x 16 chunks) are free of bank conflicts.
+    barrier_lds();  // all LDS DMA has landed (vmcnt(0) above); no fragment reads remain
+    typedef __attribute__((address_space(3))) v4 lds_v4;
+    lds_char* wbuf = smem + wave * 16384;
+    const int wr = lane & 31, rr = lane >> 4, cc = lane & 15;
+    const int64_t col = n0 + rbB + 4 * cc;
+    const int out = p.out;
+    auto combine4 = [&](const v4& a, const v4& c) {
+      v4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (Op::INT_ACC)
+          o[r] = (int)((uint32_t)a[r] + (p.use_c ? (uint32_t)p.beta_i * (uint32_t)c[r] : 0u));
+        else
+          o[r] = p.use_c ? __builtin_fmaf(p.alpha, a[r], p.beta * c[r]) : p.alpha * a[r];
+      }
+      return o;
+    };
+#pragma unroll
+    for (int i = 0; i < WTM; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      lds_char* buf = wbuf + (i & 1) * 8192;
+#pragma unroll
+      for (int j = 0; j < WTN; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int ch = 8 * j + 2 * r4 + (lane >> 5);
+          v4 x;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] = acc[i][j][4 * r4 + r];
+          *(lds_v4*)(buf + wr * 256 + ((ch ^ (wr & 15)) << 4)) = x;
+        }
+      // the reads below take other lanes' values: wait for the writes
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      v4 a[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int row = 4 * t + rr;
+        a[t] = *(const lds_v4*)(buf + row * 256 + ((cc ^ (row & 15)) << 4));
+      }
+      const int64_t rbase = (m0 + rbA + 32 * i + rr) * p.ldc + col;  // row 4t further: + 4t ldc
+      if constexpr (!Op::INT_ACC) {
+        if (out != OUT_32) {
+          const uint16_t* C16 = (const uint16_t*)p.C;
+          uint16_t* D16 = (uint16_t*)p.D;
+          i32x2 cw[8];
+          if (p.use_c) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) cw[t] = *(const i32x2*)(C16 + rbase + 4 * t * p.ldc);
+          }
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            v4 c = {};
+            if (p.use_c)
+              c = v4{from_out_bits(out, (uint32_t)cw[t].x & 0xffffu), from_out_bits(out, (uint32_t)cw[t].x >> 16),
+                     from_out_bits(out, (uint32_t)cw[t].y & 0xffffu), from_out_bits(out, (uint32_t)cw[t].y >> 16)};
+            const v4 o = combine4(a[t], c);
+            *(i32x2*)(D16 + rbase + 4 * t * p.ldc) =
+                i32x2{(int)(to_out_bits(out, o[0]) | (to_out_bits(out, o[1]) << 16)),
+                      (int)(to_out_bits(out, o[2]) | (to_out_bits(out, o[3]) << 16))};
+          }
+          continue;
+        }
+      }
+      v4 cv[8];
+      if (p.use_c) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) cv[t] = *(const v4*)(C + rbase + 4 * t * p.ldc);
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) *(v4*)(D + rbase + 4 * t * p.ldc) = combine4(a[t], p.use_c ? cv[t] : v4{});
+    }
+    return;
+  }
   if constexpr (!Op::INT_ACC) {
     if (p.out != OUT_32) {
       // bfloat16 / binary16 C and D: 4 consecutive elements = 8 bytes per lane
@@ -296,42 +378,7 @@ void gemm_fast_kernel(DenseArgs p) {
       return;
     }
   }
-  if (vec_ok && m0 + BM <= p.M && n0 + BN <= p.N) {
-    // interior tile: straight-line code, C read in batches of 16 vector loads
-    // per lane (two rows of instruction tiles), issued back to back
-    const s1* Cb = C + (m0 + rbA + (lane & 31)) * p.ldc + n0 + rbB + 4 * (lane >> 5);
-    s1* Db = D + (m0 + rbA + (lane & 31)) * p.ldc + n0 + rbB + 4 * (lane >> 5);
-    if (p.use_c) {
-#pragma unroll
-      for (int i0 = 0; i0 < WTM; i0 += 2) {
-        __builtin_amdgcn_sched_barrier(0);  // keep each batch's arithmetic after its loads
-        v4 cbuf[2][WTN][4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < WTN; ++j)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4)
-              cbuf[i][j][r4] = *(const v4*)(Cb + (32 * (i0 + i)) * p.ldc + 32 * j + 8 * r4);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < WTN; ++j)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4)
-              *(v4*)(Db + (32 * (i0 + i)) * p.ldc + 32 * j + 8 * r4) =
-                  combine(acc[i0 + i][j], r4, cbuf[i][j][r4], true);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < WTM; ++i)
-#pragma unroll
-        for (int j = 0; j < WTN; ++j)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4)
-            *(v4*)(Db + (32 * i) * p.ldc + 32 * j + 8 * r4) = combine(acc[i][j], r4, v4{}, false);
-    }
-  } else {
+  {
     // edge tile: per-element bounds
 #pragma unroll
     for (int i = 0; i < WTM; ++i) {
