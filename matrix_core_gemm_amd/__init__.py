@@ -162,7 +162,8 @@ def validate_compress24(dtype, M, K, A, lda, A_compressed, lda_c, A_index, ld_id
 def dense_path(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb) -> int:
     """Kernel gemm_dense runs for these operands (binary32/int32 D, not C):
     0 general 128 x 128, 1 the 256 x 256 kernel, 2 general 128 x 32 (N <= 32),
-    3 general 32 x 128 (M <= 32), 4 streaming kernel, 5 binary64 kernel."""
+    3 general 32 x 128 (M <= 32), 4 streaming kernel, 5 binary64 kernel,
+    6 the pipelined kernel with 128 x 128 tiles (mid-size aligned problems)."""
     return _lib.mcg_dense_path(_dt(dtypeA), _lay(layoutA), _lay(layoutB), M, N, K, _ptr(A), lda,
                                _ptr(B), ldb)
 

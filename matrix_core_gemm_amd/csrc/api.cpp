@@ -170,8 +170,9 @@ int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int6
   a.vec_cd = aligned_to(D, vb) && (!a.use_c || aligned_to(C, vb)) && ldc % 4 == 0;
   const bool aligned = dense_aligned(eb, K, A, lda, B, ldb);
   const mcg::DensePlan plan = mcg::plan_dense(dtypeA, layoutA, layoutB, a, aligned, can_split_k(a, C, D));
-  if (plan.kernel == mcg::KERNEL_FAST)
-    return hip_status(mcg::launch_fast(dtypeA, dtypeB, layoutA, layoutB, a, (hipStream_t)stream));
+  if (plan.kernel == mcg::KERNEL_FAST || plan.kernel == mcg::KERNEL_MID)
+    return hip_status(mcg::launch_fast(dtypeA, dtypeB, layoutA, layoutB, a, (hipStream_t)stream,
+                                       plan.kernel == mcg::KERNEL_MID ? 128 : 256));
   return hip_status(mcg::launch_dense(dtypeA, dtypeB, layoutA, layoutB, aligned, a, plan, (hipStream_t)stream));
 }
 

@@ -60,6 +60,12 @@ constexpr int64_t FAST_MIN_TILES = 128;   // 256 x 256 tiles from which the fast
 // K tile of a workgroup, ATOMIC_US per device-scope atomic add of D and
 // SPLIT_US for zeroing D and the extra launches.
 constexpr double KT_US = 1.0, ROUND_US = 3.0, ATOMIC_US = 1.4e-5, SPLIT_US = 5.0;
+// The 128 x 128 form of the fast kernel (KERNEL_MID) with at most one workgroup
+// per CU: MID_KT_US * nk + ROUND_US (measured over 100..256 tiles and K up to 16384).
+// Two of its workgroups on one CU disturb each other's ping-pong, so beyond
+// NUM_CU tiles the general kernel is faster; it is also taken only when it beats
+// the best general plan by MID_MARGIN.
+constexpr double MID_KT_US = 0.72, MID_MARGIN = 0.95;
 // The streaming kernel is HBM-bound: split only when there are too few blocks
 // to spread over the CUs, keeping 16 K tiles or more per split.
 constexpr int64_t STREAM_MIN_BLOCKS = 64, STREAM_MIN_KT = 16;
@@ -70,20 +76,29 @@ DensePlan plan_dense(int dtA, int la, int lb, const DenseArgs& a, bool aligned, 
   const int64_t KE = KT_BYTES / eb;
   const int64_t nk = (a.K + KE - 1) / KE;
   auto cdiv = [](int64_t x, int64_t y) { return (x + y - 1) / y; };
-  // number of K ranges for `tiles` workgroups of the general kernels
-  auto splits_for = [&](int64_t tiles) -> int64_t {
-    if (!can_split || nk < 2) return 1;
-    int64_t best = 1;
-    double best_t = 0;
-    for (int64_t s = 1; s <= nk / 2 + 1 && s <= 1024; s = s < 4 ? s + 1 : s * 2) {
-      const int64_t ss = std::min(s, nk);
+  // number of K ranges for `tiles` workgroups of the general kernels, and the
+  // modelled time of that plan
+  auto plan_general = [&](int64_t tiles, double* time) -> int64_t {
+    auto model = [&](int64_t ss) {  // ss >= 1
       const double rounds = (double)cdiv(tiles * ss, NUM_CU);
-      const double t = rounds * (KT_US * (double)cdiv(nk, ss) + ROUND_US) +
-                       ATOMIC_US * (double)ss * (double)a.M * (double)a.N + (ss > 1 ? SPLIT_US : 0.0);
-      if (s == 1 || t < best_t) { best = ss; best_t = t; }
+      return rounds * (KT_US * (double)cdiv(nk, ss) + ROUND_US) +
+             ATOMIC_US * (double)ss * (double)a.M * (double)a.N + (ss > 1 ? SPLIT_US : 0.0);
+    };
+    int64_t best = 1;
+    double best_t = model(1);
+    if (can_split && nk >= 2) {
+      for (int64_t s = 2; s <= nk / 2 + 1 && s <= 1024; s = s < 4 ? s + 1 : s * 2) {
+        const int64_t ss = std::min(s, nk);
+        const double t = model(ss);
+        if (t < best_t) { best = ss; best_t = t; }
+      }
     }
+    // the model charges atomic adds to the unsplit plan too (it only ranks split
+    // counts); the unsplit kernel stores D directly
+    if (time) *time = best_t - (best == 1 ? ATOMIC_US * (double)a.M * (double)a.N : 0.0);
     return best;
   };
+  auto splits_for = [&](int64_t tiles) { return plan_general(tiles, nullptr); };
   auto make = [&](int kernel, int64_t s) {
     DensePlan p{kernel, 1, (int)(nk > 0 ? nk : 1), 0};
     if (s > 1) {
@@ -96,6 +111,11 @@ DensePlan plan_dense(int dtA, int la, int lb, const DenseArgs& a, bool aligned, 
 
   if (fast_path_ok(dtA, la, lb, a, aligned) && cdiv(a.M, 256) * cdiv(a.N, 256) >= FAST_MIN_TILES)
     return make(KERNEL_FAST, 1);
+  if (fast_path_ok(dtA, la, lb, a, aligned, 128) && cdiv(a.M, 128) * cdiv(a.N, 128) <= NUM_CU) {
+    double t_general;
+    plan_general(cdiv(a.M, 128) * cdiv(a.N, 128), &t_general);
+    if (MID_KT_US * (double)nk + ROUND_US < MID_MARGIN * t_general) return make(KERNEL_MID, 1);
+  }
   if (stream_path_ok(dtA, la, lb, a, aligned)) {
     // 128-row blocks when that still gives most CUs a block, else 32-row blocks
     // (measured: more blocks beat wider ones below 16384 rows)

@@ -1,5 +1,6 @@
 // gemm_fast.hip -- large-tile, deeply pipelined dense MFMA GEMM for gfx950 (the fast path of
-// gemm_dense for aligned problems of at least 256 x 256).
+// gemm_dense for aligned problems of at least 256 x 256, and in a 128 x 128-tile form for
+// aligned problems with too few 256 x 256 tiles to fill the chip).
 //
 // Same operation as gemm_dense.hip (the matrix fused multiply-add of "Accurate
 // Models of AMD Matrix Cores", Section 2, Eq. (1), tiled over K as in "CDNA3
@@ -32,8 +33,11 @@
 //     line-wise store); edge tiles use per-element bounds.
 //   - the 8 XCDs receive workgroups round-robin; the tile sequence is permuted
 //     so that the workgroups resident on one XCD cover a compact block of tiles.
+//   - 128 x 128 form: the same schedule with wave tiles of 64 x 32 and 16 KiB
+//     stages (80 KiB of LDS).  Two of its workgroups on one CU slow each
+//     other's ping-pong, so the host uses it for at most one tile per CU.
 // Preconditions (checked on the host): 16-byte aligned operands, K * elem_bytes
-// and ld * elem_bytes multiples of 16, M, N >= 256, and each workgroup's
+// and ld * elem_bytes multiples of 16, M, N >= the tile size, and each workgroup's
 // operand window below 2 GiB (32-bit buffer offsets).
 #include "fast_tiles.hpp"
 #include "gemm_kernels.hpp"
@@ -44,17 +48,19 @@ namespace fast {
 constexpr int KTB = 128;     // bytes of K per LDS row and stage: one 128-byte line per row
 constexpr int NSA = 2;       // LDS stages of A
 constexpr int NSB = 3;       // LDS stages of B
-constexpr int BM = 256, BN = 256;
 constexpr int THREADS = 512;
 
-
-template <class Op, int LA, int LB>
+// TB: output tile TB x TB (256, or 128 for problems with too few 256 x 256 tiles to
+// fill the chip); each wavefront owns (TB / 2) x (TB / 4) outputs.
+template <class Op, int LA, int LB, int TB>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_fast_kernel(DenseArgs p) {
+  constexpr int BM = TB, BN = TB;
+  constexpr int SB = TB * KTB;          // bytes of one operand stage
   constexpr int EB = Op::EB;
   constexpr int LB16 = Op::LANE_BYTES;  // bytes of K per lane and instruction (16 or 32)
   constexpr int S = 64 / (2 * LB16);    // instructions per block and half K tile
-  constexpr int WTM = 4, WTN = 2;       // 32 x 32 instruction tiles per wave along m and n
+  constexpr int WTM = TB / 64, WTN = TB / 128;  // 32 x 32 instruction tiles per wave along m and n
   using GA = Geom<EB, LA, BM, KTB>;
   using GB = Geom<EB, LB, BN, KTB>;
   using RA = Reader<EB, LA, BM, KTB>;
@@ -65,17 +71,19 @@ void gemm_fast_kernel(DenseArgs p) {
   using frag_t = typename Op::frag_t;
   using v4 = typename std::conditional<Op::INT_ACC, i32x4, f32x4>::type;
   using s1 = typename std::conditional<Op::INT_ACC, int, float>::type;
-  static_assert(GA::BYTES == 32768 && GB::BYTES == 32768, "32 KiB per operand stage");
-  static_assert(LdA::INSTR == 8 && LdB::INSTR == 8, "vmcnt bookkeeping assumes 4 + 4 loads per stage and group");
+  static_assert(TB == 256 || TB == 128, "tile");
+  static_assert(GA::BYTES == SB && GB::BYTES == SB, "one stage size for both operands");
+  constexpr int LH = LdA::INSTR / 2;  // loads per wave, operand and half stage (one group's share)
+  static_assert(LdA::INSTR == LdB::INSTR && (LH == 4 || LH == 2), "vmcnt bookkeeping");
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[(NSA + NSB) * 32768];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[(NSA + NSB) * SB];
   lds_char* smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;  // 0: multiplies in even slots; 1: in odd slots
-  const int q = wave & 3;     // wavefronts q and q + 4 share a SIMD and a 128 x 128 quadrant
-  const int rbA = (q >> 1) * 128, rbB = (q & 1) * 128 + grp * 64;
+  const int q = wave & 3;     // wavefronts q and q + 4 share a SIMD and a quadrant of the tile
+  const int rbA = (q >> 1) * (TB / 2), rbB = (q & 1) * (TB / 2) + grp * (TB / 4);
   const int g = lane >> 5;
 
   int tm, tn;
@@ -100,12 +108,12 @@ void gemm_fast_kernel(DenseArgs p) {
     for (int j = 0; j < WTN; ++j) acc[i][j] = acc_t{};
 
   const int nk = (int)((p.K + KTB / EB - 1) / (KTB / EB));
-  auto stA = [&](int kt) { return smem + (kt & 1) * 32768; };
-  auto stB = [&](int kt) { return smem + NSA * 32768 + (kt % NSB) * 32768; };
-  // this group's half (4 of the 8 load instructions per wave) of operand X of K tile kt
-  const int ihalf = 4 * grp;
-  auto issueA = [&](int kt) { la.issue(stA(kt), kt, ihalf, 4, q); };
-  auto issueB = [&](int kt) { lb.issue(stB(kt), kt, ihalf, 4, q); };
+  auto stA = [&](int kt) { return smem + (kt & 1) * SB; };
+  auto stB = [&](int kt) { return smem + NSA * SB + (kt % NSB) * SB; };
+  // this group's half (LH of the 2 LH load instructions per wave) of operand X of K tile kt
+  const int ihalf = LH * grp;
+  auto issueA = [&](int kt) { la.issue(stA(kt), kt, ihalf, LH, q); };
+  auto issueB = [&](int kt) { lb.issue(stB(kt), kt, ihalf, LH, q); };
 
   frag_t fa[S][WTM], fb[S][WTN];
   // fragments of half h (K bytes [64h, 64h + 64) of each row) of K tile kt;
@@ -173,13 +181,13 @@ void gemm_fast_kernel(DenseArgs p) {
   //   slot 4t + 1 (group 0): first half of B(t+2)   -> B stage of tile t-1
   //   slot 4t + 2 (group 1): second half of B(t+2)
   //   slot 4t + 3 (group 0): first half of A(t+2)   -> A stage of tile t, free since slot 4t+3
-  // At the end of slot 4t + 2 each wave waits until only its newest 4 loads
+  // At the end of slot 4t + 2 each wave waits until only its newest LH loads
   // (its half of B(t+2)) are in flight, so tile t+1 is complete from slot 4t+3.
   // DMA of tiles at or beyond nk read nothing and fill their stage with zeros.
   issueB(0);
   issueA(0);
   issueB(1);
-  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // own shares of tile 0 have landed
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LH) : "memory");  // own shares of tile 0 have landed
   barrier_lds();
   // The two half tiles of a K tile are written out (no run-time choice between
   // the A and B loads, whose buffer descriptors then stay in scalar registers).
@@ -198,7 +206,7 @@ void gemm_fast_kernel(DenseArgs p) {
       __builtin_amdgcn_sched_barrier(0);
       multiply();  // slot 4t + 2
       __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // own shares of tile t+1
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LH) : "memory");  // own shares of tile t+1
       barrier_lds();
     }
   } else {
@@ -213,7 +221,7 @@ void gemm_fast_kernel(DenseArgs p) {
       barrier_lds();
       __builtin_amdgcn_sched_barrier(0);
       mem(std::integral_constant<int, 1>{}, t);  // slot 4t + 2
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // own shares of tile t+1
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LH) : "memory");  // own shares of tile t+1
       barrier_lds();
       __builtin_amdgcn_sched_barrier(0);
       multiply();  // slot 4t + 3
@@ -251,7 +259,7 @@ void gemm_fast_kernel(DenseArgs p) {
     }
     return o;
   };
-  if (vec_ok && m0 + BM <= p.M && n0 + BN <= p.N) {
+  if constexpr (TB == 256) if (vec_ok && m0 + BM <= p.M && n0 + BN <= p.N) {
     // Interior tile.  Each wavefront passes the 32 x 64 block of its row group i
     // through LDS (8 KiB, two buffers), so that 16 lanes then read C and write D
     // along one row segment (256 bytes of binary32 / int32, 128 of 16-bit values):
@@ -410,56 +418,62 @@ void gemm_fast_kernel(DenseArgs p) {
   }
 }
 
-template <class Op, int LA, int LB>
+template <class Op, int LA, int LB, int TB>
 static hipError_t launch_one(const DenseArgs& a0, hipStream_t s) {
   DenseArgs a = a0;
-  a.tiles_m = (int)((a.M + BM - 1) / BM);
-  a.tiles_n = (int)((a.N + BN - 1) / BN);
+  a.tiles_m = (int)((a.M + TB - 1) / TB);
+  a.tiles_n = (int)((a.N + TB - 1) / TB);
   const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_fast_kernel<Op, LA, LB>), dim3((unsigned)blocks), dim3(THREADS), 0, s, a);
+  hipLaunchKernelGGL((gemm_fast_kernel<Op, LA, LB, TB>), dim3((unsigned)blocks), dim3(THREADS), 0, s, a);
   return hipGetLastError();
 }
 
+template <class Op, int TB>
+static hipError_t launch_layouts_tb(int la, int lb, const DenseArgs& a, hipStream_t s) {
+  if (la == 0 && lb == 0) return launch_one<Op, 0, 0, TB>(a, s);
+  if (la == 0 && lb == 1) return launch_one<Op, 0, 1, TB>(a, s);
+  if (la == 1 && lb == 0) return launch_one<Op, 1, 0, TB>(a, s);
+  return launch_one<Op, 1, 1, TB>(a, s);
+}
+
 template <class Op>
-static hipError_t launch_layouts(int la, int lb, const DenseArgs& a, hipStream_t s) {
-  if (la == 0 && lb == 0) return launch_one<Op, 0, 0>(a, s);
-  if (la == 0 && lb == 1) return launch_one<Op, 0, 1>(a, s);
-  if (la == 1 && lb == 0) return launch_one<Op, 1, 0>(a, s);
-  return launch_one<Op, 1, 1>(a, s);
+static hipError_t launch_layouts(int la, int lb, const DenseArgs& a, hipStream_t s, int tile) {
+  return tile == 128 ? launch_layouts_tb<Op, 128>(la, lb, a, s) : launch_layouts_tb<Op, 256>(la, lb, a, s);
 }
 
 }  // namespace fast
 
-bool fast_path_ok(int dtA, int la, int lb, const DenseArgs& a, bool aligned) {
+bool fast_path_ok(int dtA, int la, int lb, const DenseArgs& a, bool aligned, int tile) {
   const int64_t eb = (dtA == DT_BF16 || dtA == DT_F16) ? 2 : 1;
+  if (tile != 256 && tile != 128) return false;
   if (!aligned || a.K == 0 || (a.K * eb) % 16 != 0) return false;
-  if (a.M < 256 || a.N < 256) return false;  // small problems: the 128 x 128 kernel fills the chip better
+  if (a.M < tile || a.N < tile) return false;  // smaller problems: the general kernel fills the chip better
   // every buffer window (and offset into it) must stay below 2 GiB
   const int64_t lim = (int64_t)1 << 31;
   // MN-contiguous offsets advance by whole K tiles, up to NST tiles past the end of K
   const int64_t kpad = 4 * fast::KTB / eb;
-  const int64_t wa = la == 0 ? 256 * a.lda * eb : (a.K + kpad) * a.lda * eb;
-  const int64_t wb = lb == 0 ? 256 * a.ldb * eb : (a.K + kpad) * a.ldb * eb;
+  const int64_t wa = la == 0 ? tile * a.lda * eb : (a.K + kpad) * a.lda * eb;
+  const int64_t wb = lb == 0 ? tile * a.ldb * eb : (a.K + kpad) * a.ldb * eb;
   return wa < lim && wb < lim;
 }
 
-hipError_t launch_fast(int dtA, int dtB, int la, int lb, const DenseArgs& a, hipStream_t s) {
+hipError_t launch_fast(int dtA, int dtB, int la, int lb, const DenseArgs& a, hipStream_t s, int tile) {
   using namespace fast;
-  if (dtA == DT_BF16) return launch_layouts<BF16>(la, lb, a, s);
-  if (dtA == DT_F16) return launch_layouts<F16>(la, lb, a, s);
-  if (dtA == DT_I8) return launch_layouts<I8>(la, lb, a, s);
+  if (dtA == DT_BF16) return launch_layouts<BF16>(la, lb, a, s, tile);
+  if (dtA == DT_F16) return launch_layouts<F16>(la, lb, a, s, tile);
+  if (dtA == DT_I8) return launch_layouts<I8>(la, lb, a, s, tile);
   const int fa = f8fmt(dtA), fb = f8fmt(dtB);
   if (a.K >= FP8_NATIVE_MIN_K) {
-    if (fb == 0 && fa == 0) return launch_layouts<F8<0, 0>>(la, lb, a, s);
-    if (fb == 1 && fa == 0) return launch_layouts<F8<1, 0>>(la, lb, a, s);
-    if (fb == 0 && fa == 1) return launch_layouts<F8<0, 1>>(la, lb, a, s);
-    return launch_layouts<F8<1, 1>>(la, lb, a, s);
+    if (fb == 0 && fa == 0) return launch_layouts<F8<0, 0>>(la, lb, a, s, tile);
+    if (fb == 1 && fa == 0) return launch_layouts<F8<1, 0>>(la, lb, a, s, tile);
+    if (fb == 0 && fa == 1) return launch_layouts<F8<0, 1>>(la, lb, a, s, tile);
+    return launch_layouts<F8<1, 1>>(la, lb, a, s, tile);
   }
-  if (fa == 0 && fb == 0) return launch_layouts<F8W<0, 0>>(la, lb, a, s);
-  if (fa == 0 && fb == 1) return launch_layouts<F8W<0, 1>>(la, lb, a, s);
-  if (fa == 1 && fb == 0) return launch_layouts<F8W<1, 0>>(la, lb, a, s);
-  return launch_layouts<F8W<1, 1>>(la, lb, a, s);
+  if (fa == 0 && fb == 0) return launch_layouts<F8W<0, 0>>(la, lb, a, s, tile);
+  if (fa == 0 && fb == 1) return launch_layouts<F8W<0, 1>>(la, lb, a, s, tile);
+  if (fa == 1 && fb == 0) return launch_layouts<F8W<1, 0>>(la, lb, a, s, tile);
+  return launch_layouts<F8W<1, 1>>(la, lb, a, s, tile);
 }
 
 }  // namespace mcg

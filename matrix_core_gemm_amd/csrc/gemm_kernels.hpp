@@ -32,7 +32,8 @@ enum : int {
   KERNEL_SKINNY_N = 2,  // general kernel with 128 x 32 tiles (N <= 32)
   KERNEL_SKINNY_M = 3,  // general kernel with 32 x 128 tiles (M <= 32)
   KERNEL_STREAM = 4,    // streaming kernel for N <= 32 or M <= 32 (K-contiguous, aligned)
-  KERNEL_F64 = 5        // binary64 kernel (128 x 128 tiles on the 4x4x4 FP64 instruction)
+  KERNEL_F64 = 5,       // binary64 kernel (128 x 128 tiles on the 16x16x4 FP64 instruction)
+  KERNEL_MID = 6        // the KERNEL_FAST design with 128 x 128 tiles (too few 256 x 256 tiles)
 };
 
 struct DensePlan {
@@ -120,8 +121,9 @@ hipError_t launch_skinny_n(int dtA, int dtB, int layoutA, int layoutB, const Den
 hipError_t launch_skinny_m(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
 bool stream_path_ok(int dtA, int layoutA, int layoutB, const DenseArgs& a, bool aligned);
 hipError_t launch_stream(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
-bool fast_path_ok(int dtA, int layoutA, int layoutB, const DenseArgs& a, bool aligned);
-hipError_t launch_fast(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
+// tile: 256 (KERNEL_FAST) or 128 (KERNEL_MID)
+bool fast_path_ok(int dtA, int layoutA, int layoutB, const DenseArgs& a, bool aligned, int tile = 256);
+hipError_t launch_fast(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s, int tile = 256);
 hipError_t launch_sparse(int dtA, int dtB, int layoutB, bool aligned, const SparseArgs& a, hipStream_t s);
 bool sparse_fast_ok(int dtA, int layoutB, const SparseArgs& a);
 hipError_t launch_sparse_fast(int dtA, int dtB, int layoutB, const SparseArgs& a, hipStream_t s);

@@ -31,7 +31,8 @@ def dev(a: np.ndarray) -> torch.Tensor:
 def run_dense(mcg, dtA, dtB, layA, layB, M, N, K, A, lda, B, ldb, C=None, ldc=None, alpha=1.0,
               beta=0.0, sA=1.0, sB=1.0, d_fill=float("nan"), c_dev=None, expect_path=None):
     """Run gemm_dense on host code arrays; returns D (numpy, shape (M, ldc)).
-    expect_path: 1 / 0 asserts that the call runs the 256 x 256 / general kernel."""
+    expect_path: asserts the kernel the call runs (0 general, 1 the 256 x 256 kernel,
+    6 its 128 x 128 form)."""
     i8 = dtA == "i8"
     ldc = N if ldc is None else ldc
     dA, dB = dev(A), dev(B)

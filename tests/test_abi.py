@@ -175,3 +175,42 @@ def test_compress24_host_flags_violations_like_oracle():
     ov, oi, viol = oracle.compress24("i8", A)
     assert viol > 0
     assert np.array_equal(vals, ov) and np.array_equal(idx, oi)
+
+
+# Kernel choice is host-only: addresses are never dereferenced.
+BASE = 1 << 20
+
+
+def plan(dt, M, N, K, lay=("k_contig", "k_contig"), pad=0):
+    la, lb = lay
+    lda = (K if la == "k_contig" else M) + pad
+    ldb = (K if lb == "k_contig" else N) + pad
+    path = m.dense_path(dt, la, lb, M, N, K, BASE, max(lda, 1), BASE, max(ldb, 1))
+    splits = m.dense_splits(dt, la, lb, M, N, K, BASE, max(lda, 1), BASE, max(ldb, 1), None,
+                            BASE + (1 << 34), "i32" if dt == "i8" else "f32", 0.0)
+    return path, splits
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "i8", "e4m3"])
+@pytest.mark.parametrize("shape", [(64, 48, 0), (300, 264, 0), (2048, 2048, 0), (0, 300, 256),
+                                   (300, 0, 256), (0, 0, 0)])
+def test_planner_degenerate_sizes(dt, shape):
+    """Empty problems plan without splitting (and without a host arithmetic fault)."""
+    path, splits = plan(dt, *shape)
+    assert path in (0, 1, 2, 3, 4, 6)
+    assert splits == 1
+
+
+@pytest.mark.parametrize("dt", ["bf16", "i8", "e4m3"])
+def test_planner_kernel_by_shape(dt):
+    """256 x 256 tiles from 128 of them; the 128 x 128 form for at most 256 of its tiles
+    when it beats the general kernel's best split; the general kernel beyond that and
+    for unaligned operands; the streaming kernel for N <= 32."""
+    assert plan(dt, 8192, 8192, 8192)[0] == 1
+    assert plan(dt, 2048, 2048, 2048) == (6, 1)
+    assert plan(dt, 1024, 2048, 8192) == (6, 1)
+    assert plan(dt, 2560, 2560, 2560)[0] == 0          # 400 tiles of 128 x 128
+    assert plan(dt, 2048, 2048, 2050, pad=2)[0] == 0   # K * elem_bytes not a multiple of 16
+    assert plan(dt, 256, 200, 8192)[0] == 0            # 4 tiles: split K wins
+    assert plan(dt, 256, 200, 8192)[1] > 1
+    assert plan(dt, 4096, 16, 4096)[0] == 4

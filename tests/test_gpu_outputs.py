@@ -40,7 +40,8 @@ def run_dense16(mcg, dtA, dtB, layA, layB, M, N, K, A, B, C, ldc, out, alpha, be
 
 DENSE_PAIRS = [("bf16", "bf16"), ("f16", "f16"), ("e4m3", "e4m3"), ("e4m3", "e5m2")]
 DENSE_CASES = [  # (M, N, K, pad, expected kernel, sampled)
-    (130, 140, 200, 8, 0, False),      # general kernel, ragged
+    (130, 140, 196, 8, 0, False),      # general kernel, ragged (K * 2 bytes not a multiple of 16)
+    (400, 272, 208, 16, 6, False),     # 128 x 128 form of the fast kernel, ragged M, N and K
     (2832, 2576, 208, 16, 1, True),    # 256 x 256 kernel, ragged M, N and K
     (1024, 16, 1040, 0, 4, False),     # streaming kernel (N <= 32)
 ]
@@ -49,7 +50,7 @@ DENSE_CASES = [  # (M, N, K, pad, expected kernel, sampled)
 @pytest.mark.parametrize("out", ["bf16", "f16"])
 @pytest.mark.parametrize("dtA,dtB", DENSE_PAIRS)
 @pytest.mark.parametrize("layA,layB", [("k_contig", "k_contig"), ("mn_contig", "mn_contig")])
-@pytest.mark.parametrize("case", DENSE_CASES, ids=["general", "tile256", "stream"])
+@pytest.mark.parametrize("case", DENSE_CASES, ids=["general", "tile128", "tile256", "stream"])
 def test_dense_16bit_output(out, dtA, dtB, layA, layB, case):
     mcg = need_gpu()
     M, N, K, pad, path, sampled = case
