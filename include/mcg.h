@@ -231,7 +231,8 @@ int mcg_validate_compress24(int dtype, int64_t M, int64_t K, const void* A, int6
      4 the streaming kernel (N <= 32 or M <= 32, K-contiguous aligned
      operands); 5 the binary64 kernel (dtypeA MCG_F64, any shape); 6 the
      pipelined kernel with 128 x 128 tiles (aligned operands, M and N >= 128,
-     at most 256 such tiles, too few 256 x 256 ones to fill the chip).
+     too few 256 x 256 tiles to fill the chip, faster than kernel 0 by the
+     planner's cost model).
    mcg_dense_splits: the number of K ranges (1 = no split) gemm_dense uses
      with exactly these arguments.
    mcg_sparse24_path: 1 if gemm_sparse24 runs the 256 x 256 pipelined kernel,

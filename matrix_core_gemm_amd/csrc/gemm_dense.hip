@@ -60,12 +60,10 @@ constexpr int64_t FAST_MIN_TILES = 128;   // 256 x 256 tiles from which the fast
 // K tile of a workgroup, ATOMIC_US per device-scope atomic add of D and
 // SPLIT_US for zeroing D and the extra launches.
 constexpr double KT_US = 1.0, ROUND_US = 3.0, ATOMIC_US = 1.4e-5, SPLIT_US = 5.0;
-// The 128 x 128 form of the fast kernel (KERNEL_MID) with at most one workgroup
-// per CU: MID_KT_US * nk + ROUND_US (measured over 100..256 tiles and K up to 16384).
-// Two of its workgroups on one CU disturb each other's ping-pong, so beyond
-// NUM_CU tiles the general kernel is faster; it is also taken only when it beats
-// the best general plan by MID_MARGIN.
-constexpr double MID_KT_US = 0.72, MID_MARGIN = 0.95;
+// The 128 x 128 form of the fast kernel (KERNEL_MID, one workgroup per CU):
+// ceil(tiles / NUM_CU) * (MID_KT_US * nk + MID_ROUND_US), fitted over 100..256
+// tiles and K up to 8192; taken when it beats the best general plan by MID_MARGIN.
+constexpr double MID_KT_US = 0.5, MID_ROUND_US = 8.0, MID_MARGIN = 0.95;
 // The streaming kernel is HBM-bound: split only when there are too few blocks
 // to spread over the CUs, keeping 16 K tiles or more per split.
 constexpr int64_t STREAM_MIN_BLOCKS = 64, STREAM_MIN_KT = 16;
@@ -111,10 +109,12 @@ DensePlan plan_dense(int dtA, int la, int lb, const DenseArgs& a, bool aligned, 
 
   if (fast_path_ok(dtA, la, lb, a, aligned) && cdiv(a.M, 256) * cdiv(a.N, 256) >= FAST_MIN_TILES)
     return make(KERNEL_FAST, 1);
-  if (fast_path_ok(dtA, la, lb, a, aligned, 128) && cdiv(a.M, 128) * cdiv(a.N, 128) <= NUM_CU) {
+  if (fast_path_ok(dtA, la, lb, a, aligned, 128)) {
+    const int64_t tiles = cdiv(a.M, 128) * cdiv(a.N, 128);
     double t_general;
-    plan_general(cdiv(a.M, 128) * cdiv(a.N, 128), &t_general);
-    if (MID_KT_US * (double)nk + ROUND_US < MID_MARGIN * t_general) return make(KERNEL_MID, 1);
+    plan_general(tiles, &t_general);
+    const double t_mid = (double)cdiv(tiles, NUM_CU) * (MID_KT_US * (double)nk + MID_ROUND_US);
+    if (t_mid < MID_MARGIN * t_general) return make(KERNEL_MID, 1);
   }
   if (stream_path_ok(dtA, la, lb, a, aligned)) {
     // 128-row blocks when that still gives most CUs a block, else 32-row blocks

@@ -33,9 +33,12 @@
 //     line-wise store); edge tiles use per-element bounds.
 //   - the 8 XCDs receive workgroups round-robin; the tile sequence is permuted
 //     so that the workgroups resident on one XCD cover a compact block of tiles.
-//   - 128 x 128 form: the same schedule with wave tiles of 64 x 32 and 16 KiB
-//     stages (80 KiB of LDS).  Two of its workgroups on one CU slow each
-//     other's ping-pong, so the host uses it for at most one tile per CU.
+//   - 128 x 128 form: the two wavefronts of a SIMD cover the same 64 x 64
+//     quadrant and split every K tile (one half each), so a phase holds 8
+//     instructions and a K tile 2 barriers; 3 stages of A and of B (16 KiB each)
+//     with a prefetch distance of 2 tiles; at the end each wave hands its partner
+//     the 32-row block the partner stores, through LDS.  The host uses it for at
+//     most one tile per CU.
 // Preconditions (checked on the host): 16-byte aligned operands, K * elem_bytes
 // and ld * elem_bytes multiples of 16, M, N >= the tile size, and each workgroup's
 // operand window below 2 GiB (32-bit buffer offsets).
@@ -60,7 +63,12 @@ void gemm_fast_kernel(DenseArgs p) {
   constexpr int EB = Op::EB;
   constexpr int LB16 = Op::LANE_BYTES;  // bytes of K per lane and instruction (16 or 32)
   constexpr int S = 64 / (2 * LB16);    // instructions per block and half K tile
-  constexpr int WTM = TB / 64, WTN = TB / 128;  // 32 x 32 instruction tiles per wave along m and n
+  // KS (128 x 128 tiles): the two wavefronts of a SIMD cover the same 64 x 64 quadrant
+  // and split every K tile, each multiplying one half; otherwise each covers half of
+  // the quadrant's columns over all of K
+  constexpr bool KS = TB == 128;
+  constexpr int WTM = TB / 64, WTN = KS ? 2 : TB / 128;  // 32 x 32 instruction tiles per wave
+  constexpr int NA = KS ? 3 : NSA;      // LDS stages of A (KS: prefetch distance 2 for both)
   using GA = Geom<EB, LA, BM, KTB>;
   using GB = Geom<EB, LB, BN, KTB>;
   using RA = Reader<EB, LA, BM, KTB>;
@@ -76,14 +84,14 @@ void gemm_fast_kernel(DenseArgs p) {
   constexpr int LH = LdA::INSTR / 2;  // loads per wave, operand and half stage (one group's share)
   static_assert(LdA::INSTR == LdB::INSTR && (LH == 4 || LH == 2), "vmcnt bookkeeping");
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[(NSA + NSB) * SB];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[(NA + NSB) * SB];
   lds_char* smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;  // 0: multiplies in even slots; 1: in odd slots
   const int q = wave & 3;     // wavefronts q and q + 4 share a SIMD and a quadrant of the tile
-  const int rbA = (q >> 1) * (TB / 2), rbB = (q & 1) * (TB / 2) + grp * (TB / 4);
+  const int rbA = (q >> 1) * (TB / 2), rbB = (q & 1) * (TB / 2) + (KS ? 0 : grp * (TB / 4));
   const int g = lane >> 5;
 
   int tm, tn;
@@ -108,8 +116,8 @@ void gemm_fast_kernel(DenseArgs p) {
     for (int j = 0; j < WTN; ++j) acc[i][j] = acc_t{};
 
   const int nk = (int)((p.K + KTB / EB - 1) / (KTB / EB));
-  auto stA = [&](int kt) { return smem + (kt & 1) * SB; };
-  auto stB = [&](int kt) { return smem + NSA * SB + (kt % NSB) * SB; };
+  auto stA = [&](int kt) { return smem + (KS ? kt % NA : kt & 1) * SB; };
+  auto stB = [&](int kt) { return smem + NA * SB + (kt % NSB) * SB; };
   // this group's half (LH of the 2 LH load instructions per wave) of operand X of K tile kt
   const int ihalf = LH * grp;
   auto issueA = [&](int kt) { la.issue(stA(kt), kt, ihalf, LH, q); };
@@ -184,6 +192,47 @@ void gemm_fast_kernel(DenseArgs p) {
   // At the end of slot 4t + 2 each wave waits until only its newest LH loads
   // (its half of B(t+2)) are in flight, so tile t+1 is complete from slot 4t+3.
   // DMA of tiles at or beyond nk read nothing and fill their stage with zeros.
+  if constexpr (KS) {
+    // Group g reads half g of K tile t in slot 2t - 1 + g and multiplies it in the
+    // next slot.  Each memory phase issues this wave's shares of A(t+2) and B(t+2)
+    // into the stages of tile t-1 (last read in slot 2t - 2); at the end of slot 2t
+    // each wave waits until only those newest 2 LH loads are in flight, so tile t+1
+    // is complete from slot 2t + 1.
+    issueA(0);
+    issueB(0);
+    issueA(1);
+    issueB(1);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LH) : "memory");  // own shares of tile 0
+    barrier_lds();
+    if (grp == 0) {
+      for (int t = 0; t < nk; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        issueA(t + 2);
+        issueB(t + 2);
+        read_frags(t, 0);  // slot 2t - 1
+        barrier_lds();
+        __builtin_amdgcn_sched_barrier(0);
+        multiply();  // slot 2t
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LH) : "memory");  // own shares of tile t+1
+        barrier_lds();
+      }
+    } else {
+      barrier_lds();  // slot -1
+      for (int t = 0; t < nk; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        issueA(t + 2);
+        issueB(t + 2);
+        read_frags(t, 1);  // slot 2t
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LH) : "memory");  // own shares of tile t+1
+        barrier_lds();
+        __builtin_amdgcn_sched_barrier(0);
+        multiply();  // slot 2t + 1
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 1 < nk) barrier_lds();
+      }
+    }
+  } else {
   issueB(0);
   issueA(0);
   issueB(1);
@@ -229,7 +278,39 @@ void gemm_fast_kernel(DenseArgs p) {
       if (t + 1 < nk) barrier_lds();
     }
   }
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA outstanding at exit
+  if constexpr (KS) {
+    // Sum the two K halves: wave w hands its partner (w ^ 4) the 32-row block
+    // i = 1 - grp, which the partner stores, through 8 KiB of LDS per wave.
+    using e1 = typename std::conditional<Op::INT_ACC, int, float>::type;
+    typedef __attribute__((address_space(3))) e1 lds_e1;
+    barrier_lds();  // all LDS DMA has landed; no fragment reads remain
+    lds_e1* mine = (lds_e1*)(smem + wave * 8192);
+    const lds_e1* theirs = (const lds_e1*)(smem + (wave ^ 4) * 8192);
+    auto put = [&](const acc_t (&blk)[WTN]) {
+#pragma unroll
+      for (int j = 0; j < WTN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine[(j * 16 + r) * 64 + lane] = blk[j][r];
+    };
+    auto add = [&](acc_t (&blk)[WTN]) {
+#pragma unroll
+      for (int j = 0; j < WTN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if constexpr (Op::INT_ACC)
+            blk[j][r] = (int)((uint32_t)blk[j][r] + (uint32_t)theirs[(j * 16 + r) * 64 + lane]);
+          else
+            blk[j][r] += theirs[(j * 16 + r) * 64 + lane];
+        }
+    };
+    if (grp == 0) put(acc[1]);
+    else put(acc[0]);
+    barrier_lds();
+    if (grp == 0) add(acc[0]);
+    else add(acc[1]);
+  }
 
   // epilogue: tile (i, j), register group r4: lane holds D[m][n .. n+3] with
   // m = m0 + rbA + 32 i + (lane & 31), n = n0 + rbB + 32 j + 8 r4 + 4 (lane >> 5)
@@ -357,6 +438,7 @@ void gemm_fast_kernel(DenseArgs p) {
 #pragma unroll
       for (int i = 0; i < WTM; ++i) {
         __builtin_amdgcn_sched_barrier(0);
+        if (KS && i != grp) continue;  // the partner wave stores this row block
         const int64_t m = m0 + rbA + 32 * i + (lane & 31);
         if (m >= p.M) continue;
 #pragma unroll
@@ -390,6 +472,7 @@ void gemm_fast_kernel(DenseArgs p) {
     // edge tile: per-element bounds
 #pragma unroll
     for (int i = 0; i < WTM; ++i) {
+      if (KS && i != grp) continue;  // the partner wave stores this row block
       const int64_t m = m0 + rbA + 32 * i + (lane & 31);
       if (m >= p.M) continue;
 #pragma unroll

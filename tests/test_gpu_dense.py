@@ -137,15 +137,15 @@ def test_256_tile_path_ragged(dtA, dtB, layA, layB, shape):
     check_case_sampled(mcg, dtA, dtB, layA, layB, M, N, K, pad=pad, ldc_pad=4, seed=3, expect_path=1)
 
 
-# Shapes taken by the 128 x 128 form of the same kernel (at most 256 such tiles,
-# too few 256 x 256 ones to fill the chip): ragged M and N tiles, K ending inside a
-# stage, a single partial stage, padded leading dimensions.
-MID_SHAPES = [(1936, 1808, 208, 16), (1040, 2064, 1040, 32), (2000, 1008, 80, 0)]
+# Shapes taken by the 128 x 128 form of the same kernel (too few 256 x 256 tiles to
+# fill the chip, K long enough for it to beat the general kernel): ragged M and N
+# tiles, K ending inside a stage, padded leading dimensions.
+MID_SHAPES = [(1936, 1808, 2064, 16), (1040, 2064, 2080, 32), (2000, 1008, 2128, 0)]
 
 
 @pytest.mark.parametrize("dtA,dtB", PAIRS)
 @pytest.mark.parametrize("layA,layB", LAYOUTS)
-@pytest.mark.parametrize("shape", MID_SHAPES, ids=["1936x1808x208", "1040x2064x1040", "2000x1008x80"])
+@pytest.mark.parametrize("shape", MID_SHAPES, ids=["1936x1808x2064", "1040x2064x2080", "2000x1008x2128"])
 def test_128_tile_path_ragged(dtA, dtB, layA, layB, shape):
     mcg = need_gpu()
     M, N, K, pad = shape
@@ -158,7 +158,7 @@ def test_small_integers_bit_exact_128_tiles(dtA, dtB, layA, layB):
     """Exactly representable partial sums on the 128 x 128 form (ragged M and N, K
     ending inside a stage): the sampled outputs must equal the oracle bit for bit."""
     mcg = need_gpu()
-    M, N, K = 1808, 1808, 1104
+    M, N, K = 1808, 1808, 2128
     r = min(SMALL[dtA], SMALL[dtB])
     check_case_sampled(mcg, dtA, dtB, layA, layB, M, N, K, seed=25, dist=f"smallint{r}", alpha=1.0,
                        beta=1.0, expect_path=6, exact=True)

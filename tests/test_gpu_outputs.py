@@ -41,7 +41,7 @@ def run_dense16(mcg, dtA, dtB, layA, layB, M, N, K, A, B, C, ldc, out, alpha, be
 DENSE_PAIRS = [("bf16", "bf16"), ("f16", "f16"), ("e4m3", "e4m3"), ("e4m3", "e5m2")]
 DENSE_CASES = [  # (M, N, K, pad, expected kernel, sampled)
     (130, 140, 196, 8, 0, False),      # general kernel, ragged (K * 2 bytes not a multiple of 16)
-    (400, 272, 208, 16, 6, False),     # 128 x 128 form of the fast kernel, ragged M, N and K
+    (1008, 752, 2080, 16, 6, True),    # 128 x 128 form of the fast kernel, ragged M, N and K
     (2832, 2576, 208, 16, 1, True),    # 256 x 256 kernel, ragged M, N and K
     (1024, 16, 1040, 0, 4, False),     # streaming kernel (N <= 32)
 ]
