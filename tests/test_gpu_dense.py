@@ -164,6 +164,22 @@ def test_small_integers_bit_exact_128_tiles(dtA, dtB, layA, layB):
                        beta=1.0, expect_path=6, exact=True)
 
 
+FP8_PAIRS = [p for p in PAIRS if p[0] in ("e4m3", "e5m2")]
+
+
+@pytest.mark.parametrize("dtA,dtB", FP8_PAIRS)
+@pytest.mark.parametrize("layA,layB", LAYOUTS)
+@pytest.mark.parametrize("exact", [False, True], ids=["normal", "smallint"])
+def test_128_tile_fp8_native(dtA, dtB, layA, layB, exact):
+    """K = 6160 (ragged, past 6144): the 128 x 128 form with the native fp8 instruction
+    (32 bytes of K per lane); N(0,1) within the bound, small integers bit for bit."""
+    mcg = need_gpu()
+    r = min(SMALL[dtA], SMALL[dtB])
+    check_case_sampled(mcg, dtA, dtB, layA, layB, 1040, 1168, 6160, pad=16, ldc_pad=4, seed=27,
+                       dist=f"smallint{r}" if exact else None, alpha=1.0 if exact else None,
+                       expect_path=6, exact=exact)
+
+
 @pytest.mark.parametrize("dtA,dtB", [p for p in PAIRS if p[0] != "i8"])
 @pytest.mark.parametrize("layA,layB", LAYOUTS)
 def test_small_integers_bit_exact_256_tiles(dtA, dtB, layA, layB):
