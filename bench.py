@@ -43,7 +43,7 @@ HBM_PEAK_GBS = 8000.0
 # traffic is reported as null.
 KERNEL_SOURCES = ("gemm_fast.hip", "fast_tiles.hpp", "arch_gfx950.hpp")
 TRAFFIC_MEASURED = {
-    "sources_sha256": "bc07924749f8ea8251f35e9b10d595acfd749621ba687da0bc76f05cbf495534",
+    "sources_sha256": "d4bc5af5af548a1604ab28a2a2ff218778811fdd88cadebca65a54a2290171f9",
     "read_bytes": 1806 * 2**20, "write_bytes": 256 * 2**20,
 }
 

@@ -37,8 +37,9 @@
 //     quadrant and split every K tile (one half each), so a phase holds 8
 //     instructions and a K tile 2 barriers; 3 stages of A and of B (16 KiB each)
 //     with a prefetch distance of 2 tiles; at the end each wave hands its partner
-//     the 32-row block the partner stores, through LDS.  The host uses it for at
-//     most one tile per CU.
+//     the 32-row block the partner stores, through LDS.  96 KiB of LDS: one
+//     workgroup per CU.  The host takes it for problems with too few 256 x 256
+//     tiles when its cost model puts it ahead of the general kernel.
 // Preconditions (checked on the host): 16-byte aligned operands, K * elem_bytes
 // and ld * elem_bytes multiples of 16, M, N >= the tile size, and each workgroup's
 // operand window below 2 GiB (32-bit buffer offsets).
