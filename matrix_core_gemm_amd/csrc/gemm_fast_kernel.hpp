@@ -1,0 +1,547 @@
+// gemm_fast_kernel.hpp -- the pipelined dense MFMA kernel template, shared by the
+// translation units that instantiate its two tile sizes (gemm_fast.hip: 256 x 256 and the
+// host-side choice; gemm_fast_mid.hip: 128 x 128).  It is the fast path of gemm_dense
+// for aligned problems of at least 256 x 256, and in its 128 x 128 form for aligned
+// problems with too few 256 x 256 tiles to fill the chip.
+//
+// Same operation as gemm_dense.hip (the matrix fused multiply-add of "Accurate
+// Models of AMD Matrix Cores", Section 2, Eq. (1), tiled over K as in "CDNA3
+// dense MFMA builtins", Using MFMA builtins as a compute policy); what differs
+// is the mapping onto CDNA4:
+//   - 256 x 256 output tile per workgroup of 8 wavefronts, two per SIMD
+//     (wavefronts w and w + 4 share a SIMD, measured).  Each wavefront owns a
+//     128 x 64 sub-tile = 4 x 2 instructions of 32 x 32 (128 accumulator
+//     registers per lane).
+//   - K is staged in tiles of 128 bytes per row (64 bf16 / 128 8-bit values),
+//     so that every 8 lanes of a load fetch one whole 128-byte line: twice the
+//     bytes per outstanding L1 miss of a 64-byte tile, which measured as the
+//     limit of the HBM -> LDS stream.  A has 2 LDS stages and B 3 (32 KiB each,
+//     160 KiB), filled by buffer_load ... lds (16 bytes per lane, no VGPRs).
+//     The XOR swizzle of the LDS rows is folded into the global address each
+//     lane loads; chunks outside the matrix get an out-of-range offset and the
+//     buffer unit writes zeros.
+//   - ping-pong schedule: the two wavefronts of a SIMD alternate between a
+//     multiply phase (only matrix instructions, on fragments already in
+//     registers) and a memory phase (LDS -> register reads of the next half K
+//     tile's fragments and 4 DMA issues per wave), separated by workgroup
+//     barriers, so that one of them keeps the SIMD's matrix core busy while
+//     the other waits on memory.
+//   - epilogue: a lane's accumulators hold 4 consecutive columns of one row
+//     (each instruction is issued with the B fragment as its first operand).
+//     Interior tiles pass each wavefront's 32 x 64 blocks through LDS, so that 16
+//     lanes read C and write D = alpha * acc + beta * C along one row segment
+//     (whole lines: storing from the accumulator layout wrote 32 rows x 16 or 32
+//     bytes per instruction, and the fixed cost of the launch was twice that of a
+//     line-wise store); edge tiles use per-element bounds.
+//   - the 8 XCDs receive workgroups round-robin; the tile sequence is permuted
+//     so that the workgroups resident on one XCD cover a compact block of tiles.
+//   - 128 x 128 form: the two wavefronts of a SIMD cover the same 64 x 64
+//     quadrant and split every K tile (one half each), so a phase holds 8
+//     instructions and a K tile 2 barriers; 3 stages of A and of B (16 KiB each)
+//     with a prefetch distance of 2 tiles; at the end each wave hands its partner
+//     the 32-row block the partner stores, through LDS.  96 KiB of LDS: one
+//     workgroup per CU.  The host takes it for problems with too few 256 x 256
+//     tiles when its cost model puts it ahead of the general kernel.
+// Preconditions (checked on the host): 16-byte aligned operands, K * elem_bytes
+// and ld * elem_bytes multiples of 16, M, N >= the tile size, and each workgroup's
+// operand window below 2 GiB (32-bit buffer offsets).
+#pragma once
+#include "fast_tiles.hpp"
+#include "gemm_kernels.hpp"
+
+namespace mcg {
+namespace fast {
+
+constexpr int KTB = 128;     // bytes of K per LDS row and stage: one 128-byte line per row
+constexpr int NSA = 2;       // LDS stages of A
+constexpr int NSB = 3;       // LDS stages of B
+constexpr int THREADS = 512;
+
+// TB: output tile TB x TB (256, or 128 for problems with too few 256 x 256 tiles to
+// fill the chip); each wavefront owns (TB / 2) x (TB / 4) outputs.
+template <class Op, int LA, int LB, int TB>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_fast_kernel(DenseArgs p) {
+  constexpr int BM = TB, BN = TB;
+  constexpr int SB = TB * KTB;          // bytes of one operand stage
+  constexpr int EB = Op::EB;
+  constexpr int LB16 = Op::LANE_BYTES;  // bytes of K per lane and instruction (16 or 32)
+  constexpr int S = 64 / (2 * LB16);    // instructions per block and half K tile
+  // KS (128 x 128 tiles): the two wavefronts of a SIMD cover the same 64 x 64 quadrant
+  // and split every K tile, each multiplying one half; otherwise each covers half of
+  // the quadrant's columns over all of K
+  constexpr bool KS = TB == 128;
+  constexpr int WTM = TB / 64, WTN = KS ? 2 : TB / 128;  // 32 x 32 instruction tiles per wave
+  constexpr int NA = KS ? 3 : NSA;      // LDS stages of A (KS: prefetch distance 2 for both)
+  using GA = Geom<EB, LA, BM, KTB>;
+  using GB = Geom<EB, LB, BN, KTB>;
+  using RA = Reader<EB, LA, BM, KTB>;
+  using RB = Reader<EB, LB, BN, KTB>;
+  using LdA = LineLoader<EB, LA, BM, KTB>;
+  using LdB = LineLoader<EB, LB, BN, KTB>;
+  using acc_t = typename Op::acc_t;
+  using frag_t = typename Op::frag_t;
+  using v4 = typename std::conditional<Op::INT_ACC, i32x4, f32x4>::type;
+  using s1 = typename std::conditional<Op::INT_ACC, int, float>::type;
+  static_assert(TB == 256 || TB == 128, "tile");
+  static_assert(GA::BYTES == SB && GB::BYTES == SB, "one stage size for both operands");
+  constexpr int LH = LdA::INSTR / 2;  // loads per wave, operand and half stage (one group's share)
+  static_assert(LdA::INSTR == LdB::INSTR && (LH == 4 || LH == 2), "vmcnt bookkeeping");
+
+  __shared__ __attribute__((aligned(1024))) char smem_raw[(NA + NSB) * SB];
+  lds_char* smem = (lds_char*)smem_raw;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: multiplies in even slots; 1: in odd slots
+  const int q = wave & 3;     // wavefronts q and q + 4 share a SIMD and a quadrant of the tile
+  const int rbA = (q >> 1) * (TB / 2), rbB = (q & 1) * (TB / 2) + (KS ? 0 : grp * (TB / 4));
+  const int g = lane >> 5;
+
+  int tm, tn;
+  tile_coords<4>(p.tiles_m, p.tiles_n, tm, tn);  // XCD-aware, grouped tile order
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+  LdA la;
+  LdB lb;
+  if constexpr (LA == LAYOUT_K)
+    la.init(p.A + m0 * p.lda * EB, (uint32_t)(min(p.M - m0, (int64_t)BM) * p.lda * EB), p.lda, p.K, q, lane);
+  else
+    la.init(p.A + m0 * EB, (uint32_t)((p.K * p.lda - m0) * EB), p.lda, p.K, q, lane);
+  if constexpr (LB == LAYOUT_K)
+    lb.init(p.B + n0 * p.ldb * EB, (uint32_t)(min(p.N - n0, (int64_t)BN) * p.ldb * EB), p.ldb, p.K, q, lane);
+  else
+    lb.init(p.B + n0 * EB, (uint32_t)((p.K * p.ldb - n0) * EB), p.ldb, p.K, q, lane);
+
+  acc_t acc[WTM][WTN];
+#pragma unroll
+  for (int i = 0; i < WTM; ++i)
+#pragma unroll
+    for (int j = 0; j < WTN; ++j) acc[i][j] = acc_t{};
+
+  const int nk = (int)((p.K + KTB / EB - 1) / (KTB / EB));
+  auto stA = [&](int kt) { return smem + (KS ? kt % NA : kt & 1) * SB; };
+  auto stB = [&](int kt) { return smem + NA * SB + (kt % NSB) * SB; };
+  // this group's half (LH of the 2 LH load instructions per wave) of operand X of K tile kt
+  const int ihalf = LH * grp;
+  auto issueA = [&](int kt) { la.issue(stA(kt), kt, ihalf, LH, q); };
+  auto issueB = [&](int kt) { lb.issue(stB(kt), kt, ihalf, LH, q); };
+
+  frag_t fa[S][WTM], fb[S][WTN];
+  // fragments of half h (K bytes [64h, 64h + 64) of each row) of K tile kt;
+  // instruction s of the half takes lane group g's bytes [64h + 2 LB16 s + LB16 g, +LB16)
+  auto read_frags = [&](int kt, int h) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int kb = 64 * h + 2 * LB16 * s + LB16 * g;
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        if constexpr (LB16 == 16) {
+          fa[s][i] = RA::read16k(stA(kt), rbA + 32 * i, kb, lane);
+        } else {
+          const i32x4 x = RA::read16k(stA(kt), rbA + 32 * i, kb, lane);
+          const i32x4 y = RA::read16k(stA(kt), rbA + 32 * i, kb + 16, lane);
+          fa[s][i] = frag_t{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < WTN; ++j) {
+        if constexpr (LB16 == 16) {
+          fb[s][j] = RB::read16k(stB(kt), rbB + 32 * j, kb, lane);
+        } else {
+          const i32x4 x = RB::read16k(stB(kt), rbB + 32 * j, kb, lane);
+          const i32x4 y = RB::read16k(stB(kt), rbB + 32 * j, kb + 16, lane);
+          fb[s][j] = frag_t{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+        }
+      }
+    }
+  };
+  auto multiply = [&]() {
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int i = 0; i < WTM; ++i)
+#pragma unroll
+        for (int j = 0; j < WTN; ++j) Op::mma(acc[i][j], fb[s][j], fa[s][i]);
+  };
+  // Memory phase of half tile (t, H): this group's DMA half and the fragment
+  // reads.  The DMA targets another stage than the reads, so with K-contiguous
+  // operands it goes first (more time in flight).  Transposing reads of an
+  // MN-contiguous operand are preceded by a compiler-inserted wait for all of
+  // the wave's LDS DMA, so there the reads go first.
+  auto dma = [&](auto hc, int t) {
+    if constexpr (decltype(hc)::value == 0) issueA(t + 1);
+    else issueB(t + 2);
+  };
+  auto mem = [&](auto hc, int t) {
+    if constexpr (LA == LAYOUT_K && LB == LAYOUT_K) {
+      dma(hc, t);
+      read_frags(t, decltype(hc)::value);
+    } else {
+      read_frags(t, decltype(hc)::value);
+      dma(hc, t);
+    }
+  };
+
+  // Half tiles u = 2t + h.  Group 0 reads half u in slot 2u - 1 and multiplies
+  // it in slot 2u; group 1 reads it in slot 2u and multiplies it in slot
+  // 2u + 1; slots are separated by workgroup barriers.  K tile t (A stage
+  // t % 2, B stage t % 3) is last read in slot 4t + 2 and first needed in slot
+  // 4t + 3 (= 4(t+1) - 1 for tile t + 1).  DMA halves, 4 instructions per wave
+  // in every memory phase:
+  //   slot 4t     (group 1): second half of A(t+1)  -> A stage of tile t-1, free since slot 4t-1
+  //   slot 4t + 1 (group 0): first half of B(t+2)   -> B stage of tile t-1
+  //   slot 4t + 2 (group 1): second half of B(t+2)
+  //   slot 4t + 3 (group 0): first half of A(t+2)   -> A stage of tile t, free since slot 4t+3
+  // At the end of slot 4t + 2 each wave waits until only its newest LH loads
+  // (its half of B(t+2)) are in flight, so tile t+1 is complete from slot 4t+3.
+  // DMA of tiles at or beyond nk read nothing and fill their stage with zeros.
+  if constexpr (KS) {
+    // Group g reads half g of K tile t in slot 2t - 1 + g and multiplies it in the
+    // next slot.  Each memory phase issues this wave's shares of A(t+2) and B(t+2)
+    // into the stages of tile t-1 (last read in slot 2t - 2); at the end of slot 2t
+    // each wave waits until only those newest 2 LH loads are in flight, so tile t+1
+    // is complete from slot 2t + 1.
+    issueA(0);
+    issueB(0);
+    issueA(1);
+    issueB(1);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LH) : "memory");  // own shares of tile 0
+    barrier_lds();
+    if (grp == 0) {
+      for (int t = 0; t < nk; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        issueA(t + 2);
+        issueB(t + 2);
+        read_frags(t, 0);  // slot 2t - 1
+        barrier_lds();
+        __builtin_amdgcn_sched_barrier(0);
+        multiply();  // slot 2t
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LH) : "memory");  // own shares of tile t+1
+        barrier_lds();
+      }
+    } else {
+      barrier_lds();  // slot -1
+      for (int t = 0; t < nk; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        issueA(t + 2);
+        issueB(t + 2);
+        read_frags(t, 1);  // slot 2t
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LH) : "memory");  // own shares of tile t+1
+        barrier_lds();
+        __builtin_amdgcn_sched_barrier(0);
+        multiply();  // slot 2t + 1
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 1 < nk) barrier_lds();
+      }
+    }
+  } else {
+  issueB(0);
+  issueA(0);
+  issueB(1);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LH) : "memory");  // own shares of tile 0 have landed
+  barrier_lds();
+  // The two half tiles of a K tile are written out (no run-time choice between
+  // the A and B loads, whose buffer descriptors then stay in scalar registers).
+  if (grp == 0) {
+    for (int t = 0; t < nk; ++t) {
+      __builtin_amdgcn_sched_barrier(0);
+      mem(std::integral_constant<int, 0>{}, t);  // slot 4t - 1
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      multiply();  // slot 4t
+      __builtin_amdgcn_sched_barrier(0);
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      mem(std::integral_constant<int, 1>{}, t);  // slot 4t + 1
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      multiply();  // slot 4t + 2
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LH) : "memory");  // own shares of tile t+1
+      barrier_lds();
+    }
+  } else {
+    barrier_lds();  // slot -1
+    for (int t = 0; t < nk; ++t) {
+      __builtin_amdgcn_sched_barrier(0);
+      mem(std::integral_constant<int, 0>{}, t);  // slot 4t
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      multiply();  // slot 4t + 1
+      __builtin_amdgcn_sched_barrier(0);
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      mem(std::integral_constant<int, 1>{}, t);  // slot 4t + 2
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LH) : "memory");  // own shares of tile t+1
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      multiply();  // slot 4t + 3
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < nk) barrier_lds();
+    }
+  }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA outstanding at exit
+  if constexpr (KS) {
+    // Sum the two K halves: wave w hands its partner (w ^ 4) the 32-row block
+    // i = 1 - grp, which the partner stores, through 8 KiB of LDS per wave.
+    using e1 = typename std::conditional<Op::INT_ACC, int, float>::type;
+    typedef __attribute__((address_space(3))) e1 lds_e1;
+    barrier_lds();  // all LDS DMA has landed; no fragment reads remain
+    lds_e1* mine = (lds_e1*)(smem + wave * 8192);
+    const lds_e1* theirs = (const lds_e1*)(smem + (wave ^ 4) * 8192);
+    auto put = [&](const acc_t (&blk)[WTN]) {
+#pragma unroll
+      for (int j = 0; j < WTN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine[(j * 16 + r) * 64 + lane] = blk[j][r];
+    };
+    auto add = [&](acc_t (&blk)[WTN]) {
+#pragma unroll
+      for (int j = 0; j < WTN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if constexpr (Op::INT_ACC)
+            blk[j][r] = (int)((uint32_t)blk[j][r] + (uint32_t)theirs[(j * 16 + r) * 64 + lane]);
+          else
+            blk[j][r] += theirs[(j * 16 + r) * 64 + lane];
+        }
+    };
+    if (grp == 0) put(acc[1]);
+    else put(acc[0]);
+    barrier_lds();
+    if (grp == 0) add(acc[0]);
+    else add(acc[1]);
+  }
+
+  // epilogue: tile (i, j), register group r4: lane holds D[m][n .. n+3] with
+  // m = m0 + rbA + 32 i + (lane & 31), n = n0 + rbB + 32 j + 8 r4 + 4 (lane >> 5)
+  const bool vec_ok = p.vec_cd;
+  const s1* C = (const s1*)p.C;
+  s1* D = (s1*)p.D;
+  if constexpr (Op::INT_ACC) {
+    // wrapping alpha * acc, in place (keeps the products out of the C batches)
+    if (p.alpha_i != 1) {
+#pragma unroll
+      for (int i = 0; i < WTM; ++i)
+#pragma unroll
+        for (int j = 0; j < WTN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = (int)((uint32_t)p.alpha_i * (uint32_t)acc[i][j][r]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  auto combine = [&](const acc_t& a, int r4, const v4& c, bool use_c) {
+    v4 o;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (Op::INT_ACC)
+        o[r] = (int)((uint32_t)a[4 * r4 + r] + (use_c ? (uint32_t)p.beta_i * (uint32_t)c[r] : 0u));
+      else
+        o[r] = use_c ? __builtin_fmaf(p.alpha, a[4 * r4 + r], p.beta * c[r]) : p.alpha * a[4 * r4 + r];
+    }
+    return o;
+  };
+  if constexpr (TB == 256) if (vec_ok && m0 + BM <= p.M && n0 + BN <= p.N) {
+    // Interior tile.  Each wavefront passes the 32 x 64 block of its row group i
+    // through LDS (8 KiB, two buffers), so that 16 lanes then read C and write D
+    // along one row segment (256 bytes of binary32 / int32, 128 of 16-bit values):
+    // whole lines per store instruction instead of 32 rows x 16 or 32 bytes.
+    // Chunk ch (16 bytes) of staging row r sits at ch ^ (r & 15): the writes (32
+    // rows at one chunk) and the reads (4 rows x 16 chunks) are free of bank conflicts.
+    barrier_lds();  // all LDS DMA has landed (vmcnt(0) above); no fragment reads remain
+    typedef __attribute__((address_space(3))) v4 lds_v4;
+    lds_char* wbuf = smem + wave * 16384;
+    const int wr = lane & 31, rr = lane >> 4, cc = lane & 15;
+    const int64_t col = n0 + rbB + 4 * cc;
+    const int out = p.out;
+    auto combine4 = [&](const v4& a, const v4& c) {
+      v4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (Op::INT_ACC)
+          o[r] = (int)((uint32_t)a[r] + (p.use_c ? (uint32_t)p.beta_i * (uint32_t)c[r] : 0u));
+        else
+          o[r] = p.use_c ? __builtin_fmaf(p.alpha, a[r], p.beta * c[r]) : p.alpha * a[r];
+      }
+      return o;
+    };
+#pragma unroll
+    for (int i = 0; i < WTM; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      lds_char* buf = wbuf + (i & 1) * 8192;
+#pragma unroll
+      for (int j = 0; j < WTN; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int ch = 8 * j + 2 * r4 + (lane >> 5);
+          v4 x;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] = acc[i][j][4 * r4 + r];
+          *(lds_v4*)(buf + wr * 256 + ((ch ^ (wr & 15)) << 4)) = x;
+        }
+      // the reads below take other lanes' values: wait for the writes
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      v4 a[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int row = 4 * t + rr;
+        a[t] = *(const lds_v4*)(buf + row * 256 + ((cc ^ (row & 15)) << 4));
+      }
+      const int64_t rbase = (m0 + rbA + 32 * i + rr) * p.ldc + col;  // row 4t further: + 4t ldc
+      if constexpr (!Op::INT_ACC) {
+        if (out != OUT_32) {
+          const uint16_t* C16 = (const uint16_t*)p.C;
+          uint16_t* D16 = (uint16_t*)p.D;
+          i32x2 cw[8];
+          if (p.use_c) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) cw[t] = *(const i32x2*)(C16 + rbase + 4 * t * p.ldc);
+          }
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            v4 c = {};
+            if (p.use_c)
+              c = v4{from_out_bits(out, (uint32_t)cw[t].x & 0xffffu), from_out_bits(out, (uint32_t)cw[t].x >> 16),
+                     from_out_bits(out, (uint32_t)cw[t].y & 0xffffu), from_out_bits(out, (uint32_t)cw[t].y >> 16)};
+            const v4 o = combine4(a[t], c);
+            *(i32x2*)(D16 + rbase + 4 * t * p.ldc) =
+                i32x2{(int)(to_out_bits(out, o[0]) | (to_out_bits(out, o[1]) << 16)),
+                      (int)(to_out_bits(out, o[2]) | (to_out_bits(out, o[3]) << 16))};
+          }
+          continue;
+        }
+      }
+      v4 cv[8];
+      if (p.use_c) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) cv[t] = *(const v4*)(C + rbase + 4 * t * p.ldc);
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) *(v4*)(D + rbase + 4 * t * p.ldc) = combine4(a[t], p.use_c ? cv[t] : v4{});
+    }
+    return;
+  }
+  if constexpr (!Op::INT_ACC) {
+    if (p.out != OUT_32) {
+      // bfloat16 / binary16 C and D: 4 consecutive elements = 8 bytes per lane
+      // and row segment; the fp32 result is rounded once to the output format
+      const int out = p.out;
+      const uint16_t* C16 = (const uint16_t*)p.C;
+      uint16_t* D16 = (uint16_t*)p.D;
+      auto unpack = [&](const i32x2 w) {
+        return v4{from_out_bits(out, (uint32_t)w.x & 0xffffu), from_out_bits(out, (uint32_t)w.x >> 16),
+                  from_out_bits(out, (uint32_t)w.y & 0xffffu), from_out_bits(out, (uint32_t)w.y >> 16)};
+      };
+      auto pack = [&](const v4& o) {
+        return i32x2{(int)(to_out_bits(out, o[0]) | (to_out_bits(out, o[1]) << 16)),
+                     (int)(to_out_bits(out, o[2]) | (to_out_bits(out, o[3]) << 16))};
+      };
+#pragma unroll
+      for (int i = 0; i < WTM; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (KS && i != grp) continue;  // the partner wave stores this row block
+        const int64_t m = m0 + rbA + 32 * i + (lane & 31);
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < WTN; ++j)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int64_t n = n0 + rbB + 32 * j + 8 * r4 + 4 * (lane >> 5);
+            if (n >= p.N) continue;
+            const int64_t off = m * p.ldc + n;
+            const bool full = vec_ok && n + 4 <= p.N;
+            v4 c = {};
+            if (p.use_c) {
+              if (full) c = unpack(*(const i32x2*)(C16 + off));
+              else
+                for (int r = 0; r < 4; ++r)
+                  if (n + r < p.N) c[r] = from_out_bits(out, C16[off + r]);
+            }
+            const v4 o = combine(acc[i][j], r4, c, p.use_c);
+            if (full) {
+              *(i32x2*)(D16 + off) = pack(o);
+            } else {
+              for (int r = 0; r < 4; ++r)
+                if (n + r < p.N) D16[off + r] = (uint16_t)to_out_bits(out, o[r]);
+            }
+          }
+      }
+      return;
+    }
+  }
+  {
+    // edge tile: per-element bounds
+#pragma unroll
+    for (int i = 0; i < WTM; ++i) {
+      if (KS && i != grp) continue;  // the partner wave stores this row block
+      const int64_t m = m0 + rbA + 32 * i + (lane & 31);
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < WTN; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int64_t n = n0 + rbB + 32 * j + 8 * r4 + 4 * (lane >> 5);
+          if (n >= p.N) continue;
+          const bool full = vec_ok && n + 4 <= p.N;
+          v4 c = {};
+          if (p.use_c) {
+            if (full) c = *(const v4*)(C + m * p.ldc + n);
+            else
+              for (int r = 0; r < 4; ++r)
+                if (n + r < p.N) c[r] = C[m * p.ldc + n + r];
+          }
+          const v4 o = combine(acc[i][j], r4, c, p.use_c);
+          if (full) {
+            *(v4*)(D + m * p.ldc + n) = o;
+          } else {
+            for (int r = 0; r < 4; ++r)
+              if (n + r < p.N) D[m * p.ldc + n + r] = o[r];
+          }
+        }
+    }
+  }
+}
+
+template <class Op, int LA, int LB, int TB>
+hipError_t launch_one(const DenseArgs& a0, hipStream_t s) {
+  DenseArgs a = a0;
+  a.tiles_m = (int)((a.M + TB - 1) / TB);
+  a.tiles_n = (int)((a.N + TB - 1) / TB);
+  const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_fast_kernel<Op, LA, LB, TB>), dim3((unsigned)blocks), dim3(THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+template <class Op, int TB>
+hipError_t launch_layouts_tb(int la, int lb, const DenseArgs& a, hipStream_t s) {
+  if (la == 0 && lb == 0) return launch_one<Op, 0, 0, TB>(a, s);
+  if (la == 0 && lb == 1) return launch_one<Op, 0, 1, TB>(a, s);
+  if (la == 1 && lb == 0) return launch_one<Op, 1, 0, TB>(a, s);
+  return launch_one<Op, 1, 1, TB>(a, s);
+}
+
+// Operation-type dispatch for tile size TB (one translation unit per TB).
+template <int TB>
+hipError_t launch_fast_tb(int dtA, int dtB, int la, int lb, const DenseArgs& a, hipStream_t s) {
+  if (dtA == DT_BF16) return launch_layouts_tb<BF16, TB>(la, lb, a, s);
+  if (dtA == DT_F16) return launch_layouts_tb<F16, TB>(la, lb, a, s);
+  if (dtA == DT_I8) return launch_layouts_tb<I8, TB>(la, lb, a, s);
+  const int fa = f8fmt(dtA), fb = f8fmt(dtB);
+  if (a.K >= FP8_NATIVE_MIN_K) {
+    if (fb == 0 && fa == 0) return launch_layouts_tb<F8<0, 0>, TB>(la, lb, a, s);
+    if (fb == 1 && fa == 0) return launch_layouts_tb<F8<1, 0>, TB>(la, lb, a, s);
+    if (fb == 0 && fa == 1) return launch_layouts_tb<F8<0, 1>, TB>(la, lb, a, s);
+    return launch_layouts_tb<F8<1, 1>, TB>(la, lb, a, s);
+  }
+  if (fa == 0 && fb == 0) return launch_layouts_tb<F8W<0, 0>, TB>(la, lb, a, s);
+  if (fa == 0 && fb == 1) return launch_layouts_tb<F8W<0, 1>, TB>(la, lb, a, s);
+  if (fa == 1 && fb == 0) return launch_layouts_tb<F8W<1, 0>, TB>(la, lb, a, s);
+  return launch_layouts_tb<F8W<1, 1>, TB>(la, lb, a, s);
+}
+
+}  // namespace fast
+}  // namespace mcg

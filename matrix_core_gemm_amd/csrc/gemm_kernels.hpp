@@ -124,6 +124,7 @@ hipError_t launch_stream(int dtA, int dtB, int layoutA, int layoutB, const Dense
 // tile: 256 (KERNEL_FAST) or 128 (KERNEL_MID)
 bool fast_path_ok(int dtA, int layoutA, int layoutB, const DenseArgs& a, bool aligned, int tile = 256);
 hipError_t launch_fast(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s, int tile = 256);
+hipError_t launch_fast_mid(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
 hipError_t launch_sparse(int dtA, int dtB, int layoutB, bool aligned, const SparseArgs& a, hipStream_t s);
 bool sparse_fast_ok(int dtA, int layoutB, const SparseArgs& a);
 hipError_t launch_sparse_fast(int dtA, int dtB, int layoutB, const SparseArgs& a, hipStream_t s);
