@@ -372,6 +372,12 @@ void gemm_fast_kernel(DenseArgs p) {
     for (int i = 0; i < WTM; ++i) {
       __builtin_amdgcn_sched_barrier(0);
       lds_char* buf = wbuf + (i & 1) * 8192;
+      const int64_t rbase = (m0 + rbA + 32 * i + rr) * p.ldc + col;  // row 4t further: + 4t ldc
+      v4 cv[8];
+      if (out == OUT_32 && p.use_c) {  // C loads first: their latency overlaps the staging
+#pragma unroll
+        for (int t = 0; t < 8; ++t) cv[t] = *(const v4*)(C + rbase + 4 * t * p.ldc);
+      }
 #pragma unroll
       for (int j = 0; j < WTN; ++j)
 #pragma unroll
@@ -390,7 +396,6 @@ void gemm_fast_kernel(DenseArgs p) {
         const int row = 4 * t + rr;
         a[t] = *(const lds_v4*)(buf + row * 256 + ((cc ^ (row & 15)) << 4));
       }
-      const int64_t rbase = (m0 + rbA + 32 * i + rr) * p.ldc + col;  // row 4t further: + 4t ldc
       if constexpr (!Op::INT_ACC) {
         if (out != OUT_32) {
           const uint16_t* C16 = (const uint16_t*)p.C;
@@ -413,11 +418,6 @@ void gemm_fast_kernel(DenseArgs p) {
           }
           continue;
         }
-      }
-      v4 cv[8];
-      if (p.use_c) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) cv[t] = *(const v4*)(C + rbase + 4 * t * p.ldc);
       }
 #pragma unroll
       for (int t = 0; t < 8; ++t) *(v4*)(D + rbase + 4 * t * p.ldc) = combine4(a[t], p.use_c ? cv[t] : v4{});
