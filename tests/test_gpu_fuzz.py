@@ -1,0 +1,39 @@
+"""Seeded random dense problems through gemm_dense, every output compared with the
+oracle: sizes from 1 to several tiles with ragged tails, all four layouts, every
+input pair, padded and unpadded leading dimensions, alpha and beta drawn from a
+small set (beta = 0 included).  Whatever kernel the library picks (general,
+skinny, streaming or pipelined) must meet the same bound; the case is printed
+before it runs."""
+import numpy as np
+import pytest
+
+from gpu_util import need_gpu
+from test_gpu_dense import LAYOUTS, PAIRS, check_case
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [1, 3, 16, 31, 33, 64, 100, 127, 128, 129, 200, 255, 256, 257, 300, 384]
+KS = [1, 2, 15, 16, 17, 64, 96, 130, 256, 300, 512, 700]
+
+
+def draw_case(seed):
+    """Case `seed`: a numpy generator seeded with it picks every parameter."""
+    r = np.random.default_rng(1000 + seed)
+    dtA, dtB = PAIRS[r.integers(len(PAIRS))]
+    layA, layB = LAYOUTS[r.integers(len(LAYOUTS))]
+    M, N = int(r.choice(SIZES)), int(r.choice(SIZES))
+    K = int(r.choice(KS))
+    pad = int(r.choice([0, 0, 1, 8, 16]))
+    ldc_pad = int(r.choice([0, 4]))
+    i8 = dtA == "i8"
+    alpha = float(r.choice([1, -3, 2] if i8 else [1.0, -0.75, 2.5]))
+    beta = float(r.choice([0, 1, -2] if i8 else [0.0, 1.0, 0.5]))
+    return dtA, dtB, layA, layB, M, N, K, pad, ldc_pad, alpha, beta
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_dense_problem(seed):
+    mcg = need_gpu()
+    dtA, dtB, layA, layB, M, N, K, pad, ldc_pad, alpha, beta = draw_case(seed)
+    check_case(mcg, dtA, dtB, layA, layB, M, N, K, pad=pad, beta=beta, alpha=alpha, ldc_pad=ldc_pad,
+               seed=50 + seed)
