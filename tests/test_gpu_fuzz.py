@@ -37,3 +37,29 @@ def test_random_dense_problem(seed):
     dtA, dtB, layA, layB, M, N, K, pad, ldc_pad, alpha, beta = draw_case(seed)
     check_case(mcg, dtA, dtB, layA, layB, M, N, K, pad=pad, beta=beta, alpha=alpha, ldc_pad=ldc_pad,
                seed=50 + seed)
+
+
+SPARSE_DTYPES = [("bf16", "bf16"), ("f16", "f16"), ("i8", "i8"), ("e4m3", "e4m3"), ("e4m3", "e5m2")]
+SPARSE_KS = [4, 8, 28, 32, 64, 100, 128, 260, 512, 1000]
+
+
+def draw_sparse_case(seed):
+    """2:4 case `seed`: sizes, B layout, paddings of the compressed buffers and of B,
+    beta, all drawn from a generator seeded with it (K a multiple of 4)."""
+    r = np.random.default_rng(5000 + seed)
+    dtA, dtB = SPARSE_DTYPES[r.integers(len(SPARSE_DTYPES))]
+    layB = ["k_contig", "mn_contig"][r.integers(2)]
+    M, N = int(r.choice(SIZES)), int(r.choice(SIZES))
+    K = int(r.choice(SPARSE_KS))
+    pads = (int(r.choice([0, 2, 8])), int(r.choice([0, 1, 3])), int(r.choice([0, 8, 16])))
+    beta = float(r.choice([0.0, 1.0] if dtA != "i8" else [0, 2]))
+    return dtA, dtB, layB, M, N, K, pads, beta
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_sparse_problem(seed):
+    """compress24 on the device, then gemm_sparse24 on whatever kernel it picks."""
+    from test_gpu_sparse import sparse8_case
+    mcg = need_gpu()
+    dtA, dtB, layB, M, N, K, pads, beta = draw_sparse_case(seed)
+    sparse8_case(mcg, dtA, dtB, layB, M, N, K, None, pads=pads, seed=90 + seed, beta=beta)

@@ -192,7 +192,8 @@ SP8 = [("i8", "i8"), ("e4m3", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e4m3"), ("e5m
 def sparse8_case(mcg, dtA, dtB, layB, M, N, K, path, pads=(0, 0, 0), seed=0, alpha=None, beta=1.0,
                  sample=None, A=None, B=None):
     """Compress A on the device into padded buffers, run gemm_sparse24, compare
-    with the oracle (int8 bit-exact, fp8 within the bound; fp8 scales in alpha)."""
+    with the oracle (int8 bit-exact, float inputs within the bound; fp8 scales in
+    alpha).  path: the kernel the call must take, or None for any."""
     i8 = dtA == "i8"
     pad_v, pad_i, pad_b = pads
     if A is None:
@@ -205,12 +206,15 @@ def sparse8_case(mcg, dtA, dtB, layB, M, N, K, path, pads=(0, 0, 0), seed=0, alp
     C = None if beta == 0 else W.c_matrix(M, N, "int20" if i8 else "normal", seed=72 + seed)
     nw = (K + 31) // 32
     lda_c, ld_idx = K // 2 + pad_v, nw + pad_i
-    vals = torch.full((M, lda_c), 0x5A, dtype=torch.uint8, device="cuda")
+    # M x lda_c kept values of the input's width
+    vals = torch.full((M, lda_c), 0x5A, dtype=torch.uint8 if W.ELEM_BYTES[dtA] == 1 else torch.int16,
+                      device="cuda")
     idx = torch.full((M, ld_idx), -1, dtype=torch.int32, device="cuda")
     viol = torch.zeros((1,), dtype=torch.int32, device="cuda")
     mcg.compress24(dtA, M, K, dev(A), K, vals, lda_c, idx, ld_idx, viol)
     dbb = dev(B.codes)
-    assert mcg.sparse24_path(dtA, layB, M, N, K, vals, lda_c, idx, ld_idx, dbb, B.ld) == path
+    if path is not None:
+        assert mcg.sparse24_path(dtA, layB, M, N, K, vals, lda_c, idx, ld_idx, dbb, B.ld) == path
     D = torch.full((M, N), -0x5A5A5A5A if i8 else float("nan"), dtype=torch.int32 if i8 else torch.float32,
                    device="cuda")
     mcg.gemm_sparse24(dtA, dtB, layB, M, N, K, vals, lda_c, idx, ld_idx, dbb, B.ld,
