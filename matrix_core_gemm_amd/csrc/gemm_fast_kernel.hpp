@@ -344,16 +344,19 @@ void gemm_fast_kernel(DenseArgs p) {
     }
     return o;
   };
-  if constexpr (TB == 256) if (vec_ok && m0 + BM <= p.M && n0 + BN <= p.N) {
+  if (vec_ok && m0 + BM <= p.M && n0 + BN <= p.N) {
     // Interior tile.  Each wavefront passes the 32 x 64 block of its row group i
-    // through LDS (8 KiB, two buffers), so that 16 lanes then read C and write D
+    // (KS: the one block it stores) through LDS (8 KiB; two buffers for the 256 x 256
+    // form, one for the 128 x 128 form), so that 16 lanes then read C and write D
     // along one row segment (256 bytes of binary32 / int32, 128 of 16-bit values):
     // whole lines per store instruction instead of 32 rows x 16 or 32 bytes.
     // Chunk ch (16 bytes) of staging row r sits at ch ^ (r & 15): the writes (32
     // rows at one chunk) and the reads (4 rows x 16 chunks) are free of bank conflicts.
-    barrier_lds();  // all LDS DMA has landed (vmcnt(0) above); no fragment reads remain
+    // all LDS DMA has landed (vmcnt(0) above) and no fragment reads remain; KS: the
+    // partner has read the block this wave handed it, in the same LDS
+    barrier_lds();
     typedef __attribute__((address_space(3))) v4 lds_v4;
-    lds_char* wbuf = smem + wave * 16384;
+    lds_char* wbuf = smem + wave * (KS ? 8192 : 16384);
     const int wr = lane & 31, rr = lane >> 4, cc = lane & 15;
     const int64_t col = n0 + rbB + 4 * cc;
     const int out = p.out;
@@ -371,7 +374,8 @@ void gemm_fast_kernel(DenseArgs p) {
 #pragma unroll
     for (int i = 0; i < WTM; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      lds_char* buf = wbuf + (i & 1) * 8192;
+      if (KS && i != grp) continue;  // the partner wave stores this row block
+      lds_char* buf = wbuf + (KS ? 0 : (i & 1) * 8192);
       const int64_t rbase = (m0 + rbA + 32 * i + rr) * p.ldc + col;  // row 4t further: + 4t ldc
       v4 cv[8];
       if (out == OUT_32 && p.use_c) {  // C loads first: their latency overlaps the staging
