@@ -63,7 +63,7 @@ constexpr double KT_US = 1.0, ROUND_US = 3.0, ATOMIC_US = 1.4e-5, SPLIT_US = 5.0
 // The 128 x 128 form of the fast kernel (KERNEL_MID, one workgroup per CU):
 // ceil(tiles / NUM_CU) * (MID_KT_US * nk + MID_ROUND_US), fitted over 100..256
 // tiles and K up to 8192; taken when it beats the best general plan by MID_MARGIN.
-constexpr double MID_KT_US = 0.5, MID_ROUND_US = 6.0, MID_MARGIN = 0.95;
+constexpr double MID_KT_US = 0.5, MID_ROUND_US = 3.0, MID_MARGIN = 0.95;
 // The streaming kernel is HBM-bound: split only when there are too few blocks
 // to spread over the CUs, keeping 16 K tiles or more per split.
 constexpr int64_t STREAM_MIN_BLOCKS = 64, STREAM_MIN_KT = 16;

@@ -210,8 +210,7 @@ def test_planner_kernel_by_shape(dt):
     assert plan(dt, 2048, 2048, 2048) == (6, 1)
     assert plan(dt, 1024, 2048, 8192) == (6, 1)
     assert plan(dt, 2560, 2560, 2560) == (6, 1)        # 400 tiles of 128 x 128: two rounds
-    if dt == "bf16":
-        assert plan(dt, 768, 768, 8192)[0] == 0        # 36 tiles, 128 K tiles: split K wins
+    assert plan(dt, 256, 256, 65536)[0] == 0           # 4 tiles, very long K: split K wins
     assert plan(dt, 2048, 2048, 2050, pad=2)[0] == 0   # K * elem_bytes not a multiple of 16
     assert plan(dt, 256, 200, 8192)[0] == 0            # 4 tiles: split K wins
     assert plan(dt, 256, 200, 8192)[1] > 1

@@ -188,8 +188,8 @@ def test_unaligned_skinny_takes_general_kernel():
 def test_general_split_k(dtA, dtB):
     """Few 128 x 128 tiles and a long K: K ranges on separate workgroups."""
     mcg = need_gpu()
-    run_case(mcg, dtA, dtB, "k_contig", "k_contig", 300, 264, 4160, GENERAL, True, ldc_pad=4, seed=13)
-    run_case(mcg, dtA, dtB, "mn_contig", "mn_contig", 264, 300, 4160, GENERAL, True, seed=14)
+    run_case(mcg, dtA, dtB, "k_contig", "k_contig", 300, 264, 8320, GENERAL, True, ldc_pad=4, seed=13)
+    run_case(mcg, dtA, dtB, "mn_contig", "mn_contig", 264, 300, 8320, GENERAL, True, seed=14)
 
 
 def test_general_split_k_native_fp8_and_alpha_beta():
@@ -204,7 +204,7 @@ def test_split_skipped_when_d_is_c():
     """D aliasing C with beta != 0 cannot be zeroed first: no split, same result."""
     mcg = need_gpu()
     for dt in ("bf16", "i8"):
-        M, N, K = 300, 264, 4160
+        M, N, K = 300, 264, 8320
         A, B = operands(dt, dt, "k_contig", "k_contig", M, N, K, seed=16)
         C = W.c_matrix(M, N, "int20" if dt == "i8" else "normal", seed=17)
         D = dev(C)
