@@ -90,3 +90,97 @@ def test_bound_scales_with_alpha_and_fp8_scales():
     u = 2.0 ** -24
     assert np.isclose(b1[0], 4 * u * 102 * 10 + u)
     assert np.isclose(b2[0], 4 * u * 102 * 10 * 4 + u)
+
+
+# ---------------------------------------------------------------------------
+# 16-bit outputs.  A bfloat16 / binary16 D is the kernel's binary32 result y
+# (|y - x| <= e, x the exact value, e the binary32 bound) rounded once more,
+# while the oracle's D_ref is x rounded once to the same format.  Both
+# roundings are at most half an ulp of the output format (u_out |.| in the
+# normal range, half the smallest subnormal below it), so a correct D lies
+# within e + u_out (2 |D_ref| + e) + 2 h of D_ref; with precision p (Table 1
+# of "Accurate Models of AMD Matrix Cores": 8 for bfloat16, 11 for binary16)
+# u_out = 2^-p.  At D_ref = 1 that is one ulp above 1 (2^(1-p)) plus e, so a
+# correct D is at most one ulp away there, and two ulps must fail.
+
+FMT = {"bf16": (8, -133), "f16": (11, -24)}  # precision, exponent of the smallest subnormal
+
+
+def _round16(x, out):
+    """Round binary64 values once to the 16-bit output format (nearest even),
+    through numpy / bit arithmetic that does not use the oracle."""
+    x = np.asarray(x, np.float64)
+    if out == "f16":
+        return x.astype(np.float16).astype(np.float64)
+    # bfloat16: round the binary32 image to nearest even on its top 16 bits;
+    # first round binary64 -> binary32 by truncation plus a sticky bit so the
+    # result is a single rounding of x (x is representable in 31 bits here)
+    f = x.astype(np.float32)
+    assert np.all(f.astype(np.float64) == x), "test values must be exact in binary32"
+    b = f.view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_bound_16bit_hand_value():
+    # D_ref = 1, S = 1, K = 2: e = 4u(K+2) S + u |D_ref| = 17 u (u = 2^-24)
+    u = 2.0 ** -24
+    e = 17 * u
+    for out, (p, emin) in FMT.items():
+        uo = 2.0 ** -p
+        h = 2.0 ** (emin - 1)
+        b = oracle.float_bound(np.array([1.0]), np.array([1.0]), 2, out=out)[0]
+        assert b == e + uo * (2.0 + e) + 2 * h, (out, b)
+        # one ulp above 1 plus e: the bound admits exactly one ulp of the format
+        assert 2.0 ** (1 - p) < b < 2.0 ** (1 - p) + 2.0 ** (-p)
+
+
+def test_bound_16bit_one_ulp_passes_two_ulps_fail():
+    for out, (p, _) in FMT.items():
+        ulp = 2.0 ** (1 - p)                   # ulp of [1, 2)
+        ref = np.array([1.0, 1.0, -1.0, 1.5])
+        S = np.array([1.0, 1.0, 1.0, 1.5])
+        # below 1 the format's ulp halves: 1 - ulp is two of its steps away but
+        # still one ulp of [1, 2) in distance, which is what the bound measures
+        one = np.array([1.0 + ulp, 1.0 - ulp, -1.0 - ulp, 1.5 + ulp])
+        two = np.array([1.0 + 2 * ulp, 1.0 - 1.5 * ulp, -1.0 - 2 * ulp, 1.5 + 2 * ulp])
+        assert oracle.check_float(one, ref, S, 2, out=out)["ok"], out
+        r = oracle.check_float(two, ref, S, 2, out=out)
+        assert r["violations"] == 4, (out, r)
+
+
+def test_bound_16bit_subnormal_range():
+    # D_ref = 0 with S = 0: the kernel's binary32 result is exact, and one
+    # smallest subnormal is the most two roundings can move it; two fail
+    for out, (p, emin) in FMT.items():
+        sub = 2.0 ** emin
+        zero = np.zeros(2)
+        assert oracle.check_float(np.array([sub, -sub]), zero, zero, 8, out=out)["ok"]
+        assert oracle.check_float(np.array([2 * sub, -2 * sub]), zero, zero, 8, out=out)["violations"] == 2
+
+
+def test_bound_16bit_admits_every_double_rounding():
+    # exact values x just below / above a midpoint of the 16-bit format; every
+    # binary32 result y within the binary32 bound e of x, rounded once more,
+    # must pass -- including the cases where y and x round to different
+    # neighbours (the double rounding the bound accounts for)
+    rng = np.random.default_rng(5)
+    for out, (p, _) in FMT.items():
+        ulp = 2.0 ** (1 - p)
+        n = 4000
+        base = 1.0 + rng.integers(0, 2 ** (p - 1), n) * ulp          # representable in [1, 2)
+        S = rng.uniform(0.5, 4.0, n)
+        K = 64
+        e = 4 * 2.0 ** -24 * (K + 2) * S + 2.0 ** -24 * 2.0
+        off = rng.uniform(-1, 1, n) * e
+        x = base + ulp / 2 + np.where(rng.integers(0, 2, n) == 1, 1, -1) * rng.uniform(0, 1, n) * e
+        x = x.astype(np.float32).astype(np.float64)                   # exact value, binary32-representable
+        y = (x + off).astype(np.float32).astype(np.float64)           # a kernel's binary32 result
+        y = np.clip(y, x - e, x + e)
+        y = np.where(np.abs(y - x) <= e, y, x)
+        d_gpu = _round16(y, out)
+        d_ref = _round16(x, out)
+        flips = int(np.sum(d_gpu != d_ref))
+        assert flips > n // 10, (out, flips)                          # the adversarial case occurs
+        r = oracle.check_float(d_gpu, d_ref, S, K, out=out)
+        assert r["ok"], (out, r)
