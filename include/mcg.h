@@ -74,7 +74,7 @@ typedef enum {
     MCG_ERR_UNSUPPORTED_DTYPE = 4, /* dtype/layout combination not provided          */
     MCG_ERR_MISALIGNED = 5,        /* pointer/ld alignment the entry point requires  */
     MCG_ERR_NOT_2_4_SPARSE = 6,    /* a group of four holds more than two non-zeros  */
-    MCG_ERR_INVALID_INDEX = 7,     /* reserved: malformed 2:4 index word             */
+    MCG_ERR_INVALID_INDEX = 7,     /* a 2:4 index code with p0 >= p1 (decompress24_host) */
     MCG_ERR_UNSUPPORTED_ARCH = 8,  /* current device is not gfx950                   */
     MCG_ERR_HIP = 9,               /* a HIP runtime call failed                      */
     MCG_ERR_INVALID_VALUE = 10     /* alpha/beta/scale not usable for this dtype     */
@@ -101,7 +101,9 @@ typedef enum {
  *                 wrapping mod 2^32).  F64: MCG_F64 (binary64 accumulation on
  *                 the FP64 matrix instructions, alpha and beta used as
  *                 binary64).
- * alpha, beta   : float paths use them as fp32.  The int8 path requires
+ * alpha, beta   : float paths use them as fp32: MCG_ERR_INVALID_VALUE when
+ *                 alpha*scaleA*scaleB or beta is not finite once rounded to
+ *                 fp32 (e.g. 1e39).  The int8 path requires
  *                 integral values in int32 range and computes
  *                 alpha*acc + beta*C in wrapping int32 arithmetic.
  * scaleA/scaleB : per-tensor dequantisation scales of fp8 operands (real
@@ -169,7 +171,11 @@ int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB,
  *                 p0 < p1) at bits 4*(g % 8) of word g/8; unused trailing
  *                 codes are zero.  This is the canonical layout produced by
  *                 compress24 / compress24_host; kernels re-pack it per lane.
- *                 Codes with p0 >= p1 give undefined results.
+ *                 The codes are not checked here (checking them would cost a
+ *                 pass over the index on every call): a code with p0 >= p1
+ *                 gives unspecified values in the outputs of its rows, but
+ *                 every memory access stays inside the arguments' extents.
+ *                 decompress24_host checks every code.
  * B, ldb, C, D, ldc, alpha, beta, stream: as for gemm_dense.
  */
 int gemm_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int64_t K,
@@ -206,6 +212,27 @@ int compress24(int dtype, int64_t M, int64_t K, const void* A, int64_t lda,
 int compress24_host(int dtype, int64_t M, int64_t K, const void* A, int64_t lda,
                     void* A_compressed, int64_t lda_c, uint32_t* A_index, int64_t ld_idx);
 
+/*
+ * decompress24_host -- the inverse of compress24_host ("RDNA4 sparse WMMA
+ * builtins", Structured sparsity (2:4 pattern): each group of four along K
+ * holds its two kept values at the two positions its index bits name, and
+ * zeros elsewhere; Common parameters, index: two bits per kept value).
+ *
+ * Pointers are HOST pointers; the call is synchronous and touches no device.
+ * dtype         : MCG_BF16, MCG_F16, MCG_I8, MCG_FP8_E4M3 or MCG_FP8_E5M2.
+ * A_compressed, lda_c, A_index, ld_idx: the compressed form described at
+ *                 gemm_sparse24 (M x K/2 values, M x ceil(K/32) index words).
+ * A, lda        : output, dense row-major M x K, lda >= K; for every group
+ *                 the four elements are written (the kept values at p0 and
+ *                 p1, zero bits at the other two positions).
+ * Errors        : MCG_ERR_INVALID_INDEX if any used group's code has
+ *                 p0 >= p1 (codes of groups past K/4 in a row's last word are
+ *                 ignored); all codes are checked first, so on this error
+ *                 nothing is written.  Argument errors as for compress24_host.
+ */
+int decompress24_host(int dtype, int64_t M, int64_t K, const void* A_compressed, int64_t lda_c,
+                      const uint32_t* A_index, int64_t ld_idx, void* A, int64_t lda);
+
 /* Host-only argument checks: the exact validation the entry points above run
  * before touching the device (same arguments, minus outputs' contents and the
  * stream).  They never call HIP and return an mcg_status. */
@@ -222,7 +249,8 @@ int mcg_validate_compress24(int dtype, int64_t M, int64_t K, const void* A, int6
                             int64_t ld_idx);
 
 /* Kernel selection, for callers that tune shapes and for tests.  Host-only,
-   no validation, no device access.
+   no validation, no device memory access; the cost model uses the current
+   device's compute-unit count (256, an MI355X's, when no device is visible).
    mcg_dense_path: the kernel gemm_dense runs for these operands with a
      binary32/int32 D that is not C: 0 general kernel, 128 x 128 tiles (any
      shape, alignment or leading dimension); 1 the 256 x 256 pipelined kernel;

@@ -29,7 +29,8 @@ STATUS = {0: "MCG_SUCCESS", 1: "MCG_ERR_NULL_POINTER", 2: "MCG_ERR_INVALID_SIZE"
           9: "MCG_ERR_HIP", 10: "MCG_ERR_INVALID_VALUE"}
 
 # Every symbol include/mcg.h declares.
-EXPORTS = ("gemm_dense", "gemm_sparse24", "compress24", "compress24_host", "mcg_status_string",
+EXPORTS = ("gemm_dense", "gemm_sparse24", "compress24", "compress24_host", "decompress24_host",
+           "mcg_status_string",
            "mcg_version", "mcg_validate_dense", "mcg_validate_sparse24", "mcg_validate_compress24",
            "mcg_dense_path", "mcg_dense_splits", "mcg_sparse24_path", "mcg_mfma_eval", "mcg_mfma_eval_k")
 
@@ -53,6 +54,7 @@ _lib.gemm_sparse24.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _v
                                _vp, _vp, _i64, _i32, _dbl, _dbl, _vp]
 _lib.compress24.argtypes = [_i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp]
 _lib.compress24_host.argtypes = [_i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
+_lib.decompress24_host.argtypes = [_i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
 _lib.mcg_status_string.argtypes = [_i32]
 _lib.mcg_status_string.restype = ctypes.c_char_p
 _lib.mcg_version.argtypes = []
@@ -137,6 +139,14 @@ def compress24_host(dtype, M, K, A, lda, A_compressed, lda_c, A_index, ld_idx) -
     if st not in (0, 6):
         raise MCGError("compress24_host", st)
     return st
+
+
+def decompress24_host(dtype, M, K, A_compressed, lda_c, A_index, ld_idx, A, lda) -> None:
+    """Host decompressor (inverse of compress24_host); raises MCGError, e.g.
+    MCG_ERR_INVALID_INDEX (7) for a code with p0 >= p1, in which case A is
+    left untouched."""
+    _check("decompress24_host", _lib.decompress24_host(_dt(dtype), M, K, _ptr(A_compressed), lda_c,
+                                                       _ptr(A_index), ld_idx, _ptr(A), lda))
 
 
 def validate_dense(dtypeA, dtypeB, layoutA, layoutB, M, N, K, A, lda, B, ldb, C, D, ldc, dtypeD,

@@ -39,22 +39,46 @@ bool int32_integral(double v) {
   return std::isfinite(v) && v == std::floor(v) && v >= -2147483648.0 && v <= 2147483647.0;
 }
 
-// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other;
+// and the device's compute-unit count (0 unknown).
 std::atomic<int> g_arch_state[64];
+std::atomic<int> g_num_cu[64];
+
+constexpr int kDefaultCUs = 256;  // an MI355X's compute units
+
+// Reads (once per device) the architecture name and compute-unit count.
+int probe_device(int dev) {
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MCG_ERR_HIP;
+  g_num_cu[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : kDefaultCUs,
+                      std::memory_order_relaxed);
+  g_arch_state[dev].store(std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2, std::memory_order_relaxed);
+  return MCG_SUCCESS;
+}
 
 int check_arch() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MCG_ERR_HIP;
   if (dev < 0 || dev >= 64) return MCG_ERR_UNSUPPORTED_ARCH;
-  int st = g_arch_state[dev].load(std::memory_order_relaxed);
-  if (st == 0) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MCG_ERR_HIP;
-    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-    g_arch_state[dev].store(st, std::memory_order_relaxed);
+  if (g_arch_state[dev].load(std::memory_order_relaxed) == 0) {
+    const int st = probe_device(dev);
+    if (st != MCG_SUCCESS) return st;
   }
-  return st == 1 ? MCG_SUCCESS : MCG_ERR_UNSUPPORTED_ARCH;
+  return g_arch_state[dev].load(std::memory_order_relaxed) == 1 ? MCG_SUCCESS : MCG_ERR_UNSUPPORTED_ARCH;
 }
+
+// Compute units of the current device, for the kernel planners; the MI355X
+// count when no device is visible (host-only planning queries).
+int current_num_cu() {
+  int ndev = 0, dev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return kDefaultCUs;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kDefaultCUs;
+  if (g_num_cu[dev].load(std::memory_order_relaxed) == 0 && probe_device(dev) != MCG_SUCCESS) return kDefaultCUs;
+  return g_num_cu[dev].load(std::memory_order_relaxed);
+}
+
+// A float alpha/beta the kernels receive as fp32 must stay finite there.
+bool finite_as_f32(double v) { return std::isfinite((float)v); }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MCG_SUCCESS : MCG_ERR_HIP; }
 
@@ -100,6 +124,9 @@ int mcg_validate_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t
   }
   if (!f8 && (scaleA != 1.0f || scaleB != 1.0f)) return MCG_ERR_INVALID_VALUE;
   if (f8 && (!std::isfinite(scaleA) || !std::isfinite(scaleB))) return MCG_ERR_INVALID_VALUE;
+  // the float epilogues take alpha*scaleA*scaleB and beta as fp32
+  if (!i8 && !f64 && (!finite_as_f32(alpha * (double)scaleA * (double)scaleB) || !finite_as_f32(beta)))
+    return MCG_ERR_INVALID_VALUE;
   return MCG_SUCCESS;
 }
 
@@ -144,7 +171,7 @@ int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int6
   if (st != MCG_SUCCESS) return st;
   if (dtypeA == MCG_F64) {
     const mcg::F64Args a = f64_args(M, N, K, A, lda, B, ldb, C, D, ldc, alpha, beta);
-    const mcg::F64Plan plan = mcg::plan_f64(a, !(a.use_c && C == D));
+    const mcg::F64Plan plan = mcg::plan_f64(a, !(a.use_c && C == D), current_num_cu());
     return hip_status(mcg::launch_f64(layoutA, layoutB, a, plan, (hipStream_t)stream));
   }
 
@@ -169,7 +196,8 @@ int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int6
   const int vb = 4 * elem_bytes(dtypeD);  // bytes of 4 consecutive C/D elements
   a.vec_cd = aligned_to(D, vb) && (!a.use_c || aligned_to(C, vb)) && ldc % 4 == 0;
   const bool aligned = dense_aligned(eb, K, A, lda, B, ldb);
-  const mcg::DensePlan plan = mcg::plan_dense(dtypeA, layoutA, layoutB, a, aligned, can_split_k(a, C, D));
+  const mcg::DensePlan plan =
+      mcg::plan_dense(dtypeA, layoutA, layoutB, a, aligned, can_split_k(a, C, D), current_num_cu());
   if (plan.kernel == mcg::KERNEL_FAST || plan.kernel == mcg::KERNEL_MID)
     return hip_status(mcg::launch_fast(dtypeA, dtypeB, layoutA, layoutB, a, (hipStream_t)stream,
                                        plan.kernel == mcg::KERNEL_MID ? 128 : 256));
@@ -202,8 +230,8 @@ int mcg_validate_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_
     return MCG_ERR_MISALIGNED;
   if (i8) {
     if (!int32_integral(alpha) || !int32_integral(beta)) return MCG_ERR_INVALID_VALUE;
-  } else if (!std::isfinite(alpha) || !std::isfinite(beta)) {
-    return MCG_ERR_INVALID_VALUE;
+  } else if (!finite_as_f32(alpha) || !finite_as_f32(beta)) {
+    return MCG_ERR_INVALID_VALUE;  // non-finite, or beyond fp32's range
   }
   return MCG_SUCCESS;
 }
@@ -323,6 +351,30 @@ int compress24_host(int dtype, int64_t M, int64_t K, const void* A, int64_t lda,
   return bad ? MCG_ERR_NOT_2_4_SPARSE : MCG_SUCCESS;
 }
 
+int decompress24_host(int dtype, int64_t M, int64_t K, const void* A_compressed, int64_t lda_c,
+                      const uint32_t* A_index, int64_t ld_idx, void* A, int64_t lda) {
+  int st = mcg_validate_compress24(dtype, M, K, A, lda, A_compressed, lda_c, A_index, ld_idx);
+  if (st != MCG_SUCCESS) return st;
+  const int eb = elem_bytes(dtype);
+  const int64_t ngroups = K / 4;
+  auto code = [&](int64_t i, int64_t g) { return (A_index[i * ld_idx + g / 8] >> (4 * (g % 8))) & 0xfu; };
+  // every used code must name two ascending positions; nothing is written otherwise
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t g = 0; g < ngroups; ++g)
+      if ((code(i, g) & 3u) >= (code(i, g) >> 2)) return MCG_ERR_INVALID_INDEX;
+  for (int64_t i = 0; i < M; ++i) {
+    const unsigned char* in = (const unsigned char*)A_compressed + i * lda_c * eb;
+    unsigned char* row = (unsigned char*)A + i * lda * eb;
+    for (int64_t g = 0; g < ngroups; ++g) {
+      const uint32_t c = code(i, g);
+      std::memset(row + 4 * g * eb, 0, 4 * eb);
+      std::memcpy(row + (4 * g + (c & 3u)) * eb, in + 2 * g * eb, eb);
+      std::memcpy(row + (4 * g + (c >> 2)) * eb, in + (2 * g + 1) * eb, eb);
+    }
+  }
+  return MCG_SUCCESS;
+}
+
 static mcg::DensePlan dense_plan(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
                                  const void* A, int64_t lda, const void* B, int64_t ldb, bool can_split) {
   const int eb = elem_bytes(dtypeA);
@@ -334,7 +386,8 @@ static mcg::DensePlan dense_plan(int dtypeA, int layoutA, int layoutB, int64_t M
   a.K = K;
   a.lda = lda;
   a.ldb = ldb;
-  return mcg::plan_dense(dtypeA, layoutA, layoutB, a, dense_aligned(eb, K, A, lda, B, ldb), can_split);
+  return mcg::plan_dense(dtypeA, layoutA, layoutB, a, dense_aligned(eb, K, A, lda, B, ldb), can_split,
+                         current_num_cu());
 }
 
 int mcg_dense_path(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A,
@@ -349,7 +402,7 @@ int mcg_dense_splits(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N,
                      double beta) {
   if (dtypeA == MCG_F64) {
     const mcg::F64Args a = f64_args(M, N, K, A, lda, B, ldb, C, (void*)D, N, 1.0, beta);
-    return mcg::plan_f64(a, dtypeD == MCG_F64 && !(beta != 0.0 && C == D)).splits;
+    return mcg::plan_f64(a, dtypeD == MCG_F64 && !(beta != 0.0 && C == D), current_num_cu()).splits;
   }
   if (dtypeA < MCG_BF16 || dtypeA > MCG_FP8_E5M2) return 1;
   const bool can_split = (dtypeD == MCG_F32 || dtypeD == MCG_I32) && !(beta != 0.0 && C == D);

@@ -51,17 +51,16 @@ static dim3 rows_grid(const DenseArgs& a) {
 // ------------------------------------------------------------------ plan
 
 namespace {
-constexpr int64_t NUM_CU = 256;           // gfx950 (MI355X) compute units
 constexpr int64_t FAST_MIN_TILES = 128;   // 256 x 256 tiles from which the fast kernel wins
 // Split-K cost model of the 4-wave general kernels (MI355X, measured with
 // bf16, fp8 and int8 over 256^2..2048^2 outputs and K up to 65536):
 //   time(s) ~ rounds * (KT_US * ceil(nk / s) + ROUND_US) + ATOMIC_US * s * M * N + SPLIT_US [s > 1]
-// with rounds = ceil(tiles * s / NUM_CU) workgroups per CU, KT_US per 128-byte
+// with rounds = ceil(tiles * s / num_cu) workgroups per CU, KT_US per 128-byte
 // K tile of a workgroup, ATOMIC_US per device-scope atomic add of D and
 // SPLIT_US for zeroing D and the extra launches.
 constexpr double KT_US = 1.0, ROUND_US = 3.0, ATOMIC_US = 1.4e-5, SPLIT_US = 5.0;
 // The 128 x 128 form of the fast kernel (KERNEL_MID, one workgroup per CU):
-// ceil(tiles / NUM_CU) * (MID_KT_US * nk + MID_ROUND_US), fitted over 100..256
+// ceil(tiles / num_cu) * (MID_KT_US * nk + MID_ROUND_US), fitted over 100..256
 // tiles and K up to 8192; taken when it beats the best general plan by MID_MARGIN.
 constexpr double MID_KT_US = 0.5, MID_ROUND_US = 3.0, MID_MARGIN = 0.95;
 // The streaming kernel is HBM-bound: split only when there are too few blocks
@@ -69,7 +68,8 @@ constexpr double MID_KT_US = 0.5, MID_ROUND_US = 3.0, MID_MARGIN = 0.95;
 constexpr int64_t STREAM_MIN_BLOCKS = 64, STREAM_MIN_KT = 16;
 }  // namespace
 
-DensePlan plan_dense(int dtA, int la, int lb, const DenseArgs& a, bool aligned, bool can_split) {
+DensePlan plan_dense(int dtA, int la, int lb, const DenseArgs& a, bool aligned, bool can_split, int num_cu) {
+  const int64_t NUM_CU = num_cu > 0 ? num_cu : 256;
   const int64_t eb = (dtA == DT_BF16 || dtA == DT_F16) ? 2 : 1;
   const int64_t KE = KT_BYTES / eb;
   const int64_t nk = (a.K + KE - 1) / KE;
@@ -144,6 +144,18 @@ hipError_t launch_dense(int dtA, int dtB, int la, int lb, bool aligned, const De
   a.stream_bw = plan.stream_bw;
   const bool split = a.splits > 1;
   const bool is_int = dtA == DT_I8;
+  // the launch limits of the kernel that follows are checked before D is
+  // zeroed, so a rejected plan writes nothing
+  if (a.splits < 1 || a.splits > 65535) return hipErrorInvalidValue;
+  {
+    const int64_t bm = plan.kernel == KERNEL_SKINNY_M ? 32 : 128, bn = plan.kernel == KERNEL_SKINNY_N ? 32 : 128;
+    int64_t blocks = ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+    if (plan.kernel == KERNEL_STREAM) {
+      const int64_t wide = a.N <= 32 && a.N <= a.M ? a.M : a.N;
+      blocks = (wide + a.stream_bw - 1) / (a.stream_bw > 0 ? a.stream_bw : 1);
+    }
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  }
   if (split) {
     if (a.out != OUT_32) return hipErrorInvalidValue;
     hipLaunchKernelGGL(splitk_zero_kernel, rows_grid(a), dim3(256), 0, s, a);

@@ -468,12 +468,12 @@ static bool f64_rows16(const double* X, int64_t ld) { return ((uintptr_t)X % 16)
 
 }  // namespace f64
 
-F64Plan plan_f64(const F64Args& a, bool can_split) {
+F64Plan plan_f64(const F64Args& a, bool can_split, int num_cu) {
   using namespace f64;
   F64Plan plan{1, (int)((a.K + BK - 1) / BK)};
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const int64_t nk = (a.K + BK - 1) / BK;
-  const int64_t slots = 2 * F64_NUM_CU;
+  const int64_t slots = 2 * (int64_t)num_cu;
   if (!can_split || nk < 2 * F64_SPLIT_MIN_KT || tiles >= 4 * slots) return plan;
   // Estimated time of S ranges: full waves of resident workgroups (two per CU), then the
   // last wave, whose workgroups run alone on their CUs when there are at most 256 of
@@ -484,7 +484,7 @@ F64Plan plan_f64(const F64Args& a, bool can_split) {
     const int64_t rounds = (wgs + slots - 1) / slots;
     const int64_t last = wgs - (rounds - 1) * slots;
     double t = (double)(rounds - 1) * (double)per * F64_KT_SHARED_US +
-               (double)per * (last <= F64_NUM_CU ? F64_KT_ALONE_US : F64_KT_SHARED_US);
+               (double)per * (last <= (int64_t)num_cu ? F64_KT_ALONE_US : F64_KT_SHARED_US);
     if (S > 1) t += F64_ATOMIC_US * (double)S * (double)a.M * (double)a.N + F64_SPLIT_US;
     return t;
   };

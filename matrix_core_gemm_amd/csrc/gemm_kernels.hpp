@@ -79,18 +79,17 @@ struct F64Plan {
   int kt_per_split;  // K tiles of 16 per range
 };
 
-// Split-K cost model of the binary64 kernel (microseconds; gfx950, 256 CUs, up to two
-// resident 128 x 128 workgroups each; fitted to forced-split timings from 1024^3 to
+// Split-K cost model of the binary64 kernel (microseconds; gfx950, up to two resident
+// 128 x 128 workgroups per CU; fitted on 256 CUs to forced-split timings from 1024^3 to
 // 256 x 256 x 65536).
-constexpr int64_t F64_NUM_CU = 256;
 constexpr int64_t F64_SPLIT_MIN_KT = 16;  // at least 256 K values per range
 constexpr double F64_KT_ALONE_US = 2.05;  // one K tile (16) of a workgroup alone on its CU
 constexpr double F64_KT_SHARED_US = 3.4;  // the same with two workgroups sharing the CU
 constexpr double F64_ATOMIC_US = 7e-6;    // per atomic add of a partial sum (overlaps compute)
 constexpr double F64_SPLIT_US = 5.0;      // zeroing D and the extra launch
 
-// can_split: D is not C with beta != 0.
-F64Plan plan_f64(const F64Args& a, bool can_split);
+// can_split: D is not C with beta != 0; num_cu: the device's compute units.
+F64Plan plan_f64(const F64Args& a, bool can_split, int num_cu);
 hipError_t launch_f64(int layoutA, int layoutB, const F64Args& a, const F64Plan& plan, hipStream_t s);
 
 struct CompressArgs {
@@ -110,8 +109,10 @@ struct CompressArgs {
 constexpr int64_t FP8_NATIVE_MIN_K = 6144;
 
 // Kernel and K split for a dense problem.  can_split: D is binary32/int32 and
-// is not C (split K zeroes D first and adds the partial sums into it).
-DensePlan plan_dense(int dtA, int layoutA, int layoutB, const DenseArgs& a, bool aligned, bool can_split);
+// is not C (split K zeroes D first and adds the partial sums into it);
+// num_cu: the device's compute units.
+DensePlan plan_dense(int dtA, int layoutA, int layoutB, const DenseArgs& a, bool aligned, bool can_split,
+                     int num_cu);
 
 // Enqueue the kernels; arguments were validated by the caller.
 hipError_t launch_dense(int dtA, int dtB, int layoutA, int layoutB, bool aligned, const DenseArgs& a,

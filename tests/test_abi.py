@@ -25,7 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for fn in ("gemm_dense", "gemm_sparse24", "compress24", "compress24_host", "mcg_status_string"):
+    for fn in ("gemm_dense", "gemm_sparse24", "compress24", "compress24_host", "decompress24_host",
+               "mcg_status_string"):
         assert fn in names
     assert set(names) == set(m.EXPORTS)
 
@@ -86,6 +87,12 @@ def dense_args(**kw):
     ({"dtypeA": "i8", "dtypeB": "i8", "dtypeD": "i32", "alpha": 1.5}, 10),
     ({"dtypeA": "i8", "dtypeB": "i8", "dtypeD": "i32", "beta": 2.0 ** 31, "C": FAKE}, 10),
     ({"alpha": float("nan")}, 10),
+    ({"alpha": 1e39}, 10),                           # finite in binary64, infinite as fp32
+    ({"beta": -1e39, "C": FAKE}, 10),
+    ({"alpha": 3e38}, 0),                            # still finite as fp32
+    ({"dtypeA": "e4m3", "dtypeB": "e4m3", "alpha": 1e30, "scaleA": 1e10}, 10),   # alpha*scaleA*scaleB overflows
+    ({"dtypeA": "e4m3", "dtypeB": "e4m3", "alpha": 1e30, "scaleA": 1e-10}, 0),
+    ({"dtypeA": "f64", "dtypeB": "f64", "dtypeD": "f64", "alpha": 1e39}, 0),   # binary64 keeps its range
     ({"dtypeD": "bf16"}, 0),                         # 16-bit outputs for float inputs
     ({"dtypeD": "f16", "beta": 1.0, "C": FAKE}, 0),
     ({"dtypeA": "e4m3", "dtypeB": "e5m2", "dtypeD": "bf16"}, 0),
@@ -145,6 +152,8 @@ def test_entry_points_reject_before_touching_the_device():
     ({"dtypeD": "bf16"}, 0),
     ({"dtypeD": "f16", "D": FAKE + 2}, 0),
     ({"dtypeD": "f16", "D": FAKE + 1}, 5),
+    ({"alpha": 1e39}, 10),
+    ({"beta": 1e39, "C": FAKE}, 10),
 ])
 def test_sparse_validation(kw, status):
     a = dict(dtypeA="bf16", dtypeB="bf16", layoutB="k_contig", M=64, N=96, K=64, A_compressed=FAKE,
@@ -215,3 +224,79 @@ def test_planner_kernel_by_shape(dt):
     assert plan(dt, 256, 200, 8192)[0] == 0            # 4 tiles: split K wins
     assert plan(dt, 256, 200, 8192)[1] > 1
     assert plan(dt, 4096, 16, 4096)[0] == 4
+
+
+# ---------------------------------------------------------------- decompress24_host
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "i8", "e4m3", "e5m2"])
+@pytest.mark.parametrize("shape", [(1, 4), (7, 36), (33, 200), (16, 256)])
+def test_decompress24_host_matches_oracle_and_round_trips(dt, shape):
+    M, K = shape
+    A = W.sparse24_dense(dt, M, K, dist="int8" if dt == "i8" else "normal")
+    ov, oi, viol = oracle.compress24(dt, A)
+    assert viol == 0
+    out = np.full((M, K + 3), 0x55, W.CODE_NP[dt])           # padded ld; padding must survive
+    m.decompress24_host(dt, M, K, ov, K // 2, oi, oi.shape[1], out, K + 3)
+    assert np.array_equal(out[:, :K], oracle.decompress24(dt, ov, oi, K))
+    assert np.array_equal(out[:, :K], A)                      # decompress(compress(A)) == A
+    assert np.all(out[:, K:] == 0x55)
+    # compress(decompress(v, i)) == (v, i) for canonical metadata
+    vals = np.zeros((M, K // 2), W.CODE_NP[dt])
+    idx = np.zeros((M, (K + 31) // 32), np.uint32)
+    assert m.compress24_host(dt, M, K, np.ascontiguousarray(out[:, :K]), K, vals, K // 2, idx, idx.shape[1]) == 0
+    assert np.array_equal(vals, ov) and np.array_equal(idx, oi)
+
+
+def test_decompress24_host_every_code():
+    # one row of 16 groups, one per 4-bit code: the six ascending pairs expand
+    # to their positions; any code with p0 >= p1 is MCG_ERR_INVALID_INDEX
+    good = [p0 | (p1 << 2) for p0 in range(4) for p1 in range(4) if p0 < p1]
+    assert sorted(good) == [4, 8, 9, 12, 13, 14]
+    vals = np.arange(1, 3, dtype=np.int8)
+    for code in range(16):
+        idx = np.array([[code]], np.uint32)
+        out = np.full((1, 4), 99, np.int8)
+        if code in good:
+            m.decompress24_host("i8", 1, 4, vals.reshape(1, 2), 2, idx, 1, out, 4)
+            expect = np.zeros(4, np.int8)
+            expect[code & 3], expect[code >> 2] = 1, 2
+            assert np.array_equal(out[0], expect), code
+        else:
+            with pytest.raises(m.MCGError) as e:
+                m.decompress24_host("i8", 1, 4, vals.reshape(1, 2), 2, idx, 1, out, 4)
+            assert e.value.status == 7
+            assert np.all(out == 99), "nothing is written on an invalid code"
+
+
+def test_decompress24_host_invalid_code_anywhere_writes_nothing():
+    M, K = 5, 72                                             # 18 groups: the last word holds 2 used codes
+    A = W.sparse24_dense("bf16", M, K)
+    ov, oi, _ = oracle.compress24("bf16", A)
+    bad = oi.copy()
+    bad[4, 2] = (bad[4, 2] & ~np.uint32(0xF0)) | np.uint32(0x50)   # group 17 of row 4: code 5 (1, 1)
+    out = np.zeros((M, K), np.uint16)
+    with pytest.raises(m.MCGError) as e:
+        m.decompress24_host("bf16", M, K, ov, K // 2, bad, bad.shape[1], out, K)
+    assert e.value.status == 7 and not out.any()
+    with pytest.raises(ValueError):
+        oracle.decompress24("bf16", ov, bad, K)               # the oracle rejects it too
+    # codes past K / 4 in the last word are ignored
+    pad = oi.copy()
+    pad[:, 2] |= np.uint32(0x55550000)
+    m.decompress24_host("bf16", M, K, ov, K // 2, pad, pad.shape[1], out, K)
+    assert np.array_equal(out, A)
+
+
+def test_decompress24_host_argument_errors():
+    v = np.zeros((4, 8), np.uint16)
+    i = np.zeros((4, 1), np.uint32)
+    a = np.zeros((4, 16), np.uint16)
+    for args, status in [(("bf16", 4, 18, v, 8, i, 1, a, 16), 2),      # K % 4 != 0
+                         (("bf16", 4, 16, v, 7, i, 1, a, 16), 3),
+                         (("bf16", 4, 16, v, 8, i, 1, a, 15), 3),
+                         (("f32", 4, 16, v, 8, i, 1, a, 16), 4),
+                         (("bf16", 4, 16, None, 8, i, 1, a, 16), 1)]:
+        with pytest.raises(m.MCGError) as e:
+            m.decompress24_host(*args)
+        assert e.value.status == status, args
+    m.decompress24_host("bf16", 0, 16, None, 8, None, 1, None, 16)   # empty: no-op
