@@ -137,6 +137,16 @@ def test_256_tile_path_ragged(dtA, dtB, layA, layB, shape):
     check_case_sampled(mcg, dtA, dtB, layA, layB, M, N, K, pad=pad, ldc_pad=4, seed=3, expect_path=1)
 
 
+@pytest.mark.parametrize("dtA,dtB", PAIRS)
+def test_256_tile_path_every_output(dtA, dtB):
+    """One ragged shape of the 256 x 256 kernel per input pair (the layout pair
+    rotates over the input pairs), compared with the oracle on every output."""
+    mcg = need_gpu()
+    layA, layB = LAYOUTS[PAIRS.index((dtA, dtB)) % len(LAYOUTS)]
+    M, N, K, pad = FAST_SHAPES[0]
+    check_case(mcg, dtA, dtB, layA, layB, M, N, K, pad=pad, ldc_pad=4, seed=31, expect_path=1)
+
+
 # Shapes taken by the 128 x 128 form of the same kernel (too few 256 x 256 tiles to
 # fill the chip, K long enough for it to beat the general kernel): ragged M and N
 # tiles, K ending inside a stage, padded leading dimensions.
@@ -343,11 +353,18 @@ FULL = [w for w in W.standard_workloads() if not w.sparse and w.M > 256]
 @pytest.mark.parametrize("wl", FULL, ids=[w.name.split(",")[0] for w in FULL])
 def test_full_size_configurations(wl):
     mcg = need_gpu()
-    d1 = sampled_check(mcg, wl)
+    d = sampled_check(mcg, wl)
     if wl.dtA == "i8":
-        # run-to-run determinism of the exact path over the whole output
-        d2 = sampled_check(mcg, wl)
-        assert np.array_equal(d1, d2)
+        # the exact path: every output equal to the oracle's
+        M, N, K = wl.M, wl.N, wl.K
+        A = W.operand("A", wl.dtA, M, K, wl.dist, wl.layA)
+        B = W.operand("B", wl.dtB, K, N, wl.dist, wl.layB)
+        C = W.c_matrix(M, N, wl.c_dist) if wl.c_dist else None
+        ref = oracle.gemm_i8(wl.layA, wl.layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, N,
+                             int(wl.alpha), int(wl.beta))
+        r = oracle.check_exact(d, ref)
+        assert r["ok"], f"{wl.name}: {r}"
+        say(f"  every one of {r['n']} outputs bit-exact")
 
 
 # ------------------------------------------------ fp8 accumulation-precision cases

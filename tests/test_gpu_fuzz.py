@@ -39,6 +39,45 @@ def test_random_dense_problem(seed):
                seed=50 + seed)
 
 
+def draw_large_case(seed):
+    """Large case `seed`: even seeds draw M, N above 2816 (at least 144 output
+    tiles of 256 x 256: the 256 x 256 kernel), odd seeds M, N in [1024, 2048]
+    with a long K (the kernel's 128 x 128 form); K and the leading-dimension
+    paddings are whole 16-byte chunks for every element width, as both forms
+    require."""
+    r = np.random.default_rng(3000 + seed)
+    dtA, dtB = PAIRS[r.integers(len(PAIRS))]
+    layA, layB = LAYOUTS[r.integers(len(LAYOUTS))]
+    if seed % 2 == 0:
+        M, N = int(r.integers(2833, 3329)), int(r.integers(2833, 3329))
+        K = 16 * int(r.integers(1, 25))
+        path = 1
+    else:
+        M, N = int(r.integers(1040, 2049)), int(r.integers(1040, 2049))
+        K = 16 * int(r.integers(140, 170))
+        path = 6
+    # an MN-contiguous operand's leading dimension is M or N plus the padding:
+    # that side is a whole number of 16-byte chunks (still ragged against the tiles)
+    M = M - M % 16 if layA == "mn_contig" else M
+    N = N - N % 16 if layB == "mn_contig" else N
+    pad = int(r.choice([0, 16, 32]))
+    ldc_pad = int(r.choice([0, 4]))
+    i8 = dtA == "i8"
+    alpha = float(r.choice([1, -3, 2] if i8 else [1.0, -0.75, 2.5]))
+    beta = float(r.choice([0, 1, -2] if i8 else [0.0, 1.0, 0.5]))
+    return dtA, dtB, layA, layB, M, N, K, pad, ldc_pad, alpha, beta, path
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_large_dense_problem(seed):
+    """Every output of a seeded random problem on the pipelined kernel's two tile
+    forms (the path is asserted)."""
+    mcg = need_gpu()
+    dtA, dtB, layA, layB, M, N, K, pad, ldc_pad, alpha, beta, path = draw_large_case(seed)
+    check_case(mcg, dtA, dtB, layA, layB, M, N, K, pad=pad, beta=beta, alpha=alpha, ldc_pad=ldc_pad,
+               seed=70 + seed, expect_path=path)
+
+
 SPARSE_DTYPES = [("bf16", "bf16"), ("f16", "f16"), ("i8", "i8"), ("e4m3", "e4m3"), ("e4m3", "e5m2")]
 SPARSE_KS = [4, 8, 28, 32, 64, 100, 128, 260, 512, 1000]
 
