@@ -1,30 +1,36 @@
 """Benchmark of the matrix-core GEMM hot path on one MI355X.
 
 One timed step is one pass over every entry point of the hot path on its
-full-size synthetic workload (8192^3 for every GEMM):
-  gemm_dense  bf16 x bf16 -> f32   (A row-major, B column-major, C ~ N(0,1), alpha = beta = 1)
-  gemm_dense  f16  x f16  -> f32   (same recipe)
-  gemm_dense  i8   x i8   -> i32   (C uniform int in [-2^20, 2^20], alpha = beta = 1)
-  gemm_dense  e4m3 x e4m3 -> f32   (per-tensor scales, C = 0)
-  gemm_dense  e4m3 x e5m2 -> f32   (per-tensor scales, C = 0)
+synthetic workload:
+  gemm_dense  bf16 x bf16 -> f32, 8192^3, all four A/B storage orders
+              (C ~ N(0,1), alpha = beta = 1); the A row-major / B column-major
+              pair is the headline `value`
+  gemm_dense  f16  x f16  -> f32, 8192^3, all four storage orders (same recipe)
+  gemm_dense  bf16 x bf16 -> f32, 256^3, uniform[-1, 1], beta = 0 (launch-bound:
+              one event pair brackets a batch of back-to-back launches)
+  gemm_dense  i8   x i8   -> i32, 4096^3 and 8192^3 (C uniform int in
+              [-2^20, 2^20], alpha = beta = 1)
+  gemm_dense  e4m3 x e4m3 and e4m3 x e5m2 -> f32, 8192^3 (per-tensor scales, C = 0)
   compress24  bf16 8192 x 8192     (2:4 compressor)
-  gemm_sparse24 bf16 (2:4 A) x bf16 -> f32
-  gemm_dense  bf16 x bf16 -> bf16  (C and D in bfloat16, alpha = beta = 1)
-  gemm_dense  skinny bf16 32768 x 16 x 8192 and 16 x 32768 x 8192 (C absent): HBM-bound
-  gemm_sparse24 int8 (2:4 A) x int8 -> i32 and e4m3 (2:4 A) x e4m3 -> f32 (C absent)
-  gemm_dense  f64  x f64  -> f64   (binary64, A row-major, B column-major, C ~ N(0,1), alpha = beta = 1)
-Each call is bracketed by HIP events on the stream it is launched on, so every
-kernel's average duration is measured live.  `value` is the dense bf16 8192^3
-rate (TFLOP/s); the per-dtype rates the metric asks for are in `per_dtype`.
+  gemm_sparse24 bf16 / int8 / e4m3 (2:4 A), 8192^3, C absent
+  gemm_dense  bf16 x bf16 -> bf16, 8192^3 (C and D in bfloat16)
+  gemm_dense  skinny bf16 32768 x 16 x 8192 and 16 x 32768 x 8192 (HBM-bound)
+  gemm_dense  f64  x f64  -> f64, 8192^3 (binary64, C ~ N(0,1))
+Each call (or batch) is bracketed by HIP events recorded on the stream it is
+launched on, so every kernel's average duration is measured live.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+After the timed steps every entry runs once more and sampled outputs (whole
+rows and random elements) are compared with the CPU oracle, the same
+acceptance test as the parity tests; the oracle is also timed per workload on
+the host cores (the CPU baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only a,b]
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
-import platform
 import sys
 import time
 
@@ -32,9 +38,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "TFLOP/s (TOPS int8) at 8192³ per dtype + % of MI355X MFMA peak"
-# MI355X published dense peaks (TFLOP/s or TOPS) and HBM bandwidth (GB/s)
+# MI355X published dense peaks (TFLOP/s or TOPS) and HBM bandwidth (GB/s); the
+# 2:4 sparse instructions run at twice the dense rate of their input type
 PEAK = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "i8": 5000.0, "f64": 78.6}
+SPARSE_PEAK = {"bf16": 5000.0, "i8": 10000.0, "fp8": 10000.0}
 HBM_PEAK_GBS = 8000.0
+SMALL_BATCH = 50  # launches of the 256^3 workload per event pair
 
 # HBM bytes per launch of the dense bf16 8192^3 kernel, from two rocprofv3 --pmc
 # passes (FETCH_SIZE x 2.000, WRITE_SIZE x 1.000; the factors make a plain 1 GiB
@@ -46,6 +55,9 @@ TRAFFIC_MEASURED = {
     "sources_sha256": "1890032682344e3f9d2e464b54dc92cbbe82a1053e3b3e73c6cde3f500027891",
     "read_bytes": 1810 * 2**20, "write_bytes": 256 * 2**20,
 }
+
+LAYOUT_NAMES = {("k_contig", "k_contig"): "Arow_Bcol", ("k_contig", "mn_contig"): "Arow_Brow",
+                ("mn_contig", "k_contig"): "Acol_Bcol", ("mn_contig", "mn_contig"): "Acol_Brow"}
 
 
 def kernel_sources_hash():
@@ -72,14 +84,40 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def host_cpu():
+    """CPU model name and socket count from /proc/cpuinfo."""
+    model, sockets = "unknown", set()
+    try:
+        for line in open("/proc/cpuinfo"):
+            k, _, v = line.partition(":")
+            k, v = k.strip(), v.strip()
+            if k == "model name" and model == "unknown":
+                model = v
+            elif k == "physical id":
+                sockets.add(v)
+    except OSError:
+        pass
+    return model, max(1, len(sockets))
+
+
+class Entry:
+    """One hot-path call: its arguments on the device and on the host (for the
+    oracle), and how its rate is reported."""
+
+    def __init__(self, name, kind, **kw):
+        self.name, self.kind = name, kind
+        self.__dict__.update(kw)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--size", type=int, default=8192)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-parity", action="store_true", help="skip the sampled oracle comparison")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle time for the headline workload's CPU baseline (others: a fifth)")
     ap.add_argument("--only", default="", help="comma list of entries to run (profiling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -95,184 +133,324 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    n = args.size
-    M = N = K = n
+    n = 8192
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    only = set(args.only.split(",")) if args.only else None
+    want = lambda x: only is None or x in only
 
     t0 = time.time()
-    log(f"generating inputs (n = {n}) ...")
-    ops = {}
+    log("generating inputs ...")
+    E = {}
+    C_h = W.c_matrix(n, n, "normal")
+    C = dev(C_h)
+    D = torch.empty((n, n), dtype=torch.float32, device="cuda")
+    Di = torch.empty((n, n), dtype=torch.int32, device="cuda")
+
+    # dense bf16 / f16, 8192^3, the four storage orders.  The same N(0,1) buffers
+    # serve every order (M = N = K): read column-major they are another N(0,1)
+    # matrix of the same shape.
     for dt in ("bf16", "f16"):
-        A = W.operand("A", dt, M, K, "normal", "k_contig")
-        B = W.operand("B", dt, K, N, "normal", "k_contig")
-        ops[dt] = (dev(A.codes), A.ld, dev(B.codes), B.ld, 1.0, 1.0)
-        if dt == "bf16":
-            host_bf16 = (A, B)
-    C = dev(W.c_matrix(M, N, "normal"))
-    Ci = dev(W.c_matrix(M, N, "int20"))
-    A = W.operand("A", "i8", M, K, "int8", "k_contig")
-    B = W.operand("B", "i8", K, N, "int8", "k_contig")
-    ops["i8"] = (dev(A.codes), A.ld, dev(B.codes), B.ld, 1.0, 1.0)
-    A8 = W.operand("A", "e4m3", M, K, "normal", "k_contig", fp8_scaled=True)
-    B8 = W.operand("B", "e4m3", K, N, "normal", "k_contig", fp8_scaled=True)
-    B85 = W.operand("B", "e5m2", K, N, "normal", "k_contig", fp8_scaled=True)
+        A = W.operand("A", dt, n, n, "normal", "k_contig")
+        B = W.operand("B", dt, n, n, "normal", "k_contig")
+        dA, dB = dev(A.codes), dev(B.codes)
+        for lay, tag in LAYOUT_NAMES.items():
+            name = dt if tag == "Arow_Bcol" else f"{dt}_{tag}"
+            if want(name) or name == "bf16":
+                E[name] = Entry(name, "dense", dtA=dt, dtB=dt, layA=lay[0], layB=lay[1], M=n, N=n, K=n,
+                                A=dA, B=dB, hA=A.codes, hB=B.codes, lda=n, ldb=n, C=C, hC=C_h, D=D,
+                                out="f32", alpha=1.0, beta=1.0, sA=1.0, sB=1.0, peak=PEAK[dt], unit="TFLOP/s")
+    # bf16 256^3 (launch-bound)
+    As = W.operand("A", "bf16", 256, 256, "uniform", "k_contig")
+    Bs_ = W.operand("B", "bf16", 256, 256, "uniform", "k_contig")
+    Dsm = torch.empty((256, 256), dtype=torch.float32, device="cuda")
+    E["bf16_256"] = Entry("bf16_256", "dense", dtA="bf16", dtB="bf16", layA="k_contig", layB="k_contig",
+                          M=256, N=256, K=256, A=dev(As.codes), B=dev(Bs_.codes), hA=As.codes, hB=Bs_.codes,
+                          lda=256, ldb=256, C=None, hC=None, D=Dsm, out="f32", alpha=1.0, beta=0.0, sA=1.0,
+                          sB=1.0, peak=PEAK["bf16"], unit="TFLOP/s", batch=SMALL_BATCH)
+    # int8 4096^3 and 8192^3
+    for m_ in (4096, n):
+        A = W.operand("A", "i8", m_, m_, "int8", "k_contig")
+        B = W.operand("B", "i8", m_, m_, "int8", "k_contig")
+        Ch = W.c_matrix(m_, m_, "int20")
+        name = "i8" if m_ == n else f"i8_{m_}"
+        E[name] = Entry(name, "dense", dtA="i8", dtB="i8", layA="k_contig", layB="k_contig", M=m_, N=m_,
+                        K=m_, A=dev(A.codes), B=dev(B.codes), hA=A.codes, hB=B.codes, lda=m_, ldb=m_,
+                        C=dev(Ch), hC=Ch, D=Di if m_ == n else torch.empty((m_, m_), dtype=torch.int32,
+                                                                          device="cuda"),
+                        out="i32", alpha=1, beta=1, sA=1.0, sB=1.0, peak=PEAK["i8"], unit="TOPS")
+    # fp8 pairs
+    A8 = W.operand("A", "e4m3", n, n, "normal", "k_contig", fp8_scaled=True)
     dA8 = dev(A8.codes)
-    ops["e4m3xe4m3"] = (dA8, A8.ld, dev(B8.codes), B8.ld, A8.scale, B8.scale)
-    ops["e4m3xe5m2"] = (dA8, A8.ld, dev(B85.codes), B85.ld, A8.scale, B85.scale)
-    As = dev(W.sparse24_dense("bf16", M, K))
-    Bs = ops["bf16"][2]
-    vals = torch.empty((M, K // 2), dtype=torch.int16, device="cuda")
-    idx = torch.empty((M, (K + 31) // 32), dtype=torch.int32, device="cuda")
-    # 8-bit 2:4 operands, compressed on the device before timing
-    sp8 = {}
-    for dt, B_ in (("i8", ops["i8"][2]), ("e4m3", ops["e4m3xe4m3"][2])):
-        A_ = dev(W.sparse24_dense(dt, M, K, dist="int8" if dt == "i8" else "normal"))
-        v_ = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
-        i_ = torch.empty((M, (K + 31) // 32), dtype=torch.int32, device="cuda")
-        mcg.compress24(dt, M, K, A_, K, v_, K // 2, i_, i_.shape[1], None)
-        del A_
-        sp8[dt] = (v_, i_, B_)
-    D = torch.empty((M, N), dtype=torch.float32, device="cuda")
-    Di = torch.empty((M, N), dtype=torch.int32, device="cuda")
-    # bfloat16 C and D for the 16-bit output entry
+    for dtb in ("e4m3", "e5m2"):
+        B8 = W.operand("B", dtb, n, n, "normal", "k_contig", fp8_scaled=True)
+        name = f"e4m3x{dtb}"
+        E[name] = Entry(name, "dense", dtA="e4m3", dtB=dtb, layA="k_contig", layB="k_contig", M=n, N=n, K=n,
+                        A=dA8, B=dev(B8.codes), hA=A8.codes, hB=B8.codes, lda=n, ldb=n, C=None, hC=None, D=D,
+                        out="f32", alpha=1.0, beta=0.0, sA=A8.scale, sB=B8.scale, peak=PEAK["fp8"],
+                        unit="TFLOP/s")
+    # bf16 with bfloat16 C and D
     C16 = C.to(torch.bfloat16).view(torch.int16)
-    D16 = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    kw = {k: v for k, v in E["bf16"].__dict__.items() if k not in ("name", "kind")}
+    kw.update(C=C16, hC=C16.cpu().numpy().view(np.uint16), out="bf16",
+              D=torch.empty((n, n), dtype=torch.int16, device="cuda"))
+    E["bf16_out"] = Entry("bf16_out", "dense", **kw)
+    # 2:4 sparse: bf16 compressed on the device inside the step (compress24 is
+    # itself timed); 8-bit operands compressed once before timing
+    Ad_h = W.sparse24_dense("bf16", n, n)
+    Ad = dev(Ad_h)
+    vals = torch.empty((n, n // 2), dtype=torch.int16, device="cuda")
+    idx = torch.empty((n, n // 32), dtype=torch.int32, device="cuda")
+    E["compress24"] = Entry("compress24", "compress", dt="bf16", M=n, K=n, A=Ad, hA=Ad_h, vals=vals, idx=idx,
+                            nbytes=n * n * 2 + n * n // 2 * 2 + n * (n // 32) * 4)
+    E["sparse24"] = Entry("sparse24", "sparse", dtA="bf16", dtB="bf16", M=n, N=n, K=n, vals=vals, idx=idx,
+                          B=E["bf16"].B, hB=E["bf16"].hB, ldb=n, D=D, out="f32", alpha=1.0, beta=0.0,
+                          dense="bf16", peak=PEAK["bf16"], speak=SPARSE_PEAK["bf16"], unit="TFLOP/s")
+    for dt, dense in (("i8", "i8"), ("e4m3", "e4m3xe4m3")):
+        name = f"sparse24_{dt}"
+        if not want(name):
+            continue
+        A_ = dev(W.sparse24_dense(dt, n, n, dist="int8" if dt == "i8" else "normal"))
+        v_ = torch.empty((n, n // 2), dtype=torch.uint8, device="cuda")
+        i_ = torch.empty((n, n // 32), dtype=torch.int32, device="cuda")
+        mcg.compress24(dt, n, n, A_, n, v_, n // 2, i_, n // 32, None)
+        del A_
+        eb = E[dense]
+        E[name] = Entry(name, "sparse", dtA=dt, dtB=eb.dtB, M=n, N=n, K=n, vals=v_, idx=i_, B=eb.B, hB=eb.hB,
+                        ldb=n, D=Di if dt == "i8" else D, out="i32" if dt == "i8" else "f32",
+                        alpha=1 if dt == "i8" else eb.sB, beta=0, dense=dense,
+                        peak=PEAK["i8" if dt == "i8" else "fp8"], speak=SPARSE_PEAK["i8" if dt == "i8" else "fp8"],
+                        unit="TOPS" if dt == "i8" else "TFLOP/s")
     # skinny problems: the wide operand (4n x n bf16 ~ N(0,1)) drawn on the device
-    SK = (4 * n, 16)
     g = torch.Generator(device="cuda").manual_seed(W.SEED_A)
-    Wide = torch.randn((SK[0], K), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
-    Narrow = torch.randn((SK[1], K), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
-    Dsk = torch.empty((SK[0], SK[1]), dtype=torch.float32, device="cuda")
+    Wide = torch.randn((4 * n, n), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
+    Narrow = torch.randn((16, n), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
+    Dsk = torch.empty((4 * n, 16), dtype=torch.float32, device="cuda")
+    for name, (A_, B_, M_, N_) in (("skinny_n16", (Wide, Narrow, 4 * n, 16)),
+                                   ("skinny_m16", (Narrow, Wide, 16, 4 * n))):
+        E[name] = Entry(name, "skinny", dtA="bf16", dtB="bf16", layA="k_contig", layB="k_contig", M=M_, N=N_,
+                        K=n, A=A_, B=B_, lda=n, ldb=n, C=None, D=Dsk, out="f32", alpha=1.0, beta=0.0, sA=1.0,
+                        sB=1.0, nbytes=(4 * n * n + 16 * n) * 2 + 4 * n * 16 * 4)
     # binary64 operands ~ N(0,1), drawn on the device
-    A64 = torch.randn((M, K), generator=g, dtype=torch.float64, device="cuda")
-    B64 = torch.randn((N, K), generator=g, dtype=torch.float64, device="cuda")  # column-major K x N
-    C64 = torch.randn((M, N), generator=g, dtype=torch.float64, device="cuda")
-    D64 = torch.empty((M, N), dtype=torch.float64, device="cuda")
+    if want("f64"):
+        A64 = torch.randn((n, n), generator=g, dtype=torch.float64, device="cuda")
+        B64 = torch.randn((n, n), generator=g, dtype=torch.float64, device="cuda")  # column-major K x N
+        C64 = torch.randn((n, n), generator=g, dtype=torch.float64, device="cuda")
+        E["f64"] = Entry("f64", "f64", M=n, N=n, K=n, A=A64, B=B64, C=C64,
+                         D=torch.empty((n, n), dtype=torch.float64, device="cuda"), alpha=1.0, beta=1.0,
+                         peak=PEAK["f64"], unit="TFLOP/s")
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s")
 
     stream = torch.cuda.Stream()
     s = stream.cuda_stream
 
-    def call(name):
-        if name in ("bf16", "f16"):
-            a, lda, b, ldb, sa, sb = ops[name]
-            mcg.gemm_dense(name, name, 0, 0, M, N, K, a, lda, b, ldb, C, D, N, "f32", 1.0, 1.0,
-                           stream=s)
-        elif name == "i8":
-            a, lda, b, ldb, sa, sb = ops[name]
-            mcg.gemm_dense("i8", "i8", 0, 0, M, N, K, a, lda, b, ldb, Ci, Di, N, "i32", 1, 1, stream=s)
-        elif name.startswith("e4m3x"):
-            a, lda, b, ldb, sa, sb = ops[name]
-            mcg.gemm_dense("e4m3", name.split("x")[1], 0, 0, M, N, K, a, lda, b, ldb, None, D, N, "f32",
-                           1.0, 0.0, sa, sb, stream=s)
-        elif name == "compress24":
-            mcg.compress24("bf16", M, K, As, K, vals, K // 2, idx, idx.shape[1], None, stream=s)
-        elif name == "sparse24":
-            mcg.gemm_sparse24("bf16", "bf16", 0, M, N, K, vals, K // 2, idx, idx.shape[1], Bs, K, None,
-                              D, N, "f32", 1.0, 0.0, stream=s)
-        elif name == "sparse24_i8":
-            v_, i_, B_ = sp8["i8"]
-            mcg.gemm_sparse24("i8", "i8", 0, M, N, K, v_, K // 2, i_, i_.shape[1], B_, K, None, Di, N,
-                              "i32", 1, 0, stream=s)
-        elif name == "sparse24_e4m3":
-            v_, i_, B_ = sp8["e4m3"]
-            mcg.gemm_sparse24("e4m3", "e4m3", 0, M, N, K, v_, K // 2, i_, i_.shape[1], B_, K, None, D, N,
-                              "f32", B8.scale, 0.0, stream=s)
-        elif name == "bf16_out":
-            a, lda, b, ldb, sa, sb = ops["bf16"]
-            mcg.gemm_dense("bf16", "bf16", 0, 0, M, N, K, a, lda, b, ldb, C16, D16, N, "bf16", 1.0, 1.0,
-                           stream=s)
-        elif name == "skinny_n16":  # A = Wide (M = 4n), B = Narrow (N = 16, column-major)
-            mcg.gemm_dense("bf16", "bf16", 0, 0, SK[0], SK[1], K, Wide, K, Narrow, K, None, Dsk, SK[1],
-                           "f32", 1.0, 0.0, stream=s)
-        elif name == "f64":
-            mcg.gemm_dense("f64", "f64", 0, 0, M, N, K, A64, K, B64, K, C64, D64, N, "f64", 1.0, 1.0, stream=s)
-        elif name == "skinny_m16":  # A = Narrow (M = 16), B = Wide (N = 4n, column-major)
-            mcg.gemm_dense("bf16", "bf16", 0, 0, SK[1], SK[0], K, Narrow, K, Wide, K, None, Dsk, SK[0],
-                           "f32", 1.0, 0.0, stream=s)
+    def call(e):
+        if e.kind in ("dense", "skinny"):
+            mcg.gemm_dense(e.dtA, e.dtB, e.layA, e.layB, e.M, e.N, e.K, e.A, e.lda, e.B, e.ldb, e.C, e.D, e.N,
+                           e.out, e.alpha, e.beta, e.sA, e.sB, stream=s)
+        elif e.kind == "compress":
+            mcg.compress24(e.dt, e.M, e.K, e.A, e.K, e.vals, e.K // 2, e.idx, e.K // 32, None, stream=s)
+        elif e.kind == "sparse":
+            mcg.gemm_sparse24(e.dtA, e.dtB, "k_contig", e.M, e.N, e.K, e.vals, e.K // 2, e.idx, e.K // 32, e.B,
+                              e.ldb, None, e.D, e.N, e.out, e.alpha, e.beta, stream=s)
+        elif e.kind == "f64":
+            mcg.gemm_dense("f64", "f64", 0, 0, e.M, e.N, e.K, e.A, e.K, e.B, e.K, e.C, e.D, e.N, "f64", e.alpha,
+                           e.beta, stream=s)
 
-    names = ["bf16", "f16", "i8", "e4m3xe4m3", "e4m3xe5m2", "compress24", "sparse24", "bf16_out",
-             "skinny_n16", "skinny_m16", "sparse24_i8", "sparse24_e4m3", "f64"]
-    if args.only:
-        keep = set(args.only.split(","))
-        names = [x for x in names if x in keep or x == "compress24" and "sparse24" in keep]
+    order = ["bf16", "f16", "bf16_Arow_Brow", "bf16_Acol_Bcol", "bf16_Acol_Brow", "f16_Arow_Brow",
+             "f16_Acol_Bcol", "f16_Acol_Brow", "bf16_256", "i8_4096", "i8", "e4m3xe4m3", "e4m3xe5m2",
+             "compress24", "sparse24", "bf16_out", "skinny_n16", "skinny_m16", "sparse24_i8", "sparse24_e4m3",
+             "f64"]
+    names = [x for x in order if x in E and (only is None or x in only or x == "compress24" and "sparse24" in only)]
     ev = {x: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)] for x in names}
+
+    def run(e):
+        for _ in range(getattr(e, "batch", 1)):
+            call(e)
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             for x in names:
-                call(x)
+                run(E[x])
         torch.cuda.synchronize()
         t_start = time.perf_counter()
         for step in range(args.steps):
             for x in names:
                 ev[x][step][0].record(stream)
-                call(x)
+                run(E[x])
                 ev[x][step][1].record(stream)
         torch.cuda.synchronize()
         t_end = time.perf_counter()
+    log(f"timed {args.steps} steps in {t_end - t_start:.2f} s")
 
-    ms = {x: float(np.mean([a.elapsed_time(b) for a, b in ev[x]])) for x in names}
-    flops = 2.0 * M * N * K
+    # average duration of one call, ms
+    ms = {x: float(np.mean([a.elapsed_time(b) for a, b in ev[x]])) / getattr(E[x], "batch", 1) for x in names}
     per = {}
     for x in names:
-        t = ms[x] * 1e-3
-        if x == "compress24":
-            nbytes = M * K * 2 + M * K // 2 * 2 + M * ((K + 31) // 32) * 4
-            per[x] = {"GB/s": nbytes / t / 1e9, "ms": ms[x], "frac_of_hbm_peak": nbytes / t / 1e9 / HBM_PEAK_GBS,
-                      "bytes": nbytes}
-        elif x.startswith("skinny"):
-            nbytes = SK[0] * K * 2 + SK[1] * K * 2 + SK[0] * SK[1] * 4
-            shape = (SK[0], SK[1], K) if x == "skinny_n16" else (SK[1], SK[0], K)
-            per[x] = {"GB/s": nbytes / t / 1e9, "ms": ms[x], "frac_of_hbm_peak": nbytes / t / 1e9 / HBM_PEAK_GBS,
-                      "bytes": nbytes, "TFLOP/s": 2.0 * SK[0] * SK[1] * K / t / 1e12, "MxNxK": shape}
-        elif x == "bf16_out":
-            tf = flops / t / 1e12
-            per[x] = {"TFLOP/s": tf, "ms": ms[x], "peak": PEAK["bf16"], "frac_of_peak": tf / PEAK["bf16"]}
-        elif x in ("sparse24_i8", "sparse24_e4m3"):
-            tf = flops / t / 1e12
-            dense = "i8" if x == "sparse24_i8" else "e4m3xe4m3"
-            pk = PEAK["i8"] if x == "sparse24_i8" else PEAK["fp8"]
-            u = "TOPS" if x == "sparse24_i8" else "TFLOP/s"
-            per[x] = {f"{u}_dense_equiv": tf, f"{u}_algorithmic": tf / 2, "ms": ms[x],
-                      "frac_of_dense_peak": tf / pk,
-                      f"vs_dense_{dense}": tf / (flops / (ms[dense] * 1e-3) / 1e12) if dense in ms else None}
-        elif x == "sparse24":
-            tf = flops / t / 1e12
-            per[x] = {"TFLOP/s_dense_equiv": tf, "TFLOP/s_algorithmic": tf / 2, "ms": ms[x],
-                      "frac_of_dense_bf16_peak": tf / PEAK["bf16"],
-                      "vs_dense_bf16": tf / (flops / (ms["bf16"] * 1e-3) / 1e12) if "bf16" in ms else None}
+        e, t = E[x], ms[x] * 1e-3
+        if e.kind in ("compress", "skinny"):
+            per[x] = {"GB/s": e.nbytes / t / 1e9, "ms": ms[x], "frac_of_hbm_peak": e.nbytes / t / 1e9 / HBM_PEAK_GBS,
+                      "bytes": e.nbytes}
+            if e.kind == "skinny":
+                per[x].update({"TFLOP/s": 2.0 * e.M * e.N * e.K / t / 1e12, "MxNxK": (e.M, e.N, e.K)})
+            continue
+        tf = 2.0 * e.M * e.N * e.K / t / 1e12
+        if e.kind == "sparse":
+            d = {f"{e.unit}_dense_equiv": tf, f"{e.unit}_algorithmic": tf / 2, "ms": ms[x],
+                 "frac_of_sparse_peak": tf / e.speak, "sparse_peak": e.speak, "frac_of_dense_peak": tf / e.peak}
+            if e.dense in ms:
+                d[f"vs_dense_{e.dense}"] = tf / (2.0 * e.M * e.N * e.K / (ms[e.dense] * 1e-3) / 1e12)
+            per[x] = d
         else:
-            pk = PEAK["fp8"] if x.startswith("e4m3") else PEAK[x]
-            tf = flops / t / 1e12
-            per[x] = {("TOPS" if x == "i8" else "TFLOP/s"): tf, "ms": ms[x], "peak": pk, "frac_of_peak": tf / pk}
+            per[x] = {e.unit: tf, "ms": ms[x], "peak": e.peak, "frac_of_peak": tf / e.peak,
+                      "MxNxK": (e.M, e.N, e.K)}
+            if e.kind == "dense":
+                per[x]["layout"] = LAYOUT_NAMES[(e.layA, e.layB)]
     head = "bf16" if "bf16" in names else names[0]
-    value = flops / (ms[head] * 1e-3) / 1e12 if head != "compress24" else per[head]["GB/s"]
+    value = per[head].get("TFLOP/s", per[head].get("TOPS", per[head].get("GB/s")))
 
-    # CPU oracle baseline: whole rows of D of the bf16 workload, timed on the host cores
+    # ---------------------------------------------------------------- parity
+    # Every entry once more; sampled outputs against the oracle (the acceptance
+    # test of the parity tests: the float bound, or bit-exact integers / codes).
+    parity = None
+    if not args.no_parity:
+        import oracle
+        parity = {}
+        t_par = time.perf_counter()
+        for x in names:
+            e = E[x]
+            D_ = getattr(e, "D", None)
+            with torch.cuda.stream(stream):
+                if D_ is not None:  # a stale or unwritten output must not pass
+                    D_.fill_({torch.int32: 0x7FC00000, torch.int16: 0x7FC0}.get(D_.dtype, float("nan")))
+                call(e)
+            torch.cuda.synchronize()
+            if e.kind == "compress":
+                rows = np.arange(0, e.M, 97)
+                v, i, nv = oracle.compress24(e.dt, e.hA[rows])
+                ok = (nv == 0 and np.array_equal(e.vals.cpu().numpy().view(np.uint16)[rows], v)
+                      and np.array_equal(e.idx.cpu().numpy().view(np.uint32)[rows], i))
+                parity[x] = {"ok": bool(ok), "rows": len(rows), "exact": True}
+                continue
+            rows, cols = W.sample_coords(e.M, e.N, n_random=1024, full_rows=(e.M - 1,))
+            if e.kind == "skinny":
+                hA = e.A.cpu().numpy().view(np.uint16)
+                hB = e.B.cpu().numpy().view(np.uint16)
+                dg = e.D.cpu().numpy().reshape(-1)[rows * e.N + cols]
+                ref, sm = oracle.gemm_float("bf16", "bf16", "k_contig", "k_contig", e.M, e.N, e.K, hA, e.lda,
+                                            hB, e.ldb, rows=rows, cols=cols)
+                r = oracle.check_float(dg, ref, sm, e.K)
+            elif e.kind == "f64":
+                hA, hB, hC = e.A.cpu().numpy(), e.B.cpu().numpy(), e.C.cpu().numpy()
+                dg = e.D.cpu().numpy()[rows, cols]
+                ref, sm = oracle.gemm_f64("k_contig", "k_contig", e.M, e.N, e.K, hA, e.K, hB, e.K, hC, e.N,
+                                          e.alpha, e.beta, rows=rows, cols=cols)
+                r = oracle.check_f64(dg, ref, sm, e.K, e.alpha, e.beta, hC[rows, cols])
+            elif e.kind == "sparse":
+                hv = e.vals.cpu().numpy().view(oracle.CODE_NP[e.dtA])
+                hi = e.idx.cpu().numpy().view(np.uint32)
+                ref, sm = oracle.gemm_sparse24(e.dtA, e.dtB, "k_contig", e.M, e.N, e.K, hv, hi, e.hB, e.ldb,
+                                               alpha=e.alpha, beta=0.0, rows=rows, cols=cols, out=e.out)
+                dg = e.D.cpu().numpy()[rows, cols]
+                r = (oracle.check_exact(dg, ref) if e.dtA == "i8"
+                     else oracle.check_float(dg, ref, sm, e.K, e.alpha))
+            else:
+                dD = e.D.cpu().numpy()
+                if e.out == "bf16":
+                    dg = (dD.view(np.uint16).astype(np.uint32) << 16).view(np.float32)[rows, cols]
+                else:
+                    dg = dD[rows, cols]
+                if e.dtA == "i8":
+                    ref = oracle.gemm_i8(e.layA, e.layB, e.M, e.N, e.K, e.hA, e.lda, e.hB, e.ldb, e.hC, e.N,
+                                         e.alpha, e.beta, rows=rows, cols=cols)
+                    r = oracle.check_exact(dg, ref)
+                else:
+                    ref, sm = oracle.gemm_float(e.dtA, e.dtB, e.layA, e.layB, e.M, e.N, e.K, e.hA, e.lda, e.hB,
+                                                e.ldb, e.hC, e.N, e.alpha, e.beta, e.sA, e.sB, rows=rows,
+                                                cols=cols, out=e.out)
+                    cc = None
+                    if e.beta != 0:
+                        cc = e.hC[rows, cols]
+                        if e.out == "bf16":
+                            cc = (cc.astype(np.uint32) << 16).view(np.float32)
+                    r = oracle.check_float(dg, ref, sm, e.K, e.alpha, e.sA, e.sB, e.beta, cc, out=e.out)
+            parity[x] = {"ok": bool(r["ok"]), "outputs": r["n"], "exact": "max_ratio" not in r}
+            if "max_ratio" in r:
+                parity[x]["max_err_over_bound"] = r["max_ratio"]
+            if not r["ok"]:
+                log(f"PARITY FAILURE {x}: {r}")
+        parity = {"all_ok": all(v["ok"] for v in parity.values()),
+                  "sample": "per entry: its last row and 1024 random outputs (compress24: every 97th row), "
+                            "recomputed by the oracle; float results within the acceptance bound, "
+                            "integers and codes bit-exact",
+                  "seconds": time.perf_counter() - t_par, "entries": parity}
+        log(f"parity: all_ok = {parity['all_ok']} ({parity['seconds']:.1f} s)")
+
+    # ---------------------------------------------------------------- CPU baseline
+    # The oracle as it stands, all host threads, on whole rows of each workload
+    # (bounded time), plus the 256^3 workload whole and single-threaded.
     cpu = None
     if not args.no_cpu:
         import oracle
-        A, B = host_bf16
+        model, sockets = host_cpu()
         nthr = oracle.max_threads()
-        t1 = time.perf_counter()
-        rows, cols = np.zeros(N, np.int64), np.arange(N, dtype=np.int64)
-        oracle.gemm_float("bf16", "bf16", "k_contig", "k_contig", M, N, K, A.codes, A.ld, B.codes,
-                          B.ld, rows=rows, cols=cols)
-        one = time.perf_counter() - t1
-        nrows = max(1, min(M, int(args.cpu_seconds / max(one, 1e-6))))
-        rr = np.repeat(np.arange(nrows, dtype=np.int64) * (M // nrows), N)
-        cc = np.tile(np.arange(N, dtype=np.int64), nrows)
-        t1 = time.perf_counter()
-        oracle.gemm_float("bf16", "bf16", "k_contig", "k_contig", M, N, K, A.codes, A.ld, B.codes,
-                          B.ld, rows=rr, cols=cc)
-        tcpu = time.perf_counter() - t1
-        cpu = {"value": 2.0 * nrows * N * K / tcpu / 1e12, "unit": "TFLOP/s", "cores": nthr,
-               "kind": "oracle",
-               "sample": f"{nrows} whole rows ({nrows * N} outputs, K={K}) of the dense bf16 {n}^3 "
-                         f"workload; {tcpu:.1f} s on {nthr} threads ({platform.processor() or 'host'})"}
+
+        def time_rows(e, budget):
+            def run_rows(nrows):
+                rr = np.repeat(np.arange(nrows, dtype=np.int64) * (e.M // nrows), e.N)
+                cc = np.tile(np.arange(e.N, dtype=np.int64), nrows)
+                t1 = time.perf_counter()
+                if e.kind == "sparse":
+                    oracle.gemm_sparse24(e.dtA, e.dtB, "k_contig", e.M, e.N, e.K, e.hv, e.hi, e.hB, e.ldb,
+                                         alpha=e.alpha, rows=rr, cols=cc, out=e.out)
+                elif e.dtA == "i8":
+                    oracle.gemm_i8(e.layA, e.layB, e.M, e.N, e.K, e.hA, e.lda, e.hB, e.ldb, e.hC, e.N, e.alpha,
+                                   e.beta, rows=rr, cols=cc)
+                else:
+                    oracle.gemm_float(e.dtA, e.dtB, e.layA, e.layB, e.M, e.N, e.K, e.hA, e.lda, e.hB, e.ldb,
+                                      e.hC, e.N, e.alpha, e.beta, e.sA, e.sB, rows=rr, cols=cc)
+                return time.perf_counter() - t1
+            one = run_rows(1)
+            nrows = max(1, min(e.M, int(budget / max(one, 1e-6))))
+            t = run_rows(nrows)
+            rate = 2.0 * nrows * e.N * e.K / t / 1e12
+            return {"value": rate, "unit": "TOPS" if e.dtA == "i8" else "TFLOP/s", "seconds": t,
+                    "sample": f"{nrows} whole rows ({nrows * e.N} outputs) of {e.M}x{e.N}x{e.K}",
+                    "gpu_over_cpu": per[e.name][e.unit if e.kind != "sparse" else f"{e.unit}_dense_equiv"] / rate
+                    if e.name in per else None}
+
+        per_cfg = {}
+        eh = E["bf16"]
+        per_cfg["bf16_8192"] = time_rows(eh, args.cpu_seconds)
+        for key, x in (("i8_4096", "i8_4096"), ("e4m3xe4m3_8192", "e4m3xe4m3"), ("sparse24_bf16_8192", "sparse24")):
+            if x not in E:
+                continue
+            e = E[x]
+            if e.kind == "sparse":
+                e.hv = e.vals.cpu().numpy().view(oracle.CODE_NP[e.dtA])
+                e.hi = e.idx.cpu().numpy().view(np.uint32)
+            per_cfg[key] = time_rows(e, args.cpu_seconds / 5)
+        # 256^3 whole, all threads and one thread
+        e = E["bf16_256"]
+        for tag, thr in (("bf16_256", nthr), ("bf16_256_1thread", 1)):
+            oracle.set_threads(thr)
+            t1 = time.perf_counter()
+            reps = 0
+            while reps < 3 or time.perf_counter() - t1 < 0.5:
+                oracle.gemm_float("bf16", "bf16", "k_contig", "k_contig", 256, 256, 256, e.hA, 256, e.hB, 256)
+                reps += 1
+            t = (time.perf_counter() - t1) / reps
+            per_cfg[tag] = {"value": 2.0 * 256 ** 3 / t / 1e12, "unit": "TFLOP/s", "seconds": t, "threads": thr,
+                            "sample": "the whole 256^3 product",
+                            "gpu_over_cpu": per["bf16_256"]["TFLOP/s"] / (2.0 * 256 ** 3 / t / 1e12)
+                            if "bf16_256" in per else None}
+        oracle.set_threads(nthr)
+        h = per_cfg["bf16_8192"]
+        cpu = {"value": h["value"], "unit": "TFLOP/s", "cores": nthr, "kind": "oracle",
+               "sample": f"{h['sample']} of the dense bf16 8192^3 workload (K-contiguous pair, with C); "
+                         f"{h['seconds']:.1f} s on {nthr} threads",
+               "cpu_model": model, "sockets": sockets, "per_workload": per_cfg}
 
     res = {
         "metric": METRIC,
@@ -289,17 +467,21 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"dense bf16 GEMM {n}x{n}x{n}, A row-major, B column-major, "
                                f"C ~ N(0,1) fp32, alpha=beta=1, fp32 out; step = all "
-                               f"{len(names)} hot-path calls at {n}^3",
-                   "M": M, "N": N, "K": K, "entries": names},
+                               f"{len(names)} hot-path entries (per_dtype)",
+                   "M": n, "N": n, "K": n, "entries": names},
         "roofline": {"bound": "mfma", "achieved": value, "peak": PEAK["bf16"], "unit": "TFLOP/s",
-                     "frac": value / PEAK["bf16"], "traffic": measured_traffic() if head == "bf16" and n == 8192 else None,
+                     "frac": value / PEAK["bf16"], "traffic": measured_traffic() if head == "bf16" else None,
                      "traffic_unit": "HBM bytes per launch",
-                     "algorithmic_bytes": (2 * M * K + 2 * K * N + 8 * M * N),
-                     "kernel": "mcg::fast::gemm_fast_kernel<BF16, 0, 0, 256> (256x256 tile, 8-wave ping-pong)", "kernel_ms": ms.get(head)},
+                     "algorithmic_bytes": (2 * n * n + 2 * n * n + 8 * n * n),
+                     "kernel": "mcg::fast::gemm_fast_kernel<BF16, 0, 0, 256> (256x256 tile, 8-wave ping-pong)",
+                     "kernel_ms": ms.get(head)},
         "cpu_baseline": cpu,
+        "parity": parity,
         "per_dtype": per,
     }
     print(json.dumps(res), flush=True)
+    if parity is not None and not parity["all_ok"]:
+        sys.exit(1)
 
 
 if __name__ == "__main__":

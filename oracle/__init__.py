@@ -90,6 +90,8 @@ def lib():
         L.orc_compress24.restype = i64
         L.orc_decompress24.argtypes = [i32, i64, i64, vp, i64, vp, i64, vp, i64]
         L.orc_max_threads.argtypes = []
+        L.orc_set_threads.argtypes = [i32]
+        L.orc_set_threads.restype = None
         _lib = L
     return _lib
 
@@ -107,6 +109,11 @@ def _flat(a, dtype):
 
 def max_threads() -> int:
     return int(lib().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Number of OpenMP threads the oracle's parallel loops use from now on."""
+    lib().orc_set_threads(int(n))
 
 
 def decode(dtype: str, codes) -> np.ndarray:

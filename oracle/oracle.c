@@ -471,3 +471,14 @@ int orc_max_threads(void) {
     return 1;
 #endif
 }
+
+/* Sets the number of OpenMP threads later parallel regions use (n >= 1); the
+   CPU baseline times the oracle single-threaded with it.  No arithmetic. */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
