@@ -32,6 +32,9 @@
 //    ds_read_b64_tr_b8 : output lane t, element e (0..7) = byte (t & 7) of the
 //      8 bytes addressed by lane 2e + (t >> 3).
 //
+// frag_layout.hpp holds these maps as functions, (lane, register) <-> (i, j,
+// block), together with the 32x32 and FP64 layouts; every epilogue uses them.
+//
 // fp8 operands use the OCP encodings (measured: code 0x7E of E4M3 is 448); the
 // f8f6f4 instruction takes the A/B formats in its cbsz/blgp fields
 // (0 = E4M3, 1 = E5M2) and, with zero scale operands, computes plain products.
@@ -39,6 +42,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "frag_layout.hpp"
 #include "gemm_kernels.hpp"
 
 namespace mcg {
@@ -179,10 +183,6 @@ struct OpF8W {
   }
 };
 
-// ------------------------------------------------------------ output layout
-// 16x16 output tile: lane l, register r -> (row, col) of the instruction output.
-__host__ __device__ constexpr int out_row(int lane, int r) { return 4 * (lane >> 4) + r; }
-__host__ __device__ constexpr int out_col(int lane) { return lane & 15; }
 
 // ------------------------------------------------------------ LDS primitives
 // ----------------------------------------------------- output conversions

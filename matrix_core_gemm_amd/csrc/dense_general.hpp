@@ -28,6 +28,7 @@
 #pragma once
 #include "gemm_kernels.hpp"
 #include "tile_io.hpp"
+#include "frag_layout.hpp"
 
 namespace mcg {
 
@@ -113,17 +114,21 @@ __global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs p) {
     __syncthreads();
   }
 
-  // epilogue: lane holds D[m][n .. n+3] with m = row base + (lane & 15),
-  // n = column base + 4 * (lane >> 4)
+  // epilogue: each instruction multiplied (B fragment) x (A fragment), so element
+  // (i', j') of its 16 x 16 accumulator layout is D[m][n] with m = j', n = i'
+  // within the block; register r holds (i' + r, j') for (i', j') =
+  // ACC::coord(lane, 0): 4 consecutive columns of one row per lane
+  using ACC = frag::Acc<frag::ACC_16x16>;
+  const int acc_m = ACC::coord(lane, 0).j, acc_n = ACC::coord(lane, 0).i;
   if (gridDim.y > 1) {
     // split K: add alpha * partial sum into the zeroed D (binary32 or wrapping int32)
 #pragma unroll
     for (int i = 0; i < WTM; ++i) {
-      const int64_t m = m0 + wm * (BM / 2) + i * 16 + (lane & 15);
+      const int64_t m = m0 + wm * (BM / 2) + i * 16 + acc_m;
       if (m >= p.M) continue;
 #pragma unroll
       for (int j = 0; j < WTN; ++j) {
-        const int64_t n = n0 + wn * (BN / 2) + j * 16 + 4 * (lane >> 4);
+        const int64_t n = n0 + wn * (BN / 2) + j * 16 + acc_n;
         const int64_t off = m * p.ldc + n;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -140,11 +145,11 @@ __global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs p) {
   const bool vec_ok = p.vec_cd;
 #pragma unroll
   for (int i = 0; i < WTM; ++i) {
-    const int64_t m = m0 + wm * (BM / 2) + i * 16 + (lane & 15);
+    const int64_t m = m0 + wm * (BM / 2) + i * 16 + acc_m;
     if (m >= p.M) continue;
 #pragma unroll
     for (int j = 0; j < WTN; ++j) {
-      const int64_t n = n0 + wn * (BN / 2) + j * 16 + 4 * (lane >> 4);
+      const int64_t n = n0 + wn * (BN / 2) + j * 16 + acc_n;
       if (n >= p.N) continue;
       const int64_t off = m * p.ldc + n;
       if constexpr (Op::INT_ACC) {

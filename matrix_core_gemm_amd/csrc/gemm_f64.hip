@@ -410,17 +410,19 @@ __global__ __launch_bounds__(THREADS, 2) void dgemm_kernel(F64Args p) {
     }
   }
 
-  // result register r of lane l: row 4r + (l >> 4), column l & 15 of each 16 x 16 piece
+  // result register pair r of a lane: element ACC::coord(lane, r) of each 16 x 16
+  // piece (row 4r + lane / 16, column lane mod 16: the FP64 16 x 16 layout)
+  using ACC = frag::Acc<frag::ACC_16x16_F64>;
   double* D = p.D;
 #pragma unroll
   for (int f = 0; f < FM; ++f)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t row = m0 + wm + 16 * f + 4 * r + (lane >> 4);
+      const int64_t row = m0 + wm + 16 * f + ACC::coord(lane, r).i;
       if (row >= p.M) continue;
 #pragma unroll
       for (int c = 0; c < FN; ++c) {
-        const int64_t col = n0 + wn + 16 * c + (lane & 15);
+        const int64_t col = n0 + wn + 16 * c + ACC::coord(lane, r).j;
         if (col >= p.N) continue;
         const int64_t off = row * p.ldc + col;
         if (gridDim.y > 1) {

@@ -47,6 +47,7 @@
 // operand window below 2 GiB (32-bit buffer offsets).
 #pragma once
 #include "fast_tiles.hpp"
+#include "frag_layout.hpp"
 #include "gemm_kernels.hpp"
 
 namespace mcg {
@@ -316,8 +317,14 @@ void gemm_fast_kernel(DenseArgs p) {
     else add(acc[1]);
   }
 
-  // epilogue: tile (i, j), register group r4: lane holds D[m][n .. n+3] with
-  // m = m0 + rbA + 32 i + (lane & 31), n = n0 + rbB + 32 j + 8 r4 + 4 (lane >> 5)
+  // epilogue: each instruction multiplied (B fragment) x (A fragment), so element
+  // (i', j') of its 32 x 32 accumulator layout is D[m][n] with m = j' and n = i'
+  // within the block: block (i, j), register 4 r4 + r of a lane holds
+  // D[m0 + rbA + 32 i + j'][n0 + rbB + 32 j + i' + r], (i', j') = ACC::coord(lane, 4 r4),
+  // i.e. 4 consecutive columns of one row per register group r4
+  using ACC = frag::Acc<frag::ACC_32x32>;
+  const int acc_m = ACC::coord(lane, 0).j;  // m within a block
+  auto acc_n = [&](int r4) { return ACC::coord(lane, 4 * r4).i; };  // first n of register group r4
   const bool vec_ok = p.vec_cd;
   const s1* C = (const s1*)p.C;
   s1* D = (s1*)p.D;
@@ -386,7 +393,7 @@ void gemm_fast_kernel(DenseArgs p) {
       for (int j = 0; j < WTN; ++j)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int ch = 8 * j + 2 * r4 + (lane >> 5);
+          const int ch = (32 * j + acc_n(r4)) / 4;  // 16-byte chunk of the wavefront's 64 columns
           v4 x;
 #pragma unroll
           for (int r = 0; r < 4; ++r) x[r] = acc[i][j][4 * r4 + r];
@@ -447,13 +454,13 @@ void gemm_fast_kernel(DenseArgs p) {
       for (int i = 0; i < WTM; ++i) {
         __builtin_amdgcn_sched_barrier(0);
         if (KS && i != grp) continue;  // the partner wave stores this row block
-        const int64_t m = m0 + rbA + 32 * i + (lane & 31);
+        const int64_t m = m0 + rbA + 32 * i + acc_m;
         if (m >= p.M) continue;
 #pragma unroll
         for (int j = 0; j < WTN; ++j)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const int64_t n = n0 + rbB + 32 * j + 8 * r4 + 4 * (lane >> 5);
+            const int64_t n = n0 + rbB + 32 * j + acc_n(r4);
             if (n >= p.N) continue;
             const int64_t off = m * p.ldc + n;
             const bool full = vec_ok && n + 4 <= p.N;
@@ -481,13 +488,13 @@ void gemm_fast_kernel(DenseArgs p) {
 #pragma unroll
     for (int i = 0; i < WTM; ++i) {
       if (KS && i != grp) continue;  // the partner wave stores this row block
-      const int64_t m = m0 + rbA + 32 * i + (lane & 31);
+      const int64_t m = m0 + rbA + 32 * i + acc_m;
       if (m >= p.M) continue;
 #pragma unroll
       for (int j = 0; j < WTN; ++j)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int64_t n = n0 + rbB + 32 * j + 8 * r4 + 4 * (lane >> 5);
+          const int64_t n = n0 + rbB + 32 * j + acc_n(r4);
           if (n >= p.N) continue;
           const bool full = vec_ok && n + 4 <= p.N;
           v4 c = {};

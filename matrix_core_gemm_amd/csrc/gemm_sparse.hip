@@ -255,16 +255,20 @@ __global__ __launch_bounds__(256) void gemm_sparse_kernel(SparseArgs p) {
     __syncthreads();
   }
 
-  // epilogue: lane holds D[m .. m+3][n], m = row base + 4*(lane >> 4), n = column base + (lane & 15)
+  // epilogue: the sparse (A) fragment is the instruction's first operand, so
+  // element (i', j') of its 16 x 16 accumulator layout is D[m][n] with m = i',
+  // n = j' within the block, (i', j') = ACC::coord(lane, r): 4 consecutive rows
+  // of one column per lane
+  using ACC = frag::Acc<frag::ACC_16x16>;
 #pragma unroll
   for (int i = 0; i < WTM; ++i) {
 #pragma unroll
     for (int j = 0; j < WTN; ++j) {
-      const int64_t n = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
+      const int64_t n = n0 + wn * (BN / 2) + j * 16 + ACC::coord(lane, 0).j;
       if (n >= p.N) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + wm * (BM / 2) + i * 16 + 4 * (lane >> 4) + r;
+        const int64_t m = m0 + wm * (BM / 2) + i * 16 + ACC::coord(lane, r).i;
         if (m >= p.M) continue;
         const int64_t off = m * p.ldc + n;
         if constexpr (Op::INT_ACC) {

@@ -39,6 +39,7 @@
 //     stores one 4-byte value per register (each store instruction writes two
 //     128-byte row segments).
 #include "fast_tiles.hpp"
+#include "frag_layout.hpp"
 #include "gemm_kernels.hpp"
 
 namespace mcg {
@@ -346,17 +347,20 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA outstanding at exit
 
-  // epilogue: block (i, j), register r holds D[m][n] with
-  // m = m0 + rbA + 32 i + 8 (r / 4) + 4 (lane >> 5) + r % 4, n = n0 + rbB + 32 j + (lane & 31)
+  // epilogue: the sparse (A) fragment is the instruction's first operand, so
+  // element (i', j') of its 32 x 32 accumulator layout is D[m][n] with m = i',
+  // n = j' within the block: block (i, j), register r holds
+  // D[m0 + rbA + 32 i + i'][n0 + rbB + 32 j + j'], (i', j') = ACC::coord(lane, r)
+  using ACC = frag::Acc<frag::ACC_32x32>;
   const bool interior = m0 + SP_BM <= p.M && n0 + SP_BN <= p.N;
 #pragma unroll
   for (int i = 0; i < WTM; ++i)
 #pragma unroll
     for (int j = 0; j < WTN; ++j) {
-      const int64_t n = n0 + rbB + 32 * j + (lane & 31);
+      const int64_t n = n0 + rbB + 32 * j + ACC::coord(lane, 0).j;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + rbA + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+        const int64_t m = m0 + rbA + 32 * i + ACC::coord(lane, r).i;
         if (!interior && (m >= p.M || n >= p.N)) continue;
         const int64_t off = m * p.ldc + n;
         if constexpr (Op::INT_ACC) {

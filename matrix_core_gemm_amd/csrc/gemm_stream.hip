@@ -175,11 +175,14 @@ __global__ __launch_bounds__(THREADS) void gemm_stream_kernel(DenseArgs p) {
     }
   }
 
-  // epilogue: register r = 4 r4 + e of the lane holds D[m][n] with
-  // m = m0 + rbA + (lane & 31), n = n0 + rbB + 8 r4 + 4 (lane >> 5) + e
-  const int64_t m = m0 + rbA + (lane & 31);
+  // epilogue: the instruction multiplied (B fragment) x (A fragment), so element
+  // (i', j') of its 32 x 32 accumulator layout is D[m][n] with m = j', n = i':
+  // register 4 r4 + e of the lane holds D[m][nb + 8 r4 + e] with (i', j') =
+  // ACC::coord(lane, 4 r4) = (nb - n0 - rbB + 8 r4, m - m0 - rbA)
+  using ACC = frag::Acc<frag::ACC_32x32>;
+  const int64_t m = m0 + rbA + ACC::coord(lane, 0).j;
   if (m >= p.M) return;
-  const int64_t nb = n0 + rbB + 4 * (lane >> 5);
+  const int64_t nb = n0 + rbB + ACC::coord(lane, 0).i;
   if (gridDim.y > 1) {
     // split K: add alpha * partial sum into the zeroed D
 #pragma unroll
