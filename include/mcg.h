@@ -149,6 +149,47 @@ int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB,
                double alpha, double beta, float scaleA, float scaleB, void* stream);
 
 /*
+ * gemm_dense_ws -- gemm_dense with a caller-provided device workspace.
+ *
+ * Computes exactly what gemm_dense computes (the matrix fused multiply-add of
+ * "Accurate Models of AMD Matrix Cores", Section 2, Eq. (1)), with the same
+ * arguments, validation, accuracy bound and errors.  The workspace lets problems
+ * on the 256 x 256 kernel whose tile count leaves the device's last round of
+ * tiles partly idle run in stream-K form: the whole rounds as usual, and the K
+ * iterations of the remaining tiles spread evenly over all compute units, each
+ * piece of a tile leaving its partial sums in the workspace, from which a
+ * second kernel adds them in a fixed order (K ascending) and applies the
+ * epilogue.  Results stay deterministic.  This decomposition is not from the
+ * pages; it is a scheduling choice of this library.
+ *
+ * workspace       : device memory owned by the caller, 16-byte aligned, or
+ *                   NULL.  The call may use its first
+ *                   mcg_dense_workspace_bytes(...) bytes as scratch; their
+ *                   contents on entry do not matter and are unspecified after
+ *                   the call.  Calls that share a workspace must not overlap
+ *                   (same stream, or synchronised).
+ * workspace_bytes : its size.  When the workspace is NULL or smaller than the
+ *                   plan needs, the call runs exactly as gemm_dense.
+ * Errors          : those of gemm_dense; MCG_ERR_MISALIGNED for a workspace
+ *                   that is not 16-byte aligned, MCG_ERR_INVALID_SIZE for a
+ *                   negative workspace_bytes.
+ */
+int gemm_dense_ws(int dtypeA, int dtypeB, int layoutA, int layoutB,
+                  int64_t M, int64_t N, int64_t K,
+                  const void* A, int64_t lda, const void* B, int64_t ldb,
+                  const void* C, void* D, int64_t ldc, int dtypeD,
+                  double alpha, double beta, float scaleA, float scaleB,
+                  void* workspace, int64_t workspace_bytes, void* stream);
+
+/* mcg_dense_workspace_bytes -- bytes of workspace gemm_dense_ws uses for these
+ * operands (host-only, no device work): 256 KiB per piece of a remainder tile,
+ * or 0 when the problem does not take the stream-K form (another kernel, a
+ * tile count that fills the device's rounds, or too little to gain).  Reads the
+ * current device's compute-unit count (256 when there is no device). */
+int64_t mcg_dense_workspace_bytes(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
+                                  const void* A, int64_t lda, const void* B, int64_t ldb);
+
+/*
  * gemm_sparse24 -- D = alpha*(A.B) + beta*C with A given in 2:4 compressed
  * form and multiplied on the sparse matrix cores (SMFMAC).
  *

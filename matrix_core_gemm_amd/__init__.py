@@ -29,7 +29,7 @@ STATUS = {0: "MCG_SUCCESS", 1: "MCG_ERR_NULL_POINTER", 2: "MCG_ERR_INVALID_SIZE"
           9: "MCG_ERR_HIP", 10: "MCG_ERR_INVALID_VALUE"}
 
 # Every symbol include/mcg.h declares.
-EXPORTS = ("gemm_dense", "gemm_sparse24", "compress24", "compress24_host", "decompress24_host",
+EXPORTS = ("gemm_dense", "gemm_dense_ws", "mcg_dense_workspace_bytes", "gemm_sparse24", "compress24", "compress24_host", "decompress24_host",
            "mcg_status_string",
            "mcg_version", "mcg_validate_dense", "mcg_validate_sparse24", "mcg_validate_compress24",
            "mcg_dense_path", "mcg_dense_splits", "mcg_sparse24_path", "mcg_mfma_eval", "mcg_mfma_eval_k")
@@ -50,6 +50,10 @@ _lib = ctypes.CDLL(LIB_PATH)
 _i32, _i64, _dbl, _f32, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_float, ctypes.c_void_p
 _lib.gemm_dense.argtypes = [_i32, _i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
                             _vp, _vp, _i64, _i32, _dbl, _dbl, _f32, _f32, _vp]
+_lib.gemm_dense_ws.argtypes = [_i32, _i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
+                               _vp, _vp, _i64, _i32, _dbl, _dbl, _f32, _f32, _vp, _i64, _vp]
+_lib.mcg_dense_workspace_bytes.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64]
+_lib.mcg_dense_workspace_bytes.restype = _i64
 _lib.gemm_sparse24.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                                _vp, _vp, _i64, _i32, _dbl, _dbl, _vp]
 _lib.compress24.argtypes = [_i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp]
@@ -114,6 +118,26 @@ def gemm_dense(dtypeA, dtypeB, layoutA, layoutB, M, N, K, A, lda, B, ldb, C, D, 
         _dt(dtypeA), _dt(dtypeB), _lay(layoutA), _lay(layoutB), M, N, K, _ptr(A), lda, _ptr(B), ldb,
         _ptr(C), _ptr(D), ldc, _dt(dtypeD), float(alpha), float(beta), float(scaleA), float(scaleB),
         _stream(stream)))
+
+
+def gemm_dense_ws(dtypeA, dtypeB, layoutA, layoutB, M, N, K, A, lda, B, ldb, C, D, ldc, dtypeD,
+                  alpha=1.0, beta=0.0, scaleA=1.0, scaleB=1.0, workspace=None, workspace_bytes=0,
+                  stream=None) -> None:
+    """gemm_dense with a device workspace (a tensor, whose byte size is taken
+    when workspace_bytes is 0, or an address), which the stream-K form of the
+    256 x 256 kernel uses for partial sums."""
+    if isinstance(workspace, torch.Tensor) and not workspace_bytes:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("gemm_dense_ws", _lib.gemm_dense_ws(
+        _dt(dtypeA), _dt(dtypeB), _lay(layoutA), _lay(layoutB), M, N, K, _ptr(A), lda, _ptr(B), ldb,
+        _ptr(C), _ptr(D), ldc, _dt(dtypeD), float(alpha), float(beta), float(scaleA), float(scaleB),
+        _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def dense_workspace_bytes(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb) -> int:
+    """Workspace bytes gemm_dense_ws uses for these operands (0: no stream-K form)."""
+    return _lib.mcg_dense_workspace_bytes(_dt(dtypeA), _lay(layoutA), _lay(layoutB), M, N, K, _ptr(A), lda,
+                                          _ptr(B), ldb)
 
 
 def gemm_sparse24(dtypeA, dtypeB, layoutB, M, N, K, A_compressed, lda_c, A_index, ld_idx, B, ldb,

@@ -160,13 +160,16 @@ static mcg::F64Args f64_args(int64_t M, int64_t N, int64_t K, const void* A, int
   return a;
 }
 
-int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
-               const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, void* D,
-               int64_t ldc, int dtypeD, double alpha, double beta, float scaleA, float scaleB,
-               void* stream) {
+// gemm_dense and gemm_dense_ws: ws (ws_bytes) is the caller's workspace, or null.
+static int dense_impl(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
+                      const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, void* D,
+                      int64_t ldc, int dtypeD, double alpha, double beta, float scaleA, float scaleB,
+                      void* ws, int64_t ws_bytes, void* stream) {
   int st = mcg_validate_dense(dtypeA, dtypeB, layoutA, layoutB, M, N, K, A, lda, B, ldb, C, D, ldc,
                               dtypeD, alpha, beta, scaleA, scaleB);
-  if (st != MCG_SUCCESS || M == 0 || N == 0) return st;
+  if (st != MCG_SUCCESS) return st;
+  if (ws != nullptr && (ws_bytes < 0 || !aligned_to(ws, 16))) return ws_bytes < 0 ? MCG_ERR_INVALID_SIZE : MCG_ERR_MISALIGNED;
+  if (M == 0 || N == 0) return st;
   st = check_arch();
   if (st != MCG_SUCCESS) return st;
   if (dtypeA == MCG_F64) {
@@ -198,10 +201,34 @@ int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int6
   const bool aligned = dense_aligned(eb, K, A, lda, B, ldb);
   const mcg::DensePlan plan =
       mcg::plan_dense(dtypeA, layoutA, layoutB, a, aligned, can_split_k(a, C, D), current_num_cu());
+  if (plan.kernel == mcg::KERNEL_FAST && ws != nullptr) {
+    const int64_t need = mcg::plan_streamk(dtypeA, a, current_num_cu());
+    if (need > 0 && need <= ws_bytes) {
+      a.ws = ws;
+      return hip_status(mcg::launch_fast_sk(dtypeA, dtypeB, layoutA, layoutB, a, (hipStream_t)stream));
+    }
+    a.dp_tiles = a.sk_tiles = a.sk_wgs = 0;
+  }
   if (plan.kernel == mcg::KERNEL_FAST || plan.kernel == mcg::KERNEL_MID)
     return hip_status(mcg::launch_fast(dtypeA, dtypeB, layoutA, layoutB, a, (hipStream_t)stream,
                                        plan.kernel == mcg::KERNEL_MID ? 128 : 256));
   return hip_status(mcg::launch_dense(dtypeA, dtypeB, layoutA, layoutB, aligned, a, plan, (hipStream_t)stream));
+}
+
+int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
+               const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, void* D,
+               int64_t ldc, int dtypeD, double alpha, double beta, float scaleA, float scaleB,
+               void* stream) {
+  return dense_impl(dtypeA, dtypeB, layoutA, layoutB, M, N, K, A, lda, B, ldb, C, D, ldc, dtypeD, alpha, beta,
+                    scaleA, scaleB, nullptr, 0, stream);
+}
+
+int gemm_dense_ws(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
+                  const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, void* D,
+                  int64_t ldc, int dtypeD, double alpha, double beta, float scaleA, float scaleB,
+                  void* workspace, int64_t workspace_bytes, void* stream) {
+  return dense_impl(dtypeA, dtypeB, layoutA, layoutB, M, N, K, A, lda, B, ldb, C, D, ldc, dtypeD, alpha, beta,
+                    scaleA, scaleB, workspace, workspace_bytes, stream);
 }
 
 int mcg_validate_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int64_t K,
@@ -395,6 +422,17 @@ int mcg_dense_path(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, i
   if (dtypeA == MCG_F64) return mcg::KERNEL_F64;
   if (dtypeA < MCG_BF16 || dtypeA > MCG_FP8_E5M2) return 0;
   return dense_plan(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb, true).kernel;
+}
+
+int64_t mcg_dense_workspace_bytes(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
+                                  const void* A, int64_t lda, const void* B, int64_t ldb) {
+  if (dtypeA < MCG_BF16 || dtypeA > MCG_FP8_E5M2 || M <= 0 || N <= 0 || K <= 0) return 0;
+  if (dense_plan(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb, true).kernel != mcg::KERNEL_FAST) return 0;
+  mcg::DenseArgs a{};
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  return mcg::plan_streamk(dtypeA, a, current_num_cu());
 }
 
 int mcg_dense_splits(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A,

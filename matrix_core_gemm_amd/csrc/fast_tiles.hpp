@@ -16,6 +16,7 @@
 // instruction fetches the global chunk that belongs at its (fixed) LDS slot.
 #pragma once
 #include "arch_gfx950.hpp"
+#include "tile_order.hpp"
 
 namespace mcg {
 namespace fast {
@@ -261,22 +262,23 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("" ::: "memory");
 }
 
-// Workgroup -> output tile.  Workgroups are dispatched round-robin over the 8
-// XCDs; the sequence is permuted so that the workgroups of one XCD take
-// consecutive logical tiles, which are ordered in groups of GROUP tile rows
-// (column-major inside a group) so that concurrently resident workgroups share
-// A and B panels in their XCD's L2.
+// Workgroup bid of nwg whole-tile workgroups -> output tile.  Workgroups are
+// dispatched round-robin over the 8 XCDs; the sequence is permuted so that the
+// workgroups of one XCD take consecutive logical tiles, which concurrently
+// resident workgroups then share in their XCD's L2.
+template <int GROUP>
+__device__ __forceinline__ void tile_coords_of(int bid, int nwg, int tiles_m, int tiles_n, int& tm, int& tn) {
+  int pid = bid;
+  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  int m, n;
+  grouped_tile<GROUP>(pid, tiles_m, tiles_n, m, n);
+  tm = __builtin_amdgcn_readfirstlane(m);
+  tn = __builtin_amdgcn_readfirstlane(n);
+}
+
 template <int GROUP>
 __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int nwg = tiles_m * tiles_n;
-  int pid = blockIdx.x;
-  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
-  const int tiles_in_group = GROUP * tiles_n;
-  const int gid = pid / tiles_in_group;
-  const int first_m = gid * GROUP;
-  const int gsize = min(tiles_m - first_m, GROUP);
-  tm = __builtin_amdgcn_readfirstlane(first_m + (pid % tiles_in_group) % gsize);
-  tn = __builtin_amdgcn_readfirstlane((pid % tiles_in_group) / gsize);
+  tile_coords_of<GROUP>(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
 }
 
 }  // namespace fast

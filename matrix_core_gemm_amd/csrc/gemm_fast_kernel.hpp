@@ -58,9 +58,22 @@ constexpr int NSA = 2;       // LDS stages of A
 constexpr int NSB = 3;       // LDS stages of B
 constexpr int THREADS = 512;
 
+// Where an epilogue writes: D = alpha * acc + beta * C for the tile whose first
+// element is (m0, n0) of an M x N matrix with leading dimension ld (elements).
+struct EpiDst {
+  void* D;
+  const void* C;
+  int64_t ld, M, N, m0, n0;
+  float alpha, beta;
+  int alpha_i, beta_i, use_c, vec, out;
+};
+
 // TB: output tile TB x TB (256, or 128 for problems with too few 256 x 256 tiles to
-// fill the chip); each wavefront owns (TB / 2) x (TB / 4) outputs.
-template <class Op, int LA, int LB, int TB>
+// fill the chip); each wavefront owns (TB / 2) x (TB / 4) outputs.  SK: the
+// stream-K form (TB 256 only), whose workgroups each take a range of the K
+// iterations of the tiles after the first dp_tiles, which a launch of the
+// whole-tile form covers.
+template <class Op, int LA, int LB, int TB, bool SK = false>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_fast_kernel(DenseArgs p) {
   constexpr int BM = TB, BN = TB;
@@ -85,6 +98,7 @@ void gemm_fast_kernel(DenseArgs p) {
   using v4 = typename std::conditional<Op::INT_ACC, i32x4, f32x4>::type;
   using s1 = typename std::conditional<Op::INT_ACC, int, float>::type;
   static_assert(TB == 256 || TB == 128, "tile");
+  static_assert(!SK || TB == 256, "stream-K form of the 256 x 256 kernel only");
   static_assert(GA::BYTES == SB && GB::BYTES == SB, "one stage size for both operands");
   constexpr int LH = LdA::INSTR / 2;  // loads per wave, operand and half stage (one group's share)
   static_assert(LdA::INSTR == LdB::INSTR && (LH == 4 || LH == 2), "vmcnt bookkeeping");
@@ -99,8 +113,11 @@ void gemm_fast_kernel(DenseArgs p) {
   const int rbA = (q >> 1) * (TB / 2), rbB = (q & 1) * (TB / 2) + (KS ? 0 : grp * (TB / 4));
   const int g = lane >> 5;
 
-  int tm, tn;
-  tile_coords<4>(p.tiles_m, p.tiles_n, tm, tn);  // XCD-aware, grouped tile order
+  const int nk_all = (int)((p.K + KTB / EB - 1) / (KTB / EB));  // K tiles of the problem
+
+  // One piece of work: K tiles [kb, kb + nk) of output tile (tm, tn), whose
+  // epilogue writes to d.
+  auto work = [&](int tm, int tn, int kb, int nk, const EpiDst& d) {
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
   LdA la;
@@ -120,13 +137,12 @@ void gemm_fast_kernel(DenseArgs p) {
 #pragma unroll
     for (int j = 0; j < WTN; ++j) acc[i][j] = acc_t{};
 
-  const int nk = (int)((p.K + KTB / EB - 1) / (KTB / EB));
   auto stA = [&](int kt) { return smem + (KS ? kt % NA : kt & 1) * SB; };
   auto stB = [&](int kt) { return smem + NA * SB + (kt % NSB) * SB; };
   // this group's half (LH of the 2 LH load instructions per wave) of operand X of K tile kt
   const int ihalf = LH * grp;
-  auto issueA = [&](int kt) { la.issue(stA(kt), kt, ihalf, LH, q); };
-  auto issueB = [&](int kt) { lb.issue(stB(kt), kt, ihalf, LH, q); };
+  auto issueA = [&](int kt) { la.issue(stA(kt), kb + kt, ihalf, LH, q); };
+  auto issueB = [&](int kt) { lb.issue(stB(kt), kb + kt, ihalf, LH, q); };
 
   frag_t fa[S][WTM], fb[S][WTN];
   // fragments of half h (K bytes [64h, 64h + 64) of each row) of K tile kt;
@@ -320,23 +336,25 @@ void gemm_fast_kernel(DenseArgs p) {
   // epilogue: each instruction multiplied (B fragment) x (A fragment), so element
   // (i', j') of its 32 x 32 accumulator layout is D[m][n] with m = j' and n = i'
   // within the block: block (i, j), register 4 r4 + r of a lane holds
-  // D[m0 + rbA + 32 i + j'][n0 + rbB + 32 j + i' + r], (i', j') = ACC::coord(lane, 4 r4),
-  // i.e. 4 consecutive columns of one row per register group r4
+  // D[em0 + rbA + 32 i + j'][en0 + rbB + 32 j + i' + r], (i', j') = ACC::coord(lane, 4 r4),
+  // i.e. 4 consecutive columns of one row per register group r4; (em0, en0) is the
+  // tile's first element in the destination (D, or a workspace slot)
   using ACC = frag::Acc<frag::ACC_32x32>;
+  const int64_t em0 = d.m0, en0 = d.n0;
   const int acc_m = ACC::coord(lane, 0).j;  // m within a block
   auto acc_n = [&](int r4) { return ACC::coord(lane, 4 * r4).i; };  // first n of register group r4
-  const bool vec_ok = p.vec_cd;
-  const s1* C = (const s1*)p.C;
-  s1* D = (s1*)p.D;
+  const bool vec_ok = d.vec;
+  const s1* C = (const s1*)d.C;
+  s1* D = (s1*)d.D;
   if constexpr (Op::INT_ACC) {
     // wrapping alpha * acc, in place (keeps the products out of the C batches)
-    if (p.alpha_i != 1) {
+    if (d.alpha_i != 1) {
 #pragma unroll
       for (int i = 0; i < WTM; ++i)
 #pragma unroll
         for (int j = 0; j < WTN; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = (int)((uint32_t)p.alpha_i * (uint32_t)acc[i][j][r]);
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = (int)((uint32_t)d.alpha_i * (uint32_t)acc[i][j][r]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -345,13 +363,13 @@ void gemm_fast_kernel(DenseArgs p) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if constexpr (Op::INT_ACC)
-        o[r] = (int)((uint32_t)a[4 * r4 + r] + (use_c ? (uint32_t)p.beta_i * (uint32_t)c[r] : 0u));
+        o[r] = (int)((uint32_t)a[4 * r4 + r] + (use_c ? (uint32_t)d.beta_i * (uint32_t)c[r] : 0u));
       else
-        o[r] = use_c ? __builtin_fmaf(p.alpha, a[4 * r4 + r], p.beta * c[r]) : p.alpha * a[4 * r4 + r];
+        o[r] = use_c ? __builtin_fmaf(d.alpha, a[4 * r4 + r], d.beta * c[r]) : d.alpha * a[4 * r4 + r];
     }
     return o;
   };
-  if (vec_ok && m0 + BM <= p.M && n0 + BN <= p.N) {
+  if (vec_ok && em0 + BM <= d.M && en0 + BN <= d.N) {
     // Interior tile.  Each wavefront passes the 32 x 64 block of its row group i
     // (KS: the one block it stores) through LDS (8 KiB; two buffers for the 256 x 256
     // form, one for the 128 x 128 form), so that 16 lanes then read C and write D
@@ -365,16 +383,16 @@ void gemm_fast_kernel(DenseArgs p) {
     typedef __attribute__((address_space(3))) v4 lds_v4;
     lds_char* wbuf = smem + wave * (KS ? 8192 : 16384);
     const int wr = lane & 31, rr = lane >> 4, cc = lane & 15;
-    const int64_t col = n0 + rbB + 4 * cc;
-    const int out = p.out;
+    const int64_t col = en0 + rbB + 4 * cc;
+    const int out = d.out;
     auto combine4 = [&](const v4& a, const v4& c) {
       v4 o;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if constexpr (Op::INT_ACC)
-          o[r] = (int)((uint32_t)a[r] + (p.use_c ? (uint32_t)p.beta_i * (uint32_t)c[r] : 0u));
+          o[r] = (int)((uint32_t)a[r] + (d.use_c ? (uint32_t)d.beta_i * (uint32_t)c[r] : 0u));
         else
-          o[r] = p.use_c ? __builtin_fmaf(p.alpha, a[r], p.beta * c[r]) : p.alpha * a[r];
+          o[r] = d.use_c ? __builtin_fmaf(d.alpha, a[r], d.beta * c[r]) : d.alpha * a[r];
       }
       return o;
     };
@@ -383,11 +401,11 @@ void gemm_fast_kernel(DenseArgs p) {
       __builtin_amdgcn_sched_barrier(0);
       if (KS && i != grp) continue;  // the partner wave stores this row block
       lds_char* buf = wbuf + (KS ? 0 : (i & 1) * 8192);
-      const int64_t rbase = (m0 + rbA + 32 * i + rr) * p.ldc + col;  // row 4t further: + 4t ldc
+      const int64_t rbase = (em0 + rbA + 32 * i + rr) * d.ld + col;  // row 4t further: + 4t ldc
       v4 cv[8];
-      if (out == OUT_32 && p.use_c) {  // C loads first: their latency overlaps the staging
+      if (out == OUT_32 && d.use_c) {  // C loads first: their latency overlaps the staging
 #pragma unroll
-        for (int t = 0; t < 8; ++t) cv[t] = *(const v4*)(C + rbase + 4 * t * p.ldc);
+        for (int t = 0; t < 8; ++t) cv[t] = *(const v4*)(C + rbase + 4 * t * d.ld);
       }
 #pragma unroll
       for (int j = 0; j < WTN; ++j)
@@ -409,21 +427,21 @@ void gemm_fast_kernel(DenseArgs p) {
       }
       if constexpr (!Op::INT_ACC) {
         if (out != OUT_32) {
-          const uint16_t* C16 = (const uint16_t*)p.C;
-          uint16_t* D16 = (uint16_t*)p.D;
+          const uint16_t* C16 = (const uint16_t*)d.C;
+          uint16_t* D16 = (uint16_t*)d.D;
           i32x2 cw[8];
-          if (p.use_c) {
+          if (d.use_c) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) cw[t] = *(const i32x2*)(C16 + rbase + 4 * t * p.ldc);
+            for (int t = 0; t < 8; ++t) cw[t] = *(const i32x2*)(C16 + rbase + 4 * t * d.ld);
           }
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             v4 c = {};
-            if (p.use_c)
+            if (d.use_c)
               c = v4{from_out_bits(out, (uint32_t)cw[t].x & 0xffffu), from_out_bits(out, (uint32_t)cw[t].x >> 16),
                      from_out_bits(out, (uint32_t)cw[t].y & 0xffffu), from_out_bits(out, (uint32_t)cw[t].y >> 16)};
             const v4 o = combine4(a[t], c);
-            *(i32x2*)(D16 + rbase + 4 * t * p.ldc) =
+            *(i32x2*)(D16 + rbase + 4 * t * d.ld) =
                 i32x2{(int)(to_out_bits(out, o[0]) | (to_out_bits(out, o[1]) << 16)),
                       (int)(to_out_bits(out, o[2]) | (to_out_bits(out, o[3]) << 16))};
           }
@@ -431,17 +449,17 @@ void gemm_fast_kernel(DenseArgs p) {
         }
       }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) *(v4*)(D + rbase + 4 * t * p.ldc) = combine4(a[t], p.use_c ? cv[t] : v4{});
+      for (int t = 0; t < 8; ++t) *(v4*)(D + rbase + 4 * t * d.ld) = combine4(a[t], d.use_c ? cv[t] : v4{});
     }
     return;
   }
   if constexpr (!Op::INT_ACC) {
-    if (p.out != OUT_32) {
+    if (d.out != OUT_32) {
       // bfloat16 / binary16 C and D: 4 consecutive elements = 8 bytes per lane
       // and row segment; the fp32 result is rounded once to the output format
-      const int out = p.out;
-      const uint16_t* C16 = (const uint16_t*)p.C;
-      uint16_t* D16 = (uint16_t*)p.D;
+      const int out = d.out;
+      const uint16_t* C16 = (const uint16_t*)d.C;
+      uint16_t* D16 = (uint16_t*)d.D;
       auto unpack = [&](const i32x2 w) {
         return v4{from_out_bits(out, (uint32_t)w.x & 0xffffu), from_out_bits(out, (uint32_t)w.x >> 16),
                   from_out_bits(out, (uint32_t)w.y & 0xffffu), from_out_bits(out, (uint32_t)w.y >> 16)};
@@ -454,29 +472,29 @@ void gemm_fast_kernel(DenseArgs p) {
       for (int i = 0; i < WTM; ++i) {
         __builtin_amdgcn_sched_barrier(0);
         if (KS && i != grp) continue;  // the partner wave stores this row block
-        const int64_t m = m0 + rbA + 32 * i + acc_m;
-        if (m >= p.M) continue;
+        const int64_t m = em0 + rbA + 32 * i + acc_m;
+        if (m >= d.M) continue;
 #pragma unroll
         for (int j = 0; j < WTN; ++j)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const int64_t n = n0 + rbB + 32 * j + acc_n(r4);
-            if (n >= p.N) continue;
-            const int64_t off = m * p.ldc + n;
-            const bool full = vec_ok && n + 4 <= p.N;
+            const int64_t n = en0 + rbB + 32 * j + acc_n(r4);
+            if (n >= d.N) continue;
+            const int64_t off = m * d.ld + n;
+            const bool full = vec_ok && n + 4 <= d.N;
             v4 c = {};
-            if (p.use_c) {
+            if (d.use_c) {
               if (full) c = unpack(*(const i32x2*)(C16 + off));
               else
                 for (int r = 0; r < 4; ++r)
-                  if (n + r < p.N) c[r] = from_out_bits(out, C16[off + r]);
+                  if (n + r < d.N) c[r] = from_out_bits(out, C16[off + r]);
             }
-            const v4 o = combine(acc[i][j], r4, c, p.use_c);
+            const v4 o = combine(acc[i][j], r4, c, d.use_c);
             if (full) {
               *(i32x2*)(D16 + off) = pack(o);
             } else {
               for (int r = 0; r < 4; ++r)
-                if (n + r < p.N) D16[off + r] = (uint16_t)to_out_bits(out, o[r]);
+                if (n + r < d.N) D16[off + r] = (uint16_t)to_out_bits(out, o[r]);
             }
           }
       }
@@ -488,70 +506,207 @@ void gemm_fast_kernel(DenseArgs p) {
 #pragma unroll
     for (int i = 0; i < WTM; ++i) {
       if (KS && i != grp) continue;  // the partner wave stores this row block
-      const int64_t m = m0 + rbA + 32 * i + acc_m;
-      if (m >= p.M) continue;
+      const int64_t m = em0 + rbA + 32 * i + acc_m;
+      if (m >= d.M) continue;
 #pragma unroll
       for (int j = 0; j < WTN; ++j)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int64_t n = n0 + rbB + 32 * j + acc_n(r4);
-          if (n >= p.N) continue;
-          const bool full = vec_ok && n + 4 <= p.N;
+          const int64_t n = en0 + rbB + 32 * j + acc_n(r4);
+          if (n >= d.N) continue;
+          const bool full = vec_ok && n + 4 <= d.N;
           v4 c = {};
-          if (p.use_c) {
-            if (full) c = *(const v4*)(C + m * p.ldc + n);
+          if (d.use_c) {
+            if (full) c = *(const v4*)(C + m * d.ld + n);
             else
               for (int r = 0; r < 4; ++r)
-                if (n + r < p.N) c[r] = C[m * p.ldc + n + r];
+                if (n + r < d.N) c[r] = C[m * d.ld + n + r];
           }
-          const v4 o = combine(acc[i][j], r4, c, p.use_c);
+          const v4 o = combine(acc[i][j], r4, c, d.use_c);
           if (full) {
-            *(v4*)(D + m * p.ldc + n) = o;
+            *(v4*)(D + m * d.ld + n) = o;
           } else {
             for (int r = 0; r < 4; ++r)
-              if (n + r < p.N) D[m * p.ldc + n + r] = o[r];
+              if (n + r < d.N) D[m * d.ld + n + r] = o[r];
           }
         }
     }
   }
+  };  // work
+
+  if constexpr (!SK) {
+    // XCD-aware, grouped tile order over all tiles, or over the first dp_tiles
+    // tiles when the rest are left to the stream-K form
+    int tm, tn;
+    tile_coords_of<4>(blockIdx.x, p.dp_tiles > 0 ? p.dp_tiles : p.tiles_m * p.tiles_n, p.tiles_m, p.tiles_n, tm, tn);
+    work(tm, tn, 0, nk_all,
+         EpiDst{p.D, p.C, p.ldc, p.M, p.N, (int64_t)tm * BM, (int64_t)tn * BN, p.alpha, p.beta, p.alpha_i,
+                p.beta_i, p.use_c, p.vec_cd, p.out});
+  } else {
+    // Workgroup w takes K iterations [w L, (w + 1) L) of the tiles after the
+    // first dp_tiles (which a whole-tile launch covers), numbered tile by tile:
+    // one or two pieces.  A piece that is a whole tile is stored to D; any other
+    // piece stores its raw sums (alpha 1, no C) to its own workspace slot.
+    const int64_t w = blockIdx.x;
+    const int64_t L = p.sk_iters;
+    int64_t it = w * L;
+    const int64_t end = min(it + L, (int64_t)p.sk_tiles * nk_all);
+    int64_t piece = sk_first_piece(w, L, nk_all, p.sk_period);
+    for (int pc = 0; it < end; ++pc) {
+      const int64_t x = it / nk_all;
+      const int kbeg = (int)(it - x * nk_all);
+      const int kcnt = (int)min((int64_t)(nk_all - kbeg), end - it);
+      int tm, tn;
+      {
+        int m, n;
+        grouped_tile<4>(p.dp_tiles + (int)x, p.tiles_m, p.tiles_n, m, n);
+        tm = __builtin_amdgcn_readfirstlane(m);
+        tn = __builtin_amdgcn_readfirstlane(n);
+      }
+      if (pc > 0) barrier_lds();  // the previous piece's epilogue is done with the LDS
+      const bool whole = kbeg == 0 && kcnt == nk_all;
+      const EpiDst d = whole ? EpiDst{p.D, p.C, p.ldc, p.M, p.N, (int64_t)tm * BM, (int64_t)tn * BN, p.alpha,
+                                      p.beta, p.alpha_i, p.beta_i, p.use_c, p.vec_cd, p.out}
+                             : EpiDst{(char*)p.ws + piece * (int64_t)(TB * TB * 4), nullptr, TB, TB, TB, 0, 0,
+                                      1.0f, 0.0f, 1, 0, 0, 1, OUT_32};
+      work(tm, tn, kbeg, kcnt, d);
+      it += kcnt;
+      ++piece;
+    }
+  }
 }
 
-template <class Op, int LA, int LB, int TB>
+// Stream-K fixup: for each remainder tile cut into more than one piece, add the
+// pieces' partial sums in piece order (ascending K) and apply the epilogue
+// D = alpha * sum + beta * C of the whole-tile path (binary32 fma, or wrapping
+// int32), rounding once to a 16-bit D.  Grid (sk_tiles, TB * TB / 1024), 256
+// threads: one 16-byte group of 4 columns per thread, consecutive threads along a
+// row; up to FIX_BATCH pieces are loaded before they are added, so that the
+// loads overlap.
+constexpr int FIX_BATCH = 8;
+template <bool INT, int TB>
+__global__ __launch_bounds__(256) void streamk_fixup_kernel(DenseArgs p, int64_t nk) {
+  const int64_t x = blockIdx.x, L = p.sk_iters;
+  const int64_t w0 = x * nk / L, w1 = ((x + 1) * nk - 1) / L;  // workgroups with a piece of tile x
+  if (w0 == w1) return;  // one piece: the whole tile, stored by its workgroup
+  const int64_t first = sk_first_piece(w0, L, nk, p.sk_period) + (x - w0 * L / nk);
+  const int npieces = (int)(w1 - w0 + 1);
+  int tm, tn;
+  grouped_tile<4>(p.dp_tiles + (int)x, p.tiles_m, p.tiles_n, tm, tn);
+  const int idx = blockIdx.y * 256 + threadIdx.x;  // 16-byte group of the row-major tile
+  const int r = idx / (TB / 4), c = 4 * (idx % (TB / 4));
+  const int64_t m = (int64_t)tm * TB + r, n = (int64_t)tn * TB + c;
+  if (m >= p.M || n >= p.N) return;
+  using e1 = typename std::conditional<INT, int, float>::type;
+  using v4 = typename std::conditional<INT, i32x4, f32x4>::type;
+  const char* src = (const char*)p.ws + first * (int64_t)(TB * TB * 4) + (int64_t)idx * 16;
+  auto slot = [&](int q) { return *(const v4*)(src + (int64_t)q * (TB * TB * 4)); };
+  v4 acc = slot(0);
+  for (int q0 = 1; q0 < npieces; q0 += FIX_BATCH) {
+    v4 t[FIX_BATCH];
+#pragma unroll
+    for (int u = 0; u < FIX_BATCH; ++u)
+      if (q0 + u < npieces) t[u] = slot(q0 + u);
+#pragma unroll
+    for (int u = 0; u < FIX_BATCH; ++u)
+      if (q0 + u < npieces) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (INT) acc[e] = (int)((uint32_t)acc[e] + (uint32_t)t[u][e]);
+          else acc[e] += t[u][e];
+        }
+      }
+  }
+  const int64_t doff = m * p.ldc + n;
+  const bool full = p.vec_cd && n + 4 <= p.N;
+  e1 o[4];
+  if constexpr (INT) {
+    const int* C = (const int*)p.C;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t cv = p.use_c && n + e < p.N ? (uint32_t)C[doff + e] : 0u;
+      o[e] = (int)((uint32_t)p.alpha_i * (uint32_t)acc[e] + (uint32_t)p.beta_i * cv);
+    }
+    if (full) {
+      *(i32x4*)((int*)p.D + doff) = i32x4{o[0], o[1], o[2], o[3]};
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (n + e < p.N) ((int*)p.D)[doff + e] = o[e];
+    }
+  } else if (p.out == OUT_32) {
+    const float* C = (const float*)p.C;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = p.use_c && n + e < p.N ? __builtin_fmaf(p.alpha, acc[e], p.beta * C[doff + e]) : p.alpha * acc[e];
+    if (full) {
+      *(f32x4*)((float*)p.D + doff) = f32x4{o[0], o[1], o[2], o[3]};
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (n + e < p.N) ((float*)p.D)[doff + e] = o[e];
+    }
+  } else {
+    const uint16_t* C16 = (const uint16_t*)p.C;
+    uint16_t* D16 = (uint16_t*)p.D;
+    for (int e = 0; e < 4; ++e) {
+      if (n + e >= p.N) continue;
+      const float v = p.use_c ? __builtin_fmaf(p.alpha, acc[e], p.beta * from_out_bits(p.out, C16[doff + e]))
+                              : p.alpha * acc[e];
+      D16[doff + e] = (uint16_t)to_out_bits(p.out, v);
+    }
+  }
+}
+
+template <class Op, int LA, int LB, int TB, bool SK = false>
 hipError_t launch_one(const DenseArgs& a0, hipStream_t s) {
   DenseArgs a = a0;
   a.tiles_m = (int)((a.M + TB - 1) / TB);
   a.tiles_n = (int)((a.N + TB - 1) / TB);
-  const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
-  if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_fast_kernel<Op, LA, LB, TB>), dim3((unsigned)blocks), dim3(THREADS), 0, s, a);
-  return hipGetLastError();
+  const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+  if (tiles <= 0) return hipSuccess;
+  hipError_t e = hipSuccess;
+  if (!SK || a.dp_tiles > 0) {  // whole tiles: every tile, or the first dp_tiles
+    hipLaunchKernelGGL((gemm_fast_kernel<Op, LA, LB, TB, false>), dim3((unsigned)(SK ? a.dp_tiles : tiles)),
+                       dim3(THREADS), 0, s, a);
+    e = hipGetLastError();
+  }
+  if constexpr (SK) {
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemm_fast_kernel<Op, LA, LB, TB, true>), dim3((unsigned)a.sk_wgs), dim3(THREADS), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nk = (a.K + KTB / Op::EB - 1) / (KTB / Op::EB);
+    hipLaunchKernelGGL((streamk_fixup_kernel<Op::INT_ACC, TB>), dim3((unsigned)a.sk_tiles, TB * TB / 1024), dim3(256), 0, s,
+                       a, nk);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
-template <class Op, int TB>
+template <class Op, int TB, bool SK = false>
 hipError_t launch_layouts_tb(int la, int lb, const DenseArgs& a, hipStream_t s) {
-  if (la == 0 && lb == 0) return launch_one<Op, 0, 0, TB>(a, s);
-  if (la == 0 && lb == 1) return launch_one<Op, 0, 1, TB>(a, s);
-  if (la == 1 && lb == 0) return launch_one<Op, 1, 0, TB>(a, s);
-  return launch_one<Op, 1, 1, TB>(a, s);
+  if (la == 0 && lb == 0) return launch_one<Op, 0, 0, TB, SK>(a, s);
+  if (la == 0 && lb == 1) return launch_one<Op, 0, 1, TB, SK>(a, s);
+  if (la == 1 && lb == 0) return launch_one<Op, 1, 0, TB, SK>(a, s);
+  return launch_one<Op, 1, 1, TB, SK>(a, s);
 }
 
-// Operation-type dispatch for tile size TB (one translation unit per TB).
-template <int TB>
+// Operation-type dispatch for tile size TB (one translation unit per TB and form).
+template <int TB, bool SK = false>
 hipError_t launch_fast_tb(int dtA, int dtB, int la, int lb, const DenseArgs& a, hipStream_t s) {
-  if (dtA == DT_BF16) return launch_layouts_tb<BF16, TB>(la, lb, a, s);
-  if (dtA == DT_F16) return launch_layouts_tb<F16, TB>(la, lb, a, s);
-  if (dtA == DT_I8) return launch_layouts_tb<I8, TB>(la, lb, a, s);
+  if (dtA == DT_BF16) return launch_layouts_tb<BF16, TB, SK>(la, lb, a, s);
+  if (dtA == DT_F16) return launch_layouts_tb<F16, TB, SK>(la, lb, a, s);
+  if (dtA == DT_I8) return launch_layouts_tb<I8, TB, SK>(la, lb, a, s);
   const int fa = f8fmt(dtA), fb = f8fmt(dtB);
   if (a.K >= FP8_NATIVE_MIN_K) {
-    if (fb == 0 && fa == 0) return launch_layouts_tb<F8<0, 0>, TB>(la, lb, a, s);
-    if (fb == 1 && fa == 0) return launch_layouts_tb<F8<1, 0>, TB>(la, lb, a, s);
-    if (fb == 0 && fa == 1) return launch_layouts_tb<F8<0, 1>, TB>(la, lb, a, s);
-    return launch_layouts_tb<F8<1, 1>, TB>(la, lb, a, s);
+    if (fb == 0 && fa == 0) return launch_layouts_tb<F8<0, 0>, TB, SK>(la, lb, a, s);
+    if (fb == 1 && fa == 0) return launch_layouts_tb<F8<1, 0>, TB, SK>(la, lb, a, s);
+    if (fb == 0 && fa == 1) return launch_layouts_tb<F8<0, 1>, TB, SK>(la, lb, a, s);
+    return launch_layouts_tb<F8<1, 1>, TB, SK>(la, lb, a, s);
   }
-  if (fa == 0 && fb == 0) return launch_layouts_tb<F8W<0, 0>, TB>(la, lb, a, s);
-  if (fa == 0 && fb == 1) return launch_layouts_tb<F8W<0, 1>, TB>(la, lb, a, s);
-  if (fa == 1 && fb == 0) return launch_layouts_tb<F8W<1, 0>, TB>(la, lb, a, s);
-  return launch_layouts_tb<F8W<1, 1>, TB>(la, lb, a, s);
+  if (fa == 0 && fb == 0) return launch_layouts_tb<F8W<0, 0>, TB, SK>(la, lb, a, s);
+  if (fa == 0 && fb == 1) return launch_layouts_tb<F8W<0, 1>, TB, SK>(la, lb, a, s);
+  if (fa == 1 && fb == 0) return launch_layouts_tb<F8W<1, 0>, TB, SK>(la, lb, a, s);
+  return launch_layouts_tb<F8W<1, 1>, TB, SK>(la, lb, a, s);
 }
 
 }  // namespace fast

@@ -23,6 +23,16 @@ struct DenseArgs {
   int kt_per_split;       // K tiles per range
   int stream_bw;          // streaming kernel: rows of the wide operand per workgroup
   int tiles_m, tiles_n;   // filled by the launcher
+  // stream-K form of the 256 x 256 kernel (sk_tiles > 0): the first dp_tiles
+  // tiles of the grouped tile order are whole-tile workgroups; the K iterations
+  // of the last sk_tiles tiles are cut into consecutive ranges of sk_iters over
+  // sk_wgs workgroups.  Pieces of a tile that are not the whole tile leave their
+  // partial sums in ws (one 256 x 256 binary32 / int32 slot per piece), which a
+  // second kernel adds up in piece order before the epilogue.  sk_period: the
+  // number of ranges after which a range boundary meets a tile boundary again.
+  int dp_tiles, sk_tiles, sk_wgs;
+  int64_t sk_iters, sk_period;
+  void* ws;
 };
 
 // Kernel chosen for a dense problem (also reported by mcg_dense_path).
@@ -126,6 +136,11 @@ hipError_t launch_stream(int dtA, int dtB, int layoutA, int layoutB, const Dense
 bool fast_path_ok(int dtA, int layoutA, int layoutB, const DenseArgs& a, bool aligned, int tile = 256);
 hipError_t launch_fast(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s, int tile = 256);
 hipError_t launch_fast_mid(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
+// Stream-K plan for a problem on the 256 x 256 kernel: fills the sk_* and dp_tiles
+// fields of a and returns the workspace bytes it needs, or 0 (and sk_tiles = 0)
+// when the plan would not be faster than whole tiles.
+int64_t plan_streamk(int dtA, DenseArgs& a, int num_cu);
+hipError_t launch_fast_sk(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
 hipError_t launch_sparse(int dtA, int dtB, int layoutB, bool aligned, const SparseArgs& a, hipStream_t s);
 bool sparse_fast_ok(int dtA, int layoutB, const SparseArgs& a);
 hipError_t launch_sparse_fast(int dtA, int dtB, int layoutB, const SparseArgs& a, hipStream_t s);

@@ -1,0 +1,158 @@
+"""GPU parity of the stream-K form of the 256 x 256 kernel (gemm_dense_ws)
+against the CPU oracle.
+
+Shapes whose last round of 256 x 256 tiles leaves most compute units idle take
+the stream-K form when a workspace is given: the K iterations of the remaining
+tiles are split over all CUs and their partial sums added by a second kernel.
+Every output of those tiles is compared with the oracle (float: the acceptance
+bound; int8: bit for bit), together with one whole-tile workgroup's tile and
+sampled outputs elsewhere.  The cases cover ranges that stay inside one tile
+and ranges that cross tile boundaries, the MN-contiguous storage orders, a
+bfloat16 D, D aliasing C, int8 with wrapping alpha/beta, native fp8, repeated
+calls (deterministic: the pieces are added in a fixed order) and a workspace too
+small for the plan (the call runs as gemm_dense, bit for bit).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import dev, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+SLOT = 256 * 256 * 4
+
+
+def grouped_tile(pid, tiles_m, tiles_n):
+    """The kernels' tile order: groups of four tile rows, column-major inside."""
+    g, r = divmod(pid, 4 * tiles_n)
+    gsize = min(4, tiles_m - 4 * g)
+    return 4 * g + r % gsize, r // gsize
+
+
+def remainder_tiles(M, N, num_cu):
+    tm, tn = -(-M // 256), -(-N // 256)
+    T = tm * tn
+    R = T % num_cu
+    return [grouped_tile(p, tm, tn) for p in range(T - R, T)], grouped_tile(0, tm, tn)
+
+
+def tile_coords(tiles, M, N):
+    rows, cols = [], []
+    for tm, tn in tiles:
+        r = np.arange(tm * 256, min(M, tm * 256 + 256))
+        c = np.arange(tn * 256, min(N, tn * 256 + 256))
+        rr, cc = np.meshgrid(r, c, indexing="ij")
+        rows.append(rr.ravel())
+        cols.append(cc.ravel())
+    return np.concatenate(rows), np.concatenate(cols)
+
+
+def num_cu():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def workspace(nbytes):
+    return torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device="cuda").fill_(float("nan"))
+
+
+CASES = [  # dtA, dtB, layA, layB, M, N, K, out, alpha, beta, D aliases C
+    ("bf16", "bf16", "k_contig", "k_contig", 4096, 4352, 4096, "f32", 1.5, 0.5, False),
+    ("bf16", "bf16", "mn_contig", "mn_contig", 4096, 4864, 4096, "f32", -0.75, 1.0, True),
+    ("f16", "f16", "k_contig", "mn_contig", 4096, 4864, 4096, "bf16", 1.0, -1.25, False),
+    ("i8", "i8", "k_contig", "k_contig", 4096, 4352, 8192, "i32", 3, -2, False),
+    ("e4m3", "e5m2", "k_contig", "k_contig", 4096, 4352, 8192, "f32", 1.0, 0.0, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["bf16_in_tile", "bf16_mn_cross_alias", "f16_bf16out_cross",
+                                             "i8_wrap", "fp8_native"])
+def test_streamk_against_oracle(case):
+    mcg = need_gpu()
+    dtA, dtB, layA, layB, M, N, K, out, alpha, beta, alias = case
+    say(f"stream-K {dtA}x{dtB} {layA}/{layB} {M}x{N}x{K} -> {out} alias={alias}")
+    fp8 = dtA in ("e4m3", "e5m2")
+    dist = "int8" if dtA == "i8" else "normal"
+    A = W.operand("A", dtA, M, K, dist, layA, seed=41, fp8_scaled=fp8)
+    B = W.operand("B", dtB, K, N, dist, layB, seed=42, fp8_scaled=fp8)
+    dA, dB = dev(A.codes), dev(B.codes)
+    assert mcg.dense_path(dtA, layA, layB, M, N, K, dA, A.ld, dB, B.ld) == 1
+    need = mcg.dense_workspace_bytes(dtA, layA, layB, M, N, K, dA, A.ld, dB, B.ld)
+    assert need > 0 and need % SLOT == 0
+    ldc = N
+    C = None
+    if out == "i32":
+        C = W.c_matrix(M, N, "int20", seed=43, ldc=ldc)
+        D = torch.full((M, ldc), -0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    elif out == "f32":
+        C = W.c_matrix(M, N, "normal", seed=43, ldc=ldc) if beta != 0 else None
+        D = torch.full((M, ldc), float("nan"), dtype=torch.float32, device="cuda")
+    else:
+        c16 = W.draw("normal", (M, ldc), 43).to(torch.float32).to(torch.bfloat16)
+        C = c16.view(torch.int16).numpy().view(np.uint16)
+        D = torch.full((M, ldc), 0x7FC0, dtype=torch.int32).to(torch.int16).to("cuda")
+    dC = None if C is None else dev(C.view(np.int16) if out == "bf16" else C)
+    if alias:
+        D = dC
+    ws = workspace(need)
+    mcg.gemm_dense_ws(dtA, dtB, layA, layB, M, N, K, dA, A.ld, dB, B.ld, dC, D, ldc, out, alpha, beta,
+                      A.scale, B.scale, workspace=ws)
+    torch.cuda.synchronize()
+    d = D.cpu().numpy()
+    # every output of the remainder tiles, one whole tile, and sampled others
+    sk, first = remainder_tiles(M, N, num_cu())
+    r1, c1 = tile_coords(sk + [first], M, N)
+    r2, c2 = W.sample_coords(M, N, n_random=2048, full_rows=(M - 1,), full_cols=(N - 1,))
+    rows, cols = np.concatenate([r1, r2]), np.concatenate([c1, c2])
+    say(f"  {len(sk)} stream-K tiles, {need // SLOT} pieces, {len(rows)} outputs compared")
+    if out == "i32":
+        ref = oracle.gemm_i8(layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, ldc, alpha, beta,
+                             rows=rows, cols=cols)
+        r = oracle.check_exact(d[rows, cols], ref)
+    else:
+        ref, s = oracle.gemm_float(dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, ldc,
+                                   alpha, beta, A.scale, B.scale, rows=rows, cols=cols,
+                                   out="bf16" if out == "bf16" else "f32")
+        if out == "bf16":
+            got = (d.view(np.uint16).astype(np.uint32) << 16).view(np.float32)[rows, cols]
+            cc = None if C is None else (C.astype(np.uint32) << 16).view(np.float32)[rows, cols]
+        else:
+            got = d[rows, cols]
+            cc = None if C is None else C[rows, cols]
+        r = oracle.check_float(got, ref, s, K, alpha, A.scale, B.scale, beta, cc,
+                               out="bf16" if out == "bf16" else "f32")
+    say("  ", {k: v for k, v in r.items() if k != "worst"})
+    assert r["ok"], r
+
+
+def test_streamk_deterministic_and_small_workspace_falls_back():
+    mcg = need_gpu()
+    M, N, K = 4096, 4864, 4096
+    A = W.operand("A", "bf16", M, K, "normal", "k_contig", seed=51)
+    B = W.operand("B", "bf16", K, N, "normal", "k_contig", seed=52)
+    dA, dB = dev(A.codes), dev(B.codes)
+    need = mcg.dense_workspace_bytes("bf16", "k_contig", "k_contig", M, N, K, dA, K, dB, K)
+    assert need > 0
+    outs = []
+    for ws_bytes in (need, need, need - 16):
+        ws = workspace(need)
+        D = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        mcg.gemm_dense_ws("bf16", "bf16", "k_contig", "k_contig", M, N, K, dA, K, dB, K, None, D, N, "f32",
+                          workspace=ws, workspace_bytes=ws_bytes)
+        torch.cuda.synchronize()
+        outs.append(D.cpu().numpy())
+    D = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    mcg.gemm_dense("bf16", "bf16", "k_contig", "k_contig", M, N, K, dA, K, dB, K, None, D, N, "f32")
+    torch.cuda.synchronize()
+    plain = D.cpu().numpy()
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32)), "stream-K not deterministic"
+    assert np.array_equal(outs[2].view(np.uint32), plain.view(np.uint32)), "small workspace must run gemm_dense"
+    # the stream-K tiles differ from the whole-tile order only within the bound
+    sk, _ = remainder_tiles(M, N, num_cu())
+    rows, cols = tile_coords(sk[:4], M, N)
+    ref, s = oracle.gemm_float("bf16", "bf16", "k_contig", "k_contig", M, N, K, A.codes, K, B.codes, K,
+                               rows=rows, cols=cols)
+    assert oracle.check_float(outs[0][rows, cols], ref, s, K)["ok"]
+    assert oracle.check_float(plain[rows, cols], ref, s, K)["ok"]
