@@ -77,7 +77,8 @@ typedef enum {
     MCG_ERR_INVALID_INDEX = 7,     /* a 2:4 index code with p0 >= p1 (decompress24_host) */
     MCG_ERR_UNSUPPORTED_ARCH = 8,  /* current device is not gfx950                   */
     MCG_ERR_HIP = 9,               /* a HIP runtime call failed                      */
-    MCG_ERR_INVALID_VALUE = 10     /* alpha/beta/scale not usable for this dtype     */
+    MCG_ERR_INVALID_VALUE = 10,    /* alpha/beta/scale not usable for this dtype     */
+    MCG_ERR_SCRATCH_LIMIT = 11     /* gemm_dense_noalloc: plan needs more scratch    */
 } mcg_status;
 
 /*
@@ -180,6 +181,28 @@ int gemm_dense_ws(int dtypeA, int dtypeB, int layoutA, int layoutB,
                   const void* C, void* D, int64_t ldc, int dtypeD,
                   double alpha, double beta, float scaleA, float scaleB,
                   void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * gemm_dense_noalloc -- gemm_dense_ws for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the stream-K slots come from a static device array inside
+ * the library, mcg_dense_noalloc_scratch_bytes() (64 MiB) per GPU, held until
+ * the process ends.  The call allocates nothing and frees nothing.
+ *
+ * Arguments, results and errors are those of gemm_dense_ws with a workspace
+ * of that size, except that a problem whose stream-K plan needs more than the
+ * static array (mcg_dense_workspace_bytes > mcg_dense_noalloc_scratch_bytes)
+ * returns MCG_ERR_SCRATCH_LIMIT before anything is launched or written;
+ * problems without a stream-K plan run as gemm_dense.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams, other
+ * host threads) race and must be ordered by the caller.
+ */
+int gemm_dense_noalloc(int dtypeA, int dtypeB, int layoutA, int layoutB,
+                       int64_t M, int64_t N, int64_t K,
+                       const void* A, int64_t lda, const void* B, int64_t ldb,
+                       const void* C, void* D, int64_t ldc, int dtypeD,
+                       double alpha, double beta, float scaleA, float scaleB, void* stream);
+int64_t mcg_dense_noalloc_scratch_bytes(void);
 
 /* mcg_dense_workspace_bytes -- bytes of workspace gemm_dense_ws uses for these
  * operands (host-only, no device work): 256 KiB per piece of a remainder tile,

@@ -26,10 +26,11 @@ LAYOUTS = {"k_contig": 0, "mn_contig": 1}
 STATUS = {0: "MCG_SUCCESS", 1: "MCG_ERR_NULL_POINTER", 2: "MCG_ERR_INVALID_SIZE",
           3: "MCG_ERR_INVALID_LD", 4: "MCG_ERR_UNSUPPORTED_DTYPE", 5: "MCG_ERR_MISALIGNED",
           6: "MCG_ERR_NOT_2_4_SPARSE", 7: "MCG_ERR_INVALID_INDEX", 8: "MCG_ERR_UNSUPPORTED_ARCH",
-          9: "MCG_ERR_HIP", 10: "MCG_ERR_INVALID_VALUE"}
+          9: "MCG_ERR_HIP", 10: "MCG_ERR_INVALID_VALUE", 11: "MCG_ERR_SCRATCH_LIMIT"}
 
 # Every symbol include/mcg.h declares.
-EXPORTS = ("gemm_dense", "gemm_dense_ws", "mcg_dense_workspace_bytes", "gemm_sparse24", "compress24", "compress24_host", "decompress24_host",
+EXPORTS = ("gemm_dense", "gemm_dense_ws", "gemm_dense_noalloc", "mcg_dense_noalloc_scratch_bytes",
+           "mcg_dense_workspace_bytes", "gemm_sparse24", "compress24", "compress24_host", "decompress24_host",
            "mcg_status_string",
            "mcg_version", "mcg_validate_dense", "mcg_validate_sparse24", "mcg_validate_compress24",
            "mcg_dense_path", "mcg_dense_splits", "mcg_sparse24_path", "mcg_mfma_eval", "mcg_mfma_eval_k")
@@ -52,6 +53,9 @@ _lib.gemm_dense.argtypes = [_i32, _i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64,
                             _vp, _vp, _i64, _i32, _dbl, _dbl, _f32, _f32, _vp]
 _lib.gemm_dense_ws.argtypes = [_i32, _i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
                                _vp, _vp, _i64, _i32, _dbl, _dbl, _f32, _f32, _vp, _i64, _vp]
+_lib.gemm_dense_noalloc.argtypes = _lib.gemm_dense.argtypes
+_lib.mcg_dense_noalloc_scratch_bytes.argtypes = []
+_lib.mcg_dense_noalloc_scratch_bytes.restype = _i64
 _lib.mcg_dense_workspace_bytes.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64]
 _lib.mcg_dense_workspace_bytes.restype = _i64
 _lib.gemm_sparse24.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
@@ -132,6 +136,17 @@ def gemm_dense_ws(dtypeA, dtypeB, layoutA, layoutB, M, N, K, A, lda, B, ldb, C, 
         _dt(dtypeA), _dt(dtypeB), _lay(layoutA), _lay(layoutB), M, N, K, _ptr(A), lda, _ptr(B), ldb,
         _ptr(C), _ptr(D), ldc, _dt(dtypeD), float(alpha), float(beta), float(scaleA), float(scaleB),
         _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def gemm_dense_noalloc(dtypeA, dtypeB, layoutA, layoutB, M, N, K, A, lda, B, ldb, C, D, ldc, dtypeD,
+                       alpha=1.0, beta=0.0, scaleA=1.0, scaleB=1.0, stream=None) -> None:
+    """gemm_dense taking stream-K scratch from the library's static device array
+    (no allocation); raises MCGError with MCG_ERR_SCRATCH_LIMIT (11) when the
+    plan needs more than mcg_dense_noalloc_scratch_bytes()."""
+    _check("gemm_dense_noalloc", _lib.gemm_dense_noalloc(
+        _dt(dtypeA), _dt(dtypeB), _lay(layoutA), _lay(layoutB), M, N, K, _ptr(A), lda, _ptr(B), ldb,
+        _ptr(C), _ptr(D), ldc, _dt(dtypeD), float(alpha), float(beta), float(scaleA), float(scaleB),
+        _stream(stream)))
 
 
 def dense_workspace_bytes(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb) -> int:

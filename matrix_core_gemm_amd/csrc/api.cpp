@@ -160,11 +160,13 @@ static mcg::F64Args f64_args(int64_t M, int64_t N, int64_t K, const void* A, int
   return a;
 }
 
-// gemm_dense and gemm_dense_ws: ws (ws_bytes) is the caller's workspace, or null.
+// gemm_dense, gemm_dense_ws and gemm_dense_noalloc: ws (ws_bytes) is the
+// caller's workspace, or null; use_static: take the stream-K slots from the
+// library's static scratch, rejecting plans that need more than it holds.
 static int dense_impl(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
                       const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, void* D,
                       int64_t ldc, int dtypeD, double alpha, double beta, float scaleA, float scaleB,
-                      void* ws, int64_t ws_bytes, void* stream) {
+                      void* ws, int64_t ws_bytes, void* stream, bool use_static = false) {
   int st = mcg_validate_dense(dtypeA, dtypeB, layoutA, layoutB, M, N, K, A, lda, B, ldb, C, D, ldc,
                               dtypeD, alpha, beta, scaleA, scaleB);
   if (st != MCG_SUCCESS) return st;
@@ -201,6 +203,17 @@ static int dense_impl(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t 
   const bool aligned = dense_aligned(eb, K, A, lda, B, ldb);
   const mcg::DensePlan plan =
       mcg::plan_dense(dtypeA, layoutA, layoutB, a, aligned, can_split_k(a, C, D), current_num_cu());
+  if (plan.kernel == mcg::KERNEL_FAST && use_static) {
+    const int64_t need = mcg::plan_streamk(dtypeA, a, current_num_cu());
+    if (need > mcg::STATIC_SCRATCH_BYTES) return MCG_ERR_SCRATCH_LIMIT;
+    if (need > 0) {
+      void* p = nullptr;
+      const hipError_t e = mcg::static_scratch(&p);
+      if (e != hipSuccess) return hip_status(e);
+      a.ws = p;
+      return hip_status(mcg::launch_fast_sk(dtypeA, dtypeB, layoutA, layoutB, a, (hipStream_t)stream));
+    }
+  }
   if (plan.kernel == mcg::KERNEL_FAST && ws != nullptr) {
     const int64_t need = mcg::plan_streamk(dtypeA, a, current_num_cu());
     if (need > 0 && need <= ws_bytes) {
@@ -424,6 +437,16 @@ int mcg_dense_path(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, i
   return dense_plan(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb, true).kernel;
 }
 
+int gemm_dense_noalloc(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
+                       const void* A, int64_t lda, const void* B, int64_t ldb, const void* C, void* D,
+                       int64_t ldc, int dtypeD, double alpha, double beta, float scaleA, float scaleB,
+                       void* stream) {
+  return dense_impl(dtypeA, dtypeB, layoutA, layoutB, M, N, K, A, lda, B, ldb, C, D, ldc, dtypeD, alpha, beta,
+                    scaleA, scaleB, nullptr, 0, stream, true);
+}
+
+int64_t mcg_dense_noalloc_scratch_bytes(void) { return mcg::STATIC_SCRATCH_BYTES; }
+
 int64_t mcg_dense_workspace_bytes(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
                                   const void* A, int64_t lda, const void* B, int64_t ldb) {
   if (dtypeA < MCG_BF16 || dtypeA > MCG_FP8_E5M2 || M <= 0 || N <= 0 || K <= 0) return 0;
@@ -476,6 +499,7 @@ const char* mcg_status_string(int status) {
     case MCG_ERR_UNSUPPORTED_ARCH: return "current device is not gfx950";
     case MCG_ERR_HIP: return "HIP runtime error";
     case MCG_ERR_INVALID_VALUE: return "alpha, beta or scale not usable for this dtype";
+    case MCG_ERR_SCRATCH_LIMIT: return "the stream-K plan needs more than the library's static scratch";
     default: return "unknown status";
   }
 }

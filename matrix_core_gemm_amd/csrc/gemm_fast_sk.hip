@@ -15,6 +15,7 @@
 // ascending, so the result does not depend on timing) and applies the epilogue.
 // No workgroup waits for another and nothing is added atomically.
 #include <algorithm>
+#include <mutex>
 #include <numeric>
 
 #include "gemm_fast_kernel.hpp"
@@ -62,6 +63,38 @@ int64_t plan_streamk(int dtA, DenseArgs& a, int num_cu) {
 hipError_t launch_fast_sk(int dtA, int dtB, int la, int lb, const DenseArgs& a, hipStream_t s) {
   if (a.sk_tiles <= 0 || a.ws == nullptr) return hipErrorInvalidValue;
   return fast::launch_fast_tb<256, true>(dtA, dtB, la, lb, a, s);
+}
+
+// ------------------------------------------------------------ static scratch
+// Stream-K slots for callers that cannot allocate (gemm_dense_noalloc): a
+// file-scope device array of STATIC_SCRATCH_BYTES, one copy per GPU, held until
+// the process ends.  Host code never passes the array's name to a kernel: its
+// device address is looked up once per device with that device current and
+// kept, and only that address is used.  Every call on a GPU shares that GPU's
+// copy; calls that overlap on one GPU race.  Nothing in it needs to start at
+// zero (each slot is written whole before it is read).
+static __device__ __align__(256) char scratch[STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace mcg

@@ -141,6 +141,10 @@ hipError_t launch_fast_mid(int dtA, int dtB, int layoutA, int layoutB, const Den
 // when the plan would not be faster than whole tiles.
 int64_t plan_streamk(int dtA, DenseArgs& a, int num_cu);
 hipError_t launch_fast_sk(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
+// The library's static stream-K scratch: STATIC_SCRATCH_BYTES per device; its
+// device address for the current device (looked up on the first call there).
+constexpr int64_t STATIC_SCRATCH_BYTES = (int64_t)64 << 20;
+hipError_t static_scratch(void** ptr);
 hipError_t launch_sparse(int dtA, int dtB, int layoutB, bool aligned, const SparseArgs& a, hipStream_t s);
 bool sparse_fast_ok(int dtA, int layoutB, const SparseArgs& a);
 hipError_t launch_sparse_fast(int dtA, int dtB, int layoutB, const SparseArgs& a, hipStream_t s);
