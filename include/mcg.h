@@ -155,8 +155,9 @@ int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB,
  * Computes exactly what gemm_dense computes (the matrix fused multiply-add of
  * "Accurate Models of AMD Matrix Cores", Section 2, Eq. (1)), with the same
  * arguments, validation, accuracy bound and errors.  The workspace lets problems
- * on the 256 x 256 kernel whose tile count leaves the device's last round of
- * tiles partly idle run in stream-K form: the whole rounds as usual, and the K
+ * on the pipelined kernel (256 x 256 tiles, or its 128 x 128 form for mid-size
+ * problems) whose tile count leaves the device's last round of tiles partly
+ * idle run in stream-K form: the whole rounds as usual, and the K
  * iterations of the remaining tiles spread evenly over all compute units, each
  * piece of a tile leaving its partial sums in the workspace, from which a
  * second kernel adds them in a fixed order (K ascending) and applies the
@@ -186,7 +187,7 @@ int gemm_dense_ws(int dtypeA, int dtypeB, int layoutA, int layoutB,
  * gemm_dense_noalloc -- gemm_dense_ws for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): the stream-K slots come from a static device array inside
- * the library, mcg_dense_noalloc_scratch_bytes() (64 MiB) per GPU, held until
+ * the library, mcg_dense_noalloc_scratch_bytes() (32 MiB) per GPU, held until
  * the process ends.  The call allocates nothing and frees nothing.
  *
  * Arguments, results and errors are those of gemm_dense_ws with a workspace
@@ -205,7 +206,8 @@ int gemm_dense_noalloc(int dtypeA, int dtypeB, int layoutA, int layoutB,
 int64_t mcg_dense_noalloc_scratch_bytes(void);
 
 /* mcg_dense_workspace_bytes -- bytes of workspace gemm_dense_ws uses for these
- * operands (host-only, no device work): 256 KiB per piece of a remainder tile,
+ * operands (host-only, no device work): one binary32 tile per piece of a
+ * remainder tile (256 KiB with 256 x 256 tiles, 64 KiB with 128 x 128 ones),
  * or 0 when the problem does not take the stream-K form (another kernel, a
  * tile count that fills the device's rounds, or too little to gain).  Reads the
  * current device's compute-unit count (256 when there is no device). */

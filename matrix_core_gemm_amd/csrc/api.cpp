@@ -203,22 +203,24 @@ static int dense_impl(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t 
   const bool aligned = dense_aligned(eb, K, A, lda, B, ldb);
   const mcg::DensePlan plan =
       mcg::plan_dense(dtypeA, layoutA, layoutB, a, aligned, can_split_k(a, C, D), current_num_cu());
-  if (plan.kernel == mcg::KERNEL_FAST && use_static) {
-    const int64_t need = mcg::plan_streamk(dtypeA, a, current_num_cu());
+  const bool pipelined = plan.kernel == mcg::KERNEL_FAST || plan.kernel == mcg::KERNEL_MID;
+  const int tile = plan.kernel == mcg::KERNEL_MID ? 128 : 256;
+  if (pipelined && use_static) {
+    const int64_t need = mcg::plan_streamk(dtypeA, a, current_num_cu(), tile);
     if (need > mcg::STATIC_SCRATCH_BYTES) return MCG_ERR_SCRATCH_LIMIT;
     if (need > 0) {
       void* p = nullptr;
       const hipError_t e = mcg::static_scratch(&p);
       if (e != hipSuccess) return hip_status(e);
       a.ws = p;
-      return hip_status(mcg::launch_fast_sk(dtypeA, dtypeB, layoutA, layoutB, a, (hipStream_t)stream));
+      return hip_status(mcg::launch_fast_sk(dtypeA, dtypeB, layoutA, layoutB, a, (hipStream_t)stream, tile));
     }
   }
-  if (plan.kernel == mcg::KERNEL_FAST && ws != nullptr) {
-    const int64_t need = mcg::plan_streamk(dtypeA, a, current_num_cu());
+  if (pipelined && ws != nullptr) {
+    const int64_t need = mcg::plan_streamk(dtypeA, a, current_num_cu(), tile);
     if (need > 0 && need <= ws_bytes) {
       a.ws = ws;
-      return hip_status(mcg::launch_fast_sk(dtypeA, dtypeB, layoutA, layoutB, a, (hipStream_t)stream));
+      return hip_status(mcg::launch_fast_sk(dtypeA, dtypeB, layoutA, layoutB, a, (hipStream_t)stream, tile));
     }
     a.dp_tiles = a.sk_tiles = a.sk_wgs = 0;
   }
@@ -450,12 +452,13 @@ int64_t mcg_dense_noalloc_scratch_bytes(void) { return mcg::STATIC_SCRATCH_BYTES
 int64_t mcg_dense_workspace_bytes(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K,
                                   const void* A, int64_t lda, const void* B, int64_t ldb) {
   if (dtypeA < MCG_BF16 || dtypeA > MCG_FP8_E5M2 || M <= 0 || N <= 0 || K <= 0) return 0;
-  if (dense_plan(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb, true).kernel != mcg::KERNEL_FAST) return 0;
+  const int kernel = dense_plan(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb, true).kernel;
+  if (kernel != mcg::KERNEL_FAST && kernel != mcg::KERNEL_MID) return 0;
   mcg::DenseArgs a{};
   a.M = M;
   a.N = N;
   a.K = K;
-  return mcg::plan_streamk(dtypeA, a, current_num_cu());
+  return mcg::plan_streamk(dtypeA, a, current_num_cu(), kernel == mcg::KERNEL_MID ? 128 : 256);
 }
 
 int mcg_dense_splits(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A,

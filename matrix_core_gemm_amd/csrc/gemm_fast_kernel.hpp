@@ -70,7 +70,7 @@ struct EpiDst {
 
 // TB: output tile TB x TB (256, or 128 for problems with too few 256 x 256 tiles to
 // fill the chip); each wavefront owns (TB / 2) x (TB / 4) outputs.  SK: the
-// stream-K form (TB 256 only), whose workgroups each take a range of the K
+// stream-K form, whose workgroups each take a range of the K
 // iterations of the tiles after the first dp_tiles, which a launch of the
 // whole-tile form covers.
 template <class Op, int LA, int LB, int TB, bool SK = false>
@@ -98,7 +98,6 @@ void gemm_fast_kernel(DenseArgs p) {
   using v4 = typename std::conditional<Op::INT_ACC, i32x4, f32x4>::type;
   using s1 = typename std::conditional<Op::INT_ACC, int, float>::type;
   static_assert(TB == 256 || TB == 128, "tile");
-  static_assert(!SK || TB == 256, "stream-K form of the 256 x 256 kernel only");
   static_assert(GA::BYTES == SB && GB::BYTES == SB, "one stage size for both operands");
   constexpr int LH = LdA::INSTR / 2;  // loads per wave, operand and half stage (one group's share)
   static_assert(LdA::INSTR == LdB::INSTR && (LH == 4 || LH == 2), "vmcnt bookkeeping");

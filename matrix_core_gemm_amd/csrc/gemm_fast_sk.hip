@@ -1,5 +1,6 @@
-// gemm_fast_sk.hip -- stream-K form of the 256 x 256 pipelined kernel
-// (gemm_fast_kernel.hpp) and its plan.
+// gemm_fast_sk.hip -- stream-K form of the pipelined kernel (gemm_fast_kernel.hpp):
+// the 256 x 256 instances and the plan of both tile sizes (the 128 x 128
+// instances are in gemm_fast_mid_sk.hip).
 //
 // A problem whose number of 256 x 256 tiles is not a multiple of the number of
 // compute units leaves most CUs idle in its last round of tiles (7168^3: 784
@@ -7,7 +8,8 @@
 // rounds as one launch of the whole-tile kernel, then spreads the K iterations
 // of the remaining tiles evenly over all CUs in a second launch: workgroup w
 // takes the consecutive K tiles [w L, (w + 1) L) of the remainder, numbered tile
-// by tile, so it works on one or two tiles.  (Running both parts in one launch
+// by tile (the kernel handles ranges that cross a tile boundary; the plan picks
+// L so that each range is one piece of one tile).  (Running both parts in one launch
 // measured slower: the loop over pieces costs the whole-tile rounds registers
 // and about 6-8% of their speed.)  A
 // piece that is not a whole tile writes its raw sums to a workspace slot; a
@@ -24,44 +26,57 @@ namespace mcg {
 
 namespace {
 // Cost model (one workgroup per CU): a K tile of a whole round takes at least
-// SK_KT_US (int8 / fp8; bf16 takes about 1.6 us at 8192^3), each piece writes and
-// the fixup reads one 256 KiB slot (SK_PIECE_US), and the fixup launch with its
+// KT_US (the 256 x 256 form: int8 / fp8; bf16 takes about 1.6 us at 8192^3; the
+// 128 x 128 form about half), each piece writes and the fixup reads one slot of
+// tile^2 binary32 values (PIECE_US for 256 KiB), and the fixup launch with its
 // fixed latency costs SK_FIXED_US.  Stream-K is taken when the K tiles it saves in
 // the last round outweigh its own cost.
-constexpr double SK_KT_US = 0.75, SK_PIECE_US = 0.1, SK_FIXED_US = 8.0;
+constexpr double SK_KT_US_256 = 0.75, SK_KT_US_128 = 0.4, SK_PIECE_US_256 = 0.1, SK_FIXED_US = 8.0;
 constexpr int64_t SK_MIN_ITERS = 4;  // K tiles per workgroup range at least
 }  // namespace
 
-int64_t plan_streamk(int dtA, DenseArgs& a, int num_cu) {
+int64_t plan_streamk(int dtA, DenseArgs& a, int num_cu, int tile) {
   a.dp_tiles = a.sk_tiles = a.sk_wgs = 0;
   a.sk_iters = 0;
   a.sk_period = 1;
+  if (tile != 256 && tile != 128) return 0;
   const int64_t G = num_cu > 0 ? num_cu : 256;
   const int64_t eb = (dtA == DT_BF16 || dtA == DT_F16) ? 2 : 1;
   const int64_t nk = (a.K * eb + fast::KTB - 1) / fast::KTB;
-  const int64_t T = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+  const int64_t T = ((a.M + tile - 1) / tile) * ((a.N + tile - 1) / tile);
   const int64_t R = T % G;
   if (R == 0 || nk < 2 * SK_MIN_ITERS) return 0;
-  const int64_t L = std::max((R * nk + G - 1) / G, SK_MIN_ITERS);
-  const int64_t wgs = (R * nk + L - 1) / L;
-  int64_t pieces = 0;
-  for (int64_t w = 0; w < wgs; ++w) {
-    const int64_t s = w * L, e = std::min(s + L, R * nk);
-    pieces += (e - 1) / nk - s / nk + 1;
-  }
-  const double saved = (double)(nk - L) * SK_KT_US;
-  const double cost = (double)pieces * SK_PIECE_US + SK_FIXED_US;
+  // Each remainder tile is cut into s equal pieces, s the largest divisor of nk
+  // with R s <= G and at least SK_MIN_ITERS K tiles per piece, so that every
+  // workgroup takes exactly one piece and the workgroups of one XCD (taken
+  // round-robin) walk the same K range of neighbouring tiles and share their
+  // panels in L2.  (Ranges that cross tile boundaries balance the CUs better but
+  // give every workgroup its own K offset: measured slower than whole tiles.)
+  int64_t sp = 0;
+  for (int64_t c = std::min(G / R, nk / SK_MIN_ITERS); c >= 2; --c)
+    if (nk % c == 0) {
+      sp = c;
+      break;
+    }
+  if (sp < 2) return 0;
+  const int64_t L = nk / sp;
+  const int64_t wgs = R * sp;
+  const int64_t pieces = wgs;
+  const int64_t slot = (int64_t)tile * tile * 4;
+  const double saved = (double)(nk - L) * (tile == 256 ? SK_KT_US_256 : SK_KT_US_128);
+  const double cost = (double)pieces * SK_PIECE_US_256 * (double)slot / (256.0 * 256 * 4) + SK_FIXED_US;
   if (saved <= cost || T - R + wgs > 0x7fffffff) return 0;
   a.dp_tiles = (int)(T - R);
   a.sk_tiles = (int)R;
   a.sk_wgs = (int)wgs;
   a.sk_iters = L;
   a.sk_period = nk / std::gcd(L, nk);
-  return pieces * 256 * 256 * 4;
+  return pieces * slot;
 }
 
-hipError_t launch_fast_sk(int dtA, int dtB, int la, int lb, const DenseArgs& a, hipStream_t s) {
+hipError_t launch_fast_sk(int dtA, int dtB, int la, int lb, const DenseArgs& a, hipStream_t s, int tile) {
   if (a.sk_tiles <= 0 || a.ws == nullptr) return hipErrorInvalidValue;
+  if (tile == 128) return launch_fast_mid_sk(dtA, dtB, la, lb, a, s);
   return fast::launch_fast_tb<256, true>(dtA, dtB, la, lb, a, s);
 }
 

@@ -136,14 +136,17 @@ hipError_t launch_stream(int dtA, int dtB, int layoutA, int layoutB, const Dense
 bool fast_path_ok(int dtA, int layoutA, int layoutB, const DenseArgs& a, bool aligned, int tile = 256);
 hipError_t launch_fast(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s, int tile = 256);
 hipError_t launch_fast_mid(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
-// Stream-K plan for a problem on the 256 x 256 kernel: fills the sk_* and dp_tiles
-// fields of a and returns the workspace bytes it needs, or 0 (and sk_tiles = 0)
-// when the plan would not be faster than whole tiles.
-int64_t plan_streamk(int dtA, DenseArgs& a, int num_cu);
-hipError_t launch_fast_sk(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
+// Stream-K plan for a problem on the pipelined kernel with tile x tile tiles (256,
+// or 128 for its mid-size form): fills the sk_* and dp_tiles fields of a and
+// returns the workspace bytes it needs, or 0 (and sk_tiles = 0) when the plan
+// would not be faster than whole tiles.
+int64_t plan_streamk(int dtA, DenseArgs& a, int num_cu, int tile = 256);
+hipError_t launch_fast_sk(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s,
+                          int tile = 256);
+hipError_t launch_fast_mid_sk(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
 // The library's static stream-K scratch: STATIC_SCRATCH_BYTES per device; its
 // device address for the current device (looked up on the first call there).
-constexpr int64_t STATIC_SCRATCH_BYTES = (int64_t)64 << 20;
+constexpr int64_t STATIC_SCRATCH_BYTES = (int64_t)32 << 20;
 hipError_t static_scratch(void** ptr);
 hipError_t launch_sparse(int dtA, int dtB, int layoutB, bool aligned, const SparseArgs& a, hipStream_t s);
 bool sparse_fast_ok(int dtA, int layoutB, const SparseArgs& a);

@@ -1,14 +1,15 @@
-"""GPU parity of the stream-K form of the 256 x 256 kernel (gemm_dense_ws)
+"""GPU parity of the stream-K form of the pipelined kernel (gemm_dense_ws)
 against the CPU oracle.
 
-Shapes whose last round of 256 x 256 tiles leaves most compute units idle take
+Shapes whose last round of tiles leaves most compute units idle take
 the stream-K form when a workspace is given: the K iterations of the remaining
 tiles are split over all CUs and their partial sums added by a second kernel.
 Every output of those tiles is compared with the oracle (float: the acceptance
 bound; int8: bit for bit), together with one whole-tile workgroup's tile and
-sampled outputs elsewhere.  The cases cover ranges that stay inside one tile
-and ranges that cross tile boundaries, the MN-contiguous storage orders, a
-bfloat16 D, D aliasing C, int8 with wrapping alpha/beta, native fp8, repeated
+sampled outputs elsewhere.  The cases cover both tile sizes (256 x 256 and the
+128 x 128 form), 2 to 16 pieces per tile, with and without whole-tile rounds
+before them, the MN-contiguous storage orders, bfloat16 and binary16 D, D
+aliasing C, int8 with wrapping alpha/beta, native fp8, repeated
 calls (deterministic: the pieces are added in a fixed order) and a workspace too
 small for the plan (the call runs as gemm_dense, bit for bit).
 """
@@ -22,9 +23,6 @@ from gpu_util import dev, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
-SLOT = 256 * 256 * 4
-
-
 def grouped_tile(pid, tiles_m, tiles_n):
     """The kernels' tile order: groups of four tile rows, column-major inside."""
     g, r = divmod(pid, 4 * tiles_n)
@@ -32,18 +30,18 @@ def grouped_tile(pid, tiles_m, tiles_n):
     return 4 * g + r % gsize, r // gsize
 
 
-def remainder_tiles(M, N, num_cu):
-    tm, tn = -(-M // 256), -(-N // 256)
+def remainder_tiles(M, N, num_cu, t=256):
+    tm, tn = -(-M // t), -(-N // t)
     T = tm * tn
     R = T % num_cu
     return [grouped_tile(p, tm, tn) for p in range(T - R, T)], grouped_tile(0, tm, tn)
 
 
-def tile_coords(tiles, M, N):
+def tile_coords(tiles, M, N, t=256):
     rows, cols = [], []
     for tm, tn in tiles:
-        r = np.arange(tm * 256, min(M, tm * 256 + 256))
-        c = np.arange(tn * 256, min(N, tn * 256 + 256))
+        r = np.arange(tm * t, min(M, tm * t + t))
+        c = np.arange(tn * t, min(N, tn * t + t))
         rr, cc = np.meshgrid(r, c, indexing="ij")
         rows.append(rr.ravel())
         cols.append(cc.ravel())
@@ -58,29 +56,34 @@ def workspace(nbytes):
     return torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device="cuda").fill_(float("nan"))
 
 
-CASES = [  # dtA, dtB, layA, layB, M, N, K, out, alpha, beta, D aliases C
-    ("bf16", "bf16", "k_contig", "k_contig", 4096, 4352, 4096, "f32", 1.5, 0.5, False),
-    ("bf16", "bf16", "mn_contig", "mn_contig", 4096, 4864, 4096, "f32", -0.75, 1.0, True),
-    ("f16", "f16", "k_contig", "mn_contig", 4096, 4864, 4096, "bf16", 1.0, -1.25, False),
-    ("i8", "i8", "k_contig", "k_contig", 4096, 4352, 8192, "i32", 3, -2, False),
-    ("e4m3", "e5m2", "k_contig", "k_contig", 4096, 4352, 8192, "f32", 1.0, 0.0, False),
+CASES = [  # dtA, dtB, layA, layB, M, N, K, out, alpha, beta, D aliases C, kernel (1: 256 x 256, 6: 128 x 128)
+    ("bf16", "bf16", "k_contig", "k_contig", 4096, 4352, 4096, "f32", 1.5, 0.5, False, 1),
+    ("bf16", "bf16", "mn_contig", "mn_contig", 4096, 4864, 4096, "f32", -0.75, 1.0, True, 1),
+    ("f16", "f16", "k_contig", "mn_contig", 4096, 4864, 4096, "bf16", 1.0, -1.25, False, 1),
+    ("i8", "i8", "k_contig", "k_contig", 4096, 4352, 8192, "i32", 3, -2, False, 1),
+    ("e4m3", "e5m2", "k_contig", "k_contig", 4096, 4352, 8192, "f32", 1.0, 0.0, False, 1),
+    ("bf16", "bf16", "k_contig", "k_contig", 1024, 2048, 8192, "f32", 1.0, 0.5, False, 6),
+    ("f16", "f16", "mn_contig", "k_contig", 1152, 1280, 12288, "f16", -1.5, 1.0, True, 6),
+    ("i8", "i8", "k_contig", "mn_contig", 1024, 1024, 16384, "i32", -1, 1, False, 6),
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=["bf16_in_tile", "bf16_mn_cross_alias", "f16_bf16out_cross",
-                                             "i8_wrap", "fp8_native"])
+@pytest.mark.parametrize("case", CASES, ids=["bf16_16_pieces", "bf16_mn_alias_4_pieces", "f16_bf16out",
+                                             "i8_wrap", "fp8_native", "mid_bf16", "mid_f16_f16out_alias",
+                                             "mid_i8"])
 def test_streamk_against_oracle(case):
     mcg = need_gpu()
-    dtA, dtB, layA, layB, M, N, K, out, alpha, beta, alias = case
+    dtA, dtB, layA, layB, M, N, K, out, alpha, beta, alias, kernel = case
+    t = 256 if kernel == 1 else 128
     say(f"stream-K {dtA}x{dtB} {layA}/{layB} {M}x{N}x{K} -> {out} alias={alias}")
     fp8 = dtA in ("e4m3", "e5m2")
     dist = "int8" if dtA == "i8" else "normal"
     A = W.operand("A", dtA, M, K, dist, layA, seed=41, fp8_scaled=fp8)
     B = W.operand("B", dtB, K, N, dist, layB, seed=42, fp8_scaled=fp8)
     dA, dB = dev(A.codes), dev(B.codes)
-    assert mcg.dense_path(dtA, layA, layB, M, N, K, dA, A.ld, dB, B.ld) == 1
+    assert mcg.dense_path(dtA, layA, layB, M, N, K, dA, A.ld, dB, B.ld) == kernel
     need = mcg.dense_workspace_bytes(dtA, layA, layB, M, N, K, dA, A.ld, dB, B.ld)
-    assert need > 0 and need % SLOT == 0
+    assert need > 0 and need % (t * t * 4) == 0
     ldc = N
     C = None
     if out == "i32":
@@ -90,10 +93,11 @@ def test_streamk_against_oracle(case):
         C = W.c_matrix(M, N, "normal", seed=43, ldc=ldc) if beta != 0 else None
         D = torch.full((M, ldc), float("nan"), dtype=torch.float32, device="cuda")
     else:
-        c16 = W.draw("normal", (M, ldc), 43).to(torch.float32).to(torch.bfloat16)
+        tdt = torch.bfloat16 if out == "bf16" else torch.float16
+        c16 = W.draw("normal", (M, ldc), 43).to(torch.float32).to(tdt)
         C = c16.view(torch.int16).numpy().view(np.uint16)
-        D = torch.full((M, ldc), 0x7FC0, dtype=torch.int32).to(torch.int16).to("cuda")
-    dC = None if C is None else dev(C.view(np.int16) if out == "bf16" else C)
+        D = torch.full((M, ldc), 0x7FC0 if out == "bf16" else 0x7E00, dtype=torch.int32).to(torch.int16).to("cuda")
+    dC = None if C is None else dev(C.view(np.int16) if out in ("bf16", "f16") else C)
     if alias:
         D = dC
     ws = workspace(need)
@@ -102,27 +106,27 @@ def test_streamk_against_oracle(case):
     torch.cuda.synchronize()
     d = D.cpu().numpy()
     # every output of the remainder tiles, one whole tile, and sampled others
-    sk, first = remainder_tiles(M, N, num_cu())
-    r1, c1 = tile_coords(sk + [first], M, N)
+    sk, first = remainder_tiles(M, N, num_cu(), t)
+    r1, c1 = tile_coords(sk + [first], M, N, t)
     r2, c2 = W.sample_coords(M, N, n_random=2048, full_rows=(M - 1,), full_cols=(N - 1,))
     rows, cols = np.concatenate([r1, r2]), np.concatenate([c1, c2])
-    say(f"  {len(sk)} stream-K tiles, {need // SLOT} pieces, {len(rows)} outputs compared")
+    say(f"  {len(sk)} stream-K tiles, {need // (t * t * 4)} pieces, {len(rows)} outputs compared")
     if out == "i32":
         ref = oracle.gemm_i8(layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, ldc, alpha, beta,
                              rows=rows, cols=cols)
         r = oracle.check_exact(d[rows, cols], ref)
     else:
         ref, s = oracle.gemm_float(dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, ldc,
-                                   alpha, beta, A.scale, B.scale, rows=rows, cols=cols,
-                                   out="bf16" if out == "bf16" else "f32")
-        if out == "bf16":
-            got = (d.view(np.uint16).astype(np.uint32) << 16).view(np.float32)[rows, cols]
-            cc = None if C is None else (C.astype(np.uint32) << 16).view(np.float32)[rows, cols]
+                                   alpha, beta, A.scale, B.scale, rows=rows, cols=cols, out=out)
+        if out in ("bf16", "f16"):
+            tdt = torch.bfloat16 if out == "bf16" else torch.float16
+            dec = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(tdt).double().numpy()
+            got = dec(d)[rows, cols]
+            cc = None if C is None else dec(C)[rows, cols]
         else:
             got = d[rows, cols]
             cc = None if C is None else C[rows, cols]
-        r = oracle.check_float(got, ref, s, K, alpha, A.scale, B.scale, beta, cc,
-                               out="bf16" if out == "bf16" else "f32")
+        r = oracle.check_float(got, ref, s, K, alpha, A.scale, B.scale, beta, cc, out=out)
     say("  ", {k: v for k, v in r.items() if k != "worst"})
     assert r["ok"], r
 

@@ -6,9 +6,9 @@ tile_order.hpp (built into a host program, tests/tile_order_dump.cpp):
   - sk_first_piece, a closed form, equals the count of pieces found by walking
     every workgroup's range of K tiles over the tile boundaries.
 mcg_dense_workspace_bytes (the library's host-side plan, 256 compute units when
-no device is present): 256 KiB per piece for shapes whose last round of
-256 x 256 tiles is short, 0 where whole rounds fill the device or there is too
-little to gain.
+no device is present): one binary32 tile per piece for shapes whose last round
+of tiles is short, 0 where whole rounds fill the device or there is too little
+to gain.
 """
 import os
 import subprocess
@@ -85,17 +85,19 @@ def test_workspace_plan(monkeypatch):
     assert _ws(mcg, "bf16", 6144, 6144, 6144) == 256 * slot
     # int8 7168^3: 56 K tiles of 128 bytes, ranges of 4: 224 workgroups, one piece each
     assert _ws(mcg, "i8", 7168, 7168, 7168) == 224 * slot
-    # 16 x 19 tiles = 256 + 48, K = 4096 (64 K tiles), ranges of 12 cross tile
-    # boundaries: 256 workgroups and 32 extra pieces
-    assert _ws(mcg, "bf16", 4096, 4864, 4096) == 288 * slot
-    _, total = brute_pieces(48, 64, 12)
-    assert total == 288
+    # 16 x 19 tiles = 256 + 48, K = 4096 (64 K tiles): at most 5 pieces per tile,
+    # 5 does not divide 64, so 4 pieces of 16 K tiles: 192 workgroups
+    assert _ws(mcg, "bf16", 4096, 4864, 4096) == 192 * slot
     # whole rounds, or too little to gain (5120^3: the last round is 144 of 256 tiles)
     assert _ws(mcg, "bf16", 8192, 8192, 8192) == 0
     assert _ws(mcg, "bf16", 4096, 4096, 4096) == 0
     assert _ws(mcg, "bf16", 5120, 5120, 5120) == 0
-    # not the 256 x 256 kernel (too few tiles, skinny, binary64)
-    assert _ws(mcg, "bf16", 1024, 1024, 8192) == 0
+    # the 128 x 128 form (too few 256 x 256 tiles): 1024 x 2048 is 128 tiles of
+    # 128 x 128 with 128 K tiles, each tile cut in two: 256 slots of 64 KiB;
+    # 1280^2 x 16384 is 100 tiles, cut in two (three would need 300 CUs)
+    assert _ws(mcg, "bf16", 1024, 2048, 8192) == 256 * 128 * 128 * 4
+    assert _ws(mcg, "bf16", 1280, 1280, 16384) == 200 * 128 * 128 * 4
+    # not the pipelined kernel (skinny, binary64)
     assert _ws(mcg, "bf16", 32768, 16, 8192) == 0
     assert mcg.dense_workspace_bytes("f64", "k_contig", "k_contig", 7168, 7168, 7168, 0x1000, 7168, 0x1000,
                                      7168) == 0

@@ -26,9 +26,11 @@ def test_noalloc_matches_workspace_entry_point():
     mcg = need_gpu()
     lib = mcg.lib()
     limit = lib.mcg_dense_noalloc_scratch_bytes()
-    assert limit == 64 << 20
+    assert limit == 32 << 20
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    for i, (M, N, K) in enumerate([(4096, 4352, 4096), (4096, 4352, 2048)]):
+    # 128 x 128 tiles: 1024 x 2048 x 8192 cuts 128 tiles in two, 1024^2 x 4096 cuts
+    # 64 tiles in four (16 MiB of slots each)
+    for i, (M, N, K) in enumerate([(1024, 2048, 8192), (1024, 1024, 4096)]):
         A = dev(W.operand("A", "bf16", M, K, "normal", "k_contig", seed=61 + i).codes)
         B = dev(W.operand("B", "bf16", K, N, "normal", "k_contig", seed=71 + i).codes)
         need = mcg.dense_workspace_bytes("bf16", "k_contig", "k_contig", M, N, K, A, K, B, K)
@@ -48,7 +50,7 @@ def test_noalloc_matches_workspace_entry_point():
 def test_noalloc_rejects_a_plan_beyond_the_array():
     mcg = need_gpu()
     lib = mcg.lib()
-    M, N, K = 4096, 4864, 4096  # 288 pieces of 256 KiB = 72 MiB
+    M, N, K = 4096, 4352, 4096  # 16 remainder tiles in 16 pieces of 256 KiB: 64 MiB
     A = torch.zeros(M, K, dtype=torch.int16, device="cuda")
     B = torch.zeros(N, K, dtype=torch.int16, device="cuda")
     assert mcg.dense_workspace_bytes("bf16", "k_contig", "k_contig", M, N, K, A, K, B, K) > \
