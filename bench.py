@@ -16,6 +16,9 @@ synthetic workload:
   gemm_dense  bf16 x bf16 -> bf16, 8192^3 (C and D in bfloat16)
   gemm_dense  skinny bf16 32768 x 16 x 8192 and 16 x 32768 x 8192 (HBM-bound)
   gemm_dense  f64  x f64  -> f64, 8192^3 (binary64, C ~ N(0,1))
+  gemm_dense_ws bf16 7168^3, 6144^3, 5120^3, 1024 x 2048 x 8192, 1280 x 1280 x
+              8192 (shapes whose last round of tiles is short: the stream-K form
+              where the plan takes it; leading blocks of the 8192^2 operands)
 Each call (or batch) is bracketed by HIP events recorded on the stream it is
 launched on, so every kernel's average duration is measured live.
 
@@ -159,6 +162,21 @@ def main():
                 E[name] = Entry(name, "dense", dtA=dt, dtB=dt, layA=lay[0], layB=lay[1], M=n, N=n, K=n,
                                 A=dA, B=dB, hA=A.codes, hB=B.codes, lda=n, ldb=n, C=C, hC=C_h, D=D,
                                 out="f32", alpha=1.0, beta=1.0, sA=1.0, sB=1.0, peak=PEAK[dt], unit="TFLOP/s")
+    # shapes whose last round of tiles is short, on gemm_dense_ws (stream-K form
+    # where the plan takes it): leading blocks of the 8192^2 bf16 operands
+    # (lda = ldb = 8192), no C, binary32 D
+    wsbuf = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    eh = E["bf16"]
+    for m_, n_, k_ in ((7168, 7168, 7168), (6144, 6144, 6144), (5120, 5120, 5120), (1024, 2048, 8192),
+                       (1280, 1280, 8192)):
+        name = f"bf16_{m_}" if m_ == n_ == k_ else f"bf16_{m_}x{n_}x{k_}"
+        if not want(name):
+            continue
+        need = mcg.dense_workspace_bytes("bf16", "k_contig", "k_contig", m_, n_, k_, eh.A, n, eh.B, n)
+        E[name] = Entry(name, "dense", dtA="bf16", dtB="bf16", layA="k_contig", layB="k_contig", M=m_, N=n_, K=k_,
+                        A=eh.A, B=eh.B, hA=eh.hA, hB=eh.hB, lda=n, ldb=n, C=None, hC=None,
+                        D=D.view(-1)[:m_ * n_].view(m_, n_), out="f32", alpha=1.0, beta=0.0, sA=1.0, sB=1.0,
+                        peak=PEAK["bf16"], unit="TFLOP/s", ws=wsbuf, ws_bytes=need)
     # bf16 256^3 (launch-bound)
     As = W.operand("A", "bf16", 256, 256, "uniform", "k_contig")
     Bs_ = W.operand("B", "bf16", 256, 256, "uniform", "k_contig")
@@ -245,7 +263,11 @@ def main():
     s = stream.cuda_stream
 
     def call(e):
-        if e.kind in ("dense", "skinny"):
+        if getattr(e, "ws", None) is not None:
+            mcg.gemm_dense_ws(e.dtA, e.dtB, e.layA, e.layB, e.M, e.N, e.K, e.A, e.lda, e.B, e.ldb, e.C, e.D, e.N,
+                              e.out, e.alpha, e.beta, e.sA, e.sB, workspace=e.ws, workspace_bytes=e.ws_bytes,
+                              stream=s)
+        elif e.kind in ("dense", "skinny"):
             mcg.gemm_dense(e.dtA, e.dtB, e.layA, e.layB, e.M, e.N, e.K, e.A, e.lda, e.B, e.ldb, e.C, e.D, e.N,
                            e.out, e.alpha, e.beta, e.sA, e.sB, stream=s)
         elif e.kind == "compress":
@@ -260,7 +282,7 @@ def main():
     order = ["bf16", "f16", "bf16_Arow_Brow", "bf16_Acol_Bcol", "bf16_Acol_Brow", "f16_Arow_Brow",
              "f16_Acol_Bcol", "f16_Acol_Brow", "bf16_256", "i8_4096", "i8", "e4m3xe4m3", "e4m3xe5m2",
              "compress24", "sparse24", "bf16_out", "skinny_n16", "skinny_m16", "sparse24_i8", "sparse24_e4m3",
-             "f64"]
+             "f64", "bf16_7168", "bf16_6144", "bf16_5120", "bf16_1024x2048x8192", "bf16_1280x1280x8192"]
     names = [x for x in order if x in E and (only is None or x in only or x == "compress24" and "sparse24" in only)]
     ev = {x: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)] for x in names}
@@ -307,6 +329,8 @@ def main():
                       "MxNxK": (e.M, e.N, e.K)}
             if e.kind == "dense":
                 per[x]["layout"] = LAYOUT_NAMES[(e.layA, e.layB)]
+            if getattr(e, "ws", None) is not None:
+                per[x]["stream_k_workspace_MiB"] = e.ws_bytes / 2**20  # 0: whole tiles only
     head = "bf16" if "bf16" in names else names[0]
     value = per[head].get("TFLOP/s", per[head].get("TOPS", per[head].get("GB/s")))
 
