@@ -23,10 +23,10 @@
 //     owning 128 x 64 outputs = 4 x 2 instructions of 32 x 32.
 //   - LDS: kept values in stages of 128 bytes per row (one cache line: 128
 //     dense k of 16-bit or 256 of 8-bit elements) together with their index
-//     words (16 or 32 bytes per row; rows with bit 4 set keep the two halves of
-//     their words swapped, so that the index reads of rows r and r + 16, which
-//     the same LDS cycle serves, fall in different banks), 2 stages; B in stages
-//     of 128 bytes per
+//     words (16 or 32 bytes per row, fetched 16 bytes per lane; for 8-bit
+//     elements rows with bit 4 set keep their two 16-byte chunks swapped, so
+//     that the index reads of rows r and r + 16, which the same LDS cycle
+//     serves, fall in different banks), 2 stages; B in stages of 128 bytes per
 //     column (64 or 128 dense k), 2 stages per column half.  All filled by
 //     buffer_load ... lds.
 //   - ping-pong schedule as in the dense kernel: the two wavefronts of a SIMD
@@ -162,14 +162,14 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   using SG = SpGeom<EB>;
   constexpr int A_STAGE = SG::A_STAGE, IWB = SG::IWB;
   constexpr int WPR = IWB / 4;                   // index words per row and stage
-  constexpr int II = SP_BM * WPR / (64 * NW);    // 4-byte index loads per wave and stage
+  constexpr int II = SP_BM * IWB / (1024 * NW);  // 16-byte index loads per wave of group 0 and stage
   using RA = Reader<EB, LAYOUT_K, SP_BM, 128>;
   using RB = Reader<EB, LB, 128, 128>;
   using LdA = LineLoader<EB, LAYOUT_K, SP_BM, 128>;
   using acc_t = typename Op::acc_t;
   static_assert(Geom<EB, LAYOUT_K, SP_BM, 128>::BYTES == 32768 && Geom<EB, LB, 128, 128>::BYTES == SP_BH_STAGE, "");
   static_assert(LdA::INSTR == 8, "8 loads per wave and kept-value stage");
-  static_assert(II == 4 || II == 8, "index loads per stage");
+  static_assert(II == 1 || II == 2, "index loads per stage");
 
   __shared__ __attribute__((aligned(1024))) char smem_raw[2 * A_STAGE + 4 * SP_BH_STAGE];
   lds_char* smem = (lds_char*)smem_raw;
@@ -200,24 +200,36 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   la.init(p.Ac + m0 * p.lda_c * EB, (uint32_t)(rows * p.lda_c * EB), p.lda_c, Kc, q, lane);
   BHalfLoader<EB, LB> lb;
   lb.init(p.B, n0, 1 - grp, p.N, p.K, p.ldb, q, lane);
+  // Index words: 16-byte loads, so a stage's IWB bytes per row take IWB / 16
+  // lanes.  Instruction i of wave q (group 0) fills LDS bytes [(II q + i) 1024,
+  // +1024) of the index image: lane l holds 16-byte chunk (II q + i) 64 + l,
+  // i.e. row chunk / (IWB / 16) and position chunk % (IWB / 16) of that row.  With
+  // two chunks per row (8-bit), rows with bit 4 set keep them swapped: the chunk
+  // read for step h is h ^ bit 4, and the same LDS cycle's rows r and r + 16 then
+  // fall in different banks.  With one chunk per row (16-bit), the 16 rows that
+  // one cycle of 16-byte reads serves are in different banks as they are.
+  constexpr int CPR = IWB / 16;  // 16-byte chunks per row and stage
   __amdgpu_buffer_rsrc_t rs_idx;
   uint32_t off_idx[II];
-  int word_idx[II];
+  int chunk_idx[II];
   rs_idx = make_rsrc((const char*)(p.idx + m0 * p.ld_idx), (uint32_t)(rows * p.ld_idx * 4));
 #pragma unroll
-  for (int i = 0; i < II; ++i) {  // 4-byte loads: lane -> LDS (row, position) of an IWB-byte index row
-    const int e = i * 256 + q * 64 + lane;
-    const int row = e / WPR;
-    word_idx[i] = (e % WPR) ^ ((WPR / 2) * ((row >> 4) & 1));  // the word kept at that position
-    off_idx[i] = (uint32_t)(row * p.ld_idx * 4 + word_idx[i] * 4);
+  for (int i = 0; i < II; ++i) {
+    const int e = (II * q + i) * 64 + lane;
+    const int row = e / CPR;
+    chunk_idx[i] = CPR == 2 ? (e % 2) ^ ((row >> 4) & 1) : 0;  // the chunk of the row kept at that position
+    off_idx[i] = (uint32_t)(row * p.ld_idx * 4 + chunk_idx[i] * 16);
   }
   auto issueA = [&](int T) { la.issue(stA(T), T, 4 * grp, 4, q); };
   auto issueI = [&](int T) {
 #pragma unroll
     for (int i = 0; i < II; ++i) {
-      const uint32_t o = T * WPR + word_idx[i] < nwords ? off_idx[i] + (uint32_t)(T * IWB) : BUF_OOB;
+      // chunks that start past the last index word read zeros; a chunk that
+      // straddles it reads the row's next words, which only cover groups past K
+      // (their kept values are zero)
+      const uint32_t o = T * WPR + 4 * chunk_idx[i] < nwords ? off_idx[i] + (uint32_t)(T * IWB) : BUF_OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs_idx, (__attribute__((address_space(3))) void*)(stI(T) + (i * 256 + q * 64) * 4), 4, o, 0, 0, 0);
+          rs_idx, (__attribute__((address_space(3))) void*)(stI(T) + (II * q + i) * 1024), 16, o, 0, 0, 0);
     }
   };
   auto issueB = [&](int u) { lb.issue(stBh(1 - grp, u), u, q); };  // the other group's half
@@ -235,17 +247,17 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   // [64h + 32s, +32) of stage T and B bytes [64s, +64) of step u.  Index codes:
   // 16-bit elements use half g of word 2h + s (32 dense k per instruction),
   // 8-bit elements word 4h + 2s + g (64 dense k per instruction).
-  // byte of this lane's index words in row rbA + (lane & 31) for h = 0 (h = 1: ^ IWB / 2);
-  // rows 32 i further add 32 i IWB
-  const int ibase = (rbA + (lane & 31)) * IWB + (IWB / 2) * ((lane >> 4) & 1);
+  // byte of this lane's index record in row rbA + (lane & 31) (8-bit: of its chunk
+  // for h = 0; h = 1: ^ 16); rows 32 i further add 32 i IWB
+  const int ibase = (rbA + (lane & 31)) * IWB + (EB == 1 ? 16 * ((lane >> 4) & 1) : 0);
   auto read_frags = [&](int u) {
     const int T = u >> 1, h = u & 1;
 #pragma unroll
     for (int i = 0; i < WTM; ++i) {
       if constexpr (EB == 2) {
-        const i32x2 w = *(const __attribute__((address_space(3))) i32x2*)(stI(T) + (ibase ^ (8 * h)) + 32 * i * IWB);
-        fi[0][i] = (int)((uint32_t)w.x >> (16 * g));
-        fi[1][i] = (int)((uint32_t)w.y >> (16 * g));
+        const i32x4 w = *(const __attribute__((address_space(3))) i32x4*)(stI(T) + ibase + 32 * i * IWB);
+        fi[0][i] = (int)((uint32_t)(h ? w.z : w.x) >> (16 * g));
+        fi[1][i] = (int)((uint32_t)(h ? w.w : w.y) >> (16 * g));
       } else {
         const i32x4 w = *(const __attribute__((address_space(3))) i32x4*)(stI(T) + (ibase ^ (16 * h)) + 32 * i * IWB);
         fi[0][i] = g ? w.y : w.x;
