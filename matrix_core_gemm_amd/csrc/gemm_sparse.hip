@@ -382,30 +382,15 @@ __global__ __launch_bounds__(256) void compress24_kernel(CompressArgs p) {
   if (bad && p.violations) atomicAdd(p.violations, bad);
 }
 
-// Vector form for aligned rows (K * elem_bytes a multiple of 16): one lane per
-// 16-byte chunk of a row (G = 2 groups of 16-bit or 4 groups of 8-bit values),
-// consecutive lanes on consecutive chunks, so the 16-byte loads, the 8-byte
-// stores of the kept values and the 1- or 2-byte stores of the codes are all
-// contiguous across a wavefront.  Chunk slots past the last chunk of a row,
-// up to the end of its last index word, write zero codes (the padding of a
-// partial last word).  Same selection rule as compress24_kernel.
+// One 16-byte chunk of a row (G = 2 groups of 16-bit or 4 groups of 8-bit
+// values): its 4-bit codes (group gi at bits 4 gi) and its kept values (8 bytes),
+// by the selection rule of compress24_kernel; bad counts groups with more than
+// two non-zeros.
 template <int EB, bool INT8>
-__global__ __launch_bounds__(256) void compress24_vec_kernel(CompressArgs p, int64_t slots) {
-  constexpr int G = 16 / (4 * EB);  // groups per chunk
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= p.M * slots) return;
-  const int64_t row = t / slots, c = t % slots;
-  const int64_t nchunks = p.K * EB / 16;
-  uint8_t* idxb = (uint8_t*)(p.idx + row * p.ld_idx);
-  if (c >= nchunks) {
-    if constexpr (G == 2) idxb[c] = 0;
-    else *(uint16_t*)(idxb + 2 * c) = 0;
-    return;
-  }
-  const i32x4 v = *(const i32x4*)(p.A + row * p.lda * EB + c * 16);
-  uint32_t code = 0;
-  uint64_t kept = 0;
-  int bad = 0;
+__device__ __forceinline__ void compress_chunk(const i32x4& v, uint32_t& code, uint64_t& kept, int& bad) {
+  constexpr int G = 16 / (4 * EB);
+  code = 0;
+  kept = 0;
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {
     uint32_t x[4];
@@ -438,9 +423,53 @@ __global__ __launch_bounds__(256) void compress24_vec_kernel(CompressArgs p, int
     kept |= (uint64_t)k0 << (2 * gi * 8 * EB);
     kept |= (uint64_t)k1 << ((2 * gi + 1) * 8 * EB);
   }
-  *(uint64_t*)(p.Ac + row * p.lda_c * EB + c * 8) = kept;
-  if constexpr (G == 2) idxb[c] = (uint8_t)code;
-  else *(uint16_t*)(idxb + 2 * c) = (uint16_t)code;
+}
+
+// Vector form for aligned rows (K * elem_bytes a multiple of 16): one lane per
+// index word of a row, i.e. 32 dense k (CH = 4 chunks of 16-bit or 2 of 8-bit
+// values), consecutive lanes on consecutive words.  A lane loads its 64 or 32
+// bytes as 16-byte loads, stores its 32 or 16 bytes of kept values (16-byte
+// stores when the destination rows are 16-byte aligned, else 8-byte) and its
+// index word with one 4-byte store.  Chunks past the end of a row (a partial
+// last word) give zero codes and store no values.  Grid: x covers a row's
+// words in blocks of 256, y strides over the rows.  Same selection rule as
+// compress24_kernel.
+template <int EB, bool INT8>
+__global__ __launch_bounds__(256) void compress24_vec_kernel(CompressArgs p, int a16) {
+  constexpr int CH = 32 * EB / 16;
+  constexpr int G = 16 / (4 * EB);
+  const int64_t nwords = (p.K + 31) / 32;
+  const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (w >= nwords) return;
+  const int64_t nchunks = p.K * EB / 16;
+  const int64_t c0 = w * CH;
+  int bad = 0;
+  for (int64_t row = blockIdx.y; row < p.M; row += gridDim.y) {
+    const char* src = p.A + row * p.lda * EB + c0 * 16;
+    char* dst = p.Ac + row * p.lda_c * EB + c0 * 8;
+    i32x4 v[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) v[c] = c0 + c < nchunks ? *(const i32x4*)(src + 16 * c) : i32x4{0, 0, 0, 0};
+    uint32_t word = 0;
+    uint64_t kept[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      uint32_t code;
+      compress_chunk<EB, INT8>(v[c], code, kept[c], bad);
+      if (c0 + c < nchunks) word |= code << (4 * G * c);
+    }
+    if (a16 && c0 + CH <= nchunks) {
+#pragma unroll
+      for (int c = 0; c < CH; c += 2)
+        *(i32x4*)(dst + 8 * c) = i32x4{(int)(uint32_t)kept[c], (int)(uint32_t)(kept[c] >> 32),
+                                       (int)(uint32_t)kept[c + 1], (int)(uint32_t)(kept[c + 1] >> 32)};
+    } else {
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (c0 + c < nchunks) *(uint64_t*)(dst + 8 * c) = kept[c];
+    }
+    p.idx[row * p.ld_idx + w] = word;
+  }
   if (bad && p.violations) atomicAdd(p.violations, bad);
 }
 
@@ -457,16 +486,15 @@ hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s) {
   const bool vec = (a.K * eb) % 16 == 0 && (uintptr_t)a.A % 16 == 0 && (a.lda * eb) % 16 == 0 &&
                    (uintptr_t)a.Ac % 8 == 0 && (a.lda_c * eb) % 8 == 0;
   if (vec) {
-    const int64_t slots = nwords * (eb == 2 ? 4 : 2);  // chunk slots per row (whole index words)
-    const int64_t threads = a.M * slots;
-    if (threads <= 0) return hipSuccess;
-    const int64_t blocks = (threads + 255) / 256;
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (a.M <= 0 || nwords <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((nwords + 255) / 256), (unsigned)(a.M < 65535 ? a.M : 65535));
+    if ((nwords + 255) / 256 > 0x7fffffff) return hipErrorInvalidValue;
+    const int a16 = (uintptr_t)a.Ac % 16 == 0 && (a.lda_c * eb) % 16 == 0;
     if (eb == 2)
-      hipLaunchKernelGGL((compress24_vec_kernel<2, false>), dim3((unsigned)blocks), dim3(256), 0, s, a, slots);
+      hipLaunchKernelGGL((compress24_vec_kernel<2, false>), grid, dim3(256), 0, s, a, a16);
     else if (dtype == DT_I8)
-      hipLaunchKernelGGL((compress24_vec_kernel<1, true>), dim3((unsigned)blocks), dim3(256), 0, s, a, slots);
-    else hipLaunchKernelGGL((compress24_vec_kernel<1, false>), dim3((unsigned)blocks), dim3(256), 0, s, a, slots);
+      hipLaunchKernelGGL((compress24_vec_kernel<1, true>), grid, dim3(256), 0, s, a, a16);
+    else hipLaunchKernelGGL((compress24_vec_kernel<1, false>), grid, dim3(256), 0, s, a, a16);
     return hipGetLastError();
   }
   const int64_t threads = a.M * nwords;
