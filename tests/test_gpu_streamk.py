@@ -65,12 +65,16 @@ CASES = [  # dtA, dtB, layA, layB, M, N, K, out, alpha, beta, D aliases C, kerne
     ("bf16", "bf16", "k_contig", "k_contig", 1024, 2048, 8192, "f32", 1.0, 0.5, False, 6),
     ("f16", "f16", "mn_contig", "k_contig", 1152, 1280, 12288, "f16", -1.5, 1.0, True, 6),
     ("i8", "i8", "k_contig", "mn_contig", 1024, 1024, 16384, "i32", -1, 1, False, 6),
+    # ragged M, N and K: edge tiles among the pieces, a last K tile cut short
+    ("bf16", "bf16", "k_contig", "k_contig", 4196, 4316, 4048, "f32", 1.25, -0.5, False, 1),
+    ("i8", "i8", "k_contig", "mn_contig", 4196, 4320, 8176, "i32", 2, 3, False, 1),
+    ("bf16", "bf16", "mn_contig", "k_contig", 1000, 1944, 8176, "bf16", 1.0, 1.0, True, 6),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=["bf16_16_pieces", "bf16_mn_alias_4_pieces", "f16_bf16out",
                                              "i8_wrap", "fp8_native", "mid_bf16", "mid_f16_f16out_alias",
-                                             "mid_i8"])
+                                             "mid_i8", "ragged_bf16", "ragged_i8_mn", "mid_ragged_bf16out_alias"])
 def test_streamk_against_oracle(case):
     mcg = need_gpu()
     dtA, dtB, layA, layB, M, N, K, out, alpha, beta, alias, kernel = case
