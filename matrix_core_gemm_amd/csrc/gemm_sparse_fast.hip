@@ -402,7 +402,9 @@ bool sparse_fast_ok(int dtA, int layoutB, const SparseArgs& a) {
   const int64_t eb = (dtA == DT_BF16 || dtA == DT_F16) ? 2 : 1;
   // 16-byte chunks of kept values (16 / eb values = 32 / eb dense k) and of B
   // never straddle the end of K when K * eb % 32 == 0; index words are fetched
-  // 4 bytes at a time.  Native fp8 only from the accuracy threshold on (below
+  // 16 bytes at a time from 4-byte aligned rows (a chunk that runs past a row's
+  // last word reads codes only for groups past K, whose kept values are zero).
+  // Native fp8 only from the accuracy threshold on (below
   // it fp8 is widened to bf16 by the general kernel).
   auto al = [](const void* q, int64_t n) { return ((uintptr_t)q % (uintptr_t)n) == 0; };
   const bool aligned = al(a.Ac, 16) && al(a.B, 16) && al(a.idx, 4) && (a.lda_c * eb) % 16 == 0 &&

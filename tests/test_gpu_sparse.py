@@ -116,7 +116,7 @@ def test_sparse_256_tile_path(dt, layB, shape, pads):
     lda_c, ld_idx = K // 2 + pad_v, nw + pad_i
     vp = np.zeros((M, lda_c), v.dtype)
     vp[:, :K // 2] = v
-    ip = np.full((M, ld_idx), 0xFFFFFFFF, np.uint32)  # padding words are never read
+    ip = np.full((M, ld_idx), 0xFFFFFFFF, np.uint32)  # padding words: read only for groups past K
     ip[:, :nw] = i
     D = torch.full((M, N), float("nan"), device="cuda")
     dv, di, dbb = dev(vp), dev(ip.view(np.int32)), dev(B.codes)
