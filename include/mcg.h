@@ -251,6 +251,33 @@ int gemm_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int
                   int dtypeD, double alpha, double beta, void* stream);
 
 /*
+ * gemm_sparse24_ws -- gemm_sparse24 with a caller-provided device workspace.
+ *
+ * Computes exactly what gemm_sparse24 computes (the 2:4 compressed form of
+ * "RDNA4 sparse WMMA builtins", Structured sparsity (2:4 pattern), multiplied as
+ * in "Accurate Models of AMD Matrix Cores", Section 2, Eq. (1)), with the same
+ * arguments, validation, accuracy bound and errors.  Problems on the 256 x 256
+ * sparse kernel whose tile count leaves the device's last round of tiles partly
+ * idle run in stream-K form, as gemm_dense_ws does: the remainder tiles' K range
+ * is cut into equal pieces over all compute units, each piece leaves its partial
+ * sums in the workspace, and a second kernel adds them in K order and applies
+ * the epilogue (deterministic).  A scheduling choice of this library, not of the
+ * pages.
+ * workspace, workspace_bytes : as for gemm_dense_ws (16-byte aligned device
+ *                 memory, contents irrelevant on entry and unspecified after;
+ *                 NULL or too small: the call runs as gemm_sparse24).
+ *                 mcg_sparse24_workspace_bytes reports the plan's size: 256 KiB
+ *                 per piece, 0 without a stream-K plan.
+ */
+int gemm_sparse24_ws(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int64_t K,
+                     const void* A_compressed, int64_t lda_c, const uint32_t* A_index, int64_t ld_idx,
+                     const void* B, int64_t ldb, const void* C, void* D, int64_t ldc, int dtypeD,
+                     double alpha, double beta, void* workspace, int64_t workspace_bytes, void* stream);
+int64_t mcg_sparse24_workspace_bytes(int dtypeA, int layoutB, int64_t M, int64_t N, int64_t K,
+                                     const void* A_compressed, int64_t lda_c, const uint32_t* A_index,
+                                     int64_t ld_idx, const void* B, int64_t ldb);
+
+/*
  * compress24 -- 2:4 compressor on the device ("RDNA4 sparse WMMA builtins",
  * Structured sparsity (2:4 pattern): walk K in groups of four and keep the
  * two non-zero positions).

@@ -30,7 +30,7 @@ STATUS = {0: "MCG_SUCCESS", 1: "MCG_ERR_NULL_POINTER", 2: "MCG_ERR_INVALID_SIZE"
 
 # Every symbol include/mcg.h declares.
 EXPORTS = ("gemm_dense", "gemm_dense_ws", "gemm_dense_noalloc", "mcg_dense_noalloc_scratch_bytes",
-           "mcg_dense_workspace_bytes", "gemm_sparse24", "compress24", "compress24_host", "decompress24_host",
+           "mcg_dense_workspace_bytes", "gemm_sparse24_ws", "mcg_sparse24_workspace_bytes", "gemm_sparse24", "compress24", "compress24_host", "decompress24_host",
            "mcg_status_string",
            "mcg_version", "mcg_validate_dense", "mcg_validate_sparse24", "mcg_validate_compress24",
            "mcg_dense_path", "mcg_dense_splits", "mcg_sparse24_path", "mcg_mfma_eval", "mcg_mfma_eval_k")
@@ -60,6 +60,10 @@ _lib.mcg_dense_workspace_bytes.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _
 _lib.mcg_dense_workspace_bytes.restype = _i64
 _lib.gemm_sparse24.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                                _vp, _vp, _i64, _i32, _dbl, _dbl, _vp]
+_lib.gemm_sparse24_ws.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                  _vp, _vp, _i64, _i32, _dbl, _dbl, _vp, _i64, _vp]
+_lib.mcg_sparse24_workspace_bytes.argtypes = [_i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
+_lib.mcg_sparse24_workspace_bytes.restype = _i64
 _lib.compress24.argtypes = [_i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp]
 _lib.compress24_host.argtypes = [_i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
 _lib.decompress24_host.argtypes = [_i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
@@ -161,6 +165,25 @@ def gemm_sparse24(dtypeA, dtypeB, layoutB, M, N, K, A_compressed, lda_c, A_index
         _dt(dtypeA), _dt(dtypeB), _lay(layoutB), M, N, K, _ptr(A_compressed), lda_c, _ptr(A_index),
         ld_idx, _ptr(B), ldb, _ptr(C), _ptr(D), ldc, _dt(dtypeD), float(alpha), float(beta),
         _stream(stream)))
+
+
+def gemm_sparse24_ws(dtypeA, dtypeB, layoutB, M, N, K, A_compressed, lda_c, A_index, ld_idx, B, ldb,
+                     C, D, ldc, dtypeD, alpha=1.0, beta=0.0, workspace=None, workspace_bytes=0,
+                     stream=None) -> None:
+    """gemm_sparse24 with a device workspace for the stream-K form (a tensor,
+    whose byte size is taken when workspace_bytes is 0, or an address)."""
+    if isinstance(workspace, torch.Tensor) and not workspace_bytes:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("gemm_sparse24_ws", _lib.gemm_sparse24_ws(
+        _dt(dtypeA), _dt(dtypeB), _lay(layoutB), M, N, K, _ptr(A_compressed), lda_c, _ptr(A_index),
+        ld_idx, _ptr(B), ldb, _ptr(C), _ptr(D), ldc, _dt(dtypeD), float(alpha), float(beta),
+        _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def sparse24_workspace_bytes(dtypeA, layoutB, M, N, K, A_compressed, lda_c, A_index, ld_idx, B, ldb) -> int:
+    """Workspace bytes gemm_sparse24_ws uses for these operands (0: no stream-K form)."""
+    return _lib.mcg_sparse24_workspace_bytes(_dt(dtypeA), _lay(layoutB), M, N, K, _ptr(A_compressed), lda_c,
+                                             _ptr(A_index), ld_idx, _ptr(B), ldb)
 
 
 def compress24(dtype, M, K, A, lda, A_compressed, lda_c, A_index, ld_idx, d_violations=None,

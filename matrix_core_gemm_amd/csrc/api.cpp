@@ -278,13 +278,16 @@ int mcg_validate_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_
   return MCG_SUCCESS;
 }
 
-int gemm_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int64_t K,
-                  const void* A_compressed, int64_t lda_c, const uint32_t* A_index, int64_t ld_idx,
-                  const void* B, int64_t ldb, const void* C, void* D, int64_t ldc, int dtypeD,
-                  double alpha, double beta, void* stream) {
+// gemm_sparse24 and gemm_sparse24_ws: ws (ws_bytes) is the caller's workspace, or null.
+static int sparse_impl(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int64_t K,
+                       const void* A_compressed, int64_t lda_c, const uint32_t* A_index, int64_t ld_idx,
+                       const void* B, int64_t ldb, const void* C, void* D, int64_t ldc, int dtypeD,
+                       double alpha, double beta, void* ws, int64_t ws_bytes, void* stream) {
   int st = mcg_validate_sparse24(dtypeA, dtypeB, layoutB, M, N, K, A_compressed, lda_c, A_index,
                                  ld_idx, B, ldb, C, D, ldc, dtypeD, alpha, beta);
-  if (st != MCG_SUCCESS || M == 0 || N == 0) return st;
+  if (st != MCG_SUCCESS) return st;
+  if (ws != nullptr && (ws_bytes < 0 || !aligned_to(ws, 16))) return ws_bytes < 0 ? MCG_ERR_INVALID_SIZE : MCG_ERR_MISALIGNED;
+  if (M == 0 || N == 0) return st;
   st = check_arch();
   if (st != MCG_SUCCESS) return st;
   mcg::SparseArgs a{};
@@ -312,9 +315,34 @@ int gemm_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int
   const bool aligned = K == 0 || (aligned_to(A_compressed, 16) && aligned_to(B, 16) &&
                                   aligned_to(A_index, 16) && (lda_c * eb) % 16 == 0 &&
                                   (ldb * eb) % 16 == 0 && (ld_idx * 4) % 16 == 0);
-  if (mcg::sparse_fast_ok(dtypeA, layoutB, a))
+  if (mcg::sparse_fast_ok(dtypeA, layoutB, a)) {
+    if (ws != nullptr) {
+      const int64_t need = mcg::plan_sparse_streamk(dtypeA, a, current_num_cu());
+      if (need > 0 && need <= ws_bytes) {
+        a.ws = ws;
+        return hip_status(mcg::launch_sparse_fast_sk(dtypeA, dtypeB, layoutB, a, (hipStream_t)stream));
+      }
+      a.dp_tiles = a.sk_tiles = a.sk_wgs = 0;
+    }
     return hip_status(mcg::launch_sparse_fast(dtypeA, dtypeB, layoutB, a, (hipStream_t)stream));
+  }
   return hip_status(mcg::launch_sparse(dtypeA, dtypeB, layoutB, aligned, a, (hipStream_t)stream));
+}
+
+int gemm_sparse24(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int64_t K,
+                  const void* A_compressed, int64_t lda_c, const uint32_t* A_index, int64_t ld_idx,
+                  const void* B, int64_t ldb, const void* C, void* D, int64_t ldc, int dtypeD,
+                  double alpha, double beta, void* stream) {
+  return sparse_impl(dtypeA, dtypeB, layoutB, M, N, K, A_compressed, lda_c, A_index, ld_idx, B, ldb, C, D, ldc,
+                     dtypeD, alpha, beta, nullptr, 0, stream);
+}
+
+int gemm_sparse24_ws(int dtypeA, int dtypeB, int layoutB, int64_t M, int64_t N, int64_t K,
+                     const void* A_compressed, int64_t lda_c, const uint32_t* A_index, int64_t ld_idx,
+                     const void* B, int64_t ldb, const void* C, void* D, int64_t ldc, int dtypeD,
+                     double alpha, double beta, void* workspace, int64_t workspace_bytes, void* stream) {
+  return sparse_impl(dtypeA, dtypeB, layoutB, M, N, K, A_compressed, lda_c, A_index, ld_idx, B, ldb, C, D, ldc,
+                     dtypeD, alpha, beta, workspace, workspace_bytes, stream);
 }
 
 int mcg_validate_compress24(int dtype, int64_t M, int64_t K, const void* A, int64_t lda,
@@ -471,6 +499,18 @@ int mcg_dense_splits(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N,
   if (dtypeA < MCG_BF16 || dtypeA > MCG_FP8_E5M2) return 1;
   const bool can_split = (dtypeD == MCG_F32 || dtypeD == MCG_I32) && !(beta != 0.0 && C == D);
   return dense_plan(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb, can_split).splits;
+}
+
+int64_t mcg_sparse24_workspace_bytes(int dtypeA, int layoutB, int64_t M, int64_t N, int64_t K,
+                                     const void* A_compressed, int64_t lda_c, const uint32_t* A_index,
+                                     int64_t ld_idx, const void* B, int64_t ldb) {
+  if (dtypeA < MCG_BF16 || dtypeA > MCG_FP8_E5M2 || M <= 0 || N <= 0 || K <= 0) return 0;
+  if (mcg_sparse24_path(dtypeA, layoutB, M, N, K, A_compressed, lda_c, A_index, ld_idx, B, ldb) != 1) return 0;
+  mcg::SparseArgs a{};
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  return mcg::plan_sparse_streamk(dtypeA, a, current_num_cu());
 }
 
 int mcg_sparse24_path(int dtypeA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A_compressed,

@@ -58,16 +58,6 @@ constexpr int NSA = 2;       // LDS stages of A
 constexpr int NSB = 3;       // LDS stages of B
 constexpr int THREADS = 512;
 
-// Where an epilogue writes: D = alpha * acc + beta * C for the tile whose first
-// element is (m0, n0) of an M x N matrix with leading dimension ld (elements).
-struct EpiDst {
-  void* D;
-  const void* C;
-  int64_t ld, M, N, m0, n0;
-  float alpha, beta;
-  int alpha_i, beta_i, use_c, vec, out;
-};
-
 // TB: output tile TB x TB (256, or 128 for problems with too few 256 x 256 tiles to
 // fill the chip); each wavefront owns (TB / 2) x (TB / 4) outputs.  SK: the
 // stream-K form, whose workgroups each take a range of the K

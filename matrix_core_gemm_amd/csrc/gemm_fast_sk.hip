@@ -32,28 +32,31 @@ namespace {
 // fixed latency costs SK_FIXED_US.  Stream-K is taken when the K tiles it saves in
 // the last round outweigh its own cost.
 constexpr double SK_KT_US_256 = 0.75, SK_KT_US_128 = 0.4, SK_PIECE_US_256 = 0.1, SK_FIXED_US = 8.0;
+// the 256 x 256 sparse kernel: a kept-value stage of a whole round takes at least
+// SK_STAGE_US_SPARSE (bf16 about 2.4 us at 8192^3, 8-bit about 2.9)
+constexpr double SK_STAGE_US_SPARSE = 1.5;
 constexpr int64_t SK_MIN_ITERS = 4;  // K tiles per workgroup range at least
 }  // namespace
 
-int64_t plan_streamk(int dtA, DenseArgs& a, int num_cu, int tile) {
+// The plan for T tiles of tile x tile outputs with nk K units each (K tiles of
+// 128 bytes, or kept-value stages), kt_us per K unit of a whole round: fills the
+// sk_* and dp_tiles fields and returns the workspace bytes, or 0.
+template <class Args>
+static int64_t plan_core(Args& a, int64_t T, int64_t nk, int num_cu, int tile, double kt_us, int64_t min_iters) {
   a.dp_tiles = a.sk_tiles = a.sk_wgs = 0;
   a.sk_iters = 0;
   a.sk_period = 1;
-  if (tile != 256 && tile != 128) return 0;
   const int64_t G = num_cu > 0 ? num_cu : 256;
-  const int64_t eb = (dtA == DT_BF16 || dtA == DT_F16) ? 2 : 1;
-  const int64_t nk = (a.K * eb + fast::KTB - 1) / fast::KTB;
-  const int64_t T = ((a.M + tile - 1) / tile) * ((a.N + tile - 1) / tile);
   const int64_t R = T % G;
-  if (R == 0 || nk < 2 * SK_MIN_ITERS) return 0;
+  if (R == 0 || nk < 2 * min_iters) return 0;
   // Each remainder tile is cut into s equal pieces, s the largest divisor of nk
-  // with R s <= G and at least SK_MIN_ITERS K tiles per piece, so that every
+  // with R s <= G and at least min_iters K units per piece, so that every
   // workgroup takes exactly one piece and the workgroups of one XCD (taken
   // round-robin) walk the same K range of neighbouring tiles and share their
   // panels in L2.  (Ranges that cross tile boundaries balance the CUs better but
   // give every workgroup its own K offset: measured slower than whole tiles.)
   int64_t sp = 0;
-  for (int64_t c = std::min(G / R, nk / SK_MIN_ITERS); c >= 2; --c)
+  for (int64_t c = std::min(G / R, nk / min_iters); c >= 2; --c)
     if (nk % c == 0) {
       sp = c;
       break;
@@ -63,7 +66,7 @@ int64_t plan_streamk(int dtA, DenseArgs& a, int num_cu, int tile) {
   const int64_t wgs = R * sp;
   const int64_t pieces = wgs;
   const int64_t slot = (int64_t)tile * tile * 4;
-  const double saved = (double)(nk - L) * (tile == 256 ? SK_KT_US_256 : SK_KT_US_128);
+  const double saved = (double)(nk - L) * kt_us;
   const double cost = (double)pieces * SK_PIECE_US_256 * (double)slot / (256.0 * 256 * 4) + SK_FIXED_US;
   if (saved <= cost || T - R + wgs > 0x7fffffff) return 0;
   a.dp_tiles = (int)(T - R);
@@ -72,6 +75,32 @@ int64_t plan_streamk(int dtA, DenseArgs& a, int num_cu, int tile) {
   a.sk_iters = L;
   a.sk_period = nk / std::gcd(L, nk);
   return pieces * slot;
+}
+
+int64_t plan_streamk(int dtA, DenseArgs& a, int num_cu, int tile) {
+  if (tile != 256 && tile != 128) {
+    a.dp_tiles = a.sk_tiles = a.sk_wgs = 0;
+    return 0;
+  }
+  const int64_t eb = (dtA == DT_BF16 || dtA == DT_F16) ? 2 : 1;
+  const int64_t nk = (a.K * eb + fast::KTB - 1) / fast::KTB;
+  const int64_t T = ((a.M + tile - 1) / tile) * ((a.N + tile - 1) / tile);
+  return plan_core(a, T, nk, num_cu, tile, tile == 256 ? SK_KT_US_256 : SK_KT_US_128, SK_MIN_ITERS);
+}
+
+int64_t plan_sparse_streamk(int dtA, SparseArgs& a, int num_cu) {
+  const int64_t eb = (dtA == DT_BF16 || dtA == DT_F16) ? 2 : 1;
+  const int64_t nT = (a.K * eb + 255) / 256;  // kept-value stages of 128 bytes of kept values per row
+  const int64_t T = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+  return plan_core(a, T, nT, num_cu, 256, SK_STAGE_US_SPARSE, 2);
+}
+
+hipError_t launch_streamk_fixup(const DenseArgs& a, int64_t nk, bool int_acc, hipStream_t s) {
+  if (int_acc)
+    hipLaunchKernelGGL((fast::streamk_fixup_kernel<true, 256>), dim3((unsigned)a.sk_tiles, 64), dim3(256), 0, s, a, nk);
+  else
+    hipLaunchKernelGGL((fast::streamk_fixup_kernel<false, 256>), dim3((unsigned)a.sk_tiles, 64), dim3(256), 0, s, a, nk);
+  return hipGetLastError();
 }
 
 hipError_t launch_fast_sk(int dtA, int dtB, int la, int lb, const DenseArgs& a, hipStream_t s, int tile) {

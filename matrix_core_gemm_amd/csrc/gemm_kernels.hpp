@@ -66,6 +66,11 @@ struct SparseArgs {
   int use_c, vec_cd;
   int out;  // OUT_32 (binary32 / int32), OUT_BF16 or OUT_F16: format of C and D
   int tiles_m, tiles_n;
+  // stream-K form of the 256 x 256 sparse kernel, as in DenseArgs; pieces are
+  // counted in kept-value stages (128 dense k of 16-bit, 256 of 8-bit values)
+  int dp_tiles, sk_tiles, sk_wgs;
+  int64_t sk_iters, sk_period;
+  void* ws;
 };
 
 // binary64 GEMM (DGEMM); DT_F64 continues the input codes of arch_gfx950.hpp
@@ -144,6 +149,13 @@ int64_t plan_streamk(int dtA, DenseArgs& a, int num_cu, int tile = 256);
 hipError_t launch_fast_sk(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s,
                           int tile = 256);
 hipError_t launch_fast_mid_sk(int dtA, int dtB, int layoutA, int layoutB, const DenseArgs& a, hipStream_t s);
+// The fixup of a stream-K launch with 256 x 256 slots: a carries the plan, the
+// epilogue arguments and the workspace; nk counts the pieces' K units per tile.
+hipError_t launch_streamk_fixup(const DenseArgs& a, int64_t nk, bool int_acc, hipStream_t s);
+// Stream-K plan of the 256 x 256 sparse kernel (fills the sk_* and dp_tiles
+// fields of a), and its launch; workspace bytes as plan_streamk.
+int64_t plan_sparse_streamk(int dtA, SparseArgs& a, int num_cu);
+hipError_t launch_sparse_fast_sk(int dtA, int dtB, int layoutB, const SparseArgs& a, hipStream_t s);
 // The library's static stream-K scratch: STATIC_SCRATCH_BYTES per device; its
 // device address for the current device (looked up on the first call there).
 constexpr int64_t STATIC_SCRATCH_BYTES = (int64_t)32 << 20;

@@ -154,7 +154,10 @@ struct BHalfLoader {
   }
 };
 
-template <class Op, int LB>
+// SK: the stream-K form, whose workgroups each take a range of the kept-value
+// stages of the tiles after the first dp_tiles (which a launch of the whole-tile
+// form covers); see gemm_fast_sk.hip.
+template <class Op, int LB, bool SK = false>
 __global__ __launch_bounds__(SP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_sparse_fast_kernel(SparseArgs p) {
   constexpr int WTM = 4, WTN = 2;
@@ -181,13 +184,15 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   const int rbA = (q >> 1) * 128, rbB = (q & 1) * 128 + grp * 64;  // tile coordinates
   const int rbBh = (q & 1) * 64;                                    // row in this group's B half
   const int g = lane >> 5;
-  int tm, tn;
-  tile_coords<4>(p.tiles_m, p.tiles_n, tm, tn);
+  const int nT_all = (int)((p.K + SG::KA - 1) / SG::KA);  // kept-value stages of the problem
+
+  // One piece of work: kept-value stages [Tb, Tb + nT) of output tile (tm, tn),
+  // whose epilogue writes to d.
+  auto work = [&](int tm, int tn, int Tb, int nT, const EpiDst& d) {
   const int64_t m0 = (int64_t)tm * SP_BM, n0 = (int64_t)tn * SP_BN;
   const int64_t rows = min(p.M - m0, (int64_t)SP_BM);
   const int64_t Kc = p.K / 2;  // kept values per row
   const int nwords = (int)((p.K + 31) / 32);
-  const int nT = (int)((p.K + SG::KA - 1) / SG::KA);  // kept-value stages; 2 steps of KB dense k each
 
   auto stA = [&](int T) { return smem + (T & 1) * A_STAGE; };
   auto stI = [&](int T) { return smem + (T & 1) * A_STAGE + 32768; };
@@ -220,19 +225,19 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
     chunk_idx[i] = CPR == 2 ? (e % 2) ^ ((row >> 4) & 1) : 0;  // the chunk of the row kept at that position
     off_idx[i] = (uint32_t)(row * p.ld_idx * 4 + chunk_idx[i] * 16);
   }
-  auto issueA = [&](int T) { la.issue(stA(T), T, 4 * grp, 4, q); };
+  auto issueA = [&](int T) { la.issue(stA(T), Tb + T, 4 * grp, 4, q); };
   auto issueI = [&](int T) {
 #pragma unroll
     for (int i = 0; i < II; ++i) {
       // chunks that start past the last index word read zeros; a chunk that
       // straddles it reads the row's next words, which only cover groups past K
       // (their kept values are zero)
-      const uint32_t o = T * WPR + 4 * chunk_idx[i] < nwords ? off_idx[i] + (uint32_t)(T * IWB) : BUF_OOB;
+      const uint32_t o = (Tb + T) * WPR + 4 * chunk_idx[i] < nwords ? off_idx[i] + (uint32_t)((Tb + T) * IWB) : BUF_OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs_idx, (__attribute__((address_space(3))) void*)(stI(T) + (II * q + i) * 1024), 16, o, 0, 0, 0);
     }
   };
-  auto issueB = [&](int u) { lb.issue(stBh(1 - grp, u), u, q); };  // the other group's half
+  auto issueB = [&](int u) { lb.issue(stBh(1 - grp, u), 2 * Tb + u, q); };  // the other group's half
 
   acc_t acc[WTM][WTN];
 #pragma unroll
@@ -362,38 +367,115 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   // epilogue: the sparse (A) fragment is the instruction's first operand, so
   // element (i', j') of its 32 x 32 accumulator layout is D[m][n] with m = i',
   // n = j' within the block: block (i, j), register r holds
-  // D[m0 + rbA + 32 i + i'][n0 + rbB + 32 j + j'], (i', j') = ACC::coord(lane, r)
+  // D[em0 + rbA + 32 i + i'][en0 + rbB + 32 j + j'], (i', j') = ACC::coord(lane, r)
   using ACC = frag::Acc<frag::ACC_32x32>;
-  const bool interior = m0 + SP_BM <= p.M && n0 + SP_BN <= p.N;
+  const int64_t em0 = d.m0, en0 = d.n0;  // the tile's first element in the destination (D, or a workspace slot)
+  const bool interior = em0 + SP_BM <= d.M && en0 + SP_BN <= d.N;
 #pragma unroll
   for (int i = 0; i < WTM; ++i)
 #pragma unroll
     for (int j = 0; j < WTN; ++j) {
-      const int64_t n = n0 + rbB + 32 * j + ACC::coord(lane, 0).j;
+      const int64_t n = en0 + rbB + 32 * j + ACC::coord(lane, 0).j;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + rbA + 32 * i + ACC::coord(lane, r).i;
-        if (!interior && (m >= p.M || n >= p.N)) continue;
-        const int64_t off = m * p.ldc + n;
+        const int64_t m = em0 + rbA + 32 * i + ACC::coord(lane, r).i;
+        if (!interior && (m >= d.M || n >= d.N)) continue;
+        const int64_t off = m * d.ld + n;
         if constexpr (Op::INT_ACC) {
-          const uint32_t c = p.use_c ? (uint32_t)((const int*)p.C)[off] : 0u;
-          ((int*)p.D)[off] = (int)((uint32_t)p.alpha_i * (uint32_t)acc[i][j][r] + (uint32_t)p.beta_i * c);
+          const uint32_t c = d.use_c ? (uint32_t)((const int*)d.C)[off] : 0u;
+          ((int*)d.D)[off] = (int)((uint32_t)d.alpha_i * (uint32_t)acc[i][j][r] + (uint32_t)d.beta_i * c);
         } else {
-          combine_store(p.C, p.D, off, acc[i][j][r], p.alpha, p.beta, p.use_c, p.out);
+          combine_store(d.C, d.D, off, acc[i][j][r], d.alpha, d.beta, d.use_c, d.out);
         }
       }
     }
+  };  // work
+
+  if constexpr (!SK) {
+    // XCD-aware, grouped tile order over all tiles, or over the first dp_tiles
+    // tiles when the rest are left to the stream-K form
+    int tm, tn;
+    tile_coords_of<4>(blockIdx.x, p.dp_tiles > 0 ? p.dp_tiles : p.tiles_m * p.tiles_n, p.tiles_m, p.tiles_n, tm, tn);
+    work(tm, tn, 0, nT_all,
+         EpiDst{p.D, p.C, p.ldc, p.M, p.N, (int64_t)tm * SP_BM, (int64_t)tn * SP_BN, p.alpha, p.beta, p.alpha_i,
+                p.beta_i, p.use_c, p.vec_cd, p.out});
+  } else {
+    // Workgroup w takes kept-value stages [w L, (w + 1) L) of the tiles after the
+    // first dp_tiles, numbered tile by tile; a piece that is a whole tile is
+    // stored to D, any other piece stores its raw sums to its own workspace slot.
+    const int64_t w = blockIdx.x;
+    const int64_t L = p.sk_iters;
+    int64_t it = w * L;
+    const int64_t end = min(it + L, (int64_t)p.sk_tiles * nT_all);
+    int64_t piece = sk_first_piece(w, L, nT_all, p.sk_period);
+    for (int pc = 0; it < end; ++pc) {
+      const int64_t x = it / nT_all;
+      const int Tbeg = (int)(it - x * nT_all);
+      const int Tcnt = (int)min((int64_t)(nT_all - Tbeg), end - it);
+      int tm, tn;
+      {
+        int m, n;
+        grouped_tile<4>(p.dp_tiles + (int)x, p.tiles_m, p.tiles_n, m, n);
+        tm = __builtin_amdgcn_readfirstlane(m);
+        tn = __builtin_amdgcn_readfirstlane(n);
+      }
+      if (pc > 0) barrier_lds();  // the previous piece is done with the LDS
+      const bool whole = Tbeg == 0 && Tcnt == nT_all;
+      const EpiDst d = whole ? EpiDst{p.D, p.C, p.ldc, p.M, p.N, (int64_t)tm * SP_BM, (int64_t)tn * SP_BN, p.alpha,
+                                      p.beta, p.alpha_i, p.beta_i, p.use_c, p.vec_cd, p.out}
+                             : EpiDst{(char*)p.ws + piece * (int64_t)(SP_BM * SP_BN * 4), nullptr, SP_BN, SP_BM,
+                                      SP_BN, 0, 0, 1.0f, 0.0f, 1, 0, 0, 1, OUT_32};
+      work(tm, tn, Tbeg, Tcnt, d);
+      it += Tcnt;
+      ++piece;
+    }
+  }
 }
 
-template <class Op, int LB>
+template <class Op, int LB, bool SK = false>
 static hipError_t launch_sparse_fast_one(const SparseArgs& a0, hipStream_t s) {
   SparseArgs a = a0;
   a.tiles_m = (int)((a.M + SP_BM - 1) / SP_BM);
   a.tiles_n = (int)((a.N + SP_BN - 1) / SP_BN);
-  const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
-  if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_sparse_fast_kernel<Op, LB>), dim3((unsigned)blocks), dim3(SP_THREADS), 0, s, a);
-  return hipGetLastError();
+  const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+  if (tiles <= 0) return hipSuccess;
+  hipError_t e = hipSuccess;
+  if (!SK || a.dp_tiles > 0) {  // whole tiles: every tile, or the first dp_tiles
+    hipLaunchKernelGGL((gemm_sparse_fast_kernel<Op, LB, false>), dim3((unsigned)(SK ? a.dp_tiles : tiles)),
+                       dim3(SP_THREADS), 0, s, a);
+    e = hipGetLastError();
+  }
+  if constexpr (SK) {
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemm_sparse_fast_kernel<Op, LB, true>), dim3((unsigned)a.sk_wgs), dim3(SP_THREADS), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // the fixup of the dense form, on the sparse launch's epilogue arguments
+    DenseArgs f{};
+    f.C = a.C;
+    f.D = a.D;
+    f.M = a.M;
+    f.N = a.N;
+    f.ldc = a.ldc;
+    f.alpha = a.alpha;
+    f.beta = a.beta;
+    f.alpha_i = a.alpha_i;
+    f.beta_i = a.beta_i;
+    f.use_c = a.use_c;
+    f.vec_cd = a.vec_cd;
+    f.out = a.out;
+    f.tiles_m = a.tiles_m;
+    f.tiles_n = a.tiles_n;
+    f.dp_tiles = a.dp_tiles;
+    f.sk_tiles = a.sk_tiles;
+    f.sk_wgs = a.sk_wgs;
+    f.sk_iters = a.sk_iters;
+    f.sk_period = a.sk_period;
+    f.ws = a.ws;
+    const int64_t nT = (a.K + SpGeom<Op::EB>::KA - 1) / SpGeom<Op::EB>::KA;
+    e = launch_streamk_fixup(f, nT, Op::INT_ACC, s);
+  }
+  return e;
 }
 
 }  // namespace fast
@@ -423,22 +505,32 @@ bool sparse_fast_ok(int dtA, int layoutB, const SparseArgs& a) {
   return wa < lim && wi < lim && wb < lim && tiles <= 0x7fffffff;
 }
 
-template <class Op>
+template <class Op, bool SK>
 static hipError_t launch_sparse_fast_layouts(int layoutB, const SparseArgs& a, hipStream_t s) {
-  return layoutB == LAYOUT_K ? fast::launch_sparse_fast_one<Op, LAYOUT_K>(a, s)
-                             : fast::launch_sparse_fast_one<Op, LAYOUT_MN>(a, s);
+  return layoutB == LAYOUT_K ? fast::launch_sparse_fast_one<Op, LAYOUT_K, SK>(a, s)
+                             : fast::launch_sparse_fast_one<Op, LAYOUT_MN, SK>(a, s);
+}
+
+template <bool SK>
+static hipError_t launch_sparse_fast_sk_or_not(int dtA, int dtB, int layoutB, const SparseArgs& a, hipStream_t s) {
+  using namespace fast;
+  if (dtA == DT_BF16) return launch_sparse_fast_layouts<Sp32BF16, SK>(layoutB, a, s);
+  if (dtA == DT_F16) return launch_sparse_fast_layouts<Sp32F16, SK>(layoutB, a, s);
+  if (dtA == DT_I8) return launch_sparse_fast_layouts<Sp32I8, SK>(layoutB, a, s);
+  const int fa = f8fmt(dtA), fb = f8fmt(dtB);
+  if (fa == 0 && fb == 0) return launch_sparse_fast_layouts<Sp32F8<0, 0>, SK>(layoutB, a, s);
+  if (fa == 0 && fb == 1) return launch_sparse_fast_layouts<Sp32F8<0, 1>, SK>(layoutB, a, s);
+  if (fa == 1 && fb == 0) return launch_sparse_fast_layouts<Sp32F8<1, 0>, SK>(layoutB, a, s);
+  return launch_sparse_fast_layouts<Sp32F8<1, 1>, SK>(layoutB, a, s);
 }
 
 hipError_t launch_sparse_fast(int dtA, int dtB, int layoutB, const SparseArgs& a, hipStream_t s) {
-  using namespace fast;
-  if (dtA == DT_BF16) return launch_sparse_fast_layouts<Sp32BF16>(layoutB, a, s);
-  if (dtA == DT_F16) return launch_sparse_fast_layouts<Sp32F16>(layoutB, a, s);
-  if (dtA == DT_I8) return launch_sparse_fast_layouts<Sp32I8>(layoutB, a, s);
-  const int fa = f8fmt(dtA), fb = f8fmt(dtB);
-  if (fa == 0 && fb == 0) return launch_sparse_fast_layouts<Sp32F8<0, 0>>(layoutB, a, s);
-  if (fa == 0 && fb == 1) return launch_sparse_fast_layouts<Sp32F8<0, 1>>(layoutB, a, s);
-  if (fa == 1 && fb == 0) return launch_sparse_fast_layouts<Sp32F8<1, 0>>(layoutB, a, s);
-  return launch_sparse_fast_layouts<Sp32F8<1, 1>>(layoutB, a, s);
+  return launch_sparse_fast_sk_or_not<false>(dtA, dtB, layoutB, a, s);
+}
+
+hipError_t launch_sparse_fast_sk(int dtA, int dtB, int layoutB, const SparseArgs& a, hipStream_t s) {
+  if (a.sk_tiles <= 0 || a.ws == nullptr) return hipErrorInvalidValue;
+  return launch_sparse_fast_sk_or_not<true>(dtA, dtB, layoutB, a, s);
 }
 
 }  // namespace mcg

@@ -1,6 +1,7 @@
 // tile_order.hpp -- the order in which the pipelined kernels take output tiles,
-// and the numbering of stream-K pieces.  Plain integer functions for host and
-// device: the kernels, their launchers and the host-side tests use the same code.
+// the numbering of stream-K pieces, and where a piece's epilogue writes.  Plain
+// integer functions for host and device: the kernels, their launchers and the
+// host-side tests use the same code.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -28,6 +29,16 @@ __host__ __device__ inline void grouped_tile(int pid, int tiles_m, int tiles_n, 
 __host__ __device__ inline int64_t sk_first_piece(int64_t w, int64_t L, int64_t nk, int64_t P) {
   return w == 0 ? 0 : w + (w * L - 1) / nk - (w - 1) / P;
 }
+
+// Where an epilogue writes: D = alpha * acc + beta * C for the tile whose first
+// element is (m0, n0) of an M x N matrix with leading dimension ld (elements).
+struct EpiDst {
+  void* D;
+  const void* C;
+  int64_t ld, M, N, m0, n0;
+  float alpha, beta;
+  int alpha_i, beta_i, use_c, vec, out;
+};
 
 }  // namespace fast
 }  // namespace mcg

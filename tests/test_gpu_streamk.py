@@ -164,3 +164,70 @@ def test_streamk_deterministic_and_small_workspace_falls_back():
                                rows=rows, cols=cols)
     assert oracle.check_float(outs[0][rows, cols], ref, s, K)["ok"]
     assert oracle.check_float(plain[rows, cols], ref, s, K)["ok"]
+
+
+SPARSE_CASES = [  # dtA, dtB, layB, M, N, K, out, alpha, beta, D aliases C
+    ("bf16", "bf16", "k_contig", 2048, 2048, 8192, "f32", 1.5, 0.5, False),          # 64 tiles, 4 pieces each
+    ("i8", "i8", "mn_contig", 2048, 2048, 8192, "i32", 3, -2, False),                # int8, MN-contiguous B
+    ("f16", "f16", "k_contig", 4096, 4352, 8192, "f16", -0.75, 1.0, True),          # whole rounds + 16 tiles
+    ("e4m3", "e5m2", "k_contig", 2100, 2000, 8192, "f32", 1.0, 0.0, False),         # ragged, native fp8
+]
+
+
+@pytest.mark.parametrize("case", SPARSE_CASES, ids=["sparse_bf16", "sparse_i8_mn", "sparse_f16_f16out_alias",
+                                                    "sparse_fp8_ragged"])
+def test_sparse_streamk_against_oracle(case):
+    """gemm_sparse24_ws: every output of the stream-K tiles, one whole tile and
+    sampled others against the oracle (A compressed on the host by the oracle)."""
+    mcg = need_gpu()
+    dtA, dtB, layB, M, N, K, out, alpha, beta, alias = case
+    say(f"sparse stream-K {dtA}x{dtB} B {layB} {M}x{N}x{K} -> {out} alias={alias}")
+    i8 = dtA == "i8"
+    A = W.sparse24_dense(dtA, M, K, dist="int8" if i8 else "normal", seed=81)
+    B = W.operand("B", dtB, K, N, "int8" if i8 else "normal", layB, seed=82, fp8_scaled=not i8)
+    if not i8:
+        alpha = alpha * B.scale
+    v, ix, nv = oracle.compress24(dtA, A)
+    assert nv == 0
+    dv, di, dB = dev(v), dev(ix.view(np.int32)), dev(B.codes)
+    lda_c, ld_idx = K // 2, (K + 31) // 32
+    assert mcg.sparse24_path(dtA, layB, M, N, K, dv, lda_c, di, ld_idx, dB, B.ld) == 1
+    need = mcg.sparse24_workspace_bytes(dtA, layB, M, N, K, dv, lda_c, di, ld_idx, dB, B.ld)
+    assert need > 0 and need % (256 * 256 * 4) == 0
+    C = None
+    if out == "i32":
+        C = W.c_matrix(M, N, "int20", seed=83)
+        D = torch.full((M, N), -0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    elif out == "f32":
+        C = W.c_matrix(M, N, "normal", seed=83) if beta != 0 else None
+        D = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    else:
+        c16 = W.draw("normal", (M, N), 83).to(torch.float32).to(torch.float16)
+        C = c16.view(torch.int16).numpy().view(np.uint16)
+        D = torch.full((M, N), 0x7E00, dtype=torch.int32).to(torch.int16).to("cuda")
+    dC = None if C is None else dev(C.view(np.int16) if out == "f16" else C)
+    if alias:
+        D = dC
+    ws = workspace(need)
+    mcg.gemm_sparse24_ws(dtA, dtB, layB, M, N, K, dv, lda_c, di, ld_idx, dB, B.ld, dC, D, N, out, alpha, beta,
+                         workspace=ws)
+    torch.cuda.synchronize()
+    d = D.cpu().numpy()
+    sk, first = remainder_tiles(M, N, num_cu(), 256)
+    r1, c1 = tile_coords(sk + [first], M, N, 256)
+    r2, c2 = W.sample_coords(M, N, n_random=2048, full_rows=(M - 1,), full_cols=(N - 1,))
+    rows, cols = np.concatenate([r1, r2]), np.concatenate([c1, c2])
+    say(f"  {len(sk)} stream-K tiles, {need // (256 * 256 * 4)} pieces, {len(rows)} outputs compared")
+    ref, s = oracle.gemm_sparse24(dtA, dtB, layB, M, N, K, v, ix, B.codes, B.ld, C, N, alpha, beta,
+                                  rows=rows, cols=cols, out=out if out in ("f16", "bf16") else "f32")
+    if i8:
+        r = oracle.check_exact(d[rows, cols], ref)
+    else:
+        if out == "f16":
+            dec = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.float16).double().numpy()
+            got, cc = dec(d)[rows, cols], dec(C)[rows, cols]
+        else:
+            got, cc = d[rows, cols], None if C is None else C[rows, cols]
+        r = oracle.check_float(got, ref, s, K, alpha, beta=beta, c=cc, out=out if out == "f16" else "f32")
+    say("  ", {k: v for k, v in r.items() if k != "worst"})
+    assert r["ok"], r
