@@ -113,3 +113,22 @@ def test_gemm_dense_ws_argument_errors():
     bad = list(args)
     bad[4] = -1
     assert lib.gemm_dense_ws(*bad, 0x1000, 1 << 20, None) == lib.mcg_validate_dense(*bad)
+
+
+def _sws(mcg, dt, M, N, K):
+    return mcg.sparse24_workspace_bytes(dt, "k_contig", M, N, K, 0x1000, K // 2, 0x1000, (K + 31) // 32, 0x1000, K)
+
+
+def test_sparse_workspace_plan():
+    mcg = pytest.importorskip("matrix_core_gemm_amd")
+    slot = 256 * 256 * 4
+    # 2048^2 x 8192 bf16: 64 tiles of 256 x 256, 64 kept-value stages each, cut in 4
+    assert _sws(mcg, "bf16", 2048, 2048, 8192) == 256 * slot
+    # 1536^2: 36 tiles, at most 7 pieces each, 4 divides 64 stages: 144 pieces
+    assert _sws(mcg, "bf16", 1536, 1536, 8192) == 144 * slot
+    # int8: 256 dense k per stage, 2048^2 x 8192 has 32 stages per tile, cut in 4
+    assert _sws(mcg, "i8", 2048, 2048, 8192) == 256 * slot
+    # whole rounds, too little to gain, or not the 256 x 256 sparse kernel
+    assert _sws(mcg, "bf16", 8192, 8192, 8192) == 0
+    assert _sws(mcg, "bf16", 2048, 2048, 2048) == 0
+    assert _sws(mcg, "bf16", 200, 2048, 8192) == 0
