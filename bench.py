@@ -19,6 +19,7 @@ synthetic workload:
   gemm_dense_ws bf16 7168^3, 6144^3, 5120^3, 1024 x 2048 x 8192, 1280 x 1280 x
               8192 (shapes whose last round of tiles is short: the stream-K form
               where the plan takes it; leading blocks of the 8192^2 operands)
+  gemm_sparse24_ws bf16 2048 x 2048 x 8192 (the 2:4 stream-K form)
 Each call (or batch) is bracketed by HIP events recorded on the stream it is
 launched on, so every kernel's average duration is measured live.
 
@@ -56,8 +57,8 @@ SMALL_BATCH = 50  # launches of the 256^3 workload per event pair
 KERNEL_SOURCES = ("gemm_fast_kernel.hpp", "gemm_fast.hip", "fast_tiles.hpp", "tile_order.hpp", "arch_gfx950.hpp",
                   "frag_layout.hpp")
 TRAFFIC_MEASURED = {
-    "sources_sha256": "6761e257d9a30d12994065d984d52bda0cfac127fe5010d03cb7e213857e0412",
-    "read_bytes": 1831 * 2**20, "write_bytes": 256 * 2**20,
+    "sources_sha256": "64d7d2972459008ad4bc2ffa05bd7b75c27f53d3f41f9a5c965cbaebfab4a076",
+    "read_bytes": 1839 * 2**20, "write_bytes": 256 * 2**20,
 }
 
 LAYOUT_NAMES = {("k_contig", "k_contig"): "Arow_Bcol", ("k_contig", "mn_contig"): "Arow_Brow",
@@ -239,6 +240,17 @@ def main():
                         alpha=1 if dt == "i8" else eb.sB, beta=0, dense=dense,
                         peak=PEAK["i8" if dt == "i8" else "fp8"], speak=SPARSE_PEAK["i8" if dt == "i8" else "fp8"],
                         unit="TOPS" if dt == "i8" else "TFLOP/s")
+    # 2:4 bf16 2048^2 x 8192 on gemm_sparse24_ws (stream-K form): leading blocks
+    # of the 8192^3 entry's compressed A (lda_c = n / 2, ld_idx = n / 32) and B
+    if want("sparse24_2048x2048x8192"):
+        m_, n_, k_ = 2048, 2048, 8192
+        es = E["sparse24"]
+        need = mcg.sparse24_workspace_bytes("bf16", "k_contig", m_, n_, k_, vals, n // 2, idx, n // 32, es.B, n)
+        E["sparse24_2048x2048x8192"] = Entry(
+            "sparse24_2048x2048x8192", "sparse", dtA="bf16", dtB="bf16", M=m_, N=n_, K=k_, vals=vals, idx=idx,
+            B=es.B, hB=es.hB, ldb=n, D=D.view(-1)[:m_ * n_].view(m_, n_), out="f32", alpha=1.0, beta=0.0,
+            dense=None, peak=PEAK["bf16"], speak=SPARSE_PEAK["bf16"], unit="TFLOP/s", ws=wsbuf, ws_bytes=need,
+            lda_c=n // 2, ld_idx=n // 32)
     # skinny problems: the wide operand (4n x n bf16 ~ N(0,1)) drawn on the device
     g = torch.Generator(device="cuda").manual_seed(W.SEED_A)
     Wide = torch.randn((4 * n, n), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
@@ -264,7 +276,7 @@ def main():
     s = stream.cuda_stream
 
     def call(e):
-        if getattr(e, "ws", None) is not None:
+        if e.kind == "dense" and getattr(e, "ws", None) is not None:
             mcg.gemm_dense_ws(e.dtA, e.dtB, e.layA, e.layB, e.M, e.N, e.K, e.A, e.lda, e.B, e.ldb, e.C, e.D, e.N,
                               e.out, e.alpha, e.beta, e.sA, e.sB, workspace=e.ws, workspace_bytes=e.ws_bytes,
                               stream=s)
@@ -273,6 +285,10 @@ def main():
                            e.out, e.alpha, e.beta, e.sA, e.sB, stream=s)
         elif e.kind == "compress":
             mcg.compress24(e.dt, e.M, e.K, e.A, e.K, e.vals, e.K // 2, e.idx, e.K // 32, None, stream=s)
+        elif e.kind == "sparse" and getattr(e, "ws", None) is not None:
+            mcg.gemm_sparse24_ws(e.dtA, e.dtB, "k_contig", e.M, e.N, e.K, e.vals, e.lda_c, e.idx, e.ld_idx, e.B,
+                                 e.ldb, None, e.D, e.N, e.out, e.alpha, e.beta, workspace=e.ws,
+                                 workspace_bytes=e.ws_bytes, stream=s)
         elif e.kind == "sparse":
             mcg.gemm_sparse24(e.dtA, e.dtB, "k_contig", e.M, e.N, e.K, e.vals, e.K // 2, e.idx, e.K // 32, e.B,
                               e.ldb, None, e.D, e.N, e.out, e.alpha, e.beta, stream=s)
@@ -283,7 +299,8 @@ def main():
     order = ["bf16", "f16", "bf16_Arow_Brow", "bf16_Acol_Bcol", "bf16_Acol_Brow", "f16_Arow_Brow",
              "f16_Acol_Bcol", "f16_Acol_Brow", "bf16_256", "i8_4096", "i8", "e4m3xe4m3", "e4m3xe5m2",
              "compress24", "sparse24", "bf16_out", "skinny_n16", "skinny_m16", "sparse24_i8", "sparse24_e4m3",
-             "f64", "bf16_7168", "bf16_6144", "bf16_5120", "bf16_1024x2048x8192", "bf16_1280x1280x8192"]
+             "f64", "bf16_7168", "bf16_6144", "bf16_5120", "bf16_1024x2048x8192", "bf16_1280x1280x8192",
+             "sparse24_2048x2048x8192"]
     names = [x for x in order if x in E and (only is None or x in only or x == "compress24" and "sparse24" in only)]
     ev = {x: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)] for x in names}
@@ -324,6 +341,9 @@ def main():
                  "frac_of_sparse_peak": tf / e.speak, "sparse_peak": e.speak, "frac_of_dense_peak": tf / e.peak}
             if e.dense in ms:
                 d[f"vs_dense_{e.dense}"] = tf / (2.0 * e.M * e.N * e.K / (ms[e.dense] * 1e-3) / 1e12)
+            if getattr(e, "ws", None) is not None:
+                d["MxNxK"] = (e.M, e.N, e.K)
+                d["stream_k_workspace_MiB"] = e.ws_bytes / 2**20
             per[x] = d
         else:
             per[x] = {e.unit: tf, "ms": ms[x], "peak": e.peak, "frac_of_peak": tf / e.peak,
