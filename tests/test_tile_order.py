@@ -132,3 +132,14 @@ def test_sparse_workspace_plan():
     assert _sws(mcg, "bf16", 8192, 8192, 8192) == 0
     assert _sws(mcg, "bf16", 2048, 2048, 2048) == 0
     assert _sws(mcg, "bf16", 200, 2048, 8192) == 0
+
+
+def test_gemm_sparse24_ws_argument_errors():
+    mcg = pytest.importorskip("matrix_core_gemm_amd")
+    lib = mcg.lib()
+    args = (0, 0, 0, 256, 256, 256, 0x1000, 128, 0x1000, 8, 0x1000, 256, None, 0x1000, 256, 5, 1.0, 0.0)
+    assert lib.gemm_sparse24_ws(*args, 0x1008, 1 << 20, None) == 5   # workspace not 16-byte aligned
+    assert lib.gemm_sparse24_ws(*args, 0x1000, -1, None) == 2        # negative size
+    bad = list(args)
+    bad[5] = 6  # K not a multiple of 4
+    assert lib.gemm_sparse24_ws(*bad, 0x1000, 1 << 20, None) == lib.mcg_validate_sparse24(*bad) == 2
