@@ -37,9 +37,9 @@
 //     so that the workgroups resident on one XCD cover a compact block of tiles.
 //   - 128 x 128 form: the two wavefronts of a SIMD cover the same 64 x 64
 //     quadrant and split every K tile (one half each), so a phase holds 8
-//     instructions and a K tile 2 barriers; 3 stages of A and of B (16 KiB each)
-//     with a prefetch distance of 2 tiles; at the end each wave hands its partner
-//     the 32-row block the partner stores, through LDS.  96 KiB of LDS: one
+//     instructions and a K tile 2 barriers; 4 stages of A and of B (16 KiB each)
+//     with a prefetch distance of 3 tiles; at the end each wave hands its partner
+//     the 32-row block the partner stores, through LDS.  128 KiB of LDS: one
 //     workgroup per CU.  The host takes it for problems with too few 256 x 256
 //     tiles when its cost model puts it ahead of the general kernel.
 // Preconditions (checked on the host): 16-byte aligned operands, K * elem_bytes
@@ -76,7 +76,11 @@ void gemm_fast_kernel(DenseArgs p) {
   // the quadrant's columns over all of K
   constexpr bool KS = TB == 128;
   constexpr int WTM = TB / 64, WTN = KS ? 2 : TB / 128;  // 32 x 32 instruction tiles per wave
-  constexpr int NA = KS ? 3 : NSA;      // LDS stages of A (KS: prefetch distance 2 for both)
+  // KS: prefetch distance KPD for both operands (KPD + 1 stages each, 128 KiB of LDS;
+  // measured 3-15% faster than distance 2 over 1024..3072-row outputs, distance 4 slower)
+  constexpr int KPD = 3;
+  constexpr int NA = KS ? KPD + 1 : NSA;  // LDS stages of A
+  constexpr int NB = KS ? KPD + 1 : NSB;  // LDS stages of B
   using GA = Geom<EB, LA, BM, KTB>;
   using GB = Geom<EB, LB, BN, KTB>;
   using RA = Reader<EB, LA, BM, KTB>;
@@ -92,7 +96,7 @@ void gemm_fast_kernel(DenseArgs p) {
   constexpr int LH = LdA::INSTR / 2;  // loads per wave, operand and half stage (one group's share)
   static_assert(LdA::INSTR == LdB::INSTR && (LH == 4 || LH == 2), "vmcnt bookkeeping");
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[(NA + NSB) * SB];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[(NA + NB) * SB];
   lds_char* smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -127,7 +131,7 @@ void gemm_fast_kernel(DenseArgs p) {
     for (int j = 0; j < WTN; ++j) acc[i][j] = acc_t{};
 
   auto stA = [&](int kt) { return smem + (KS ? kt % NA : kt & 1) * SB; };
-  auto stB = [&](int kt) { return smem + NA * SB + (kt % NSB) * SB; };
+  auto stB = [&](int kt) { return smem + NA * SB + (kt % NB) * SB; };
   // this group's half (LH of the 2 LH load instructions per wave) of operand X of K tile kt
   const int ihalf = LH * grp;
   auto issueA = [&](int kt) { la.issue(stA(kt), kb + kt, ihalf, LH, q); };
@@ -204,37 +208,39 @@ void gemm_fast_kernel(DenseArgs p) {
   // DMA of tiles at or beyond nk read nothing and fill their stage with zeros.
   if constexpr (KS) {
     // Group g reads half g of K tile t in slot 2t - 1 + g and multiplies it in the
-    // next slot.  Each memory phase issues this wave's shares of A(t+2) and B(t+2)
-    // into the stages of tile t-1 (last read in slot 2t - 2); at the end of slot 2t
-    // each wave waits until only those newest 2 LH loads are in flight, so tile t+1
-    // is complete from slot 2t + 1.
-    issueA(0);
-    issueB(0);
-    issueA(1);
-    issueB(1);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LH) : "memory");  // own shares of tile 0
+    // next slot.  Each memory phase issues this wave's shares of A(t+KPD) and
+    // B(t+KPD) into the stages of tile t-1 (stage index mod KPD + 1; last read in
+    // slot 2t - 2); at the end of slot 2t each wave waits until only the loads of
+    // tiles t+2 .. t+KPD ((KPD - 1) 2 LH) are in flight, so tile t+1 is complete
+    // from slot 2t + 1.
+#pragma unroll
+    for (int t0 = 0; t0 < KPD; ++t0) {
+      issueA(t0);
+      issueB(t0);
+    }
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((KPD - 1) * 2 * LH) : "memory");  // own shares of tile 0
     barrier_lds();
     if (grp == 0) {
       for (int t = 0; t < nk; ++t) {
         __builtin_amdgcn_sched_barrier(0);
-        issueA(t + 2);
-        issueB(t + 2);
+        issueA(t + KPD);
+        issueB(t + KPD);
         read_frags(t, 0);  // slot 2t - 1
         barrier_lds();
         __builtin_amdgcn_sched_barrier(0);
         multiply();  // slot 2t
         __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LH) : "memory");  // own shares of tile t+1
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((KPD - 1) * 2 * LH) : "memory");  // own shares of tile t+1
         barrier_lds();
       }
     } else {
       barrier_lds();  // slot -1
       for (int t = 0; t < nk; ++t) {
         __builtin_amdgcn_sched_barrier(0);
-        issueA(t + 2);
-        issueB(t + 2);
+        issueA(t + KPD);
+        issueB(t + KPD);
         read_frags(t, 1);  // slot 2t
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LH) : "memory");  // own shares of tile t+1
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((KPD - 1) * 2 * LH) : "memory");  // own shares of tile t+1
         barrier_lds();
         __builtin_amdgcn_sched_barrier(0);
         multiply();  // slot 2t + 1
