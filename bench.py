@@ -124,6 +124,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="oracle time for the headline workload's CPU baseline (others: a fifth)")
     ap.add_argument("--only", default="", help="comma list of entries to run (profiling)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the matrix-core rate probe on each entry's operand bits")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -355,6 +357,63 @@ def main():
     head = "bf16" if "bf16" in names else names[0]
     value = per[head].get("TFLOP/s", per[head].get("TOPS", per[head].get("GB/s")))
 
+    # ---------------------------------------------------------------- matrix-core ceiling
+    # The published peaks hold at the peak clock; under full matrix-core load the
+    # clock depends on the operand bits.  mcg_mfma_probe runs each entry's
+    # instruction in the kernels' arrangement on fragments of that entry's own
+    # operands, with no other traffic: the rate no data-movement schedule can
+    # exceed for those bits (after the timed steps, outside their events).
+    ceiling = None
+    if not args.no_ceiling:
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
+        sink = torch.empty(ncu * 512, device="cuda")
+        clocks = torch.zeros(2 * ncu, dtype=torch.int64, device="cuda")
+        # dense k of one instruction: mfma 32x32x{16,32,64}; smfmac 32x32x{32,64,64}
+        kd = {0: {"bf16": 16, "f16": 16, "i8": 32, "e4m3": 64, "e5m2": 64},
+              1: {"bf16": 32, "f16": 32, "i8": 64, "e4m3": 64, "e5m2": 64}}
+        instr = 16384
+        cache = {}
+
+        def probe(dtA, dtB, sparse, a, b, idx):
+            key = (dtA, dtB, sparse, a.data_ptr(), b.data_ptr())
+            if key not in cache:
+                times = []
+                with torch.cuda.stream(stream):
+                    mcg.mfma_probe(dtA, dtB, sparse, a, b, idx, instr, ncu, sink, clocks, stream=s)
+                    for _ in range(3):
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        mcg.mfma_probe(dtA, dtB, sparse, a, b, idx, instr, ncu, sink, clocks, stream=s)
+                        e1.record(stream)
+                        times.append((e0, e1))
+                torch.cuda.synchronize()
+                t = sorted(a_.elapsed_time(b_) for a_, b_ in times)[1] * 1e-3
+                c = clocks.view(ncu, 2).double().cpu()
+                flops = ncu * 8 * instr * 2 * 32 * 32 * kd[sparse][dtA]
+                cache[key] = (flops / t / 1e12, float((c[:, 0] / c[:, 1]).mean()) * 0.1)
+            return cache[key]
+
+        for x in names:
+            e = E[x]
+            if e.kind == "dense" and e.dtA in kd[0]:
+                rate, ghz = probe(e.dtA, e.dtB, 0, e.A, e.B, None)
+                got = per[x][e.unit]
+            elif e.kind == "sparse":
+                rate, ghz = probe(e.dtA, e.dtB, 1, e.vals, e.B, e.idx)
+                got = per[x][f"{e.unit}_dense_equiv"]
+            else:
+                continue
+            pk = e.speak if e.kind == "sparse" else e.peak
+            per[x]["mfma_ceiling"] = {"value": rate, "unit": e.unit + ("_dense_equiv" if e.kind == "sparse" else ""),
+                                      "clock_ghz": ghz, "frac_of_peak": rate / pk}
+            per[x]["frac_of_ceiling"] = got / rate
+        if head in per and "mfma_ceiling" in per[head]:
+            ceiling = dict(per[head]["mfma_ceiling"])
+            ceiling.update({"achieved_frac_of_ceiling": per[head]["frac_of_ceiling"],
+                            "probe": f"mcg_mfma_probe: {instr} instructions per wavefront, {ncu} workgroups "
+                                     "of 8 wavefronts, fragments from the entry's own operands"})
+        log(f"matrix-core ceiling on the headline operands: {ceiling}")
+
     # ---------------------------------------------------------------- parity
     # Every entry once more; sampled outputs against the oracle (the acceptance
     # test of the parity tests: the float bound, or bit-exact integers / codes).
@@ -521,6 +580,7 @@ def main():
                      "kernel": "mcg::fast::gemm_fast_kernel<BF16, 0, 0, 256> (256x256 tile, 8-wave ping-pong)",
                      "kernel_ms": ms.get(head)},
         "cpu_baseline": cpu,
+        "mfma_ceiling": ceiling,
         "parity": parity,
         "per_dtype": per,
     }

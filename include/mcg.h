@@ -395,6 +395,47 @@ int mcg_mfma_eval(int dtype, int shape, int64_t n, const void* a, const void* b,
 /* Elements per test vector for mcg_mfma_eval (0 if unsupported). */
 int mcg_mfma_eval_k(int dtype, int shape);
 
+/*
+ * mcg_mfma_probe -- sustained matrix-core rate on given operand bits (a
+ * measurement aid for the GEMM roofline; computes no GEMM).
+ *
+ * The published peak of an instruction ("CDNA3 dense MFMA builtins",
+ * Instruction throughput: operations per instruction x instructions per cycle
+ * x CUs x clock) assumes the peak clock; under full matrix-core load the
+ * gfx950 clock depends on the operand bits.  The probe runs the instructions
+ * of the GEMM kernels (mfma 32x32x16 bf16/f16, 32x32x32 i8, 32x32x64 fp8; for
+ * 2:4 the smfmac of "RDNA4 sparse WMMA builtins", Structured sparsity) in their
+ * arrangement -- num_wg workgroups of 8 wavefronts, one per CU, two wavefronts
+ * per SIMD alternating between workgroup barriers, 16 instructions per
+ * wavefront and phase on a 4 x 2 grid of 32 x 32 accumulators -- on fragments
+ * loaded once, with no other memory traffic.  Its rate bounds what any data
+ * movement schedule can reach with those operand bits.
+ *
+ * dtypeA/B        : as for gemm_dense (sparse == 0: BF16xBF16, F16xF16,
+ *                   I8xI8, any FP8 pair) or gemm_sparse24 (sparse == 1).
+ * a, b            : DEVICE operand bytes (for 2:4: kept values and dense B),
+ *                   16-byte aligned, at least 65536 readable bytes each; lane
+ *                   l of wavefront w of workgroup g takes its fragments from
+ *                   the 128 bytes at ((4096 g) mod 32768) + 64 (64 w + l).
+ * idx             : DEVICE 2:4 index words (sparse == 1 only; 16-byte
+ *                   aligned, 65536 readable bytes), else ignored.
+ * instr_per_wave  : matrix instructions per wavefront, a positive multiple of
+ *                   16, at most 2^24.
+ * num_wg          : workgroups (the CU count fills the chip once), 1..65536.
+ * sink            : DEVICE float[num_wg * 512], receives each thread's sum of
+ *                   its accumulators (keeps the work live; with every operand
+ *                   byte of the 16-bit kinds equal to bf16/f16 1.0 it is
+ *                   256 * instr_per_wave exactly).
+ * clocks          : DEVICE int64[2 * num_wg]: per workgroup, shader-clock
+ *                   cycles and 100 MHz reference ticks between its first and
+ *                   last matrix phase (s_memtime, s_memrealtime).
+ * Errors: MCG_ERR_UNSUPPORTED_DTYPE, MCG_ERR_INVALID_SIZE, MCG_ERR_NULL_POINTER,
+ * MCG_ERR_MISALIGNED, MCG_ERR_UNSUPPORTED_ARCH, MCG_ERR_HIP.  Asynchronous on
+ * stream; the caller times it (one launch).
+ */
+int mcg_mfma_probe(int dtypeA, int dtypeB, int sparse, const void* a, const void* b, const void* idx,
+                   int64_t instr_per_wave, int num_wg, float* sink, int64_t* clocks, void* stream);
+
 /* Human-readable name of an mcg_status value (static storage). */
 const char* mcg_status_string(int status);
 

@@ -33,7 +33,8 @@ EXPORTS = ("gemm_dense", "gemm_dense_ws", "gemm_dense_noalloc", "mcg_dense_noall
            "mcg_dense_workspace_bytes", "gemm_sparse24_ws", "mcg_sparse24_workspace_bytes", "gemm_sparse24", "compress24", "compress24_host", "decompress24_host",
            "mcg_status_string",
            "mcg_version", "mcg_validate_dense", "mcg_validate_sparse24", "mcg_validate_compress24",
-           "mcg_dense_path", "mcg_dense_splits", "mcg_sparse24_path", "mcg_mfma_eval", "mcg_mfma_eval_k")
+           "mcg_dense_path", "mcg_dense_splits", "mcg_sparse24_path", "mcg_mfma_eval", "mcg_mfma_eval_k",
+           "mcg_mfma_probe")
 
 
 class MCGError(RuntimeError):
@@ -81,6 +82,7 @@ _lib.mcg_dense_splits.argtypes = [_i32, _i32, _i32, _i64, _i64, _i64, _vp, _i64,
 _lib.mcg_sparse24_path.argtypes = [_i32, _i32, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
 _lib.mcg_mfma_eval.argtypes = [_i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp]
 _lib.mcg_mfma_eval_k.argtypes = [_i32, _i32]
+_lib.mcg_mfma_probe.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp]
 
 
 def lib():
@@ -270,3 +272,13 @@ def mfma_eval(dtype, shape, n, a, b, c, d, stream=None) -> None:
     instruction fed with a[t*k:], b[t*k:] and c[t] (see mcg.h)."""
     _check("mcg_mfma_eval", _lib.mcg_mfma_eval(_dt(dtype), int(shape), n, _ptr(a), _ptr(b), _ptr(c), _ptr(d),
                                                _stream(stream)))
+
+
+def mfma_probe(dtypeA, dtypeB, sparse, a, b, idx, instr_per_wave, num_wg, sink, clocks, stream=None) -> None:
+    """Matrix-core rate probe on the operand bits of a, b (and idx for 2:4): the
+    GEMM kernels' instructions on fragments loaded once, no other traffic (see
+    mcg.h).  sink: float32 tensor of num_wg * 512; clocks: int64 tensor of
+    2 * num_wg (shader cycles, 100 MHz ticks per workgroup)."""
+    _check("mcg_mfma_probe", _lib.mcg_mfma_probe(_dt(dtypeA), _dt(dtypeB), int(sparse), _ptr(a), _ptr(b),
+                                                 _ptr(idx), int(instr_per_wave), int(num_wg), _ptr(sink),
+                                                 _ptr(clocks), _stream(stream)))

@@ -17,8 +17,8 @@ LIB = os.path.join(HERE, "_libmcg.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["gemm_dense.hip", "gemm_skinny_n.hip", "gemm_skinny_m.hip", "gemm_stream.hip", "gemm_fast.hip", "gemm_fast_mid.hip", "gemm_fast_sk.hip", "gemm_fast_mid_sk.hip", "gemm_sparse.hip",
-           "gemm_sparse_fast.hip", "gemm_f64.hip", "numerics.hip", "api.cpp"]
-HEADERS = ["arch_gfx950.hpp", "frag_layout.hpp", "tile_io.hpp", "fast_tiles.hpp", "tile_order.hpp", "gemm_fast_kernel.hpp", "gemm_kernels.hpp", "dense_general.hpp"]
+           "gemm_sparse_fast.hip", "gemm_f64.hip", "numerics.hip", "mfma_probe.hip", "api.cpp"]
+HEADERS = ["arch_gfx950.hpp", "frag_layout.hpp", "tile_io.hpp", "fast_tiles.hpp", "tile_order.hpp", "gemm_fast_kernel.hpp", "gemm_kernels.hpp", "dense_general.hpp", "sparse_ops.hpp"]
 
 # Packed fp32 VALU forms are disabled for all device code (hipcc's host pass
 # reports the feature as unknown, which is harmless).

@@ -566,6 +566,24 @@ int mcg_mfma_eval(int dtype, int shape, int64_t n, const void* a, const void* b,
       mcg::launch_mfma_eval(dtype == MCG_F64 ? mcg::DT_F64 : dtype, shape, a, b, c, d, n, (hipStream_t)stream));
 }
 
+int mcg_mfma_probe(int dtypeA, int dtypeB, int sparse, const void* a, const void* b, const void* idx,
+                   int64_t instr_per_wave, int num_wg, float* sink, int64_t* clocks, void* stream) {
+  if (dtypeA < 0 || dtypeA > MCG_FP8_E5M2 || dtypeB < 0 || dtypeB > MCG_FP8_E5M2 ||
+      !mcg::mfma_probe_supported(dtypeA, dtypeB, sparse))
+    return MCG_ERR_UNSUPPORTED_DTYPE;
+  if (instr_per_wave <= 0 || instr_per_wave % 16 != 0 || instr_per_wave > ((int64_t)1 << 24) || num_wg <= 0 ||
+      num_wg > 65536)
+    return MCG_ERR_INVALID_SIZE;
+  if (!a || !b || !sink || !clocks || (sparse && !idx)) return MCG_ERR_NULL_POINTER;
+  if (!aligned_to(a, 16) || !aligned_to(b, 16) || (sparse && !aligned_to(idx, 16)) || !aligned_to(sink, 4) ||
+      !aligned_to(clocks, 8))
+    return MCG_ERR_MISALIGNED;
+  int st = check_arch();
+  if (st != MCG_SUCCESS) return st;
+  return hip_status(mcg::launch_mfma_probe(dtypeA, dtypeB, sparse, a, b, sparse ? idx : nullptr, instr_per_wave,
+                                           num_wg, sink, clocks, (hipStream_t)stream));
+}
+
 int mcg_version(void) { return kVersion; }
 
 }  // extern "C"

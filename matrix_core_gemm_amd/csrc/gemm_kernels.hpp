@@ -167,5 +167,11 @@ hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s);
 int mfma_eval_k(int dt, int shape);
 hipError_t launch_mfma_eval(int dt, int shape, const void* a, const void* b, const void* c, void* d,
                             int64_t n, hipStream_t s);
+// Matrix-core rate probe (mfma_probe.hip): the GEMM kernels' instructions on
+// fragments loaded once from a, b (and idx for 2:4), instr_per_wave (a multiple
+// of 16) per wavefront, num_wg workgroups of 512 threads.
+bool mfma_probe_supported(int dtA, int dtB, int sparse);
+hipError_t launch_mfma_probe(int dtA, int dtB, int sparse, const void* a, const void* b, const void* idx,
+                             int64_t instr_per_wave, int num_wg, float* sink, int64_t* clocks, hipStream_t s);
 
 }  // namespace mcg

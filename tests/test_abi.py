@@ -300,3 +300,30 @@ def test_decompress24_host_argument_errors():
             m.decompress24_host(*args)
         assert e.value.status == status, args
     m.decompress24_host("bf16", 0, 16, None, 8, None, 1, None, 16)   # empty: no-op
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"dtypeA": "bf16", "dtypeB": "f16"}, 4),       # mixed 16-bit pair
+    ({"dtypeA": "i8", "dtypeB": "e4m3"}, 4),
+    ({"sparse": 2}, 4),
+    ({"instr_per_wave": 0}, 2),
+    ({"instr_per_wave": 24}, 2),                    # not a multiple of 16
+    ({"instr_per_wave": (1 << 24) + 16}, 2),
+    ({"num_wg": 0}, 2),
+    ({"num_wg": 65537}, 2),
+    ({"a": None}, 1),
+    ({"sink": None}, 1),
+    ({"clocks": None}, 1),
+    ({"sparse": 1, "idx": None}, 1),
+    ({"a": FAKE + 8}, 5),
+    ({"sparse": 1, "idx": FAKE + 4}, 5),
+    ({"clocks": FAKE + 4}, 5),
+])
+def test_mfma_probe_rejects_bad_arguments_on_the_host(kw, status):
+    # every case fails validation before any HIP call (no GPU here)
+    a = dict(dtypeA="bf16", dtypeB="bf16", sparse=0, a=FAKE, b=FAKE, idx=None, instr_per_wave=64, num_wg=1,
+             sink=FAKE, clocks=FAKE)
+    a.update(kw)
+    with pytest.raises(m.MCGError) as e:
+        m.mfma_probe(**a, stream=0)
+    assert e.value.status == status
