@@ -22,12 +22,12 @@
 //   - 256 x 256 output tile per workgroup of 8 wavefronts, two per SIMD, each
 //     owning 128 x 64 outputs = 4 x 2 instructions of 32 x 32.
 //   - LDS: kept values in stages of 128 bytes per row (one cache line: 128
-//     dense k of 16-bit or 256 of 8-bit elements) together with their index
-//     words (16 or 32 bytes per row, fetched 16 bytes per lane; for 8-bit
-//     elements rows with bit 4 set keep their two 16-byte chunks swapped, so
-//     that the index reads of rows r and r + 16, which the same LDS cycle
-//     serves, fall in different banks), 2 stages; B in stages of 128 bytes per
-//     column (64 or 128 dense k), 2 stages per column half.  All filled by
+//     dense k of 16-bit or 256 of 8-bit elements), 2 stages; their index words
+//     (16 or 32 bytes per row and stage) in blocks of 64 bytes per row (4 or 2
+//     stages), fetched as 64 contiguous bytes per row by 4 lanes, 2 blocks, with
+//     the row's 16-byte chunks rotated by row / 4 so that the 16 rows one LDS
+//     cycle serves fall in different banks; B in stages of 128 bytes per column
+//     (64 or 128 dense k), 2 stages per column half.  160 KiB, all filled by
 //     buffer_load ... lds.
 //   - ping-pong schedule as in the dense kernel: the two wavefronts of a SIMD
 //     alternate between multiplying one step (16 instructions) and a memory
@@ -50,16 +50,19 @@ constexpr int SP_BM = 256, SP_BN = 256;
 constexpr int SP_THREADS = 512;
 constexpr int SP_BH_STAGE = 16384;  // one column half of B: 128 columns x 128 bytes
 
-// Per element width EB: a kept-value stage holds 128 bytes per row (KA dense k)
-// plus the index words of those k (IWB bytes per row); a B stage holds 128
-// bytes per column (KB dense k); one instruction takes 32 kept bytes and 64
-// B bytes of each row / column.
+// Per element width EB: a kept-value stage holds 128 bytes per row (KA dense k),
+// whose index words take IWB bytes per row; a B stage holds 128 bytes per
+// column (KB dense k); one instruction takes 32 kept bytes and 64 B bytes of each
+// row / column.  Index words move in blocks of 64 bytes per row (SPB kept-value
+// stages), so that 4 lanes fetch one row's 64 contiguous bytes.
 template <int EB>
 struct SpGeom {
-  static constexpr int KA = 256 / EB;                       // dense k per kept-value stage
-  static constexpr int KB = 128 / EB;                       // dense k per B stage
-  static constexpr int IWB = KA / 32 * 4;                   // index bytes per row and stage
-  static constexpr int A_STAGE = SP_BM * 128 + SP_BM * IWB;  // kept values + index words
+  static constexpr int KA = 256 / EB;            // dense k per kept-value stage
+  static constexpr int KB = 128 / EB;            // dense k per B stage
+  static constexpr int IWB = KA / 32 * 4;        // index bytes per row and stage
+  static constexpr int A_STAGE = SP_BM * 128;    // kept values
+  static constexpr int SPB = 64 / IWB;           // kept-value stages per index block
+  static constexpr int I_BLOCK = SP_BM * 64;     // one index block in LDS
 };
 
 // HBM -> LDS loader of one column half of the B tile.  Half c holds the
@@ -125,8 +128,7 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   constexpr int WTM = 4, WTN = 2;
   constexpr int EB = Op::EB;
   using SG = SpGeom<EB>;
-  constexpr int A_STAGE = SG::A_STAGE, IWB = SG::IWB;
-  constexpr int WPR = IWB / 4;                   // index words per row and stage
+  constexpr int A_STAGE = SG::A_STAGE, IWB = SG::IWB, SPB = SG::SPB, I_BLOCK = SG::I_BLOCK;
   constexpr int II = SP_BM * IWB / (1024 * NW);  // 16-byte index loads per wave of group 0 and stage
   using RA = Reader<EB, LAYOUT_K, SP_BM, 128>;
   using RB = Reader<EB, LB, 128, 128>;
@@ -135,8 +137,9 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   static_assert(Geom<EB, LAYOUT_K, SP_BM, 128>::BYTES == 32768 && Geom<EB, LB, 128, 128>::BYTES == SP_BH_STAGE, "");
   static_assert(LdA::INSTR == 8, "8 loads per wave and kept-value stage");
   static_assert(II == 1 || II == 2, "index loads per stage");
+  static_assert(II * NW * SPB == I_BLOCK / 1024, "a block's loads, one part per stage");
 
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * A_STAGE + 4 * SP_BH_STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * A_STAGE + 4 * SP_BH_STAGE + 2 * I_BLOCK];
   lds_char* smem = (lds_char*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -157,9 +160,10 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   const int nwords = (int)((p.K + 31) / 32);
 
   auto stA = [&](int T) { return smem + (T & 1) * A_STAGE; };
-  auto stI = [&](int T) { return smem + (T & 1) * A_STAGE + 32768; };
   // B half c of step u
   auto stBh = [&](int c, int u) { return smem + 2 * A_STAGE + (2 * c + (u & 1)) * SP_BH_STAGE; };
+  // index block b (kept-value stages [SPB b, SPB b + SPB) of the problem)
+  auto stIB = [&](int b) { return smem + 2 * A_STAGE + 4 * SP_BH_STAGE + (b & 1) * I_BLOCK; };
 
   // every wave loads half of the kept values (instructions 4 grp .. 4 grp + 3)
   // and the other group's half of B; group 0 also loads the index words
@@ -167,37 +171,42 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   la.init(p.Ac + m0 * p.lda_c * EB, (uint32_t)(rows * p.lda_c * EB), p.lda_c, Kc, q, lane);
   BHalfLoader<EB, LB> lb;
   lb.init(p.B, n0, 1 - grp, p.N, p.K, p.ldb, q, lane);
-  // Index words: 16-byte loads, so a stage's IWB bytes per row take IWB / 16
-  // lanes.  Instruction i of wave q (group 0) fills LDS bytes [(II q + i) 1024,
-  // +1024) of the index image: lane l holds 16-byte chunk (II q + i) 64 + l,
-  // i.e. row chunk / (IWB / 16) and position chunk % (IWB / 16) of that row.  With
-  // two chunks per row (8-bit), rows with bit 4 set keep them swapped: the chunk
-  // read for step h is h ^ bit 4, and the same LDS cycle's rows r and r + 16 then
-  // fall in different banks.  With one chunk per row (16-bit), the 16 rows that
-  // one cycle of 16-byte reads serves are in different banks as they are.
+  // Index words: block b holds words [16 b, 16 b + 16) of each of the tile's rows,
+  // 64 bytes per row, in 16 load instructions of 16 rows (4 lanes per row, 16 bytes
+  // each).  LDS row r of a block keeps its 16-byte chunk c (the words of stage
+  // SPB b + c / CPR) at position (c + r / 4) mod 4, so that the 16 rows that one
+  // LDS cycle of 16-byte reads serves fall in 16 different bank groups; the
+  // rotation is applied on the global side (lane l of an instruction, at
+  // position l mod 4 of row l / 4, fetches the chunk that belongs there).  Group 0
+  // loads part t = S mod SPB of block S / SPB + 1 while stage S is current
+  // (instructions t 16 / SPB + II q + i of wave q), so a block is complete two
+  // slots before its first stage is read; the first block of a piece, and the
+  // parts of the next block that belong to stages before the piece, are loaded
+  // with the first stage.
   constexpr int CPR = IWB / 16;  // 16-byte chunks per row and stage
-  __amdgpu_buffer_rsrc_t rs_idx;
-  uint32_t off_idx[II];
-  int chunk_idx[II];
-  rs_idx = make_rsrc((const char*)(p.idx + m0 * p.ld_idx), (uint32_t)(rows * p.ld_idx * 4));
-#pragma unroll
-  for (int i = 0; i < II; ++i) {
-    const int e = (II * q + i) * 64 + lane;
-    const int row = e / CPR;
-    chunk_idx[i] = CPR == 2 ? (e % 2) ^ ((row >> 4) & 1) : 0;  // the chunk of the row kept at that position
-    off_idx[i] = (uint32_t)(row * p.ld_idx * 4 + chunk_idx[i] * 16);
-  }
-  auto issueA = [&](int T) { la.issue(stA(T), Tb + T, 4 * grp, 4, q); };
-  auto issueI = [&](int T) {
+  const __amdgpu_buffer_rsrc_t rs_idx =
+      make_rsrc((const char*)(p.idx + m0 * p.ld_idx), (uint32_t)(rows * p.ld_idx * 4));
+  const int ilr = lane >> 2;                    // row within an instruction's 16
+  const int ichunk = ((lane & 3) - (ilr >> 2)) & 3;  // chunk this lane fetches
+  const uint32_t ioff = (uint32_t)(ilr * p.ld_idx * 4 + ichunk * 16);
+  const uint32_t istride = (uint32_t)(16 * p.ld_idx * 4);  // bytes per instruction (16 rows)
+  auto issueIpart = [&](int b, int t) {
 #pragma unroll
     for (int i = 0; i < II; ++i) {
+      const int k = t * (16 / SPB) + II * q + i;
       // chunks that start past the last index word read zeros; a chunk that
       // straddles it reads the row's next words, which only cover groups past K
       // (their kept values are zero)
-      const uint32_t o = (Tb + T) * WPR + 4 * chunk_idx[i] < nwords ? off_idx[i] + (uint32_t)((Tb + T) * IWB) : BUF_OOB;
+      const uint32_t o = 16 * b + 4 * ichunk < nwords ? ioff + (uint32_t)k * istride + (uint32_t)(64 * b) : BUF_OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs_idx, (__attribute__((address_space(3))) void*)(stI(T) + (II * q + i) * 1024), 16, o, 0, 0, 0);
+          rs_idx, (__attribute__((address_space(3))) void*)(stIB(b) + k * 1024), 16, o, 0, 0, 0);
     }
+  };
+  auto issueA = [&](int T) { la.issue(stA(T), Tb + T, 4 * grp, 4, q); };
+  // while kept-value stage T of the piece is current: the next block's part
+  auto issueI = [&](int T) {
+    const int S = Tb + T;
+    issueIpart(S / SPB + 1, S % SPB);
   };
   auto issueB = [&](int u) { lb.issue(stBh(1 - grp, u), 2 * Tb + u, q); };  // the other group's half
 
@@ -210,23 +219,43 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   i32x4 fa[2][WTM];
   i32x8 fb[2][WTN];
   int fi[2][WTM];
+  int fi_next[2][WTM];  // 16-bit: the second step's codes, from the first step's read of the stage's record
   // fragments of step u = 2T + h (KB dense k): instruction s covers kept bytes
   // [64h + 32s, +32) of stage T and B bytes [64s, +64) of step u.  Index codes:
   // 16-bit elements use half g of word 2h + s (32 dense k per instruction),
   // 8-bit elements word 4h + 2s + g (64 dense k per instruction).
-  // byte of this lane's index record in row rbA + (lane & 31) (8-bit: of its chunk
-  // for h = 0; h = 1: ^ 16); rows 32 i further add 32 i IWB
-  const int ibase = (rbA + (lane & 31)) * IWB + (EB == 1 ? 16 * ((lane >> 4) & 1) : 0);
+  // this lane's index row rbA + (lane & 31) of a block (rows 32 i further add 32 i 64
+  // bytes; their rotation is the same, 32 i / 4 being a multiple of 4)
+  const int ibase = (rbA + (lane & 31)) * 64;
+  const int irot = (lane & 31) >> 2;
   auto read_frags = [&](int u) {
     const int T = u >> 1, h = u & 1;
+    const int S = Tb + T;
+    // the stage's chunk (8-bit: the step's) in its block, at its rotated position
+    const int c = (S % SPB) * CPR + (CPR == 2 ? h : 0);
+    const lds_char* ib = stIB(S / SPB) + ibase + (((c + irot) & 3) << 4);
 #pragma unroll
     for (int i = 0; i < WTM; ++i) {
-      if constexpr (EB == 2) {
-        const i32x4 w = *(const __attribute__((address_space(3))) i32x4*)(stI(T) + ibase + 32 * i * IWB);
+      if constexpr (EB == 2 && !SK) {
+        // one 16-byte record per row and stage: words 0, 1 for the first step,
+        // 2, 3 for the second, which keeps them from this read (the stream-K form
+        // reads it in both steps: the 8 more registers made it spill)
+        if (h == 0) {
+          const i32x4 w = *(const __attribute__((address_space(3))) i32x4*)(ib + 32 * i * 64);
+          fi[0][i] = (int)((uint32_t)w.x >> (16 * g));
+          fi[1][i] = (int)((uint32_t)w.y >> (16 * g));
+          fi_next[0][i] = (int)((uint32_t)w.z >> (16 * g));
+          fi_next[1][i] = (int)((uint32_t)w.w >> (16 * g));
+        } else {
+          fi[0][i] = fi_next[0][i];
+          fi[1][i] = fi_next[1][i];
+        }
+      } else if constexpr (EB == 2) {
+        const i32x4 w = *(const __attribute__((address_space(3))) i32x4*)(ib + 32 * i * 64);
         fi[0][i] = (int)((uint32_t)(h ? w.z : w.x) >> (16 * g));
         fi[1][i] = (int)((uint32_t)(h ? w.w : w.y) >> (16 * g));
       } else {
-        const i32x4 w = *(const __attribute__((address_space(3))) i32x4*)(stI(T) + (ibase ^ (16 * h)) + 32 * i * IWB);
+        const i32x4 w = *(const __attribute__((address_space(3))) i32x4*)(ib + 32 * i * 64);
         fi[0][i] = g ? w.y : w.x;
         fi[1][i] = g ? w.w : w.z;
       }
@@ -258,16 +287,20 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
   // group c has read it, and the other group refills it in its next memory
   // phase: group 0 loads group 1's half of B(u + 1) in slot 2u - 1, group 1
   // loads group 0's half of B(u + 2) in slot 2u; each has 3 slots in flight.
-  // Kept-value stage T (and its index words) is last read in slot 4T + 2;
-  // group 0 loads its half of stage T + 2 and the index words in slot 4T + 3,
-  // group 1 the other half in slot 4T + 4.  Every wave waits for its loads at
+  // Kept-value stage T is last read in slot 4T + 2; group 0 loads its half of
+  // stage T + 2 and a part of the next index block in slot 4T + 3, group 1 the
+  // other half in slot 4T + 4.  Every wave waits for its loads at
   // the end of its memory phases, just early enough for their first reader.
   // Loads past K read nothing and fill their stage with zeros (an odd number
   // of steps is padded with one such zero step).
   if (grp == 0) {
     issueB(0);
     issueA(0);
-    issueI(0);
+    // the piece's first index block, and the parts of the next one that belong
+    // to stages before the piece (the loop loads the rest)
+    const int b0 = Tb / SPB, p0 = Tb % SPB;
+    for (int t = 0; t < SPB; ++t) issueIpart(b0, t);
+    for (int t = 0; t < p0; ++t) issueIpart(b0 + 1, t);
   } else {
     issueB(0);
     issueB(1);
@@ -282,7 +315,7 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
       read_frags(u);  // slot 4T - 1
       issueB(u + 1);
       issueA(T + 1);
-      issueI(T + 1);
+      issueI(T);
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 + II) : "memory");  // group 1's half of B(u)
       barrier_lds();
       __builtin_amdgcn_sched_barrier(0);
