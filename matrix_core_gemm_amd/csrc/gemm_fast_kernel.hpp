@@ -391,64 +391,85 @@ void gemm_fast_kernel(DenseArgs p) {
       }
       return o;
     };
+    // The passes over the row blocks, for binary32 / int32 (O16 false) or 16-bit
+    // (O16 true) C and D.  Each pass's C rows are loaded one pass ahead: pass i + 1's
+    // loads go out once pass i has staged its accumulators (whose registers they
+    // reuse), so their latency overlaps pass i's staging, reads and stores; the first
+    // pass's loads go out before any staging.  C is read once, so its loads are
+    // non-temporal (they keep the operand panels in the caches: measured 0.75-0.9%
+    // faster at 8192^3 with an N(0,1) C, bit-identical).
+    auto passes = [&](auto o16) {
+      constexpr bool O16 = decltype(o16)::value;
+      using cvec = typename std::conditional<O16, i32x2, v4>::type;
+      cvec cn[8];
+      auto load_c = [&](int i) {
+        const int64_t rb = (em0 + rbA + 32 * i + rr) * d.ld + col;
 #pragma unroll
-    for (int i = 0; i < WTM; ++i) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (KS && i != grp) continue;  // the partner wave stores this row block
-      lds_char* buf = wbuf + (KS ? 0 : (i & 1) * 8192);
-      const int64_t rbase = (em0 + rbA + 32 * i + rr) * d.ld + col;  // row 4t further: + 4t ldc
-      v4 cv[8];
-      // C loads first: their latency overlaps the staging.  C is read once, so its
-      // loads are non-temporal (they keep the operand panels in the caches:
-      // measured 0.75-0.9% faster at 8192^3 with an N(0,1) C, bit-identical)
-      if (out == OUT_32 && d.use_c) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) cv[t] = __builtin_nontemporal_load((const v4*)(C + rbase + 4 * t * d.ld));
-      }
-#pragma unroll
-      for (int j = 0; j < WTN; ++j)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int ch = (32 * j + acc_n(r4)) / 4;  // 16-byte chunk of the wavefront's 64 columns
-          v4 x;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) x[r] = acc[i][j][4 * r4 + r];
-          *(lds_v4*)(buf + wr * 256 + ((ch ^ (wr & 15)) << 4)) = x;
+        for (int t = 0; t < 8; ++t) {
+          if constexpr (O16)
+            cn[t] = __builtin_nontemporal_load((const i32x2*)((const uint16_t*)d.C + rb + 4 * t * d.ld));
+          else
+            cn[t] = __builtin_nontemporal_load((const v4*)(C + rb + 4 * t * d.ld));
         }
-      // the reads below take other lanes' values: wait for the writes
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      v4 a[8];
+      };
+      if (d.use_c) load_c(KS ? grp : 0);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int row = 4 * t + rr;
-        a[t] = *(const lds_v4*)(buf + row * 256 + ((cc ^ (row & 15)) << 4));
-      }
-      if constexpr (!Op::INT_ACC) {
-        if (out != OUT_32) {
-          const uint16_t* C16 = (const uint16_t*)d.C;
-          uint16_t* D16 = (uint16_t*)d.D;
-          i32x2 cw[8];
-          if (d.use_c) {
+      for (int i = 0; i < WTM; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (KS && i != grp) continue;  // the partner wave stores this row block
+        lds_char* buf = wbuf + (KS ? 0 : (i & 1) * 8192);
+        const int64_t rbase = (em0 + rbA + 32 * i + rr) * d.ld + col;  // row 4t further: + 4t ldc
+        cvec cv[8];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) cw[t] = __builtin_nontemporal_load((const i32x2*)(C16 + rbase + 4 * t * d.ld));
+        for (int t = 0; t < 8; ++t) cv[t] = cn[t];
+#pragma unroll
+        for (int j = 0; j < WTN; ++j)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int ch = (32 * j + acc_n(r4)) / 4;  // 16-byte chunk of the wavefront's 64 columns
+            v4 x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = acc[i][j][4 * r4 + r];
+            *(lds_v4*)(buf + wr * 256 + ((ch ^ (wr & 15)) << 4)) = x;
           }
+        if (!KS && i + 1 < WTM && d.use_c) load_c(i + 1);
+        // the reads below take other lanes' values: wait for the writes
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        v4 a[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int row = 4 * t + rr;
+          a[t] = *(const lds_v4*)(buf + row * 256 + ((cc ^ (row & 15)) << 4));
+        }
+        if constexpr (O16) {
+          uint16_t* D16 = (uint16_t*)d.D;
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
             v4 c = {};
-            if (d.use_c)
-              c = v4{from_out_bits(out, (uint32_t)cw[t].x & 0xffffu), from_out_bits(out, (uint32_t)cw[t].x >> 16),
-                     from_out_bits(out, (uint32_t)cw[t].y & 0xffffu), from_out_bits(out, (uint32_t)cw[t].y >> 16)};
+            if (d.use_c) {  // (16-bit D only with binary32 accumulators)
+              c[0] = from_out_bits(out, (uint32_t)cv[t].x & 0xffffu);
+              c[1] = from_out_bits(out, (uint32_t)cv[t].x >> 16);
+              c[2] = from_out_bits(out, (uint32_t)cv[t].y & 0xffffu);
+              c[3] = from_out_bits(out, (uint32_t)cv[t].y >> 16);
+            }
             const v4 o = combine4(a[t], c);
             *(i32x2*)(D16 + rbase + 4 * t * d.ld) =
                 i32x2{(int)(to_out_bits(out, o[0]) | (to_out_bits(out, o[1]) << 16)),
                       (int)(to_out_bits(out, o[2]) | (to_out_bits(out, o[3]) << 16))};
           }
-          continue;
+        } else {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) *(v4*)(D + rbase + 4 * t * d.ld) = combine4(a[t], d.use_c ? cv[t] : v4{});
         }
       }
-#pragma unroll
-      for (int t = 0; t < 8; ++t) *(v4*)(D + rbase + 4 * t * d.ld) = combine4(a[t], d.use_c ? cv[t] : v4{});
+    };
+    if constexpr (!Op::INT_ACC) {
+      if (out != OUT_32) {
+        passes(std::true_type{});
+        return;
+      }
     }
+    passes(std::false_type{});
     return;
   }
   if constexpr (!Op::INT_ACC) {
