@@ -438,7 +438,14 @@ __device__ __forceinline__ void compress_chunk(const i32x4& v, uint32_t& code, u
 // 16-bit elements: one lane per 16-byte chunk (2 groups), consecutive lanes on
 // consecutive chunks, so every 16-byte load and 8-byte store of a wavefront
 // covers 1 KiB or 512 bytes of contiguous memory.  The 4 lanes of one index word
-// combine their codes with lane shuffles and the first stores the word.
+// combine their codes with lane shuffles and the first stores the word.  Each
+// lane takes the same chunk of VR consecutive rows, all loads first, and the
+// dense input is read once, with non-temporal loads.  Measured at 8192^2 bf16
+// against one row per lane and ordinary loads (bit-identical): 1.18-1.23x faster
+// with L2 and MALL flushed first (the usual case: a matrix compressed once), 4-6%
+// slower when the same input is compressed again while it sits in the MALL (4
+// rows per lane: a little faster flushed, 9% slower cached).
+constexpr int VR = 2;
 template <int EB, bool INT8>
 __global__ __launch_bounds__(256) void compress24_vec_kernel(CompressArgs p) {
   constexpr int CH = 32 * EB / 16;  // chunks per index word
@@ -448,18 +455,28 @@ __global__ __launch_bounds__(256) void compress24_vec_kernel(CompressArgs p) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;  // chunk slot; blocks start at a word boundary
   const int sub = threadIdx.x % CH;                            // chunk of its word
   int bad = 0;
-  for (int64_t row = blockIdx.y; row < p.M; row += gridDim.y) {
-    uint32_t code = 0;
-    uint64_t kept = 0;
-    if (c < nchunks) {
-      const i32x4 v = *(const i32x4*)(p.A + row * p.lda * EB + c * 16);
-      compress_chunk<EB, INT8>(v, code, kept, bad);
-      *(uint64_t*)(p.Ac + row * p.lda_c * EB + c * 8) = kept;
-    }
-    uint32_t word = code << (4 * G * sub);
+  for (int64_t r0 = (int64_t)blockIdx.y * VR; r0 < p.M; r0 += (int64_t)gridDim.y * VR) {
+    i32x4 v[VR];
 #pragma unroll
-    for (int d = 1; d < CH; d <<= 1) word |= (uint32_t)__shfl_xor((int)word, d, CH);
-    if (sub == 0 && c / CH < nwords) p.idx[row * p.ld_idx + c / CH] = word;
+    for (int r = 0; r < VR; ++r)
+      v[r] = c < nchunks && r0 + r < p.M
+                 ? __builtin_nontemporal_load((const i32x4*)(p.A + (r0 + r) * p.lda * EB + c * 16))
+                 : i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < VR; ++r) {
+      const int64_t row = r0 + r;
+      if (row >= p.M) break;
+      uint32_t code = 0;
+      uint64_t kept = 0;
+      if (c < nchunks) {
+        compress_chunk<EB, INT8>(v[r], code, kept, bad);
+        *(uint64_t*)(p.Ac + row * p.lda_c * EB + c * 8) = kept;
+      }
+      uint32_t word = code << (4 * G * sub);
+#pragma unroll
+      for (int d = 1; d < CH; d <<= 1) word |= (uint32_t)__shfl_xor((int)word, d, CH);
+      if (sub == 0 && c / CH < nwords) p.idx[row * p.ld_idx + c / CH] = word;
+    }
   }
   if (bad && p.violations) atomicAdd(p.violations, bad);
 }
@@ -467,7 +484,10 @@ __global__ __launch_bounds__(256) void compress24_vec_kernel(CompressArgs p) {
 // 8-bit elements: one lane per index word of a row (2 chunks of 4 groups),
 // consecutive lanes on consecutive words: two 16-byte loads and one 16-byte
 // store of kept values per lane (8-byte stores when the destination rows are not
-// 16-byte aligned), and the word stored whole.
+// 16-byte aligned), and the word stored whole.  Non-temporal loads (the input is
+// read once): int8 and E4M3 8192^2 1.08-1.15x faster with L2 and MALL flushed
+// first, 4-6% slower when compressed again from the MALL; more rows per lane
+// measured slower here.
 template <bool INT8>
 __global__ __launch_bounds__(256) void compress24_word8_kernel(CompressArgs p, int a16) {
   const int64_t nwords = (p.K + 31) / 32;
@@ -481,7 +501,8 @@ __global__ __launch_bounds__(256) void compress24_word8_kernel(CompressArgs p, i
     char* dst = p.Ac + row * p.lda_c + c0 * 8;
     i32x4 v[2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) v[k] = c0 + k < nchunks ? *(const i32x4*)(src + 16 * k) : i32x4{0, 0, 0, 0};
+    for (int k = 0; k < 2; ++k)
+      v[k] = c0 + k < nchunks ? __builtin_nontemporal_load((const i32x4*)(src + 16 * k)) : i32x4{0, 0, 0, 0};
     uint32_t word = 0;
     uint64_t kept[2];
 #pragma unroll
@@ -519,10 +540,11 @@ hipError_t launch_compress(int dtype, const CompressArgs& a, hipStream_t s) {
     if (a.M <= 0 || nwords <= 0) return hipSuccess;
     const unsigned rows = (unsigned)(a.M < 65535 ? a.M : 65535);
     if (eb == 2) {
+      const int64_t ry = (a.M + VR - 1) / VR;  // row blocks of VR rows
       const int64_t slots = nwords * 4;  // chunk slots per row (whole index words)
       if ((slots + 255) / 256 > 0x7fffffff) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((compress24_vec_kernel<2, false>), dim3((unsigned)((slots + 255) / 256), rows), dim3(256),
-                         0, s, a);
+      hipLaunchKernelGGL((compress24_vec_kernel<2, false>),
+                         dim3((unsigned)((slots + 255) / 256), (unsigned)(ry < 65535 ? ry : 65535)), dim3(256), 0, s, a);
       return hipGetLastError();
     }
     if ((nwords + 255) / 256 > 0x7fffffff) return hipErrorInvalidValue;
