@@ -171,11 +171,16 @@ SPARSE_CASES = [  # dtA, dtB, layB, M, N, K, out, alpha, beta, D aliases C
     ("i8", "i8", "mn_contig", 2048, 2048, 8192, "i32", 3, -2, False),                # int8, MN-contiguous B
     ("f16", "f16", "k_contig", 4096, 4352, 8192, "f16", -0.75, 1.0, True),          # whole rounds + 16 tiles
     ("e4m3", "e5m2", "k_contig", 2100, 2000, 8192, "f32", 1.0, 0.0, False),         # ragged, native fp8
+    # pieces of 3 kept-value stages: most pieces start inside an index block (4
+    # stages of 16-bit, 2 of 8-bit elements), whose earlier parts they load first
+    ("bf16", "bf16", "k_contig", 1024, 1024, 6144, "f32", 1.0, 0.0, False),         # 16 tiles, 16 pieces each
+    ("i8", "i8", "k_contig", 1024, 1536, 6144, "i32", 1, 1, False),                 # 24 tiles, 8 pieces each
 ]
 
 
 @pytest.mark.parametrize("case", SPARSE_CASES, ids=["sparse_bf16", "sparse_i8_mn", "sparse_f16_f16out_alias",
-                                                    "sparse_fp8_ragged"])
+                                                    "sparse_fp8_ragged", "sparse_bf16_pieces_of_3",
+                                                    "sparse_i8_pieces_of_3"])
 def test_sparse_streamk_against_oracle(case):
     """gemm_sparse24_ws: every output of the stream-K tiles, one whole tile and
     sampled others against the oracle (A compressed on the host by the oracle)."""

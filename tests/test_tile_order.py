@@ -128,6 +128,11 @@ def test_sparse_workspace_plan():
     assert _sws(mcg, "bf16", 1536, 1536, 8192) == 144 * slot
     # int8: 256 dense k per stage, 2048^2 x 8192 has 32 stages per tile, cut in 4
     assert _sws(mcg, "i8", 2048, 2048, 8192) == 256 * slot
+    # pieces of 3 stages (the GPU tests' cases whose pieces start inside an index
+    # block of 4 or 2 stages): bf16 1024^2 x 6144, 48 stages cut in 16; int8
+    # 1024 x 1536 x 6144, 24 stages cut in 8
+    assert _sws(mcg, "bf16", 1024, 1024, 6144) == 16 * 16 * slot
+    assert _sws(mcg, "i8", 1024, 1536, 6144) == 24 * 8 * slot
     # whole rounds, too little to gain, or not the 256 x 256 sparse kernel
     assert _sws(mcg, "bf16", 8192, 8192, 8192) == 0
     assert _sws(mcg, "bf16", 2048, 2048, 2048) == 0
