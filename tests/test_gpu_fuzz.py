@@ -192,3 +192,87 @@ def test_random_streamk_problem(seed):
         r = oracle.check_float(got, ref, s, K, alpha, A.scale, B.scale, beta, cc, out=out)
     say("  ", {k: v for k, v in r.items() if k != "worst"})
     assert r["ok"], r
+
+
+def draw_sparse_streamk_case(seed):
+    """Random 2:4 problem with a stream-K plan: input pair, B layout, sizes, output
+    format and beta drawn from a generator seeded with its index until the plan
+    takes the stream-K form.  K is a multiple of 32 (the 256 x 256 kernel's
+    alignment for every width); the pieces' lengths in kept-value stages vary
+    with it, so pieces start at every offset within an index block."""
+    import matrix_core_gemm_amd as mcg
+    r = np.random.default_rng(9000 + seed)
+    for _ in range(1000):
+        dtA, dtB = SPARSE_DTYPES[r.integers(len(SPARSE_DTYPES))]
+        layB = ["k_contig", "mn_contig"][r.integers(2)]
+        M = 16 * int(r.integers(16, 190))
+        N = 16 * int(r.integers(16, 190))
+        K = 32 * int(r.integers(16, 384))
+        if dtA in ("e4m3", "e5m2"):
+            K = max(K, 6144)
+        ldb = K if layB == "k_contig" else N
+        if mcg.sparse24_workspace_bytes(dtA, layB, M, N, K, 0x1000, K // 2, 0x1000, (K + 31) // 32, 0x1000,
+                                        ldb) > 0:
+            out = "i32" if dtA == "i8" else ["f32", {"bf16": "bf16", "f16": "f16"}.get(dtA, "f32")][r.integers(2)]
+            beta = [0.0, 1.0, -0.5][r.integers(3)] if dtA != "i8" else [0, 1, -2][r.integers(3)]
+            return dtA, dtB, layB, M, N, K, out, beta
+    raise AssertionError("no 2:4 stream-K shape drawn")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_sparse_streamk_problem(seed):
+    """gemm_sparse24_ws on a random stream-K problem: every output of the first and
+    the last stream-K tile and sampled others against the oracle."""
+    from test_gpu_streamk import grouped_tile, tile_coords, workspace
+    mcg = need_gpu()
+    dtA, dtB, layB, M, N, K, out, beta = draw_sparse_streamk_case(seed)
+    say(f"2:4 stream-K fuzz {seed}: {dtA}x{dtB} B {layB} {M}x{N}x{K} -> {out} beta={beta}")
+    i8 = dtA == "i8"
+    A = W.sparse24_dense(dtA, M, K, dist="int8" if i8 else "normal", seed=400 + seed)
+    B = W.operand("B", dtB, K, N, "int8" if i8 else "normal", layB, seed=410 + seed, fp8_scaled=not i8)
+    alpha = 2 if i8 else 1.25 * B.scale
+    v, ix, nv = oracle.compress24(dtA, A)
+    assert nv == 0
+    dv, di, dB = dev(v), dev(ix.view(np.int32)), dev(B.codes)
+    lda_c, ld_idx = K // 2, (K + 31) // 32
+    assert mcg.sparse24_path(dtA, layB, M, N, K, dv, lda_c, di, ld_idx, dB, B.ld) == 1
+    need = mcg.sparse24_workspace_bytes(dtA, layB, M, N, K, dv, lda_c, di, ld_idx, dB, B.ld)
+    C = None
+    if out == "i32":
+        C = W.c_matrix(M, N, "int20", seed=420 + seed)
+        D = torch.full((M, N), -0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    elif out == "f32":
+        C = W.c_matrix(M, N, "normal", seed=420 + seed) if beta != 0 else None
+        D = torch.full((M, N), float("nan"), device="cuda")
+    else:
+        tdt = torch.bfloat16 if out == "bf16" else torch.float16
+        C = W.draw("normal", (M, N), 420 + seed).to(tdt).view(torch.int16).numpy().view(np.uint16)
+        D = torch.full((M, N), 0x7FC0 if out == "bf16" else 0x7E00, dtype=torch.int32).to(torch.int16).to("cuda")
+    dC = None if C is None or beta == 0 else dev(C.view(np.int16) if out in ("bf16", "f16") else C)
+    mcg.gemm_sparse24_ws(dtA, dtB, layB, M, N, K, dv, lda_c, di, ld_idx, dB, B.ld, dC, D, N, out, alpha, beta,
+                         workspace=workspace(need))
+    torch.cuda.synchronize()
+    d = D.cpu().numpy()
+    tm, tn = -(-M // 256), -(-N // 256)
+    T = tm * tn
+    R = T % torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = [grouped_tile(p, tm, tn) for p in (T - R, T - 1)]
+    r1, c1 = tile_coords(tiles, M, N, 256)
+    r2, c2 = W.sample_coords(M, N, n_random=1024, full_rows=(M - 1,), full_cols=(N - 1,))
+    rows, cols = np.concatenate([r1, r2]), np.concatenate([c1, c2])
+    Cr = C if dC is not None else None
+    say(f"  {R} stream-K tiles, {need // (256 * 256 * 4)} pieces, {len(rows)} outputs compared")
+    ref, s = oracle.gemm_sparse24(dtA, dtB, layB, M, N, K, v, ix, B.codes, B.ld, Cr, N, alpha, beta, rows=rows,
+                                  cols=cols, out=out if out in ("f16", "bf16") else "f32")
+    if i8:
+        r = oracle.check_exact(d[rows, cols], ref)
+    else:
+        if out in ("bf16", "f16"):
+            tdt = torch.bfloat16 if out == "bf16" else torch.float16
+            dec = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(tdt).double().numpy()
+            got, cc = dec(d)[rows, cols], None if Cr is None else dec(C)[rows, cols]
+        else:
+            got, cc = d[rows, cols], None if Cr is None else C[rows, cols]
+        r = oracle.check_float(got, ref, s, K, alpha, beta=beta, c=cc, out=out if out in ("f16", "bf16") else "f32")
+    say("  ", {k: v for k, v in r.items() if k != "worst"})
+    assert r["ok"], r
