@@ -75,6 +75,12 @@ def test_graph_dense_paths_and_streamk():
     assert need > 0
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     assert mcg.dense_path("bf16", "k_contig", "k_contig", 1024, 1024, 1024, dA, 1024, dB, 1024) in (1, 6)
+    D4 = torch.empty((M3, N3), device="cuda")  # the same stream-K problem on the library's static scratch
+    assert need <= mcg._lib.mcg_dense_noalloc_scratch_bytes()
+    g = torch.Generator(device="cuda").manual_seed(10)
+    A5 = torch.randn((384, 320), generator=g, dtype=torch.float64, device="cuda")
+    B5 = torch.randn((160, 320), generator=g, dtype=torch.float64, device="cuda")  # column-major K x N
+    D5 = torch.empty((384, 160), dtype=torch.float64, device="cuda")
 
     def run(s):
         mcg.gemm_dense("bf16", "bf16", 0, 0, 1024, 1024, 1024, dA, 1024, dB, 1024, C, D1, 1024, "f32", 1.5, -0.5,
@@ -82,13 +88,29 @@ def test_graph_dense_paths_and_streamk():
         mcg.gemm_dense("i8", "i8", 0, 0, 300, 40, 2048, Ai, 2048, Bi, 2048, None, D2, 40, "i32", 1, 0, stream=s)
         mcg.gemm_dense_ws("bf16", "bf16", 0, 0, M3, N3, K3, A3, K3, B3, K3, None, D3, N3, "f32", 1.0, 0.0,
                           workspace=ws, stream=s)
-    replay_and_compare(run, [D1, D2, D3], [float("nan"), -0x5A5A5A5A, float("nan")])
+        mcg.gemm_dense_noalloc("bf16", "bf16", 0, 0, M3, N3, K3, A3, K3, B3, K3, None, D4, N3, "f32", 1.0, 0.0,
+                               stream=s)
+        mcg.gemm_dense("f64", "f64", 0, 0, 384, 160, 320, A5, 320, B5, 320, None, D5, 160, "f64", 1.0, 0.0,
+                       stream=s)
+    replay_and_compare(run, [D1, D2, D3, D4, D5], [float("nan"), -0x5A5A5A5A, float("nan"), float("nan"),
+                                                   float("nan")])
 
 
 def test_graph_compress_then_sparse():
-    # compress24 on the device, then the 2:4 GEMM on its output, in one graph
+    # compress24 on the device, then the 2:4 GEMM on its output, in one graph; and
+    # the 2:4 stream-K form with a workspace
     mcg = need_gpu()
     M, N, K = 512, 768, 1024
+    M2, N2, K2 = 2048, 2048, 8192
+    vals2 = dev(W.sparse24_dense("bf16", M2, K2, seed=13))  # compressed below, eagerly
+    v2 = torch.empty((M2, K2 // 2), dtype=torch.int16, device="cuda")
+    i2 = torch.empty((M2, K2 // 32), dtype=torch.int32, device="cuda")
+    mcg.compress24("bf16", M2, K2, vals2, K2, v2, K2 // 2, i2, K2 // 32, None)
+    B2 = dev(W.operand("B", "bf16", K2, N2, "normal", "k_contig", seed=14).codes)
+    need = mcg.sparse24_workspace_bytes("bf16", "k_contig", M2, N2, K2, v2, K2 // 2, i2, K2 // 32, B2, K2)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    D2 = torch.empty((M2, N2), device="cuda")
     Ad = dev(W.sparse24_dense("bf16", M, K, seed=11))
     B = dev(W.operand("B", "bf16", K, N, "normal", "k_contig", seed=12).codes)
     vals = torch.empty((M, K // 2), dtype=torch.int16, device="cuda")
@@ -99,4 +121,6 @@ def test_graph_compress_then_sparse():
         mcg.compress24("bf16", M, K, Ad, K, vals, K // 2, idx, K // 32, None, stream=s)
         mcg.gemm_sparse24("bf16", "bf16", "k_contig", M, N, K, vals, K // 2, idx, K // 32, B, K, None, D, N, "f32",
                           1.0, 0.0, stream=s)
-    replay_and_compare(run, [vals, idx, D], [0x7BCD, 0x7BCDEF01, float("nan")])
+        mcg.gemm_sparse24_ws("bf16", "bf16", "k_contig", M2, N2, K2, v2, K2 // 2, i2, K2 // 32, B2, K2, None, D2, N2,
+                             "f32", 1.0, 0.0, workspace=ws, stream=s)
+    replay_and_compare(run, [vals, idx, D, D2], [0x7BCD, 0x7BCDEF01, float("nan"), float("nan")])
