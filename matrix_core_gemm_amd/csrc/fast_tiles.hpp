@@ -137,14 +137,16 @@ struct LineLoader {
   __device__ __forceinline__ void issue(lds_char* dst, int kt, int i0, int n, int wave) const {
     issue_if(dst, kt, i0, n, wave, true);
   }
-  // the same; when !live the instructions read nothing and fill the stage with zeros
+  // the same; when !live the instructions read nothing and fill the stage with zeros.
+  // AUX: the loads' cache-policy bits (2: non-temporal, for data read once)
+  template <int AUX = 0>
   __device__ __forceinline__ void issue_if(lds_char* dst, int kt, int i0, int n, int wave, bool live) const {
     const uint32_t v = live && kt < klim ? voff + (uint32_t)kt * kstride : BUF_OOB;
 #pragma unroll
     for (int i = i0; i < i0 + n; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsrc, (__attribute__((address_space(3))) void*)(dst + (i * NW + wave) * 1024), 16,
-          v + (uint32_t)i * istride, 0, 0, 0);
+          v + (uint32_t)i * istride, 0, 0, AUX);
   }
 };
 

@@ -38,6 +38,8 @@ constexpr int KTB = 128;      // bytes of K per LDS row and stage
 constexpr int NR = 32;        // narrow rows
 constexpr int THREADS = 256;  // 4 wavefronts (fast::NW)
 constexpr int LDS_RING = 147456;  // bytes of LDS ring per workgroup (one workgroup per CU)
+constexpr int AUX_NT = 2;         // buffer cache-policy bit: non-temporal (gfx950)
+
 static_assert(THREADS == 64 * NW, "loaders assume NW wavefronts");
 
 template <int N>
@@ -114,8 +116,10 @@ __global__ __launch_bounds__(THREADS) void gemm_stream_kernel(DenseArgs p) {
     const bool live = t < nkl;
     int kt = t + rot;
     kt = kt0 + (kt >= nkl ? kt - nkl : kt);
-    la.issue_if(stage(t), kt, 0, LdA::INSTR, wave, live);
-    lb.issue_if(stage(t) + GA::BYTES, kt, 0, LdB::INSTR, wave, live);
+    // the wide operand is read once: non-temporal, so that its lines do not
+    // displace the narrow operand, which every workgroup reads, from the caches
+    la.template issue_if<WIDE_A ? AUX_NT : 0>(stage(t), kt, 0, LdA::INSTR, wave, live);
+    lb.template issue_if<WIDE_A ? 0 : AUX_NT>(stage(t) + GA::BYTES, kt, 0, LdB::INSTR, wave, live);
   };
 
   acc_t acc{};
