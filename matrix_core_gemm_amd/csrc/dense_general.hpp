@@ -69,8 +69,9 @@ __global__ __launch_bounds__(256) void gemm_dense_kernel(DenseArgs p) {
   const int kt_begin = (int)blockIdx.y * p.kt_per_split;
   const int nk = min(nk_all - kt_begin, p.kt_per_split);
 
-  TileLoader<EB, LA, BM, NT, ALIGNED> la;
-  TileLoader<EB, LB, BN, NT, ALIGNED> lb;
+  // skinny tiles (BN or BM of 32 for N or M <= 32): the other operand is read once
+  TileLoader<EB, LA, BM, NT, ALIGNED, KT_BYTES, (BN <= 32)> la;
+  TileLoader<EB, LB, BN, NT, ALIGNED, KT_BYTES, (BM <= 32)> lb;
   auto load_tiles = [&](int kt) {
     const int64_t k0 = (int64_t)(kt_begin + kt) * KE;
     if constexpr (LA == LAYOUT_K) la.load(p.A, p.lda, m0, k0, p.M, p.K, tid);

@@ -57,8 +57,10 @@ __device__ __forceinline__ int swz(int row) {
 // Global -> registers -> LDS staging of one operand tile by NT threads.
 // The tile covers storage rows [row0, row0 + R) and contiguous elements
 // [col0, col0 + W/EB) of a matrix with leading dimension ld (elements); rows at
-// or beyond rlim and elements at or beyond clim read as zero.
-template <int EB, int LAYOUT, int ROWS_MN, int NT, bool ALIGNED, int KTB = KT_BYTES>
+// or beyond rlim and elements at or beyond clim read as zero.  ONCE: every
+// element is read by one workgroup only (the wide operand of a skinny problem),
+// so the 16-byte loads are non-temporal.
+template <int EB, int LAYOUT, int ROWS_MN, int NT, bool ALIGNED, int KTB = KT_BYTES, bool ONCE = false>
 struct TileLoader {
   using G = TileGeom<EB, LAYOUT, ROWS_MN, KTB>;
   static constexpr int PER_THREAD = G::CHUNKS / NT;
@@ -76,7 +78,7 @@ struct TileLoader {
       const int64_t gr = row0 + r, gc = col0 + (int64_t)cc * EPC;
       const char* p = base + (gr * ld + gc) * EB;
       if (ALIGNED && gr < rlim && gc + EPC <= clim) {
-        regs[t] = *(const i32x4*)p;
+        regs[t] = ONCE ? __builtin_nontemporal_load((const i32x4*)p) : *(const i32x4*)p;
       } else {
         union { i32x4 v; char b[16]; } u;
         u.v = i32x4{0, 0, 0, 0};
