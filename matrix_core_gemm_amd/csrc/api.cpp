@@ -160,6 +160,37 @@ static mcg::F64Args f64_args(int64_t M, int64_t N, int64_t K, const void* A, int
   return a;
 }
 
+// The stream-K form of a pipelined plan: fills the sk_* fields of a, sets *tile
+// (the tile size to launch) and returns the workspace bytes, or 0 for none.  A
+// 128 x 128 plan that has no stream-K split of its own although its last round
+// leaves CUs idle takes the 256 x 256 split instead when K is long (at least
+// LONG_K_TILES K tiles of 128 bytes) and that split needs at most alt_cap bytes:
+// a few 256 x 256 tiles cut along K then beat the 128 x 128 tiles whole
+// (measured, bf16 1536^2 x 16384: 110 against 126 us, 134 against 169 us from a
+// flushed cache; 2560^2 x 16384: 213 against 252 us; below about 256 K tiles the
+// two are even, and with whole rounds of 128 x 128 tiles, as at 2048^2, the
+// 128 x 128 tiles are faster while the operands stay in the caches).
+constexpr int64_t LONG_K_TILES = 256;
+
+static int64_t dense_streamk(int dtypeA, int layoutA, int layoutB, mcg::DenseArgs& a, bool aligned, int kernel,
+                             int64_t alt_cap, int* tile) {
+  const int ncu = current_num_cu();
+  *tile = kernel == mcg::KERNEL_MID ? 128 : 256;
+  const int64_t need = mcg::plan_streamk(dtypeA, a, ncu, *tile);
+  if (need > 0 || kernel != mcg::KERNEL_MID) return need;
+  const int64_t tiles128 = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+  if (tiles128 % ncu == 0 || a.K * elem_bytes(dtypeA) < LONG_K_TILES * 128 ||
+      !mcg::fast_path_ok(dtypeA, layoutA, layoutB, a, aligned, 256))
+    return 0;
+  const int64_t alt = mcg::plan_streamk(dtypeA, a, ncu, 256);
+  if (alt <= 0 || alt > alt_cap) {
+    a.dp_tiles = a.sk_tiles = a.sk_wgs = 0;
+    return 0;
+  }
+  *tile = 256;
+  return alt;
+}
+
 // gemm_dense, gemm_dense_ws and gemm_dense_noalloc: ws (ws_bytes) is the
 // caller's workspace, or null; use_static: take the stream-K slots from the
 // library's static scratch, rejecting plans that need more than it holds.
@@ -204,9 +235,10 @@ static int dense_impl(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t 
   const mcg::DensePlan plan =
       mcg::plan_dense(dtypeA, layoutA, layoutB, a, aligned, can_split_k(a, C, D), current_num_cu());
   const bool pipelined = plan.kernel == mcg::KERNEL_FAST || plan.kernel == mcg::KERNEL_MID;
-  const int tile = plan.kernel == mcg::KERNEL_MID ? 128 : 256;
+  int tile = 0;
   if (pipelined && use_static) {
-    const int64_t need = mcg::plan_streamk(dtypeA, a, current_num_cu(), tile);
+    const int64_t need =
+        dense_streamk(dtypeA, layoutA, layoutB, a, aligned, plan.kernel, mcg::STATIC_SCRATCH_BYTES, &tile);
     if (need > mcg::STATIC_SCRATCH_BYTES) return MCG_ERR_SCRATCH_LIMIT;
     if (need > 0) {
       void* p = nullptr;
@@ -217,7 +249,7 @@ static int dense_impl(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t 
     }
   }
   if (pipelined && ws != nullptr) {
-    const int64_t need = mcg::plan_streamk(dtypeA, a, current_num_cu(), tile);
+    const int64_t need = dense_streamk(dtypeA, layoutA, layoutB, a, aligned, plan.kernel, INT64_MAX, &tile);
     if (need > 0 && need <= ws_bytes) {
       a.ws = ws;
       return hip_status(mcg::launch_fast_sk(dtypeA, dtypeB, layoutA, layoutB, a, (hipStream_t)stream, tile));
@@ -483,10 +515,16 @@ int64_t mcg_dense_workspace_bytes(int dtypeA, int layoutA, int layoutB, int64_t 
   const int kernel = dense_plan(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb, true).kernel;
   if (kernel != mcg::KERNEL_FAST && kernel != mcg::KERNEL_MID) return 0;
   mcg::DenseArgs a{};
+  a.A = (const char*)A;
+  a.B = (const char*)B;
   a.M = M;
   a.N = N;
   a.K = K;
-  return mcg::plan_streamk(dtypeA, a, current_num_cu(), kernel == mcg::KERNEL_MID ? 128 : 256);
+  a.lda = lda;
+  a.ldb = ldb;
+  int tile = 0;
+  return dense_streamk(dtypeA, layoutA, layoutB, a, dense_aligned(elem_bytes(dtypeA), K, A, lda, B, ldb), kernel,
+                       INT64_MAX, &tile);
 }
 
 int mcg_dense_splits(int dtypeA, int layoutA, int layoutB, int64_t M, int64_t N, int64_t K, const void* A,

@@ -236,3 +236,72 @@ def test_sparse_streamk_against_oracle(case):
         r = oracle.check_float(got, ref, s, K, alpha, beta=beta, c=cc, out=out if out == "f16" else "f32")
     say("  ", {k: v for k, v in r.items() if k != "worst"})
     assert r["ok"], r
+
+
+LONG_K_CASES = [  # dtA, dtB, layA, layB, M, N, K, out, alpha, beta, D aliases C
+    # 144 tiles of 128 x 128 fill no second round and cannot be cut (2 pieces would
+    # need 288 CUs): 36 tiles of 256 x 256 in 4 pieces of 64 K tiles instead
+    ("bf16", "bf16", "k_contig", "k_contig", 1536, 1536, 16384, "f32", 1.0, 0.5, False),
+    ("i8", "i8", "k_contig", "mn_contig", 1536, 1536, 32768, "i32", 2, -1, False),
+    # ragged M and N, a last K tile cut short (K = 16592: 260 K tiles, the last a
+    # quarter full), 42 tiles in 5 pieces, D aliasing C
+    ("bf16", "bf16", "mn_contig", "k_contig", 1504, 1700, 16592, "bf16", -1.0, 1.0, True),
+]
+
+
+@pytest.mark.parametrize("case", LONG_K_CASES, ids=["bf16", "i8_mn", "ragged_bf16out_alias"])
+def test_long_k_mid_plan_takes_256_streamk(case):
+    """A 128 x 128 plan with no stream-K split of its own and at least 256 K
+    tiles runs as 256 x 256 stream-K when a workspace is given."""
+    mcg = need_gpu()
+    dtA, dtB, layA, layB, M, N, K, out, alpha, beta, alias = case
+    say(f"long-K stream-K {dtA} {layA}/{layB} {M}x{N}x{K} -> {out} alias={alias}")
+    dist = "int8" if dtA == "i8" else "normal"
+    A = W.operand("A", dtA, M, K, dist, layA, seed=81)
+    B = W.operand("B", dtB, K, N, dist, layB, seed=82)
+    dA, dB = dev(A.codes), dev(B.codes)
+    assert mcg.dense_path(dtA, layA, layB, M, N, K, dA, A.ld, dB, B.ld) == 6
+    need = mcg.dense_workspace_bytes(dtA, layA, layB, M, N, K, dA, A.ld, dB, B.ld)
+    tm, tn = -(-M // 256), -(-N // 256)
+    assert need > 0 and need % (256 * 256 * 4) == 0 and need // (256 * 256 * 4) % (tm * tn) == 0
+    ldc = N
+    if out == "i32":
+        C = W.c_matrix(M, N, "int20", seed=83, ldc=ldc)
+        D = torch.full((M, ldc), -0x5A5A5A5A, dtype=torch.int32, device="cuda")
+        dC = dev(C)
+    elif out == "f32":
+        C = W.c_matrix(M, N, "normal", seed=83, ldc=ldc)
+        D = torch.full((M, ldc), float("nan"), dtype=torch.float32, device="cuda")
+        dC = dev(C)
+    else:
+        C = W.draw("normal", (M, ldc), 83).to(torch.float32).to(torch.bfloat16).view(torch.int16).numpy()
+        dC = dev(C)
+        C = C.view(np.uint16)
+        D = torch.full((M, ldc), 0x7FC0, dtype=torch.int16, device="cuda")
+    if alias:
+        D = dC
+    mcg.gemm_dense_ws(dtA, dtB, layA, layB, M, N, K, dA, A.ld, dB, B.ld, dC, D, ldc, out, alpha, beta,
+                      A.scale, B.scale, workspace=workspace(need))
+    torch.cuda.synchronize()
+    d = D.cpu().numpy()
+    # four whole tiles (the last one ragged when M, N are) and sampled outputs
+    tiles = [(0, 0), (1, 2), (tm - 1, 0), (tm - 1, tn - 1)]
+    r1, c1 = tile_coords(tiles, M, N)
+    r2, c2 = W.sample_coords(M, N, n_random=2048, full_rows=(M - 1,), full_cols=(N - 1,))
+    rows, cols = np.concatenate([r1, r2]), np.concatenate([c1, c2])
+    say(f"  {tm * tn} tiles, {need // (256 * 256 * 4)} pieces, {len(rows)} outputs compared")
+    if out == "i32":
+        ref = oracle.gemm_i8(layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, ldc, alpha, beta,
+                             rows=rows, cols=cols)
+        r = oracle.check_exact(d[rows, cols], ref)
+    else:
+        ref, s = oracle.gemm_float(dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, ldc,
+                                   alpha, beta, A.scale, B.scale, rows=rows, cols=cols, out=out)
+        if out == "bf16":
+            dec = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).double().numpy()
+            got, cc = dec(d)[rows, cols], dec(C)[rows, cols]
+        else:
+            got, cc = d[rows, cols], C[rows, cols]
+        r = oracle.check_float(got, ref, s, K, alpha, A.scale, B.scale, beta, cc, out=out)
+    say("  ", {k: v for k, v in r.items() if k != "worst"})
+    assert r["ok"], r

@@ -97,6 +97,15 @@ def test_workspace_plan(monkeypatch):
     # 1280^2 x 16384 is 100 tiles, cut in two (three would need 300 CUs)
     assert _ws(mcg, "bf16", 1024, 2048, 8192) == 256 * 128 * 128 * 4
     assert _ws(mcg, "bf16", 1280, 1280, 16384) == 200 * 128 * 128 * 4
+    # long K on the 128 x 128 form without a split of its own (1536^2 is 144 tiles:
+    # two pieces each would need 288 CUs): from 256 K tiles of 128 bytes on, the
+    # 256 x 256 split, here 36 tiles in 4 pieces of 64 K tiles (2560^2: 100 tiles in 2)
+    assert _ws(mcg, "bf16", 1536, 1536, 16384) == 144 * slot
+    assert _ws(mcg, "i8", 1536, 1536, 32768) == 144 * slot
+    assert _ws(mcg, "bf16", 2560, 2560, 16384) == 200 * slot
+    assert _ws(mcg, "bf16", 2048, 2048, 16384) == 0  # 256 tiles of 128 x 128: one whole round
+    assert _ws(mcg, "bf16", 1536, 1536, 12288) == 0  # 192 K tiles: the two forms are even
+    assert _ws(mcg, "i8", 1536, 1536, 16384) == 0
     # not the pipelined kernel (skinny, binary64)
     assert _ws(mcg, "bf16", 32768, 16, 8192) == 0
     assert mcg.dense_workspace_bytes("f64", "k_contig", "k_contig", 7168, 7168, 7168, 0x1000, 7168, 0x1000,
