@@ -249,4 +249,107 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const lds_char* base, int off) {
       (__attribute__((address_space(3))) i32x2*)(const_cast<lds_char*>(base) + off));
 }
 
+// Transposing LDS reads in inline asm: four 8-byte reads per address a[n], at byte
+// offsets 0, O1, O2, O3 from it, in one block that waits for all of them
+// (lgkmcnt(0)) before it ends, so that no read is still in flight once the
+// compiler owns the output registers.  The compiler precedes its own
+// transposing-read builtins with a wait for all of the wavefront's outstanding
+// buffer_load ... lds transfers (it cannot tell which LDS bytes those write),
+// which drains a kernel's prefetch ring at every K tile; these reads are ordered
+// against the transfers by the kernel's own vmcnt waits and barriers, as its
+// ordinary LDS reads are.  Issue the ordinary LDS reads of the same phase before
+// the block: its wait then covers them too.
+#define MCG_TR_X2(OP)                                                    \
+  asm volatile(                                                          \
+      OP " %0, %8\n\t"                                                   \
+      OP " %1, %8 offset:%c10\n\t"                                       \
+      OP " %2, %8 offset:%c11\n\t"                                       \
+      OP " %3, %8 offset:%c12\n\t"                                       \
+      OP " %4, %9\n\t"                                                   \
+      OP " %5, %9 offset:%c10\n\t"                                       \
+      OP " %6, %9 offset:%c11\n\t"                                       \
+      OP " %7, %9 offset:%c12\n\t"                                       \
+      "s_waitcnt lgkmcnt(0)"                                             \
+      : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]),  \
+        "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(r[1][2]), "=&v"(r[1][3])   \
+      : "v"(a[0]), "v"(a[1]), "i"(O1), "i"(O2), "i"(O3)                  \
+      : "memory")
+#define MCG_TR_X4(OP)                                                          \
+  asm volatile(                                                                \
+      OP " %0, %16\n\t"                                                        \
+      OP " %1, %16 offset:%c20\n\t"                                            \
+      OP " %2, %16 offset:%c21\n\t"                                            \
+      OP " %3, %16 offset:%c22\n\t"                                            \
+      OP " %4, %17\n\t"                                                        \
+      OP " %5, %17 offset:%c20\n\t"                                            \
+      OP " %6, %17 offset:%c21\n\t"                                            \
+      OP " %7, %17 offset:%c22\n\t"                                            \
+      OP " %8, %18\n\t"                                                        \
+      OP " %9, %18 offset:%c20\n\t"                                            \
+      OP " %10, %18 offset:%c21\n\t"                                           \
+      OP " %11, %18 offset:%c22\n\t"                                           \
+      OP " %12, %19\n\t"                                                       \
+      OP " %13, %19 offset:%c20\n\t"                                           \
+      OP " %14, %19 offset:%c21\n\t"                                           \
+      OP " %15, %19 offset:%c22\n\t"                                           \
+      "s_waitcnt lgkmcnt(0)"                                                   \
+      : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]),        \
+        "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(r[1][2]), "=&v"(r[1][3]),        \
+        "=&v"(r[2][0]), "=&v"(r[2][1]), "=&v"(r[2][2]), "=&v"(r[2][3]),        \
+        "=&v"(r[3][0]), "=&v"(r[3][1]), "=&v"(r[3][2]), "=&v"(r[3][3])         \
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(O1), "i"(O2), "i"(O3)  \
+      : "memory")
+#define MCG_TR_X6(OP)                                                                                \
+  asm volatile(                                                                                      \
+      OP " %0, %24\n\t"                                                                              \
+      OP " %1, %24 offset:%c30\n\t"                                                                  \
+      OP " %2, %24 offset:%c31\n\t"                                                                  \
+      OP " %3, %24 offset:%c32\n\t"                                                                  \
+      OP " %4, %25\n\t"                                                                              \
+      OP " %5, %25 offset:%c30\n\t"                                                                  \
+      OP " %6, %25 offset:%c31\n\t"                                                                  \
+      OP " %7, %25 offset:%c32\n\t"                                                                  \
+      OP " %8, %26\n\t"                                                                              \
+      OP " %9, %26 offset:%c30\n\t"                                                                  \
+      OP " %10, %26 offset:%c31\n\t"                                                                 \
+      OP " %11, %26 offset:%c32\n\t"                                                                 \
+      OP " %12, %27\n\t"                                                                             \
+      OP " %13, %27 offset:%c30\n\t"                                                                 \
+      OP " %14, %27 offset:%c31\n\t"                                                                 \
+      OP " %15, %27 offset:%c32\n\t"                                                                 \
+      OP " %16, %28\n\t"                                                                             \
+      OP " %17, %28 offset:%c30\n\t"                                                                 \
+      OP " %18, %28 offset:%c31\n\t"                                                                 \
+      OP " %19, %28 offset:%c32\n\t"                                                                 \
+      OP " %20, %29\n\t"                                                                             \
+      OP " %21, %29 offset:%c30\n\t"                                                                 \
+      OP " %22, %29 offset:%c31\n\t"                                                                 \
+      OP " %23, %29 offset:%c32\n\t"                                                                 \
+      "s_waitcnt lgkmcnt(0)"                                                                         \
+      : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3]),                              \
+        "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(r[1][2]), "=&v"(r[1][3]),                              \
+        "=&v"(r[2][0]), "=&v"(r[2][1]), "=&v"(r[2][2]), "=&v"(r[2][3]),                              \
+        "=&v"(r[3][0]), "=&v"(r[3][1]), "=&v"(r[3][2]), "=&v"(r[3][3]),                              \
+        "=&v"(r[4][0]), "=&v"(r[4][1]), "=&v"(r[4][2]), "=&v"(r[4][3]),                              \
+        "=&v"(r[5][0]), "=&v"(r[5][1]), "=&v"(r[5][2]), "=&v"(r[5][3])                               \
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "i"(O1), "i"(O2), "i"(O3)  \
+      : "memory")
+
+template <int EB, int O1, int O2, int O3, int N>
+__device__ __forceinline__ void lds_read_tr_x4(const uint32_t (&a)[N], i32x2 (&r)[N][4]) {
+  static_assert(N == 2 || N == 4 || N == 6, "2, 4 or 6 addresses");
+  static_assert(O1 > 0 && O2 > O1 && O3 > O2 && O3 < 65536, "ds offsets");
+  if constexpr (EB == 2 && N == 2) MCG_TR_X2("ds_read_b64_tr_b16");
+  else if constexpr (EB == 2 && N == 4) MCG_TR_X4("ds_read_b64_tr_b16");
+  else if constexpr (EB == 2) MCG_TR_X6("ds_read_b64_tr_b16");
+  else if constexpr (N == 2) MCG_TR_X2("ds_read_b64_tr_b8");
+  else if constexpr (N == 4) MCG_TR_X4("ds_read_b64_tr_b8");
+  else MCG_TR_X6("ds_read_b64_tr_b8");
+}
+#undef MCG_TR_X2
+#undef MCG_TR_X4
+#undef MCG_TR_X6
+
+__device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
+
 }  // namespace mcg

@@ -182,6 +182,20 @@ struct Reader {
       return i32x4{lo.x, lo.y, hi.x, hi.y};
     }
   }
+  // MN-contiguous tiles: LDS byte address of the first of the transposing reads
+  // read16k makes for block rb and K bytes kb; the reads of kb + 32 (16-bit) or
+  // kb + 16, kb + 32 (8-bit) lie whole rows further, in rows of the same swizzle
+  __device__ static __forceinline__ uint32_t mn_addr(const lds_char* tile, int rb, int kb, int lane) {
+    static_assert(LAYOUT == LAYOUT_MN, "transposing reads");
+    const int L = lane & 15;
+    if constexpr (EB == 2) {
+      const int col = rb + 16 * ((lane >> 4) & 1) + 4 * (L & 3);
+      return lds_addr(tile + addr(kb / 2 + (L >> 2), 2 * col));
+    } else {
+      const int col = rb + 16 * ((lane >> 4) & 1) + 8 * (L & 1);
+      return lds_addr(tile + addr(kb + (L >> 1), col));
+    }
+  }
   // dense 32x32 instructions: lane group g owns tile K bytes [32g, 32g + 32);
   // sub-step s is its half [32g + 16s, +16)
   __device__ static __forceinline__ i32x4 read16(const lds_char* tile, int rb, int s, int lane) {

@@ -139,31 +139,69 @@ void gemm_fast_kernel(DenseArgs p) {
 
   frag_t fa[S][WTM], fb[S][WTN];
   // fragments of half h (K bytes [64h, 64h + 64) of each row) of K tile kt;
-  // instruction s of the half takes lane group g's bytes [64h + 2 LB16 s + LB16 g, +LB16)
+  // instruction s of the half takes lane group g's bytes [64h + 2 LB16 s + LB16 g, +LB16).
+  // K-contiguous operands take ordinary LDS reads; MN-contiguous ones take their
+  // transposing reads in inline-asm blocks (lds_read_tr_x4), issued after the
+  // ordinary reads.  A lane's 4 transposing reads of a 32-row block lie TR_O1,
+  // TR_O2, TR_O3 bytes after the first: the second read of a 16-byte part is 4
+  // (16-bit) or 8 (8-bit) rows further, the next part 16 or 32 rows.
+  constexpr int TRW = TB * EB;  // bytes per LDS row (one k) of an MN-contiguous tile
+  constexpr int TR_O1 = EB == 2 ? 4 * TRW : 8 * TRW;
+  constexpr int TR_O2 = (LB16 == 32 || EB == 2) ? 16 * TRW : 32 * TRW;
+  constexpr int TR_O3 = TR_O2 + TR_O1;
+  constexpr int NTA = LA == LAYOUT_MN ? WTM : 0, NTB = LB == LAYOUT_MN ? WTN : 0;
+  auto unpack = [&](const i32x2 (&r)[4], frag_t& f0, frag_t& f1) {
+    if constexpr (LB16 == 16) {
+      f0 = frag_t{r[0].x, r[0].y, r[1].x, r[1].y};
+      f1 = frag_t{r[2].x, r[2].y, r[3].x, r[3].y};
+    } else {
+      f0 = frag_t{r[0].x, r[0].y, r[1].x, r[1].y, r[2].x, r[2].y, r[3].x, r[3].y};
+    }
+  };
   auto read_frags = [&](int kt, int h) {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int kb = 64 * h + 2 * LB16 * s + LB16 * g;
+      if constexpr (LA == LAYOUT_K) {
 #pragma unroll
-      for (int i = 0; i < WTM; ++i) {
-        if constexpr (LB16 == 16) {
-          fa[s][i] = RA::read16k(stA(kt), rbA + 32 * i, kb, lane);
-        } else {
-          const i32x4 x = RA::read16k(stA(kt), rbA + 32 * i, kb, lane);
-          const i32x4 y = RA::read16k(stA(kt), rbA + 32 * i, kb + 16, lane);
-          fa[s][i] = frag_t{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+        for (int i = 0; i < WTM; ++i) {
+          if constexpr (LB16 == 16) {
+            fa[s][i] = RA::read16k(stA(kt), rbA + 32 * i, kb, lane);
+          } else {
+            const i32x4 x = RA::read16k(stA(kt), rbA + 32 * i, kb, lane);
+            const i32x4 y = RA::read16k(stA(kt), rbA + 32 * i, kb + 16, lane);
+            fa[s][i] = frag_t{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+          }
         }
       }
+      if constexpr (LB == LAYOUT_K) {
 #pragma unroll
-      for (int j = 0; j < WTN; ++j) {
-        if constexpr (LB16 == 16) {
-          fb[s][j] = RB::read16k(stB(kt), rbB + 32 * j, kb, lane);
-        } else {
-          const i32x4 x = RB::read16k(stB(kt), rbB + 32 * j, kb, lane);
-          const i32x4 y = RB::read16k(stB(kt), rbB + 32 * j, kb + 16, lane);
-          fb[s][j] = frag_t{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+        for (int j = 0; j < WTN; ++j) {
+          if constexpr (LB16 == 16) {
+            fb[s][j] = RB::read16k(stB(kt), rbB + 32 * j, kb, lane);
+          } else {
+            const i32x4 x = RB::read16k(stB(kt), rbB + 32 * j, kb, lane);
+            const i32x4 y = RB::read16k(stB(kt), rbB + 32 * j, kb + 16, lane);
+            fb[s][j] = frag_t{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+          }
         }
       }
+    }
+    if constexpr (NTA + NTB > 0) {
+      const int kb0 = 64 * h + LB16 * g;
+      uint32_t ad[NTA + NTB];  // one block: 2, 4 or 6 addresses
+      i32x2 r[NTA + NTB][4];
+      if constexpr (NTA > 0)
+#pragma unroll
+        for (int i = 0; i < NTA; ++i) ad[i] = RA::mn_addr(stA(kt), rbA + 32 * i, kb0, lane);
+      if constexpr (NTB > 0)
+#pragma unroll
+        for (int j = 0; j < NTB; ++j) ad[NTA + j] = RB::mn_addr(stB(kt), rbB + 32 * j, kb0, lane);
+      lds_read_tr_x4<EB, TR_O1, TR_O2, TR_O3>(ad, r);
+#pragma unroll
+      for (int i = 0; i < NTA; ++i) unpack(r[i], fa[0][i], fa[S - 1][i]);
+#pragma unroll
+      for (int j = 0; j < NTB; ++j) unpack(r[NTA + j], fb[0][j], fb[S - 1][j]);
     }
   };
   auto multiply = [&]() {
@@ -174,23 +212,13 @@ void gemm_fast_kernel(DenseArgs p) {
 #pragma unroll
         for (int j = 0; j < WTN; ++j) Op::mma(acc[i][j], fb[s][j], fa[s][i]);
   };
-  // Memory phase of half tile (t, H): this group's DMA half and the fragment
-  // reads.  The DMA targets another stage than the reads, so with K-contiguous
-  // operands it goes first (more time in flight).  Transposing reads of an
-  // MN-contiguous operand are preceded by a compiler-inserted wait for all of
-  // the wave's LDS DMA, so there the reads go first.
-  auto dma = [&](auto hc, int t) {
+  // Memory phase of half tile (t, H): this group's DMA half, then the fragment
+  // reads (the DMA targets another stage than the reads, so it goes first: more
+  // time in flight).
+  auto mem = [&](auto hc, int t) {
     if constexpr (decltype(hc)::value == 0) issueA(t + 1);
     else issueB(t + 2);
-  };
-  auto mem = [&](auto hc, int t) {
-    if constexpr (LA == LAYOUT_K && LB == LAYOUT_K) {
-      dma(hc, t);
-      read_frags(t, decltype(hc)::value);
-    } else {
-      read_frags(t, decltype(hc)::value);
-      dma(hc, t);
-    }
+    read_frags(t, decltype(hc)::value);
   };
 
   // Half tiles u = 2t + h.  Group 0 reads half u in slot 2u - 1 and multiplies

@@ -262,14 +262,36 @@ void gemm_sparse_fast_kernel(SparseArgs p) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) fa[s][i] = RA::read16k(stA(T), rbA + 32 * i, 64 * h + 32 * s + 16 * g, lane);
     }
+    if constexpr (LB == LAYOUT_K) {
 #pragma unroll
-    for (int j = 0; j < WTN; ++j)
+      for (int j = 0; j < WTN; ++j)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const i32x4 lo = RB::read16k(stBh(grp, u), rbBh + 32 * j, 64 * s + 16 * g, lane);
-        const i32x4 hi = RB::read16k(stBh(grp, u), rbBh + 32 * j, 64 * s + 32 + 16 * g, lane);
-        fb[s][j] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      }
+        for (int s = 0; s < 2; ++s) {
+          const i32x4 lo = RB::read16k(stBh(grp, u), rbBh + 32 * j, 64 * s + 16 * g, lane);
+          const i32x4 hi = RB::read16k(stBh(grp, u), rbBh + 32 * j, 64 * s + 32 + 16 * g, lane);
+          fb[s][j] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        }
+    } else {
+      // transposing reads in one inline-asm block, after the ordinary reads above
+      // (lds_read_tr_x4): per block j and step s, the reads of lo lie at rows r and
+      // r + 4 (16-bit) or r + 8 (8-bit), those of hi 16 or 32 rows further
+      constexpr int TRW = 128 * EB;  // bytes per LDS row (one k) of a B half
+      constexpr int O1 = EB == 2 ? 4 * TRW : 8 * TRW, O2 = EB == 2 ? 16 * TRW : 32 * TRW;
+      uint32_t ad[2 * WTN];
+      i32x2 r[2 * WTN][4];
+#pragma unroll
+      for (int j = 0; j < WTN; ++j)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) ad[2 * j + s] = RB::mn_addr(stBh(grp, u), rbBh + 32 * j, 64 * s + 16 * g, lane);
+      lds_read_tr_x4<EB, O1, O2, O1 + O2>(ad, r);
+#pragma unroll
+      for (int j = 0; j < WTN; ++j)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const i32x2(&q)[4] = r[2 * j + s];
+          fb[s][j] = i32x8{q[0].x, q[0].y, q[1].x, q[1].y, q[2].x, q[2].y, q[3].x, q[3].y};
+        }
+    }
   };
   auto multiply = [&]() {
 #pragma unroll
