@@ -212,13 +212,16 @@ void gemm_fast_kernel(DenseArgs p) {
 #pragma unroll
         for (int j = 0; j < WTN; ++j) Op::mma(acc[i][j], fb[s][j], fa[s][i]);
   };
-  // Memory phase of half tile (t, H): this group's DMA half, then the fragment
-  // reads (the DMA targets another stage than the reads, so it goes first: more
-  // time in flight).
+  // Memory phase of half tile (t, H): this group's DMA half and the fragment
+  // reads.  The DMA targets another stage than the reads, so it goes first (more
+  // time in flight), except with both operands MN-contiguous, where the reads go
+  // first (measured: 1-2% faster there and 18% less HBM traffic at bf16 8192^3,
+  // 1-2% slower with one MN-contiguous operand).
   auto mem = [&](auto hc, int t) {
+    if constexpr (LA == LAYOUT_MN && LB == LAYOUT_MN) read_frags(t, decltype(hc)::value);
     if constexpr (decltype(hc)::value == 0) issueA(t + 1);
     else issueB(t + 2);
-    read_frags(t, decltype(hc)::value);
+    if constexpr (!(LA == LAYOUT_MN && LB == LAYOUT_MN)) read_frags(t, decltype(hc)::value);
   };
 
   // Half tiles u = 2t + h.  Group 0 reads half u in slot 2u - 1 and multiplies
