@@ -259,6 +259,16 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const lds_char* base, int off) {
 // against the transfers by the kernel's own vmcnt waits and barriers, as its
 // ordinary LDS reads are.  Issue the ordinary LDS reads of the same phase before
 // the block: its wait then covers them too.
+#define MCG_TR_X1(OP)                                                   \
+  asm volatile(                                                         \
+      OP " %0, %4\n\t"                                                  \
+      OP " %1, %4 offset:%c5\n\t"                                       \
+      OP " %2, %4 offset:%c6\n\t"                                       \
+      OP " %3, %4 offset:%c7\n\t"                                       \
+      "s_waitcnt lgkmcnt(0)"                                            \
+      : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[0][2]), "=&v"(r[0][3])  \
+      : "v"(a[0]), "i"(O1), "i"(O2), "i"(O3)                            \
+      : "memory")
 #define MCG_TR_X2(OP)                                                    \
   asm volatile(                                                          \
       OP " %0, %8\n\t"                                                   \
@@ -334,21 +344,55 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const lds_char* base, int off) {
         "=&v"(r[5][0]), "=&v"(r[5][1]), "=&v"(r[5][2]), "=&v"(r[5][3])                               \
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "i"(O1), "i"(O2), "i"(O3)  \
       : "memory")
+#define MCG_TR_P1(OP)                   \
+  asm volatile(                         \
+      OP " %0, %2\n\t"                  \
+      OP " %1, %2 offset:%c3\n\t"       \
+      "s_waitcnt lgkmcnt(0)"            \
+      : "=&v"(r[0][0]), "=&v"(r[0][1])  \
+      : "v"(a[0]), "i"(O1)              \
+      : "memory")
+#define MCG_TR_P2(OP)                    \
+  asm volatile(                          \
+      OP " %0, %4\n\t"                   \
+      OP " %1, %4 offset:%c6\n\t"        \
+      OP " %2, %5\n\t"                   \
+      OP " %3, %5 offset:%c6\n\t"        \
+      "s_waitcnt lgkmcnt(0)"             \
+      : "=&v"(r[0][0]), "=&v"(r[0][1]),  \
+        "=&v"(r[1][0]), "=&v"(r[1][1])   \
+      : "v"(a[0]), "v"(a[1]), "i"(O1)    \
+      : "memory")
 
 template <int EB, int O1, int O2, int O3, int N>
 __device__ __forceinline__ void lds_read_tr_x4(const uint32_t (&a)[N], i32x2 (&r)[N][4]) {
-  static_assert(N == 2 || N == 4 || N == 6, "2, 4 or 6 addresses");
+  static_assert(N == 1 || N == 2 || N == 4 || N == 6, "1, 2, 4 or 6 addresses");
   static_assert(O1 > 0 && O2 > O1 && O3 > O2 && O3 < 65536, "ds offsets");
-  if constexpr (EB == 2 && N == 2) MCG_TR_X2("ds_read_b64_tr_b16");
+  if constexpr (EB == 2 && N == 1) MCG_TR_X1("ds_read_b64_tr_b16");
+  else if constexpr (EB == 2 && N == 2) MCG_TR_X2("ds_read_b64_tr_b16");
   else if constexpr (EB == 2 && N == 4) MCG_TR_X4("ds_read_b64_tr_b16");
   else if constexpr (EB == 2) MCG_TR_X6("ds_read_b64_tr_b16");
+  else if constexpr (N == 1) MCG_TR_X1("ds_read_b64_tr_b8");
   else if constexpr (N == 2) MCG_TR_X2("ds_read_b64_tr_b8");
   else if constexpr (N == 4) MCG_TR_X4("ds_read_b64_tr_b8");
   else MCG_TR_X6("ds_read_b64_tr_b8");
 }
+// The same with two reads per address, at byte offsets 0 and O1.
+template <int EB, int O1, int N>
+__device__ __forceinline__ void lds_read_tr_x2(const uint32_t (&a)[N], i32x2 (&r)[N][2]) {
+  static_assert(N == 1 || N == 2, "1 or 2 addresses");
+  static_assert(O1 > 0 && O1 < 65536, "ds offset");
+  if constexpr (EB == 2 && N == 1) MCG_TR_P1("ds_read_b64_tr_b16");
+  else if constexpr (EB == 2) MCG_TR_P2("ds_read_b64_tr_b16");
+  else if constexpr (N == 1) MCG_TR_P1("ds_read_b64_tr_b8");
+  else MCG_TR_P2("ds_read_b64_tr_b8");
+}
+#undef MCG_TR_X1
 #undef MCG_TR_X2
 #undef MCG_TR_X4
 #undef MCG_TR_X6
+#undef MCG_TR_P1
+#undef MCG_TR_P2
 
 __device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
 

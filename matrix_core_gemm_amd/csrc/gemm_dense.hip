@@ -65,7 +65,7 @@ constexpr double KT_US = 1.0, ROUND_US = 3.0, ATOMIC_US = 1.4e-5, SPLIT_US = 5.0
 constexpr double MID_KT_US = 0.5, MID_ROUND_US = 3.0, MID_MARGIN = 0.95;
 // The streaming kernel is HBM-bound: split only when there are too few blocks
 // to spread over the CUs, keeping 16 K tiles or more per split.
-constexpr int64_t STREAM_MIN_BLOCKS = 64, STREAM_MIN_KT = 16;
+constexpr int64_t STREAM_MIN_BLOCKS = 64, STREAM_MIN_KT = 16, STREAM_MN_MIN_WIDE = 2048;
 }  // namespace
 
 DensePlan plan_dense(int dtA, int la, int lb, const DenseArgs& a, bool aligned, bool can_split, int num_cu) {
@@ -116,15 +116,26 @@ DensePlan plan_dense(int dtA, int la, int lb, const DenseArgs& a, bool aligned, 
     const double t_mid = (double)cdiv(tiles, NUM_CU) * (MID_KT_US * (double)nk + MID_ROUND_US);
     if (t_mid < MID_MARGIN * t_general) return make(KERNEL_MID, 1);
   }
-  if (stream_path_ok(dtA, la, lb, a, aligned)) {
+  // Skinny problems: the streaming kernel, except with an MN-contiguous wide
+  // operand of fewer than STREAM_MN_MIN_WIDE rows, where the general kernel's
+  // 128 x 32 / 32 x 128 tiles were faster (bf16 1024 x 16 x 3008: 13.2 against
+  // 14.6-17.5 us)
+  const bool wide_a = a.N <= 32 && a.N <= a.M;
+  const int64_t wide = wide_a ? a.M : a.N;
+  const bool wide_mn = (wide_a ? la : lb) == LAYOUT_MN;
+  if (stream_path_ok(dtA, la, lb, a, aligned) && !(wide_mn && wide < STREAM_MN_MIN_WIDE)) {
     // 128-row blocks when that still gives most CUs a block, else 32-row blocks
-    // (measured: more blocks beat wider ones below 16384 rows)
-    const int64_t wide = a.N <= 32 && a.N <= a.M ? a.M : a.N;
-    const int bw = wide >= 64 * NUM_CU ? 128 : 32;
+    // (measured: more blocks beat wider ones below 16384 rows), except for an
+    // MN-contiguous wide operand: its LDS rows are one k of the block's rows, so
+    // only 128-row blocks fetch whole 128-byte lines; those fewer blocks are split
+    // until about 128 workgroups run (measured: 64 blocks unsplit ran at half the
+    // HBM rate, 256 workgroups were slower than 128 at 16384 rows)
+    const int bw = wide >= 64 * NUM_CU || wide_mn ? 128 : 32;
     const int64_t blocks = cdiv(wide, bw);
+    const int64_t want = wide_mn ? 2 * STREAM_MIN_BLOCKS : STREAM_MIN_BLOCKS;
     int64_t s = 1;
-    if (can_split && blocks < STREAM_MIN_BLOCKS)
-      s = std::max<int64_t>(1, std::min(cdiv(STREAM_MIN_BLOCKS, blocks), nk / STREAM_MIN_KT));
+    if (can_split && blocks < want)
+      s = std::max<int64_t>(1, std::min(cdiv(want, blocks), nk / STREAM_MIN_KT));
     DensePlan pl = make(KERNEL_STREAM, s);
     pl.stream_bw = bw;
     return pl;

@@ -11,6 +11,8 @@
 //     per workgroup of 4 wavefronts, BW chosen so that every CU gets a block;
 //     the "narrow" operand has at most 32 rows, zero-filled past M or N, and
 //     is shared by every workgroup through L2;
+//   - either operand may be K- or MN-contiguous (an MN-contiguous tile keeps one
+//     LDS row per k and is gathered with transposing reads);
 //   - K is staged in tiles of 128 bytes per row through a ring of LDS stages
 //     (144 KiB, one workgroup per CU) filled by buffer_load ... lds (whole
 //     128-byte lines per 8 lanes, no VGPRs); all but one stage are in flight
@@ -53,6 +55,40 @@ template <int EB, int BW>
 constexpr int ring_stages() {
   return LDS_RING / ((BW + NR) * KTB);
 }
+
+// One instruction's fragment of a 32-row block of a stage: K-contiguous tiles
+// take ordinary LDS reads; MN-contiguous ones (W bytes per LDS row) take their
+// transposing reads from one inline-asm block that waits for its own reads
+// (lds_read_tr_x2 / lds_read_tr_x4): the read16k reads of kb lie at rows r and
+// r + 4 (16-bit) or r + 8 (8-bit), those of kb + 16 (32-byte lanes) 16 and 24
+// rows after r.
+template <class Op, class Rd, int LAYOUT, int W>
+struct StreamFrag {
+  using frag_t = typename Op::frag_t;
+  static constexpr int EB = Op::EB, LB16 = Op::LANE_BYTES;
+  static __device__ __forceinline__ frag_t read(const lds_char* tile, int rb, int kb, int lane) {
+    if constexpr (LAYOUT == LAYOUT_K) {
+      if constexpr (LB16 == 16) {
+        return Rd::read16k(tile, rb, kb, lane);
+      } else {
+        const i32x4 x = Rd::read16k(tile, rb, kb, lane), y = Rd::read16k(tile, rb, kb + 16, lane);
+        return frag_t{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+      }
+    } else {
+      const uint32_t ad[1] = {Rd::mn_addr(tile, rb, kb, lane)};
+      if constexpr (LB16 == 16) {
+        i32x2 r[1][2];
+        lds_read_tr_x2<EB, (EB == 2 ? 4 : 8) * W>(ad, r);
+        return frag_t{r[0][0].x, r[0][0].y, r[0][1].x, r[0][1].y};
+      } else {
+        static_assert(EB == 1, "32-byte lanes: 8-bit operands");
+        i32x2 r[1][4];
+        lds_read_tr_x4<EB, 8 * W, 16 * W, 24 * W>(ad, r);
+        return frag_t{r[0][0].x, r[0][0].y, r[0][1].x, r[0][1].y, r[0][2].x, r[0][2].y, r[0][3].x, r[0][3].y};
+      }
+    }
+  }
+};
 
 template <class Op, int LA, int LB, bool WIDE_A, int BW>
 __global__ __launch_bounds__(THREADS) void gemm_stream_kernel(DenseArgs p) {
@@ -136,15 +172,15 @@ __global__ __launch_bounds__(THREADS) void gemm_stream_kernel(DenseArgs p) {
     for (int s = 0; s < SPS; ++s) {
       if (KG > 1 && (t * SPS + s) % KG != kg) continue;
       const int kb = 2 * LB16 * s + LB16 * g;  // lane group g's K bytes of instruction s
+      // a K-contiguous operand's ordinary reads go before the other's asm block,
+      // whose wait then covers them
       frag_t fa, fb;
-      if constexpr (LB16 == 16) {
-        fa = RdA::read16k(sA, rbA, kb, lane);
-        fb = RdB::read16k(sB, rbB, kb, lane);
+      if constexpr (LA == LAYOUT_K || LB == LAYOUT_MN) {
+        fa = StreamFrag<Op, RdA, LA, RA_ROWS * EB>::read(sA, rbA, kb, lane);
+        fb = StreamFrag<Op, RdB, LB, RB_ROWS * EB>::read(sB, rbB, kb, lane);
       } else {
-        const i32x4 x = RdA::read16k(sA, rbA, kb, lane), y = RdA::read16k(sA, rbA, kb + 16, lane);
-        const i32x4 u = RdB::read16k(sB, rbB, kb, lane), v = RdB::read16k(sB, rbB, kb + 16, lane);
-        fa = frag_t{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-        fb = frag_t{u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+        fb = StreamFrag<Op, RdB, LB, RB_ROWS * EB>::read(sB, rbB, kb, lane);
+        fa = StreamFrag<Op, RdA, LA, RA_ROWS * EB>::read(sA, rbA, kb, lane);
       }
       Op::mma(acc, fb, fa);
     }
@@ -254,13 +290,12 @@ static hipError_t launch_one(const DenseArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// K-contiguous operands only: the transposing LDS reads of MN-contiguous tiles
-// are preceded by a compiler-inserted wait for all outstanding LDS DMA, which
-// would drain the ring every stage (those layouts take the general kernel).
 template <class Op, bool WIDE_A>
 static hipError_t launch_layouts(int la, int lb, const DenseArgs& a, hipStream_t s) {
   if (la == LAYOUT_K && lb == LAYOUT_K) return launch_one<Op, LAYOUT_K, LAYOUT_K, WIDE_A>(a, s);
-  return hipErrorInvalidValue;
+  if (la == LAYOUT_K) return launch_one<Op, LAYOUT_K, LAYOUT_MN, WIDE_A>(a, s);
+  if (lb == LAYOUT_K) return launch_one<Op, LAYOUT_MN, LAYOUT_K, WIDE_A>(a, s);
+  return launch_one<Op, LAYOUT_MN, LAYOUT_MN, WIDE_A>(a, s);
 }
 
 template <bool WIDE_A>
@@ -287,7 +322,6 @@ static hipError_t launch_ops(int dtA, int dtB, int la, int lb, const DenseArgs& 
 bool stream_path_ok(int dtA, int la, int lb, const DenseArgs& a, bool aligned) {
   const int64_t eb = (dtA == DT_BF16 || dtA == DT_F16) ? 2 : 1;
   if (!aligned || a.K == 0 || (a.K * eb) % 16 != 0) return false;
-  if (la != LAYOUT_K || lb != LAYOUT_K) return false;
   if (a.N > stream::NR && a.M > stream::NR) return false;
   // buffer windows and every offset into them (K tiles up to one past the end
   // of K, out-of-range offsets up to 2^31 + window) below 2 GiB

@@ -55,7 +55,7 @@ def test_dense_16bit_output(out, dtA, dtB, layA, layB, case):
     mcg = need_gpu()
     M, N, K, pad, path, sampled = case
     if path == 4 and layA != "k_contig":
-        path = 2  # MN-contiguous skinny problems take the general kernel with 128 x 32 tiles
+        path = 2  # a small MN-contiguous wide operand takes the general kernel with 128 x 32 tiles
     say(f"dense {dtA}x{dtB} {layA}/{layB} {M}x{N}x{K} -> {out}")
     fp8 = dtA in ("e4m3", "e5m2")
     A = W.operand("A", dtA, M, K, "normal", layA, seed=31,

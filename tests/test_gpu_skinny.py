@@ -1,6 +1,6 @@
 """GPU parity of the skinny and few-tile dense paths against the CPU oracle:
-the streaming kernel (N <= 32 or M <= 32, K-contiguous operands), the general
-kernel with 128 x 32 / 32 x 128 tiles (other layouts), and split K (partial
+the streaming kernel (N <= 32 or M <= 32, any storage order), the general
+kernel with 128 x 32 / 32 x 128 tiles (a small MN-contiguous wide operand), and split K (partial
 sums added into D with atomic adds, beta * C added after).  Float results must
 meet the accuracy bound, int8 results must be bit-exact; every case asserts
 the kernel and split the library reports for it, so each code path is known
@@ -49,7 +49,9 @@ def run_case(mcg, dtA, dtB, layA, layB, M, N, K, kernel, split, alpha=None, beta
     got_split = mcg.dense_splits(dtA, layA, layB, M, N, K, dA, A.ld, dB, B.ld, dC, D, dtD, beta)
     say(f"{dtA}x{dtB} {layA}/{layB} {M}x{N}x{K}: kernel {got_kernel}, splits {got_split}")
     assert got_kernel == kernel
-    if split is True:
+    if split is None:
+        pass
+    elif split is True:
         assert got_split > 1
     elif split is False:
         assert got_split == 1
@@ -163,15 +165,32 @@ def test_stream_split_int8_is_deterministic():
 
 # ------------------------------------------------------------ general kernel, skinny tiles
 
+def skinny_kernel(layA, layB, M, N):
+    """The library's choice for an aligned skinny problem: the streaming kernel,
+    or the general kernel's 128 x 32 / 32 x 128 tiles when the wide operand is
+    MN-contiguous with fewer than 2048 rows."""
+    wide_a = N <= 32 and N <= M
+    wide, lay = (M, layA) if wide_a else (N, layB)
+    if lay == "mn_contig" and wide < 2048:
+        return SKINNY_N if wide_a else SKINNY_M
+    return STREAM
+
+
 @pytest.mark.parametrize("dtA,dtB", [("bf16", "bf16"), ("i8", "i8"), ("e4m3", "e5m2"), ("f16", "f16")])
 @pytest.mark.parametrize("layA,layB", [("k_contig", "mn_contig"), ("mn_contig", "k_contig"),
                                        ("mn_contig", "mn_contig")])
-def test_skinny_tiles_other_layouts(dtA, dtB, layA, layB):
-    """MN-contiguous operands take the general kernel with 128 x 32 / 32 x 128 tiles."""
+def test_skinny_other_layouts(dtA, dtB, layA, layB):
+    """MN-contiguous operands: the streaming kernel (transposing reads of the wide
+    and the narrow tiles), or the general kernel's skinny tiles for a small
+    MN-contiguous wide operand; split and unsplit, padded leading dimensions,
+    ragged edges."""
     mcg = need_gpu()
-    run_case(mcg, dtA, dtB, layA, layB, 1024, 16, 3008, SKINNY_N, True, ldc_pad=4, seed=9)
-    run_case(mcg, dtA, dtB, layA, layB, 16, 1024, 3008, SKINNY_M, True, seed=10)
-    run_case(mcg, dtA, dtB, layA, layB, 304, 32, 256, SKINNY_N, False, pad=16, seed=11)
+    K = 3008 if dtA in ("bf16", "f16") else 6016  # 47 K tiles of 128 bytes: split
+    for M, N, K, split, kw in ((1024, 16, K, True, dict(ldc_pad=4, seed=9)), (16, 1024, K, True, dict(seed=10)),
+                               (304, 32, 256, False, dict(pad=16, seed=11)),
+                               (16, 4112, 1040, None, dict(pad=16, seed=18)),
+                               (2048, 32, 2048, None, dict(seed=19))):
+        run_case(mcg, dtA, dtB, layA, layB, M, N, K, skinny_kernel(layA, layB, M, N), split, **kw)
 
 
 def test_unaligned_skinny_takes_general_kernel():
