@@ -64,8 +64,10 @@ constexpr double KT_US = 1.0, ROUND_US = 3.0, ATOMIC_US = 1.4e-5, SPLIT_US = 5.0
 // tiles and K up to 8192; taken when it beats the best general plan by MID_MARGIN.
 constexpr double MID_KT_US = 0.5, MID_ROUND_US = 3.0, MID_MARGIN = 0.95;
 // The streaming kernel is HBM-bound: split only when there are too few blocks
-// to spread over the CUs, keeping 16 K tiles or more per split.
-constexpr int64_t STREAM_MIN_BLOCKS = 64, STREAM_MIN_KT = 16, STREAM_MN_MIN_WIDE = 2048;
+// to spread over the CUs (fewer than 128: splitting 64 blocks in two measured
+// 1.2-1.5x faster on bf16 2048 x 16 x 16384 and 3072 x 16 x 8192), keeping 16 K
+// tiles or more per split.
+constexpr int64_t STREAM_MIN_BLOCKS = 128, STREAM_MIN_KT = 16, STREAM_MN_MIN_WIDE = 2048;
 }  // namespace
 
 DensePlan plan_dense(int dtA, int la, int lb, const DenseArgs& a, bool aligned, bool can_split, int num_cu) {
@@ -127,15 +129,14 @@ DensePlan plan_dense(int dtA, int la, int lb, const DenseArgs& a, bool aligned, 
     // 128-row blocks when that still gives most CUs a block, else 32-row blocks
     // (measured: more blocks beat wider ones below 16384 rows), except for an
     // MN-contiguous wide operand: its LDS rows are one k of the block's rows, so
-    // only 128-row blocks fetch whole 128-byte lines; those fewer blocks are split
-    // until about 128 workgroups run (measured: 64 blocks unsplit ran at half the
-    // HBM rate, 256 workgroups were slower than 128 at 16384 rows)
+    // only 128-row blocks fetch whole 128-byte lines.  Fewer than
+    // STREAM_MIN_BLOCKS blocks are split along K (measured: 64 blocks unsplit ran
+    // at half the HBM rate; 256 workgroups were slower than 128 at 16384 rows)
     const int bw = wide >= 64 * NUM_CU || wide_mn ? 128 : 32;
     const int64_t blocks = cdiv(wide, bw);
-    const int64_t want = wide_mn ? 2 * STREAM_MIN_BLOCKS : STREAM_MIN_BLOCKS;
     int64_t s = 1;
-    if (can_split && blocks < want)
-      s = std::max<int64_t>(1, std::min(cdiv(want, blocks), nk / STREAM_MIN_KT));
+    if (can_split && blocks < STREAM_MIN_BLOCKS)
+      s = std::max<int64_t>(1, std::min(cdiv(STREAM_MIN_BLOCKS, blocks), nk / STREAM_MIN_KT));
     DensePlan pl = make(KERNEL_STREAM, s);
     pl.stream_bw = bw;
     return pl;
