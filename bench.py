@@ -57,7 +57,7 @@ SMALL_BATCH = 50  # launches of the 256^3 workload per event pair (one HIP graph
 KERNEL_SOURCES = ("gemm_fast_kernel.hpp", "gemm_fast.hip", "fast_tiles.hpp", "tile_order.hpp", "arch_gfx950.hpp",
                   "frag_layout.hpp")
 TRAFFIC_MEASURED = {
-    "sources_sha256": "6eae455ad6bec8e197abd07ae3df225de34ef69de360a2fc7bbb6f4879a9a544",
+    "sources_sha256": "d2bd7e997c58ed70c470bffb29292b832d46764f0828d0e2ddab74c24619da70",
     "read_bytes": 1806 * 2**20, "write_bytes": 256 * 2**20,
 }
 
