@@ -164,8 +164,11 @@ int gemm_dense(int dtypeA, int dtypeB, int layoutA, int layoutB,
  * epilogue.  Results stay deterministic.  A problem on the 128 x 128 form
  * whose tiles cannot be cut that way although its last round leaves compute
  * units idle takes the 256 x 256 split instead when K is long (at least 256 K
- * tiles of 128 bytes: 16384 16-bit or 32768 8-bit values).  This decomposition
- * is not from the pages; it is a scheduling choice of this library.
+ * tiles of 128 bytes: 16384 16-bit or 32768 8-bit values), and an aligned
+ * problem of at least 128 x 128 with so few tiles and so long a K that
+ * gemm_dense runs it on the general kernel takes the 128 x 128 form's split
+ * when it has one.  This decomposition is not from the pages; it is a
+ * scheduling choice of this library.
  *
  * workspace       : device memory owned by the caller, 16-byte aligned, or
  *                   NULL.  The call may use its first
@@ -198,8 +201,9 @@ int gemm_dense_ws(int dtypeA, int dtypeB, int layoutA, int layoutB,
  * static array (mcg_dense_workspace_bytes > mcg_dense_noalloc_scratch_bytes)
  * returns MCG_ERR_SCRATCH_LIMIT before anything is launched or written;
  * problems without a stream-K plan run as gemm_dense.  The long-K 256 x 256
- * split of a 128 x 128 problem (see gemm_dense_ws) is optional: it is taken
- * only when it fits the array, and otherwise the problem runs as gemm_dense.  Every call on one GPU
+ * split of a 128 x 128 problem and the 128 x 128 split of a general-kernel
+ * problem (see gemm_dense_ws) are optional: each is taken only when it fits
+ * the array, and otherwise the problem runs as gemm_dense.  Every call on one GPU
  * shares that GPU's array: calls that overlap on one GPU (other streams, other
  * host threads) race and must be ordered by the caller.
  */

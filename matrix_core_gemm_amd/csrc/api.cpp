@@ -175,6 +175,20 @@ constexpr int64_t LONG_K_TILES = 256;
 static int64_t dense_streamk(int dtypeA, int layoutA, int layoutB, mcg::DenseArgs& a, bool aligned, int kernel,
                              int64_t alt_cap, int* tile) {
   const int ncu = current_num_cu();
+  if (kernel == mcg::KERNEL_GENERAL) {
+    // Few tiles and a long K, which the cost model without a workspace leaves
+    // to the general kernel (with split K): the 128 x 128 form's stream-K split
+    // when it has one and it fits alt_cap (measured, bf16 1024^2 x 16384: 50
+    // against 120 us; 1024^2 x 32768: 79 against 176 us)
+    a.dp_tiles = a.sk_tiles = a.sk_wgs = 0;
+    if (!mcg::fast_path_ok(dtypeA, layoutA, layoutB, a, aligned, 128)) return 0;
+    *tile = 128;
+    const int64_t need = mcg::plan_streamk(dtypeA, a, ncu, 128);
+    if (need > 0 && need <= alt_cap) return need;
+    a.dp_tiles = a.sk_tiles = a.sk_wgs = 0;
+    return 0;
+  }
+  if (kernel != mcg::KERNEL_FAST && kernel != mcg::KERNEL_MID) return 0;
   *tile = kernel == mcg::KERNEL_MID ? 128 : 256;
   const int64_t need = mcg::plan_streamk(dtypeA, a, ncu, *tile);
   if (need > 0 || kernel != mcg::KERNEL_MID) return need;
@@ -234,7 +248,10 @@ static int dense_impl(int dtypeA, int dtypeB, int layoutA, int layoutB, int64_t 
   const bool aligned = dense_aligned(eb, K, A, lda, B, ldb);
   const mcg::DensePlan plan =
       mcg::plan_dense(dtypeA, layoutA, layoutB, a, aligned, can_split_k(a, C, D), current_num_cu());
-  const bool pipelined = plan.kernel == mcg::KERNEL_FAST || plan.kernel == mcg::KERNEL_MID;
+  // the pipelined kernels, and few-tile problems of the general kernel, may
+  // take a stream-K form with a workspace (dense_streamk)
+  const bool pipelined = plan.kernel == mcg::KERNEL_FAST || plan.kernel == mcg::KERNEL_MID ||
+                         plan.kernel == mcg::KERNEL_GENERAL;
   int tile = 0;
   if (pipelined && use_static) {
     const int64_t need =
@@ -513,7 +530,7 @@ int64_t mcg_dense_workspace_bytes(int dtypeA, int layoutA, int layoutB, int64_t 
                                   const void* A, int64_t lda, const void* B, int64_t ldb) {
   if (dtypeA < MCG_BF16 || dtypeA > MCG_FP8_E5M2 || M <= 0 || N <= 0 || K <= 0) return 0;
   const int kernel = dense_plan(dtypeA, layoutA, layoutB, M, N, K, A, lda, B, ldb, true).kernel;
-  if (kernel != mcg::KERNEL_FAST && kernel != mcg::KERNEL_MID) return 0;
+  if (kernel != mcg::KERNEL_FAST && kernel != mcg::KERNEL_MID && kernel != mcg::KERNEL_GENERAL) return 0;
   mcg::DenseArgs a{};
   a.A = (const char*)A;
   a.B = (const char*)B;

@@ -305,3 +305,66 @@ def test_long_k_mid_plan_takes_256_streamk(case):
         r = oracle.check_float(got, ref, s, K, alpha, A.scale, B.scale, beta, cc, out=out)
     say("  ", {k: v for k, v in r.items() if k != "worst"})
     assert r["ok"], r
+
+
+GENERAL_SK_CASES = [  # dtA, dtB, layA, layB, M, N, K, out, alpha, beta, D aliases C
+    # 64 tiles of 128 x 128 in 4 pieces of 64 K tiles (without a workspace: the
+    # general kernel with K split in 4)
+    ("bf16", "bf16", "k_contig", "k_contig", 1024, 1024, 16384, "f32", 1.0, 0.5, False),
+    ("bf16", "bf16", "mn_contig", "k_contig", 768, 768, 32768, "bf16", -0.5, 1.0, True),
+    # ragged: 9 tiles in 26 pieces of 5 K tiles, the last K tile cut short
+    ("i8", "i8", "k_contig", "k_contig", 300, 264, 16592, "i32", 3, -2, False),
+    ("e4m3", "e5m2", "k_contig", "k_contig", 256, 384, 8192, "f32", 1.0, 0.0, False),
+]
+
+
+@pytest.mark.parametrize("case", GENERAL_SK_CASES, ids=["bf16", "bf16_mn_bf16out_alias", "i8_ragged", "fp8"])
+def test_general_plan_takes_128_streamk(case):
+    """A few-tile, long-K problem that the general kernel takes without a
+    workspace runs as 128 x 128 stream-K with one; every output is compared."""
+    mcg = need_gpu()
+    dtA, dtB, layA, layB, M, N, K, out, alpha, beta, alias = case
+    say(f"general -> 128 x 128 stream-K {dtA}x{dtB} {layA}/{layB} {M}x{N}x{K} -> {out} alias={alias}")
+    fp8 = dtA in ("e4m3", "e5m2")
+    dist = "int8" if dtA == "i8" else "normal"
+    A = W.operand("A", dtA, M, K, dist, layA, seed=85, fp8_scaled=fp8)
+    B = W.operand("B", dtB, K, N, dist, layB, seed=86, fp8_scaled=fp8)
+    dA, dB = dev(A.codes), dev(B.codes)
+    assert mcg.dense_path(dtA, layA, layB, M, N, K, dA, A.ld, dB, B.ld) == 0
+    need = mcg.dense_workspace_bytes(dtA, layA, layB, M, N, K, dA, A.ld, dB, B.ld)
+    assert need > 0 and need % (128 * 128 * 4) == 0
+    ldc = N
+    if out == "i32":
+        C = W.c_matrix(M, N, "int20", seed=87, ldc=ldc)
+        D = torch.full((M, ldc), -0x5A5A5A5A, dtype=torch.int32, device="cuda")
+        dC = dev(C)
+    elif out == "f32":
+        C = W.c_matrix(M, N, "normal", seed=87, ldc=ldc) if beta != 0 else None
+        D = torch.full((M, ldc), float("nan"), dtype=torch.float32, device="cuda")
+        dC = None if C is None else dev(C)
+    else:
+        C = W.draw("normal", (M, ldc), 87).to(torch.float32).to(torch.bfloat16).view(torch.int16).numpy()
+        dC = dev(C)
+        C = C.view(np.uint16)
+        D = torch.full((M, ldc), 0x7FC0, dtype=torch.int16, device="cuda")
+    if alias:
+        D = dC
+    mcg.gemm_dense_ws(dtA, dtB, layA, layB, M, N, K, dA, A.ld, dB, B.ld, dC, D, ldc, out, alpha, beta,
+                      A.scale, B.scale, workspace=workspace(need))
+    torch.cuda.synchronize()
+    d = D.cpu().numpy()
+    say(f"  {need // (128 * 128 * 4)} pieces, {M * N} outputs compared")
+    if out == "i32":
+        ref = oracle.gemm_i8(layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, ldc, alpha, beta)
+        r = oracle.check_exact(d[:M, :N], ref)
+    else:
+        ref, s = oracle.gemm_float(dtA, dtB, layA, layB, M, N, K, A.codes, A.ld, B.codes, B.ld, C, ldc,
+                                   alpha, beta, A.scale, B.scale, out=out)
+        if out == "bf16":
+            dec = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).double().numpy()
+            got, cc = dec(d)[:M, :N], dec(C)[:M, :N]
+        else:
+            got, cc = d[:M, :N], None if C is None else C[:M, :N]
+        r = oracle.check_float(got, ref, s, K, alpha, A.scale, B.scale, beta, cc, out=out)
+    say("  ", {k: v for k, v in r.items() if k != "worst"})
+    assert r["ok"], r

@@ -106,6 +106,10 @@ def test_workspace_plan(monkeypatch):
     assert _ws(mcg, "bf16", 2048, 2048, 16384) == 0  # 256 tiles of 128 x 128: one whole round
     assert _ws(mcg, "bf16", 1536, 1536, 12288) == 0  # 192 K tiles: the two forms are even
     assert _ws(mcg, "i8", 1536, 1536, 16384) == 0
+    # few tiles, long K: the general kernel without a workspace, the 128 x 128
+    # split with one (1024^2 x 16384: 64 tiles in 4 pieces; 300 x 264: 9 in 26)
+    assert _ws(mcg, "bf16", 1024, 1024, 16384) == 256 * 128 * 128 * 4
+    assert _ws(mcg, "i8", 300, 264, 16592) == 234 * 128 * 128 * 4
     # not the pipelined kernel (skinny, binary64)
     assert _ws(mcg, "bf16", 32768, 16, 8192) == 0
     assert mcg.dense_workspace_bytes("f64", "k_contig", "k_contig", 7168, 7168, 7168, 0x1000, 7168, 0x1000,
