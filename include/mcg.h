@@ -356,10 +356,11 @@ int mcg_validate_compress24(int dtype, int64_t M, int64_t K, const void* A, int6
    mcg_dense_path: the kernel gemm_dense runs for these operands with a
      binary32/int32 D that is not C: 0 general kernel, 128 x 128 tiles (any
      shape, alignment or leading dimension); 1 the 256 x 256 pipelined kernel;
-     2 general kernel with 128 x 32 tiles (N <= 32, aligned operands);
-     3 general kernel with 32 x 128 tiles (M <= 32, aligned operands);
-     4 the streaming kernel (N <= 32 or M <= 32, K-contiguous aligned
-     operands); 5 the binary64 kernel (dtypeA MCG_F64, any shape); 6 the
+     2 general kernel with 128 x 32 tiles (N <= 32, aligned operands, the
+     M x K operand MN-contiguous with M < 2048, or operand windows of 2 GiB);
+     3 general kernel with 32 x 128 tiles (M <= 32, likewise for B and N);
+     4 the streaming kernel (N <= 32 or M <= 32, aligned operands in any
+     storage order, otherwise); 5 the binary64 kernel (dtypeA MCG_F64, any shape); 6 the
      pipelined kernel with 128 x 128 tiles (aligned operands, M and N >= 128,
      too few 256 x 256 tiles to fill the chip, faster than kernel 0 by the
      planner's cost model).
