@@ -264,3 +264,20 @@ def test_full_size_skinny(M, N, K):
     r = run_case(mcg, "bf16", "bf16", "k_contig", "k_contig", M, N, K, STREAM, False, alpha=1.0,
                  beta=0.0, seed=19, sample=sample)
     say(f"  sampled {r['n']} outputs; max |delta|/bound = {r['max_ratio']}")
+
+
+@pytest.mark.parametrize("dt,layA,layB,M,N,K", [
+    ("bf16", "mn_contig", "k_contig", 32768, 16, 8192), ("bf16", "k_contig", "mn_contig", 16, 32768, 8192),
+    ("bf16", "mn_contig", "mn_contig", 8192, 16, 8192), ("i8", "mn_contig", "k_contig", 32768, 16, 8192)])
+def test_full_size_skinny_mn_contiguous(dt, layA, layB, M, N, K):
+    """The skinny benchmark shapes with a column-major (MN-contiguous) wide
+    operand on the streaming kernel: sampled outputs, including every output
+    of the first and last narrow column / row (int8 bit-exact)."""
+    mcg = need_gpu()
+    if N <= 32:
+        sample = W.sample_coords(M, N, n_random=4096, full_cols=(0, N - 1))
+    else:
+        sample = W.sample_coords(M, N, n_random=4096, full_rows=(0, M - 1))
+    r = run_case(mcg, dt, dt, layA, layB, M, N, K, STREAM, None, alpha=2 if dt == "i8" else 1.0,
+                 beta=0.0, seed=20, sample=sample)
+    say(f"  sampled outputs checked: {r}")
